@@ -1,0 +1,346 @@
+#!/usr/bin/env python3
+"""Benchmark of the RWKV WKV operators on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A "step" is one RWKV-4 WKV forward over the workload B=8 T=1024 C=768
+(float32 k, v, y; seeded synthetic inputs already resident in HBM).  Five
+copies of (k, v, y) rotate so that the 377 MB working set exceeds
+the 256 MB Infinity Cache and every step reads from HBM.
+
+Printed: ONE JSON line.  `value` is achieved algorithmic HBM bandwidth
+(12 bytes per element: read k, v; write y) over the timed steps.
+`roofline` relates the forward kernel's algorithmic bytes per launch to its
+mean launch duration (HIP events around every launch, on the launch stream)
+and to the 8 TB/s HBM peak.  `cpu_baseline` is the fp64 NumPy oracle timed
+on this host on the same workload.  `secondary` holds the other entry points
+(long-sequence forward, the 4096-step decode loop, the Eagle forward).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import platform
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "WKV4 fwd achieved HBM GB/s (% of peak) + Gelem/s (B·T·C), fp32"
+HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "linear_attention_sequence_rwkv_amd", "csrc")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(files=("wkv4.hip", "wkv_device.h")) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_counter_summary(name: str, src_hash: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or
+    None when the summary is missing or was taken on other kernel source."""
+    path = os.path.join(PROFILES, name)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            m = re.match(r"^\s*-?\s*`?(\w+)`?\s*[:=]\s*`?([0-9a-fA-F.eE+-]+)`?\s*$", line)
+            if m:
+                vals[m.group(1)] = m.group(2)
+    if vals.get("kernel_source_sha256") != src_hash:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Timer:
+    """HIP events on the current stream: whole region plus one pair per launch."""
+
+    def __init__(self, torch, n):
+        E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+        self.start, self.end = E(), E()
+        self.pairs = [(E(), E()) for _ in range(n)]
+
+
+def bench_wkv4_forward(torch, rw, cfg, steps, warmup, rotate):
+    import synth
+    dev = torch.device("cuda:0")
+    inp = synth.wkv4_inputs_for(cfg)
+    B, T, C = cfg.B, cfg.T, cfg.C
+    w = torch.from_numpy(inp["w"]).to(dev)
+    u = torch.from_numpy(inp["u"]).to(dev)
+    k0 = torch.from_numpy(inp["k"]).to(dev)
+    v0 = torch.from_numpy(inp["v"]).to(dev)
+    ks = [k0] + [k0.clone() for _ in range(rotate - 1)]
+    vs = [v0] + [v0.clone() for _ in range(rotate - 1)]
+    ys = [torch.empty_like(k0) for _ in range(rotate)]
+    lib = rw.load_library()
+    need = lib.rwkv_wkv4_forward_workspace(B, T, C)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    # Marshalled once; the timed loop is nothing but C-ABI calls.
+    calls = [(B, T, C, P(w), P(u), P(ks[i]), P(vs[i]), P(ys[i]), P(ws), need, sh)
+             for i in range(rotate)]
+    fn = lib.rwkv_wkv4_forward
+    for i in range(warmup):
+        assert fn(*calls[i % rotate]) == 0
+    torch.cuda.synchronize()
+    tm = Timer(torch, steps)
+    tm.start.record(stream)
+    for i in range(steps):
+        s, e = tm.pairs[i]
+        s.record(stream)
+        st = fn(*calls[i % rotate])
+        e.record(stream)
+        if st != 0:
+            raise RuntimeError(f"rwkv_wkv4_forward status {st}")
+    tm.end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = tm.start.elapsed_time(tm.end)
+    kern_ms = sum(s.elapsed_time(e) for s, e in tm.pairs) / steps
+    # sanity: the output of the last launch is finite and the first token is v
+    y_last = ys[(steps - 1) % rotate]
+    assert torch.isfinite(y_last).all().item()
+    assert torch.equal(y_last[:, 0], vs[(steps - 1) % rotate][:, 0])
+    return {"ms_per_step": total_ms / steps, "kernel_ms": kern_ms,
+            "elems": B * T * C, "bytes": 12 * B * T * C}
+
+
+def bench_copy_peak(torch, nbytes=1 << 30, reps=20):
+    dev = torch.device("cuda:0")
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def bench_decode(torch, rw, cfg, reps):
+    import synth
+    dev = torch.device("cuda:0")
+    inp = synth.wkv4_step_inputs(cfg.B, cfg.C, cfg.pool, cfg.seed)
+    w = torch.from_numpy(inp["w"]).to(dev)
+    u = torch.from_numpy(inp["u"]).to(dev)
+    k_all = torch.from_numpy(inp["k"]).to(dev)
+    v_all = torch.from_numpy(inp["v"]).to(dev)
+    a, b, p = rw.rwkv_wkv4_state_init(cfg.B, cfg.C, device=dev)
+    y = torch.empty((cfg.B, cfg.C), dtype=torch.float32, device=dev)
+    lib = rw.load_library()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+
+    def run(stream):
+        sh = ctypes.c_void_p(stream.cuda_stream)
+        for t in range(cfg.steps):
+            i = t % cfg.pool
+            st = lib.rwkv_wkv4_step(cfg.B, cfg.C, P(a), P(b), P(p), P(w), P(u), P(k_all[i]),
+                                    P(v_all[i]), P(y), sh)
+            if st != 0:
+                raise RuntimeError(f"rwkv_wkv4_step status {st}")
+
+    stream = torch.cuda.current_stream(dev)
+    run(stream)  # warm-up
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for _ in range(reps):
+        run(stream)
+    e.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = s.elapsed_time(e) / reps
+    # The same 4096 launches captured once in a HIP graph and replayed.
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream(dev)
+    cap.wait_stream(stream)
+    with torch.cuda.graph(g, stream=cap):
+        run(torch.cuda.current_stream(dev))
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    s.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = s.elapsed_time(e) / reps
+    assert torch.isfinite(y).all().item()
+    elems = cfg.B * cfg.C * cfg.steps
+    return {"eager_ms": eager_ms, "graph_ms": graph_ms, "elems": elems, "bytes": 36 * elems}
+
+
+def bench_wkv5(torch, rw, cfg, reps):
+    import synth
+    dev = torch.device("cuda:0")
+    inp = synth.wkv5_inputs_for(cfg)
+    to = lambda x: torch.from_numpy(x).to(dev)  # noqa: E731
+    r, k, v = (to(inp[n + "_bits"]).view(torch.bfloat16) for n in ("r", "k", "v"))
+    w, u = to(inp["w"]), to(inp["u"])
+    o = torch.empty((cfg.B, cfg.T, cfg.H, cfg.D), dtype=torch.float32, device=dev)
+    rw.rwkv_wkv5_forward(r, k, v, w, u, o=o)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        rw.rwkv_wkv5_forward(r, k, v, w, u, o=o)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    elems = cfg.B * cfg.T * cfg.H * cfg.D
+    return {"ms": ms, "elems": elems, "bytes": 10 * elems, "flops": 4 * cfg.D * elems}
+
+
+def cpu_baseline(cfg, budget_s):
+    """The fp64 oracle's recurrence on the full workload, repeated for about
+    `budget_s` seconds of host time."""
+    import numpy as np
+    import oracle.wkv_oracle as O
+    import synth
+    inp = synth.wkv4_inputs_for(cfg)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        O.wkv4_recurrent(inp["w"], inp["u"], inp["k"], inp["v"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    elems = cfg.B * cfg.T * cfg.C * reps
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    del np
+    return {"value": round(12 * elems / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": (f"fp64 NumPy recurrence over the full B={cfg.B} T={cfg.T} C={cfg.C} "
+                       f"workload, {reps} run(s) in {el:.1f} s on one core of {cpu} "
+                       f"({len(os.sched_getaffinity(0))} cores visible)"),
+            "gelem_per_s": round(elems / el / 1e9, 6)}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rotate", type=int, default=5)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB copy (counter calibration runs)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(the operator shards over batch/channels with no communication); "
+              "run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import linear_attention_sequence_rwkv_amd as rw
+    import synth
+    rw.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+
+    cfg = synth.CFG_WKV4_169M
+    if args.copy_calibration:
+        copy_gbps = bench_copy_peak(torch)
+    log(f"bench: {cfg.name} steps={args.steps} warmup={args.warmup} rotate={args.rotate}")
+    prim = bench_wkv4_forward(torch, rw, cfg, args.steps, args.warmup, args.rotate)
+    value = prim["bytes"] / (prim["ms_per_step"] * 1e-3) / 1e9
+    achieved = prim["bytes"] / (prim["kernel_ms"] * 1e-3) / 1e9
+    src_hash = kernel_source_hash()
+    traffic = read_counter_summary("wkv4_fwd_B8_T1024_C768_counters.md", src_hash)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(prim["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "C": cfg.C,
+                   "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+                   "gelem_per_s": round(prim["elems"] / (prim["ms_per_step"] * 1e-3) / 1e9, 2),
+                   "bytes_per_elem": 12, "rotated_copies": args.rotate},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel": "wkv4_fwd_tiled",
+                     "kernel_us": round(prim["kernel_ms"] * 1e3, 3),
+                     "kernel_source": src_hash},
+    }
+    if args.copy_calibration:
+        line["copy_peak_GBps"] = round(copy_gbps, 1)
+
+    if not args.no_secondary:
+        sec = {}
+        lc = synth.CFG_WKV4_LONG
+        log(f"bench: {lc.name}")
+        r = bench_wkv4_forward(torch, rw, lc, steps=10, warmup=2, rotate=1)
+        sec[lc.name] = {"ms": round(r["ms_per_step"], 4), "kernel_ms": round(r["kernel_ms"], 4),
+                        "GBps": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9, 1),
+                        "gelem_per_s": round(r["elems"] / (r["kernel_ms"] * 1e-3) / 1e9, 1)}
+        dc = synth.CFG_WKV4_DECODE
+        log(f"bench: {dc.name}")
+        r = bench_decode(torch, rw, dc, reps=3)
+        sec[dc.name] = {"eager_ms": round(r["eager_ms"], 3), "graph_ms": round(r["graph_ms"], 3),
+                        "graph_GBps": round(r["bytes"] / (r["graph_ms"] * 1e-3) / 1e9, 1),
+                        "eager_GBps": round(r["bytes"] / (r["eager_ms"] * 1e-3) / 1e9, 1),
+                        "us_per_step_graph": round(1e3 * r["graph_ms"] / dc.steps, 3)}
+        ec = synth.CFG_WKV5_EAGLE
+        log(f"bench: {ec.name}")
+        r = bench_wkv5(torch, rw, ec, reps=5)
+        sec[ec.name] = {"ms": round(r["ms"], 4),
+                        "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
+                        "algorithmic_TFLOPs": round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 2)}
+        line["secondary"] = sec
+
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
+
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,150 @@
+/*
+ * rwkv_wkv.h - C ABI of the RWKV WKV operator library for AMD MI355X (gfx950).
+ *
+ * Sources, by page title and section (the formulas each call evaluates):
+ *   [RWKV-digest]  "RWKV - Reinventing RNNs for the Transformer Era" (Korean
+ *                  paper digest, irregular6612.github.io), Method > core
+ *                  components > (2) Time-mixing (WKV): the WKV_t equation and
+ *                  its recurrent form with states a_t, b_t.
+ *   [RWKV-summary] "RWKV: Reinventing RNNs for the Transformer Era"
+ *                  (flashpapers.ai summary), sec. 3 "The WKV Operator".
+ *   [Eagle-Finch]  "RWKV-5 Eagle and RWKV-6 Finch" (ql.gl blog), section
+ *                  "Eagle: extending vector memory to matrix memory".
+ *
+ * Common rules for every entry point:
+ *   - Pointers named as device pointers are device memory of the current HIP
+ *     device, owned by the caller, dense row-major with the last index
+ *     fastest, and 16-byte aligned.  The library never allocates, frees,
+ *     synchronises or prints.
+ *   - Calls enqueue work on `stream` (0 = the null stream) and return without
+ *     waiting.  A fault inside a kernel surfaces at the caller's next
+ *     synchronisation, not in the return value.
+ *   - Arguments are checked on the host before any HIP call.  A failed check
+ *     returns a negative status and enqueues nothing.  Zero-sized problems
+ *     return RWKV_OK and enqueue nothing.
+ *   - Values are not checked: NaN/Inf in the inputs propagate to the outputs.
+ *   - Outputs must not overlap inputs, except the in-place recurrent state.
+ *   - All entry points are thread-safe; concurrent calls that share a
+ *     workspace or a state buffer race and are not allowed.
+ */
+#ifndef RWKV_WKV_H
+#define RWKV_WKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* HIP's stream handle (the same typedef as in hip_runtime_api.h). */
+typedef struct ihipStream_t* hipStream_t;
+
+#define RWKV_WKV_ABI_VERSION 1
+
+/* Status codes returned by every int-valued entry point. */
+#define RWKV_OK               0
+#define RWKV_ERR_NULLPTR     -1  /* a required pointer is NULL */
+#define RWKV_ERR_SHAPE       -2  /* negative size, or a size product overflows */
+#define RWKV_ERR_UNSUPPORTED -3  /* a shape this build does not implement */
+#define RWKV_ERR_WORKSPACE   -4  /* workspace NULL or smaller than required */
+#define RWKV_ERR_ALIGN       -5  /* a pointer is not 16-byte aligned */
+#define RWKV_ERR_HIP         -6  /* a HIP launch failed; see rwkv_last_hip_error */
+
+/* Version of this ABI (RWKV_WKV_ABI_VERSION of the build). */
+int rwkv_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* rwkv_status_str(int status);
+
+/* hipError_t value of the last RWKV_ERR_HIP returned on this thread (0 if none). */
+int rwkv_last_hip_error(void);
+
+/* ------------------------------------------------------------------------
+ * RWKV-4 time-parallel forward.   [RWKV-digest] (2) Time-mixing, WKV_t;
+ * [RWKV-summary] sec. 3 "The WKV Operator".
+ *
+ * For every batch b, token t and channel c (0-based):
+ *   y[b,t,c] = ( sum_{i<t} e^{-(t-1-i) w[c] + k[b,i,c]} v[b,i,c] + e^{u[c]+k[b,t,c]} v[b,t,c] )
+ *            / ( sum_{i<t} e^{-(t-1-i) w[c] + k[b,i,c]}          + e^{u[c]+k[b,t,c]} )
+ * i.e. the history starts empty at t = 0.
+ *
+ *   w  [C]      float32  decay rate >= 0; one step back multiplies by e^{-w}
+ *   u  [C]      float32  current-token bonus
+ *   k, v [B,T,C] float32
+ *   y  [B,T,C]  float32  output
+ *   ws, ws_bytes         device workspace of at least
+ *                        rwkv_wkv4_forward_workspace(B,T,C) bytes.  It must be
+ *                        zero-filled before its first use; each call leaves it
+ *                        ready for the next call on the same stream.  A call
+ *                        whose workspace size is 0 accepts ws == NULL.
+ * Accuracy: max |y - exact| <= 1e-4 * S, where S is the same weighted mean
+ * taken over |v| (float32 arithmetic, hardware exp2 and reciprocal).
+ * ---------------------------------------------------------------------- */
+size_t rwkv_wkv4_forward_workspace(int64_t B, int64_t T, int64_t C);
+int rwkv_wkv4_forward(int64_t B, int64_t T, int64_t C,
+                      const float* w, const float* u,
+                      const float* k, const float* v,
+                      float* y,
+                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * RWKV-4 recurrent state.   [RWKV-digest] (2) Time-mixing, recurrent form
+ *   a_t = e^{-w} a_{t-1} + e^{k_t} v_t,   b_t = e^{-w} b_{t-1} + e^{k_t}.
+ * The library stores the sums scaled: a_true = a * e^{p}, b_true = b * e^{p},
+ * three float32 arrays a, b, p of shape [B,C].  Only a/b and log(b)+p are
+ * meaningful; the triple itself is not unique.
+ *
+ * rwkv_wkv4_state_init: empty history (a = b = 0, p = -1e38).
+ * ---------------------------------------------------------------------- */
+int rwkv_wkv4_state_init(int64_t B, int64_t C, float* a, float* b, float* p,
+                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * RWKV-4 fused single-token step.   [RWKV-digest] (2) Time-mixing:
+ *   y = (a_{t-1} + e^{u+k} v) / (b_{t-1} + e^{u+k})   using the OLD state,
+ * then the state advances in place with this token's k, v.
+ *
+ *   a, b, p  [B,C]  float32  state, read and updated in place
+ *   w, u     [C]    float32  as for the forward
+ *   k, v     [B,C]  float32  this token
+ *   y        [B,C]  float32  output
+ * N steps from rwkv_wkv4_state_init give the same y as the forward over the
+ * same N tokens (within the forward's accuracy bound).
+ * ---------------------------------------------------------------------- */
+int rwkv_wkv4_step(int64_t B, int64_t C,
+                   float* a, float* b, float* p,
+                   const float* w, const float* u,
+                   const float* k, const float* v,
+                   float* y, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Eagle (RWKV-5) matrix-state forward.   [Eagle-Finch] "Eagle":
+ *   s' = diag(w) s + k^T v,   wkv' = s + diag(u) k^T v,  read by r.
+ * Per batch b and head h, with a D x D state s[i][j] (key i, value j) that
+ * starts at zero:
+ *   o[b,t,h,j] = sum_i r[b,t,h,i] * ( s_t[i][j] + u[h,i] k[b,t,h,i] v[b,t,h,j] )
+ *   s_{t+1}[i][j] = w[h,i] s_t[i][j] + k[b,t,h,i] v[b,t,h,j]
+ *
+ *   r, k, v  [B,T,H,D]  bfloat16 bit patterns (uint16)
+ *   w        [H,D]      float32 decay factor in (0, 1]
+ *   u        [H,D]      float32 current-token bonus
+ *   o        [B,T,H,D]  float32 output
+ *   D must be 64 (RWKV_ERR_UNSUPPORTED otherwise).
+ *   ws, ws_bytes: at least rwkv_wkv5_forward_workspace(B,T,H,D) bytes (may
+ *   be 0, then ws may be NULL).
+ * Accuracy: max |o - exact| <= 2e-2 * o_abs, where o_abs is the same sum
+ * over |r|, |k|, |v|, |u| (bf16 products, float32 accumulation).
+ * ---------------------------------------------------------------------- */
+size_t rwkv_wkv5_forward_workspace(int64_t B, int64_t T, int64_t H, int64_t D);
+int rwkv_wkv5_forward(int64_t B, int64_t T, int64_t H, int64_t D,
+                      const uint16_t* r, const uint16_t* k, const uint16_t* v,
+                      const float* w, const float* u,
+                      float* o,
+                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RWKV_WKV_H */

@@ -1,0 +1,261 @@
+"""Python binding of librwkv_wkv.so: the RWKV WKV operators on MI355X.
+
+Argument marshalling only.  Each function has the name of the C entry point
+it calls (declared in include/rwkv_wkv.h), takes torch tensors that already
+live on the GPU, passes their device pointers and torch's current HIP stream,
+and turns a negative status into an exception.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback: if the
+library is missing, every call raises.
+
+torch is used only to allocate outputs/workspaces and to name the stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = [
+    "LIB_PATH", "load_library", "RwkvError",
+    "rwkv_abi_version", "rwkv_status_str", "rwkv_last_hip_error",
+    "rwkv_wkv4_forward_workspace", "rwkv_wkv4_forward",
+    "rwkv_wkv4_state_init", "rwkv_wkv4_step",
+    "rwkv_wkv5_forward_workspace", "rwkv_wkv5_forward",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librwkv_wkv.so")
+
+_lib = None
+_lib_lock = threading.Lock()
+
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+_p = ctypes.c_void_p
+
+# name -> (restype, argtypes), mirroring include/rwkv_wkv.h
+_SIGNATURES = {
+    "rwkv_abi_version": (ctypes.c_int, []),
+    "rwkv_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "rwkv_last_hip_error": (ctypes.c_int, []),
+    "rwkv_wkv4_forward_workspace": (_sz, [_i64, _i64, _i64]),
+    "rwkv_wkv4_forward": (ctypes.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "rwkv_wkv4_state_init": (ctypes.c_int, [_i64, _i64, _p, _p, _p, _p]),
+    "rwkv_wkv4_step": (ctypes.c_int, [_i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "rwkv_wkv5_forward_workspace": (_sz, [_i64, _i64, _i64, _i64]),
+    "rwkv_wkv5_forward": (ctypes.c_int,
+                          [_i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+}
+
+
+class RwkvError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str, hip_error: int = 0):
+        super().__init__(f"{fn}: status {status} ({msg})"
+                         + (f", hipError {hip_error}" if hip_error else ""))
+        self.status = status
+        self.hip_error = hip_error
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise ImportError(
+                f"{p} not found: build it with "
+                "`python -m linear_attention_sequence_rwkv_amd.build`")
+        lib = ctypes.CDLL(p)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+        return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status == 0:
+        return
+    lib = load_library()
+    msg = lib.rwkv_status_str(status).decode()
+    if status == -6:
+        raise RwkvError(fn, status, msg, lib.rwkv_last_hip_error())
+    raise ValueError(f"{fn}: status {status} ({msg})")
+
+
+def rwkv_abi_version() -> int:
+    return load_library().rwkv_abi_version()
+
+
+def rwkv_status_str(status: int) -> str:
+    return load_library().rwkv_status_str(status).decode()
+
+
+def rwkv_last_hip_error() -> int:
+    return load_library().rwkv_last_hip_error()
+
+
+# ---------------------------------------------------------------- helpers ---
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev_tensor(name, t, dtypes, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU, got {t.device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return t
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
+
+
+def _stream(device, stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# Workspaces are zero-filled once and reused per (device, stream): the
+# library leaves them ready for the next call on the same stream.
+_ws_cache: dict = {}
+_ws_lock = threading.Lock()
+
+
+def _workspace(kind: str, device, stream_handle: int, nbytes: int):
+    if nbytes == 0:
+        return None
+    torch = _torch()
+    key = (kind, device.index, stream_handle)
+    with _ws_lock:
+        buf = _ws_cache.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+            _ws_cache[key] = buf
+        return buf
+
+
+# ----------------------------------------------------------------- RWKV-4 ---
+
+def rwkv_wkv4_forward_workspace(B: int, T: int, C: int) -> int:
+    return int(load_library().rwkv_wkv4_forward_workspace(B, T, C))
+
+
+def rwkv_wkv4_forward(w, u, k, v, y=None, ws=None, stream=None):
+    """y[B,T,C] = WKV(w, u, k, v); see rwkv_wkv4_forward in rwkv_wkv.h.
+
+    ``ws`` (optional) is a caller-owned zero-initialised uint8 GPU tensor of at
+    least rwkv_wkv4_forward_workspace(B, T, C) bytes; by default a cached one
+    per (device, stream) is used.
+    """
+    torch = _torch()
+    lib = load_library()
+    f32 = (torch.float32,)
+    k = _dev_tensor("k", k, f32, 3)
+    v = _dev_tensor("v", v, f32, 3)
+    w = _dev_tensor("w", w, f32, 1)
+    u = _dev_tensor("u", u, f32, 1)
+    B, T, C = k.shape
+    if tuple(v.shape) != (B, T, C) or w.shape[0] != C or u.shape[0] != C:
+        raise ValueError("shape mismatch among w, u, k, v")
+    if y is None:
+        y = torch.empty_like(k)
+    else:
+        y = _dev_tensor("y", y, f32, 3)
+        if tuple(y.shape) != (B, T, C):
+            raise ValueError("y has the wrong shape")
+    st = _stream(k.device, stream)
+    need = lib.rwkv_wkv4_forward_workspace(B, T, C)
+    if ws is None:
+        ws = _workspace("wkv4", k.device, st.value or 0, need)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    status = lib.rwkv_wkv4_forward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
+                                   _ptr(ws), nbytes, st)
+    _check("rwkv_wkv4_forward", status)
+    return y
+
+
+def rwkv_wkv4_state_init(B: int, C: int, device="cuda", stream=None):
+    """Return an empty recurrent state (a, b, p), three float32 [B, C] tensors."""
+    torch = _torch()
+    lib = load_library()
+    dev = torch.device(device)
+    a, b, p = (torch.empty((B, C), dtype=torch.float32, device=dev) for _ in range(3))
+    status = lib.rwkv_wkv4_state_init(B, C, _ptr(a), _ptr(b), _ptr(p), _stream(dev, stream))
+    _check("rwkv_wkv4_state_init", status)
+    return a, b, p
+
+
+def rwkv_wkv4_step(a, b, p, w, u, k, v, y=None, stream=None):
+    """One token: returns y[B,C] and updates the state (a, b, p) in place."""
+    torch = _torch()
+    lib = load_library()
+    f32 = (torch.float32,)
+    a, b, p = (_dev_tensor(n, t, f32, 2) for n, t in (("a", a), ("b", b), ("p", p)))
+    k = _dev_tensor("k", k, f32, 2)
+    v = _dev_tensor("v", v, f32, 2)
+    w = _dev_tensor("w", w, f32, 1)
+    u = _dev_tensor("u", u, f32, 1)
+    B, C = a.shape
+    for n, t in (("b", b), ("p", p), ("k", k), ("v", v)):
+        if tuple(t.shape) != (B, C):
+            raise ValueError(f"{n} has the wrong shape")
+    if w.shape[0] != C or u.shape[0] != C:
+        raise ValueError("w, u must have C entries")
+    if y is None:
+        y = torch.empty_like(k)
+    else:
+        y = _dev_tensor("y", y, f32, 2)
+    status = lib.rwkv_wkv4_step(B, C, _ptr(a), _ptr(b), _ptr(p), _ptr(w), _ptr(u), _ptr(k),
+                                _ptr(v), _ptr(y), _stream(a.device, stream))
+    _check("rwkv_wkv4_step", status)
+    return y
+
+
+# ------------------------------------------------------------------ Eagle ---
+
+def rwkv_wkv5_forward_workspace(B: int, T: int, H: int, D: int) -> int:
+    return int(load_library().rwkv_wkv5_forward_workspace(B, T, H, D))
+
+
+def rwkv_wkv5_forward(r, k, v, w, u, o=None, ws=None, stream=None):
+    """o[B,T,H,D] float32 from bf16 r, k, v [B,T,H,D] and float32 w, u [H,D]."""
+    torch = _torch()
+    lib = load_library()
+    half = (torch.bfloat16, torch.int16, torch.uint16)
+    r = _dev_tensor("r", r, half, 4)
+    k = _dev_tensor("k", k, half, 4)
+    v = _dev_tensor("v", v, half, 4)
+    w = _dev_tensor("w", w, (torch.float32,), 2)
+    u = _dev_tensor("u", u, (torch.float32,), 2)
+    B, T, H, D = r.shape
+    if tuple(k.shape) != (B, T, H, D) or tuple(v.shape) != (B, T, H, D):
+        raise ValueError("r, k, v shapes differ")
+    if tuple(w.shape) != (H, D) or tuple(u.shape) != (H, D):
+        raise ValueError("w, u must be [H, D]")
+    if o is None:
+        o = torch.empty((B, T, H, D), dtype=torch.float32, device=r.device)
+    else:
+        o = _dev_tensor("o", o, (torch.float32,), 4)
+    st = _stream(r.device, stream)
+    need = lib.rwkv_wkv5_forward_workspace(B, T, H, D)
+    if ws is None:
+        ws = _workspace("wkv5", r.device, st.value or 0, need)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    status = lib.rwkv_wkv5_forward(B, T, H, D, _ptr(r), _ptr(k), _ptr(v), _ptr(w), _ptr(u),
+                                   _ptr(o), _ptr(ws), nbytes, st)
+    _check("rwkv_wkv5_forward", status)
+    return o

@@ -1,0 +1,145 @@
+// C ABI of the WKV library: argument checks, plans, workspace sizing and
+// launches.  Every check runs on the host before any HIP call; nothing here
+// allocates, synchronises or prints.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include <initializer_list>
+
+#include "rwkv_wkv.h"
+#include "wkv_internal.h"
+
+#define RWKV_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+// Largest element count accepted for any array (keeps byte sizes and 64-bit
+// index arithmetic far from overflow).
+constexpr int64_t kMaxElems = int64_t(1) << 56;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// out = a * b with a, b >= 0; false on overflow past kMaxElems.
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > kMaxElems / a) return false;
+  *out = a * b;
+  return true;
+}
+
+bool dims_ok(std::initializer_list<int64_t> dims, int64_t* numel) {
+  int64_t n = 1;
+  for (int64_t d : dims)
+    if (!mul_ok(n, d, &n)) return false;
+  *numel = n;
+  return true;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return RWKV_OK;
+  g_last_hip_error = int(e);
+  return RWKV_ERR_HIP;
+}
+
+}  // namespace
+
+RWKV_API int rwkv_abi_version(void) { return RWKV_WKV_ABI_VERSION; }
+
+RWKV_API const char* rwkv_status_str(int status) {
+  switch (status) {
+    case RWKV_OK: return "ok";
+    case RWKV_ERR_NULLPTR: return "a required pointer is NULL";
+    case RWKV_ERR_SHAPE: return "negative size or size overflow";
+    case RWKV_ERR_UNSUPPORTED: return "shape not supported by this build";
+    case RWKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case RWKV_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case RWKV_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+RWKV_API int rwkv_last_hip_error(void) { return g_last_hip_error; }
+
+// ------------------------------------------------------------------ RWKV-4
+
+RWKV_API size_t rwkv_wkv4_forward_workspace(int64_t B, int64_t T, int64_t C) {
+  int64_t n;
+  if (!dims_ok({B, T, C}, &n) || n == 0) return 0;
+  rwkv::Wkv4Plan plan;
+  if (!rwkv::wkv4_plan(B, T, C, &plan)) return 0;
+  return plan.ws_bytes;
+}
+
+RWKV_API int rwkv_wkv4_forward(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                               const float* k, const float* v, float* y, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  int64_t n;
+  if (!dims_ok({B, T, C}, &n)) return RWKV_ERR_SHAPE;
+  if (n == 0) return RWKV_OK;
+  if (!w || !u || !k || !v || !y) return RWKV_ERR_NULLPTR;
+  if (!aligned16(w) || !aligned16(u) || !aligned16(k) || !aligned16(v) || !aligned16(y))
+    return RWKV_ERR_ALIGN;
+  rwkv::Wkv4Plan plan;
+  if (!rwkv::wkv4_plan(B, T, C, &plan)) return RWKV_ERR_UNSUPPORTED;
+  if (plan.ws_bytes > 0) {
+    if (!ws || ws_bytes < plan.ws_bytes) return RWKV_ERR_WORKSPACE;
+    if (!aligned16(ws)) return RWKV_ERR_ALIGN;
+  }
+  return hip_status(rwkv::wkv4_forward_launch(plan, B, T, C, w, u, k, v, y, ws, stream));
+}
+
+RWKV_API int rwkv_wkv4_state_init(int64_t B, int64_t C, float* a, float* b, float* p,
+                                  hipStream_t stream) {
+  int64_t n;
+  if (!dims_ok({B, C}, &n)) return RWKV_ERR_SHAPE;
+  if (n == 0) return RWKV_OK;
+  if (!a || !b || !p) return RWKV_ERR_NULLPTR;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(p)) return RWKV_ERR_ALIGN;
+  return hip_status(rwkv::wkv4_state_init_launch(B, C, a, b, p, stream));
+}
+
+RWKV_API int rwkv_wkv4_step(int64_t B, int64_t C, float* a, float* b, float* p, const float* w,
+                            const float* u, const float* k, const float* v, float* y,
+                            hipStream_t stream) {
+  int64_t n;
+  if (!dims_ok({B, C}, &n)) return RWKV_ERR_SHAPE;
+  if (n == 0) return RWKV_OK;
+  if (!a || !b || !p || !w || !u || !k || !v || !y) return RWKV_ERR_NULLPTR;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(p) || !aligned16(w) || !aligned16(u) ||
+      !aligned16(k) || !aligned16(v) || !aligned16(y))
+    return RWKV_ERR_ALIGN;
+  if (C >= (int64_t(1) << 31) || B >= (int64_t(1) << 31)) return RWKV_ERR_UNSUPPORTED;
+  return hip_status(rwkv::wkv4_step_launch(B, C, a, b, p, w, u, k, v, y, stream));
+}
+
+// ------------------------------------------------------------------- Eagle
+
+RWKV_API size_t rwkv_wkv5_forward_workspace(int64_t B, int64_t T, int64_t H, int64_t D) {
+  int64_t n;
+  if (!dims_ok({B, T, H, D}, &n) || n == 0 || D != 64) return 0;
+  return rwkv::wkv5_workspace_bytes(B, T, H, D);
+}
+
+RWKV_API int rwkv_wkv5_forward(int64_t B, int64_t T, int64_t H, int64_t D, const uint16_t* r,
+                               const uint16_t* k, const uint16_t* v, const float* w,
+                               const float* u, float* o, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  int64_t n;
+  if (!dims_ok({B, T, H, D}, &n)) return RWKV_ERR_SHAPE;
+  if (n == 0) return RWKV_OK;
+  if (D != 64) return RWKV_ERR_UNSUPPORTED;
+  if (T >= (int64_t(1) << 31) || B * H >= (int64_t(1) << 31)) return RWKV_ERR_UNSUPPORTED;
+  if (!r || !k || !v || !w || !u || !o) return RWKV_ERR_NULLPTR;
+  if (!aligned16(r) || !aligned16(k) || !aligned16(v) || !aligned16(w) || !aligned16(u) ||
+      !aligned16(o))
+    return RWKV_ERR_ALIGN;
+  const size_t need = rwkv::wkv5_workspace_bytes(B, T, H, D);
+  if (need > 0) {
+    if (!ws || ws_bytes < need) return RWKV_ERR_WORKSPACE;
+    if (!aligned16(ws)) return RWKV_ERR_ALIGN;
+  }
+  return hip_status(rwkv::wkv5_forward_launch(B, T, H, D, r, k, v, w, u, o, ws, stream));
+}

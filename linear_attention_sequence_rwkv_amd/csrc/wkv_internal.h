@@ -1,0 +1,52 @@
+// Host-side declarations shared between the C ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rwkv {
+
+// ----- RWKV-4 forward: single-pass tiled scan with decoupled look-back -----
+//
+// A tile is L tokens x 64 channels per wave, NW waves per workgroup stacked
+// along time, so a workgroup covers TILE = L * NW tokens of one 64-channel
+// block.  Workspace = header + per (tile, channel block) two published
+// histories (aggregate, inclusive), 3 tagged 64-bit words per lane each.
+struct Wkv4Plan {
+  int L;         // tokens per wave
+  int NW;        // waves per workgroup
+  int64_t tile;  // L * NW
+  int64_t n_tiles;
+  int64_t n_cblk;  // ceil(C / 64)
+  int64_t groups;  // B * n_cblk
+  size_t ws_bytes;
+};
+
+constexpr size_t kWkv4HeaderBytes = 256;
+constexpr int kWkv4SlotWords = 6;  // aggregate (A, B, p) then inclusive (A, B, p)
+
+// Plan for a shape; honours RWKV_WKV4_TILE="L,NW" for tests and sweeps.
+// Returns false if the shape cannot be planned (too large for 32-bit tickets).
+bool wkv4_plan(int64_t B, int64_t T, int64_t C, Wkv4Plan* plan);
+
+hipError_t wkv4_forward_launch(const Wkv4Plan& plan, int64_t B, int64_t T, int64_t C,
+                               const float* w, const float* u, const float* k,
+                               const float* v, float* y, void* ws, hipStream_t stream);
+
+hipError_t wkv4_state_init_launch(int64_t B, int64_t C, float* a, float* b, float* p,
+                                  hipStream_t stream);
+
+hipError_t wkv4_step_launch(int64_t B, int64_t C, float* a, float* b, float* p,
+                            const float* w, const float* u, const float* k,
+                            const float* v, float* y, hipStream_t stream);
+
+// ----- Eagle (RWKV-5) forward -----
+size_t wkv5_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t D);
+
+hipError_t wkv5_forward_launch(int64_t B, int64_t T, int64_t H, int64_t D,
+                               const uint16_t* r, const uint16_t* k, const uint16_t* v,
+                               const float* w, const float* u, float* o, void* ws,
+                               hipStream_t stream);
+
+}  // namespace rwkv

@@ -1,0 +1,147 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments with the documented status before
+any HIP call.
+
+Every call here is built to fail validation (or to be a zero-size no-op), so
+no kernel is ever launched.  The fake device pointers are never dereferenced.
+On a host with a GPU this module is skipped anyway: a validation bug there
+would otherwise launch a kernel on fake pointers.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_sequence_rwkv_amd as rw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER_DIR = os.path.join(ROOT, "include")
+
+OK, NULLPTR, SHAPE, UNSUPPORTED, WORKSPACE, ALIGN, HIP = 0, -1, -2, -3, -4, -5, -6
+
+
+def _declared_functions():
+    names = set()
+    for fn in os.listdir(HEADER_DIR):
+        if fn.endswith(".h"):
+            text = open(os.path.join(HEADER_DIR, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(rwkv_\w+)\s*\(", text))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rw.LIB_PATH):
+        pytest.fail("librwkv_wkv.so is not built (run __graft_entry__.build())")
+    return rw.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    assert names == sorted([
+        "rwkv_abi_version", "rwkv_status_str", "rwkv_last_hip_error",
+        "rwkv_wkv4_forward_workspace", "rwkv_wkv4_forward", "rwkv_wkv4_state_init",
+        "rwkv_wkv4_step", "rwkv_wkv5_forward_workspace", "rwkv_wkv5_forward",
+    ])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert name in rw._SIGNATURES, name
+
+
+def test_exports_nothing_else(lib):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", rw.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert {n for n in exported if n.startswith("rwkv_")} == set(_declared_functions())
+
+
+def test_version_and_status_strings(lib):
+    assert lib.rwkv_abi_version() == 1
+    for s in (OK, NULLPTR, SHAPE, UNSUPPORTED, WORKSPACE, ALIGN, HIP):
+        assert lib.rwkv_status_str(s)
+    assert lib.rwkv_status_str(12345) == b"unknown status"
+    assert lib.rwkv_last_hip_error() == 0
+
+
+def _skip_if_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("error-path checks run on hosts without a GPU only")
+
+
+FAKE = ctypes.c_void_p(0x10000)       # aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p(0x10004)
+NULL = ctypes.c_void_p(0)
+
+
+def test_wkv4_forward_rejections(lib):
+    _skip_if_gpu()
+    f = lib.rwkv_wkv4_forward
+    need = lib.rwkv_wkv4_forward_workspace(8, 1024, 768)
+    assert need > 0
+    args = lambda **kw: [kw.get(n, FAKE) for n in ("w", "u", "k", "v", "y")]  # noqa: E731
+    # zero sizes are a no-op even with NULL pointers
+    assert f(0, 1024, 768, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) == OK
+    assert f(8, 0, 768, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) == OK
+    assert f(8, 1024, 0, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) == OK
+    # negative and overflowing sizes
+    assert f(-1, 1024, 768, *args(), FAKE, need, NULL) == SHAPE
+    assert f(8, -5, 768, *args(), FAKE, need, NULL) == SHAPE
+    assert f(1 << 40, 1 << 20, 1 << 20, *args(), FAKE, need, NULL) == SHAPE
+    # each required pointer
+    for n in ("w", "u", "k", "v", "y"):
+        assert f(8, 1024, 768, *args(**{n: NULL}), FAKE, need, NULL) == NULLPTR, n
+        assert f(8, 1024, 768, *args(**{n: MISALIGNED}), FAKE, need, NULL) == ALIGN, n
+    # workspace
+    assert f(8, 1024, 768, *args(), NULL, need, NULL) == WORKSPACE
+    assert f(8, 1024, 768, *args(), FAKE, need - 1, NULL) == WORKSPACE
+    assert f(8, 1024, 768, *args(), MISALIGNED, need, NULL) == ALIGN
+    # too many tiles for 32-bit tickets
+    assert f(1 << 24, 1 << 20, 64, *args(), FAKE, 1 << 62, NULL) == UNSUPPORTED
+    assert lib.rwkv_last_hip_error() == 0
+
+
+def test_wkv4_workspace_sizes(lib):
+    assert lib.rwkv_wkv4_forward_workspace(0, 10, 10) == 0
+    assert lib.rwkv_wkv4_forward_workspace(-1, 10, 10) == 0
+    small = lib.rwkv_wkv4_forward_workspace(1, 64, 64)
+    big = lib.rwkv_wkv4_forward_workspace(1, 65536, 5120)
+    assert 0 < small < big
+    # grows with the number of tiles and channel blocks
+    assert lib.rwkv_wkv4_forward_workspace(2, 65536, 5120) > big
+
+
+def test_wkv4_step_and_init_rejections(lib):
+    _skip_if_gpu()
+    s = lib.rwkv_wkv4_step
+    ptrs = lambda **kw: [kw.get(n, FAKE) for n in "a b p w u k v y".split()]  # noqa: E731
+    assert s(0, 4096, *[NULL] * 8, NULL) == OK
+    assert s(-2, 4096, *ptrs(), NULL) == SHAPE
+    for n in "a b p w u k v y".split():
+        assert s(256, 4096, *ptrs(**{n: NULL}), NULL) == NULLPTR, n
+        assert s(256, 4096, *ptrs(**{n: MISALIGNED}), NULL) == ALIGN, n
+    i = lib.rwkv_wkv4_state_init
+    assert i(0, 4, NULL, NULL, NULL, NULL) == OK
+    assert i(4, -4, FAKE, FAKE, FAKE, NULL) == SHAPE
+    assert i(4, 4, FAKE, NULL, FAKE, NULL) == NULLPTR
+    assert i(4, 4, FAKE, FAKE, MISALIGNED, NULL) == ALIGN
+
+
+def test_wkv5_rejections(lib):
+    _skip_if_gpu()
+    f = lib.rwkv_wkv5_forward
+    ptrs = lambda **kw: [kw.get(n, FAKE) for n in "r k v w u o".split()]  # noqa: E731
+    need = lib.rwkv_wkv5_forward_workspace(4, 4096, 32, 64)
+    assert f(0, 4096, 32, 64, *[NULL] * 6, NULL, 0, NULL) == OK
+    assert f(4, 4096, 32, 32, *ptrs(), FAKE, need, NULL) == UNSUPPORTED
+    assert f(4, -1, 32, 64, *ptrs(), FAKE, need, NULL) == SHAPE
+    for n in "r k v w u o".split():
+        assert f(4, 4096, 32, 64, *ptrs(**{n: NULL}), FAKE, need, NULL) == NULLPTR, n
+        assert f(4, 4096, 32, 64, *ptrs(**{n: MISALIGNED}), FAKE, need, NULL) == ALIGN, n
+    assert lib.rwkv_wkv5_forward_workspace(4, 4096, 32, 32) == 0

@@ -1,0 +1,232 @@
+"""GPU parity of the RWKV-4 entry points against the fp64 oracle.
+
+Tolerance (floating point): max |y_gpu - y_oracle| / S <= 1e-4, where S is
+the oracle's weighted mean of |v| with the same weights (S >= |y|): the
+condition scale of a convex combination.  Index-only properties (first
+token, identity map, shift map) are checked bit for bit.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import linear_attention_sequence_rwkv_amd as rw
+import oracle.wkv_oracle as O
+import synth
+from wkv_testutil import WKV4_TOL, log, to_dev, torch_dev, wkv4_scaled_err
+
+pytestmark = pytest.mark.gpu
+
+TILE_VARIANTS = ["64,4", "64,1", "32,4", "32,8", "16,4", "64,2", "16,1"]
+
+
+def gpu_forward(inp, tile=None):
+    torch, _ = torch_dev()
+    old = os.environ.get("RWKV_WKV4_TILE")
+    if tile is not None:
+        os.environ["RWKV_WKV4_TILE"] = tile
+    try:
+        y = rw.rwkv_wkv4_forward(to_dev(inp["w"]), to_dev(inp["u"]), to_dev(inp["k"]),
+                                 to_dev(inp["v"]))
+        torch.cuda.synchronize()
+    finally:
+        if tile is not None:
+            if old is None:
+                del os.environ["RWKV_WKV4_TILE"]
+            else:
+                os.environ["RWKV_WKV4_TILE"] = old
+    return y.cpu().numpy()
+
+
+def oracle_forward(inp, channels=None):
+    w, u, k, v = inp["w"], inp["u"], inp["k"], inp["v"]
+    if channels is not None:
+        w, u, k, v = w[channels], u[channels], k[..., channels], v[..., channels]
+    y, _ = O.wkv4_recurrent(w, u, k, v)
+    S = O.wkv4_scale(w, u, k, v)
+    return y, S
+
+
+def test_tiny_workload_matches_direct_sum():
+    cfg = synth.CFG_WKV4_TINY
+    log(f"wkv4_forward {cfg.name} seed={cfg.seed}")
+    inp = synth.wkv4_inputs_for(cfg)
+    y = gpu_forward(inp)
+    yd = O.wkv4_direct(inp["w"], inp["u"], inp["k"], inp["v"])
+    S = O.wkv4_scale(inp["w"], inp["u"], inp["k"], inp["v"])
+    err = wkv4_scaled_err(y, yd, S)
+    log(f"  err={err:.3e}")
+    assert err <= WKV4_TOL
+    assert np.array_equal(y[:, 0, :], inp["v"][:, 0, :])
+
+
+@pytest.mark.parametrize("tile", TILE_VARIANTS)
+@pytest.mark.parametrize("shape", [(2, 1000, 200), (1, 777, 64), (3, 64, 65), (1, 1, 7),
+                                   (2, 2051, 130)])
+def test_ragged_shapes_all_tiles(shape, tile):
+    B, T, C = shape
+    log(f"wkv4_forward B={B} T={T} C={C} tile={tile}")
+    inp = synth.wkv4_inputs(B, T, C, seed=17 + T + C, omega_lo=-5.0, omega_hi=2.0,
+                            u_std=1.0, k_std=3.0)
+    y = gpu_forward(inp, tile)
+    y_ref, S = oracle_forward(inp)
+    err = wkv4_scaled_err(y, y_ref, S)
+    log(f"  err={err:.3e}")
+    assert err <= WKV4_TOL
+    assert np.array_equal(y[:, 0, :], inp["v"][:, 0, :])
+
+
+def test_169m_width_workload_full():
+    cfg = synth.CFG_WKV4_169M
+    log(f"wkv4_forward {cfg.name} seed={cfg.seed}")
+    inp = synth.wkv4_inputs_for(cfg)
+    y = gpu_forward(inp)
+    y_ref, S = oracle_forward(inp)
+    err = wkv4_scaled_err(y, y_ref, S)
+    log(f"  err={err:.3e}")
+    assert err <= WKV4_TOL
+
+
+def test_long_sequence_workload_sampled_channels():
+    """B=1 T=65536 C=5120 on the GPU; the oracle runs 320 of the channels
+    (every 16th, plus the last) over the full sequence."""
+    cfg = synth.CFG_WKV4_LONG
+    log(f"wkv4_forward {cfg.name} seed={cfg.seed} (oracle on sampled channels)")
+    inp = synth.wkv4_inputs_for(cfg)
+    y = gpu_forward(inp)
+    ch = np.unique(np.concatenate([np.arange(0, cfg.C, 16), [cfg.C - 1]]))
+    y_ref, S = oracle_forward(inp, ch)
+    err = wkv4_scaled_err(y[..., ch], y_ref, S)
+    log(f"  err={err:.3e} over {len(ch)} channels")
+    assert err <= WKV4_TOL
+    assert np.all(np.isfinite(y))
+
+
+def test_identity_and_shift_maps_bit_exact():
+    """u=+100: the current token dominates, y == v.  w=100, u=-100: only the
+    previous token survives, y[t] == v[t-1].  Holds across tile boundaries."""
+    B, T, C = 2, 1500, 192
+    inp = synth.wkv4_inputs(B, T, C, seed=99)
+    for tile in ("64,4", "16,4"):
+        log(f"wkv4_forward identity/shift maps tile={tile}")
+        ident = dict(inp, u=np.full(C, 100.0, np.float32))
+        assert np.array_equal(gpu_forward(ident, tile), inp["v"])
+        shift = dict(inp, w=np.full(C, 100.0, np.float32), u=np.full(C, -100.0, np.float32))
+        y = gpu_forward(shift, tile)
+        assert np.array_equal(y[:, 0], inp["v"][:, 0])
+        assert np.array_equal(y[:, 1:], inp["v"][:, :-1])
+
+
+@pytest.mark.parametrize("shift", [-80.0, 80.0])
+def test_key_shift_stability(shift):
+    B, T, C = 1, 3000, 128
+    inp = synth.wkv4_inputs(B, T, C, seed=5, omega_lo=-5.0, omega_hi=2.0, u_std=1.0, k_std=3.0)
+    log(f"wkv4_forward key shift {shift}")
+    shifted = dict(inp, k=(inp["k"] + np.float32(shift)).astype(np.float32))
+    y = gpu_forward(shifted)
+    y_ref, S = oracle_forward(shifted)
+    assert wkv4_scaled_err(y, y_ref, S) <= WKV4_TOL
+
+
+def test_zero_decay_long_average():
+    B, T, C = 1, 20000, 64
+    inp = synth.wkv4_inputs(B, T, C, seed=6)
+    inp["w"] = np.zeros(C, np.float32)
+    log("wkv4_forward w=0")
+    y = gpu_forward(inp)
+    y_ref, S = oracle_forward(inp)
+    assert wkv4_scaled_err(y, y_ref, S) <= WKV4_TOL
+
+
+def test_workspace_reuse_across_shapes():
+    """The cached workspace keeps working across many calls and shapes."""
+    a = synth.wkv4_inputs(2, 900, 96, seed=1)
+    b = synth.wkv4_inputs(1, 5000, 300, seed=2)
+    ya_ref, Sa = oracle_forward(a)
+    yb_ref, Sb = oracle_forward(b)
+    log("wkv4_forward 40 alternating calls")
+    for i in range(20):
+        assert wkv4_scaled_err(gpu_forward(a), ya_ref, Sa) <= WKV4_TOL, i
+        assert wkv4_scaled_err(gpu_forward(b), yb_ref, Sb) <= WKV4_TOL, i
+
+
+# ------------------------------------------------------------------ step ---
+
+def _run_steps(inp, n_steps, pool=None):
+    torch, dev = torch_dev()
+    B, C = inp["k"].shape[-2:]
+    w, u = to_dev(inp["w"]), to_dev(inp["u"])
+    k_all, v_all = to_dev(inp["k"]), to_dev(inp["v"])
+    a, b, p = rw.rwkv_wkv4_state_init(B, C, device=dev)
+    ys = []
+    for t in range(n_steps):
+        i = t % pool if pool else t
+        ys.append(rw.rwkv_wkv4_step(a, b, p, w, u, k_all[i], v_all[i]))
+    torch.cuda.synchronize()
+    return torch.stack(ys).cpu().numpy(), (a.cpu().numpy(), b.cpu().numpy(), p.cpu().numpy())
+
+
+@pytest.mark.parametrize("C", [768, 771])
+def test_steps_match_oracle_and_forward(C):
+    B, N = 4, 300
+    fwd = synth.wkv4_inputs(B, N, C, seed=31)
+    log(f"wkv4_step B={B} C={C} x{N}")
+    step_inp = dict(fwd, k=np.ascontiguousarray(fwd["k"].transpose(1, 0, 2)),
+                    v=np.ascontiguousarray(fwd["v"].transpose(1, 0, 2)))
+    ys, (a, b, p) = _run_steps(step_inp, N)
+    ys = ys.transpose(1, 0, 2)  # -> [B, N, C]
+    y_ref, st = O.wkv4_recurrent(fwd["w"], fwd["u"], fwd["k"], fwd["v"])
+    S = O.wkv4_scale(fwd["w"], fwd["u"], fwd["k"], fwd["v"])
+    assert wkv4_scaled_err(ys, y_ref, S) <= WKV4_TOL
+    assert np.array_equal(ys[:, 0], fwd["v"][:, 0])
+    # step mode and the time-parallel forward agree
+    y_fwd = gpu_forward(fwd)
+    assert wkv4_scaled_err(ys, y_fwd.astype(np.float64), S) <= 2 * WKV4_TOL
+    # state: only a/b and log(b)+p are defined
+    mean_ref, logden_ref = O.wkv4_canonical_state(st)
+    a64, b64, p64 = (x.astype(np.float64) for x in (a, b, p))
+    Sv = np.abs(fwd["v"]).max(axis=1)
+    assert np.max(np.abs(a64 / b64 - mean_ref) / Sv) <= WKV4_TOL
+    assert np.max(np.abs(np.log(b64) + p64 - logden_ref)) <= 1e-4 * (1 + np.abs(logden_ref)).max()
+
+
+def test_state_init_is_empty():
+    torch, dev = torch_dev()
+    a, b, p = rw.rwkv_wkv4_state_init(3, 70, device=dev)
+    torch.cuda.synchronize()
+    assert torch.all(a == 0) and torch.all(b == 0)
+    assert torch.all(p == torch.tensor(-1e38, dtype=torch.float32, device=dev))
+
+
+def test_decode_workload_sampled_lanes():
+    """B=256 C=4096, 4096 steps from a pool of 64 token draws; the oracle
+    follows 512 sampled (stream, channel) lanes through all steps."""
+    torch, dev = torch_dev()
+    cfg = synth.CFG_WKV4_DECODE
+    log(f"wkv4_step {cfg.name} seed={cfg.seed}")
+    inp = synth.wkv4_step_inputs(cfg.B, cfg.C, cfg.pool, cfg.seed)
+    rng = np.random.default_rng(0)
+    lanes = np.sort(rng.choice(cfg.B * cfg.C, size=512, replace=False))
+    lanes_t = torch.from_numpy(lanes).to(dev)
+    w, u = to_dev(inp["w"]), to_dev(inp["u"])
+    k_all, v_all = to_dev(inp["k"]), to_dev(inp["v"])
+    a, b, p = rw.rwkv_wkv4_state_init(cfg.B, cfg.C, device=dev)
+    y = torch.empty((cfg.B, cfg.C), dtype=torch.float32, device=dev)
+    got = torch.empty((cfg.steps, len(lanes)), dtype=torch.float32, device=dev)
+    for t in range(cfg.steps):
+        i = t % cfg.pool
+        rw.rwkv_wkv4_step(a, b, p, w, u, k_all[i], v_all[i], y=y)
+        got[t] = y.view(-1)[lanes_t]
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    bi, ci = lanes // cfg.C, lanes % cfg.C
+    kk = inp["k"][:, bi, ci]          # [pool, L]
+    vv = inp["v"][:, bi, ci]
+    idx = np.arange(cfg.steps) % cfg.pool
+    k_seq = kk[idx][None]             # [1, steps, L]
+    v_seq = vv[idx][None]
+    y_ref, _ = O.wkv4_recurrent(inp["w"][ci], inp["u"][ci], k_seq, v_seq)
+    S = O.wkv4_scale(inp["w"][ci], inp["u"][ci], k_seq, v_seq)
+    err = wkv4_scaled_err(got[None], y_ref, S)
+    log(f"  err={err:.3e}")
+    assert err <= WKV4_TOL
