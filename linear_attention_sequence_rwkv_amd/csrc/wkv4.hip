@@ -51,7 +51,37 @@ __device__ __forceinline__ uint32_t hdr_add(uint32_t* h, int i, uint32_t x) {
 __device__ __forceinline__ void publish(uint64_t* slot, const Hist& h, uint32_t tag) {
   tagged_store(slot + 0 * 64, h.A, tag);
   tagged_store(slot + 1 * 64, h.Bd, tag);
-  tagged_store(slot + 2 * 64, h.p, tag);
+  tagged_store(slot + 2 * 64, h.kr, tag);
+  tagged_store(slot + 3 * 64, h.n, tag);
+}
+
+// History of `n` tokens (n <= L) from an empty start, evaluated after the
+// last one, by a fixed reference instead of a running maximum: token s has
+// log2-weight m_s = k2_s - (n-1-s) w2; with P = max_s m_s every term is
+// 2^(m_s - P) <= 1 and the largest is exactly 1, so nothing overflows and the
+// sum never underflows to 0.  Costs one exp2 per token and no selects.
+template <int L>
+__device__ __forceinline__ Hist summarize(const float (&kk)[L], const float (&vv)[L], int n,
+                                          float w2) {
+  // Decay steps from token s to the evaluation point (padding: none, and the
+  // padding exponent is pushed far below the maximum).
+  auto expo = [&](int s) {
+    const bool full = n == L;
+    const float back = full ? float(L - 1 - s) : float(n - 1 - s);
+    const float m = fmaf(-back, w2, kk[s]);
+    return (full || s < n) ? m : kEmptyP;
+  };
+  float P = kEmptyP;
+#pragma unroll
+  for (int s = 0; s < L; ++s) P = fmaxf(P, expo(s));
+  float A = 0.f, Bd = 0.f;
+#pragma unroll
+  for (int s = 0; s < L; ++s) {
+    const float e = exp2_fast(expo(s) - P);  // exactly 0 for the padding tokens
+    A = fmaf(e, vv[s], A);
+    Bd += e;
+  }
+  return n > 0 ? Hist{A, Bd, P, 0.f} : hist_empty();
 }
 
 template <int L, int NW>
@@ -61,21 +91,22 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
     const float* __restrict__ k, const float* __restrict__ v, float* __restrict__ y,
     uint32_t* __restrict__ hdr, uint64_t* __restrict__ slots) {
   constexpr int TILE = L * NW;
+  constexpr int SLOT = kWkv4SlotWords * 64;  // words per (tile, channel block)
   __shared__ int s_ticket;
   __shared__ uint32_t s_tag;
-  __shared__ float s_sum[NW][3][64];
-  __shared__ float s_pre[3][64];
+  __shared__ float s_sum[NW][4][64];
+  __shared__ float s_pre[4][64];
 
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t total = uint32_t(n_tiles) * uint32_t(groups);
   if (threadIdx.x == 0) {
     s_tag = hdr_load(hdr, kHdrEpoch) + 1u;
     s_ticket = int(hdr_add(hdr, kHdrTicket, 1u));
   }
   __syncthreads();
-  const int ticket = s_ticket;
-  const uint32_t tag = s_tag;
+  const int ticket = __builtin_amdgcn_readfirstlane(s_ticket);
+  const uint32_t tag = __builtin_amdgcn_readfirstlane(s_tag);
   // A workspace that was not zero-filled can hand out tickets past the grid;
   // flag it and touch nothing.
   if (uint32_t(ticket) >= total) {
@@ -96,83 +127,86 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
   const int tile_t0 = tile * TILE;
   const int t0 = tile_t0 + wid * L;
   const int n = max(0, min(L, T - t0));
-  const size_t base = (size_t(bi) * size_t(T) + size_t(t0)) * size_t(C) + size_t(cc);
-  const float* kp = k + base;
-  const float* vp = v + base;
+  // Wave-uniform row base; the lane adds only its channel.
+  const size_t row0 = (size_t(bi) * size_t(T) + size_t(t0)) * size_t(C) + size_t(cb) * 64;
+  const float* kp = k + row0;
+  const float* vp = v + row0;
+  const int lc = valid ? lane : (C - 1) - cb * 64;
 
   float kk[L], vv[L];
-  if (valid && n == L) {
+  if (n == L) {
 #pragma unroll
     for (int s = 0; s < L; ++s) {
-      kk[s] = kp[size_t(s) * C];
-      vv[s] = vp[size_t(s) * C];
+      kk[s] = kp[size_t(s) * C + lc];
+      vv[s] = vp[size_t(s) * C + lc];
     }
   } else {
 #pragma unroll
     for (int s = 0; s < L; ++s) {
-      const bool in = valid && s < n;
-      kk[s] = in ? kp[size_t(s) * C] : 0.f;
-      vv[s] = in ? vp[size_t(s) * C] : 0.f;
+      kk[s] = s < n ? kp[size_t(s) * C + lc] : 0.f;
+      vv[s] = s < n ? vp[size_t(s) * C + lc] : 0.f;
     }
   }
 #pragma unroll
   for (int s = 0; s < L; ++s) kk[s] *= kLog2e;
 
   // Pass 1: this wave's tokens from an empty history.
-  Hist h = hist_empty();
-#pragma unroll
-  for (int s = 0; s < L; ++s)
-    if (s < n) hist_push(h, kk[s], vv[s], w2);
-  s_sum[wid][0][lane] = h.A;
-  s_sum[wid][1][lane] = h.Bd;
-  s_sum[wid][2][lane] = h.p;
+  {
+    const Hist h = summarize<L>(kk, vv, n, w2);
+    s_sum[wid][0][lane] = h.A;
+    s_sum[wid][1][lane] = h.Bd;
+    s_sum[wid][2][lane] = h.kr;
+    s_sum[wid][3][lane] = h.n;
+  }
   __syncthreads();
 
   // Tile prefix: wave 0 publishes the aggregate and looks back.
   if (wid == 0) {
-    Hist agg = Hist{s_sum[0][0][lane], s_sum[0][1][lane], s_sum[0][2][lane]};
+    Hist agg = Hist{s_sum[0][0][lane], s_sum[0][1][lane], s_sum[0][2][lane], s_sum[0][3][lane]};
 #pragma unroll
     for (int i = 1; i < NW; ++i) {
       const int ni = max(0, min(L, T - (tile_t0 + i * L)));
-      agg = hist_concat(agg, Hist{s_sum[i][0][lane], s_sum[i][1][lane], s_sum[i][2][lane]},
-                        float(ni) * w2);
+      agg = hist_concat(agg, Hist{s_sum[i][0][lane], s_sum[i][1][lane], s_sum[i][2][lane],
+                                  s_sum[i][3][lane]},
+                        float(ni), w2);
     }
     const int tile_n = min(TILE, T - tile_t0);
-    uint64_t* mine = slots + (size_t(tile) * groups + g) * (kWkv4SlotWords * 64) + lane;
+    uint64_t* mine = slots + (size_t(tile) * groups + g) * SLOT + lane;
     Hist pre = hist_empty();
     if (tile == 0) {
-      publish(mine + 3 * 64, agg, tag);
+      publish(mine + 4 * 64, agg, tag);
     } else {
       publish(mine, agg, tag);
       Hist acc = hist_empty();  // tiles (pos, tile) folded so far
-      int acc_n = 0;
+      float acc_n = 0.f;
       int pos = tile - 1;
       uint32_t spins = 0;
       while (true) {
-        const uint64_t* sp = slots + (size_t(pos) * groups + g) * (kWkv4SlotWords * 64) + lane;
+        const uint64_t* sp = slots + (size_t(pos) * groups + g) * SLOT + lane;
         // One lane polls the first word of each history; the whole wave
         // reads the payload only once it is there.  0: nothing yet,
         // 1: aggregate, 2: inclusive.
         int state = 0;
         if (lane == 0) {
-          const uint64_t iw = tagged_load(sp + 3 * 64);
+          const uint64_t iw = tagged_load(sp + 4 * 64);
           const uint64_t aw = tagged_load(sp);
           state = tag_ok(iw, tag) ? 2 : ((pos > 0 && tag_ok(aw, tag)) ? 1 : 0);
         }
-        state = __shfl(state, 0);
+        state = __builtin_amdgcn_readfirstlane(__shfl(state, 0));
         if (state != 0) {
-          const uint64_t* q = sp + (state == 2 ? 3 * 64 : 0);
+          const uint64_t* q = sp + (state == 2 ? 4 * 64 : 0);
           const uint64_t x0 = tagged_load(q);
           const uint64_t x1 = tagged_load(q + 64);
           const uint64_t x2 = tagged_load(q + 128);
-          if (__all(tag_ok(x0, tag) && tag_ok(x1, tag) && tag_ok(x2, tag))) {
-            const Hist hx = Hist{tag_val(x0), tag_val(x1), tag_val(x2)};
-            acc = hist_concat(hx, acc, float(acc_n) * w2);
+          const uint64_t x3 = tagged_load(q + 192);
+          if (__all(tag_ok(x0, tag) && tag_ok(x1, tag) && tag_ok(x2, tag) && tag_ok(x3, tag))) {
+            const Hist hx = Hist{tag_val(x0), tag_val(x1), tag_val(x2), tag_val(x3)};
+            acc = hist_concat(hx, acc, acc_n, w2);
             if (state == 2) {
               pre = acc;
               break;
             }
-            acc_n += TILE;
+            acc_n += float(TILE);
             --pos;
             continue;
           }
@@ -182,38 +216,40 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
             __hip_atomic_fetch_or(hdr + kHdrError, 1u, __ATOMIC_RELAXED,
                                   __HIP_MEMORY_SCOPE_AGENT);
           const float nan = __builtin_nanf("");
-          pre = Hist{nan, nan, nan};
+          pre = Hist{nan, nan, nan, 0.f};
           break;
         }
         __builtin_amdgcn_s_sleep(1);
       }
-      publish(mine + 3 * 64, hist_concat(pre, agg, float(tile_n) * w2), tag);
+      publish(mine + 4 * 64, hist_concat(pre, agg, float(tile_n), w2), tag);
     }
     s_pre[0][lane] = pre.A;
     s_pre[1][lane] = pre.Bd;
-    s_pre[2][lane] = pre.p;
+    s_pre[2][lane] = pre.kr;
+    s_pre[3][lane] = pre.n;
   }
   __syncthreads();
 
   // Pass 2: start from the tile prefix plus the earlier waves, emit y.
   if (n > 0) {
-    Hist hs = Hist{s_pre[0][lane], s_pre[1][lane], s_pre[2][lane]};
-    const float lw2 = float(L) * w2;
+    Hist hs = Hist{s_pre[0][lane], s_pre[1][lane], s_pre[2][lane], s_pre[3][lane]};
     for (int i = 0; i < wid; ++i)
-      hs = hist_concat(hs, Hist{s_sum[i][0][lane], s_sum[i][1][lane], s_sum[i][2][lane]}, lw2);
-    float* yp = y + base;
-    if (valid && n == L) {
+      hs = hist_concat(hs, Hist{s_sum[i][0][lane], s_sum[i][1][lane], s_sum[i][2][lane],
+                                s_sum[i][3][lane]},
+                       float(L), w2);
+    float* yp = y + row0;
+    if (n == L) {
 #pragma unroll
       for (int s = 0; s < L; ++s) {
-        yp[size_t(s) * C] = hist_read(hs, kk[s], vv[s], u2);
-        hist_push(hs, kk[s], vv[s], w2);
+        const float ys = hist_read_push(hs, kk[s], vv[s], u2, w2);
+        if (valid) yp[size_t(s) * C + lane] = ys;
       }
-    } else if (valid) {
+    } else {
 #pragma unroll
       for (int s = 0; s < L; ++s) {
         if (s < n) {
-          yp[size_t(s) * C] = hist_read(hs, kk[s], vv[s], u2);
-          hist_push(hs, kk[s], vv[s], w2);
+          const float ys = hist_read_push(hs, kk[s], vv[s], u2, w2);
+          if (valid) yp[size_t(s) * C + lane] = ys;
         }
       }
     }
@@ -234,13 +270,12 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
 // elementwise, 36 bytes of traffic per element.
 __device__ __forceinline__ void step_one(float& a, float& b, float& p, float w, float u,
                                          float k, float v, float& y) {
-  Hist h{a, b, p * kLog2e};
-  const float k2 = k * kLog2e;
-  y = hist_read(h, k2, v, u * kLog2e);
-  hist_push(h, k2, v, w * kLog2e);
+  const float w2 = w * kLog2e;
+  Hist h{a, b, p * kLog2e, 0.f};
+  y = hist_read_push(h, k * kLog2e, v, u * kLog2e, w2);
   a = h.A;
   b = h.Bd;
-  p = h.p * kLn2;
+  p = hist_p(h, w2) * kLn2;
 }
 
 __global__ __launch_bounds__(256) void wkv4_step_vec4(
@@ -316,8 +351,13 @@ hipError_t launch_tiled(const Wkv4Plan& pl, int64_t T, int64_t C, const float* w
 }  // namespace
 
 bool wkv4_plan(int64_t B, int64_t T, int64_t C, Wkv4Plan* plan) {
-  int L = 64, NW = 4;
-  if (T <= 64) NW = 1;
+  // 32 tokens per wave keeps k, v and the history in about 100 VGPRs
+  // (4 waves per SIMD); 8 waves stack a 256-token tile.
+  int L = 32, NW = 8;
+  if (T <= 64) {
+    L = 64;
+    NW = 1;
+  }
   if (const char* env = getenv("RWKV_WKV4_TILE")) {
     int l = 0, nw = 0;
     if (sscanf(env, "%d,%d", &l, &nw) == 2) {

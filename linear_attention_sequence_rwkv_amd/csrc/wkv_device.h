@@ -18,58 +18,63 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // ---------------------------------------------------------------------------
-// RWKV-4 state arithmetic in the base-2 domain.
+// RWKV-4 history arithmetic in the base-2 domain.
 //
-// A lane's history is (A, Bd, p): numerator and denominator sums scaled by
-// 2^p, with k, w, u pre-multiplied by log2(e).  Each update keeps the larger
-// of the two exponents as the new scale, so one of the two terms is taken at
-// factor 1 and a single exp2 of a non-positive number is needed.
+// A lane's history is (A, Bd): the numerator and denominator sums are A * 2^p
+// and Bd * 2^p, with k, w, u pre-multiplied by log2(e).  The scale is carried as an
+// anchor: p = kr - n * w2, where kr is a (pre-scaled) key and n an integer
+// count of decay steps since it.  Every comparison of two scales is formed
+// as fma(-(n_a - n_b), w2, kr_a - kr_b), which rounds once at the size of the
+// difference and never accumulates rounding along the sequence: a plain
+// running p -= w2 would drift by ulp(|p|) per token.
+//
+// Each update keeps the larger of the two scales at factor 1, so a single
+// exp2 of a non-positive number is needed.  Exact integers up to 2^24 are
+// held in the float n.
 // ---------------------------------------------------------------------------
 struct Hist {
-  float A, Bd, p;
+  float A, Bd, kr, n;
 };
 
-__device__ __forceinline__ Hist hist_empty() { return Hist{0.f, 0.f, kEmptyP}; }
+__device__ __forceinline__ Hist hist_empty() { return Hist{0.f, 0.f, kEmptyP, 0.f}; }
 
-// Advance the history by one token: decay by 2^-w2, add 2^k2 * (v, 1).
-__device__ __forceinline__ void hist_push(Hist& h, float k2, float v, float w2) {
-  const float pd = h.p - w2;
-  const float d = pd - k2;
-  const float e = exp2_fast(-fabsf(d));
-  const bool keep = d >= 0.f;  // history dominates: it stays at factor 1
-  const float a_one = keep ? h.A : v;
-  const float a_scl = keep ? v : h.A;
-  const float b_one = keep ? h.Bd : 1.f;
-  const float b_scl = keep ? 1.f : h.Bd;
-  h.A = fmaf(e, a_scl, a_one);
-  h.Bd = fmaf(e, b_scl, b_one);
-  h.p = keep ? pd : k2;
-}
+// Scale of the history as a plain exponent (for the recurrent-state ABI).
+__device__ __forceinline__ float hist_p(const Hist& h, float w2) { return fmaf(-h.n, w2, h.kr); }
 
-// Output for the current token: (history + 2^(u2+k2) v) / (history + 2^(u2+k2)).
-__device__ __forceinline__ float hist_read(const Hist& h, float k2, float v, float u2) {
-  const float cur = u2 + k2;
-  const float d = h.p - cur;
-  const float e = exp2_fast(-fabsf(d));
-  const bool keep = d >= 0.f;
-  const float num = keep ? fmaf(e, v, h.A) : fmaf(e, h.A, v);
-  const float den = keep ? (h.Bd + e) : fmaf(e, h.Bd, 1.f);
-  return num * rcp_fast(den);
+// Output for the current token, (history + 2^(u2+k2) v) / (history + 2^(u2+k2)),
+// fused with advancing the history by that token (decay by 2^-w2, then add
+// 2^k2 * (v, 1)).  Both exponents share kr - k2.
+__device__ __forceinline__ float hist_read_push(Hist& h, float k2, float v, float u2, float w2) {
+  const float base = fmaf(-h.n, w2, h.kr - k2);  // p - k2
+  const float dr = base - u2;                     // p - (u2 + k2)
+  const float dp = base - w2;                     // (p - w2) - k2
+  const float er = exp2_fast(-fabsf(dr));
+  const float ep = exp2_fast(-fabsf(dp));
+  const bool kr_keep = dr >= 0.f;
+  const float num = kr_keep ? fmaf(er, v, h.A) : fmaf(er, h.A, v);
+  const float den = kr_keep ? (h.Bd + er) : fmaf(er, h.Bd, 1.f);
+  const float y = num * rcp_fast(den);
+  const bool kp_keep = dp >= 0.f;
+  h.A = kp_keep ? fmaf(ep, v, h.A) : fmaf(ep, h.A, v);
+  h.Bd = kp_keep ? (h.Bd + ep) : fmaf(ep, h.Bd, 1.f);
+  h.kr = kp_keep ? h.kr : k2;
+  h.n = kp_keep ? (h.n + 1.f) : 0.f;
+  return y;
 }
 
 // Concatenate histories: `x` covers an earlier stretch, `y` the `ny` tokens
-// right after it (y was accumulated from an empty history).  Decay and sum
-// are associative, so this is the combine step of the time scan.  ny * w2 is
-// one multiply, never a repeated subtraction.
-__device__ __forceinline__ Hist hist_concat(const Hist& x, const Hist& y, float ny_w2) {
-  const float px = x.p - ny_w2;
-  const float d = px - y.p;
+// right after it (y was accumulated from an empty history).  Decay-then-add
+// is associative, so this is the combine step of the time scan.
+__device__ __forceinline__ Hist hist_concat(const Hist& x, const Hist& y, float ny, float w2) {
+  const float nx = x.n + ny;
+  const float d = fmaf(-(nx - y.n), w2, x.kr - y.kr);  // scale of x minus scale of y
   const float e = exp2_fast(-fabsf(d));
   const bool keep = d >= 0.f;
   Hist r;
   r.A = keep ? fmaf(e, y.A, x.A) : fmaf(e, x.A, y.A);
   r.Bd = keep ? fmaf(e, y.Bd, x.Bd) : fmaf(e, x.Bd, y.Bd);
-  r.p = keep ? px : y.p;
+  r.kr = keep ? x.kr : y.kr;
+  r.n = keep ? nx : y.n;
   return r;
 }
 

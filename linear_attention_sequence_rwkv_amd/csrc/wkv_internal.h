@@ -12,7 +12,7 @@ namespace rwkv {
 // A tile is L tokens x 64 channels per wave, NW waves per workgroup stacked
 // along time, so a workgroup covers TILE = L * NW tokens of one 64-channel
 // block.  Workspace = header + per (tile, channel block) two published
-// histories (aggregate, inclusive), 3 tagged 64-bit words per lane each.
+// histories (aggregate, inclusive), 4 tagged 64-bit words per lane each.
 struct Wkv4Plan {
   int L;         // tokens per wave
   int NW;        // waves per workgroup
@@ -24,7 +24,7 @@ struct Wkv4Plan {
 };
 
 constexpr size_t kWkv4HeaderBytes = 256;
-constexpr int kWkv4SlotWords = 6;  // aggregate (A, B, p) then inclusive (A, B, p)
+constexpr int kWkv4SlotWords = 8;  // aggregate (A, B, kr, n) then inclusive (A, B, kr, n)
 
 // Plan for a shape; honours RWKV_WKV4_TILE="L,NW" for tests and sweeps.
 // Returns false if the shape cannot be planned (too large for 32-bit tickets).
