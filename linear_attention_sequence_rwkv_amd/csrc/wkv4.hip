@@ -8,67 +8,84 @@
 // form rests on the associativity of "decay then add" (same page, atomic
 // insight on the training/inference duality).
 //
-// Forward design (one launch, 12 bytes of HBM traffic per element):
-//   * a workgroup owns one 64-channel block of one sequence and a tile of
-//     L*NW tokens; each of its NW waves holds L tokens of k and v for its 64
-//     channels in registers (one lane per channel, loads coalesced along c);
+// Forward design (one launch, 12 bytes of HBM traffic per element plus a
+// few percent of workspace):
+//   * a channel block is 64*CPL channels of one sequence; each lane owns CPL
+//     adjacent channels and loads them with one vector load per token;
+//   * a workgroup owns one tile of one channel block: NW waves stacked along
+//     time, L tokens each, k and v held in registers;
 //   * each wave summarises its L tokens from an empty history; wave 0 joins
 //     the NW summaries into the tile aggregate and publishes it;
-//   * wave 0 then walks back over earlier tiles of the same channel block
-//     (decoupled look-back): an earlier tile's inclusive history ends the
-//     walk, its aggregate is folded in and the walk continues;
-//   * every wave rebuilds its own starting history from the tile prefix and
-//     the summaries of the waves before it, then rescans its tokens from
-//     registers and writes y.
-// Workgroups take tiles in ticket order, so every tile a workgroup waits on
-// belongs to a workgroup that is already running: the waits always end.
+//   * wave 0 then walks back over earlier tiles of the same block (decoupled
+//     look-back, 16 tiles polled per round trip): aggregates are folded in
+//     until an earlier tile's inclusive history ends the walk;
+//   * every wave rebuilds its starting history from the tile prefix and the
+//     summaries of the waves before it, rescans its tokens from registers and
+//     writes y.
+// Tiles of a channel block are claimed in order from that block's own
+// counter, so a workgroup only ever waits on workgroups that are already
+// running: every wait ends.  Every word the kernel writes to the workspace
+// carries the call's tag (unique and increasing per process), so nothing has
+// to be reset between calls, whatever shapes they have.
 #include "wkv_device.h"
 #include "wkv_internal.h"
 
-#include <stdlib.h>
 #include <stdio.h>
+#include <stdlib.h>
+
+#include <atomic>
 
 namespace rwkv {
 
 namespace {
 
-// Header words (uint32) at the start of the forward workspace.
-enum : int { kHdrTicket = 0, kHdrDone = 1, kHdrEpoch = 2, kHdrError = 3 };
-// Look-back polls before a workgroup gives up (about seconds); then it
-// raises the error word and writes NaN so that no wait can last forever.
+// Look-back polls without progress before a workgroup gives up (seconds);
+// it then raises the error word and writes NaN, so no wait lasts forever.
 constexpr uint32_t kSpinLimit = 1u << 24;
+// Earlier tiles polled per round trip by the look-back.
+constexpr int kWin = 16;
 
-__device__ __forceinline__ uint32_t hdr_load(uint32_t* h, int i) {
-  return __hip_atomic_load(h + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void hdr_store(uint32_t* h, int i, uint32_t x) {
-  __hip_atomic_store(h + i, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t hdr_add(uint32_t* h, int i, uint32_t x) {
-  return __hip_atomic_fetch_add(h + i, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void raise_error(uint32_t* err, uint32_t bit) {
+  __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void publish(uint64_t* slot, const Hist& h, uint32_t tag) {
-  tagged_store(slot + 0 * 64, h.A, tag);
-  tagged_store(slot + 1 * 64, h.Bd, tag);
-  tagged_store(slot + 2 * 64, h.kr, tag);
-  tagged_store(slot + 3 * 64, h.n, tag);
+// CPL adjacent floats of one row, loaded/stored with a single vector access.
+template <int CPL>
+__device__ __forceinline__ void load_vec(const float* p, float (&x)[CPL]) {
+  if constexpr (CPL == 4) {
+    const float4 t = *reinterpret_cast<const float4*>(p);
+    x[0] = t.x; x[1] = t.y; x[2] = t.z; x[3] = t.w;
+  } else if constexpr (CPL == 2) {
+    const float2 t = *reinterpret_cast<const float2*>(p);
+    x[0] = t.x; x[1] = t.y;
+  } else {
+    x[0] = *p;
+  }
 }
 
-// History of `n` tokens (n <= L) from an empty start, evaluated after the
-// last one, by a fixed reference instead of a running maximum: token s has
-// log2-weight m_s = k2_s - (n-1-s) w2; with P = max_s m_s every term is
-// 2^(m_s - P) <= 1 and the largest is exactly 1, so nothing overflows and the
-// sum never underflows to 0.  Costs one exp2 per token and no selects.
-template <int L>
-__device__ __forceinline__ Hist summarize(const float (&kk)[L], const float (&vv)[L], int n,
-                                          float w2) {
-  // Decay steps from token s to the evaluation point (padding: none, and the
-  // padding exponent is pushed far below the maximum).
+template <int CPL>
+__device__ __forceinline__ void store_vec(float* p, const float (&x)[CPL]) {
+  if constexpr (CPL == 4) {
+    *reinterpret_cast<float4*>(p) = float4{x[0], x[1], x[2], x[3]};
+  } else if constexpr (CPL == 2) {
+    *reinterpret_cast<float2*>(p) = float2{x[0], x[1]};
+  } else {
+    *p = x[0];
+  }
+}
+
+// History of `n` tokens (n <= L) of one channel from an empty start,
+// evaluated after the last one, with a fixed reference instead of a running
+// maximum: token s has log2-weight m_s = k2_s - (n-1-s) w2; with
+// P = max_s m_s every term is 2^(m_s - P) <= 1 and the largest is exactly 1,
+// so nothing overflows and the sum never underflows to 0.
+template <int L, int CPL>
+__device__ __forceinline__ Hist summarize(const float (&kk)[L][CPL], const float (&vv)[L][CPL],
+                                          int c, int n, float w2) {
   auto expo = [&](int s) {
     const bool full = n == L;
     const float back = full ? float(L - 1 - s) : float(n - 1 - s);
-    const float m = fmaf(-back, w2, kk[s]);
+    const float m = fmaf(-back, w2, kk[s][c]);
     return (full || s < n) ? m : kEmptyP;
   };
   float P = kEmptyP;
@@ -77,191 +94,229 @@ __device__ __forceinline__ Hist summarize(const float (&kk)[L], const float (&vv
   float A = 0.f, Bd = 0.f;
 #pragma unroll
   for (int s = 0; s < L; ++s) {
-    const float e = exp2_fast(expo(s) - P);  // exactly 0 for the padding tokens
-    A = fmaf(e, vv[s], A);
+    const float e = exp2_fast(expo(s) - P);  // exactly 0 for padding tokens
+    A = fmaf(e, vv[s][c], A);
     Bd += e;
   }
   return n > 0 ? Hist{A, Bd, P, 0.f} : hist_empty();
 }
 
-template <int L, int NW>
+// Shared-memory copy of per-channel histories, [field][channel].
+template <int W>
+struct HistLds {
+  float f[4][W];
+  __device__ __forceinline__ Hist get(int ch) const {
+    return Hist{f[0][ch], f[1][ch], f[2][ch], f[3][ch]};
+  }
+  __device__ __forceinline__ void put(int ch, const Hist& h) {
+    f[0][ch] = h.A;
+    f[1][ch] = h.Bd;
+    f[2][ch] = h.kr;
+    f[3][ch] = h.n;
+  }
+};
+
+template <int CPL, int L, int NW>
 __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
-    int T, int C, int n_cblk, int groups, int n_tiles,
+    int T, int C, int n_cblk, int groups, int n_tiles, uint32_t tag,
     const float* __restrict__ w, const float* __restrict__ u,
     const float* __restrict__ k, const float* __restrict__ v, float* __restrict__ y,
-    uint32_t* __restrict__ hdr, uint64_t* __restrict__ slots) {
-  constexpr int TILE = L * NW;
-  constexpr int SLOT = kWkv4SlotWords * 64;  // words per (tile, channel block)
-  __shared__ int s_ticket;
-  __shared__ uint32_t s_tag;
-  __shared__ float s_sum[NW][4][64];
-  __shared__ float s_pre[4][64];
+    uint32_t* __restrict__ err, uint64_t* __restrict__ counters, uint64_t* __restrict__ slots) {
+  constexpr int W = 64 * CPL;        // channels per block
+  constexpr int TILE = L * NW;       // tokens per tile
+  constexpr int SLOT = 8 * W;        // words per (tile, block): agg A,B,kr,n then inc A,B,kr,n
+  __shared__ int s_tile;
+  __shared__ HistLds<W> s_sum[NW];
+  __shared__ HistLds<W> s_pre;
 
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t total = uint32_t(n_tiles) * uint32_t(groups);
+  const int g = int(blockIdx.x) % groups;
   if (threadIdx.x == 0) {
-    s_tag = hdr_load(hdr, kHdrEpoch) + 1u;
-    s_ticket = int(hdr_add(hdr, kHdrTicket, 1u));
+    // Claim the next tile of this block.  The counter word is {tag, count}:
+    // raising it to {tag, 0} first makes whatever an earlier call (of any
+    // shape) left there harmless, as every earlier tag is smaller.
+    uint64_t* ctr = counters + size_t(g) * (kWkv4CounterStride / sizeof(uint64_t));
+    __hip_atomic_fetch_max(ctr, uint64_t(tag) << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t old =
+        __hip_atomic_fetch_add(ctr, uint64_t(1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_tile = uint32_t(old >> 32) == tag ? int(uint32_t(old)) : -1;
   }
   __syncthreads();
-  const int ticket = __builtin_amdgcn_readfirstlane(s_ticket);
-  const uint32_t tag = __builtin_amdgcn_readfirstlane(s_tag);
-  // A workspace that was not zero-filled can hand out tickets past the grid;
-  // flag it and touch nothing.
-  if (uint32_t(ticket) >= total) {
-    if (threadIdx.x == 0)
-      __hip_atomic_fetch_or(hdr + kHdrError, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int tile = __builtin_amdgcn_readfirstlane(s_tile);
+  // Only a workspace that was never zero-filled can get here: flag it and
+  // touch nothing.
+  if (tile < 0 || tile >= n_tiles) {
+    if (threadIdx.x == 0) raise_error(err, 2u);
     return;
   }
-  const int tile = ticket / groups;
-  const int g = ticket - tile * groups;
   const int bi = g / n_cblk;
   const int cb = g - bi * n_cblk;
-  const int c = cb * 64 + lane;
-  const bool valid = c < C;
-  const int cc = valid ? c : C - 1;  // parameter reads stay in bounds
-  const float w2 = w[cc] * kLog2e;
-  const float u2 = u[cc] * kLog2e;
+  const int ch0 = lane * CPL;                 // first channel of this lane in the block
+  const bool valid = cb * W + ch0 < C;        // C % CPL == 0: all CPL valid or none
+  const int cl = valid ? ch0 : (C - cb * W - CPL);  // loads stay in bounds
+  float w2[CPL], u2[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    w2[c] = w[cb * W + cl + c] * kLog2e;
+    u2[c] = u[cb * W + cl + c] * kLog2e;
+  }
 
   const int tile_t0 = tile * TILE;
   const int t0 = tile_t0 + wid * L;
   const int n = max(0, min(L, T - t0));
-  // Wave-uniform row base; the lane adds only its channel.
-  const size_t row0 = (size_t(bi) * size_t(T) + size_t(t0)) * size_t(C) + size_t(cb) * 64;
-  const float* kp = k + row0;
-  const float* vp = v + row0;
-  const int lc = valid ? lane : (C - 1) - cb * 64;
+  const size_t row0 = (size_t(bi) * size_t(T) + size_t(t0)) * size_t(C) + size_t(cb) * W;
+  const float* kp = k + row0 + cl;
+  const float* vp = v + row0 + cl;
 
-  float kk[L], vv[L];
-  if (n == L) {
+  float kk[L][CPL], vv[L][CPL];
 #pragma unroll
-    for (int s = 0; s < L; ++s) {
-      kk[s] = kp[size_t(s) * C + lc];
-      vv[s] = vp[size_t(s) * C + lc];
-    }
-  } else {
+  for (int s = 0; s < L; ++s) {
+    if (n == L || s < n) {
+      load_vec<CPL>(kp + size_t(s) * C, kk[s]);
+      load_vec<CPL>(vp + size_t(s) * C, vv[s]);
+    } else {
 #pragma unroll
-    for (int s = 0; s < L; ++s) {
-      kk[s] = s < n ? kp[size_t(s) * C + lc] : 0.f;
-      vv[s] = s < n ? vp[size_t(s) * C + lc] : 0.f;
+      for (int c = 0; c < CPL; ++c) kk[s][c] = vv[s][c] = 0.f;
     }
   }
 #pragma unroll
-  for (int s = 0; s < L; ++s) kk[s] *= kLog2e;
+  for (int s = 0; s < L; ++s)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) kk[s][c] *= kLog2e;
 
   // Pass 1: this wave's tokens from an empty history.
-  {
-    const Hist h = summarize<L>(kk, vv, n, w2);
-    s_sum[wid][0][lane] = h.A;
-    s_sum[wid][1][lane] = h.Bd;
-    s_sum[wid][2][lane] = h.kr;
-    s_sum[wid][3][lane] = h.n;
-  }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) s_sum[wid].put(ch0 + c, summarize<L, CPL>(kk, vv, c, n, w2[c]));
   __syncthreads();
 
   // Tile prefix: wave 0 publishes the aggregate and looks back.
   if (wid == 0) {
-    Hist agg = Hist{s_sum[0][0][lane], s_sum[0][1][lane], s_sum[0][2][lane], s_sum[0][3][lane]};
-#pragma unroll
-    for (int i = 1; i < NW; ++i) {
-      const int ni = max(0, min(L, T - (tile_t0 + i * L)));
-      agg = hist_concat(agg, Hist{s_sum[i][0][lane], s_sum[i][1][lane], s_sum[i][2][lane],
-                                  s_sum[i][3][lane]},
-                        float(ni), w2);
-    }
     const int tile_n = min(TILE, T - tile_t0);
-    uint64_t* mine = slots + (size_t(tile) * groups + g) * SLOT + lane;
-    Hist pre = hist_empty();
+    uint64_t* mine = slots + (size_t(tile) * groups + g) * SLOT + ch0;
+    Hist agg[CPL], pre[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      agg[c] = s_sum[0].get(ch0 + c);
+      for (int i = 1; i < NW; ++i) {
+        const int ni = max(0, min(L, T - (tile_t0 + i * L)));
+        agg[c] = hist_concat(agg[c], s_sum[i].get(ch0 + c), float(ni), w2[c]);
+      }
+      pre[c] = hist_empty();
+    }
+    auto publish = [&](int kind, const Hist (&h)[CPL]) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        uint64_t* q = mine + kind * 4 * W + c;
+        tagged_store(q + 0 * W, h[c].A, tag);
+        tagged_store(q + 1 * W, h[c].Bd, tag);
+        tagged_store(q + 2 * W, h[c].kr, tag);
+        tagged_store(q + 3 * W, h[c].n, tag);
+      }
+    };
     if (tile == 0) {
-      publish(mine + 4 * 64, agg, tag);
+      publish(1, agg);
     } else {
-      publish(mine, agg, tag);
-      Hist acc = hist_empty();  // tiles (pos, tile) folded so far
-      float acc_n = 0.f;
-      int pos = tile - 1;
+      publish(0, agg);
+      Hist acc[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) acc[c] = hist_empty();
+      float acc_n = 0.f;   // tokens covered by acc: tiles (pos, tile)
+      int pos = tile - 1;  // nearest tile not folded yet
       uint32_t spins = 0;
-      while (true) {
-        const uint64_t* sp = slots + (size_t(pos) * groups + g) * SLOT + lane;
-        // One lane polls the first word of each history; the whole wave
-        // reads the payload only once it is there.  0: nothing yet,
-        // 1: aggregate, 2: inclusive.
-        int state = 0;
-        if (lane == 0) {
-          const uint64_t iw = tagged_load(sp + 4 * 64);
-          const uint64_t aw = tagged_load(sp);
-          state = tag_ok(iw, tag) ? 2 : ((pos > 0 && tag_ok(aw, tag)) ? 1 : 0);
+      bool found = false;
+      while (!found) {
+        // Poll kWin earlier tiles in one round trip: lane i reads the first
+        // word of tile (pos - i)'s inclusive and aggregate histories.
+        const int pi = pos - lane;
+        bool inc_ok = false, agg_ok = false;
+        if (lane < kWin && pi >= 0) {
+          const uint64_t* sp = slots + (size_t(pi) * groups + g) * SLOT;
+          inc_ok = tag_ok(tagged_load(sp + 4 * W), tag);
+          agg_ok = pi > 0 && tag_ok(tagged_load(sp), tag);  // tile 0 has no aggregate
         }
-        state = __builtin_amdgcn_readfirstlane(__shfl(state, 0));
-        if (state != 0) {
-          const uint64_t* q = sp + (state == 2 ? 4 * 64 : 0);
-          const uint64_t x0 = tagged_load(q);
-          const uint64_t x1 = tagged_load(q + 64);
-          const uint64_t x2 = tagged_load(q + 128);
-          const uint64_t x3 = tagged_load(q + 192);
-          if (__all(tag_ok(x0, tag) && tag_ok(x1, tag) && tag_ok(x2, tag) && tag_ok(x3, tag))) {
-            const Hist hx = Hist{tag_val(x0), tag_val(x1), tag_val(x2), tag_val(x3)};
-            acc = hist_concat(hx, acc, acc_n, w2);
-            if (state == 2) {
-              pre = acc;
-              break;
-            }
+        const uint64_t inc_mask = __ballot(inc_ok);
+        const uint64_t agg_mask = __ballot(agg_ok);
+        // Fold the run of aggregates from pos back to the nearest inclusive.
+        const int m = inc_mask ? int(__builtin_ctzll(inc_mask)) : kWin;
+        const int a = int(__builtin_ctzll(~agg_mask));  // bits >= kWin are 0
+        const int n_agg = min(a, m);
+        const bool take_inc = inc_mask != 0 && a >= m;
+        const int todo = n_agg + (take_inc ? 1 : 0);
+        int folded = 0;
+        for (int j = 0; j < todo; ++j) {
+          const bool is_inc = take_inc && j == n_agg;
+          const uint64_t* q =
+              slots + (size_t(pos - j) * groups + g) * SLOT + (is_inc ? 4 * W : 0) + ch0;
+          uint64_t x[CPL][4];
+#pragma unroll
+          for (int c = 0; c < CPL; ++c)
+#pragma unroll
+            for (int f = 0; f < 4; ++f) x[c][f] = tagged_load(q + f * W + c);
+          bool ok = true;
+#pragma unroll
+          for (int c = 0; c < CPL; ++c)
+#pragma unroll
+            for (int f = 0; f < 4; ++f) ok = ok && tag_ok(x[c][f], tag);
+          if (!__all(ok)) break;  // payload not visible on every lane yet: poll again
+#pragma unroll
+          for (int c = 0; c < CPL; ++c)
+            acc[c] = hist_concat(Hist{tag_val(x[c][0]), tag_val(x[c][1]), tag_val(x[c][2]),
+                                      tag_val(x[c][3])},
+                                 acc[c], acc_n, w2[c]);
+          if (is_inc) {
+            found = true;
+          } else {
             acc_n += float(TILE);
-            --pos;
-            continue;
+            ++folded;
           }
         }
-        if (++spins > kSpinLimit) {
-          if (lane == 0)
-            __hip_atomic_fetch_or(hdr + kHdrError, 1u, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-          const float nan = __builtin_nanf("");
-          pre = Hist{nan, nan, nan, 0.f};
-          break;
+        pos -= folded;
+        if (found) break;
+        if (folded == 0) {
+          if (++spins > kSpinLimit) {
+            if (lane == 0) raise_error(err, 1u);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+              const float nan = __builtin_nanf("");
+              acc[c] = Hist{nan, nan, nan, 0.f};
+            }
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
         }
-        __builtin_amdgcn_s_sleep(1);
       }
-      publish(mine + 4 * 64, hist_concat(pre, agg, float(tile_n), w2), tag);
+      Hist inc[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        pre[c] = acc[c];
+        inc[c] = hist_concat(pre[c], agg[c], float(tile_n), w2[c]);
+      }
+      publish(1, inc);
     }
-    s_pre[0][lane] = pre.A;
-    s_pre[1][lane] = pre.Bd;
-    s_pre[2][lane] = pre.kr;
-    s_pre[3][lane] = pre.n;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) s_pre.put(ch0 + c, pre[c]);
   }
   __syncthreads();
 
   // Pass 2: start from the tile prefix plus the earlier waves, emit y.
   if (n > 0) {
-    Hist hs = Hist{s_pre[0][lane], s_pre[1][lane], s_pre[2][lane], s_pre[3][lane]};
-    for (int i = 0; i < wid; ++i)
-      hs = hist_concat(hs, Hist{s_sum[i][0][lane], s_sum[i][1][lane], s_sum[i][2][lane],
-                                s_sum[i][3][lane]},
-                       float(L), w2);
-    float* yp = y + row0;
-    if (n == L) {
+    Hist hs[CPL];
 #pragma unroll
-      for (int s = 0; s < L; ++s) {
-        const float ys = hist_read_push(hs, kk[s], vv[s], u2, w2);
-        if (valid) yp[size_t(s) * C + lane] = ys;
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < L; ++s) {
-        if (s < n) {
-          const float ys = hist_read_push(hs, kk[s], vv[s], u2, w2);
-          if (valid) yp[size_t(s) * C + lane] = ys;
-        }
-      }
+    for (int c = 0; c < CPL; ++c) {
+      hs[c] = s_pre.get(ch0 + c);
+      for (int i = 0; i < wid; ++i)
+        hs[c] = hist_concat(hs[c], s_sum[i].get(ch0 + c), float(L), w2[c]);
     }
-  }
-
-  // The last workgroup to finish resets the counters for the next call.
-  if (threadIdx.x == 0) {
-    const uint32_t d = hdr_add(hdr, kHdrDone, 1u);
-    if (d == total - 1u) {
-      hdr_store(hdr, kHdrTicket, 0u);
-      hdr_store(hdr, kHdrDone, 0u);
-      hdr_store(hdr, kHdrEpoch, tag);
+    float* yp = y + row0 + cl;
+#pragma unroll
+    for (int s = 0; s < L; ++s) {
+      if (n == L || s < n) {
+        float ys[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) ys[c] = hist_read_push(hs[c], kk[s][c], vv[s][c], u2[c], w2[c]);
+        if (valid) store_vec<CPL>(yp + size_t(s) * C, ys);
+      }
     }
   }
 }
@@ -330,57 +385,78 @@ __global__ __launch_bounds__(256) void wkv4_state_fill(size_t n, float* __restri
 }
 
 struct Variant {
-  int L, NW;
+  int cpl, L, NW;
 };
-// Instantiated tile shapes (tokens per wave, waves per workgroup).
-constexpr Variant kVariants[] = {{64, 4}, {64, 1}, {32, 4}, {32, 8}, {16, 4}, {64, 2}, {16, 1}};
+// Instantiated tile shapes: channels per lane, tokens per wave, waves per
+// workgroup.
+constexpr Variant kVariants[] = {{4, 8, 8}, {4, 16, 4}, {4, 16, 8},
+                                 {2, 16, 8}, {2, 32, 4}, {2, 16, 4},
+                                 {1, 32, 8}, {1, 32, 4}, {1, 64, 1}, {1, 16, 4}};
 
-template <int L, int NW>
+// Launch tags: unique and increasing per call in this process, never 0 (the
+// tag of a zero-filled workspace word), so a word left by an earlier call can
+// never pass for one of this call.
+std::atomic<uint32_t> g_launch_tag{0};
+
+uint32_t next_tag() {
+  uint32_t t = g_launch_tag.fetch_add(1, std::memory_order_relaxed) + 1u;
+  if (t == 0) t = g_launch_tag.fetch_add(1, std::memory_order_relaxed) + 1u;
+  return t;
+}
+
+template <int CPL, int L, int NW>
 hipError_t launch_tiled(const Wkv4Plan& pl, int64_t T, int64_t C, const float* w,
                         const float* u, const float* k, const float* v, float* y, void* ws,
                         hipStream_t stream) {
-  uint32_t* hdr = static_cast<uint32_t*>(ws);
-  uint64_t* slots = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + kWkv4HeaderBytes);
+  char* base = static_cast<char*>(ws);
+  uint32_t* err = reinterpret_cast<uint32_t*>(base);
+  uint64_t* counters = reinterpret_cast<uint64_t*>(base + kWkv4HeaderBytes);
+  uint64_t* slots = reinterpret_cast<uint64_t*>(base + pl.slots_offset);
   const unsigned grid = unsigned(pl.n_tiles * pl.groups);
-  hipLaunchKernelGGL((wkv4_fwd_tiled<L, NW>), dim3(grid), dim3(64 * NW), 0, stream, int(T),
-                     int(C), int(pl.n_cblk), int(pl.groups), int(pl.n_tiles), w, u, k, v, y,
-                     hdr, slots);
+  hipLaunchKernelGGL((wkv4_fwd_tiled<CPL, L, NW>), dim3(grid), dim3(64 * NW), 0, stream,
+                     int(T), int(C), int(pl.n_cblk), int(pl.groups), int(pl.n_tiles),
+                     next_tag(), w, u, k, v, y, err, counters, slots);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool wkv4_plan(int64_t B, int64_t T, int64_t C, Wkv4Plan* plan) {
-  // 32 tokens per wave keeps k, v and the history in about 100 VGPRs
-  // (4 waves per SIMD); 8 waves stack a 256-token tile.
-  int L = 32, NW = 8;
+  // One channel per lane, 32 tokens per wave, 4 waves per tile: about 100
+  // VGPRs (4 waves per SIMD).  Measured faster than wider vector loads with
+  // several channels per lane, which lengthen each lane's serial scan.
+  int cpl = 1, L = 32, NW = 4;
   if (T <= 64) {
     L = 64;
     NW = 1;
   }
   if (const char* env = getenv("RWKV_WKV4_TILE")) {
-    int l = 0, nw = 0;
-    if (sscanf(env, "%d,%d", &l, &nw) == 2) {
+    int c = 0, l = 0, nw = 0;
+    if (sscanf(env, "%d,%d,%d", &c, &l, &nw) == 3 && C % c == 0) {
       for (const Variant& vv : kVariants)
-        if (vv.L == l && vv.NW == nw) {
+        if (vv.cpl == c && vv.L == l && vv.NW == nw) {
+          cpl = c;
           L = l;
           NW = nw;
         }
     }
   }
   Wkv4Plan p;
+  p.cpl = cpl;
   p.L = L;
   p.NW = NW;
   p.tile = int64_t(L) * NW;
   p.n_tiles = (T + p.tile - 1) / p.tile;
-  p.n_cblk = (C + 63) / 64;
+  p.n_cblk = (C + 64 * cpl - 1) / (64 * cpl);
   p.groups = B * p.n_cblk;
-  // Tickets, token indices and channel indices are 32-bit in the kernel.
+  // Tiles, token and channel indices are 32-bit in the kernel.
   if (p.n_tiles * p.groups >= (int64_t(1) << 31) || T >= (int64_t(1) << 31) ||
       C >= (int64_t(1) << 31) || p.groups >= (int64_t(1) << 31))
     return false;
-  p.ws_bytes = kWkv4HeaderBytes +
-               size_t(p.n_tiles) * size_t(p.groups) * kWkv4SlotWords * 64 * sizeof(uint64_t);
+  const size_t ctr_bytes = size_t(p.groups) * kWkv4CounterStride;
+  p.slots_offset = (kWkv4HeaderBytes + ctr_bytes + 255) / 256 * 256;
+  p.ws_bytes = p.slots_offset + size_t(p.n_tiles) * size_t(p.groups) * 8 * 64 * size_t(cpl) *
+                                    sizeof(uint64_t);
   *plan = p;
   return true;
 }
@@ -389,14 +465,17 @@ hipError_t wkv4_forward_launch(const Wkv4Plan& pl, int64_t B, int64_t T, int64_t
                                const float* w, const float* u, const float* k,
                                const float* v, float* y, void* ws, hipStream_t stream) {
   (void)B;
-  switch (pl.L * 100 + pl.NW) {
-    case 6404: return launch_tiled<64, 4>(pl, T, C, w, u, k, v, y, ws, stream);
-    case 6401: return launch_tiled<64, 1>(pl, T, C, w, u, k, v, y, ws, stream);
-    case 3204: return launch_tiled<32, 4>(pl, T, C, w, u, k, v, y, ws, stream);
-    case 3208: return launch_tiled<32, 8>(pl, T, C, w, u, k, v, y, ws, stream);
-    case 1604: return launch_tiled<16, 4>(pl, T, C, w, u, k, v, y, ws, stream);
-    case 6402: return launch_tiled<64, 2>(pl, T, C, w, u, k, v, y, ws, stream);
-    case 1601: return launch_tiled<16, 1>(pl, T, C, w, u, k, v, y, ws, stream);
+  switch (pl.cpl * 10000 + pl.L * 100 + pl.NW) {
+    case 40808: return launch_tiled<4, 8, 8>(pl, T, C, w, u, k, v, y, ws, stream);
+    case 41604: return launch_tiled<4, 16, 4>(pl, T, C, w, u, k, v, y, ws, stream);
+    case 41608: return launch_tiled<4, 16, 8>(pl, T, C, w, u, k, v, y, ws, stream);
+    case 21608: return launch_tiled<2, 16, 8>(pl, T, C, w, u, k, v, y, ws, stream);
+    case 23204: return launch_tiled<2, 32, 4>(pl, T, C, w, u, k, v, y, ws, stream);
+    case 21604: return launch_tiled<2, 16, 4>(pl, T, C, w, u, k, v, y, ws, stream);
+    case 13208: return launch_tiled<1, 32, 8>(pl, T, C, w, u, k, v, y, ws, stream);
+    case 13204: return launch_tiled<1, 32, 4>(pl, T, C, w, u, k, v, y, ws, stream);
+    case 16401: return launch_tiled<1, 64, 1>(pl, T, C, w, u, k, v, y, ws, stream);
+    case 11604: return launch_tiled<1, 16, 4>(pl, T, C, w, u, k, v, y, ws, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -9,24 +9,28 @@ namespace rwkv {
 
 // ----- RWKV-4 forward: single-pass tiled scan with decoupled look-back -----
 //
-// A tile is L tokens x 64 channels per wave, NW waves per workgroup stacked
-// along time, so a workgroup covers TILE = L * NW tokens of one 64-channel
-// block.  Workspace = header + per (tile, channel block) two published
-// histories (aggregate, inclusive), 4 tagged 64-bit words per lane each.
+// A channel block is 64*CPL channels (CPL per lane); a tile is L tokens per
+// wave x NW waves stacked along time, so a workgroup covers TILE = L * NW
+// tokens of one block.  Workspace: a header (error word), one 64-bit tagged
+// ticket counter per (batch, block) every kWkv4CounterStride bytes, then per
+// (tile, block) two published histories (aggregate, inclusive) of 4 tagged
+// 64-bit words per channel each.
 struct Wkv4Plan {
+  int cpl;       // channels per lane (vector width of the loads)
   int L;         // tokens per wave
   int NW;        // waves per workgroup
   int64_t tile;  // L * NW
   int64_t n_tiles;
-  int64_t n_cblk;  // ceil(C / 64)
+  int64_t n_cblk;  // ceil(C / (64 * cpl))
   int64_t groups;  // B * n_cblk
+  size_t slots_offset;
   size_t ws_bytes;
 };
 
-constexpr size_t kWkv4HeaderBytes = 256;
-constexpr int kWkv4SlotWords = 8;  // aggregate (A, B, kr, n) then inclusive (A, B, kr, n)
+constexpr size_t kWkv4HeaderBytes = 128;
+constexpr size_t kWkv4CounterStride = 128;  // one counter per 128-byte line
 
-// Plan for a shape; honours RWKV_WKV4_TILE="L,NW" for tests and sweeps.
+// Plan for a shape; honours RWKV_WKV4_TILE="CPL,L,NW" for tests and sweeps.
 // Returns false if the shape cannot be planned (too large for 32-bit tickets).
 bool wkv4_plan(int64_t B, int64_t T, int64_t C, Wkv4Plan* plan);
 

@@ -17,7 +17,8 @@ from wkv_testutil import WKV4_TOL, log, to_dev, torch_dev, wkv4_scaled_err
 
 pytestmark = pytest.mark.gpu
 
-TILE_VARIANTS = ["64,4", "64,1", "32,4", "32,8", "16,4", "64,2", "16,1"]
+TILE_VARIANTS = ["4,8,8", "4,16,4", "4,16,8", "2,16,8", "2,32,4", "2,16,4", "1,32,8",
+                 "1,32,4", "1,64,1", "1,16,4"]
 
 
 def gpu_forward(inp, tile=None):
@@ -107,7 +108,7 @@ def test_identity_and_shift_maps_bit_exact():
     previous token survives, y[t] == v[t-1].  Holds across tile boundaries."""
     B, T, C = 2, 1500, 192
     inp = synth.wkv4_inputs(B, T, C, seed=99)
-    for tile in ("64,4", "16,4"):
+    for tile in ("4,8,8", "2,16,4", "1,16,4"):
         log(f"wkv4_forward identity/shift maps tile={tile}")
         ident = dict(inp, u=np.full(C, 100.0, np.float32))
         assert np.array_equal(gpu_forward(ident, tile), inp["v"])
@@ -148,6 +149,20 @@ def test_workspace_reuse_across_shapes():
     for i in range(20):
         assert wkv4_scaled_err(gpu_forward(a), ya_ref, Sa) <= WKV4_TOL, i
         assert wkv4_scaled_err(gpu_forward(b), yb_ref, Sb) <= WKV4_TOL, i
+
+
+def test_workspace_layout_changes():
+    """Regression: one workspace serves calls whose channel-block counts grow
+    and shrink, so earlier calls' words sit where later calls keep their
+    counters and histories."""
+    shapes = [(1, 300, 64), (4, 300, 771), (1, 700, 5120), (8, 300, 770), (2, 300, 64),
+              (16, 200, 1028)]
+    cases = [(synth.wkv4_inputs(B, T, C, seed=3 + i), (B, T, C)) for i, (B, T, C) in enumerate(shapes)]
+    refs = [oracle_forward(inp) for inp, _ in cases]
+    for rnd in range(2):
+        for (inp, shp), (y_ref, S) in zip(cases, refs):
+            log(f"wkv4_forward layout change round {rnd} shape {shp}")
+            assert wkv4_scaled_err(gpu_forward(inp), y_ref, S) <= WKV4_TOL, shp
 
 
 # ------------------------------------------------------------------ step ---
