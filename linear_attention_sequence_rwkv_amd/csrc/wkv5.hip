@@ -1,10 +1,27 @@
-// Eagle (RWKV-5) matrix-state WKV kernels for gfx950.
+// Eagle (RWKV-5) matrix-state WKV forward for gfx950.
 //
 // What is computed: [Eagle-Finch] "RWKV-5 Eagle and RWKV-6 Finch" (ql.gl
 // blog), section "Eagle: extending vector memory to matrix memory":
 //   s' = diag(w) s + k^T v,   wkv' = s + diag(u) k^T v,
-// with the receptance reading wkv' like a query.  Per (batch, head) the state
-// s is D x D, indexed [key i][value j]; diag(w) scales key rows.
+// read by the receptance like a query.  Per (batch, head) the state s is
+// D x D (D = 64), indexed [key i][value j]; diag(w) scales key rows.
+//
+// Chunked form (chunks of L = 64 tokens; tau, sigma are positions in the
+// chunk, S the state at the chunk start).  Unrolling the recurrence,
+//   o_tau = r_tau (diag(w^tau) S)
+//         + sum_{sigma<tau} (sum_i r_tau[i] w_i^(tau-1-sigma) k_sigma[i]) v_sigma
+//         + (sum_i r_tau[i] u_i k_tau[i]) v_tau,
+//   S_next = diag(w^L) S + sum_sigma diag(w^(L-1-sigma)) k_sigma^T v_sigma.
+// With rt = r (.) w^(tau-32), kt = k (.) w^(31-sigma) and kh = k (.) w^(63-sigma)
+// (per element, a mid-chunk reference keeps both factors within
+// w^(+-32)), the chunk is four dense products on bf16 MFMA with fp32
+// accumulation:
+//   A  = strict_lower(rt kt^T) + diag(beta)         (64 x 64)
+//   O  = A V + rt (diag(w^32) S)                    (64 x 32 per workgroup)
+//   S' = diag(w^64) S + kh^T V                      (64 x 32, kept in fp32)
+// The factorisation needs w^(-32) and w^(31) inside bf16/fp32 range, i.e.
+// |log2 w| <= 3.6 for every channel of the head; a head outside that range
+// runs the exact fp32 recurrence instead (one branch per workgroup).
 #include "wkv_device.h"
 #include "wkv_internal.h"
 
@@ -12,44 +29,305 @@ namespace rwkv {
 
 namespace {
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 64;        // head size
+constexpr int kL = 64;        // chunk length
+constexpr int kDV = 32;       // value columns per workgroup
+constexpr int kPad = 72;      // LDS row length in bf16 (144 bytes: 16-byte aligned rows)
+constexpr int kExpLo = -32;   // decay table covers w^e for e in [kExpLo, kExpHi]
+constexpr int kExpHi = 64;
+constexpr int kExpN = kExpHi - kExpLo + 1;
+// Largest |log2 w| for which w^(-32) and w^31 stay far inside fp32/bf16 range.
+constexpr float kMaxLog2Decay = 3.6f;
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t x) {
   return __uint_as_float(uint32_t(x) << 16);
 }
 
-// Token-by-token recurrence: one workgroup per (batch, head), one lane per
-// value column j holding the state column s[:, j] (64 floats) in registers.
-// Exact float32 arithmetic on the bf16 inputs.
-__global__ __launch_bounds__(64) void wkv5_fwd_recurrent64(
-    int T, int H, const uint16_t* __restrict__ r, const uint16_t* __restrict__ k,
+// float -> bf16, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ __bf16 to_bf16(float x) { return static_cast<__bf16>(x); }
+
+struct Lds {
+  __bf16 rt[kL][kPad];    // rt[tau][i]
+  __bf16 kt[kL][kPad];    // kt[sigma][i]
+  __bf16 kh[kD][kPad];    // kh^T[i][sigma]
+  __bf16 vt[kDV][kPad];   // v^T[j][sigma]
+  __bf16 ap[4][16][kPad]; // A'[tau][sigma], 16 rows per wave
+  __bf16 sp[kDV][kPad];   // (diag(w^32) S)^T[j][i]
+  float dec[kExpN][kD];   // w_i^e
+  float beta[kL];
+  float u[kD];
+  int fallback;
+};
+
+// Exact fp32 recurrence for one (batch, head, value half): lane j < kDV
+// keeps the state column s[:, j] in registers.
+__device__ void eagle_recurrent_half(int T, int H, int b, int h, int j0,
+                                     const uint16_t* __restrict__ r,
+                                     const uint16_t* __restrict__ k,
+                                     const uint16_t* __restrict__ v,
+                                     const float* __restrict__ w,
+                                     const float* __restrict__ u, float* __restrict__ o,
+                                     Lds& s) {
+  float* s_r = &s.dec[0][0];
+  float* s_k = &s.dec[1][0];
+  float* s_w = &s.dec[2][0];
+  float* s_u = &s.dec[3][0];
+  const int tid = threadIdx.x;
+  if (tid < kD) {
+    s_w[tid] = w[h * kD + tid];
+    s_u[tid] = u[h * kD + tid];
+  }
+  float S[kD];
+#pragma unroll
+  for (int i = 0; i < kD; ++i) S[i] = 0.f;
+  for (int t = 0; t < T; ++t) {
+    const size_t off = ((size_t(b) * T + t) * H + h) * kD;
+    __syncthreads();
+    if (tid < kD) {
+      s_r[tid] = bf16_to_f32(r[off + tid]);
+      s_k[tid] = bf16_to_f32(k[off + tid]);
+    }
+    __syncthreads();
+    if (tid < kDV) {
+      const float vj = bf16_to_f32(v[off + j0 + tid]);
+      float acc = 0.f, beta = 0.f;
+#pragma unroll
+      for (int i = 0; i < kD; ++i) {
+        const float ri = s_r[i], ki = s_k[i];
+        acc = fmaf(ri, S[i], acc);
+        beta = fmaf(ri * s_u[i], ki, beta);
+        S[i] = fmaf(s_w[i], S[i], ki * vj);
+      }
+      o[off + j0 + tid] = fmaf(beta, vj, acc);
+    }
+  }
+}
+
+// One chunk's raw inputs for this thread: token tau = tid/4, dims 16*(tid%4)
+// of r and k, and 8 value dims of this workgroup's half.
+struct ChunkRegs {
+  uint4 r0, r1, k0, k1, v0;
+};
+
+__device__ __forceinline__ void load_chunk(ChunkRegs& x, int t0, int T, int H, int b, int h,
+                                           int j0, const uint16_t* __restrict__ r,
+                                           const uint16_t* __restrict__ k,
+                                           const uint16_t* __restrict__ v) {
+  const int tid = threadIdx.x;
+  const int tau = tid >> 2, q4 = tid & 3;
+  if (t0 + tau < T) {
+    const size_t off = ((size_t(b) * T + t0 + tau) * H + h) * kD;
+    const uint4* rp = reinterpret_cast<const uint4*>(r + off + 16 * q4);
+    const uint4* kp = reinterpret_cast<const uint4*>(k + off + 16 * q4);
+    x.r0 = rp[0];
+    x.r1 = rp[1];
+    x.k0 = kp[0];
+    x.k1 = kp[1];
+    x.v0 = *reinterpret_cast<const uint4*>(v + off + j0 + 8 * q4);
+  } else {
+    x.r0 = x.r1 = x.k0 = x.k1 = x.v0 = uint4{0u, 0u, 0u, 0u};
+  }
+}
+
+__device__ __forceinline__ float lo_half(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float hi_half(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// Scale one chunk into LDS: rt, kt, kh^T, v^T, beta.
+__device__ __forceinline__ void stage_chunk(const ChunkRegs& x, Lds& s) {
+  const int tid = threadIdx.x;
+  const int tau = tid >> 2, q4 = tid & 3;
+  const int d0 = 16 * q4;
+  float rv[16], kv[16];
+  const uint32_t rw[8] = {x.r0.x, x.r0.y, x.r0.z, x.r0.w, x.r1.x, x.r1.y, x.r1.z, x.r1.w};
+  const uint32_t kw[8] = {x.k0.x, x.k0.y, x.k0.z, x.k0.w, x.k1.x, x.k1.y, x.k1.z, x.k1.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    rv[2 * e] = lo_half(rw[e]);
+    rv[2 * e + 1] = hi_half(rw[e]);
+    kv[2 * e] = lo_half(kw[e]);
+    kv[2 * e + 1] = hi_half(kw[e]);
+  }
+  const float* dr = s.dec[tau - kExpLo - 32];   // w^(tau-32)
+  const float* dk = s.dec[31 - tau - kExpLo];   // w^(31-sigma)
+  const float* dh = s.dec[63 - tau - kExpLo];   // w^(63-sigma)
+  float bpart = 0.f;
+  bf16x8 rt0, rt1, kt0, kt1;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    rt0[e] = to_bf16(rv[e] * dr[d0 + e]);
+    rt1[e] = to_bf16(rv[8 + e] * dr[d0 + 8 + e]);
+    kt0[e] = to_bf16(kv[e] * dk[d0 + e]);
+    kt1[e] = to_bf16(kv[8 + e] * dk[d0 + 8 + e]);
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    s.kh[d0 + e][tau] = to_bf16(kv[e] * dh[d0 + e]);
+    bpart = fmaf(rv[e] * s.u[d0 + e], kv[e], bpart);
+  }
+  *reinterpret_cast<bf16x8*>(&s.rt[tau][d0]) = rt0;
+  *reinterpret_cast<bf16x8*>(&s.rt[tau][d0 + 8]) = rt1;
+  *reinterpret_cast<bf16x8*>(&s.kt[tau][d0]) = kt0;
+  *reinterpret_cast<bf16x8*>(&s.kt[tau][d0 + 8]) = kt1;
+  const uint32_t vw[4] = {x.v0.x, x.v0.y, x.v0.z, x.v0.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    s.vt[8 * q4 + 2 * e][tau] = to_bf16(lo_half(vw[e]));
+    s.vt[8 * q4 + 2 * e + 1][tau] = to_bf16(hi_half(vw[e]));
+  }
+  // the four threads of a token sit in adjacent lanes of one wave
+  bpart += __shfl_xor(bpart, 1);
+  bpart += __shfl_xor(bpart, 2);
+  if (q4 == 0) s.beta[tau] = bpart;
+}
+
+__device__ __forceinline__ floatx4 mfma(const bf16x8& a, const bf16x8& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Workgroup: 4 waves; (batch, head, value half).  blockIdx pairs the two
+// halves of a head 8 apart so that they land on the same XCD (dispatch is
+// round-robin over 8 XCDs) and share r, k reads in its L2.
+__global__ __launch_bounds__(256) void wkv5_fwd_chunked(
+    int T, int H, int BH, const uint16_t* __restrict__ r, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ w,
     const float* __restrict__ u, float* __restrict__ o) {
-  constexpr int D = 64;
-  __shared__ float s_r[D], s_k[D], s_w[D], s_u[D];
-  const int bh = blockIdx.x;
-  const int b = bh / H;
-  const int h = bh - b * H;
-  const int j = threadIdx.x;
-  s_w[j] = w[h * D + j];
-  s_u[j] = u[h * D + j];
-  float S[D];
-#pragma unroll
-  for (int i = 0; i < D; ++i) S[i] = 0.f;
-  for (int t = 0; t < T; ++t) {
-    const size_t off = ((size_t(b) * T + t) * H + h) * D;
-    const float vj = bf16_to_f32(v[off + j]);
-    s_r[j] = bf16_to_f32(r[off + j]);
-    s_k[j] = bf16_to_f32(k[off + j]);
+  __shared__ Lds s;
+  const int bx = blockIdx.x;
+  const int bh = (bx >> 4) * 8 + (bx & 7);
+  const int half = (bx >> 3) & 1;
+  if (bh >= BH) return;
+  const int b = bh / H, h = bh - (bh / H) * H;
+  const int j0 = half * kDV;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int q = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // Decay table w^e and the range check that picks the path.
+  if (tid == 0) s.fallback = 0;
+  __syncthreads();
+  if (tid < kD) {
+    const float wi = w[h * kD + tid];
+    s.u[tid] = u[h * kD + tid];
+    const float l2w = __log2f(wi);
+    if (!(fabsf(l2w) <= kMaxLog2Decay)) atomicOr(&s.fallback, 1);  // also catches NaN, w<=0
+  }
+  for (int idx = tid; idx < kExpN * kD; idx += 256) {
+    const int e = idx / kD + kExpLo, i = idx % kD;
+    s.dec[e - kExpLo][i] = exp2f(float(e) * __log2f(w[h * kD + i]));
+  }
+  __syncthreads();
+  if (s.fallback) {
+    eagle_recurrent_half(T, H, b, h, j0, r, k, v, w, u, o, s);
+    return;
+  }
+
+  // S' starts at zero; S itself lives in registers (wave q: key rows 16q..).
+  for (int idx = tid; idx < kDV * kPad; idx += 256) (&s.sp[0][0])[idx] = to_bf16(0.f);
+  floatx4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+
+  const int row = lane & 15;         // MFMA operand row/column of this lane
+  const int kq = 8 * (lane >> 4);    // first K element of this lane in a 32-wide step
+  const int crow = 4 * (lane >> 4);  // first accumulator row of this lane
+
+  const int n_chunks = (T + kL - 1) / kL;
+  ChunkRegs cur, nxt;
+  load_chunk(cur, 0, T, H, b, h, j0, r, k, v);
+  for (int c = 0; c < n_chunks; ++c) {
+    const int t0 = c * kL;
+    stage_chunk(cur, s);
     __syncthreads();
-    float acc = 0.f, beta = 0.f;
+    if (c + 1 < n_chunks) load_chunk(nxt, t0 + kL, T, H, b, h, j0, r, k, v);
+
+    // A = rt kt^T for rows 16q..16q+15 and sigma blocks 0..q.
+    floatx4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
+                      {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int i = 0; i < D; ++i) {
-      const float ri = s_r[i], ki = s_k[i];
-      acc = fmaf(ri, S[i], acc);
-      beta = fmaf(ri * s_u[i], ki, beta);
-      S[i] = fmaf(s_w[i], S[i], ki * vj);
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.rt[16 * q + row][32 * ks + kq]);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        if (nb <= q) {
+          const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s.kt[16 * nb + row][32 * ks + kq]);
+          acc[nb] = mfma(a, bb, acc[nb]);
+        }
     }
-    o[off + j] = fmaf(beta, vj, acc);
-    __syncthreads();
+    // Causal mask, bonus on the diagonal, bf16 into this wave's A' rows.
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int sig = 16 * nb + row;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int tau = 16 * q + crow + rr;
+        float val = 0.f;
+        if (nb <= q) val = sig < tau ? acc[nb][rr] : (sig == tau ? s.beta[tau] : 0.f);
+        s.ap[q][crow + rr][sig] = to_bf16(val);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // O = A' V + rt S'  (16 rows x 32 columns per wave).
+    floatx4 oacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    const int nks = (q + 2) >> 1;  // 32-wide sigma steps that can be non-zero
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      if (ks < nks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.ap[q][row][32 * ks + kq]);
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+          const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s.vt[16 * jb + row][32 * ks + kq]);
+          oacc[jb] = mfma(a, bb, oacc[jb]);
+        }
+      }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.rt[16 * q + row][32 * ks + kq]);
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s.sp[16 * jb + row][32 * ks + kq]);
+        oacc[jb] = mfma(a, bb, oacc[jb]);
+      }
+    }
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int tau = 16 * q + crow + rr;
+        if (t0 + tau < T)
+          o[((size_t(b) * T + t0 + tau) * H + h) * kD + j0 + 16 * jb + row] = oacc[jb][rr];
+      }
+
+    // S <- diag(w^64) S + kh^T V for key rows 16q..16q+15.
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float d64 = s.dec[64 - kExpLo][16 * q + crow + rr];
+      sacc[0][rr] *= d64;
+      sacc[1][rr] *= d64;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.kh[16 * q + row][32 * ks + kq]);
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s.vt[16 * jb + row][32 * ks + kq]);
+        sacc[jb] = mfma(a, bb, sacc[jb]);
+      }
+    }
+    __syncthreads();  // every wave is done with rt, kt, kh, vt, sp of this chunk
+
+    // S' = diag(w^32) S for the next chunk, transposed to [j][i].
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int i = 16 * q + crow + rr;
+        s.sp[16 * jb + row][i] = to_bf16(sacc[jb][rr] * s.dec[32 - kExpLo][i]);
+      }
+    cur = nxt;
   }
 }
 
@@ -63,8 +341,10 @@ hipError_t wkv5_forward_launch(int64_t B, int64_t T, int64_t H, int64_t D,
                                hipStream_t stream) {
   (void)D;
   (void)ws;
-  hipLaunchKernelGGL(wkv5_fwd_recurrent64, dim3(unsigned(B * H)), dim3(64), 0, stream, int(T),
-                     int(H), r, k, v, w, u, o);
+  const int64_t BH = B * H;
+  const unsigned grid = unsigned((BH + 7) / 8 * 16);
+  hipLaunchKernelGGL(wkv5_fwd_chunked, dim3(grid), dim3(256), 0, stream, int(T), int(H),
+                     int(BH), r, k, v, w, u, o);
   return hipGetLastError();
 }
 
