@@ -143,7 +143,7 @@ def bench_copy_peak(torch, nbytes=1 << 30, reps=20):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def bench_decode(torch, rw, cfg, reps):
+def bench_decode(torch, rw, cfg, reps, graph=True):
     import synth
     dev = torch.device("cuda:0")
     inp = synth.wkv4_step_inputs(cfg.B, cfg.C, cfg.pool, cfg.seed)
@@ -175,6 +175,10 @@ def bench_decode(torch, rw, cfg, reps):
     e.record(stream)
     torch.cuda.synchronize()
     eager_ms = s.elapsed_time(e) / reps
+    elems = cfg.B * cfg.C * cfg.steps
+    if not graph:
+        assert torch.isfinite(y).all().item()
+        return {"eager_ms": eager_ms, "graph_ms": None, "elems": elems, "bytes": 36 * elems}
     # The same 4096 launches captured once in a HIP graph and replayed.
     g = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream(dev)
@@ -191,7 +195,6 @@ def bench_decode(torch, rw, cfg, reps):
     torch.cuda.synchronize()
     graph_ms = s.elapsed_time(e) / reps
     assert torch.isfinite(y).all().item()
-    elems = cfg.B * cfg.C * cfg.steps
     return {"eager_ms": eager_ms, "graph_ms": graph_ms, "elems": elems, "bytes": 36 * elems}
 
 
@@ -260,6 +263,8 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB copy (counter calibration runs)")
+    ap.add_argument("--secondary", default="long,decode,decode-graph,eagle",
+                    help="comma list of secondary workloads: long, decode, decode-graph, eagle")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -284,7 +289,7 @@ def main(argv=None):
     value = prim["bytes"] / (prim["ms_per_step"] * 1e-3) / 1e9
     achieved = prim["bytes"] / (prim["kernel_ms"] * 1e-3) / 1e9
     src_hash = kernel_source_hash()
-    traffic = read_counter_summary("wkv4_fwd_B8_T1024_C768_counters.md", src_hash)
+    traffic = read_counter_summary("wkv4_fwd_tiled_B8_T1024_C768.md", src_hash)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -311,27 +316,35 @@ def main(argv=None):
     if args.copy_calibration:
         line["copy_peak_GBps"] = round(copy_gbps, 1)
 
-    if not args.no_secondary:
+    want = set() if args.no_secondary else {x for x in args.secondary.split(",") if x}
+    if want:
         sec = {}
-        lc = synth.CFG_WKV4_LONG
-        log(f"bench: {lc.name}")
-        r = bench_wkv4_forward(torch, rw, lc, steps=10, warmup=2, rotate=1)
-        sec[lc.name] = {"ms": round(r["ms_per_step"], 4), "kernel_ms": round(r["kernel_ms"], 4),
-                        "GBps": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9, 1),
-                        "gelem_per_s": round(r["elems"] / (r["kernel_ms"] * 1e-3) / 1e9, 1)}
-        dc = synth.CFG_WKV4_DECODE
-        log(f"bench: {dc.name}")
-        r = bench_decode(torch, rw, dc, reps=3)
-        sec[dc.name] = {"eager_ms": round(r["eager_ms"], 3), "graph_ms": round(r["graph_ms"], 3),
-                        "graph_GBps": round(r["bytes"] / (r["graph_ms"] * 1e-3) / 1e9, 1),
-                        "eager_GBps": round(r["bytes"] / (r["eager_ms"] * 1e-3) / 1e9, 1),
-                        "us_per_step_graph": round(1e3 * r["graph_ms"] / dc.steps, 3)}
-        ec = synth.CFG_WKV5_EAGLE
-        log(f"bench: {ec.name}")
-        r = bench_wkv5(torch, rw, ec, reps=5)
-        sec[ec.name] = {"ms": round(r["ms"], 4),
-                        "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
-                        "algorithmic_TFLOPs": round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 2)}
+        if "long" in want:
+            lc = synth.CFG_WKV4_LONG
+            log(f"bench: {lc.name}")
+            r = bench_wkv4_forward(torch, rw, lc, steps=10, warmup=2, rotate=1)
+            sec[lc.name] = {"ms": round(r["ms_per_step"], 4),
+                            "kernel_ms": round(r["kernel_ms"], 4),
+                            "GBps": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9, 1),
+                            "gelem_per_s": round(r["elems"] / (r["kernel_ms"] * 1e-3) / 1e9, 1)}
+        if "decode" in want or "decode-graph" in want:
+            dc = synth.CFG_WKV4_DECODE
+            log(f"bench: {dc.name}")
+            r = bench_decode(torch, rw, dc, reps=3, graph="decode-graph" in want)
+            d = {"eager_ms": round(r["eager_ms"], 3),
+                 "eager_GBps": round(r["bytes"] / (r["eager_ms"] * 1e-3) / 1e9, 1)}
+            if r["graph_ms"] is not None:
+                d.update({"graph_ms": round(r["graph_ms"], 3),
+                          "graph_GBps": round(r["bytes"] / (r["graph_ms"] * 1e-3) / 1e9, 1),
+                          "us_per_step_graph": round(1e3 * r["graph_ms"] / dc.steps, 3)})
+            sec[dc.name] = d
+        if "eagle" in want:
+            ec = synth.CFG_WKV5_EAGLE
+            log(f"bench: {ec.name}")
+            r = bench_wkv5(torch, rw, ec, reps=5)
+            sec[ec.name] = {"ms": round(r["ms"], 4),
+                            "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
+                            "algorithmic_TFLOPs": round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 2)}
         line["secondary"] = sec
 
     if not args.no_cpu_baseline:
