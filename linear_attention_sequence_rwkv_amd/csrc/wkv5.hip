@@ -54,7 +54,6 @@ struct Lds {
   __bf16 kt[kL][kPad];    // kt[sigma][i]
   __bf16 kh[kD][kPad];    // kh^T[i][sigma]
   __bf16 vt[kDV][kPad];   // v^T[j][sigma]
-  __bf16 ap[4][16][kPad]; // A'[tau][sigma], 16 rows per wave
   __bf16 sp[kDV][kPad];   // (diag(w^32) S)^T[j][i]
   float dec[kExpN][kD];   // w_i^e
   float beta[kL];
@@ -135,8 +134,31 @@ __device__ __forceinline__ void load_chunk(ChunkRegs& x, int t0, int T, int H, i
 __device__ __forceinline__ float lo_half(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float hi_half(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
+// Decay factors and bonus of the 16 channels this thread scales.  The
+// thread's token position in a chunk never changes, so they are computed once
+// and kept in registers (reading them from the shared table would put every
+// lane of a 16-token column on one LDS bank).
+struct StageConsts {
+  float fr[16];  // w^(tau-32)
+  float fk[16];  // w^(31-tau)
+  float fh[16];  // w^(63-tau)
+  float ur[16];  // u
+};
+
+__device__ __forceinline__ void stage_consts(StageConsts& c, const Lds& s) {
+  const int tid = threadIdx.x;
+  const int tau = tid >> 2, d0 = 16 * (tid & 3);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    c.fr[e] = s.dec[tau - 32 - kExpLo][d0 + e];
+    c.fk[e] = s.dec[31 - tau - kExpLo][d0 + e];
+    c.fh[e] = s.dec[63 - tau - kExpLo][d0 + e];
+    c.ur[e] = s.u[d0 + e];
+  }
+}
+
 // Scale one chunk into LDS: rt, kt, kh^T, v^T, beta.
-__device__ __forceinline__ void stage_chunk(const ChunkRegs& x, Lds& s) {
+__device__ __forceinline__ void stage_chunk(const ChunkRegs& x, const StageConsts& f, Lds& s) {
   const int tid = threadIdx.x;
   const int tau = tid >> 2, q4 = tid & 3;
   const int d0 = 16 * q4;
@@ -150,22 +172,19 @@ __device__ __forceinline__ void stage_chunk(const ChunkRegs& x, Lds& s) {
     kv[2 * e] = lo_half(kw[e]);
     kv[2 * e + 1] = hi_half(kw[e]);
   }
-  const float* dr = s.dec[tau - kExpLo - 32];   // w^(tau-32)
-  const float* dk = s.dec[31 - tau - kExpLo];   // w^(31-sigma)
-  const float* dh = s.dec[63 - tau - kExpLo];   // w^(63-sigma)
   float bpart = 0.f;
   bf16x8 rt0, rt1, kt0, kt1;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    rt0[e] = to_bf16(rv[e] * dr[d0 + e]);
-    rt1[e] = to_bf16(rv[8 + e] * dr[d0 + 8 + e]);
-    kt0[e] = to_bf16(kv[e] * dk[d0 + e]);
-    kt1[e] = to_bf16(kv[8 + e] * dk[d0 + 8 + e]);
+    rt0[e] = to_bf16(rv[e] * f.fr[e]);
+    rt1[e] = to_bf16(rv[8 + e] * f.fr[8 + e]);
+    kt0[e] = to_bf16(kv[e] * f.fk[e]);
+    kt1[e] = to_bf16(kv[8 + e] * f.fk[8 + e]);
   }
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    s.kh[d0 + e][tau] = to_bf16(kv[e] * dh[d0 + e]);
-    bpart = fmaf(rv[e] * s.u[d0 + e], kv[e], bpart);
+    s.kh[d0 + e][tau] = to_bf16(kv[e] * f.fh[e]);
+    bpart = fmaf(rv[e] * f.ur[e], kv[e], bpart);
   }
   *reinterpret_cast<bf16x8*>(&s.rt[tau][d0]) = rt0;
   *reinterpret_cast<bf16x8*>(&s.rt[tau][d0 + 8]) = rt1;
@@ -232,55 +251,62 @@ __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
   const int kq = 8 * (lane >> 4);    // first K element of this lane in a 32-wide step
   const int crow = 4 * (lane >> 4);  // first accumulator row of this lane
 
+  StageConsts f;
+  stage_consts(f, s);
   const int n_chunks = (T + kL - 1) / kL;
   ChunkRegs cur, nxt;
   load_chunk(cur, 0, T, H, b, h, j0, r, k, v);
   for (int c = 0; c < n_chunks; ++c) {
     const int t0 = c * kL;
-    stage_chunk(cur, s);
+    stage_chunk(cur, f, s);
     __syncthreads();
     if (c + 1 < n_chunks) load_chunk(nxt, t0 + kL, T, H, b, h, j0, r, k, v);
 
-    // A = rt kt^T for rows 16q..16q+15 and sigma blocks 0..q.
+    // A^T = kt rt^T for sigma blocks 0..q against this wave's 16 tokens:
+    // lane holds column tau = 16q + row, rows sigma = 16nb + crow .. +3.
     floatx4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
                       {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.rt[16 * q + row][32 * ks + kq]);
+      const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s.rt[16 * q + row][32 * ks + kq]);
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
         if (nb <= q) {
-          const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s.kt[16 * nb + row][32 * ks + kq]);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.kt[16 * nb + row][32 * ks + kq]);
           acc[nb] = mfma(a, bb, acc[nb]);
         }
     }
-    // Causal mask, bonus on the diagonal, bf16 into this wave's A' rows.
+    // Causal mask and the bonus on the diagonal, in registers.  The pair of
+    // sigma tiles (2ks, 2ks+1) held by a lane is directly an A operand of a
+    // 32-wide K step, with K ordered as sigma = 32ks + crow + 0..3, then
+    // 32ks + 16 + crow + 0..3; V below is read in the same order.
+    const int tau_l = 16 * q + row;
+    const float beta = s.beta[tau_l];
+    bf16x8 ap[2];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int sig = 16 * nb + row;
+    for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int tau = 16 * q + crow + rr;
+        const int sig = 16 * nb + crow + rr;
         float val = 0.f;
-        if (nb <= q) val = sig < tau ? acc[nb][rr] : (sig == tau ? s.beta[tau] : 0.f);
-        s.ap[q][crow + rr][sig] = to_bf16(val);
+        if (nb <= q) val = sig < tau_l ? acc[nb][rr] : (sig == tau_l ? beta : 0.f);
+        ap[nb >> 1][(nb & 1) * 4 + rr] = to_bf16(val);
       }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // O = A' V + rt S'  (16 rows x 32 columns per wave).
+    // O = A' V + rt S'  (16 tokens x 32 value columns per wave).
     floatx4 oacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     const int nks = (q + 2) >> 1;  // 32-wide sigma steps that can be non-zero
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
       if (ks < nks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.ap[q][row][32 * ks + kq]);
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
-          const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s.vt[16 * jb + row][32 * ks + kq]);
-          oacc[jb] = mfma(a, bb, oacc[jb]);
+          const __bf16* vr = &s.vt[16 * jb + row][32 * ks + crow];
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
+          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 16);
+          const bf16x8 bb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          oacc[jb] = mfma(ap[ks], bb, oacc[jb]);
         }
       }
 #pragma unroll
@@ -319,14 +345,19 @@ __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
     }
     __syncthreads();  // every wave is done with rt, kt, kh, vt, sp of this chunk
 
-    // S' = diag(w^32) S for the next chunk, transposed to [j][i].
+    // S' = diag(w^32) S for the next chunk, transposed to [j][i]: a lane's
+    // four key rows are adjacent, one 8-byte store per value tile.
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
+    for (int jb = 0; jb < 2; ++jb) {
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      bf16x4 pk;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int i = 16 * q + crow + rr;
-        s.sp[16 * jb + row][i] = to_bf16(sacc[jb][rr] * s.dec[32 - kExpLo][i]);
+        pk[rr] = to_bf16(sacc[jb][rr] * s.dec[32 - kExpLo][i]);
       }
+      *reinterpret_cast<bf16x4*>(&s.sp[16 * jb + row][16 * q + crow]) = pk;
+    }
     cur = nxt;
   }
 }
