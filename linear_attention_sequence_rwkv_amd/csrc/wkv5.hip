@@ -25,6 +25,8 @@
 #include "wkv_device.h"
 #include "wkv_internal.h"
 
+#include <stdlib.h>
+
 namespace rwkv {
 
 namespace {
@@ -34,7 +36,6 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 64;        // head size
 constexpr int kL = 64;        // chunk length
-constexpr int kDV = 32;       // value columns per workgroup
 constexpr int kPad = 72;      // LDS row length in bf16 (144 bytes: 16-byte aligned rows)
 constexpr int kExpLo = -32;   // decay table covers w^e for e in [kExpLo, kExpHi]
 constexpr int kExpHi = 64;
@@ -49,27 +50,29 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t x) {
 // float -> bf16, round to nearest even (finite inputs; NaN stays NaN).
 __device__ __forceinline__ __bf16 to_bf16(float x) { return static_cast<__bf16>(x); }
 
+template <int DV>
 struct Lds {
   __bf16 rt[kL][kPad];    // rt[tau][i]
   __bf16 kt[kL][kPad];    // kt[sigma][i]
   __bf16 kh[kD][kPad];    // kh^T[i][sigma]
-  __bf16 vt[kDV][kPad];   // v^T[j][sigma]
-  __bf16 sp[kDV][kPad];   // (diag(w^32) S)^T[j][i]
+  __bf16 vt[DV][kPad];    // v^T[j][sigma]
+  __bf16 sp[DV][kPad];    // (diag(w^32) S)^T[j][i]
   float dec[kExpN][kD];   // w_i^e
   float beta[kL];
   float u[kD];
   int fallback;
 };
 
-// Exact fp32 recurrence for one (batch, head, value half): lane j < kDV
+// Exact fp32 recurrence for one (batch, head, value slice): lane j < DV
 // keeps the state column s[:, j] in registers.
-__device__ void eagle_recurrent_half(int T, int H, int b, int h, int j0,
+template <int DV>
+__device__ void eagle_recurrent_slice(int T, int H, int b, int h, int j0,
                                      const uint16_t* __restrict__ r,
                                      const uint16_t* __restrict__ k,
                                      const uint16_t* __restrict__ v,
                                      const float* __restrict__ w,
                                      const float* __restrict__ u, float* __restrict__ o,
-                                     Lds& s) {
+                                     Lds<DV>& s) {
   float* s_r = &s.dec[0][0];
   float* s_k = &s.dec[1][0];
   float* s_w = &s.dec[2][0];
@@ -90,7 +93,7 @@ __device__ void eagle_recurrent_half(int T, int H, int b, int h, int j0,
       s_k[tid] = bf16_to_f32(k[off + tid]);
     }
     __syncthreads();
-    if (tid < kDV) {
+    if (tid < DV) {
       const float vj = bf16_to_f32(v[off + j0 + tid]);
       float acc = 0.f, beta = 0.f;
 #pragma unroll
@@ -106,11 +109,12 @@ __device__ void eagle_recurrent_half(int T, int H, int b, int h, int j0,
 }
 
 // One chunk's raw inputs for this thread: token tau = tid/4, dims 16*(tid%4)
-// of r and k, and 8 value dims of this workgroup's half.
+// of r and k, and DV/4 value dims of this workgroup's slice (8 or 4).
 struct ChunkRegs {
   uint4 r0, r1, k0, k1, v0;
 };
 
+template <int DV>
 __device__ __forceinline__ void load_chunk(ChunkRegs& x, int t0, int T, int H, int b, int h,
                                            int j0, const uint16_t* __restrict__ r,
                                            const uint16_t* __restrict__ k,
@@ -125,7 +129,12 @@ __device__ __forceinline__ void load_chunk(ChunkRegs& x, int t0, int T, int H, i
     x.r1 = rp[1];
     x.k0 = kp[0];
     x.k1 = kp[1];
-    x.v0 = *reinterpret_cast<const uint4*>(v + off + j0 + 8 * q4);
+    if constexpr (DV == 32) {
+      x.v0 = *reinterpret_cast<const uint4*>(v + off + j0 + 8 * q4);
+    } else {
+      const uint2 t = *reinterpret_cast<const uint2*>(v + off + j0 + 4 * q4);
+      x.v0 = uint4{t.x, t.y, 0u, 0u};
+    }
   } else {
     x.r0 = x.r1 = x.k0 = x.k1 = x.v0 = uint4{0u, 0u, 0u, 0u};
   }
@@ -145,7 +154,8 @@ struct StageConsts {
   float ur[16];  // u
 };
 
-__device__ __forceinline__ void stage_consts(StageConsts& c, const Lds& s) {
+template <int DV>
+__device__ __forceinline__ void stage_consts(StageConsts& c, const Lds<DV>& s) {
   const int tid = threadIdx.x;
   const int tau = tid >> 2, d0 = 16 * (tid & 3);
 #pragma unroll
@@ -158,7 +168,9 @@ __device__ __forceinline__ void stage_consts(StageConsts& c, const Lds& s) {
 }
 
 // Scale one chunk into LDS: rt, kt, kh^T, v^T, beta.
-__device__ __forceinline__ void stage_chunk(const ChunkRegs& x, const StageConsts& f, Lds& s) {
+template <int DV>
+__device__ __forceinline__ void stage_chunk(const ChunkRegs& x, const StageConsts& f,
+                                            Lds<DV>& s) {
   const int tid = threadIdx.x;
   const int tau = tid >> 2, q4 = tid & 3;
   const int d0 = 16 * q4;
@@ -191,10 +203,11 @@ __device__ __forceinline__ void stage_chunk(const ChunkRegs& x, const StageConst
   *reinterpret_cast<bf16x8*>(&s.kt[tau][d0]) = kt0;
   *reinterpret_cast<bf16x8*>(&s.kt[tau][d0 + 8]) = kt1;
   const uint32_t vw[4] = {x.v0.x, x.v0.y, x.v0.z, x.v0.w};
+  constexpr int VPT = DV / 4;  // value dims per thread
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    s.vt[8 * q4 + 2 * e][tau] = to_bf16(lo_half(vw[e]));
-    s.vt[8 * q4 + 2 * e + 1][tau] = to_bf16(hi_half(vw[e]));
+  for (int e = 0; e < VPT / 2; ++e) {
+    s.vt[VPT * q4 + 2 * e][tau] = to_bf16(lo_half(vw[e]));
+    s.vt[VPT * q4 + 2 * e + 1][tau] = to_bf16(hi_half(vw[e]));
   }
   // the four threads of a token sit in adjacent lanes of one wave
   bpart += __shfl_xor(bpart, 1);
@@ -206,20 +219,23 @@ __device__ __forceinline__ floatx4 mfma(const bf16x8& a, const bf16x8& b, const 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Workgroup: 4 waves; (batch, head, value half).  blockIdx pairs the two
-// halves of a head 8 apart so that they land on the same XCD (dispatch is
-// round-robin over 8 XCDs) and share r, k reads in its L2.
+// Workgroup: 4 waves; (batch, head, slice of DV value columns).  blockIdx
+// places the 64/DV slices of a head 8 apart, so that they land on the same
+// XCD (dispatch is round-robin over 8 XCDs) and share r, k reads in its L2.
+template <int DV>
 __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
     int T, int H, int BH, const uint16_t* __restrict__ r, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ w,
     const float* __restrict__ u, float* __restrict__ o) {
-  __shared__ Lds s;
+  constexpr int NS = kD / DV;  // slices per head
+  constexpr int NJB = DV / 16; // 16-wide value tiles per slice
+  __shared__ Lds<DV> s;
   const int bx = blockIdx.x;
-  const int bh = (bx >> 4) * 8 + (bx & 7);
-  const int half = (bx >> 3) & 1;
+  const int bh = (bx / (8 * NS)) * 8 + (bx & 7);
+  const int slice = (bx >> 3) % NS;
   if (bh >= BH) return;
   const int b = bh / H, h = bh - (bh / H) * H;
-  const int j0 = half * kDV;
+  const int j0 = slice * DV;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int q = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -239,13 +255,15 @@ __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
   }
   __syncthreads();
   if (s.fallback) {
-    eagle_recurrent_half(T, H, b, h, j0, r, k, v, w, u, o, s);
+    eagle_recurrent_slice<DV>(T, H, b, h, j0, r, k, v, w, u, o, s);
     return;
   }
 
   // S' starts at zero; S itself lives in registers (wave q: key rows 16q..).
-  for (int idx = tid; idx < kDV * kPad; idx += 256) (&s.sp[0][0])[idx] = to_bf16(0.f);
-  floatx4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  for (int idx = tid; idx < DV * kPad; idx += 256) (&s.sp[0][0])[idx] = to_bf16(0.f);
+  floatx4 sacc[NJB];
+#pragma unroll
+  for (int jb = 0; jb < NJB; ++jb) sacc[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const int row = lane & 15;         // MFMA operand row/column of this lane
   const int kq = 8 * (lane >> 4);    // first K element of this lane in a 32-wide step
@@ -255,12 +273,12 @@ __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
   stage_consts(f, s);
   const int n_chunks = (T + kL - 1) / kL;
   ChunkRegs cur, nxt;
-  load_chunk(cur, 0, T, H, b, h, j0, r, k, v);
+  load_chunk<DV>(cur, 0, T, H, b, h, j0, r, k, v);
   for (int c = 0; c < n_chunks; ++c) {
     const int t0 = c * kL;
     stage_chunk(cur, f, s);
     __syncthreads();
-    if (c + 1 < n_chunks) load_chunk(nxt, t0 + kL, T, H, b, h, j0, r, k, v);
+    if (c + 1 < n_chunks) load_chunk<DV>(nxt, t0 + kL, T, H, b, h, j0, r, k, v);
 
     // A^T = kt rt^T for sigma blocks 0..q against this wave's 16 tokens:
     // lane holds column tau = 16q + row, rows sigma = 16nb + crow .. +3.
@@ -294,13 +312,15 @@ __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
       }
 
     // O = A' V + rt S'  (16 tokens x 32 value columns per wave).
-    floatx4 oacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    floatx4 oacc[NJB];
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) oacc[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
     const int nks = (q + 2) >> 1;  // 32-wide sigma steps that can be non-zero
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
       if (ks < nks) {
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
+        for (int jb = 0; jb < NJB; ++jb) {
           const __bf16* vr = &s.vt[16 * jb + row][32 * ks + crow];
           typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
           const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
@@ -313,13 +333,13 @@ __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
     for (int ks = 0; ks < 2; ++ks) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.rt[16 * q + row][32 * ks + kq]);
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
+      for (int jb = 0; jb < NJB; ++jb) {
         const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s.sp[16 * jb + row][32 * ks + kq]);
         oacc[jb] = mfma(a, bb, oacc[jb]);
       }
     }
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
+    for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int tau = 16 * q + crow + rr;
@@ -331,14 +351,14 @@ __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const float d64 = s.dec[64 - kExpLo][16 * q + crow + rr];
-      sacc[0][rr] *= d64;
-      sacc[1][rr] *= d64;
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) sacc[jb][rr] *= d64;
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.kh[16 * q + row][32 * ks + kq]);
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
+      for (int jb = 0; jb < NJB; ++jb) {
         const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s.vt[16 * jb + row][32 * ks + kq]);
         sacc[jb] = mfma(a, bb, sacc[jb]);
       }
@@ -348,7 +368,7 @@ __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
     // S' = diag(w^32) S for the next chunk, transposed to [j][i]: a lane's
     // four key rows are adjacent, one 8-byte store per value tile.
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
+    for (int jb = 0; jb < NJB; ++jb) {
       typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
       bf16x4 pk;
 #pragma unroll
@@ -373,9 +393,15 @@ hipError_t wkv5_forward_launch(int64_t B, int64_t T, int64_t H, int64_t D,
   (void)D;
   (void)ws;
   const int64_t BH = B * H;
-  const unsigned grid = unsigned((BH + 7) / 8 * 16);
-  hipLaunchKernelGGL(wkv5_fwd_chunked, dim3(grid), dim3(256), 0, stream, int(T), int(H),
-                     int(BH), r, k, v, w, u, o);
+  int dv = 32;
+  if (const char* env = getenv("RWKV_WKV5_DV")) dv = atoi(env) == 16 ? 16 : 32;
+  const unsigned grid = unsigned((BH + 7) / 8 * 8 * (kD / dv));
+  if (dv == 16)
+    hipLaunchKernelGGL(wkv5_fwd_chunked<16>, dim3(grid), dim3(256), 0, stream, int(T), int(H),
+                       int(BH), r, k, v, w, u, o);
+  else
+    hipLaunchKernelGGL(wkv5_fwd_chunked<32>, dim3(grid), dim3(256), 0, stream, int(T), int(H),
+                       int(BH), r, k, v, w, u, o);
   return hipGetLastError();
 }
 

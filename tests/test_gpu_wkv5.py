@@ -4,6 +4,8 @@ Tolerance: max |o_gpu - o_oracle| / o_abs <= 2e-2, where o_abs is the same
 recurrence over |r|, |k|, |v|, |u| (a bound on |o| that scales the rounding
 error of bf16 products with float32 accumulation).
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -15,13 +17,23 @@ from wkv_testutil import WKV5_TOL, log, to_dev, torch_dev, wkv5_scaled_err
 pytestmark = pytest.mark.gpu
 
 
-def gpu_wkv5(inp):
+def gpu_wkv5(inp, dv=None):
     torch, _ = torch_dev()
-    o = rw.rwkv_wkv5_forward(to_dev(inp["r_bits"], torch.bfloat16),
-                             to_dev(inp["k_bits"], torch.bfloat16),
-                             to_dev(inp["v_bits"], torch.bfloat16),
-                             to_dev(inp["w"]), to_dev(inp["u"]))
-    torch.cuda.synchronize()
+    old = os.environ.get("RWKV_WKV5_DV")
+    if dv is not None:
+        os.environ["RWKV_WKV5_DV"] = str(dv)
+    try:
+        o = rw.rwkv_wkv5_forward(to_dev(inp["r_bits"], torch.bfloat16),
+                                 to_dev(inp["k_bits"], torch.bfloat16),
+                                 to_dev(inp["v_bits"], torch.bfloat16),
+                                 to_dev(inp["w"]), to_dev(inp["u"]))
+        torch.cuda.synchronize()
+    finally:
+        if dv is not None:
+            if old is None:
+                del os.environ["RWKV_WKV5_DV"]
+            else:
+                os.environ["RWKV_WKV5_DV"] = old
     return o.cpu().numpy()
 
 
@@ -35,12 +47,13 @@ def oracle_wkv5(inp, b_idx=None, h_idx=None):
     return o, O.wkv5_scale(r, k, v, w, u)
 
 
-@pytest.mark.parametrize("shape", [(1, 1, 1), (2, 100, 3), (1, 257, 2), (3, 64, 1)])
-def test_small_shapes(shape):
+@pytest.mark.parametrize("dv", [32, 16])
+@pytest.mark.parametrize("shape", [(1, 1, 1), (2, 100, 3), (1, 257, 2), (3, 64, 1), (2, 200, 9)])
+def test_small_shapes(shape, dv):
     B, T, H = shape
-    log(f"wkv5_forward B={B} T={T} H={H} D=64")
+    log(f"wkv5_forward B={B} T={T} H={H} D=64 value slice {dv}")
     inp = synth.wkv5_inputs(B, T, H, 64, seed=40 + T)
-    o = gpu_wkv5(inp)
+    o = gpu_wkv5(inp, dv)
     o_ref, o_abs = oracle_wkv5(inp)
     err = wkv5_scaled_err(o, o_ref, o_abs)
     log(f"  err={err:.3e}")
@@ -61,12 +74,13 @@ def test_eagle_workload_sampled_heads():
     assert np.all(np.isfinite(o))
 
 
-def test_no_decay_and_fast_decay_extremes():
+@pytest.mark.parametrize("dv", [32, 16])
+def test_no_decay_and_fast_decay_extremes(dv):
     B, T, H = 1, 300, 2
     inp = synth.wkv5_inputs(B, T, H, 64, seed=77)
     for name, wv in (("w=1", 1.0), ("w=0.05", 0.05)):
-        log(f"wkv5_forward {name}")
+        log(f"wkv5_forward {name} value slice {dv}")
         case = dict(inp, w=np.full((H, 64), wv, np.float32))
-        o = gpu_wkv5(case)
+        o = gpu_wkv5(case, dv)
         o_ref, o_abs = oracle_wkv5(case)
         assert wkv5_scaled_err(o, o_ref, o_abs) <= WKV5_TOL, name
