@@ -25,15 +25,15 @@
 // Tiles of a channel block are claimed in order from that block's own
 // counter, so a workgroup only ever waits on workgroups that are already
 // running: every wait ends.  Every word the kernel writes to the workspace
-// carries the call's tag (unique and increasing per process), so nothing has
-// to be reset between calls, whatever shapes they have.
+// carries the call's tag, the workspace epoch + 1, which the call that
+// completes advances; nothing is reset between calls whatever their shapes,
+// and launches replayed from a captured graph stay correct.
 #include "wkv_device.h"
 #include "wkv_internal.h"
 
 #include <stdio.h>
 #include <stdlib.h>
 
-#include <atomic>
 
 namespace rwkv {
 
@@ -47,6 +47,19 @@ constexpr int kWin = 16;
 
 __device__ __forceinline__ void raise_error(uint32_t* err, uint32_t bit) {
   __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Header words (uint32) at the start of the forward workspace.
+enum : int { kHdrError = 0, kHdrEpoch = 1, kHdrClaimed = 2 };
+
+__device__ __forceinline__ uint32_t hdr_load(uint32_t* h, int i) {
+  return __hip_atomic_load(h + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void hdr_store(uint32_t* h, int i, uint32_t x) {
+  __hip_atomic_store(h + i, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t hdr_add(uint32_t* h, int i, uint32_t x) {
+  return __hip_atomic_fetch_add(h + i, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // CPL adjacent floats of one row, loaded/stored with a single vector access.
@@ -118,14 +131,15 @@ struct HistLds {
 
 template <int CPL, int L, int NW>
 __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
-    int T, int C, int n_cblk, int groups, int n_tiles, uint32_t tag,
+    int T, int C, int n_cblk, int groups, int n_tiles,
     const float* __restrict__ w, const float* __restrict__ u,
     const float* __restrict__ k, const float* __restrict__ v, float* __restrict__ y,
-    uint32_t* __restrict__ err, uint64_t* __restrict__ counters, uint64_t* __restrict__ slots) {
+    uint32_t* __restrict__ hdr, uint64_t* __restrict__ counters, uint64_t* __restrict__ slots) {
   constexpr int W = 64 * CPL;        // channels per block
   constexpr int TILE = L * NW;       // tokens per tile
   constexpr int SLOT = 8 * W;        // words per (tile, block): agg A,B,kr,n then inc A,B,kr,n
   __shared__ int s_tile;
+  __shared__ uint32_t s_tag;
   __shared__ HistLds<W> s_sum[NW];
   __shared__ HistLds<W> s_pre;
 
@@ -133,21 +147,46 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = int(blockIdx.x) % groups;
   if (threadIdx.x == 0) {
-    // Claim the next tile of this block.  The counter word is {tag, count}:
-    // raising it to {tag, 0} first makes whatever an earlier call (of any
-    // shape) left there harmless, as every earlier tag is smaller.
+    // The call's tag is the workspace epoch + 1 (read on the device, so a
+    // launch replayed from a captured graph still gets a fresh tag).  Claim
+    // the next tile of this block from its counter word {tag, count}.
+    const uint32_t tg = hdr_load(hdr, kHdrEpoch) + 1u;
     uint64_t* ctr = counters + size_t(g) * (kWkv4CounterStride / sizeof(uint64_t));
-    __hip_atomic_fetch_max(ctr, uint64_t(tag) << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t old =
-        __hip_atomic_fetch_add(ctr, uint64_t(1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_tile = uint32_t(old >> 32) == tag ? int(uint32_t(old)) : -1;
+    // The claim must not be performed before the epoch read has returned
+    // (else this workgroup could see an epoch advanced after its claim): tie
+    // the increment to the loaded value.
+    uint64_t one = 1;
+    asm volatile("" : "+v"(one) : "v"(tg));
+    uint64_t old = __hip_atomic_fetch_add(ctr, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (uint32_t(old >> 32) != tg) {
+      // The word is left over from a call of another shape: raise it to
+      // {tag, 0} (earlier tags are smaller) and claim again.
+      __hip_atomic_fetch_max(ctr, uint64_t(tg) << 32, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      old = __hip_atomic_fetch_add(ctr, uint64_t(1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const int t = uint32_t(old >> 32) == tg ? int(uint32_t(old)) : -1;
+    if (t == n_tiles - 1) {
+      // Every tile of this block is claimed: prime the counter for the next
+      // call, and the block that completes all claims advances the epoch
+      // (every workgroup of this call has read it by then).
+      __hip_atomic_store(ctr, uint64_t(tg + 1u) << 32, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      if (hdr_add(hdr, kHdrClaimed, 1u) == uint32_t(groups - 1)) {
+        hdr_store(hdr, kHdrClaimed, 0u);
+        hdr_store(hdr, kHdrEpoch, tg);
+      }
+    }
+    s_tile = t;
+    s_tag = tg;
   }
   __syncthreads();
   const int tile = __builtin_amdgcn_readfirstlane(s_tile);
+  const uint32_t tag = __builtin_amdgcn_readfirstlane(s_tag);
   // Only a workspace that was never zero-filled can get here: flag it and
   // touch nothing.
   if (tile < 0 || tile >= n_tiles) {
-    if (threadIdx.x == 0) raise_error(err, 2u);
+    if (threadIdx.x == 0) raise_error(hdr + kHdrError, 2u);
     return;
   }
   const int bi = g / n_cblk;
@@ -275,7 +314,7 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
         if (found) break;
         if (folded == 0) {
           if (++spins > kSpinLimit) {
-            if (lane == 0) raise_error(err, 1u);
+            if (lane == 0) raise_error(hdr + kHdrError, 1u);
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
               const float nan = __builtin_nanf("");
@@ -393,29 +432,18 @@ constexpr Variant kVariants[] = {{4, 8, 8}, {4, 16, 4}, {4, 16, 8},
                                  {2, 16, 8}, {2, 32, 4}, {2, 16, 4},
                                  {1, 32, 8}, {1, 32, 4}, {1, 64, 1}, {1, 16, 4}};
 
-// Launch tags: unique and increasing per call in this process, never 0 (the
-// tag of a zero-filled workspace word), so a word left by an earlier call can
-// never pass for one of this call.
-std::atomic<uint32_t> g_launch_tag{0};
-
-uint32_t next_tag() {
-  uint32_t t = g_launch_tag.fetch_add(1, std::memory_order_relaxed) + 1u;
-  if (t == 0) t = g_launch_tag.fetch_add(1, std::memory_order_relaxed) + 1u;
-  return t;
-}
-
 template <int CPL, int L, int NW>
 hipError_t launch_tiled(const Wkv4Plan& pl, int64_t T, int64_t C, const float* w,
                         const float* u, const float* k, const float* v, float* y, void* ws,
                         hipStream_t stream) {
   char* base = static_cast<char*>(ws);
-  uint32_t* err = reinterpret_cast<uint32_t*>(base);
+  uint32_t* hdr = reinterpret_cast<uint32_t*>(base);
   uint64_t* counters = reinterpret_cast<uint64_t*>(base + kWkv4HeaderBytes);
   uint64_t* slots = reinterpret_cast<uint64_t*>(base + pl.slots_offset);
   const unsigned grid = unsigned(pl.n_tiles * pl.groups);
   hipLaunchKernelGGL((wkv4_fwd_tiled<CPL, L, NW>), dim3(grid), dim3(64 * NW), 0, stream,
                      int(T), int(C), int(pl.n_cblk), int(pl.groups), int(pl.n_tiles),
-                     next_tag(), w, u, k, v, y, err, counters, slots);
+                     w, u, k, v, y, hdr, counters, slots);
   return hipGetLastError();
 }
 

@@ -165,6 +165,42 @@ def test_workspace_layout_changes():
             assert wkv4_scaled_err(gpu_forward(inp), y_ref, S) <= WKV4_TOL, shp
 
 
+def test_forward_replayed_from_captured_graph():
+    """Calls captured in a HIP graph and replayed must still see fresh
+    workspace tags: replay several times, with eager calls on the same
+    workspace and new inputs in between, and check every replay."""
+    torch, dev = torch_dev()
+    shapes = [(2, 900, 96), (1, 1500, 320)]
+    inps = [synth.wkv4_inputs(B, T, C, seed=60 + i) for i, (B, T, C) in enumerate(shapes)]
+    alts = [synth.wkv4_inputs(B, T, C, seed=70 + i) for i, (B, T, C) in enumerate(shapes)]
+    need = max(rw.rwkv_wkv4_forward_workspace(*shp) for shp in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    bufs = [{n: to_dev(inp[n]) for n in ("w", "u", "k", "v")} for inp in inps]
+    ys = [torch.empty_like(bf["k"]) for bf in bufs]
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.graph(graph, stream=side):
+        for bf, y in zip(bufs, ys):
+            rw.rwkv_wkv4_forward(bf["w"], bf["u"], bf["k"], bf["v"], y=y, ws=ws)
+    torch.cuda.synchronize()
+    for rnd in range(4):
+        src = inps if rnd % 2 == 0 else alts
+        for bf, inp in zip(bufs, src):
+            for n in ("w", "u", "k", "v"):
+                bf[n].copy_(to_dev(inp[n]))
+        # eager calls on the same workspace between replays
+        for bf, y in zip(bufs, ys):
+            rw.rwkv_wkv4_forward(bf["w"], bf["u"], bf["k"], bf["v"], ws=ws)
+        torch.cuda.synchronize()
+        log(f"wkv4_forward graph replay {rnd}")
+        graph.replay()
+        torch.cuda.synchronize()
+        for y, inp in zip(ys, src):
+            y_ref, S = oracle_forward(inp)
+            assert wkv4_scaled_err(y.cpu().numpy(), y_ref, S) <= WKV4_TOL, rnd
+
+
 # ------------------------------------------------------------------ step ---
 
 def _run_steps(inp, n_steps, pool=None):
