@@ -105,8 +105,17 @@ def bench_wkv4_forward(torch, rw, cfg, steps, warmup, rotate):
     for i in range(warmup):
         assert fn(*calls[i % rotate]) == 0
     torch.cuda.synchronize()
+    # Timed region: K launches back to back, bracketed by two events.
     tm = Timer(torch, steps)
     tm.start.record(stream)
+    for i in range(steps):
+        st = fn(*calls[i % rotate])
+        if st != 0:
+            raise RuntimeError(f"rwkv_wkv4_forward status {st}")
+    tm.end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = tm.start.elapsed_time(tm.end)
+    # Kernel duration: the same K launches again, each between an event pair.
     for i in range(steps):
         s, e = tm.pairs[i]
         s.record(stream)
@@ -114,9 +123,7 @@ def bench_wkv4_forward(torch, rw, cfg, steps, warmup, rotate):
         e.record(stream)
         if st != 0:
             raise RuntimeError(f"rwkv_wkv4_forward status {st}")
-    tm.end.record(stream)
     torch.cuda.synchronize()
-    total_ms = tm.start.elapsed_time(tm.end)
     kern_ms = sum(s.elapsed_time(e) for s, e in tm.pairs) / steps
     # sanity: the output of the last launch is finite and the first token is v
     y_last = ys[(steps - 1) % rotate]
@@ -219,6 +226,69 @@ def bench_wkv5(torch, rw, cfg, reps):
     return {"ms": ms, "elems": elems, "bytes": 10 * elems, "flops": 4 * cfg.D * elems}
 
 
+def _cpu_name():
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return cpu
+
+
+def cpu_sample_long(budget_s=4.0):
+    """Oracle on channels of the long-sequence workload, over the full T."""
+    import numpy as np
+    import oracle.wkv_oracle as O
+    import synth
+    cfg = synth.CFG_WKV4_LONG
+    inp = synth.wkv4_inputs(1, cfg.T, 64, cfg.seed, omega_lo=cfg.omega_lo, omega_hi=cfg.omega_hi,
+                            u_std=cfg.u_std, k_std=cfg.k_std)
+    t0 = time.perf_counter()
+    O.wkv4_recurrent(inp["w"], inp["u"], inp["k"], inp["v"])
+    el = time.perf_counter() - t0
+    elems = cfg.T * 64
+    del np
+    return {"value": round(12 * elems / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"64 channels x T={cfg.T} of the same distributions, {el:.1f} s"}
+
+
+def cpu_sample_decode():
+    """Oracle steps for 16384 (stream, channel) lanes over 512 steps."""
+    import numpy as np
+    import oracle.wkv_oracle as O
+    rng = np.random.default_rng(7)
+    L, N = 16384, 512
+    w = np.exp(rng.uniform(-3, 1, L)).astype(np.float32)
+    u = (rng.standard_normal(L) * 0.5).astype(np.float32)
+    k = rng.standard_normal((N, 1, L)).astype(np.float32)
+    v = rng.standard_normal((N, 1, L)).astype(np.float32)
+    st = O.wkv4_empty_state(1, L)
+    t0 = time.perf_counter()
+    for t in range(N):
+        _, st = O.wkv4_step(st, w, u, k[t], v[t])
+    el = time.perf_counter() - t0
+    elems = L * N
+    return {"value": round(36 * elems / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{L} lanes x {N} steps, {el:.1f} s"}
+
+
+def cpu_sample_eagle():
+    """Oracle recurrence for 2 (batch, head) pairs over the full T."""
+    import oracle.wkv_oracle as O
+    import synth
+    cfg = synth.CFG_WKV5_EAGLE
+    inp = synth.wkv5_inputs(1, cfg.T, 2, cfg.D, cfg.seed)
+    t0 = time.perf_counter()
+    O.wkv5_recurrent(inp["r"], inp["k"], inp["v"], inp["w"], inp["u"])
+    el = time.perf_counter() - t0
+    elems = cfg.T * 2 * cfg.D
+    return {"value": round(10 * elems / el / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"2 heads x T={cfg.T} x D={cfg.D}, {el:.1f} s"}
+
+
 def cpu_baseline(cfg, budget_s):
     """The fp64 oracle's recurrence on the full workload, repeated for about
     `budget_s` seconds of host time."""
@@ -234,15 +304,7 @@ def cpu_baseline(cfg, budget_s):
         if el >= budget_s:
             break
     elems = cfg.B * cfg.T * cfg.C * reps
-    cpu = platform.processor() or platform.machine()
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    cpu = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
+    cpu = _cpu_name()
     del np
     return {"value": round(12 * elems / el / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
@@ -350,6 +412,13 @@ def main(argv=None):
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
+        sec = line.get("secondary", {})
+        samplers = {synth.CFG_WKV4_LONG.name: cpu_sample_long,
+                    synth.CFG_WKV4_DECODE.name: cpu_sample_decode,
+                    synth.CFG_WKV5_EAGLE.name: cpu_sample_eagle}
+        for name, fn in samplers.items():
+            if name in sec:
+                sec[name]["cpu_baseline"] = fn()
 
     print(json.dumps(line), flush=True)
     return 0

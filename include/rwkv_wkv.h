@@ -101,6 +101,30 @@ int rwkv_wkv4_state_init(int64_t B, int64_t C, float* a, float* b, float* p,
                          hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * RWKV-4 forward continuing from, and handing on, a recurrent state.
+ * [RWKV-digest] (2) Time-mixing: the recurrent form carries the whole
+ * history in (a, b), so a sequence may be cut anywhere and resumed.
+ *
+ * As rwkv_wkv4_forward, except that the history before token 0 is the state
+ * (a_in, b_in, p_in) instead of empty, and the state after token T-1 is
+ * written to (a_out, b_out, p_out), in the representation described for
+ * rwkv_wkv4_state_init below.  Each triple is given whole or left NULL
+ * (RWKV_ERR_NULLPTR if only part of one is given): a NULL input triple means
+ * the empty history, a NULL output triple means the state is not wanted.
+ * The output triple may be the input triple (update in place); otherwise the
+ * state arrays must not overlap each other or k, v, y.  With both NULL this
+ * is rwkv_wkv4_forward.  The same workspace rules and accuracy apply, the
+ * scale S then including the state's terms.
+ * ---------------------------------------------------------------------- */
+int rwkv_wkv4_forward_state(int64_t B, int64_t T, int64_t C,
+                            const float* w, const float* u,
+                            const float* k, const float* v,
+                            float* y,
+                            const float* a_in, const float* b_in, const float* p_in,
+                            float* a_out, float* b_out, float* p_out,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * RWKV-4 fused single-token step.   [RWKV-digest] (2) Time-mixing:
  *   y = (a_{t-1} + e^{u+k} v) / (b_{t-1} + e^{u+k})   using the OLD state,
  * then the state advances in place with this token's k, v.
@@ -142,6 +166,45 @@ int rwkv_wkv5_forward(int64_t B, int64_t T, int64_t H, int64_t D,
                       const float* w, const float* u,
                       float* o,
                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Eagle forward continuing from, and handing on, a matrix state.
+ * [Eagle-Finch] "Eagle": the state s carries the whole history.
+ *
+ * As rwkv_wkv5_forward, except that s starts at s_in instead of zero, and
+ * the state after the last token (s_T) is written to s_out.
+ *   s_in, s_out  [B,H,D,D]  float32, s[b,h,i,j] = s[i][j] of (b, h); either
+ *                           may be NULL (start at zero / not wanted).  s_out
+ *                           may equal s_in (update in place); otherwise it
+ *                           must not overlap any other argument.
+ * With T = 0 nothing is enqueued (s_out is not written).  Accuracy as for
+ * rwkv_wkv5_forward with |s_in| included in o_abs; s_out meets the same
+ * bound against the state of that magnitude recurrence.
+ * ---------------------------------------------------------------------- */
+int rwkv_wkv5_forward_state(int64_t B, int64_t T, int64_t H, int64_t D,
+                            const uint16_t* r, const uint16_t* k, const uint16_t* v,
+                            const float* w, const float* u,
+                            float* o,
+                            const float* s_in, float* s_out,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Eagle single-token step.   [Eagle-Finch] "Eagle": one application of
+ *   o = r (s + diag(u) k^T v),   s <- diag(w) s + k^T v.
+ *
+ *   s        [B,H,D,D]  float32 state, read and updated in place
+ *   r, k, v  [B,H,D]    bfloat16 bit patterns of this token
+ *   w, u     [H,D]      float32 as for the forward
+ *   o        [B,H,D]    float32 output
+ *   D must be 64.  Exact float32 arithmetic on the bf16 inputs; T steps
+ *   from a zero state match rwkv_wkv5_forward over the same T tokens within
+ *   the forward's bound.
+ * ---------------------------------------------------------------------- */
+int rwkv_wkv5_step(int64_t B, int64_t H, int64_t D,
+                   float* s,
+                   const uint16_t* r, const uint16_t* k, const uint16_t* v,
+                   const float* w, const float* u,
+                   float* o, hipStream_t stream);
 
 #ifdef __cplusplus
 }

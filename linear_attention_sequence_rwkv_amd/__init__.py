@@ -39,11 +39,16 @@ _SIGNATURES = {
     "rwkv_last_hip_error": (ctypes.c_int, []),
     "rwkv_wkv4_forward_workspace": (_sz, [_i64, _i64, _i64]),
     "rwkv_wkv4_forward": (ctypes.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "rwkv_wkv4_forward_state": (ctypes.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _p,
+                                               _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "rwkv_wkv4_state_init": (ctypes.c_int, [_i64, _i64, _p, _p, _p, _p]),
     "rwkv_wkv4_step": (ctypes.c_int, [_i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "rwkv_wkv5_forward_workspace": (_sz, [_i64, _i64, _i64, _i64]),
     "rwkv_wkv5_forward": (ctypes.c_int,
                           [_i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "rwkv_wkv5_forward_state": (ctypes.c_int, [_i64, _i64, _i64, _i64, _p, _p, _p, _p, _p,
+                                               _p, _p, _p, _p, _sz, _p]),
+    "rwkv_wkv5_step": (ctypes.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p]),
 }
 
 
@@ -154,15 +159,8 @@ def rwkv_wkv4_forward_workspace(B: int, T: int, C: int) -> int:
     return int(load_library().rwkv_wkv4_forward_workspace(B, T, C))
 
 
-def rwkv_wkv4_forward(w, u, k, v, y=None, ws=None, stream=None):
-    """y[B,T,C] = WKV(w, u, k, v); see rwkv_wkv4_forward in rwkv_wkv.h.
-
-    ``ws`` (optional) is a caller-owned zero-initialised uint8 GPU tensor of at
-    least rwkv_wkv4_forward_workspace(B, T, C) bytes; by default a cached one
-    per (device, stream) is used.
-    """
+def _wkv4_forward_args(w, u, k, v, y):
     torch = _torch()
-    lib = load_library()
     f32 = (torch.float32,)
     k = _dev_tensor("k", k, f32, 3)
     v = _dev_tensor("v", v, f32, 3)
@@ -177,15 +175,71 @@ def rwkv_wkv4_forward(w, u, k, v, y=None, ws=None, stream=None):
         y = _dev_tensor("y", y, f32, 3)
         if tuple(y.shape) != (B, T, C):
             raise ValueError("y has the wrong shape")
-    st = _stream(k.device, stream)
+    return w, u, k, v, y
+
+
+def _wkv4_ws(lib, k, ws, st):
+    B, T, C = k.shape
     need = lib.rwkv_wkv4_forward_workspace(B, T, C)
     if ws is None:
         ws = _workspace("wkv4", k.device, st.value or 0, need)
-    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    return ws, (0 if ws is None else ws.numel() * ws.element_size())
+
+
+def rwkv_wkv4_forward(w, u, k, v, y=None, ws=None, stream=None):
+    """y[B,T,C] = WKV(w, u, k, v); see rwkv_wkv4_forward in rwkv_wkv.h.
+
+    ``ws`` (optional) is a caller-owned zero-initialised uint8 GPU tensor of at
+    least rwkv_wkv4_forward_workspace(B, T, C) bytes; by default a cached one
+    per (device, stream) is used.
+    """
+    lib = load_library()
+    w, u, k, v, y = _wkv4_forward_args(w, u, k, v, y)
+    B, T, C = k.shape
+    st = _stream(k.device, stream)
+    ws, nbytes = _wkv4_ws(lib, k, ws, st)
     status = lib.rwkv_wkv4_forward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
                                    _ptr(ws), nbytes, st)
     _check("rwkv_wkv4_forward", status)
     return y
+
+
+def _wkv4_state_args(name, state, B, C):
+    torch = _torch()
+    if len(state) != 3:
+        raise ValueError(f"{name} must be a triple (a, b, p)")
+    out = tuple(_dev_tensor(f"{name}[{i}]", t, (torch.float32,), 2) for i, t in enumerate(state))
+    for t in out:
+        if tuple(t.shape) != (B, C):
+            raise ValueError(f"{name} arrays must be [B, C] = [{B}, {C}]")
+    return out
+
+
+def rwkv_wkv4_forward_state(w, u, k, v, state_in=None, state_out=None, y=None, ws=None,
+                            stream=None):
+    """Forward from the history ``state_in`` (a, b, p) or empty if None.
+
+    ``state_out``: None (final state not wanted), True (allocate), or a triple
+    of float32 [B, C] tensors to write (may be ``state_in`` itself).  Returns
+    (y, state_out).
+    """
+    torch = _torch()
+    lib = load_library()
+    w, u, k, v, y = _wkv4_forward_args(w, u, k, v, y)
+    B, T, C = k.shape
+    sin = (None, None, None) if state_in is None else _wkv4_state_args("state_in", state_in, B, C)
+    if state_out is True:
+        state_out = tuple(torch.empty((B, C), dtype=torch.float32, device=k.device)
+                          for _ in range(3))
+    sout = (None, None, None) if state_out is None else _wkv4_state_args("state_out", state_out,
+                                                                        B, C)
+    st = _stream(k.device, stream)
+    ws, nbytes = _wkv4_ws(lib, k, ws, st)
+    status = lib.rwkv_wkv4_forward_state(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
+                                         *(_ptr(t) for t in sin), *(_ptr(t) for t in sout),
+                                         _ptr(ws), nbytes, st)
+    _check("rwkv_wkv4_forward_state", status)
+    return y, (None if state_out is None else sout)
 
 
 def rwkv_wkv4_state_init(B: int, C: int, device="cuda", stream=None):
@@ -219,6 +273,8 @@ def rwkv_wkv4_step(a, b, p, w, u, k, v, y=None, stream=None):
         y = torch.empty_like(k)
     else:
         y = _dev_tensor("y", y, f32, 2)
+        if tuple(y.shape) != (B, C):
+            raise ValueError("y has the wrong shape")
     status = lib.rwkv_wkv4_step(B, C, _ptr(a), _ptr(b), _ptr(p), _ptr(w), _ptr(u), _ptr(k),
                                 _ptr(v), _ptr(y), _stream(a.device, stream))
     _check("rwkv_wkv4_step", status)
@@ -231,31 +287,94 @@ def rwkv_wkv5_forward_workspace(B: int, T: int, H: int, D: int) -> int:
     return int(load_library().rwkv_wkv5_forward_workspace(B, T, H, D))
 
 
-def rwkv_wkv5_forward(r, k, v, w, u, o=None, ws=None, stream=None):
-    """o[B,T,H,D] float32 from bf16 r, k, v [B,T,H,D] and float32 w, u [H,D]."""
+def _wkv5_args(r, k, v, w, u, o, ndim):
     torch = _torch()
-    lib = load_library()
     half = (torch.bfloat16, torch.int16, torch.uint16)
-    r = _dev_tensor("r", r, half, 4)
-    k = _dev_tensor("k", k, half, 4)
-    v = _dev_tensor("v", v, half, 4)
+    r = _dev_tensor("r", r, half, ndim)
+    k = _dev_tensor("k", k, half, ndim)
+    v = _dev_tensor("v", v, half, ndim)
     w = _dev_tensor("w", w, (torch.float32,), 2)
     u = _dev_tensor("u", u, (torch.float32,), 2)
-    B, T, H, D = r.shape
-    if tuple(k.shape) != (B, T, H, D) or tuple(v.shape) != (B, T, H, D):
+    shape = tuple(r.shape)
+    H, D = shape[-2], shape[-1]
+    if tuple(k.shape) != shape or tuple(v.shape) != shape:
         raise ValueError("r, k, v shapes differ")
     if tuple(w.shape) != (H, D) or tuple(u.shape) != (H, D):
         raise ValueError("w, u must be [H, D]")
     if o is None:
-        o = torch.empty((B, T, H, D), dtype=torch.float32, device=r.device)
+        o = torch.empty(shape, dtype=torch.float32, device=r.device)
     else:
-        o = _dev_tensor("o", o, (torch.float32,), 4)
-    st = _stream(r.device, stream)
+        o = _dev_tensor("o", o, (torch.float32,), ndim)
+        if tuple(o.shape) != shape:
+            raise ValueError("o has the wrong shape")
+    return r, k, v, w, u, o
+
+
+def _wkv5_ws(lib, r, ws, st):
+    B, T, H, D = r.shape
     need = lib.rwkv_wkv5_forward_workspace(B, T, H, D)
     if ws is None:
         ws = _workspace("wkv5", r.device, st.value or 0, need)
-    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    return ws, (0 if ws is None else ws.numel() * ws.element_size())
+
+
+def rwkv_wkv5_forward(r, k, v, w, u, o=None, ws=None, stream=None):
+    """o[B,T,H,D] float32 from bf16 r, k, v [B,T,H,D] and float32 w, u [H,D]."""
+    lib = load_library()
+    r, k, v, w, u, o = _wkv5_args(r, k, v, w, u, o, 4)
+    B, T, H, D = r.shape
+    st = _stream(r.device, stream)
+    ws, nbytes = _wkv5_ws(lib, r, ws, st)
     status = lib.rwkv_wkv5_forward(B, T, H, D, _ptr(r), _ptr(k), _ptr(v), _ptr(w), _ptr(u),
                                    _ptr(o), _ptr(ws), nbytes, st)
     _check("rwkv_wkv5_forward", status)
+    return o
+
+
+def _wkv5_state_arg(name, s, B, H, D):
+    torch = _torch()
+    s = _dev_tensor(name, s, (torch.float32,), 4)
+    if tuple(s.shape) != (B, H, D, D):
+        raise ValueError(f"{name} must be [B, H, D, D] = [{B}, {H}, {D}, {D}]")
+    return s
+
+
+def rwkv_wkv5_forward_state(r, k, v, w, u, s_in=None, s_out=None, o=None, ws=None,
+                            stream=None):
+    """Eagle forward from the state ``s_in`` [B,H,D,D] (zero if None).
+
+    ``s_out``: None (not wanted), True (allocate) or a float32 [B,H,D,D]
+    tensor (may be ``s_in``).  Returns (o, s_out).
+    """
+    torch = _torch()
+    lib = load_library()
+    r, k, v, w, u, o = _wkv5_args(r, k, v, w, u, o, 4)
+    B, T, H, D = r.shape
+    if s_in is not None:
+        s_in = _wkv5_state_arg("s_in", s_in, B, H, D)
+    if s_out is True:
+        s_out = torch.empty((B, H, D, D), dtype=torch.float32, device=r.device)
+    if s_out is not None:
+        s_out = _wkv5_state_arg("s_out", s_out, B, H, D)
+    st = _stream(r.device, stream)
+    ws, nbytes = _wkv5_ws(lib, r, ws, st)
+    status = lib.rwkv_wkv5_forward_state(B, T, H, D, _ptr(r), _ptr(k), _ptr(v), _ptr(w),
+                                         _ptr(u), _ptr(o), _ptr(s_in), _ptr(s_out), _ptr(ws),
+                                         nbytes, st)
+    _check("rwkv_wkv5_forward_state", status)
+    return o, s_out
+
+
+def rwkv_wkv5_step(s, r, k, v, w, u, o=None, stream=None):
+    """One Eagle token: r, k, v [B,H,D] bf16; s [B,H,D,D] updated in place.
+
+    Returns o [B,H,D] float32.
+    """
+    lib = load_library()
+    r, k, v, w, u, o = _wkv5_args(r, k, v, w, u, o, 3)
+    B, H, D = r.shape
+    s = _wkv5_state_arg("s", s, B, H, D)
+    status = lib.rwkv_wkv5_step(B, H, D, _ptr(s), _ptr(r), _ptr(k), _ptr(v), _ptr(w), _ptr(u),
+                                _ptr(o), _stream(r.device, stream))
+    _check("rwkv_wkv5_step", status)
     return o

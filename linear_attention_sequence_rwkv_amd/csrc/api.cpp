@@ -73,14 +73,24 @@ RWKV_API size_t rwkv_wkv4_forward_workspace(int64_t B, int64_t T, int64_t C) {
   return plan.ws_bytes;
 }
 
-RWKV_API int rwkv_wkv4_forward(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
-                               const float* k, const float* v, float* y, void* ws,
-                               size_t ws_bytes, hipStream_t stream) {
+namespace {
+
+int wkv4_forward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                      const float* k, const float* v, float* y, const float* a_in,
+                      const float* b_in, const float* p_in, float* a_out, float* b_out,
+                      float* p_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   int64_t n;
   if (!dims_ok({B, T, C}, &n)) return RWKV_ERR_SHAPE;
   if (n == 0) return RWKV_OK;
   if (!w || !u || !k || !v || !y) return RWKV_ERR_NULLPTR;
   if (!aligned16(w) || !aligned16(u) || !aligned16(k) || !aligned16(v) || !aligned16(y))
+    return RWKV_ERR_ALIGN;
+  // A state triple is given whole or not at all.
+  const int n_in = (a_in != nullptr) + (b_in != nullptr) + (p_in != nullptr);
+  const int n_out = (a_out != nullptr) + (b_out != nullptr) + (p_out != nullptr);
+  if ((n_in != 0 && n_in != 3) || (n_out != 0 && n_out != 3)) return RWKV_ERR_NULLPTR;
+  if ((a_in && (!aligned16(a_in) || !aligned16(b_in) || !aligned16(p_in))) ||
+      (a_out && (!aligned16(a_out) || !aligned16(b_out) || !aligned16(p_out))))
     return RWKV_ERR_ALIGN;
   rwkv::Wkv4Plan plan;
   if (!rwkv::wkv4_plan(B, T, C, &plan)) return RWKV_ERR_UNSUPPORTED;
@@ -88,7 +98,26 @@ RWKV_API int rwkv_wkv4_forward(int64_t B, int64_t T, int64_t C, const float* w, 
     if (!ws || ws_bytes < plan.ws_bytes) return RWKV_ERR_WORKSPACE;
     if (!aligned16(ws)) return RWKV_ERR_ALIGN;
   }
-  return hip_status(rwkv::wkv4_forward_launch(plan, B, T, C, w, u, k, v, y, ws, stream));
+  return hip_status(rwkv::wkv4_forward_launch(plan, B, T, C, w, u, k, v, y, ws, a_in, b_in,
+                                              p_in, a_out, b_out, p_out, stream));
+}
+
+}  // namespace
+
+RWKV_API int rwkv_wkv4_forward(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                               const float* k, const float* v, float* y, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  return wkv4_forward_impl(B, T, C, w, u, k, v, y, nullptr, nullptr, nullptr, nullptr, nullptr,
+                           nullptr, ws, ws_bytes, stream);
+}
+
+RWKV_API int rwkv_wkv4_forward_state(int64_t B, int64_t T, int64_t C, const float* w,
+                                     const float* u, const float* k, const float* v, float* y,
+                                     const float* a_in, const float* b_in, const float* p_in,
+                                     float* a_out, float* b_out, float* p_out, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  return wkv4_forward_impl(B, T, C, w, u, k, v, y, a_in, b_in, p_in, a_out, b_out, p_out, ws,
+                           ws_bytes, stream);
 }
 
 RWKV_API int rwkv_wkv4_state_init(int64_t B, int64_t C, float* a, float* b, float* p,
@@ -123,10 +152,12 @@ RWKV_API size_t rwkv_wkv5_forward_workspace(int64_t B, int64_t T, int64_t H, int
   return rwkv::wkv5_workspace_bytes(B, T, H, D);
 }
 
-RWKV_API int rwkv_wkv5_forward(int64_t B, int64_t T, int64_t H, int64_t D, const uint16_t* r,
-                               const uint16_t* k, const uint16_t* v, const float* w,
-                               const float* u, float* o, void* ws, size_t ws_bytes,
-                               hipStream_t stream) {
+namespace {
+
+int wkv5_forward_impl(int64_t B, int64_t T, int64_t H, int64_t D, const uint16_t* r,
+                      const uint16_t* k, const uint16_t* v, const float* w, const float* u,
+                      float* o, const float* s_in, float* s_out, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
   int64_t n;
   if (!dims_ok({B, T, H, D}, &n)) return RWKV_ERR_SHAPE;
   if (n == 0) return RWKV_OK;
@@ -134,12 +165,46 @@ RWKV_API int rwkv_wkv5_forward(int64_t B, int64_t T, int64_t H, int64_t D, const
   if (T >= (int64_t(1) << 31) || B * H >= (int64_t(1) << 31)) return RWKV_ERR_UNSUPPORTED;
   if (!r || !k || !v || !w || !u || !o) return RWKV_ERR_NULLPTR;
   if (!aligned16(r) || !aligned16(k) || !aligned16(v) || !aligned16(w) || !aligned16(u) ||
-      !aligned16(o))
+      !aligned16(o) || (s_in && !aligned16(s_in)) || (s_out && !aligned16(s_out)))
     return RWKV_ERR_ALIGN;
   const size_t need = rwkv::wkv5_workspace_bytes(B, T, H, D);
   if (need > 0) {
     if (!ws || ws_bytes < need) return RWKV_ERR_WORKSPACE;
     if (!aligned16(ws)) return RWKV_ERR_ALIGN;
   }
-  return hip_status(rwkv::wkv5_forward_launch(B, T, H, D, r, k, v, w, u, o, ws, stream));
+  return hip_status(
+      rwkv::wkv5_forward_launch(B, T, H, D, r, k, v, w, u, o, ws, s_in, s_out, stream));
+}
+
+}  // namespace
+
+RWKV_API int rwkv_wkv5_forward(int64_t B, int64_t T, int64_t H, int64_t D, const uint16_t* r,
+                               const uint16_t* k, const uint16_t* v, const float* w,
+                               const float* u, float* o, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  return wkv5_forward_impl(B, T, H, D, r, k, v, w, u, o, nullptr, nullptr, ws, ws_bytes,
+                           stream);
+}
+
+RWKV_API int rwkv_wkv5_forward_state(int64_t B, int64_t T, int64_t H, int64_t D,
+                                     const uint16_t* r, const uint16_t* k, const uint16_t* v,
+                                     const float* w, const float* u, float* o,
+                                     const float* s_in, float* s_out, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  return wkv5_forward_impl(B, T, H, D, r, k, v, w, u, o, s_in, s_out, ws, ws_bytes, stream);
+}
+
+RWKV_API int rwkv_wkv5_step(int64_t B, int64_t H, int64_t D, float* s, const uint16_t* r,
+                            const uint16_t* k, const uint16_t* v, const float* w,
+                            const float* u, float* o, hipStream_t stream) {
+  int64_t n;
+  if (!dims_ok({B, H, D}, &n)) return RWKV_ERR_SHAPE;
+  if (n == 0) return RWKV_OK;
+  if (D != 64) return RWKV_ERR_UNSUPPORTED;
+  if (B * H >= (int64_t(1) << 31)) return RWKV_ERR_UNSUPPORTED;
+  if (!s || !r || !k || !v || !w || !u || !o) return RWKV_ERR_NULLPTR;
+  if (!aligned16(s) || !aligned16(r) || !aligned16(k) || !aligned16(v) || !aligned16(w) ||
+      !aligned16(u) || !aligned16(o))
+    return RWKV_ERR_ALIGN;
+  return hip_status(rwkv::wkv5_step_launch(B, H, s, r, k, v, w, u, o, stream));
 }

@@ -114,6 +114,30 @@ __device__ __forceinline__ Hist summarize(const float (&kk)[L][CPL], const float
   return n > 0 ? Hist{A, Bd, P, 0.f} : hist_empty();
 }
 
+// Optional recurrent state around a forward call, in the step API's form
+// (a, b, p: true sums a*e^p and b*e^p), [B, C] each; null pointers mean
+// "empty history" (in) and "not wanted" (out).
+struct StateIO {
+  const float* a_in;
+  const float* b_in;
+  const float* p_in;
+  float* a_out;
+  float* b_out;
+  float* p_out;
+};
+
+template <int CPL>
+__device__ __forceinline__ void write_state(const StateIO& sio, const Hist (&h)[CPL],
+                                            const float (&w2)[CPL], bool valid, size_t si) {
+  if (!sio.a_out || !valid) return;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    sio.a_out[si + c] = h[c].A;
+    sio.b_out[si + c] = h[c].Bd;
+    sio.p_out[si + c] = hist_p(h[c], w2[c]) * kLn2;
+  }
+}
+
 // Shared-memory copy of per-channel histories, [field][channel].
 template <int W>
 struct HistLds {
@@ -134,10 +158,14 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
     int T, int C, int n_cblk, int groups, int n_tiles,
     const float* __restrict__ w, const float* __restrict__ u,
     const float* __restrict__ k, const float* __restrict__ v, float* __restrict__ y,
-    uint32_t* __restrict__ hdr, uint64_t* __restrict__ counters, uint64_t* __restrict__ slots) {
+    uint32_t* __restrict__ hdr, uint64_t* __restrict__ counters, uint64_t* __restrict__ slots,
+    StateIO sio) {
   constexpr int W = 64 * CPL;        // channels per block
   constexpr int TILE = L * NW;       // tokens per tile
   constexpr int SLOT = 8 * W;        // words per (tile, block): agg A,B,kr,n then inc A,B,kr,n
+  // Predecessor payloads loaded per round trip while folding a prefix
+  // (the batch costs 8 VGPRs per payload and channel).
+  constexpr int kFoldBatch = CPL == 1 ? 2 : 1;
   __shared__ int s_tile;
   __shared__ uint32_t s_tag;
   __shared__ HistLds<W> s_sum[NW];
@@ -254,20 +282,32 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
       }
     };
     if (tile == 0) {
-      publish(1, agg);
+      // History before the first token: empty, or the caller's state.
+      if (sio.a_in) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const size_t si = size_t(bi) * C + size_t(cb) * W + cl + c;
+          pre[c] = Hist{sio.a_in[si], sio.b_in[si], sio.p_in[si] * kLog2e, 0.f};
+        }
+      }
+      Hist inc[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) inc[c] = hist_concat(pre[c], agg[c], float(tile_n), w2[c]);
+      publish(1, inc);
+      if (tile == n_tiles - 1) write_state(sio, inc, w2, valid, size_t(bi) * C + size_t(cb) * W + ch0);
     } else {
       publish(0, agg);
+      // The prefix is rebuilt as inc(p) + agg(p+1) + ... + agg(tile-1),
+      // folded in that order for the nearest p (within kWin) whose inclusive
+      // history is out.  That is the order in which the chain of inclusive
+      // histories is built, so the result has the same bits whichever p the
+      // timing offers: the forward is deterministic.
       Hist acc[CPL];
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) acc[c] = hist_empty();
-      float acc_n = 0.f;   // tokens covered by acc: tiles (pos, tile)
-      int pos = tile - 1;  // nearest tile not folded yet
       uint32_t spins = 0;
-      bool found = false;
-      while (!found) {
+      for (;;) {
         // Poll kWin earlier tiles in one round trip: lane i reads the first
-        // word of tile (pos - i)'s inclusive and aggregate histories.
-        const int pi = pos - lane;
+        // word of tile (tile-1-i)'s inclusive and aggregate histories.
+        const int pi = tile - 1 - lane;
         bool inc_ok = false, agg_ok = false;
         if (lane < kWin && pi >= 0) {
           const uint64_t* sp = slots + (size_t(pi) * groups + g) * SLOT;
@@ -276,54 +316,57 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
         }
         const uint64_t inc_mask = __ballot(inc_ok);
         const uint64_t agg_mask = __ballot(agg_ok);
-        // Fold the run of aggregates from pos back to the nearest inclusive.
         const int m = inc_mask ? int(__builtin_ctzll(inc_mask)) : kWin;
         const int a = int(__builtin_ctzll(~agg_mask));  // bits >= kWin are 0
-        const int n_agg = min(a, m);
-        const bool take_inc = inc_mask != 0 && a >= m;
-        const int todo = n_agg + (take_inc ? 1 : 0);
-        int folded = 0;
-        for (int j = 0; j < todo; ++j) {
-          const bool is_inc = take_inc && j == n_agg;
-          const uint64_t* q =
-              slots + (size_t(pos - j) * groups + g) * SLOT + (is_inc ? 4 * W : 0) + ch0;
-          uint64_t x[CPL][4];
-#pragma unroll
-          for (int c = 0; c < CPL; ++c)
-#pragma unroll
-            for (int f = 0; f < 4; ++f) x[c][f] = tagged_load(q + f * W + c);
+        if (inc_mask != 0 && a >= m) {
+          // Payload j = 0 is inc(tile-1-m), payload j >= 1 is agg(tile-1-m+j).
+          const int p0 = tile - 1 - m;
           bool ok = true;
+          for (int j0 = 0; j0 <= m && ok; j0 += kFoldBatch) {
+            uint64_t x[kFoldBatch][CPL][4];
 #pragma unroll
-          for (int c = 0; c < CPL; ++c)
+            for (int jj = 0; jj < kFoldBatch; ++jj) {
+              const int j = j0 + jj;
+              const uint64_t* q =
+                  slots + (size_t(p0 + j) * groups + g) * SLOT + (j == 0 ? 4 * W : 0) + ch0;
 #pragma unroll
-            for (int f = 0; f < 4; ++f) ok = ok && tag_ok(x[c][f], tag);
-          if (!__all(ok)) break;  // payload not visible on every lane yet: poll again
+              for (int c = 0; c < CPL; ++c)
 #pragma unroll
-          for (int c = 0; c < CPL; ++c)
-            acc[c] = hist_concat(Hist{tag_val(x[c][0]), tag_val(x[c][1]), tag_val(x[c][2]),
-                                      tag_val(x[c][3])},
-                                 acc[c], acc_n, w2[c]);
-          if (is_inc) {
-            found = true;
-          } else {
-            acc_n += float(TILE);
-            ++folded;
-          }
-        }
-        pos -= folded;
-        if (found) break;
-        if (folded == 0) {
-          if (++spins > kSpinLimit) {
-            if (lane == 0) raise_error(hdr + kHdrError, 1u);
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-              const float nan = __builtin_nanf("");
-              acc[c] = Hist{nan, nan, nan, 0.f};
+                for (int f = 0; f < 4; ++f)
+                  x[jj][c][f] = j <= m ? tagged_load(q + f * W + c) : (uint64_t(tag) << 32);
             }
-            break;
+#pragma unroll
+            for (int jj = 0; jj < kFoldBatch; ++jj)
+#pragma unroll
+              for (int c = 0; c < CPL; ++c)
+#pragma unroll
+                for (int f = 0; f < 4; ++f) ok = ok && tag_ok(x[jj][c][f], tag);
+            ok = __all(ok);  // a payload not yet visible on every lane: poll again
+            if (!ok) break;
+#pragma unroll
+            for (int jj = 0; jj < kFoldBatch; ++jj) {
+              const int j = j0 + jj;
+              if (j > m) break;
+#pragma unroll
+              for (int c = 0; c < CPL; ++c) {
+                const Hist h{tag_val(x[jj][c][0]), tag_val(x[jj][c][1]), tag_val(x[jj][c][2]),
+                             tag_val(x[jj][c][3])};
+                acc[c] = j == 0 ? h : hist_concat(acc[c], h, float(TILE), w2[c]);
+              }
+            }
           }
-          __builtin_amdgcn_s_sleep(1);
+          if (ok) break;
         }
+        if (++spins > kSpinLimit) {
+          if (lane == 0) raise_error(hdr + kHdrError, 1u);
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            const float nan = __builtin_nanf("");
+            acc[c] = Hist{nan, nan, nan, 0.f};
+          }
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
       }
       Hist inc[CPL];
 #pragma unroll
@@ -332,6 +375,7 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
         inc[c] = hist_concat(pre[c], agg[c], float(tile_n), w2[c]);
       }
       publish(1, inc);
+      if (tile == n_tiles - 1) write_state(sio, inc, w2, valid, size_t(bi) * C + size_t(cb) * W + ch0);
     }
 #pragma unroll
     for (int c = 0; c < CPL; ++c) s_pre.put(ch0 + c, pre[c]);
@@ -435,7 +479,7 @@ constexpr Variant kVariants[] = {{4, 8, 8}, {4, 16, 4}, {4, 16, 8},
 template <int CPL, int L, int NW>
 hipError_t launch_tiled(const Wkv4Plan& pl, int64_t T, int64_t C, const float* w,
                         const float* u, const float* k, const float* v, float* y, void* ws,
-                        hipStream_t stream) {
+                        const StateIO& sio, hipStream_t stream) {
   char* base = static_cast<char*>(ws);
   uint32_t* hdr = reinterpret_cast<uint32_t*>(base);
   uint64_t* counters = reinterpret_cast<uint64_t*>(base + kWkv4HeaderBytes);
@@ -443,7 +487,7 @@ hipError_t launch_tiled(const Wkv4Plan& pl, int64_t T, int64_t C, const float* w
   const unsigned grid = unsigned(pl.n_tiles * pl.groups);
   hipLaunchKernelGGL((wkv4_fwd_tiled<CPL, L, NW>), dim3(grid), dim3(64 * NW), 0, stream,
                      int(T), int(C), int(pl.n_cblk), int(pl.groups), int(pl.n_tiles),
-                     w, u, k, v, y, hdr, counters, slots);
+                     w, u, k, v, y, hdr, counters, slots, sio);
   return hipGetLastError();
 }
 
@@ -491,19 +535,22 @@ bool wkv4_plan(int64_t B, int64_t T, int64_t C, Wkv4Plan* plan) {
 
 hipError_t wkv4_forward_launch(const Wkv4Plan& pl, int64_t B, int64_t T, int64_t C,
                                const float* w, const float* u, const float* k,
-                               const float* v, float* y, void* ws, hipStream_t stream) {
+                               const float* v, float* y, void* ws, const float* a_in,
+                               const float* b_in, const float* p_in, float* a_out,
+                               float* b_out, float* p_out, hipStream_t stream) {
   (void)B;
+  const StateIO sio{a_in, b_in, p_in, a_out, b_out, p_out};
   switch (pl.cpl * 10000 + pl.L * 100 + pl.NW) {
-    case 40808: return launch_tiled<4, 8, 8>(pl, T, C, w, u, k, v, y, ws, stream);
-    case 41604: return launch_tiled<4, 16, 4>(pl, T, C, w, u, k, v, y, ws, stream);
-    case 41608: return launch_tiled<4, 16, 8>(pl, T, C, w, u, k, v, y, ws, stream);
-    case 21608: return launch_tiled<2, 16, 8>(pl, T, C, w, u, k, v, y, ws, stream);
-    case 23204: return launch_tiled<2, 32, 4>(pl, T, C, w, u, k, v, y, ws, stream);
-    case 21604: return launch_tiled<2, 16, 4>(pl, T, C, w, u, k, v, y, ws, stream);
-    case 13208: return launch_tiled<1, 32, 8>(pl, T, C, w, u, k, v, y, ws, stream);
-    case 13204: return launch_tiled<1, 32, 4>(pl, T, C, w, u, k, v, y, ws, stream);
-    case 16401: return launch_tiled<1, 64, 1>(pl, T, C, w, u, k, v, y, ws, stream);
-    case 11604: return launch_tiled<1, 16, 4>(pl, T, C, w, u, k, v, y, ws, stream);
+    case 40808: return launch_tiled<4, 8, 8>(pl, T, C, w, u, k, v, y, ws, sio, stream);
+    case 41604: return launch_tiled<4, 16, 4>(pl, T, C, w, u, k, v, y, ws, sio, stream);
+    case 41608: return launch_tiled<4, 16, 8>(pl, T, C, w, u, k, v, y, ws, sio, stream);
+    case 21608: return launch_tiled<2, 16, 8>(pl, T, C, w, u, k, v, y, ws, sio, stream);
+    case 23204: return launch_tiled<2, 32, 4>(pl, T, C, w, u, k, v, y, ws, sio, stream);
+    case 21604: return launch_tiled<2, 16, 4>(pl, T, C, w, u, k, v, y, ws, sio, stream);
+    case 13208: return launch_tiled<1, 32, 8>(pl, T, C, w, u, k, v, y, ws, sio, stream);
+    case 13204: return launch_tiled<1, 32, 4>(pl, T, C, w, u, k, v, y, ws, sio, stream);
+    case 16401: return launch_tiled<1, 64, 1>(pl, T, C, w, u, k, v, y, ws, sio, stream);
+    case 11604: return launch_tiled<1, 16, 4>(pl, T, C, w, u, k, v, y, ws, sio, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -72,6 +72,7 @@ __device__ void eagle_recurrent_slice(int T, int H, int b, int h, int j0,
                                      const uint16_t* __restrict__ v,
                                      const float* __restrict__ w,
                                      const float* __restrict__ u, float* __restrict__ o,
+                                     const float* s_in, float* s_out,
                                      Lds<DV>& s) {
   float* s_r = &s.dec[0][0];
   float* s_k = &s.dec[1][0];
@@ -82,9 +83,10 @@ __device__ void eagle_recurrent_slice(int T, int H, int b, int h, int j0,
     s_w[tid] = w[h * kD + tid];
     s_u[tid] = u[h * kD + tid];
   }
+  const size_t sbase = (size_t(b) * H + h) * kD * kD + j0 + tid;  // s[i][j0+tid] at + i*kD
   float S[kD];
 #pragma unroll
-  for (int i = 0; i < kD; ++i) S[i] = 0.f;
+  for (int i = 0; i < kD; ++i) S[i] = (s_in && tid < DV) ? s_in[sbase + size_t(i) * kD] : 0.f;
   for (int t = 0; t < T; ++t) {
     const size_t off = ((size_t(b) * T + t) * H + h) * kD;
     __syncthreads();
@@ -105,6 +107,10 @@ __device__ void eagle_recurrent_slice(int T, int H, int b, int h, int j0,
       }
       o[off + j0 + tid] = fmaf(beta, vj, acc);
     }
+  }
+  if (s_out && tid < DV) {
+#pragma unroll
+    for (int i = 0; i < kD; ++i) s_out[sbase + size_t(i) * kD] = S[i];
   }
 }
 
@@ -168,9 +174,11 @@ __device__ __forceinline__ void stage_consts(StageConsts& c, const Lds<DV>& s) {
 }
 
 // Scale one chunk into LDS: rt, kt, kh^T, v^T, beta.
+// `n_last` > 0 marks a final chunk of n_last < kL tokens whose state update
+// must decay from its own end: kh = k w^(n_last-1-sigma) (else w^(63-sigma)).
 template <int DV>
 __device__ __forceinline__ void stage_chunk(const ChunkRegs& x, const StageConsts& f,
-                                            Lds<DV>& s) {
+                                            Lds<DV>& s, int n_last = 0) {
   const int tid = threadIdx.x;
   const int tau = tid >> 2, q4 = tid & 3;
   const int d0 = 16 * q4;
@@ -193,10 +201,20 @@ __device__ __forceinline__ void stage_chunk(const ChunkRegs& x, const StageConst
     kt0[e] = to_bf16(kv[e] * f.fk[e]);
     kt1[e] = to_bf16(kv[8 + e] * f.fk[8 + e]);
   }
+  if (n_last > 0) {
+    // rare: once per call, only when the final state is wanted
+    const float* dh = s.dec[max(n_last - 1 - tau, 0) - kExpLo];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    s.kh[d0 + e][tau] = to_bf16(kv[e] * f.fh[e]);
-    bpart = fmaf(rv[e] * f.ur[e], kv[e], bpart);
+    for (int e = 0; e < 16; ++e) {
+      s.kh[d0 + e][tau] = to_bf16(tau < n_last ? kv[e] * dh[d0 + e] : 0.f);
+      bpart = fmaf(rv[e] * f.ur[e], kv[e], bpart);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      s.kh[d0 + e][tau] = to_bf16(kv[e] * f.fh[e]);
+      bpart = fmaf(rv[e] * f.ur[e], kv[e], bpart);
+    }
   }
   *reinterpret_cast<bf16x8*>(&s.rt[tau][d0]) = rt0;
   *reinterpret_cast<bf16x8*>(&s.rt[tau][d0 + 8]) = rt1;
@@ -226,7 +244,7 @@ template <int DV>
 __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
     int T, int H, int BH, const uint16_t* __restrict__ r, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ w,
-    const float* __restrict__ u, float* __restrict__ o) {
+    const float* __restrict__ u, float* __restrict__ o, const float* s_in, float* s_out) {
   constexpr int NS = kD / DV;  // slices per head
   constexpr int NJB = DV / 16; // 16-wide value tiles per slice
   __shared__ Lds<DV> s;
@@ -255,19 +273,38 @@ __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
   }
   __syncthreads();
   if (s.fallback) {
-    eagle_recurrent_slice<DV>(T, H, b, h, j0, r, k, v, w, u, o, s);
+    eagle_recurrent_slice<DV>(T, H, b, h, j0, r, k, v, w, u, o, s_in, s_out, s);
     return;
   }
-
-  // S' starts at zero; S itself lives in registers (wave q: key rows 16q..).
-  for (int idx = tid; idx < DV * kPad; idx += 256) (&s.sp[0][0])[idx] = to_bf16(0.f);
-  floatx4 sacc[NJB];
-#pragma unroll
-  for (int jb = 0; jb < NJB; ++jb) sacc[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const int row = lane & 15;         // MFMA operand row/column of this lane
   const int kq = 8 * (lane >> 4);    // first K element of this lane in a 32-wide step
   const int crow = 4 * (lane >> 4);  // first accumulator row of this lane
+  const size_t sbase = size_t(bh) * kD * kD;  // state s[i][j] at sbase + i*kD + j
+
+  // S lives in registers (wave q: key rows 16q..16q+15); S' = diag(w^32) S
+  // goes to LDS, transposed, for the inter-chunk product.
+  floatx4 sacc[NJB];
+#pragma unroll
+  for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      sacc[jb][rr] = s_in ? s_in[sbase + size_t(16 * q + crow + rr) * kD + j0 + 16 * jb + row]
+                          : 0.f;
+  auto write_sp = [&]() {
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) {
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      bf16x4 pk;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int i = 16 * q + crow + rr;
+        pk[rr] = to_bf16(sacc[jb][rr] * s.dec[32 - kExpLo][i]);
+      }
+      *reinterpret_cast<bf16x4*>(&s.sp[16 * jb + row][16 * q + crow]) = pk;
+    }
+  };
+  write_sp();
 
   StageConsts f;
   stage_consts(f, s);
@@ -276,7 +313,8 @@ __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
   load_chunk<DV>(cur, 0, T, H, b, h, j0, r, k, v);
   for (int c = 0; c < n_chunks; ++c) {
     const int t0 = c * kL;
-    stage_chunk(cur, f, s);
+    const int n_last = (s_out && c == n_chunks - 1 && T - t0 < kL) ? T - t0 : 0;
+    stage_chunk(cur, f, s, n_last);
     __syncthreads();
     if (c + 1 < n_chunks) load_chunk<DV>(nxt, t0 + kL, T, H, b, h, j0, r, k, v);
 
@@ -347,10 +385,11 @@ __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
           o[((size_t(b) * T + t0 + tau) * H + h) * kD + j0 + 16 * jb + row] = oacc[jb][rr];
       }
 
-    // S <- diag(w^64) S + kh^T V for key rows 16q..16q+15.
+    // S <- diag(w^64) S + kh^T V for key rows 16q..16q+15 (a ragged final
+    // chunk decays by w^n_last).
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const float d64 = s.dec[64 - kExpLo][16 * q + crow + rr];
+      const float d64 = s.dec[(n_last > 0 ? n_last : 64) - kExpLo][16 * q + crow + rr];
 #pragma unroll
       for (int jb = 0; jb < NJB; ++jb) sacc[jb][rr] *= d64;
     }
@@ -365,21 +404,51 @@ __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
     }
     __syncthreads();  // every wave is done with rt, kt, kh, vt, sp of this chunk
 
-    // S' = diag(w^32) S for the next chunk, transposed to [j][i]: a lane's
-    // four key rows are adjacent, one 8-byte store per value tile.
-#pragma unroll
-    for (int jb = 0; jb < NJB; ++jb) {
-      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-      bf16x4 pk;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int i = 16 * q + crow + rr;
-        pk[rr] = to_bf16(sacc[jb][rr] * s.dec[32 - kExpLo][i]);
-      }
-      *reinterpret_cast<bf16x4*>(&s.sp[16 * jb + row][16 * q + crow]) = pk;
-    }
+    write_sp();  // S' for the next chunk
     cur = nxt;
   }
+  if (s_out) {
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        s_out[sbase + size_t(16 * q + crow + rr) * kD + j0 + 16 * jb + row] = sacc[jb][rr];
+  }
+}
+
+// One token of the recurrence for every (batch, head): lane j keeps the
+// state column s[:, j] (read, updated and written back in place).
+__global__ __launch_bounds__(64) void wkv5_step_kernel(
+    int H, float* __restrict__ S, const uint16_t* __restrict__ r,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ w, const float* __restrict__ u, float* __restrict__ o) {
+  __shared__ float s_r[kD], s_k[kD], s_w[kD], s_ru[kD];
+  const int bh = blockIdx.x;
+  const int h = bh % H;
+  const int j = threadIdx.x;
+  const size_t off = size_t(bh) * kD;
+  float* Sc = S + size_t(bh) * kD * kD + j;
+  float col[kD];
+#pragma unroll
+  for (int i = 0; i < kD; ++i) col[i] = Sc[size_t(i) * kD];
+  const float rj = bf16_to_f32(r[off + j]);
+  const float kj = bf16_to_f32(k[off + j]);
+  s_r[j] = rj;
+  s_k[j] = kj;
+  s_w[j] = w[h * kD + j];
+  s_ru[j] = rj * u[h * kD + j];
+  __syncthreads();
+  const float vj = bf16_to_f32(v[off + j]);
+  float acc = 0.f, beta = 0.f;
+#pragma unroll
+  for (int i = 0; i < kD; ++i) {
+    acc = fmaf(s_r[i], col[i], acc);
+    beta = fmaf(s_ru[i], s_k[i], beta);
+    col[i] = fmaf(s_w[i], col[i], s_k[i] * vj);
+  }
+  o[off + j] = fmaf(beta, vj, acc);
+#pragma unroll
+  for (int i = 0; i < kD; ++i) Sc[size_t(i) * kD] = col[i];
 }
 
 }  // namespace
@@ -389,7 +458,7 @@ size_t wkv5_workspace_bytes(int64_t, int64_t, int64_t, int64_t) { return 0; }
 hipError_t wkv5_forward_launch(int64_t B, int64_t T, int64_t H, int64_t D,
                                const uint16_t* r, const uint16_t* k, const uint16_t* v,
                                const float* w, const float* u, float* o, void* ws,
-                               hipStream_t stream) {
+                               const float* s_in, float* s_out, hipStream_t stream) {
   (void)D;
   (void)ws;
   const int64_t BH = B * H;
@@ -398,10 +467,18 @@ hipError_t wkv5_forward_launch(int64_t B, int64_t T, int64_t H, int64_t D,
   const unsigned grid = unsigned((BH + 7) / 8 * 8 * (kD / dv));
   if (dv == 16)
     hipLaunchKernelGGL(wkv5_fwd_chunked<16>, dim3(grid), dim3(256), 0, stream, int(T), int(H),
-                       int(BH), r, k, v, w, u, o);
+                       int(BH), r, k, v, w, u, o, s_in, s_out);
   else
     hipLaunchKernelGGL(wkv5_fwd_chunked<32>, dim3(grid), dim3(256), 0, stream, int(T), int(H),
-                       int(BH), r, k, v, w, u, o);
+                       int(BH), r, k, v, w, u, o, s_in, s_out);
+  return hipGetLastError();
+}
+
+hipError_t wkv5_step_launch(int64_t B, int64_t H, float* s, const uint16_t* r,
+                            const uint16_t* k, const uint16_t* v, const float* w,
+                            const float* u, float* o, hipStream_t stream) {
+  hipLaunchKernelGGL(wkv5_step_kernel, dim3(unsigned(B * H)), dim3(64), 0, stream, int(H), s, r,
+                     k, v, w, u, o);
   return hipGetLastError();
 }
 

@@ -34,9 +34,13 @@ constexpr size_t kWkv4CounterStride = 128;  // one counter per 128-byte line
 // Returns false if the shape cannot be planned (too large for 32-bit tickets).
 bool wkv4_plan(int64_t B, int64_t T, int64_t C, Wkv4Plan* plan);
 
+// a/b/p_in: optional history before the first token; a/b/p_out: optional
+// state after the last token (both [B, C], step-API form; may be null).
 hipError_t wkv4_forward_launch(const Wkv4Plan& plan, int64_t B, int64_t T, int64_t C,
                                const float* w, const float* u, const float* k,
-                               const float* v, float* y, void* ws, hipStream_t stream);
+                               const float* v, float* y, void* ws, const float* a_in,
+                               const float* b_in, const float* p_in, float* a_out,
+                               float* b_out, float* p_out, hipStream_t stream);
 
 hipError_t wkv4_state_init_launch(int64_t B, int64_t C, float* a, float* b, float* p,
                                   hipStream_t stream);
@@ -48,9 +52,15 @@ hipError_t wkv4_step_launch(int64_t B, int64_t C, float* a, float* b, float* p,
 // ----- Eagle (RWKV-5) forward -----
 size_t wkv5_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t D);
 
+// s_in / s_out: optional [B, H, D, D] float32 states before the first and
+// after the last token (may be null: zero start, not wanted).
 hipError_t wkv5_forward_launch(int64_t B, int64_t T, int64_t H, int64_t D,
                                const uint16_t* r, const uint16_t* k, const uint16_t* v,
                                const float* w, const float* u, float* o, void* ws,
-                               hipStream_t stream);
+                               const float* s_in, float* s_out, hipStream_t stream);
+
+hipError_t wkv5_step_launch(int64_t B, int64_t H, float* s, const uint16_t* r,
+                            const uint16_t* k, const uint16_t* v, const float* w,
+                            const float* u, float* o, hipStream_t stream);
 
 }  // namespace rwkv

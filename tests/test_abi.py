@@ -42,8 +42,9 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     assert names == sorted([
         "rwkv_abi_version", "rwkv_status_str", "rwkv_last_hip_error",
-        "rwkv_wkv4_forward_workspace", "rwkv_wkv4_forward", "rwkv_wkv4_state_init",
-        "rwkv_wkv4_step", "rwkv_wkv5_forward_workspace", "rwkv_wkv5_forward",
+        "rwkv_wkv4_forward_workspace", "rwkv_wkv4_forward", "rwkv_wkv4_forward_state",
+        "rwkv_wkv4_state_init", "rwkv_wkv4_step", "rwkv_wkv5_forward_workspace",
+        "rwkv_wkv5_forward", "rwkv_wkv5_forward_state", "rwkv_wkv5_step",
     ])
 
 
@@ -145,3 +146,47 @@ def test_wkv5_rejections(lib):
         assert f(4, 4096, 32, 64, *ptrs(**{n: NULL}), FAKE, need, NULL) == NULLPTR, n
         assert f(4, 4096, 32, 64, *ptrs(**{n: MISALIGNED}), FAKE, need, NULL) == ALIGN, n
     assert lib.rwkv_wkv5_forward_workspace(4, 4096, 32, 32) == 0
+
+
+def test_wkv4_forward_state_rejections(lib):
+    _skip_if_gpu()
+    f = lib.rwkv_wkv4_forward_state
+    need = lib.rwkv_wkv4_forward_workspace(2, 300, 128)
+    names = "w u k v y a_in b_in p_in a_out b_out p_out".split()
+    args = lambda **kw: [kw.get(n, FAKE) for n in names]  # noqa: E731
+    assert f(0, 300, 128, *[NULL] * 11, NULL, 0, NULL) == OK
+    assert f(2, -1, 128, *args(), FAKE, need, NULL) == SHAPE
+    for n in names[:5]:
+        assert f(2, 300, 128, *args(**{n: NULL}), FAKE, need, NULL) == NULLPTR, n
+    # a state triple is all or nothing
+    for n in names[5:]:
+        assert f(2, 300, 128, *args(**{n: NULL}), FAKE, need, NULL) == NULLPTR, n
+        assert f(2, 300, 128, *args(**{n: MISALIGNED}), FAKE, need, NULL) == ALIGN, n
+    # both triples absent: the plain forward's checks
+    none = dict(a_in=NULL, b_in=NULL, p_in=NULL, a_out=NULL, b_out=NULL, p_out=NULL)
+    assert f(2, 300, 128, *args(**none), NULL, need, NULL) == WORKSPACE
+    assert f(2, 300, 128, *args(**none, y=MISALIGNED), FAKE, need, NULL) == ALIGN
+    assert lib.rwkv_last_hip_error() == 0
+
+
+def test_wkv5_state_and_step_rejections(lib):
+    _skip_if_gpu()
+    f = lib.rwkv_wkv5_forward_state
+    names = "r k v w u o s_in s_out".split()
+    ptrs = lambda **kw: [kw.get(n, FAKE) for n in names]  # noqa: E731
+    assert f(0, 64, 2, 64, *[NULL] * 8, NULL, 0, NULL) == OK
+    assert f(1, 64, 2, 16, *ptrs(), NULL, 0, NULL) == UNSUPPORTED
+    for n in names[:6]:
+        assert f(1, 64, 2, 64, *ptrs(**{n: NULL}), NULL, 0, NULL) == NULLPTR, n
+    for n in names:
+        assert f(1, 64, 2, 64, *ptrs(**{n: MISALIGNED}), NULL, 0, NULL) == ALIGN, n
+    s = lib.rwkv_wkv5_step
+    names = "s r k v w u o".split()
+    ptrs = lambda **kw: [kw.get(n, FAKE) for n in names]  # noqa: E731
+    assert s(0, 2, 64, *[NULL] * 7, NULL) == OK
+    assert s(1, 2, 32, *ptrs(), NULL) == UNSUPPORTED
+    assert s(1, -2, 64, *ptrs(), NULL) == SHAPE
+    for n in names:
+        assert s(1, 2, 64, *ptrs(**{n: NULL}), NULL) == NULLPTR, n
+        assert s(1, 2, 64, *ptrs(**{n: MISALIGNED}), NULL) == ALIGN, n
+    assert lib.rwkv_last_hip_error() == 0

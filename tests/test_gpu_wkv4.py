@@ -281,3 +281,100 @@ def test_decode_workload_sampled_lanes():
     err = wkv4_scaled_err(got[None], y_ref, S)
     log(f"  err={err:.3e}")
     assert err <= WKV4_TOL
+
+
+# ------------------------------------------------- forward with a state ---
+
+def _with_tile(tile, fn):
+    old = os.environ.get("RWKV_WKV4_TILE")
+    if tile is not None:
+        os.environ["RWKV_WKV4_TILE"] = tile
+    try:
+        return fn()
+    finally:
+        if tile is not None:
+            if old is None:
+                del os.environ["RWKV_WKV4_TILE"]
+            else:
+                os.environ["RWKV_WKV4_TILE"] = old
+
+
+@pytest.mark.parametrize("tile", [None, "4,8,8", "2,16,4", "1,64,1"])
+@pytest.mark.parametrize("cut", [(500, 7, 333), (40, 0, 1), (1, 3, 1000), (256, 1, 64)])
+def test_forward_state_chain_matches_whole_sequence(cut, tile):
+    """forward(T1) -> N steps -> forward(T2), the state handed on each time
+    (the last hand-over in place), equals one pass over T1+N+T2 tokens."""
+    torch, dev = torch_dev()
+    T1, N, T2 = cut
+    B, C = 3, 200
+    log(f"wkv4_forward_state B={B} C={C} cut={cut} tile={tile}")
+    inp = synth.wkv4_inputs(B, T1 + N + T2, C, seed=90 + T1 + T2)
+    w, u = to_dev(inp["w"]), to_dev(inp["u"])
+    k, v = to_dev(inp["k"]), to_dev(inp["v"])
+
+    def run():
+        y1, st = rw.rwkv_wkv4_forward_state(w, u, k[:, :T1].contiguous(),
+                                            v[:, :T1].contiguous(), state_out=True)
+        ys = [y1]
+        for t in range(T1, T1 + N):
+            ys.append(rw.rwkv_wkv4_step(*st, w, u, k[:, t].contiguous(),
+                                        v[:, t].contiguous())[:, None])
+        y3, _ = rw.rwkv_wkv4_forward_state(w, u, k[:, T1 + N:].contiguous(),
+                                           v[:, T1 + N:].contiguous(), state_in=st,
+                                           state_out=st)
+        ys.append(y3)
+        torch.cuda.synchronize()
+        return torch.cat(ys, dim=1).cpu().numpy(), [x.cpu().numpy() for x in st]
+
+    y, (a, b, p) = _with_tile(tile, run)
+    y_ref, st_ref = O.wkv4_recurrent(inp["w"], inp["u"], inp["k"], inp["v"])
+    S = O.wkv4_scale(inp["w"], inp["u"], inp["k"], inp["v"])
+    err = wkv4_scaled_err(y, y_ref, S)
+    log(f"  err={err:.3e}")
+    assert err <= WKV4_TOL
+    mean_ref, logden_ref = O.wkv4_canonical_state(st_ref)
+    a64, b64, p64 = (x.astype(np.float64) for x in (a, b, p))
+    Sv = np.abs(inp["v"]).max(axis=1)
+    assert np.max(np.abs(a64 / b64 - mean_ref) / Sv) <= WKV4_TOL
+    assert np.max(np.abs(np.log(b64) + p64 - logden_ref)) <= 1e-4 * (1 + np.abs(logden_ref)).max()
+
+
+def test_forward_state_without_states_is_the_plain_forward():
+    torch, dev = torch_dev()
+    inp = synth.wkv4_inputs(2, 700, 130, seed=5)
+    y0 = gpu_forward(inp)
+    y1, st = rw.rwkv_wkv4_forward_state(to_dev(inp["w"]), to_dev(inp["u"]), to_dev(inp["k"]),
+                                        to_dev(inp["v"]))
+    torch.cuda.synchronize()
+    assert st is None
+    assert np.array_equal(y0, y1.cpu().numpy())
+
+
+def test_forward_state_from_empty_state_init():
+    """An explicit empty state (state_init) gives the plain forward's output."""
+    torch, dev = torch_dev()
+    B, T, C = 2, 300, 96
+    inp = synth.wkv4_inputs(B, T, C, seed=6)
+    st = rw.rwkv_wkv4_state_init(B, C, device=dev)
+    y, _ = rw.rwkv_wkv4_forward_state(to_dev(inp["w"]), to_dev(inp["u"]), to_dev(inp["k"]),
+                                      to_dev(inp["v"]), state_in=st)
+    torch.cuda.synchronize()
+    y_ref, S = oracle_forward(inp)
+    assert wkv4_scaled_err(y.cpu().numpy(), y_ref, S) <= WKV4_TOL
+
+
+@pytest.mark.parametrize("cfg_name", ["169m", "long"])
+def test_forward_is_deterministic(cfg_name):
+    """Repeated calls give the same bits: the look-back folds predecessors in
+    chain order whatever the timing (the long workload has 512 tiles per
+    channel block, so deep look-backs do happen)."""
+    torch, dev = torch_dev()
+    cfg = synth.CFG_WKV4_169M if cfg_name == "169m" else synth.CFG_WKV4_LONG
+    log(f"wkv4_forward {cfg.name} x3 bitwise")
+    inp = synth.wkv4_inputs_for(cfg)
+    w, u, k, v = (to_dev(inp[n]) for n in ("w", "u", "k", "v"))
+    y0 = rw.rwkv_wkv4_forward(w, u, k, v)
+    for _ in range(2):
+        y1 = rw.rwkv_wkv4_forward(w, u, k, v)
+        torch.cuda.synchronize()
+        assert torch.equal(y0, y1)

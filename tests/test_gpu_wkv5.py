@@ -84,3 +84,119 @@ def test_no_decay_and_fast_decay_extremes(dv):
         o = gpu_wkv5(case, dv)
         o_ref, o_abs = oracle_wkv5(case)
         assert wkv5_scaled_err(o, o_ref, o_abs) <= WKV5_TOL, name
+
+
+# ------------------------------------------------ state in/out and step ---
+
+def _bits(inp, name, sl):
+    torch, _ = torch_dev()
+    return to_dev(np.ascontiguousarray(inp[name + "_bits"][sl]), torch.bfloat16)
+
+
+def _magnitude(inp):
+    """(o_abs, S_abs): the recurrence on |r|, |k|, |v|, |u| from a zero state."""
+    return O.wkv5_recurrent(np.abs(inp["r"]), np.abs(inp["k"]), np.abs(inp["v"]), inp["w"],
+                            np.abs(inp["u"]))
+
+
+def _with_dv(dv, fn):
+    old = os.environ.get("RWKV_WKV5_DV")
+    os.environ["RWKV_WKV5_DV"] = str(dv)
+    try:
+        return fn()
+    finally:
+        if old is None:
+            del os.environ["RWKV_WKV5_DV"]
+        else:
+            os.environ["RWKV_WKV5_DV"] = old
+
+
+@pytest.mark.parametrize("dv", [32, 16])
+@pytest.mark.parametrize("case", [("decay", 100, 5, 129), ("decay", 128, 0, 64),
+                                  ("decay", 1, 2, 63), ("w=0.05", 70, 3, 90)])
+def test_forward_state_chain_matches_whole_sequence(case, dv):
+    """forward(T1) -> N steps -> forward(T2) with the state handed on (the
+    last hand-over in place) equals one pass over the whole sequence; the
+    w=0.05 case runs the exact-recurrence path of the forward."""
+    torch, dev = torch_dev()
+    kind, T1, N, T2 = case
+    B, H = 2, 3
+    log(f"wkv5_forward_state/step {case} value slice {dv}")
+    inp = synth.wkv5_inputs(B, T1 + N + T2, H, 64, seed=60 + T1 + N)
+    if kind == "w=0.05":
+        inp = dict(inp, w=np.full((H, 64), 0.05, np.float32))
+    w, u = to_dev(inp["w"]), to_dev(inp["u"])
+
+    def run():
+        sl = np.s_[:, :T1]
+        o1, s = rw.rwkv_wkv5_forward_state(_bits(inp, "r", sl), _bits(inp, "k", sl),
+                                           _bits(inp, "v", sl), w, u, s_out=True)
+        outs = [o1]
+        for t in range(T1, T1 + N):
+            sl = np.s_[:, t]
+            outs.append(rw.rwkv_wkv5_step(s, _bits(inp, "r", sl), _bits(inp, "k", sl),
+                                          _bits(inp, "v", sl), w, u)[:, None])
+        sl = np.s_[:, T1 + N:]
+        o3, _ = rw.rwkv_wkv5_forward_state(_bits(inp, "r", sl), _bits(inp, "k", sl),
+                                           _bits(inp, "v", sl), w, u, s_in=s, s_out=s)
+        outs.append(o3)
+        torch.cuda.synchronize()
+        return torch.cat(outs, dim=1).cpu().numpy(), s.cpu().numpy()
+
+    o, s = _with_dv(dv, run)
+    o_ref, s_ref = O.wkv5_recurrent(inp["r"], inp["k"], inp["v"], inp["w"], inp["u"])
+    o_abs, s_abs = _magnitude(inp)
+    err_o = wkv5_scaled_err(o, o_ref, o_abs)
+    err_s = wkv5_scaled_err(s, s_ref, s_abs)
+    log(f"  err o={err_o:.3e} state={err_s:.3e}")
+    assert err_o <= WKV5_TOL
+    assert err_s <= WKV5_TOL
+
+
+def test_steps_from_a_given_state():
+    """The step kernel is exact float32 arithmetic on bf16 inputs: 40 steps
+    from a random state agree with the oracle to float32 rounding."""
+    torch, dev = torch_dev()
+    B, H, N = 3, 5, 40
+    inp = synth.wkv5_inputs(B, N, H, 64, seed=123)
+    rng = np.random.default_rng(7)
+    s0 = rng.standard_normal((B, H, 64, 64)).astype(np.float32)
+    s = to_dev(s0)
+    w, u = to_dev(inp["w"]), to_dev(inp["u"])
+    outs = []
+    for t in range(N):
+        sl = np.s_[:, t]
+        outs.append(rw.rwkv_wkv5_step(s, _bits(inp, "r", sl), _bits(inp, "k", sl),
+                                      _bits(inp, "v", sl), w, u))
+    torch.cuda.synchronize()
+    o = torch.stack(outs, dim=1).cpu().numpy()
+    o_ref, s_ref = O.wkv5_recurrent(inp["r"], inp["k"], inp["v"], inp["w"], inp["u"], S0=s0)
+    o_abs, s_abs = O.wkv5_recurrent(np.abs(inp["r"]), np.abs(inp["k"]), np.abs(inp["v"]),
+                                    inp["w"], np.abs(inp["u"]), S0=np.abs(s0))
+    err_o = wkv5_scaled_err(o, o_ref, o_abs)
+    err_s = wkv5_scaled_err(s.cpu().numpy(), s_ref, s_abs)
+    log(f"  err o={err_o:.3e} state={err_s:.3e}")
+    assert err_o <= 1e-5 and err_s <= 1e-5
+
+
+@pytest.mark.parametrize("dv", [32, 16])
+def test_forward_from_a_given_state(dv):
+    """A random (not chain-built) starting state through the chunked path."""
+    torch, dev = torch_dev()
+    B, T, H = 2, 150, 2
+    inp = synth.wkv5_inputs(B, T, H, 64, seed=321)
+    s0 = (np.random.default_rng(8).standard_normal((B, H, 64, 64)) * 0.5).astype(np.float32)
+
+    def run():
+        o, s = rw.rwkv_wkv5_forward_state(_bits(inp, "r", np.s_[:]), _bits(inp, "k", np.s_[:]),
+                                          _bits(inp, "v", np.s_[:]), to_dev(inp["w"]),
+                                          to_dev(inp["u"]), s_in=to_dev(s0), s_out=True)
+        torch.cuda.synchronize()
+        return o.cpu().numpy(), s.cpu().numpy()
+
+    o, s = _with_dv(dv, run)
+    o_ref, s_ref = O.wkv5_recurrent(inp["r"], inp["k"], inp["v"], inp["w"], inp["u"], S0=s0)
+    o_abs, s_abs = O.wkv5_recurrent(np.abs(inp["r"]), np.abs(inp["k"]), np.abs(inp["v"]),
+                                    inp["w"], np.abs(inp["u"]), S0=np.abs(s0))
+    assert wkv5_scaled_err(o, o_ref, o_abs) <= WKV5_TOL
+    assert wkv5_scaled_err(s, s_ref, s_abs) <= WKV5_TOL
