@@ -62,28 +62,62 @@ __device__ __forceinline__ uint32_t hdr_add(uint32_t* h, int i, uint32_t x) {
   return __hip_atomic_fetch_add(h + i, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// k, v and y stream through buffer resources: a row's offset (s * C * 4
+// bytes, the same for the whole wave) goes in a scalar register and the
+// lane's channel offset in a vector register, so no 64-bit vector address
+// arithmetic is spent per row.  Every byte is touched once: loads and stores
+// are non-temporal.  A store whose offset is at or beyond the resource's
+// size is dropped by the hardware; lanes without a channel use that.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit access, gfx9 family
+constexpr int kNonTemporal = 2;
+constexpr uint32_t kDropOffset = 0x80000000u;
+
+__device__ __forceinline__ Rsrc make_rsrc(const float* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, int(bytes), kRsrcWord3);
+}
+
 // CPL adjacent floats of one row, loaded/stored with a single vector access.
 template <int CPL>
-__device__ __forceinline__ void load_vec(const float* p, float (&x)[CPL]) {
+__device__ __forceinline__ void load_row(Rsrc r, uint32_t voff, uint32_t soff,
+                                         float (&x)[CPL]) {
   if constexpr (CPL == 4) {
-    const float4 t = *reinterpret_cast<const float4*>(p);
-    x[0] = t.x; x[1] = t.y; x[2] = t.z; x[3] = t.w;
+    typedef int iv4 __attribute__((ext_vector_type(4)));
+    const float4 t = __builtin_bit_cast(
+        float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNonTemporal));
+    x[0] = t.x;
+    x[1] = t.y;
+    x[2] = t.z;
+    x[3] = t.w;
   } else if constexpr (CPL == 2) {
-    const float2 t = *reinterpret_cast<const float2*>(p);
-    x[0] = t.x; x[1] = t.y;
+    const float2 t = __builtin_bit_cast(
+        float2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kNonTemporal));
+    x[0] = t.x;
+    x[1] = t.y;
   } else {
-    x[0] = *p;
+    x[0] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kNonTemporal));
   }
 }
 
 template <int CPL>
-__device__ __forceinline__ void store_vec(float* p, const float (&x)[CPL]) {
+__device__ __forceinline__ void store_row(Rsrc r, uint32_t voff, uint32_t soff,
+                                          const float (&x)[CPL]) {
   if constexpr (CPL == 4) {
-    *reinterpret_cast<float4*>(p) = float4{x[0], x[1], x[2], x[3]};
+    typedef int iv4 __attribute__((ext_vector_type(4)));
+    const iv4 t = {__float_as_int(x[0]), __float_as_int(x[1]), __float_as_int(x[2]),
+                   __float_as_int(x[3])};
+    // A store wider than 8 bytes must not see its data registers rewritten
+    // in the next cycle.  The compiler inserts that wait state only when the
+    // scalar offset is a constant, so the row offset moves into the vector
+    // offset here (with a register soffset the first data register was
+    // observed to be overwritten before it was stored).
+    __builtin_amdgcn_raw_buffer_store_b128(t, r, voff + soff, 0, kNonTemporal);
   } else if constexpr (CPL == 2) {
-    *reinterpret_cast<float2*>(p) = float2{x[0], x[1]};
+    typedef int iv2 __attribute__((ext_vector_type(2)));
+    const iv2 t = {__float_as_int(x[0]), __float_as_int(x[1])};
+    __builtin_amdgcn_raw_buffer_store_b64(t, r, voff, soff, kNonTemporal);
   } else {
-    *p = x[0];
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(x[0]), r, voff, soff, kNonTemporal);
   }
 }
 
@@ -92,14 +126,13 @@ __device__ __forceinline__ void store_vec(float* p, const float (&x)[CPL]) {
 // maximum: token s has log2-weight m_s = k2_s - (n-1-s) w2; with
 // P = max_s m_s every term is 2^(m_s - P) <= 1 and the largest is exactly 1,
 // so nothing overflows and the sum never underflows to 0.
-template <int L, int CPL>
+template <int L, int CPL, bool FULL>
 __device__ __forceinline__ Hist summarize(const float (&kk)[L][CPL], const float (&vv)[L][CPL],
                                           int c, int n, float w2) {
+  if constexpr (FULL) n = L;
   auto expo = [&](int s) {
-    const bool full = n == L;
-    const float back = full ? float(L - 1 - s) : float(n - 1 - s);
-    const float m = fmaf(-back, w2, kk[s][c]);
-    return (full || s < n) ? m : kEmptyP;
+    const float m = fmaf(-float(n - 1 - s), w2, kk[s][c]);
+    return (FULL || s < n) ? m : kEmptyP;
   };
   float P = kEmptyP;
 #pragma unroll
@@ -112,6 +145,52 @@ __device__ __forceinline__ Hist summarize(const float (&kk)[L][CPL], const float
     Bd += e;
   }
   return n > 0 ? Hist{A, Bd, P, 0.f} : hist_empty();
+}
+
+// Loads of a wave's rows (FULL: all L of them, else the first n; the rest
+// are zero) and its second pass, specialised so that a full wave carries no
+// per-row checks.
+template <int L, int CPL, bool FULL>
+__device__ __forceinline__ void load_rows(Rsrc rk, Rsrc rv, uint32_t voff, uint32_t row_bytes,
+                                          int n, float (&kk)[L][CPL], float (&vv)[L][CPL]) {
+#pragma unroll
+  for (int s = 0; s < L; ++s) {
+    // Rows go through value temporaries: stores into kk/vv from two branches
+    // would otherwise be merged into one store through a pointer select,
+    // which keeps the arrays out of registers.
+    float tk[CPL], tv[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) tk[c] = tv[c] = 0.f;
+    if (FULL || s < n) {
+      load_row<CPL>(rk, voff, uint32_t(s) * row_bytes, tk);
+      load_row<CPL>(rv, voff, uint32_t(s) * row_bytes, tv);
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      kk[s][c] = tk[c];
+      vv[s][c] = tv[c];
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < L; ++s)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) kk[s][c] *= kLog2e;
+}
+
+template <int L, int CPL, bool FULL>
+__device__ __forceinline__ void emit_rows(Rsrc ry, uint32_t voff, uint32_t row_bytes, int n,
+                                          Hist (&hs)[CPL], const float (&kk)[L][CPL],
+                                          const float (&vv)[L][CPL], const float (&u2)[CPL],
+                                          const float (&w2)[CPL]) {
+#pragma unroll
+  for (int s = 0; s < L; ++s) {
+    if (FULL || s < n) {
+      float ys[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) ys[c] = hist_read_push(hs[c], kk[s][c], vv[s][c], u2[c], w2[c]);
+      store_row<CPL>(ry, voff, uint32_t(s) * row_bytes, ys);
+    }
+  }
 }
 
 // Optional recurrent state around a forward call, in the step API's form
@@ -233,28 +312,30 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
   const int t0 = tile_t0 + wid * L;
   const int n = max(0, min(L, T - t0));
   const size_t row0 = (size_t(bi) * size_t(T) + size_t(t0)) * size_t(C) + size_t(cb) * W;
-  const float* kp = k + row0 + cl;
-  const float* vp = v + row0 + cl;
+  // Offsets within a wave's rows stay below 2^31 (checked by the plan).
+  const uint32_t row_bytes = uint32_t(C) * 4u;
+  const uint32_t span = uint32_t(L - 1) * row_bytes + uint32_t(W) * 4u;
+  const Rsrc rk = make_rsrc(k + row0, span);
+  const Rsrc rv = make_rsrc(v + row0, span);
+  const uint32_t voff_in = uint32_t(cl) * 4u;
 
   float kk[L][CPL], vv[L][CPL];
-#pragma unroll
-  for (int s = 0; s < L; ++s) {
-    if (n == L || s < n) {
-      load_vec<CPL>(kp + size_t(s) * C, kk[s]);
-      load_vec<CPL>(vp + size_t(s) * C, vv[s]);
-    } else {
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) kk[s][c] = vv[s][c] = 0.f;
-    }
-  }
-#pragma unroll
-  for (int s = 0; s < L; ++s)
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) kk[s][c] *= kLog2e;
+  const bool full = n == L;
+  if (full)
+    load_rows<L, CPL, true>(rk, rv, voff_in, row_bytes, n, kk, vv);
+  else
+    load_rows<L, CPL, false>(rk, rv, voff_in, row_bytes, n, kk, vv);
 
   // Pass 1: this wave's tokens from an empty history.
+  if (full) {
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) s_sum[wid].put(ch0 + c, summarize<L, CPL>(kk, vv, c, n, w2[c]));
+    for (int c = 0; c < CPL; ++c)
+      s_sum[wid].put(ch0 + c, summarize<L, CPL, true>(kk, vv, c, n, w2[c]));
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+      s_sum[wid].put(ch0 + c, summarize<L, CPL, false>(kk, vv, c, n, w2[c]));
+  }
   __syncthreads();
 
   // Tile prefix: wave 0 publishes the aggregate and looks back.
@@ -391,16 +472,12 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
       for (int i = 0; i < wid; ++i)
         hs[c] = hist_concat(hs[c], s_sum[i].get(ch0 + c), float(L), w2[c]);
     }
-    float* yp = y + row0 + cl;
-#pragma unroll
-    for (int s = 0; s < L; ++s) {
-      if (n == L || s < n) {
-        float ys[CPL];
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) ys[c] = hist_read_push(hs[c], kk[s][c], vv[s][c], u2[c], w2[c]);
-        if (valid) store_vec<CPL>(yp + size_t(s) * C, ys);
-      }
-    }
+    const Rsrc ry = make_rsrc(y + row0, span);
+    const uint32_t voff_out = valid ? uint32_t(ch0) * 4u : kDropOffset;
+    if (full)
+      emit_rows<L, CPL, true>(ry, voff_out, row_bytes, n, hs, kk, vv, u2, w2);
+    else
+      emit_rows<L, CPL, false>(ry, voff_out, row_bytes, n, hs, kk, vv, u2, w2);
   }
 }
 
@@ -522,8 +599,10 @@ bool wkv4_plan(int64_t B, int64_t T, int64_t C, Wkv4Plan* plan) {
   p.n_cblk = (C + 64 * cpl - 1) / (64 * cpl);
   p.groups = B * p.n_cblk;
   // Tiles, token and channel indices are 32-bit in the kernel.
+  // Byte offsets within a wave's rows are 32-bit, below the 2^31 drop offset.
   if (p.n_tiles * p.groups >= (int64_t(1) << 31) || T >= (int64_t(1) << 31) ||
-      C >= (int64_t(1) << 31) || p.groups >= (int64_t(1) << 31))
+      p.groups >= (int64_t(1) << 31) ||
+      (int64_t(L - 1) * C + 64 * cpl) * 4 >= (int64_t(1) << 31))
     return false;
   const size_t ctr_bytes = size_t(p.groups) * kWkv4CounterStride;
   p.slots_offset = (kWkv4HeaderBytes + ctr_bytes + 255) / 256 * 256;
