@@ -226,6 +226,47 @@ def bench_wkv5(torch, rw, cfg, reps):
     return {"ms": ms, "elems": elems, "bytes": 10 * elems, "flops": 4 * cfg.D * elems}
 
 
+def wkv5_step_bytes(B, H, D):
+    """Algorithmic bytes of one Eagle step: the fp32 state read and written,
+    r, k, v in bf16, o in fp32."""
+    return B * H * (2 * D * D * 4 + 3 * D * 2 + D * 4)
+
+
+def bench_wkv5_decode(torch, rw, cfg, reps):
+    import synth
+    dev = torch.device("cuda:0")
+    inp = synth.wkv5_step_inputs(cfg)
+    to = lambda x: torch.from_numpy(x).to(dev)  # noqa: E731
+    # [B, pool, H, D] -> [pool, B, H, D]: one contiguous token per step
+    r, k, v = (to(inp[n + "_bits"]).view(torch.bfloat16).transpose(0, 1).contiguous()
+               for n in ("r", "k", "v"))
+    w, u = to(inp["w"]), to(inp["u"])
+    s = torch.zeros((cfg.B, cfg.H, cfg.D, cfg.D), dtype=torch.float32, device=dev)
+    o = torch.empty((cfg.B, cfg.H, cfg.D), dtype=torch.float32, device=dev)
+    lib = rw.load_library()
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    calls = [(cfg.B, cfg.H, cfg.D, P(s), P(r[i]), P(k[i]), P(v[i]), P(w), P(u), P(o), sh)
+             for i in range(cfg.pool)]
+    fn = lib.rwkv_wkv5_step
+    for i in range(8):
+        assert fn(*calls[i % cfg.pool]) == 0
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st.record(stream)
+        for t in range(cfg.steps):
+            assert fn(*calls[t % cfg.pool]) == 0
+        en.record(stream)
+        torch.cuda.synchronize()
+        ms = st.elapsed_time(en)
+        best = ms if best is None else min(best, ms)
+    assert torch.isfinite(s).all().item()
+    return {"ms": best, "bytes": cfg.steps * wkv5_step_bytes(cfg.B, cfg.H, cfg.D)}
+
+
 def _cpu_name():
     cpu = platform.processor() or platform.machine()
     try:
@@ -289,6 +330,24 @@ def cpu_sample_eagle():
             "sample": f"2 heads x T={cfg.T} x D={cfg.D}, {el:.1f} s"}
 
 
+def cpu_sample_eagle_decode():
+    """Oracle steps for 4 (stream, head) pairs over all steps of the decode."""
+    import numpy as np
+    import oracle.wkv_oracle as O
+    import synth
+    cfg = synth.CFG_WKV5_DECODE
+    inp = synth.wkv5_inputs(4, cfg.pool, 1, cfg.D, cfg.seed)
+    S = np.zeros((4, 1, cfg.D, cfg.D))
+    t0 = time.perf_counter()
+    for t in range(cfg.steps):
+        i = t % cfg.pool
+        _, S = O.wkv5_step(S, inp["w"], inp["u"], inp["r"][:, i], inp["k"][:, i], inp["v"][:, i])
+    el = time.perf_counter() - t0
+    nbytes = cfg.steps * wkv5_step_bytes(4, 1, cfg.D)
+    return {"value": round(nbytes / el / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"4 (stream, head) pairs x {cfg.steps} steps, {el:.2f} s"}
+
+
 def cpu_baseline(cfg, budget_s):
     """The fp64 oracle's recurrence on the full workload, repeated for about
     `budget_s` seconds of host time."""
@@ -324,9 +383,10 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB copy (counter calibration runs)")
-    ap.add_argument("--secondary", default="long,decode,decode-graph,eagle",
-                    help="comma list of secondary workloads: long, decode, decode-graph, eagle")
+                    help="accepted for older command lines; the 1 GiB copy always runs")
+    ap.add_argument("--secondary", default="hot,long,decode,decode-graph,eagle,eagle-decode",
+                    help="comma list of secondary workloads: hot, long, decode, decode-graph, "
+                         "eagle, eagle-decode")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -344,8 +404,7 @@ def main(argv=None):
         return 1
 
     cfg = synth.CFG_WKV4_169M
-    if args.copy_calibration:
-        copy_gbps = bench_copy_peak(torch)
+    copy_gbps = bench_copy_peak(torch)
     log(f"bench: {cfg.name} steps={args.steps} warmup={args.warmup} rotate={args.rotate}")
     prim = bench_wkv4_forward(torch, rw, cfg, args.steps, args.warmup, args.rotate)
     value = prim["bytes"] / (prim["ms_per_step"] * 1e-3) / 1e9
@@ -367,6 +426,7 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "C": cfg.C,
                    "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+                   "pct_of_copy_peak": round(100 * value / copy_gbps, 2),
                    "gelem_per_s": round(prim["elems"] / (prim["ms_per_step"] * 1e-3) / 1e9, 2),
                    "bytes_per_elem": 12, "rotated_copies": args.rotate},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
@@ -375,12 +435,17 @@ def main(argv=None):
                      "kernel_us": round(prim["kernel_ms"] * 1e3, 3),
                      "kernel_source": src_hash},
     }
-    if args.copy_calibration:
-        line["copy_peak_GBps"] = round(copy_gbps, 1)
+    line["copy_peak_GBps"] = round(copy_gbps, 1)
 
     want = set() if args.no_secondary else {x for x in args.secondary.split(",") if x}
     if want:
         sec = {}
+        if "hot" in want:
+            log(f"bench: {cfg.name} hot (one copy of k, v, y)")
+            r = bench_wkv4_forward(torch, rw, cfg, steps=args.steps, warmup=args.warmup, rotate=1)
+            sec[cfg.name + "_hot"] = {
+                "ms": round(r["ms_per_step"], 5), "kernel_ms": round(r["kernel_ms"], 5),
+                "GBps": round(r["bytes"] / (r["ms_per_step"] * 1e-3) / 1e9, 1)}
         if "long" in want:
             lc = synth.CFG_WKV4_LONG
             log(f"bench: {lc.name}")
@@ -407,6 +472,13 @@ def main(argv=None):
             sec[ec.name] = {"ms": round(r["ms"], 4),
                             "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
                             "algorithmic_TFLOPs": round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 2)}
+        if "eagle-decode" in want:
+            ed = synth.CFG_WKV5_DECODE
+            log(f"bench: {ed.name}")
+            r = bench_wkv5_decode(torch, rw, ed, reps=3)
+            sec[ed.name] = {"ms": round(r["ms"], 4),
+                            "us_per_step": round(1e3 * r["ms"] / ed.steps, 3),
+                            "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1)}
         line["secondary"] = sec
 
     if not args.no_cpu_baseline:
@@ -415,7 +487,8 @@ def main(argv=None):
         sec = line.get("secondary", {})
         samplers = {synth.CFG_WKV4_LONG.name: cpu_sample_long,
                     synth.CFG_WKV4_DECODE.name: cpu_sample_decode,
-                    synth.CFG_WKV5_EAGLE.name: cpu_sample_eagle}
+                    synth.CFG_WKV5_EAGLE.name: cpu_sample_eagle,
+                    synth.CFG_WKV5_DECODE.name: cpu_sample_eagle_decode}
         for name, fn in samplers.items():
             if name in sec:
                 sec[name]["cpu_baseline"] = fn()

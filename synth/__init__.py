@@ -26,8 +26,8 @@ import numpy as np
 __all__ = [
     "Wkv4Config", "Wkv4StepConfig", "Wkv5Config",
     "CFG_WKV4_TINY", "CFG_WKV4_169M", "CFG_WKV4_LONG", "CFG_WKV4_DECODE",
-    "CFG_WKV5_EAGLE",
-    "rng_for", "wkv4_inputs", "wkv4_step_inputs", "wkv5_inputs",
+    "CFG_WKV5_EAGLE", "CFG_WKV5_DECODE", "Wkv5StepConfig",
+    "rng_for", "wkv4_inputs", "wkv4_step_inputs", "wkv5_inputs", "wkv5_step_inputs",
     "bf16_bits_from_f32", "f32_from_bf16_bits",
 ]
 
@@ -72,7 +72,18 @@ class Wkv5Config:
     u_std: float = 0.5
 
 
-# The five workloads.  Seeds are 1000 + workload number.
+@dataclasses.dataclass(frozen=True)
+class Wkv5StepConfig:
+    name: str
+    B: int
+    H: int
+    D: int
+    steps: int
+    pool: int
+    seed: int
+
+
+# The workloads.  Seeds are 1000 + workload number.
 CFG_WKV4_TINY = Wkv4Config("wkv4_fwd_B1_T64_C64", 1, 64, 64, 1001)
 CFG_WKV4_169M = Wkv4Config("wkv4_fwd_B8_T1024_C768", 8, 1024, 768, 1002)
 CFG_WKV4_LONG = Wkv4Config("wkv4_fwd_B1_T65536_C5120", 1, 65536, 5120, 1003,
@@ -82,6 +93,9 @@ CFG_WKV4_LONG = Wkv4Config("wkv4_fwd_B1_T65536_C5120", 1, 65536, 5120, 1003,
 # resident on the device.
 CFG_WKV4_DECODE = Wkv4StepConfig("wkv4_step_B256_C4096_x4096", 256, 4096, 4096, 64, 1004)
 CFG_WKV5_EAGLE = Wkv5Config("wkv5_fwd_B4_T4096_H32_D64", 4, 4096, 32, 64, 1005)
+# Eagle decode: 64 streams of 32 heads (a 32 MB fp32 state), 256 steps drawn
+# from a pool of 16 tokens (step t uses token t mod 16).
+CFG_WKV5_DECODE = Wkv5StepConfig("wkv5_step_B64_H32_D64_x256", 64, 32, 64, 256, 16, 1006)
 
 
 def rng_for(seed: int) -> np.random.Generator:
@@ -157,6 +171,12 @@ def wkv5_inputs(B: int, T: int, H: int, D: int, seed: int, *, omega_lo=-6.0,
         out[name + "_bits"] = bits
         out[name] = f32_from_bf16_bits(bits)
     return out
+
+
+def wkv5_step_inputs(cfg: Wkv5StepConfig) -> dict:
+    """Eagle decode inputs: the forward recipe with T = pool, so that
+    ``r[:, t % pool]`` etc. ([B, H, D]) is the token of step t."""
+    return wkv5_inputs(cfg.B, cfg.pool, cfg.H, cfg.D, cfg.seed)
 
 
 def wkv5_inputs_for(cfg: Wkv5Config) -> dict:

@@ -200,3 +200,35 @@ def test_forward_from_a_given_state(dv):
                                     inp["w"], np.abs(inp["u"]), S0=np.abs(s0))
     assert wkv5_scaled_err(o, o_ref, o_abs) <= WKV5_TOL
     assert wkv5_scaled_err(s, s_ref, s_abs) <= WKV5_TOL
+
+
+def test_eagle_decode_workload_sampled_heads():
+    """64 streams x 32 heads, 64 steps from the 16-token pool (the bench's
+    launch shape); the oracle follows 4 sampled (stream, head) pairs."""
+    torch, dev = torch_dev()
+    cfg = synth.CFG_WKV5_DECODE
+    log(f"wkv5_step {cfg.name} (64 steps, sampled pairs)")
+    inp = synth.wkv5_step_inputs(cfg)
+    to = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)  # noqa: E731
+    s = torch.zeros((cfg.B, cfg.H, cfg.D, cfg.D), dtype=torch.float32, device=dev)
+    w, u = to(inp["w"]), to(inp["u"])
+    N = 64
+    outs = []
+    for t in range(N):
+        i = t % cfg.pool
+        r, k, v = (to(inp[n + "_bits"][:, i]).view(torch.bfloat16) for n in ("r", "k", "v"))
+        outs.append(rw.rwkv_wkv5_step(s, r, k, v, w, u))
+    torch.cuda.synchronize()
+    o = torch.stack(outs, dim=1).cpu().numpy()           # [B, N, H, D]
+    pairs = [(0, 0), (17, 5), (40, 31), (63, 12)]
+    idx = np.arange(N) % cfg.pool
+    for b, h in pairs:
+        sel = lambda n: inp[n][b:b + 1][:, idx][:, :, h:h + 1]  # noqa: E731
+        r, k, v = sel("r"), sel("k"), sel("v")
+        o_ref, s_ref = O.wkv5_recurrent(r, k, v, inp["w"][h:h + 1], inp["u"][h:h + 1])
+        o_abs, s_abs = O.wkv5_recurrent(np.abs(r), np.abs(k), np.abs(v), inp["w"][h:h + 1],
+                                        np.abs(inp["u"][h:h + 1]))
+        err_o = wkv5_scaled_err(o[b:b + 1, :, h:h + 1], o_ref, o_abs)
+        err_s = wkv5_scaled_err(s[b:b + 1, h:h + 1].cpu().numpy(), s_ref, s_abs)
+        log(f"  pair {(b, h)}: err o={err_o:.3e} state={err_s:.3e}")
+        assert err_o <= 1e-5 and err_s <= 1e-5
