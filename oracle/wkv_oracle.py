@@ -31,6 +31,12 @@ Conventions (readings of the pages where they are silent or garbled):
   scales key rows; the receptance contracts the key index; the output reads
   the state *before* the current token's update.
 
+RWKV-4 backward: the pages give WKV_t but not its derivatives.  They are
+obtained here by differentiating the definition (chain rule through the
+log-weights), and pinned by central finite differences of ``wkv4_direct``,
+by float64 autograd of an independent torch transcription of the
+definition, and by the k-shift and v-offset invariants.
+
 Pins (tests/test_oracle.py): the direct O(T^2) sum against the recurrence,
 closed forms (T=1, constant v, k=0 geometric series with the simulator's
 w=0.5/u=1 defaults, w=0 prefix softmax against scipy, very large w), the
@@ -45,6 +51,7 @@ import numpy as np
 __all__ = [
     "wkv4_direct", "wkv4_recurrent", "wkv4_scale", "wkv4_empty_state",
     "wkv4_step", "wkv4_canonical_state",
+    "wkv4_backward_direct", "wkv4_backward_recurrent", "wkv4_backward_scale",
     "wkv5_recurrent", "wkv5_unrolled", "wkv5_scale", "wkv5_step",
 ]
 
@@ -157,6 +164,121 @@ def wkv4_canonical_state(state):
     num, den, ref = state
     with np.errstate(divide="ignore", invalid="ignore"):
         return num / den, np.log(den) + ref
+
+
+# ---------------------------------------------------------------------------
+# RWKV-4 backward: gradients of L = sum_{b,t,c} gy[b,t,c] * WKV[b,t,c]
+# ---------------------------------------------------------------------------
+#
+# With alpha_{t,i} the weight of token i in WKV_t (exp(k_i - (t-1-i) w) for
+# i < t, exp(u + k_t) for i = t), D_t = sum_i alpha_{t,i} and
+# p_{t,i} = alpha_{t,i} / D_t, WKV_t = sum_i p_{t,i} v_i, hence
+#   d WKV_t / d v_i            = p_{t,i},
+#   d WKV_t / d log alpha_{t,i} = p_{t,i} (v_i - WKV_t),
+# and log alpha_{t,i} is k_i - (t-1-i) w (i < t) or u + k_t (i = t).
+
+
+def wkv4_backward_direct(w, u, k, v, gy):
+    """The four gradients by the definition above, O(T^2) (tiny inputs).
+
+    w, u: [C]; k, v, gy: [B, T, C].  Returns (gw [C], gu [C], gk [B, T, C],
+    gv [B, T, C]); gw and gu are summed over batch and time.
+    """
+    w, u = _f64(w), _f64(u)
+    k, v, gy = _f64(k), _f64(v), _f64(gy)
+    B, T, C = k.shape
+    gk, gv = np.zeros((B, T, C)), np.zeros((B, T, C))
+    gw, gu = np.zeros(C), np.zeros(C)
+    for t in range(T):
+        age = (t - 1 - np.arange(t))[None, :, None].astype(np.float64)   # [1, t, 1]
+        logit = np.concatenate([k[:, :t] - age * w, (u + k[:, t])[:, None]], axis=1)
+        a = np.exp(logit - logit.max(axis=1, keepdims=True))
+        p = a / a.sum(axis=1, keepdims=True)                               # [B, t+1, C]
+        y = (p * v[:, :t + 1]).sum(axis=1)                                 # [B, C]
+        g = gy[:, t][:, None]                                              # [B, 1, C]
+        gv[:, :t + 1] += g * p
+        dlog = g * p * (v[:, :t + 1] - y[:, None])                         # d L / d log alpha
+        gk[:, :t + 1] += dlog
+        gu += dlog[:, t].sum(axis=0)
+        gw -= (dlog[:, :t] * age).sum(axis=(0, 1))
+    return gw, gu, gk, gv
+
+
+def _wkv4_backward(w, u, k, v, gy, absolute):
+    """Reverse-time evaluation shared by the gradients and their magnitudes.
+
+    Forward: WKV_t and log D_t from the recurrent form.  Reverse, for the
+    terms t > i of each sum:
+      G_i  = sum_{t>i} gy_t e^{-(t-1-i) w - log D_t},      H_i  likewise with gy_t WKV_t,
+      G'_i = sum_{t>i} (t-1-i) gy_t e^{-(t-1-i) w - log D_t}, H'_i likewise,
+    so that G_{i-1} = e^{-w} G_i + gy_i / D_i and G'_{i-1} = e^{-w} (G'_i + G_i).
+    Then (p_ii = e^{u + k_i} / D_i)
+      gv_i = gy_i p_ii + e^{k_i} G_i
+      gk_i = gy_i p_ii (v_i - WKV_i) + e^{k_i} (v_i G_i - H_i)
+      gu   = sum_i gy_i p_ii (v_i - WKV_i)
+      gw   = -sum_i e^{k_i} (v_i G'_i - H'_i).
+    With ``absolute`` every term is replaced by a bound on its magnitude
+    (|gy| for gy, |v_i| + |WKV_t| for v_i - WKV_t).  Exponentials are taken
+    relative to a per-(b, c) shift, the smallest log D_t, so every stored
+    factor is at most 1.
+    """
+    w, u = _f64(w), _f64(u)
+    k, v, gy = _f64(k), _f64(v), _f64(gy)
+    B, T, C = k.shape
+    y = np.empty((B, T, C))
+    logd = np.empty((B, T, C))
+    st = wkv4_empty_state(B, C)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        for t in range(T):
+            num, den, ref = st
+            logd[:, t] = np.logaddexp(np.log(den) + ref, u + k[:, t])
+            y[:, t], st = wkv4_step(st, w, u, k[:, t], v[:, t])
+    if absolute:
+        gy = np.abs(gy)
+    shift = logd.min(axis=1)                              # [B, C]
+    decay = np.exp(-w)
+    G, H, G1, H1 = (np.zeros((B, C)) for _ in range(4))
+    gk, gv = np.empty((B, T, C)), np.empty((B, T, C))
+    gw, gu = np.zeros((B, C)), np.zeros((B, C))
+    for i in range(T - 1, -1, -1):
+        p_ii = np.exp(u + k[:, i] - logd[:, i])
+        ek = np.exp(k[:, i] - shift)
+        g, vi, yi = gy[:, i], v[:, i], y[:, i]
+        if absolute:
+            d_own = np.abs(vi) + np.abs(yi)
+            gv[:, i] = g * p_ii + ek * G
+            gk[:, i] = g * p_ii * d_own + ek * (np.abs(vi) * G + H)
+            gw += ek * (np.abs(vi) * G1 + H1)
+        else:
+            d_own = vi - yi
+            gv[:, i] = g * p_ii + ek * G
+            gk[:, i] = g * p_ii * d_own + ek * (vi * G - H)
+            gw -= ek * (vi * G1 - H1)
+        gu += g * p_ii * d_own
+        # terms of token i for the sums seen from i - 1
+        f = np.exp(shift - logd[:, i])
+        yi_t = np.abs(yi) if absolute else yi
+        G1 = decay * (G1 + G)
+        H1 = decay * (H1 + H)
+        G = decay * G + g * f
+        H = decay * H + g * yi_t * f
+    return gw.sum(axis=0), gu.sum(axis=0), gk, gv
+
+
+def wkv4_backward_recurrent(w, u, k, v, gy):
+    """The four gradients in O(T) by reverse-time sums (any length).
+
+    Same result as ``wkv4_backward_direct`` up to rounding.  Returns
+    (gw [C], gu [C], gk [B, T, C], gv [B, T, C]).
+    """
+    return _wkv4_backward(w, u, k, v, gy, absolute=False)
+
+
+def wkv4_backward_scale(w, u, k, v, gy):
+    """Magnitudes against which rounding errors of the gradients are measured:
+    the same sums with every term replaced by its absolute bound.  Each is
+    >= the magnitude of the matching gradient.  Returns (gw, gu, gk, gv)."""
+    return _wkv4_backward(w, u, k, v, gy, absolute=True)
 
 
 # ---------------------------------------------------------------------------

@@ -292,6 +292,99 @@ def test_eagle_split_sequence():
     np.testing.assert_allclose(S2, S_all, rtol=1e-13, atol=1e-16)
 
 
+# ------------------------------------------------- RWKV-4 backward pins ---
+
+def _grad_case(B=2, T=24, C=6, seed=11, **kw):
+    inp = synth.wkv4_inputs(B, T, C, seed, **kw)
+    gy = synth.rng_for(seed + 100).standard_normal((B, T, C))
+    return inp, gy
+
+
+def _grads(fn, inp, gy):
+    return fn(inp["w"], inp["u"], inp["k"], inp["v"], gy)
+
+
+@pytest.mark.parametrize("kw", [{}, {"k_std": 3.0, "omega_lo": -5.0, "omega_hi": 2.0},
+                                {"omega_lo": -8.0, "omega_hi": -6.0}])
+def test_backward_direct_equals_recurrence(kw):
+    inp, gy = _grad_case(**kw)
+    d = _grads(O.wkv4_backward_direct, inp, gy)
+    r = _grads(O.wkv4_backward_recurrent, inp, gy)
+    sc = _grads(O.wkv4_backward_scale, inp, gy)
+    for a, b, m in zip(d, r, sc):
+        assert _rel(a, b, m) < 1e-12
+
+
+def test_backward_key_shift_is_harmless():
+    inp, gy = _grad_case()
+    ref = _grads(O.wkv4_backward_recurrent, inp, gy)
+    shifted = _grads(O.wkv4_backward_recurrent, dict(inp, k=inp["k"].astype(np.float64) + 80.0),
+                     gy)
+    sc = _grads(O.wkv4_backward_scale, inp, gy)
+    for a, b, m in zip(ref, shifted, sc):
+        assert _rel(a, b, m) < 1e-10
+
+
+def test_backward_matches_finite_differences():
+    """Central differences of the direct forward sum, every input scalar."""
+    inp, gy = _grad_case(B=1, T=7, C=3, seed=5)
+    args = {n: np.asarray(inp[n], np.float64) for n in ("w", "u", "k", "v")}
+
+    def loss(a):
+        return float((O.wkv4_direct(a["w"], a["u"], a["k"], a["v"]) * gy).sum())
+
+    gw, gu, gk, gv = O.wkv4_backward_direct(args["w"], args["u"], args["k"], args["v"], gy)
+    h = 1e-6
+    for name, g in (("w", gw), ("u", gu), ("k", gk), ("v", gv)):
+        fd = np.zeros_like(g)
+        for idx in np.ndindex(g.shape):
+            plus = {n: a.copy() for n, a in args.items()}
+            minus = {n: a.copy() for n, a in args.items()}
+            plus[name][idx] += h
+            minus[name][idx] -= h
+            fd[idx] = (loss(plus) - loss(minus)) / (2 * h)
+        np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+def test_backward_matches_autograd_of_the_definition():
+    """float64 autograd through an independent torch transcription of WKV_t."""
+    torch = pytest.importorskip("torch")
+    inp, gy = _grad_case(B=2, T=12, C=4, seed=9)
+    w, u, k, v = (torch.tensor(np.asarray(inp[n], np.float64), requires_grad=True)
+                  for n in ("w", "u", "k", "v"))
+    T = k.shape[1]
+    ys = []
+    for t in range(T):
+        age = torch.arange(t - 1, -1, -1, dtype=torch.float64)[None, :, None]
+        logits = torch.cat([k[:, :t] - age * w, (u + k[:, t])[:, None]], dim=1)
+        ys.append((torch.softmax(logits, dim=1) * v[:, :t + 1]).sum(dim=1))
+    (torch.stack(ys, dim=1) * torch.tensor(gy)).sum().backward()
+    got = O.wkv4_backward_direct(inp["w"], inp["u"], inp["k"], inp["v"], gy)
+    for g, t_ in zip(got, (w, u, k, v)):
+        np.testing.assert_allclose(g, t_.grad.numpy(), rtol=1e-11, atol=1e-13)
+
+
+def test_backward_invariants():
+    inp, gy = _grad_case(T=30)
+    gw, gu, gk, gv = _grads(O.wkv4_backward_recurrent, inp, gy)
+    # y is unchanged by k -> k + c and moves by b under v -> v + b
+    np.testing.assert_allclose(gk.sum(axis=1), 0.0, atol=1e-11)
+    np.testing.assert_allclose(gv.sum(axis=1), gy.sum(axis=1), rtol=1e-11, atol=1e-12)
+    # a single token: y = v whatever w, u, k
+    one = {n: (inp[n][:, :1] if n in ("k", "v") else inp[n]) for n in inp}
+    gw1, gu1, gk1, gv1 = _grads(O.wkv4_backward_recurrent, one, gy[:, :1])
+    assert np.all(gw1 == 0) and np.all(gu1 == 0) and np.all(gk1 == 0)
+    np.testing.assert_allclose(gv1, gy[:, :1], rtol=1e-15)
+
+
+def test_backward_scale_bounds_every_gradient():
+    inp, gy = _grad_case(k_std=3.0)
+    got = _grads(O.wkv4_backward_recurrent, inp, gy)
+    sc = _grads(O.wkv4_backward_scale, inp, gy)
+    for g, m in zip(got, sc):
+        assert np.all(np.abs(g) <= m * (1 + 1e-12) + 1e-300)
+
+
 # ------------------------------------------------------- planted mistakes ---
 
 _WKV4_STEP = O.wkv4_step
@@ -318,6 +411,15 @@ def test_pins_catch_planted_wkv4_mistakes(monkeypatch, mutant):
     yd = O.wkv4_direct(inp["w"], inp["u"], inp["k"], inp["v"])
     yr, _ = O.wkv4_recurrent(inp["w"], inp["u"], inp["k"], inp["v"])
     assert np.max(np.abs(yd - yr)) > 1e-3
+
+
+def test_pins_catch_planted_backward_mistake(monkeypatch):
+    # a forward without the bonus inside the reverse-time evaluation
+    monkeypatch.setattr(O, "wkv4_step", _mut_no_bonus)
+    inp, gy = _grad_case()
+    d = _grads(O.wkv4_backward_direct, inp, gy)
+    r = _grads(O.wkv4_backward_recurrent, inp, gy)
+    assert max(float(np.max(np.abs(a - b))) for a, b in zip(d, r)) > 1e-3
 
 
 def test_pins_catch_transposed_eagle_state(monkeypatch):
