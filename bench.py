@@ -133,6 +133,54 @@ def bench_wkv4_forward(torch, rw, cfg, steps, warmup, rotate):
             "elems": B * T * C, "bytes": 12 * B * T * C}
 
 
+def bench_wkv4_backward(torch, rw, cfg, steps, warmup):
+    """One backward call (prefix pass, reverse scan, reduction) per step."""
+    import synth
+    dev = torch.device("cuda:0")
+    inp = synth.wkv4_backward_inputs(cfg.B, cfg.T, cfg.C, cfg.seed, omega_lo=cfg.omega_lo,
+                                     omega_hi=cfg.omega_hi, u_std=cfg.u_std, k_std=cfg.k_std,
+                                     v_std=cfg.v_std)
+    B, T, C = cfg.B, cfg.T, cfg.C
+    w, u, k, v, gy = (torch.from_numpy(inp[n]).to(dev) for n in ("w", "u", "k", "v", "gy"))
+    gw, gu = torch.empty_like(w), torch.empty_like(u)
+    gk, gv = torch.empty_like(k), torch.empty_like(k)
+    lib = rw.load_library()
+    need = lib.rwkv_wkv4_backward_workspace(B, T, C)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    args = (B, T, C, P(w), P(u), P(k), P(v), P(gy), P(gw), P(gu), P(gk), P(gv), P(ws), need,
+            ctypes.c_void_p(stream.cuda_stream))
+    fn = lib.rwkv_wkv4_backward
+    for _ in range(warmup):
+        assert fn(*args) == 0
+    torch.cuda.synchronize()
+    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st.record(stream)
+    for _ in range(steps):
+        assert fn(*args) == 0
+    en.record(stream)
+    torch.cuda.synchronize()
+    assert torch.isfinite(gk).all().item() and torch.isfinite(gw).all().item()
+    ms = st.elapsed_time(en) / steps
+    return {"ms": ms, "elems": B * T * C, "bytes": 20 * B * T * C}
+
+
+def cpu_sample_backward():
+    """Oracle backward (reverse-time form) on 32 channels of the 8x1024x768
+    workload, full T."""
+    import oracle.wkv_oracle as O
+    import synth
+    cfg = synth.CFG_WKV4_169M
+    inp = synth.wkv4_backward_inputs(cfg.B, cfg.T, 32, cfg.seed)
+    t0 = time.perf_counter()
+    O.wkv4_backward_recurrent(inp["w"], inp["u"], inp["k"], inp["v"], inp["gy"])
+    el = time.perf_counter() - t0
+    elems = cfg.B * cfg.T * 32
+    return {"value": round(20 * elems / el / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"B={cfg.B} T={cfg.T} x 32 channels, {el:.2f} s"}
+
+
 def bench_copy_peak(torch, nbytes=1 << 30, reps=20):
     dev = torch.device("cuda:0")
     a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -384,9 +432,10 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="accepted for older command lines; the 1 GiB copy always runs")
-    ap.add_argument("--secondary", default="hot,long,decode,decode-graph,eagle,eagle-decode",
+    ap.add_argument("--secondary",
+                    default="hot,long,decode,decode-graph,eagle,eagle-decode,backward,backward-long",
                     help="comma list of secondary workloads: hot, long, decode, decode-graph, "
-                         "eagle, eagle-decode")
+                         "eagle, eagle-decode, backward, backward-long")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -472,6 +521,15 @@ def main(argv=None):
             sec[ec.name] = {"ms": round(r["ms"], 4),
                             "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
                             "algorithmic_TFLOPs": round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 2)}
+        for key, bc, n_steps in (("backward", cfg, 100), ("backward-long", synth.CFG_WKV4_LONG, 3)):
+            if key in want:
+                name = bc.name.replace("wkv4_fwd", "wkv4_bwd")
+                log(f"bench: {name}")
+                r = bench_wkv4_backward(torch, rw, bc, steps=n_steps, warmup=2)
+                sec[name] = {"ms": round(r["ms"], 5),
+                             "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
+                             "bytes_per_elem": 20,
+                             "gelem_per_s": round(r["elems"] / (r["ms"] * 1e-3) / 1e9, 1)}
         if "eagle-decode" in want:
             ed = synth.CFG_WKV5_DECODE
             log(f"bench: {ed.name}")
@@ -488,7 +546,8 @@ def main(argv=None):
         samplers = {synth.CFG_WKV4_LONG.name: cpu_sample_long,
                     synth.CFG_WKV4_DECODE.name: cpu_sample_decode,
                     synth.CFG_WKV5_EAGLE.name: cpu_sample_eagle,
-                    synth.CFG_WKV5_DECODE.name: cpu_sample_eagle_decode}
+                    synth.CFG_WKV5_DECODE.name: cpu_sample_eagle_decode,
+                    synth.CFG_WKV4_169M.name.replace("wkv4_fwd", "wkv4_bwd"): cpu_sample_backward}
         for name, fn in samplers.items():
             if name in sec:
                 sec[name]["cpu_baseline"] = fn()

@@ -89,6 +89,35 @@ int rwkv_wkv4_forward(int64_t B, int64_t T, int64_t C,
                       void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * RWKV-4 backward: gradients of L = sum_{b,t,c} gy[b,t,c] * y[b,t,c], with y
+ * the output of rwkv_wkv4_forward (empty starting history).
+ * [RWKV-digest] (2) Time-mixing, WKV_t; the pages give no derivatives.  With
+ * p[t,i] the normalised weight of token i in y[t] (per b, c):
+ *   gv[b,i,c] = sum_{t>=i} gy[b,t,c] p[t,i]
+ *   gk[b,i,c] = sum_{t>=i} gy[b,t,c] p[t,i] (v[b,i,c] - y[b,t,c])
+ *   gu[c]     = sum_{b,t} gy[b,t,c] p[t,t] (v[b,t,c] - y[b,t,c])
+ *   gw[c]     = -sum_{b,t} sum_{i<t} (t-1-i) gy[b,t,c] p[t,i] (v[b,i,c] - y[b,t,c])
+ *
+ *   w, u        [C]      float32  as for the forward
+ *   k, v, gy    [B,T,C]  float32
+ *   gw, gu      [C]      float32  output (overwritten, summed over b and t)
+ *   gk, gv      [B,T,C]  float32  output
+ *   ws, ws_bytes         device workspace of at least
+ *                        rwkv_wkv4_backward_workspace(B,T,C) bytes, zero-filled
+ *                        before its first use (as for the forward; it is not
+ *                        interchangeable with a forward workspace).
+ * Deterministic: repeated calls give the same bits.  Accuracy: each gradient
+ * within 1e-4 of the same sum taken over absolute terms (|gy|, and
+ * |v| + |y| for v - y).
+ * ---------------------------------------------------------------------- */
+size_t rwkv_wkv4_backward_workspace(int64_t B, int64_t T, int64_t C);
+int rwkv_wkv4_backward(int64_t B, int64_t T, int64_t C,
+                       const float* w, const float* u,
+                       const float* k, const float* v, const float* gy,
+                       float* gw, float* gu, float* gk, float* gv,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * RWKV-4 recurrent state.   [RWKV-digest] (2) Time-mixing, recurrent form
  *   a_t = e^{-w} a_{t-1} + e^{k_t} v_t,   b_t = e^{-w} b_{t-1} + e^{k_t}.
  * The library stores the sums scaled: a_true = a * e^{p}, b_true = b * e^{p},

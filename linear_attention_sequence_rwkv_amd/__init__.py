@@ -41,6 +41,9 @@ _SIGNATURES = {
     "rwkv_wkv4_forward": (ctypes.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "rwkv_wkv4_forward_state": (ctypes.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _p,
                                                _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "rwkv_wkv4_backward_workspace": (_sz, [_i64, _i64, _i64]),
+    "rwkv_wkv4_backward": (ctypes.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                          _p, _sz, _p]),
     "rwkv_wkv4_state_init": (ctypes.c_int, [_i64, _i64, _p, _p, _p, _p]),
     "rwkv_wkv4_step": (ctypes.c_int, [_i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "rwkv_wkv5_forward_workspace": (_sz, [_i64, _i64, _i64, _i64]),
@@ -159,7 +162,7 @@ def rwkv_wkv4_forward_workspace(B: int, T: int, C: int) -> int:
     return int(load_library().rwkv_wkv4_forward_workspace(B, T, C))
 
 
-def _wkv4_forward_args(w, u, k, v, y):
+def _wkv4_inputs(w, u, k, v):
     torch = _torch()
     f32 = (torch.float32,)
     k = _dev_tensor("k", k, f32, 3)
@@ -169,6 +172,14 @@ def _wkv4_forward_args(w, u, k, v, y):
     B, T, C = k.shape
     if tuple(v.shape) != (B, T, C) or w.shape[0] != C or u.shape[0] != C:
         raise ValueError("shape mismatch among w, u, k, v")
+    return w, u, k, v
+
+
+def _wkv4_forward_args(w, u, k, v, y):
+    torch = _torch()
+    f32 = (torch.float32,)
+    w, u, k, v = _wkv4_inputs(w, u, k, v)
+    B, T, C = k.shape
     if y is None:
         y = torch.empty_like(k)
     else:
@@ -240,6 +251,48 @@ def rwkv_wkv4_forward_state(w, u, k, v, state_in=None, state_out=None, y=None, w
                                          _ptr(ws), nbytes, st)
     _check("rwkv_wkv4_forward_state", status)
     return y, (None if state_out is None else sout)
+
+
+def rwkv_wkv4_backward_workspace(B: int, T: int, C: int) -> int:
+    return int(load_library().rwkv_wkv4_backward_workspace(B, T, C))
+
+
+def rwkv_wkv4_backward(w, u, k, v, gy, gw=None, gu=None, gk=None, gv=None, ws=None,
+                       stream=None):
+    """Gradients of sum(gy * WKV(w, u, k, v)).  Returns (gw, gu, gk, gv).
+
+    ``ws`` (optional) is a caller-owned zero-initialised uint8 GPU tensor of at
+    least rwkv_wkv4_backward_workspace(B, T, C) bytes; by default a cached one
+    per (device, stream) is used.
+    """
+    torch = _torch()
+    lib = load_library()
+    f32 = (torch.float32,)
+    w, u, k, v = _wkv4_inputs(w, u, k, v)
+    B, T, C = k.shape
+    gy = _dev_tensor("gy", gy, f32, 3)
+    if tuple(gy.shape) != (B, T, C):
+        raise ValueError("gy has the wrong shape")
+
+    def out(name, t, shape):
+        if t is None:
+            return torch.empty(shape, dtype=torch.float32, device=k.device)
+        t = _dev_tensor(name, t, f32, len(shape))
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} has the wrong shape")
+        return t
+
+    gw, gu = out("gw", gw, (C,)), out("gu", gu, (C,))
+    gk, gv = out("gk", gk, (B, T, C)), out("gv", gv, (B, T, C))
+    st = _stream(k.device, stream)
+    need = lib.rwkv_wkv4_backward_workspace(B, T, C)
+    if ws is None:
+        ws = _workspace("wkv4_bwd", k.device, st.value or 0, need)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    status = lib.rwkv_wkv4_backward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(gy),
+                                    _ptr(gw), _ptr(gu), _ptr(gk), _ptr(gv), _ptr(ws), nbytes, st)
+    _check("rwkv_wkv4_backward", status)
+    return gw, gu, gk, gv
 
 
 def rwkv_wkv4_state_init(B: int, C: int, device="cuda", stream=None):

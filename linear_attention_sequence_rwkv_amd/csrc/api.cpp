@@ -144,6 +144,33 @@ RWKV_API int rwkv_wkv4_step(int64_t B, int64_t C, float* a, float* b, float* p, 
   return hip_status(rwkv::wkv4_step_launch(B, C, a, b, p, w, u, k, v, y, stream));
 }
 
+RWKV_API size_t rwkv_wkv4_backward_workspace(int64_t B, int64_t T, int64_t C) {
+  int64_t n;
+  if (!dims_ok({B, T, C}, &n) || n == 0) return 0;
+  rwkv::Wkv4BwdPlan plan;
+  if (!rwkv::wkv4_backward_plan(B, T, C, &plan)) return 0;
+  return plan.ws_bytes;
+}
+
+RWKV_API int rwkv_wkv4_backward(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                                const float* k, const float* v, const float* gy, float* gw,
+                                float* gu, float* gk, float* gv, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  int64_t n;
+  if (!dims_ok({B, T, C}, &n)) return RWKV_ERR_SHAPE;
+  if (n == 0) return RWKV_OK;
+  if (!w || !u || !k || !v || !gy || !gw || !gu || !gk || !gv) return RWKV_ERR_NULLPTR;
+  if (!aligned16(w) || !aligned16(u) || !aligned16(k) || !aligned16(v) || !aligned16(gy) ||
+      !aligned16(gw) || !aligned16(gu) || !aligned16(gk) || !aligned16(gv))
+    return RWKV_ERR_ALIGN;
+  rwkv::Wkv4BwdPlan plan;
+  if (!rwkv::wkv4_backward_plan(B, T, C, &plan)) return RWKV_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < plan.ws_bytes) return RWKV_ERR_WORKSPACE;
+  if (!aligned16(ws)) return RWKV_ERR_ALIGN;
+  return hip_status(
+      rwkv::wkv4_backward_launch(plan, B, T, C, w, u, k, v, gy, gw, gu, gk, gv, ws, stream));
+}
+
 // ------------------------------------------------------------------- Eagle
 
 RWKV_API size_t rwkv_wkv5_forward_workspace(int64_t B, int64_t T, int64_t H, int64_t D) {

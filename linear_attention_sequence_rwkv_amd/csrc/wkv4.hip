@@ -28,6 +28,7 @@
 // carries the call's tag, the workspace epoch + 1, which the call that
 // completes advances; nothing is reset between calls whatever their shapes,
 // and launches replayed from a captured graph stay correct.
+#include "wkv4_scan.h"
 #include "wkv_device.h"
 #include "wkv_internal.h"
 
@@ -39,143 +40,7 @@ namespace rwkv {
 
 namespace {
 
-// Look-back polls without progress before a workgroup gives up (seconds);
-// it then raises the error word and writes NaN, so no wait lasts forever.
-constexpr uint32_t kSpinLimit = 1u << 24;
-// Earlier tiles polled per round trip by the look-back.
-constexpr int kWin = 16;
-
-__device__ __forceinline__ void raise_error(uint32_t* err, uint32_t bit) {
-  __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Header words (uint32) at the start of the forward workspace.
-enum : int { kHdrError = 0, kHdrEpoch = 1, kHdrClaimed = 2 };
-
-__device__ __forceinline__ uint32_t hdr_load(uint32_t* h, int i) {
-  return __hip_atomic_load(h + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void hdr_store(uint32_t* h, int i, uint32_t x) {
-  __hip_atomic_store(h + i, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t hdr_add(uint32_t* h, int i, uint32_t x) {
-  return __hip_atomic_fetch_add(h + i, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// k, v and y stream through buffer resources: a row's offset (s * C * 4
-// bytes, the same for the whole wave) goes in a scalar register and the
-// lane's channel offset in a vector register, so no 64-bit vector address
-// arithmetic is spent per row.  Every byte is touched once: loads and stores
-// are non-temporal.  A store whose offset is at or beyond the resource's
-// size is dropped by the hardware; lanes without a channel use that.
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit access, gfx9 family
-constexpr int kNonTemporal = 2;
-constexpr uint32_t kDropOffset = 0x80000000u;
-
-__device__ __forceinline__ Rsrc make_rsrc(const float* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, int(bytes), kRsrcWord3);
-}
-
-// CPL adjacent floats of one row, loaded/stored with a single vector access.
-template <int CPL>
-__device__ __forceinline__ void load_row(Rsrc r, uint32_t voff, uint32_t soff,
-                                         float (&x)[CPL]) {
-  if constexpr (CPL == 4) {
-    typedef int iv4 __attribute__((ext_vector_type(4)));
-    const float4 t = __builtin_bit_cast(
-        float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNonTemporal));
-    x[0] = t.x;
-    x[1] = t.y;
-    x[2] = t.z;
-    x[3] = t.w;
-  } else if constexpr (CPL == 2) {
-    const float2 t = __builtin_bit_cast(
-        float2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kNonTemporal));
-    x[0] = t.x;
-    x[1] = t.y;
-  } else {
-    x[0] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kNonTemporal));
-  }
-}
-
-template <int CPL>
-__device__ __forceinline__ void store_row(Rsrc r, uint32_t voff, uint32_t soff,
-                                          const float (&x)[CPL]) {
-  if constexpr (CPL == 4) {
-    typedef int iv4 __attribute__((ext_vector_type(4)));
-    const iv4 t = {__float_as_int(x[0]), __float_as_int(x[1]), __float_as_int(x[2]),
-                   __float_as_int(x[3])};
-    // A store wider than 8 bytes must not see its data registers rewritten
-    // in the next cycle.  The compiler inserts that wait state only when the
-    // scalar offset is a constant, so the row offset moves into the vector
-    // offset here (with a register soffset the first data register was
-    // observed to be overwritten before it was stored).
-    __builtin_amdgcn_raw_buffer_store_b128(t, r, voff + soff, 0, kNonTemporal);
-  } else if constexpr (CPL == 2) {
-    typedef int iv2 __attribute__((ext_vector_type(2)));
-    const iv2 t = {__float_as_int(x[0]), __float_as_int(x[1])};
-    __builtin_amdgcn_raw_buffer_store_b64(t, r, voff, soff, kNonTemporal);
-  } else {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(x[0]), r, voff, soff, kNonTemporal);
-  }
-}
-
-// History of `n` tokens (n <= L) of one channel from an empty start,
-// evaluated after the last one, with a fixed reference instead of a running
-// maximum: token s has log2-weight m_s = k2_s - (n-1-s) w2; with
-// P = max_s m_s every term is 2^(m_s - P) <= 1 and the largest is exactly 1,
-// so nothing overflows and the sum never underflows to 0.
-template <int L, int CPL, bool FULL>
-__device__ __forceinline__ Hist summarize(const float (&kk)[L][CPL], const float (&vv)[L][CPL],
-                                          int c, int n, float w2) {
-  if constexpr (FULL) n = L;
-  auto expo = [&](int s) {
-    const float m = fmaf(-float(n - 1 - s), w2, kk[s][c]);
-    return (FULL || s < n) ? m : kEmptyP;
-  };
-  float P = kEmptyP;
-#pragma unroll
-  for (int s = 0; s < L; ++s) P = fmaxf(P, expo(s));
-  float A = 0.f, Bd = 0.f;
-#pragma unroll
-  for (int s = 0; s < L; ++s) {
-    const float e = exp2_fast(expo(s) - P);  // exactly 0 for padding tokens
-    A = fmaf(e, vv[s][c], A);
-    Bd += e;
-  }
-  return n > 0 ? Hist{A, Bd, P, 0.f} : hist_empty();
-}
-
-// Loads of a wave's rows (FULL: all L of them, else the first n; the rest
-// are zero) and its second pass, specialised so that a full wave carries no
-// per-row checks.
-template <int L, int CPL, bool FULL>
-__device__ __forceinline__ void load_rows(Rsrc rk, Rsrc rv, uint32_t voff, uint32_t row_bytes,
-                                          int n, float (&kk)[L][CPL], float (&vv)[L][CPL]) {
-#pragma unroll
-  for (int s = 0; s < L; ++s) {
-    // Rows go through value temporaries: stores into kk/vv from two branches
-    // would otherwise be merged into one store through a pointer select,
-    // which keeps the arrays out of registers.
-    float tk[CPL], tv[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) tk[c] = tv[c] = 0.f;
-    if (FULL || s < n) {
-      load_row<CPL>(rk, voff, uint32_t(s) * row_bytes, tk);
-      load_row<CPL>(rv, voff, uint32_t(s) * row_bytes, tv);
-    }
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      kk[s][c] = tk[c];
-      vv[s][c] = tv[c];
-    }
-  }
-#pragma unroll
-  for (int s = 0; s < L; ++s)
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) kk[s][c] *= kLog2e;
-}
+using namespace scan;
 
 template <int L, int CPL, bool FULL>
 __device__ __forceinline__ void emit_rows(Rsrc ry, uint32_t voff, uint32_t row_bytes, int n,
@@ -217,22 +82,9 @@ __device__ __forceinline__ void write_state(const StateIO& sio, const Hist (&h)[
   }
 }
 
-// Shared-memory copy of per-channel histories, [field][channel].
-template <int W>
-struct HistLds {
-  float f[4][W];
-  __device__ __forceinline__ Hist get(int ch) const {
-    return Hist{f[0][ch], f[1][ch], f[2][ch], f[3][ch]};
-  }
-  __device__ __forceinline__ void put(int ch, const Hist& h) {
-    f[0][ch] = h.A;
-    f[1][ch] = h.Bd;
-    f[2][ch] = h.kr;
-    f[3][ch] = h.n;
-  }
-};
-
-template <int CPL, int L, int NW>
+// EMIT = false: publish the tiles' histories only (the backward's prefix
+// pass); no output rows, no state.
+template <int CPL, int L, int NW, bool EMIT = true>
 __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
     int T, int C, int n_cblk, int groups, int n_tiles,
     const float* __restrict__ w, const float* __restrict__ u,
@@ -254,37 +106,8 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = int(blockIdx.x) % groups;
   if (threadIdx.x == 0) {
-    // The call's tag is the workspace epoch + 1 (read on the device, so a
-    // launch replayed from a captured graph still gets a fresh tag).  Claim
-    // the next tile of this block from its counter word {tag, count}.
-    const uint32_t tg = hdr_load(hdr, kHdrEpoch) + 1u;
-    uint64_t* ctr = counters + size_t(g) * (kWkv4CounterStride / sizeof(uint64_t));
-    // The claim must not be performed before the epoch read has returned
-    // (else this workgroup could see an epoch advanced after its claim): tie
-    // the increment to the loaded value.
-    uint64_t one = 1;
-    asm volatile("" : "+v"(one) : "v"(tg));
-    uint64_t old = __hip_atomic_fetch_add(ctr, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (uint32_t(old >> 32) != tg) {
-      // The word is left over from a call of another shape: raise it to
-      // {tag, 0} (earlier tags are smaller) and claim again.
-      __hip_atomic_fetch_max(ctr, uint64_t(tg) << 32, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-      old = __hip_atomic_fetch_add(ctr, uint64_t(1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    const int t = uint32_t(old >> 32) == tg ? int(uint32_t(old)) : -1;
-    if (t == n_tiles - 1) {
-      // Every tile of this block is claimed: prime the counter for the next
-      // call, and the block that completes all claims advances the epoch
-      // (every workgroup of this call has read it by then).
-      __hip_atomic_store(ctr, uint64_t(tg + 1u) << 32, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-      if (hdr_add(hdr, kHdrClaimed, 1u) == uint32_t(groups - 1)) {
-        hdr_store(hdr, kHdrClaimed, 0u);
-        hdr_store(hdr, kHdrEpoch, tg);
-      }
-    }
-    s_tile = t;
+    uint32_t tg;
+    s_tile = claim_tile(hdr, counters, g, n_tiles, groups, tg);
     s_tag = tg;
   }
   __syncthreads();
@@ -464,7 +287,7 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
   __syncthreads();
 
   // Pass 2: start from the tile prefix plus the earlier waves, emit y.
-  if (n > 0) {
+  if (EMIT && n > 0) {
     Hist hs[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
@@ -570,8 +393,31 @@ hipError_t launch_tiled(const Wkv4Plan& pl, int64_t T, int64_t C, const float* w
 
 }  // namespace
 
+bool wkv4_plan_fixed(int64_t B, int64_t T, int64_t C, int cpl, int L, int NW, Wkv4Plan* plan) {
+  Wkv4Plan p;
+  p.cpl = cpl;
+  p.L = L;
+  p.NW = NW;
+  p.tile = int64_t(L) * NW;
+  p.n_tiles = (T + p.tile - 1) / p.tile;
+  p.n_cblk = (C + 64 * cpl - 1) / (64 * cpl);
+  p.groups = B * p.n_cblk;
+  // Tiles, token and channel indices are 32-bit in the kernel; byte offsets
+  // within a wave's rows are 32-bit, below the 2^31 drop offset.
+  if (p.n_tiles * p.groups >= (int64_t(1) << 31) || T >= (int64_t(1) << 31) ||
+      p.groups >= (int64_t(1) << 31) ||
+      (int64_t(L - 1) * C + 64 * cpl) * 4 >= (int64_t(1) << 31))
+    return false;
+  const size_t ctr_bytes = size_t(p.groups) * kWkv4CounterStride;
+  p.slots_offset = (kWkv4HeaderBytes + ctr_bytes + 255) / 256 * 256;
+  p.ws_bytes = p.slots_offset + size_t(p.n_tiles) * size_t(p.groups) * 8 * 64 * size_t(cpl) *
+                                    sizeof(uint64_t);
+  *plan = p;
+  return true;
+}
+
 bool wkv4_plan(int64_t B, int64_t T, int64_t C, Wkv4Plan* plan) {
-  // One channel per lane, 32 tokens per wave, 4 waves per tile: about 100
+  // One channel per lane, 32 tokens per wave, 4 waves per tile: about 116
   // VGPRs (4 waves per SIMD).  Measured faster than wider vector loads with
   // several channels per lane, which lengthen each lane's serial scan.
   int cpl = 1, L = 32, NW = 4;
@@ -590,26 +436,23 @@ bool wkv4_plan(int64_t B, int64_t T, int64_t C, Wkv4Plan* plan) {
         }
     }
   }
-  Wkv4Plan p;
-  p.cpl = cpl;
-  p.L = L;
-  p.NW = NW;
-  p.tile = int64_t(L) * NW;
-  p.n_tiles = (T + p.tile - 1) / p.tile;
-  p.n_cblk = (C + 64 * cpl - 1) / (64 * cpl);
-  p.groups = B * p.n_cblk;
-  // Tiles, token and channel indices are 32-bit in the kernel.
-  // Byte offsets within a wave's rows are 32-bit, below the 2^31 drop offset.
-  if (p.n_tiles * p.groups >= (int64_t(1) << 31) || T >= (int64_t(1) << 31) ||
-      p.groups >= (int64_t(1) << 31) ||
-      (int64_t(L - 1) * C + 64 * cpl) * 4 >= (int64_t(1) << 31))
-    return false;
-  const size_t ctr_bytes = size_t(p.groups) * kWkv4CounterStride;
-  p.slots_offset = (kWkv4HeaderBytes + ctr_bytes + 255) / 256 * 256;
-  p.ws_bytes = p.slots_offset + size_t(p.n_tiles) * size_t(p.groups) * 8 * 64 * size_t(cpl) *
-                                    sizeof(uint64_t);
-  *plan = p;
-  return true;
+  return wkv4_plan_fixed(B, T, C, cpl, L, NW, plan);
+}
+
+hipError_t wkv4_prefix_launch(const Wkv4Plan& pl, int64_t T, int64_t C, const float* w,
+                              const float* u, const float* k, const float* v, void* ws,
+                              hipStream_t stream) {
+  if (pl.cpl != 1 || pl.L != 16 || pl.NW != 4) return hipErrorInvalidValue;
+  char* base = static_cast<char*>(ws);
+  uint32_t* hdr = reinterpret_cast<uint32_t*>(base);
+  uint64_t* counters = reinterpret_cast<uint64_t*>(base + kWkv4HeaderBytes);
+  uint64_t* slots = reinterpret_cast<uint64_t*>(base + pl.slots_offset);
+  const unsigned grid = unsigned(pl.n_tiles * pl.groups);
+  const StateIO none{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  hipLaunchKernelGGL((wkv4_fwd_tiled<1, 16, 4, false>), dim3(grid), dim3(256), 0, stream,
+                     int(T), int(C), int(pl.n_cblk), int(pl.groups), int(pl.n_tiles), w, u, k,
+                     v, nullptr, hdr, counters, slots, none);
+  return hipGetLastError();
 }
 
 hipError_t wkv4_forward_launch(const Wkv4Plan& pl, int64_t B, int64_t T, int64_t C,

@@ -33,6 +33,14 @@ constexpr size_t kWkv4CounterStride = 128;  // one counter per 128-byte line
 // Plan for a shape; honours RWKV_WKV4_TILE="CPL,L,NW" for tests and sweeps.
 // Returns false if the shape cannot be planned (too large for 32-bit tickets).
 bool wkv4_plan(int64_t B, int64_t T, int64_t C, Wkv4Plan* plan);
+// The same for a given tile shape.
+bool wkv4_plan_fixed(int64_t B, int64_t T, int64_t C, int cpl, int L, int NW, Wkv4Plan* plan);
+
+// The forward scan without output rows: publishes every tile's inclusive
+// history in the workspace (plan: one channel per lane, 16 x 4 tiles).
+hipError_t wkv4_prefix_launch(const Wkv4Plan& plan, int64_t T, int64_t C, const float* w,
+                              const float* u, const float* k, const float* v, void* ws,
+                              hipStream_t stream);
 
 // a/b/p_in: optional history before the first token; a/b/p_out: optional
 // state after the last token (both [B, C], step-API form; may be null).
@@ -48,6 +56,27 @@ hipError_t wkv4_state_init_launch(int64_t B, int64_t C, float* a, float* b, floa
 hipError_t wkv4_step_launch(int64_t B, int64_t C, float* a, float* b, float* p,
                             const float* w, const float* u, const float* k,
                             const float* v, float* y, hipStream_t stream);
+
+// ----- RWKV-4 backward -----
+//
+// Workspace: the prefix pass's forward workspace (its header and counters
+// serve both passes), then the reverse scan's published histories (6
+// fields, aggregate and inclusive, per tile and channel), then the gw and gu
+// partial sums per (tile, sequence, channel) as tagged words.
+struct Wkv4BwdPlan {
+  Wkv4Plan fwd;  // tiling shared by both passes
+  size_t rev_slots_offset;
+  size_t part_offset;
+  int64_t part_rows;  // n_tiles * B
+  size_t ws_bytes;
+};
+
+bool wkv4_backward_plan(int64_t B, int64_t T, int64_t C, Wkv4BwdPlan* plan);
+
+hipError_t wkv4_backward_launch(const Wkv4BwdPlan& plan, int64_t B, int64_t T, int64_t C,
+                                const float* w, const float* u, const float* k,
+                                const float* v, const float* gy, float* gw, float* gu,
+                                float* gk, float* gv, void* ws, hipStream_t stream);
 
 // ----- Eagle (RWKV-5) forward -----
 size_t wkv5_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t D);

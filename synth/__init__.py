@@ -15,6 +15,9 @@ Recipe (the same for every caller):
   are cast float64 -> float32 -> bfloat16 with round-to-nearest-even and are
   returned both as raw bf16 bit patterns (uint16) and as the exact float32
   values those bits encode.
+* RWKV-4 backward: the upstream gradient gy ~ N(0, 1) [B, T, C] comes from
+  its own generator, ``PCG64(seed + 100000)``, so the forward inputs of a
+  seed are unchanged.
 * "N(0, s)" means standard deviation ``s``.
 """
 from __future__ import annotations
@@ -28,6 +31,7 @@ __all__ = [
     "CFG_WKV4_TINY", "CFG_WKV4_169M", "CFG_WKV4_LONG", "CFG_WKV4_DECODE",
     "CFG_WKV5_EAGLE", "CFG_WKV5_DECODE", "Wkv5StepConfig",
     "rng_for", "wkv4_inputs", "wkv4_step_inputs", "wkv5_inputs", "wkv5_step_inputs",
+    "wkv4_backward_inputs",
     "bf16_bits_from_f32", "f32_from_bf16_bits",
 ]
 
@@ -139,6 +143,13 @@ def wkv4_inputs_for(cfg: Wkv4Config) -> dict:
     return wkv4_inputs(cfg.B, cfg.T, cfg.C, cfg.seed, omega_lo=cfg.omega_lo,
                        omega_hi=cfg.omega_hi, u_std=cfg.u_std,
                        k_std=cfg.k_std, v_std=cfg.v_std)
+
+
+def wkv4_backward_inputs(B: int, T: int, C: int, seed: int, **kw) -> dict:
+    """Forward inputs of ``wkv4_inputs`` plus an upstream gradient ``gy``."""
+    out = wkv4_inputs(B, T, C, seed, **kw)
+    out["gy"] = _f32(rng_for(seed + 100000).standard_normal((B, T, C)))
+    return out
 
 
 def wkv4_step_inputs(B: int, C: int, pool: int, seed: int, *, omega_lo=-3.0,

@@ -43,6 +43,7 @@ def test_header_declares_the_boundary():
     assert names == sorted([
         "rwkv_abi_version", "rwkv_status_str", "rwkv_last_hip_error",
         "rwkv_wkv4_forward_workspace", "rwkv_wkv4_forward", "rwkv_wkv4_forward_state",
+        "rwkv_wkv4_backward_workspace", "rwkv_wkv4_backward",
         "rwkv_wkv4_state_init", "rwkv_wkv4_step", "rwkv_wkv5_forward_workspace",
         "rwkv_wkv5_forward", "rwkv_wkv5_forward_state", "rwkv_wkv5_step",
     ])
@@ -189,4 +190,23 @@ def test_wkv5_state_and_step_rejections(lib):
     for n in names:
         assert s(1, 2, 64, *ptrs(**{n: NULL}), NULL) == NULLPTR, n
         assert s(1, 2, 64, *ptrs(**{n: MISALIGNED}), NULL) == ALIGN, n
+    assert lib.rwkv_last_hip_error() == 0
+
+
+def test_wkv4_backward_rejections(lib):
+    _skip_if_gpu()
+    f = lib.rwkv_wkv4_backward
+    need = lib.rwkv_wkv4_backward_workspace(2, 300, 128)
+    assert need > lib.rwkv_wkv4_forward_workspace(2, 300, 128)
+    names = "w u k v gy gw gu gk gv".split()
+    args = lambda **kw: [kw.get(n, FAKE) for n in names]  # noqa: E731
+    assert f(0, 300, 128, *[NULL] * 9, NULL, 0, NULL) == OK
+    assert f(2, -1, 128, *args(), FAKE, need, NULL) == SHAPE
+    for n in names:
+        assert f(2, 300, 128, *args(**{n: NULL}), FAKE, need, NULL) == NULLPTR, n
+        assert f(2, 300, 128, *args(**{n: MISALIGNED}), FAKE, need, NULL) == ALIGN, n
+    assert f(2, 300, 128, *args(), NULL, need, NULL) == WORKSPACE
+    assert f(2, 300, 128, *args(), FAKE, need - 1, NULL) == WORKSPACE
+    assert f(2, 300, 128, *args(), MISALIGNED, need, NULL) == ALIGN
+    assert lib.rwkv_wkv4_backward_workspace(0, 10, 10) == 0
     assert lib.rwkv_last_hip_error() == 0

@@ -1,0 +1,124 @@
+"""GPU parity of the RWKV-4 backward against the fp64 oracle.
+
+Tolerance: for each gradient, max |g_gpu - g_oracle| / g_abs <= 1e-4, where
+g_abs is the same sum with every term replaced by its magnitude bound
+(oracle.wkv4_backward_scale): float32 rounding of a sum is relative to the
+sum of its terms' magnitudes, not to the (possibly cancelling) result.
+"""
+import numpy as np
+import pytest
+
+import linear_attention_sequence_rwkv_amd as rw
+import oracle.wkv_oracle as O
+import synth
+from wkv_testutil import WKV4_TOL, log, to_dev, torch_dev
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("gw", "gu", "gk", "gv")
+
+
+def gpu_backward(inp):
+    torch, _ = torch_dev()
+    out = rw.rwkv_wkv4_backward(to_dev(inp["w"]), to_dev(inp["u"]), to_dev(inp["k"]),
+                                to_dev(inp["v"]), to_dev(inp["gy"]))
+    torch.cuda.synchronize()
+    return [o.cpu().numpy().astype(np.float64) for o in out]
+
+
+def errors(got, ref, scale):
+    return {n: float(np.max(np.abs(g - r) / np.maximum(s, 1e-30))) if g.size else 0.0
+            for n, g, r, s in zip(NAMES, got, ref, scale)}
+
+
+def check(inp, channels=None, tol=WKV4_TOL):
+    got = gpu_backward(inp)
+    w, u, k, v, gy = (inp[n] for n in ("w", "u", "k", "v", "gy"))
+    if channels is not None:
+        w, u, k, v, gy = w[channels], u[channels], k[..., channels], v[..., channels], \
+            gy[..., channels]
+        got = [g[..., channels] for g in got]
+    ref = O.wkv4_backward_recurrent(w, u, k, v, gy)
+    scale = O.wkv4_backward_scale(w, u, k, v, gy)
+    err = errors(got, ref, scale)
+    log("  " + " ".join(f"{n}={e:.2e}" for n, e in err.items()))
+    for n, e in err.items():
+        assert e <= tol, (n, e)
+    for g in got:
+        assert np.all(np.isfinite(g))
+
+
+def test_tiny_workload_matches_the_definition():
+    inp = synth.wkv4_backward_inputs(1, 64, 64, 1001)
+    log("wkv4_backward B=1 T=64 C=64 vs direct definition")
+    got = gpu_backward(inp)
+    ref = O.wkv4_backward_direct(*(inp[n] for n in ("w", "u", "k", "v", "gy")))
+    scale = O.wkv4_backward_scale(*(inp[n] for n in ("w", "u", "k", "v", "gy")))
+    err = errors(got, ref, scale)
+    log("  " + " ".join(f"{n}={e:.2e}" for n, e in err.items()))
+    assert max(err.values()) <= WKV4_TOL
+
+
+@pytest.mark.parametrize("shape", [(2, 1000, 200), (1, 777, 64), (3, 64, 65), (1, 1, 7),
+                                   (2, 65, 130), (1, 17, 3), (2, 129, 64)])
+def test_ragged_shapes(shape):
+    B, T, C = shape
+    log(f"wkv4_backward B={B} T={T} C={C}")
+    check(synth.wkv4_backward_inputs(B, T, C, seed=3 + T + C))
+
+
+def test_169m_width_workload_full():
+    cfg = synth.CFG_WKV4_169M
+    log(f"wkv4_backward {cfg.name} (full oracle)")
+    check(synth.wkv4_backward_inputs(cfg.B, cfg.T, cfg.C, cfg.seed))
+
+
+def test_long_sequence_workload_sampled_channels():
+    cfg = synth.CFG_WKV4_LONG
+    log(f"wkv4_backward {cfg.name} (oracle on 40 sampled channels)")
+    inp = synth.wkv4_backward_inputs(cfg.B, cfg.T, cfg.C, cfg.seed, omega_lo=cfg.omega_lo,
+                                     omega_hi=cfg.omega_hi, u_std=cfg.u_std, k_std=cfg.k_std)
+    chans = np.sort(np.random.default_rng(2).choice(cfg.C, 40, replace=False))
+    check(inp, channels=chans)
+
+
+@pytest.mark.parametrize("shift", [-80.0, 80.0])
+def test_key_shift_stability(shift):
+    inp = synth.wkv4_backward_inputs(2, 500, 96, seed=21)
+    inp = dict(inp, k=(inp["k"].astype(np.float64) + shift).astype(np.float32))
+    log(f"wkv4_backward k{shift:+.0f}")
+    check(inp)
+
+
+def test_backward_is_deterministic():
+    torch, _ = torch_dev()
+    cfg = synth.CFG_WKV4_169M
+    inp = synth.wkv4_backward_inputs(cfg.B, cfg.T, cfg.C, cfg.seed)
+    args = [to_dev(inp[n]) for n in ("w", "u", "k", "v", "gy")]
+    first = rw.rwkv_wkv4_backward(*args)
+    for _ in range(2):
+        again = rw.rwkv_wkv4_backward(*args)
+        torch.cuda.synchronize()
+        for a, b in zip(first, again):
+            assert torch.equal(a, b)
+
+
+def test_backward_after_forward_calls_of_other_shapes():
+    """The two workspaces (forward's, backward's) are independent; calls of
+    different shapes in any order stay correct."""
+    torch, _ = torch_dev()
+    for B, T, C in ((1, 300, 64), (2, 70, 130), (1, 300, 64)):
+        inp = synth.wkv4_backward_inputs(B, T, C, seed=B + T + C)
+        rw.rwkv_wkv4_forward(to_dev(inp["w"]), to_dev(inp["u"]), to_dev(inp["k"]),
+                             to_dev(inp["v"]))
+        check(inp)
+
+
+def test_workspace_layout_changes():
+    """One cached workspace through calls whose layouts differ (large to
+    small and back): wherever a call's counters land, the words it finds
+    there carry earlier tags, so every call claims all of its tiles."""
+    for B, T, C in ((1, 4096, 256), (1, 300, 64), (3, 64, 65), (2, 1000, 200), (1, 300, 64),
+                    (4, 2048, 64)):
+        log(f"wkv4_backward B={B} T={T} C={C} (shared workspace)")
+        check(synth.wkv4_backward_inputs(B, T, C, seed=T + C))
