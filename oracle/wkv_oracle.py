@@ -18,7 +18,9 @@ or bf16 inputs upcast to float64).  Sources, by page title and section:
 * [Eagle-Finch] "RWKV-5 Eagle and RWKV-6 Finch" (ql.gl blog), section
   "Eagle: extending vector memory to matrix memory": the update
   s' = diag(w) s + k^T v, the read-out wkv' = s + diag(u) k^T v, and the
-  decay parameterisation w = exp(-exp(omega)).
+  decay parameterisation w = exp(-exp(omega)); section "Finch: making the
+  recurrence respond to the input": the decay becomes data-dependent, i.e.
+  a w_t per token (and channel) in the same update.
 
 Conventions (readings of the pages where they are silent or garbled):
 
@@ -30,6 +32,9 @@ Conventions (readings of the pages where they are silent or garbled):
 * Eagle ``k^T v`` is an outer product indexed [key i][value j]; ``diag(w)``
   scales key rows; the receptance contracts the key index; the output reads
   the state *before* the current token's update.
+* Finch: token t's decay w_t [key i] multiplies the state before token t's
+  k^T v is added, s_{t+1} = diag(w_t) s_t + k_t^T v_t (the Eagle update with
+  w replaced by w_t); u stays per (head, key channel).
 
 RWKV-4 backward: the pages give WKV_t but not its derivatives.  They are
 obtained here by differentiating the definition (chain rule through the
@@ -53,6 +58,7 @@ __all__ = [
     "wkv4_step", "wkv4_canonical_state",
     "wkv4_backward_direct", "wkv4_backward_recurrent", "wkv4_backward_scale",
     "wkv5_recurrent", "wkv5_unrolled", "wkv5_scale", "wkv5_step",
+    "wkv6_step", "wkv6_recurrent", "wkv6_unrolled", "wkv6_scale",
 ]
 
 
@@ -347,3 +353,65 @@ def wkv5_scale(r, k, v, w, u):
     o, _ = wkv5_recurrent(np.abs(_f64(r)), np.abs(_f64(k)), np.abs(_f64(v)),
                           w, np.abs(_f64(u)))
     return o
+
+
+# ---------------------------------------------------------------------------
+# Finch (RWKV-6): the Eagle recurrence with a per-token decay w_t
+# ---------------------------------------------------------------------------
+
+def wkv6_step(S, w_t, u, r_t, k_t, v_t):
+    """One token with its own decay.  w_t, r_t, k_t, v_t: [B, H, D]; u: [H, D].
+
+    [Eagle-Finch] "Finch": the Eagle read-out r (s + diag(u) k^T v), then
+    s' = diag(w_t) s + k^T v with this token's decay.
+    """
+    w_t, u = _f64(w_t), _f64(u)
+    r_t, k_t, v_t = _f64(r_t), _f64(k_t), _f64(v_t)
+    kv = k_t[..., :, None] * v_t[..., None, :]
+    read = S + u[None, :, :, None] * kv
+    o_t = np.matmul(r_t[..., None, :], read)[..., 0, :]
+    S_new = w_t[..., :, None] * S + kv
+    return o_t, S_new
+
+
+def wkv6_recurrent(r, k, v, w, u, S0=None):
+    """Finch output over a sequence by the recurrence.
+
+    r, k, v, w: [B, T, H, D] (w the per-token decay factor); u: [H, D].
+    Returns (o [B, T, H, D], final S).
+    """
+    r, k, v, w = _f64(r), _f64(k), _f64(v), _f64(w)
+    B, T, H, D = r.shape
+    S = np.zeros((B, H, D, D)) if S0 is None else _f64(S0).copy()
+    o = np.empty((B, T, H, D))
+    for t in range(T):
+        o[:, t], S = wkv6_step(S, w[:, t], u, r[:, t], k[:, t], v[:, t])
+    return o, S
+
+
+def wkv6_unrolled(r, k, v, w, u):
+    """Finch output as an explicit sum over past tokens (tiny inputs only).
+
+    Unrolling s_{t+1} = diag(w_t) s_t + k_t^T v_t from s_0 = 0, token
+    tau < t reaches s_t scaled by prod_{j=tau+1}^{t-1} w_j (per key channel),
+    so o_t[j] = sum_{tau<t} (sum_i r_t[i] prod_j w_j[i] k_tau[i]) v_tau[j]
+                + (sum_i r_t[i] u[i] k_t[i]) v_t[j].
+    """
+    r, k, v, w, u = _f64(r), _f64(k), _f64(v), _f64(w), _f64(u)
+    B, T, H, D = r.shape
+    o = np.zeros((B, T, H, D))
+    for t in range(T):
+        for tau in range(t):
+            decay = np.prod(w[:, tau + 1:t], axis=1)          # [B, H, D]; empty product = 1
+            coef = (r[:, t] * decay * k[:, tau]).sum(-1)        # [B, H]
+            o[:, t] += coef[..., None] * v[:, tau]
+        bonus = (r[:, t] * u[None] * k[:, t]).sum(-1)
+        o[:, t] += bonus[..., None] * v[:, t]
+    return o
+
+
+def wkv6_scale(r, k, v, w, u, S0=None):
+    """Magnitude bounds for the tolerance: the same recurrence on |r|, |k|,
+    |v|, |u| (and |S0|), w_t being in (0, 1].  Returns (o_abs, S_abs)."""
+    return wkv6_recurrent(np.abs(_f64(r)), np.abs(_f64(k)), np.abs(_f64(v)), w,
+                          np.abs(_f64(u)), None if S0 is None else np.abs(_f64(S0)))

@@ -15,6 +15,9 @@ Recipe (the same for every caller):
   are cast float64 -> float32 -> bfloat16 with round-to-nearest-even and are
   returned both as raw bf16 bit patterns (uint16) and as the exact float32
   values those bits encode.
+* Finch: the Eagle recipe, then a per-token decay w_t = exp(-exp(omega +
+  delta_t)) with delta_t ~ N(0, delta_std) [B, T, H, D] drawn after r (a
+  synthetic stand-in for the data-dependent correction), cast to float32.
 * RWKV-4 backward: the upstream gradient gy ~ N(0, 1) [B, T, C] comes from
   its own generator, ``PCG64(seed + 100000)``, so the forward inputs of a
   seed are unchanged.
@@ -31,7 +34,7 @@ __all__ = [
     "CFG_WKV4_TINY", "CFG_WKV4_169M", "CFG_WKV4_LONG", "CFG_WKV4_DECODE",
     "CFG_WKV5_EAGLE", "CFG_WKV5_DECODE", "Wkv5StepConfig",
     "rng_for", "wkv4_inputs", "wkv4_step_inputs", "wkv5_inputs", "wkv5_step_inputs",
-    "wkv4_backward_inputs",
+    "wkv4_backward_inputs", "wkv6_inputs", "CFG_WKV6_FINCH",
     "bf16_bits_from_f32", "f32_from_bf16_bits",
 ]
 
@@ -97,6 +100,8 @@ CFG_WKV4_LONG = Wkv4Config("wkv4_fwd_B1_T65536_C5120", 1, 65536, 5120, 1003,
 # resident on the device.
 CFG_WKV4_DECODE = Wkv4StepConfig("wkv4_step_B256_C4096_x4096", 256, 4096, 4096, 64, 1004)
 CFG_WKV5_EAGLE = Wkv5Config("wkv5_fwd_B4_T4096_H32_D64", 4, 4096, 32, 64, 1005)
+# Finch forward at the Eagle workload's shape, with per-token decays.
+CFG_WKV6_FINCH = Wkv5Config("wkv6_fwd_B4_T4096_H32_D64", 4, 4096, 32, 64, 1007)
 # Eagle decode: 64 streams of 32 heads (a 32 MB fp32 state), 256 steps drawn
 # from a pool of 16 tokens (step t uses token t mod 16).
 CFG_WKV5_DECODE = Wkv5StepConfig("wkv5_step_B64_H32_D64_x256", 64, 32, 64, 256, 16, 1006)
@@ -181,6 +186,25 @@ def wkv5_inputs(B: int, T: int, H: int, D: int, seed: int, *, omega_lo=-6.0,
         bits = bf16_bits_from_f32(x)
         out[name + "_bits"] = bits
         out[name] = f32_from_bf16_bits(bits)
+    return out
+
+
+def wkv6_inputs(B: int, T: int, H: int, D: int, seed: int, *, omega_lo=-6.0, omega_hi=0.0,
+                u_std=0.5, delta_std=0.5) -> dict:
+    """Finch inputs: the Eagle recipe plus ``wt`` [B, T, H, D] float32, the
+    per-token decay factors (``w`` stays the static part's factor)."""
+    rng = rng_for(seed)
+    omega = rng.uniform(omega_lo, omega_hi, size=(H, D))
+    u = rng.standard_normal((H, D)) * u_std
+    out = {"w": _f32(np.exp(-np.exp(omega))), "u": _f32(u)}
+    scale = 1.0 / np.sqrt(D)
+    for name in ("k", "v", "r"):
+        x = _f32(rng.standard_normal((B, T, H, D)) * scale)
+        bits = bf16_bits_from_f32(x)
+        out[name + "_bits"] = bits
+        out[name] = f32_from_bf16_bits(bits)
+    delta = rng.standard_normal((B, T, H, D)) * delta_std
+    out["wt"] = _f32(np.exp(-np.exp(omega[None, None] + delta)))
     return out
 
 

@@ -385,6 +385,74 @@ def test_backward_scale_bounds_every_gradient():
         assert np.all(np.abs(g) <= m * (1 + 1e-12) + 1e-300)
 
 
+# ------------------------------------------------------------ Finch pins ---
+
+def _small6(B=2, T=11, H=3, D=5, seed=13, **kw):
+    return synth.wkv6_inputs(B, T, H, D, seed, **kw)
+
+
+def _finch_err(e):
+    o1, _ = O.wkv6_recurrent(e["r"], e["k"], e["v"], e["wt"], e["u"])
+    o2 = O.wkv6_unrolled(e["r"], e["k"], e["v"], e["wt"], e["u"])
+    o_abs, _ = O.wkv6_scale(e["r"], e["k"], e["v"], e["wt"], e["u"])
+    return _rel(o1, o2, o_abs)
+
+
+def test_finch_recurrence_equals_unrolled_sum():
+    assert _finch_err(_small6()) < 1e-13
+    assert _finch_err(_small6(delta_std=2.0, seed=3)) < 1e-13
+
+
+def test_finch_with_constant_decay_is_eagle():
+    e = _small6()
+    wt = np.broadcast_to(e["w"][None, None], e["wt"].shape)
+    o6, S6 = O.wkv6_recurrent(e["r"], e["k"], e["v"], wt, e["u"])
+    o5, S5 = O.wkv5_recurrent(e["r"], e["k"], e["v"], e["w"], e["u"])
+    np.testing.assert_array_equal(o6, o5)
+    np.testing.assert_array_equal(S6, S5)
+
+
+def test_finch_no_decay_single_channel_is_a_prefix_sum():
+    rng = np.random.default_rng(4)
+    T = 40
+    r, k, v = (rng.standard_normal((1, T, 1, 1)) for _ in range(3))
+    u = np.array([[0.3]])
+    o, _ = O.wkv6_recurrent(r, k, v, np.ones((1, T, 1, 1)), u)
+    kv = (k * v)[0, :, 0, 0]
+    hist = np.concatenate([[0.0], np.cumsum(kv)[:-1]])
+    np.testing.assert_allclose(o[0, :, 0, 0], r[0, :, 0, 0] * (hist + 0.3 * kv), rtol=1e-13)
+
+
+def test_finch_hand_worked_decay_timing():
+    """D=1, u=0: s1 = k0 v0 = 1, s2 = w1 s1 + k1 v1 = 0.25 + 2 = 2.25.  The
+    first token's decay w0 multiplies the empty state and cannot matter; the
+    second token's decay w1 = 0.25 is the one applied to s1."""
+    r = np.ones((1, 3, 1, 1))
+    k = np.array([1.0, 2.0, 0.5]).reshape(1, 3, 1, 1)
+    v = np.array([1.0, 1.0, 2.0]).reshape(1, 3, 1, 1)
+    w = np.array([0.5, 0.25, 0.125]).reshape(1, 3, 1, 1)
+    o, S = O.wkv6_recurrent(r, k, v, w, np.zeros((1, 1)))
+    np.testing.assert_array_equal(o[0, :, 0, 0], [0.0, 1.0, 2.25])
+    np.testing.assert_array_equal(S[0, 0], [[0.125 * 2.25 + 1.0]])
+
+
+def test_finch_split_sequence():
+    e = _small6(T=20)
+    args = [e[n] for n in ("r", "k", "v", "wt")]
+    o_all, S_all = O.wkv6_recurrent(*args, e["u"])
+    o1, S1 = O.wkv6_recurrent(*(a[:, :7] for a in args), e["u"])
+    o2, S2 = O.wkv6_recurrent(*(a[:, 7:] for a in args), e["u"], S0=S1)
+    np.testing.assert_allclose(np.concatenate([o1, o2], 1), o_all, rtol=1e-13, atol=1e-16)
+    np.testing.assert_allclose(S2, S_all, rtol=1e-13, atol=1e-16)
+
+
+def test_finch_scale_bounds_output():
+    e = _small6(delta_std=1.0)
+    o, S = O.wkv6_recurrent(e["r"], e["k"], e["v"], e["wt"], e["u"])
+    o_abs, S_abs = O.wkv6_scale(e["r"], e["k"], e["v"], e["wt"], e["u"])
+    assert np.all(np.abs(o) <= o_abs * (1 + 1e-12)) and np.all(np.abs(S) <= S_abs * (1 + 1e-12))
+
+
 # ------------------------------------------------------- planted mistakes ---
 
 _WKV4_STEP = O.wkv4_step
@@ -441,3 +509,14 @@ def test_pins_catch_eagle_decay_on_value_index(monkeypatch):
     original = O.wkv5_step
     monkeypatch.setattr(O, "wkv5_step", value_decay)
     assert recurrent_vs_unrolled_err(_small5()) > 1e-3
+
+
+def test_pins_catch_finch_decay_after_adding(monkeypatch):
+    def decay_after(S, w_t, u, r_t, k_t, v_t):
+        # the token's own k^T v decayed by its own w_t
+        o, _ = original(S, w_t, u, r_t, k_t, v_t)
+        kv = np.asarray(k_t, float)[..., :, None] * np.asarray(v_t, float)[..., None, :]
+        return o, np.asarray(w_t, float)[..., :, None] * (S + kv)
+    original = O.wkv6_step
+    monkeypatch.setattr(O, "wkv6_step", decay_after)
+    assert _finch_err(_small6()) > 1e-3
