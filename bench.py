@@ -274,6 +274,47 @@ def bench_wkv5(torch, rw, cfg, reps):
     return {"ms": ms, "elems": elems, "bytes": 10 * elems, "flops": 4 * cfg.D * elems}
 
 
+def bench_wkv6(torch, rw, cfg, reps):
+    import synth
+    dev = torch.device("cuda:0")
+    e = synth.wkv6_inputs(cfg.B, cfg.T, cfg.H, cfg.D, cfg.seed)
+    to = lambda x: torch.from_numpy(x).to(dev)  # noqa: E731
+    r, k, v = (to(e[n + "_bits"]).view(torch.bfloat16) for n in ("r", "k", "v"))
+    wt, u = to(e["wt"]), to(e["u"])
+    o = torch.empty((cfg.B, cfg.T, cfg.H, cfg.D), dtype=torch.float32, device=dev)
+    lib = rw.load_library()
+    stream = torch.cuda.current_stream(dev)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    args = (cfg.B, cfg.T, cfg.H, cfg.D, P(r), P(k), P(v), P(wt), P(u), P(o), None, None,
+            ctypes.c_void_p(stream.cuda_stream))
+    assert lib.rwkv_wkv6_forward(*args) == 0
+    torch.cuda.synchronize()
+    s, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for _ in range(reps):
+        assert lib.rwkv_wkv6_forward(*args) == 0
+    en.record(stream)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all().item()
+    ms = s.elapsed_time(en) / reps
+    elems = cfg.B * cfg.T * cfg.H * cfg.D
+    return {"ms": ms, "elems": elems, "bytes": 14 * elems, "flops": 4 * cfg.D * elems}
+
+
+def cpu_sample_finch():
+    """Oracle recurrence for 2 (batch, head) pairs over the full T."""
+    import oracle.wkv_oracle as O
+    import synth
+    cfg = synth.CFG_WKV6_FINCH
+    e = synth.wkv6_inputs(1, cfg.T, 2, cfg.D, cfg.seed)
+    t0 = time.perf_counter()
+    O.wkv6_recurrent(e["r"], e["k"], e["v"], e["wt"], e["u"])
+    el = time.perf_counter() - t0
+    elems = cfg.T * 2 * cfg.D
+    return {"value": round(14 * elems / el / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"2 heads x T={cfg.T} x D={cfg.D}, {el:.1f} s"}
+
+
 def wkv5_step_bytes(B, H, D):
     """Algorithmic bytes of one Eagle step: the fp32 state read and written,
     r, k, v in bf16, o in fp32."""
@@ -433,9 +474,10 @@ def main(argv=None):
     ap.add_argument("--copy-calibration", action="store_true",
                     help="accepted for older command lines; the 1 GiB copy always runs")
     ap.add_argument("--secondary",
-                    default="hot,long,decode,decode-graph,eagle,eagle-decode,backward,backward-long",
+                    default="hot,long,decode,decode-graph,eagle,eagle-decode,finch,backward,"
+                            "backward-long",
                     help="comma list of secondary workloads: hot, long, decode, decode-graph, "
-                         "eagle, eagle-decode, backward, backward-long")
+                         "eagle, eagle-decode, finch, backward, backward-long")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -530,6 +572,14 @@ def main(argv=None):
                              "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
                              "bytes_per_elem": 20,
                              "gelem_per_s": round(r["elems"] / (r["ms"] * 1e-3) / 1e9, 1)}
+        if "finch" in want:
+            fc = synth.CFG_WKV6_FINCH
+            log(f"bench: {fc.name}")
+            r = bench_wkv6(torch, rw, fc, reps=5)
+            sec[fc.name] = {"ms": round(r["ms"], 4),
+                            "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
+                            "bytes_per_elem": 14,
+                            "algorithmic_TFLOPs": round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 2)}
         if "eagle-decode" in want:
             ed = synth.CFG_WKV5_DECODE
             log(f"bench: {ed.name}")
@@ -547,6 +597,7 @@ def main(argv=None):
                     synth.CFG_WKV4_DECODE.name: cpu_sample_decode,
                     synth.CFG_WKV5_EAGLE.name: cpu_sample_eagle,
                     synth.CFG_WKV5_DECODE.name: cpu_sample_eagle_decode,
+                    synth.CFG_WKV6_FINCH.name: cpu_sample_finch,
                     synth.CFG_WKV4_169M.name.replace("wkv4_fwd", "wkv4_bwd"): cpu_sample_backward}
         for name, fn in samplers.items():
             if name in sec:

@@ -235,6 +235,45 @@ int rwkv_wkv5_step(int64_t B, int64_t H, int64_t D,
                    const float* w, const float* u,
                    float* o, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Finch (RWKV-6) forward: the Eagle recurrence with a decay per token.
+ * [Eagle-Finch] "Finch": the decay becomes data-dependent.  Read as the Eagle
+ * update with token t's own decay, applied to the state before its k^T v:
+ *   o[b,t,h,j] = sum_i r[b,t,h,i] * ( s_t[i][j] + u[h,i] k[b,t,h,i] v[b,t,h,j] )
+ *   s_{t+1}[i][j] = w[b,t,h,i] s_t[i][j] + k[b,t,h,i] v[b,t,h,j]
+ *
+ *   r, k, v  [B,T,H,D]  bfloat16 bit patterns (uint16)
+ *   w        [B,T,H,D]  float32 decay factor of each token, in (0, 1]
+ *                       (factors below 2^-126 act as 2^-126)
+ *   u        [H,D]      float32 current-token bonus
+ *   o        [B,T,H,D]  float32 output
+ *   s_in, s_out [B,H,D,D] float32 states before the first / after the last
+ *                       token, either may be NULL (zero start / not wanted);
+ *                       s_out may equal s_in.
+ *   D must be 64.  No workspace.
+ * Accuracy: as rwkv_wkv5_forward, against the same magnitude recurrence with
+ * the per-token decays.
+ * ---------------------------------------------------------------------- */
+int rwkv_wkv6_forward(int64_t B, int64_t T, int64_t H, int64_t D,
+                      const uint16_t* r, const uint16_t* k, const uint16_t* v,
+                      const float* w, const float* u,
+                      float* o,
+                      const float* s_in, float* s_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Finch single-token step: as rwkv_wkv5_step with this token's decay.
+ *   s        [B,H,D,D]  float32 state, read and updated in place
+ *   r, k, v  [B,H,D]    bfloat16 bit patterns of this token
+ *   w        [B,H,D]    float32 this token's decay factors
+ *   u        [H,D]      float32
+ *   o        [B,H,D]    float32 output
+ * ---------------------------------------------------------------------- */
+int rwkv_wkv6_step(int64_t B, int64_t H, int64_t D,
+                   float* s,
+                   const uint16_t* r, const uint16_t* k, const uint16_t* v,
+                   const float* w, const float* u,
+                   float* o, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -52,6 +52,9 @@ _SIGNATURES = {
     "rwkv_wkv5_forward_state": (ctypes.c_int, [_i64, _i64, _i64, _i64, _p, _p, _p, _p, _p,
                                                _p, _p, _p, _p, _sz, _p]),
     "rwkv_wkv5_step": (ctypes.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "rwkv_wkv6_forward": (ctypes.c_int, [_i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p,
+                                         _p]),
+    "rwkv_wkv6_step": (ctypes.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p]),
 }
 
 
@@ -346,13 +349,14 @@ def _wkv5_args(r, k, v, w, u, o, ndim):
     r = _dev_tensor("r", r, half, ndim)
     k = _dev_tensor("k", k, half, ndim)
     v = _dev_tensor("v", v, half, ndim)
-    w = _dev_tensor("w", w, (torch.float32,), 2)
+    if w is not None:  # None: the caller checks a per-token decay itself
+        w = _dev_tensor("w", w, (torch.float32,), 2)
     u = _dev_tensor("u", u, (torch.float32,), 2)
     shape = tuple(r.shape)
     H, D = shape[-2], shape[-1]
     if tuple(k.shape) != shape or tuple(v.shape) != shape:
         raise ValueError("r, k, v shapes differ")
-    if tuple(w.shape) != (H, D) or tuple(u.shape) != (H, D):
+    if (w is not None and tuple(w.shape) != (H, D)) or tuple(u.shape) != (H, D):
         raise ValueError("w, u must be [H, D]")
     if o is None:
         o = torch.empty(shape, dtype=torch.float32, device=r.device)
@@ -430,4 +434,49 @@ def rwkv_wkv5_step(s, r, k, v, w, u, o=None, stream=None):
     status = lib.rwkv_wkv5_step(B, H, D, _ptr(s), _ptr(r), _ptr(k), _ptr(v), _ptr(w), _ptr(u),
                                 _ptr(o), _stream(r.device, stream))
     _check("rwkv_wkv5_step", status)
+    return o
+
+
+# ------------------------------------------------------------------ Finch ---
+
+def _finch_w(w, shape):
+    torch = _torch()
+    w = _dev_tensor("w", w, (torch.float32,), len(shape))
+    if tuple(w.shape) != shape:
+        raise ValueError(f"w must have the shape of r, {shape}")
+    return w
+
+
+def rwkv_wkv6_forward(r, k, v, w, u, s_in=None, s_out=None, o=None, stream=None):
+    """Finch forward: r, k, v [B,T,H,D] bf16, w [B,T,H,D] float32 per-token
+    decays, u [H,D].  ``s_in``/``s_out`` as for rwkv_wkv5_forward_state.
+    Returns (o, s_out)."""
+    torch = _torch()
+    lib = load_library()
+    r, k, v, _, u, o = _wkv5_args(r, k, v, None, u, o, 4)
+    B, T, H, D = r.shape
+    w = _finch_w(w, (B, T, H, D))
+    if s_in is not None:
+        s_in = _wkv5_state_arg("s_in", s_in, B, H, D)
+    if s_out is True:
+        s_out = torch.empty((B, H, D, D), dtype=torch.float32, device=r.device)
+    if s_out is not None:
+        s_out = _wkv5_state_arg("s_out", s_out, B, H, D)
+    status = lib.rwkv_wkv6_forward(B, T, H, D, _ptr(r), _ptr(k), _ptr(v), _ptr(w), _ptr(u),
+                                   _ptr(o), _ptr(s_in), _ptr(s_out), _stream(r.device, stream))
+    _check("rwkv_wkv6_forward", status)
+    return o, s_out
+
+
+def rwkv_wkv6_step(s, r, k, v, w, u, o=None, stream=None):
+    """One Finch token: r, k, v [B,H,D] bf16, w [B,H,D] float32; s updated in
+    place.  Returns o [B,H,D] float32."""
+    lib = load_library()
+    r, k, v, _, u, o = _wkv5_args(r, k, v, None, u, o, 3)
+    B, H, D = r.shape
+    w = _finch_w(w, (B, H, D))
+    s = _wkv5_state_arg("s", s, B, H, D)
+    status = lib.rwkv_wkv6_step(B, H, D, _ptr(s), _ptr(r), _ptr(k), _ptr(v), _ptr(w), _ptr(u),
+                                _ptr(o), _stream(r.device, stream))
+    _check("rwkv_wkv6_step", status)
     return o

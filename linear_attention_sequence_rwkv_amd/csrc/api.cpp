@@ -235,3 +235,36 @@ RWKV_API int rwkv_wkv5_step(int64_t B, int64_t H, int64_t D, float* s, const uin
     return RWKV_ERR_ALIGN;
   return hip_status(rwkv::wkv5_step_launch(B, H, s, r, k, v, w, u, o, stream));
 }
+
+// ------------------------------------------------------------------- Finch
+
+RWKV_API int rwkv_wkv6_forward(int64_t B, int64_t T, int64_t H, int64_t D, const uint16_t* r,
+                               const uint16_t* k, const uint16_t* v, const float* w,
+                               const float* u, float* o, const float* s_in, float* s_out,
+                               hipStream_t stream) {
+  int64_t n;
+  if (!dims_ok({B, T, H, D}, &n)) return RWKV_ERR_SHAPE;
+  if (n == 0) return RWKV_OK;
+  if (D != 64) return RWKV_ERR_UNSUPPORTED;
+  if (T >= (int64_t(1) << 31) || B * H >= (int64_t(1) << 31)) return RWKV_ERR_UNSUPPORTED;
+  if (!r || !k || !v || !w || !u || !o) return RWKV_ERR_NULLPTR;
+  if (!aligned16(r) || !aligned16(k) || !aligned16(v) || !aligned16(w) || !aligned16(u) ||
+      !aligned16(o) || (s_in && !aligned16(s_in)) || (s_out && !aligned16(s_out)))
+    return RWKV_ERR_ALIGN;
+  return hip_status(rwkv::wkv6_forward_launch(B, T, H, r, k, v, w, u, o, s_in, s_out, stream));
+}
+
+RWKV_API int rwkv_wkv6_step(int64_t B, int64_t H, int64_t D, float* s, const uint16_t* r,
+                            const uint16_t* k, const uint16_t* v, const float* w,
+                            const float* u, float* o, hipStream_t stream) {
+  int64_t n;
+  if (!dims_ok({B, H, D}, &n)) return RWKV_ERR_SHAPE;
+  if (n == 0) return RWKV_OK;
+  if (D != 64) return RWKV_ERR_UNSUPPORTED;
+  if (B * H >= (int64_t(1) << 31)) return RWKV_ERR_UNSUPPORTED;
+  if (!s || !r || !k || !v || !w || !u || !o) return RWKV_ERR_NULLPTR;
+  if (!aligned16(s) || !aligned16(r) || !aligned16(k) || !aligned16(v) || !aligned16(w) ||
+      !aligned16(u) || !aligned16(o))
+    return RWKV_ERR_ALIGN;
+  return hip_status(rwkv::wkv6_step_launch(B, H, s, r, k, v, w, u, o, stream));
+}

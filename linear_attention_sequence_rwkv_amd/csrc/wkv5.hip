@@ -22,6 +22,7 @@
 // The factorisation needs w^(-32) and w^(31) inside bf16/fp32 range, i.e.
 // |log2 w| <= 3.6 for every channel of the head; a head outside that range
 // runs the exact fp32 recurrence instead (one branch per workgroup).
+#include "eagle_common.h"
 #include "wkv_device.h"
 #include "wkv_internal.h"
 
@@ -31,24 +32,13 @@ namespace rwkv {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
+using namespace eagle;
 
-constexpr int kD = 64;        // head size
-constexpr int kL = 64;        // chunk length
-constexpr int kPad = 72;      // LDS row length in bf16 (144 bytes: 16-byte aligned rows)
 constexpr int kExpLo = -32;   // decay table covers w^e for e in [kExpLo, kExpHi]
 constexpr int kExpHi = 64;
 constexpr int kExpN = kExpHi - kExpLo + 1;
 // Largest |log2 w| for which w^(-32) and w^31 stay far inside fp32/bf16 range.
 constexpr float kMaxLog2Decay = 3.6f;
-
-__device__ __forceinline__ float bf16_to_f32(uint16_t x) {
-  return __uint_as_float(uint32_t(x) << 16);
-}
-
-// float -> bf16, round to nearest even (finite inputs; NaN stays NaN).
-__device__ __forceinline__ __bf16 to_bf16(float x) { return static_cast<__bf16>(x); }
 
 template <int DV>
 struct Lds {
@@ -113,41 +103,6 @@ __device__ void eagle_recurrent_slice(int T, int H, int b, int h, int j0,
     for (int i = 0; i < kD; ++i) s_out[sbase + size_t(i) * kD] = S[i];
   }
 }
-
-// One chunk's raw inputs for this thread: token tau = tid/4, dims 16*(tid%4)
-// of r and k, and DV/4 value dims of this workgroup's slice (8 or 4).
-struct ChunkRegs {
-  uint4 r0, r1, k0, k1, v0;
-};
-
-template <int DV>
-__device__ __forceinline__ void load_chunk(ChunkRegs& x, int t0, int T, int H, int b, int h,
-                                           int j0, const uint16_t* __restrict__ r,
-                                           const uint16_t* __restrict__ k,
-                                           const uint16_t* __restrict__ v) {
-  const int tid = threadIdx.x;
-  const int tau = tid >> 2, q4 = tid & 3;
-  if (t0 + tau < T) {
-    const size_t off = ((size_t(b) * T + t0 + tau) * H + h) * kD;
-    const uint4* rp = reinterpret_cast<const uint4*>(r + off + 16 * q4);
-    const uint4* kp = reinterpret_cast<const uint4*>(k + off + 16 * q4);
-    x.r0 = rp[0];
-    x.r1 = rp[1];
-    x.k0 = kp[0];
-    x.k1 = kp[1];
-    if constexpr (DV == 32) {
-      x.v0 = *reinterpret_cast<const uint4*>(v + off + j0 + 8 * q4);
-    } else {
-      const uint2 t = *reinterpret_cast<const uint2*>(v + off + j0 + 4 * q4);
-      x.v0 = uint4{t.x, t.y, 0u, 0u};
-    }
-  } else {
-    x.r0 = x.r1 = x.k0 = x.k1 = x.v0 = uint4{0u, 0u, 0u, 0u};
-  }
-}
-
-__device__ __forceinline__ float lo_half(uint32_t x) { return __uint_as_float(x << 16); }
-__device__ __forceinline__ float hi_half(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
 // Decay factors and bonus of the 16 channels this thread scales.  The
 // thread's token position in a chunk never changes, so they are computed once
@@ -231,10 +186,6 @@ __device__ __forceinline__ void stage_chunk(const ChunkRegs& x, const StageConst
   bpart += __shfl_xor(bpart, 1);
   bpart += __shfl_xor(bpart, 2);
   if (q4 == 0) s.beta[tau] = bpart;
-}
-
-__device__ __forceinline__ floatx4 mfma(const bf16x8& a, const bf16x8& b, const floatx4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // Workgroup: 4 waves; (batch, head, slice of DV value columns).  blockIdx
@@ -417,7 +368,9 @@ __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
 }
 
 // One token of the recurrence for every (batch, head): lane j keeps the
-// state column s[:, j] (read, updated and written back in place).
+// state column s[:, j] (read, updated and written back in place).  With
+// PER_TOKEN_W (Finch) the decay is this token's [B, H, D] instead of [H, D].
+template <bool PER_TOKEN_W>
 __global__ __launch_bounds__(64) void wkv5_step_kernel(
     int H, float* __restrict__ S, const uint16_t* __restrict__ r,
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -435,7 +388,7 @@ __global__ __launch_bounds__(64) void wkv5_step_kernel(
   const float kj = bf16_to_f32(k[off + j]);
   s_r[j] = rj;
   s_k[j] = kj;
-  s_w[j] = w[h * kD + j];
+  s_w[j] = PER_TOKEN_W ? w[off + j] : w[h * kD + j];
   s_ru[j] = rj * u[h * kD + j];
   __syncthreads();
   const float vj = bf16_to_f32(v[off + j]);
@@ -477,8 +430,16 @@ hipError_t wkv5_forward_launch(int64_t B, int64_t T, int64_t H, int64_t D,
 hipError_t wkv5_step_launch(int64_t B, int64_t H, float* s, const uint16_t* r,
                             const uint16_t* k, const uint16_t* v, const float* w,
                             const float* u, float* o, hipStream_t stream) {
-  hipLaunchKernelGGL(wkv5_step_kernel, dim3(unsigned(B * H)), dim3(64), 0, stream, int(H), s, r,
-                     k, v, w, u, o);
+  hipLaunchKernelGGL(wkv5_step_kernel<false>, dim3(unsigned(B * H)), dim3(64), 0, stream, int(H),
+                     s, r, k, v, w, u, o);
+  return hipGetLastError();
+}
+
+hipError_t wkv6_step_launch(int64_t B, int64_t H, float* s, const uint16_t* r,
+                            const uint16_t* k, const uint16_t* v, const float* w,
+                            const float* u, float* o, hipStream_t stream) {
+  hipLaunchKernelGGL(wkv5_step_kernel<true>, dim3(unsigned(B * H)), dim3(64), 0, stream, int(H),
+                     s, r, k, v, w, u, o);
   return hipGetLastError();
 }
 

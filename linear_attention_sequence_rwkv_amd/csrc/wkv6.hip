@@ -1,0 +1,379 @@
+// Finch (RWKV-6) matrix-state WKV forward for gfx950: the Eagle recurrence
+// with a decay per token and key channel.
+//
+// What is computed: [Eagle-Finch] "RWKV-5 Eagle and RWKV-6 Finch" (ql.gl
+// blog), section "Finch: making the recurrence respond to the input": the
+// Eagle update s' = diag(w) s + k^T v, read out as r (s + diag(u) k^T v),
+// with the decay w_t now depending on the token.  Token t's decay multiplies
+// the state before its own k^T v is added.
+//
+// Chunked form (64-token chunks; tau, sigma positions in the chunk; S the
+// state at the chunk start; c_tau[i] = sum_{j<tau} log2 w_j[i], so c is
+// non-increasing and c_0 = 0):
+//   o_tau = r_tau diag(2^c_tau) S
+//         + sum_{sigma<tau} (sum_i r_tau[i] k_sigma[i] 2^(c_tau - c_{sigma+1})[i]) v_sigma
+//         + (sum_i r_tau[i] u[i] k_tau[i]) v_tau,
+//   S_next = diag(2^c_64) S + sum_sigma diag(2^(c_64 - c_{sigma+1})) k_sigma^T v_sigma.
+// A decay per token can span any range over a chunk, so one reference point
+// (the Eagle kernel's mid-chunk factorisation) could overflow.  The chunk is
+// cut into four 16-token blocks, one per wave (wave q owns queries 16q..):
+//   * key block b < q: keys scaled by 2^(c_{16b+16} - c_{sigma+1}) and the
+//     queries by 2^(c_tau - c_{16b+16}), both factors <= 1;
+//   * the diagonal block b = q: a mid-block reference 16q+8, both factors
+//     within 2^(8 * 15) as long as every |log2 w| <= 15 in the chunk; a chunk
+//     with a faster decay computes its diagonal blocks exactly in fp32;
+//   * the inter-chunk term uses r 2^c_tau and the update k 2^(c_64 - c_{sigma+1}),
+//     factors <= 1.
+// Every product runs on bf16 MFMA with fp32 accumulation; S stays fp32.
+#include "eagle_common.h"
+#include "wkv_device.h"
+#include "wkv_internal.h"
+
+namespace rwkv {
+
+namespace {
+
+using namespace eagle;
+
+constexpr int kCPad = 65;                // fp32 row length of the log-decay prefix table
+constexpr float kMaxDiagLog2 = 15.f;     // fast diagonal blocks need every |log2 w| <= this
+constexpr float kMinLog2Decay = -126.f;  // log2 w below this counts as this (2^-126: no memory)
+
+template <int DV>
+struct LdsF {
+  __bf16 rr[kL][kPad];   // r, raw [tau][i]
+  __bf16 r0[kL][kPad];   // r 2^c_tau [tau][i]
+  __bf16 kb[kL][kPad];   // k 2^(c_{block end} - c_{sigma+1}) [sigma][i]
+  __bf16 kd[kL][kPad];   // k 2^(c_{block mid} - c_{sigma+1}), or raw k for exact diagonals
+  __bf16 kh[kD][kPad];   // (k 2^(c_64 - c_{sigma+1}))^T [i][sigma]
+  __bf16 vt[DV][kPad];   // v^T [j][sigma]
+  __bf16 sp[DV][kPad];   // S^T [j][i]
+  float c[kL + 1][kCPad];
+  float beta[kL];
+  float u[kD];
+};
+
+// This thread's 16 decay factors (token tid/4, channels 16*(tid%4)..).
+struct ChunkW {
+  float4 a, b, c, d;
+};
+
+__device__ __forceinline__ void load_w(ChunkW& x, int t0, int T, int H, int b, int h,
+                                       const float* __restrict__ w) {
+  const int tid = threadIdx.x;
+  const int tau = tid >> 2, q4 = tid & 3;
+  if (t0 + tau < T) {
+    const float4* p =
+        reinterpret_cast<const float4*>(w + ((size_t(b) * T + t0 + tau) * H + h) * kD + 16 * q4);
+    x.a = p[0];
+    x.b = p[1];
+    x.c = p[2];
+    x.d = p[3];
+  } else {
+    // past the end: no decay, so the chunk's end state is the last token's
+    const float4 one = {1.f, 1.f, 1.f, 1.f};
+    x.a = x.b = x.c = x.d = one;
+  }
+}
+
+// Exclusive prefix c[tau][i] of log2 w over the chunk's tokens.  Returns
+// whether some |log2 w| exceeds the fast diagonal's range (block-wide).
+template <int DV>
+__device__ __forceinline__ bool decay_prefix(const ChunkW& x, LdsF<DV>& s) {
+  const int tid = threadIdx.x;
+  const int tau = tid >> 2, d0 = 16 * (tid & 3);
+  const float wv[16] = {x.a.x, x.a.y, x.a.z, x.a.w, x.b.x, x.b.y, x.b.z, x.b.w,
+                        x.c.x, x.c.y, x.c.z, x.c.w, x.d.x, x.d.y, x.d.z, x.d.w};
+  int fast_ok = 1;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float l2 = fmaxf(__log2f(wv[e]), kMinLog2Decay);
+    fast_ok &= l2 >= -kMaxDiagLog2;
+    s.c[tau + 1][d0 + e] = l2;
+  }
+  if (tid < kD) s.c[0][tid] = 0.f;
+  const bool exact = __syncthreads_or(!fast_ok) != 0;
+  // per channel: four threads each take 16 rows, then add the totals of the
+  // segments before theirs
+  const int ch = tid & 63, sg = tid >> 6;
+  float run = 0.f;
+#pragma unroll
+  for (int j = 1; j <= 16; ++j) {
+    run += s.c[16 * sg + j][ch];
+    s.c[16 * sg + j][ch] = run;
+  }
+  __syncthreads();
+  float off = 0.f;
+  for (int j = 0; j < sg; ++j) off += s.c[16 * j + 16][ch];
+  __syncthreads();
+  if (sg > 0) {
+#pragma unroll
+    for (int j = 1; j <= 16; ++j) s.c[16 * sg + j][ch] += off;
+  }
+  __syncthreads();
+  return exact;
+}
+
+// Scaled copies of one chunk into LDS (the decay prefix must be in place).
+template <int DV>
+__device__ __forceinline__ void stage_chunk_f(const ChunkRegs& x, bool exact, LdsF<DV>& s) {
+  const int tid = threadIdx.x;
+  const int tau = tid >> 2, q4 = tid & 3;
+  const int d0 = 16 * q4;
+  const int blk = tau >> 4;
+  float rv[16], kv[16];
+  const uint32_t rw[8] = {x.r0.x, x.r0.y, x.r0.z, x.r0.w, x.r1.x, x.r1.y, x.r1.z, x.r1.w};
+  const uint32_t kw[8] = {x.k0.x, x.k0.y, x.k0.z, x.k0.w, x.k1.x, x.k1.y, x.k1.z, x.k1.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    rv[2 * e] = lo_half(rw[e]);
+    rv[2 * e + 1] = hi_half(rw[e]);
+    kv[2 * e] = lo_half(kw[e]);
+    kv[2 * e + 1] = hi_half(kw[e]);
+  }
+  *reinterpret_cast<uint4*>(&s.rr[tau][d0]) = x.r0;
+  *reinterpret_cast<uint4*>(&s.rr[tau][d0 + 8]) = x.r1;
+  float bpart = 0.f;
+  bf16x8 r0a, r0b, kba, kbb, kda, kdb;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int i = d0 + e;
+    const float ct = s.c[tau][i], ct1 = s.c[tau + 1][i];
+    const float fr0 = exp2_fast(ct);
+    const float fkb = exp2_fast(s.c[16 * blk + 16][i] - ct1);
+    const float fkd = exp2_fast(s.c[16 * blk + 8][i] - ct1);
+    const float fkh = exp2_fast(s.c[kL][i] - ct1);
+    const __bf16 vr0 = to_bf16(rv[e] * fr0), vkb = to_bf16(kv[e] * fkb);
+    const __bf16 vkd = exact ? to_bf16(kv[e]) : to_bf16(kv[e] * fkd);
+    if (e < 8) {
+      r0a[e] = vr0;
+      kba[e] = vkb;
+      kda[e] = vkd;
+    } else {
+      r0b[e - 8] = vr0;
+      kbb[e - 8] = vkb;
+      kdb[e - 8] = vkd;
+    }
+    s.kh[i][tau] = to_bf16(kv[e] * fkh);
+    bpart = fmaf(rv[e] * s.u[i], kv[e], bpart);
+  }
+  *reinterpret_cast<bf16x8*>(&s.r0[tau][d0]) = r0a;
+  *reinterpret_cast<bf16x8*>(&s.r0[tau][d0 + 8]) = r0b;
+  *reinterpret_cast<bf16x8*>(&s.kb[tau][d0]) = kba;
+  *reinterpret_cast<bf16x8*>(&s.kb[tau][d0 + 8]) = kbb;
+  *reinterpret_cast<bf16x8*>(&s.kd[tau][d0]) = kda;
+  *reinterpret_cast<bf16x8*>(&s.kd[tau][d0 + 8]) = kdb;
+  const uint32_t vw[4] = {x.v0.x, x.v0.y, x.v0.z, x.v0.w};
+  constexpr int VPT = DV / 4;
+#pragma unroll
+  for (int e = 0; e < VPT / 2; ++e) {
+    s.vt[VPT * q4 + 2 * e][tau] = to_bf16(lo_half(vw[e]));
+    s.vt[VPT * q4 + 2 * e + 1][tau] = to_bf16(hi_half(vw[e]));
+  }
+  bpart += __shfl_xor(bpart, 1);
+  bpart += __shfl_xor(bpart, 2);
+  if (q4 == 0) s.beta[tau] = bpart;
+}
+
+// Queries of this lane's B operand (token tau, channels i0..i0+7) scaled by
+// 2^(c_tau - c_ref).
+template <int DV>
+__device__ __forceinline__ bf16x8 scaled_queries(const LdsF<DV>& s, int tau, int i0, int ref) {
+  const bf16x8 raw = *reinterpret_cast<const bf16x8*>(&s.rr[tau][i0]);
+  bf16x8 out;
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    out[e] = to_bf16(float(raw[e]) * exp2_fast(s.c[tau][i0 + e] - s.c[ref][i0 + e]));
+  return out;
+}
+
+// Workgroup: 4 waves; (batch, head, slice of DV value columns), placed as in
+// the Eagle kernel.
+template <int DV>
+__global__ __launch_bounds__(256) void wkv6_fwd_chunked(
+    int T, int H, int BH, const uint16_t* __restrict__ r, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const float* __restrict__ w,
+    const float* __restrict__ u, float* __restrict__ o, const float* s_in, float* s_out) {
+  constexpr int NS = kD / DV;
+  constexpr int NJB = DV / 16;
+  __shared__ LdsF<DV> s;
+  const int bx = blockIdx.x;
+  const int bh = (bx / (8 * NS)) * 8 + (bx & 7);
+  const int slice = (bx >> 3) % NS;
+  if (bh >= BH) return;
+  const int b = bh / H, h = bh - (bh / H) * H;
+  const int j0 = slice * DV;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int q = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row = lane & 15;
+  const int kq = 8 * (lane >> 4);
+  const int crow = 4 * (lane >> 4);
+  const size_t sbase = size_t(bh) * kD * kD;
+
+  if (tid < kD) s.u[tid] = u[h * kD + tid];
+
+  floatx4 sacc[NJB];
+#pragma unroll
+  for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      sacc[jb][rr] = s_in ? s_in[sbase + size_t(16 * q + crow + rr) * kD + j0 + 16 * jb + row]
+                          : 0.f;
+  auto write_sp = [&]() {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) {
+      bf16x4 pk;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) pk[rr] = to_bf16(sacc[jb][rr]);
+      *reinterpret_cast<bf16x4*>(&s.sp[16 * jb + row][16 * q + crow]) = pk;
+    }
+  };
+  write_sp();
+
+  const int n_chunks = (T + kL - 1) / kL;
+  ChunkRegs cur, nxt;
+  ChunkW wc, wn;
+  load_chunk<DV>(cur, 0, T, H, b, h, j0, r, k, v);
+  load_w(wc, 0, T, H, b, h, w);
+  for (int c = 0; c < n_chunks; ++c) {
+    const int t0 = c * kL;
+    const bool exact = decay_prefix(wc, s);
+    stage_chunk_f(cur, exact, s);
+    __syncthreads();
+    if (c + 1 < n_chunks) {
+      load_chunk<DV>(nxt, t0 + kL, T, H, b, h, j0, r, k, v);
+      load_w(wn, t0 + kL, T, H, b, h, w);
+    }
+
+    // A^T: key blocks nb <= q against this wave's 16 queries (column
+    // tau = 16q + row of the lane, rows sigma = 16nb + crow .. +3).
+    const int tau_l = 16 * q + row;
+    floatx4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
+                      {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int i0 = 32 * ks + kq;
+#pragma unroll
+      for (int nb = 0; nb < 3; ++nb)
+        if (nb < q) {
+          const bf16x8 bq = scaled_queries(s, tau_l, i0, 16 * nb + 16);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.kb[16 * nb + row][i0]);
+          acc[nb] = mfma(a, bq, acc[nb]);
+        }
+      if (!exact) {
+        const bf16x8 bq = scaled_queries(s, tau_l, i0, 16 * q + 8);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.kd[16 * q + row][i0]);
+        acc[q] = mfma(a, bq, acc[q]);
+      }
+    }
+    if (exact) {
+      // diagonal block in fp32: sum_i r[tau][i] k[sigma][i] 2^(c_tau - c_{sigma+1})[i]
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int sig = 16 * q + crow + rr;
+        float a = 0.f;
+        if (sig < tau_l) {
+          for (int i = 0; i < kD; ++i)
+            a = fmaf(float(s.rr[tau_l][i]) * float(s.kd[sig][i]),
+                     exp2_fast(s.c[tau_l][i] - s.c[sig + 1][i]), a);
+        }
+        acc[q][rr] = a;
+      }
+    }
+
+    // Causal mask and the bonus, in registers (as in the Eagle kernel).
+    const float beta = s.beta[tau_l];
+    bf16x8 ap[2];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int sig = 16 * nb + crow + rr;
+        float val = 0.f;
+        if (nb <= q) val = sig < tau_l ? acc[nb][rr] : (sig == tau_l ? beta : 0.f);
+        ap[nb >> 1][(nb & 1) * 4 + rr] = to_bf16(val);
+      }
+
+    // O = A' V + (r 2^c) S.
+    floatx4 oacc[NJB];
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb) oacc[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const int nks = (q + 2) >> 1;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      if (ks < nks) {
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) {
+          const __bf16* vr = &s.vt[16 * jb + row][32 * ks + crow];
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
+          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 16);
+          const bf16x8 bb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          oacc[jb] = mfma(ap[ks], bb, oacc[jb]);
+        }
+      }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.r0[16 * q + row][32 * ks + kq]);
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) {
+        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s.sp[16 * jb + row][32 * ks + kq]);
+        oacc[jb] = mfma(a, bb, oacc[jb]);
+      }
+    }
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int tau = 16 * q + crow + rr;
+        if (t0 + tau < T)
+          o[((size_t(b) * T + t0 + tau) * H + h) * kD + j0 + 16 * jb + row] = oacc[jb][rr];
+      }
+
+    // S <- diag(2^c_64) S + kh^T V for key rows 16q..16q+15.
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float dall = exp2_fast(s.c[kL][16 * q + crow + rr]);
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) sacc[jb][rr] *= dall;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.kh[16 * q + row][32 * ks + kq]);
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) {
+        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s.vt[16 * jb + row][32 * ks + kq]);
+        sacc[jb] = mfma(a, bb, sacc[jb]);
+      }
+    }
+    __syncthreads();  // every wave is done with this chunk's LDS
+
+    write_sp();
+    cur = nxt;
+    wc = wn;
+  }
+  if (s_out) {
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        s_out[sbase + size_t(16 * q + crow + rr) * kD + j0 + 16 * jb + row] = sacc[jb][rr];
+  }
+}
+
+}  // namespace
+
+hipError_t wkv6_forward_launch(int64_t B, int64_t T, int64_t H, const uint16_t* r,
+                               const uint16_t* k, const uint16_t* v, const float* w,
+                               const float* u, float* o, const float* s_in, float* s_out,
+                               hipStream_t stream) {
+  const int64_t BH = B * H;
+  const unsigned grid = unsigned((BH + 7) / 8 * 8 * (kD / 32));
+  hipLaunchKernelGGL(wkv6_fwd_chunked<32>, dim3(grid), dim3(256), 0, stream, int(T), int(H),
+                     int(BH), r, k, v, w, u, o, s_in, s_out);
+  return hipGetLastError();
+}
+
+}  // namespace rwkv

@@ -92,4 +92,14 @@ hipError_t wkv5_step_launch(int64_t B, int64_t H, float* s, const uint16_t* r,
                             const uint16_t* k, const uint16_t* v, const float* w,
                             const float* u, float* o, hipStream_t stream);
 
+// ----- Finch (RWKV-6): per-token decay w [B, T, H, D] (step: [B, H, D]) -----
+hipError_t wkv6_forward_launch(int64_t B, int64_t T, int64_t H, const uint16_t* r,
+                               const uint16_t* k, const uint16_t* v, const float* w,
+                               const float* u, float* o, const float* s_in, float* s_out,
+                               hipStream_t stream);
+
+hipError_t wkv6_step_launch(int64_t B, int64_t H, float* s, const uint16_t* r,
+                            const uint16_t* k, const uint16_t* v, const float* w,
+                            const float* u, float* o, hipStream_t stream);
+
 }  // namespace rwkv

@@ -46,6 +46,7 @@ def test_header_declares_the_boundary():
         "rwkv_wkv4_backward_workspace", "rwkv_wkv4_backward",
         "rwkv_wkv4_state_init", "rwkv_wkv4_step", "rwkv_wkv5_forward_workspace",
         "rwkv_wkv5_forward", "rwkv_wkv5_forward_state", "rwkv_wkv5_step",
+        "rwkv_wkv6_forward", "rwkv_wkv6_step",
     ])
 
 
@@ -209,4 +210,27 @@ def test_wkv4_backward_rejections(lib):
     assert f(2, 300, 128, *args(), FAKE, need - 1, NULL) == WORKSPACE
     assert f(2, 300, 128, *args(), MISALIGNED, need, NULL) == ALIGN
     assert lib.rwkv_wkv4_backward_workspace(0, 10, 10) == 0
+    assert lib.rwkv_last_hip_error() == 0
+
+
+def test_wkv6_rejections(lib):
+    _skip_if_gpu()
+    f = lib.rwkv_wkv6_forward
+    names = "r k v w u o s_in s_out".split()
+    ptrs = lambda **kw: [kw.get(n, FAKE) for n in names]  # noqa: E731
+    assert f(0, 64, 2, 64, *[NULL] * 8, NULL) == OK
+    assert f(1, 64, 2, 32, *ptrs(), NULL) == UNSUPPORTED
+    assert f(1, -64, 2, 64, *ptrs(), NULL) == SHAPE
+    for n in names[:6]:
+        assert f(1, 64, 2, 64, *ptrs(**{n: NULL}), NULL) == NULLPTR, n
+    for n in names:
+        assert f(1, 64, 2, 64, *ptrs(**{n: MISALIGNED}), NULL) == ALIGN, n
+    st = lib.rwkv_wkv6_step
+    names = "s r k v w u o".split()
+    ptrs = lambda **kw: [kw.get(n, FAKE) for n in names]  # noqa: E731
+    assert st(0, 2, 64, *[NULL] * 7, NULL) == OK
+    assert st(1, 2, 16, *ptrs(), NULL) == UNSUPPORTED
+    for n in names:
+        assert st(1, 2, 64, *ptrs(**{n: NULL}), NULL) == NULLPTR, n
+        assert st(1, 2, 64, *ptrs(**{n: MISALIGNED}), NULL) == ALIGN, n
     assert lib.rwkv_last_hip_error() == 0

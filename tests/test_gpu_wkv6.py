@@ -1,0 +1,145 @@
+"""GPU parity of the Finch (per-token decay) forward and step against the
+fp64 oracle.
+
+Tolerance as for Eagle: max |o - o_ref| / o_abs <= 2e-2 for the bf16-MFMA
+forward (o_abs: the same recurrence over |r|, |k|, |v|, |u|); the step is
+exact float32 arithmetic on the bf16 inputs (1e-5).
+"""
+import numpy as np
+import pytest
+
+import linear_attention_sequence_rwkv_amd as rw
+import oracle.wkv_oracle as O
+import synth
+from wkv_testutil import WKV5_TOL, log, to_dev, torch_dev, wkv5_scaled_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(e, name, sl=np.s_[:]):
+    torch, _ = torch_dev()
+    return to_dev(np.ascontiguousarray(e[name + "_bits"][sl]), torch.bfloat16)
+
+
+def gpu_finch(e, s_in=None, s_out=None):
+    torch, _ = torch_dev()
+    o, s = rw.rwkv_wkv6_forward(_bits(e, "r"), _bits(e, "k"), _bits(e, "v"), to_dev(e["wt"]),
+                                to_dev(e["u"]), s_in=s_in, s_out=s_out)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), (None if s is None else s.cpu().numpy())
+
+
+def check(e, bs=None, hs=None, tol=WKV5_TOL):
+    o, _ = gpu_finch(e)
+    r, k, v, wt, u = (e[n] for n in ("r", "k", "v", "wt", "u"))
+    if bs is not None:
+        r, k, v, wt = r[bs], k[bs], v[bs], wt[bs]
+        o = o[bs]
+    if hs is not None:
+        r, k, v, wt, u = r[:, :, hs], k[:, :, hs], v[:, :, hs], wt[:, :, hs], u[hs]
+        o = o[:, :, hs]
+    o_ref, _ = O.wkv6_recurrent(r, k, v, wt, u)
+    o_abs, _ = O.wkv6_scale(r, k, v, wt, u)
+    err = wkv5_scaled_err(o, o_ref, o_abs)
+    log(f"  err={err:.3e}")
+    assert err <= tol
+    assert np.all(np.isfinite(o))
+    return err
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1), (2, 100, 3), (1, 257, 2), (3, 64, 1), (2, 200, 9)])
+def test_small_shapes(shape):
+    B, T, H = shape
+    log(f"wkv6_forward B={B} T={T} H={H}")
+    check(synth.wkv6_inputs(B, T, H, 64, seed=50 + T))
+
+
+@pytest.mark.parametrize("case", [("fast", 2.0, 3.5, 0.5), ("mixed", -6.0, 3.0, 1.5),
+                                  ("slow", -9.0, -6.0, 0.1)])
+def test_decay_ranges(case):
+    """fast: every |log2 w| > 15, every chunk computes its diagonal blocks
+    exactly; mixed: chunks of both kinds; slow: decays very close to 1."""
+    name, lo, hi, dstd = case
+    log(f"wkv6_forward decays {name}")
+    check(synth.wkv6_inputs(2, 300, 2, 64, seed=7, omega_lo=lo, omega_hi=hi, delta_std=dstd))
+
+
+def test_extreme_decays():
+    e = synth.wkv6_inputs(1, 200, 2, 64, seed=8)
+    wt = e["wt"].copy()
+    wt[:, 50:60] = 1e-30      # forget everything
+    wt[:, 100:140] = 1.0      # remember everything
+    log("wkv6_forward with w=1e-30 and w=1 stretches")
+    check(dict(e, wt=wt))
+
+
+def test_constant_decay_matches_eagle():
+    torch, _ = torch_dev()
+    e = synth.wkv6_inputs(2, 190, 3, 64, seed=9)
+    wt = np.ascontiguousarray(np.broadcast_to(e["w"][None, None], e["wt"].shape))
+    o6, _ = gpu_finch(dict(e, wt=wt))
+    o5 = rw.rwkv_wkv5_forward(_bits(e, "r"), _bits(e, "k"), _bits(e, "v"), to_dev(e["w"]),
+                              to_dev(e["u"]))
+    torch.cuda.synchronize()
+    o_abs = O.wkv5_scale(e["r"], e["k"], e["v"], e["w"], e["u"])
+    o_ref, _ = O.wkv5_recurrent(e["r"], e["k"], e["v"], e["w"], e["u"])
+    assert wkv5_scaled_err(o6, o_ref, o_abs) <= WKV5_TOL
+    assert wkv5_scaled_err(o6, o5.cpu().numpy().astype(np.float64), o_abs) <= WKV5_TOL
+
+
+def test_finch_workload_sampled_heads():
+    cfg = synth.CFG_WKV6_FINCH
+    log(f"wkv6_forward {cfg.name} (oracle on 2 batches x 3 heads)")
+    e = synth.wkv6_inputs(cfg.B, cfg.T, cfg.H, cfg.D, cfg.seed)
+    check(e, bs=np.array([0, 3]), hs=np.array([1, 16, 30]))
+
+
+@pytest.mark.parametrize("cut", [(100, 5, 129), (128, 0, 64), (1, 2, 63)])
+def test_forward_state_chain_matches_whole_sequence(cut):
+    torch, dev = torch_dev()
+    T1, N, T2 = cut
+    B, H = 2, 3
+    log(f"wkv6_forward/step chain {cut}")
+    e = synth.wkv6_inputs(B, T1 + N + T2, H, 64, seed=70 + T1 + N, delta_std=1.0)
+    u = to_dev(e["u"])
+    sl = np.s_[:, :T1]
+    o1, s = rw.rwkv_wkv6_forward(_bits(e, "r", sl), _bits(e, "k", sl), _bits(e, "v", sl),
+                                 to_dev(e["wt"][sl]), u, s_out=True)
+    outs = [o1]
+    for t in range(T1, T1 + N):
+        sl = np.s_[:, t]
+        outs.append(rw.rwkv_wkv6_step(s, _bits(e, "r", sl), _bits(e, "k", sl), _bits(e, "v", sl),
+                                      to_dev(e["wt"][sl]), u)[:, None])
+    sl = np.s_[:, T1 + N:]
+    o3, _ = rw.rwkv_wkv6_forward(_bits(e, "r", sl), _bits(e, "k", sl), _bits(e, "v", sl),
+                                 to_dev(e["wt"][sl]), u, s_in=s, s_out=s)
+    outs.append(o3)
+    torch.cuda.synchronize()
+    o = torch.cat(outs, dim=1).cpu().numpy()
+    o_ref, s_ref = O.wkv6_recurrent(e["r"], e["k"], e["v"], e["wt"], e["u"])
+    o_abs, s_abs = O.wkv6_scale(e["r"], e["k"], e["v"], e["wt"], e["u"])
+    err_o = wkv5_scaled_err(o, o_ref, o_abs)
+    err_s = wkv5_scaled_err(s.cpu().numpy(), s_ref, s_abs)
+    log(f"  err o={err_o:.3e} state={err_s:.3e}")
+    assert err_o <= WKV5_TOL and err_s <= WKV5_TOL
+
+
+def test_steps_from_a_given_state():
+    torch, dev = torch_dev()
+    B, H, N = 3, 4, 30
+    e = synth.wkv6_inputs(B, N, H, 64, seed=11, delta_std=1.0)
+    s0 = np.random.default_rng(3).standard_normal((B, H, 64, 64)).astype(np.float32)
+    s = to_dev(s0)
+    outs = []
+    for t in range(N):
+        sl = np.s_[:, t]
+        outs.append(rw.rwkv_wkv6_step(s, _bits(e, "r", sl), _bits(e, "k", sl), _bits(e, "v", sl),
+                                      to_dev(e["wt"][sl]), to_dev(e["u"])))
+    torch.cuda.synchronize()
+    o = torch.stack(outs, dim=1).cpu().numpy()
+    o_ref, s_ref = O.wkv6_recurrent(e["r"], e["k"], e["v"], e["wt"], e["u"], S0=s0)
+    o_abs, s_abs = O.wkv6_scale(e["r"], e["k"], e["v"], e["wt"], e["u"], S0=s0)
+    err_o = wkv5_scaled_err(o, o_ref, o_abs)
+    err_s = wkv5_scaled_err(s.cpu().numpy(), s_ref, s_abs)
+    log(f"  err o={err_o:.3e} state={err_s:.3e}")
+    assert err_o <= 1e-5 and err_s <= 1e-5
