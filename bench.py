@@ -43,7 +43,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash(files=("wkv4.hip", "wkv_device.h")) -> str:
+def kernel_source_hash(files=("wkv4.hip", "wkv4_scan.h", "wkv_device.h")) -> str:
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(CSRC, f), "rb") as fh:
