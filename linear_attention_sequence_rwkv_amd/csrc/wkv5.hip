@@ -28,15 +28,14 @@
 
 #include <stdlib.h>
 
+#include <algorithm>
+
 namespace rwkv {
 
 namespace {
 
 using namespace eagle;
 
-constexpr int kExpLo = -32;   // decay table covers w^e for e in [kExpLo, kExpHi]
-constexpr int kExpHi = 64;
-constexpr int kExpN = kExpHi - kExpLo + 1;
 // Largest |log2 w| for which w^(-32) and w^31 stay far inside fp32/bf16 range.
 constexpr float kMaxLog2Decay = 3.6f;
 
@@ -47,7 +46,10 @@ struct Lds {
   __bf16 kh[kD][kPad];    // kh^T[i][sigma]
   __bf16 vt[DV][kPad];    // v^T[j][sigma]
   __bf16 sp[DV][kPad];    // (diag(w^32) S)^T[j][i]
-  float dec[kExpN][kD];   // w_i^e
+  float l2w[kD];          // log2 w_i
+  float w32[kD];          // w_i^32
+  float w64[kD];          // w_i^64
+  float scratch[4][kD];   // the exact recurrence's per-token vectors
   float beta[kL];
   float u[kD];
   int fallback;
@@ -64,10 +66,10 @@ __device__ void eagle_recurrent_slice(int T, int H, int b, int h, int j0,
                                      const float* __restrict__ u, float* __restrict__ o,
                                      const float* s_in, float* s_out,
                                      Lds<DV>& s) {
-  float* s_r = &s.dec[0][0];
-  float* s_k = &s.dec[1][0];
-  float* s_w = &s.dec[2][0];
-  float* s_u = &s.dec[3][0];
+  float* s_r = s.scratch[0];
+  float* s_k = s.scratch[1];
+  float* s_w = s.scratch[2];
+  float* s_u = s.scratch[3];
   const int tid = threadIdx.x;
   if (tid < kD) {
     s_w[tid] = w[h * kD + tid];
@@ -121,9 +123,10 @@ __device__ __forceinline__ void stage_consts(StageConsts& c, const Lds<DV>& s) {
   const int tau = tid >> 2, d0 = 16 * (tid & 3);
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    c.fr[e] = s.dec[tau - 32 - kExpLo][d0 + e];
-    c.fk[e] = s.dec[31 - tau - kExpLo][d0 + e];
-    c.fh[e] = s.dec[63 - tau - kExpLo][d0 + e];
+    const float l2 = s.l2w[d0 + e];
+    c.fr[e] = exp2f(float(tau - 32) * l2);
+    c.fk[e] = exp2f(float(31 - tau) * l2);
+    c.fh[e] = exp2f(float(63 - tau) * l2);
     c.ur[e] = s.u[d0 + e];
   }
 }
@@ -158,10 +161,11 @@ __device__ __forceinline__ void stage_chunk(const ChunkRegs& x, const StageConst
   }
   if (n_last > 0) {
     // rare: once per call, only when the final state is wanted
-    const float* dh = s.dec[max(n_last - 1 - tau, 0) - kExpLo];
+    const float back = float(max(n_last - 1 - tau, 0));
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      s.kh[d0 + e][tau] = to_bf16(tau < n_last ? kv[e] * dh[d0 + e] : 0.f);
+      const float dh = exp2f(back * s.l2w[d0 + e]);
+      s.kh[d0 + e][tau] = to_bf16(tau < n_last ? kv[e] * dh : 0.f);
       bpart = fmaf(rv[e] * f.ur[e], kv[e], bpart);
     }
   } else {
@@ -195,11 +199,14 @@ template <int DV>
 __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
     int T, int H, int BH, const uint16_t* __restrict__ r, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ w,
-    const float* __restrict__ u, float* __restrict__ o, const float* s_in, float* s_out) {
+    const float* __restrict__ u, float* __restrict__ o, const float* s_in, float* s_out,
+    int seg_chunks, const float* __restrict__ seg_state) {
   constexpr int NS = kD / DV;  // slices per head
   constexpr int NJB = DV / 16; // 16-wide value tiles per slice
   __shared__ Lds<DV> s;
-  const int bx = blockIdx.x;
+  const int per_seg = (BH + 7) / 8 * 8 * NS;  // workgroups per time segment
+  const int seg = blockIdx.x / per_seg;
+  const int bx = blockIdx.x - seg * per_seg;
   const int bh = (bx / (8 * NS)) * 8 + (bx & 7);
   const int slice = (bx >> 3) % NS;
   if (bh >= BH) return;
@@ -209,22 +216,23 @@ __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
   const int lane = tid & 63;
   const int q = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // Decay table w^e and the range check that picks the path.
+  // log2 w, the powers used every chunk, and the range check that picks the
+  // path.
   if (tid == 0) s.fallback = 0;
   __syncthreads();
   if (tid < kD) {
     const float wi = w[h * kD + tid];
     s.u[tid] = u[h * kD + tid];
     const float l2w = __log2f(wi);
+    s.l2w[tid] = l2w;
+    s.w32[tid] = exp2f(32.f * l2w);
+    s.w64[tid] = exp2f(64.f * l2w);
     if (!(fabsf(l2w) <= kMaxLog2Decay)) atomicOr(&s.fallback, 1);  // also catches NaN, w<=0
-  }
-  for (int idx = tid; idx < kExpN * kD; idx += 256) {
-    const int e = idx / kD + kExpLo, i = idx % kD;
-    s.dec[e - kExpLo][i] = exp2f(float(e) * __log2f(w[h * kD + i]));
   }
   __syncthreads();
   if (s.fallback) {
-    eagle_recurrent_slice<DV>(T, H, b, h, j0, r, k, v, w, u, o, s_in, s_out, s);
+    // the exact recurrence runs the whole sequence in the first segment
+    if (seg == 0) eagle_recurrent_slice<DV>(T, H, b, h, j0, r, k, v, w, u, o, s_in, s_out, s);
     return;
   }
 
@@ -242,6 +250,24 @@ __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
     for (int rr = 0; rr < 4; ++rr)
       sacc[jb][rr] = s_in ? s_in[sbase + size_t(16 * q + crow + rr) * kD + j0 + 16 * jb + row]
                           : 0.f;
+  // A later segment starts from the earlier segments' local end states,
+  // each decayed over the segments after it: S <- w^len S + S_seg.
+  if (seg > 0) {
+    float dseg[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      dseg[rr] = exp2f(float(seg_chunks * kL) * s.l2w[16 * q + crow + rr]);
+    const int nseg = int(gridDim.x) / per_seg;
+    for (int sg = 0; sg < seg; ++sg) {
+      const float* src = seg_state + (size_t(bh) * (nseg - 1) + sg) * kD * kD;
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          sacc[jb][rr] = fmaf(dseg[rr], sacc[jb][rr],
+                              src[size_t(16 * q + crow + rr) * kD + j0 + 16 * jb + row]);
+    }
+  }
   auto write_sp = [&]() {
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) {
@@ -250,7 +276,7 @@ __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int i = 16 * q + crow + rr;
-        pk[rr] = to_bf16(sacc[jb][rr] * s.dec[32 - kExpLo][i]);
+        pk[rr] = to_bf16(sacc[jb][rr] * s.w32[i]);
       }
       *reinterpret_cast<bf16x4*>(&s.sp[16 * jb + row][16 * q + crow]) = pk;
     }
@@ -260,14 +286,16 @@ __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
   StageConsts f;
   stage_consts(f, s);
   const int n_chunks = (T + kL - 1) / kL;
+  const int c_begin = seg * seg_chunks;
+  const int c_end = min(n_chunks, c_begin + seg_chunks);
   ChunkRegs cur, nxt;
-  load_chunk<DV>(cur, 0, T, H, b, h, j0, r, k, v);
-  for (int c = 0; c < n_chunks; ++c) {
+  load_chunk<DV>(cur, c_begin * kL, T, H, b, h, j0, r, k, v);
+  for (int c = c_begin; c < c_end; ++c) {
     const int t0 = c * kL;
     const int n_last = (s_out && c == n_chunks - 1 && T - t0 < kL) ? T - t0 : 0;
     stage_chunk(cur, f, s, n_last);
     __syncthreads();
-    if (c + 1 < n_chunks) load_chunk<DV>(nxt, t0 + kL, T, H, b, h, j0, r, k, v);
+    if (c + 1 < c_end) load_chunk<DV>(nxt, t0 + kL, T, H, b, h, j0, r, k, v);
 
     // A^T = kt rt^T for sigma blocks 0..q against this wave's 16 tokens:
     // lane holds column tau = 16q + row, rows sigma = 16nb + crow .. +3.
@@ -340,7 +368,8 @@ __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
     // chunk decays by w^n_last).
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const float d64 = s.dec[(n_last > 0 ? n_last : 64) - kExpLo][16 * q + crow + rr];
+      const int i = 16 * q + crow + rr;
+      const float d64 = n_last > 0 ? exp2f(float(n_last) * s.l2w[i]) : s.w64[i];
 #pragma unroll
       for (int jb = 0; jb < NJB; ++jb) sacc[jb][rr] *= d64;
     }
@@ -358,13 +387,110 @@ __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
     write_sp();  // S' for the next chunk
     cur = nxt;
   }
-  if (s_out) {
+  if (s_out && c_end == n_chunks) {
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
         s_out[sbase + size_t(16 * q + crow + rr) * kD + j0 + 16 * jb + row] = sacc[jb][rr];
   }
+}
+
+// Local end state of one time segment (all but the last), from a zero
+// start: S <- w^64 S + kh^T V over its chunks, for one value slice.  Written
+// to seg_state[bh][seg] as [key i][value j].
+template <int DV>
+__global__ __launch_bounds__(256) void wkv5_seg_state(int T, int H, int BH, int seg_chunks,
+                                                      int nseg, const uint16_t* __restrict__ k,
+                                                      const uint16_t* __restrict__ v,
+                                                      const float* __restrict__ w,
+                                                      float* __restrict__ seg_state) {
+  constexpr int NS = kD / DV;
+  constexpr int NJB = DV / 16;
+  __shared__ __bf16 s_kh[kD][kPad];
+  __shared__ __bf16 s_vt[DV][kPad];
+  __shared__ float s_l2w[kD];
+  __shared__ float s_w64[kD];
+  __shared__ int s_fallback;
+  const int per_seg = (BH + 7) / 8 * 8 * NS;
+  const int seg = blockIdx.x / per_seg;
+  const int bx = blockIdx.x - seg * per_seg;
+  const int bh = (bx / (8 * NS)) * 8 + (bx & 7);
+  const int slice = (bx >> 3) % NS;
+  if (bh >= BH) return;
+  const int b = bh / H, h = bh - (bh / H) * H;
+  const int j0 = slice * DV;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int q = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row = lane & 15, kq = 8 * (lane >> 4), crow = 4 * (lane >> 4);
+  if (tid == 0) s_fallback = 0;
+  __syncthreads();
+  if (tid < kD) {
+    const float l2w = __log2f(w[h * kD + tid]);
+    s_l2w[tid] = l2w;
+    s_w64[tid] = exp2f(64.f * l2w);
+    if (!(fabsf(l2w) <= kMaxLog2Decay)) atomicOr(&s_fallback, 1);
+  }
+  __syncthreads();
+  if (s_fallback) return;  // that head runs the exact recurrence in one piece
+  const int tau = tid >> 2, q4 = tid & 3, d0 = 16 * q4;
+  float fh[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) fh[e] = exp2f(float(63 - tau) * s_l2w[d0 + e]);
+  floatx4 sacc[NJB];
+#pragma unroll
+  for (int jb = 0; jb < NJB; ++jb) sacc[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int c_begin = seg * seg_chunks;
+  for (int c = c_begin; c < c_begin + seg_chunks; ++c) {
+    // every chunk here is whole: only the last segment reaches the end of T
+    const size_t off = ((size_t(b) * T + size_t(c) * kL + tau) * H + h) * kD;
+    const uint4* kp = reinterpret_cast<const uint4*>(k + off + d0);
+    const uint4 k0 = kp[0], k1 = kp[1];
+    uint4 v0;
+    if constexpr (DV == 32) {
+      v0 = *reinterpret_cast<const uint4*>(v + off + j0 + 8 * q4);
+    } else {
+      const uint2 t2 = *reinterpret_cast<const uint2*>(v + off + j0 + 4 * q4);
+      v0 = uint4{t2.x, t2.y, 0u, 0u};
+    }
+    const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      s_kh[d0 + 2 * e][tau] = to_bf16(lo_half(kw[e]) * fh[2 * e]);
+      s_kh[d0 + 2 * e + 1][tau] = to_bf16(hi_half(kw[e]) * fh[2 * e + 1]);
+    }
+    const uint32_t vw[4] = {v0.x, v0.y, v0.z, v0.w};
+    constexpr int VPT = DV / 4;
+#pragma unroll
+    for (int e = 0; e < VPT / 2; ++e) {
+      s_vt[VPT * q4 + 2 * e][tau] = to_bf16(lo_half(vw[e]));
+      s_vt[VPT * q4 + 2 * e + 1][tau] = to_bf16(hi_half(vw[e]));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float d64 = s_w64[16 * q + crow + rr];
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) sacc[jb][rr] *= d64;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s_kh[16 * q + row][32 * ks + kq]);
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) {
+        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s_vt[16 * jb + row][32 * ks + kq]);
+        sacc[jb] = mfma(a, bb, sacc[jb]);
+      }
+    }
+    __syncthreads();
+  }
+  float* dst = seg_state + (size_t(bh) * (nseg - 1) + seg) * kD * kD;
+#pragma unroll
+  for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      dst[size_t(16 * q + crow + rr) * kD + j0 + 16 * jb + row] = sacc[jb][rr];
 }
 
 // One token of the recurrence for every (batch, head): lane j keeps the
@@ -406,24 +532,67 @@ __global__ __launch_bounds__(64) void wkv5_step_kernel(
 
 }  // namespace
 
-size_t wkv5_workspace_bytes(int64_t, int64_t, int64_t, int64_t) { return 0; }
+namespace {
+
+// Time segments per head: about four workgroups per CU over the launch (two
+// are resident at a time within the register budget; measured 197 us in one
+// segment, 175 us in two, 168 us in four at B=4 T=4096 H=32), segments of
+// at least four chunks.  RWKV_WKV5_SEGS overrides (tests, sweeps).
+constexpr int64_t kTargetWorkgroups = 1024;
+
+int wkv5_segments(int64_t BH, int64_t T, int ns) {
+  const int64_t n_chunks = (T + kL - 1) / kL;
+  const int64_t per_seg = (BH + 7) / 8 * 8 * ns;
+  int64_t nseg = (kTargetWorkgroups + per_seg - 1) / per_seg;
+  if (const char* env = getenv("RWKV_WKV5_SEGS")) nseg = atoi(env);
+  nseg = std::max<int64_t>(1, std::min<int64_t>(nseg, n_chunks / 4));
+  const int64_t seg_chunks = (n_chunks + nseg - 1) / nseg;
+  return int((n_chunks + seg_chunks - 1) / seg_chunks);
+}
+
+int wkv5_dv() {
+  if (const char* env = getenv("RWKV_WKV5_DV")) return atoi(env) == 16 ? 16 : 32;
+  return 32;
+}
+
+}  // namespace
+
+size_t wkv5_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t D) {
+  (void)D;
+  const int nseg = wkv5_segments(B * H, T, kD / wkv5_dv());
+  return size_t(B * H) * size_t(nseg - 1) * kD * kD * sizeof(float);
+}
 
 hipError_t wkv5_forward_launch(int64_t B, int64_t T, int64_t H, int64_t D,
                                const uint16_t* r, const uint16_t* k, const uint16_t* v,
                                const float* w, const float* u, float* o, void* ws,
                                const float* s_in, float* s_out, hipStream_t stream) {
   (void)D;
-  (void)ws;
   const int64_t BH = B * H;
-  int dv = 32;
-  if (const char* env = getenv("RWKV_WKV5_DV")) dv = atoi(env) == 16 ? 16 : 32;
-  const unsigned grid = unsigned((BH + 7) / 8 * 8 * (kD / dv));
+  const int dv = wkv5_dv();
+  const int ns = kD / dv;
+  const int nseg = wkv5_segments(BH, T, ns);
+  const int64_t n_chunks = (T + kL - 1) / kL;
+  const int seg_chunks = int((n_chunks + nseg - 1) / nseg);
+  const unsigned per_seg = unsigned((BH + 7) / 8 * 8 * ns);
+  float* seg_state = static_cast<float*>(ws);
+  if (nseg > 1) {
+    if (dv == 16)
+      hipLaunchKernelGGL(wkv5_seg_state<16>, dim3(per_seg * unsigned(nseg - 1)), dim3(256), 0,
+                         stream, int(T), int(H), int(BH), seg_chunks, nseg, k, v, w, seg_state);
+    else
+      hipLaunchKernelGGL(wkv5_seg_state<32>, dim3(per_seg * unsigned(nseg - 1)), dim3(256), 0,
+                         stream, int(T), int(H), int(BH), seg_chunks, nseg, k, v, w, seg_state);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid(per_seg * unsigned(nseg));
   if (dv == 16)
-    hipLaunchKernelGGL(wkv5_fwd_chunked<16>, dim3(grid), dim3(256), 0, stream, int(T), int(H),
-                       int(BH), r, k, v, w, u, o, s_in, s_out);
+    hipLaunchKernelGGL(wkv5_fwd_chunked<16>, grid, dim3(256), 0, stream, int(T), int(H), int(BH),
+                       r, k, v, w, u, o, s_in, s_out, seg_chunks, seg_state);
   else
-    hipLaunchKernelGGL(wkv5_fwd_chunked<32>, dim3(grid), dim3(256), 0, stream, int(T), int(H),
-                       int(BH), r, k, v, w, u, o, s_in, s_out);
+    hipLaunchKernelGGL(wkv5_fwd_chunked<32>, grid, dim3(256), 0, stream, int(T), int(H), int(BH),
+                       r, k, v, w, u, o, s_in, s_out, seg_chunks, seg_state);
   return hipGetLastError();
 }
 

@@ -232,3 +232,56 @@ def test_eagle_decode_workload_sampled_heads():
         err_s = wkv5_scaled_err(s[b:b + 1, h:h + 1].cpu().numpy(), s_ref, s_abs)
         log(f"  pair {(b, h)}: err o={err_o:.3e} state={err_s:.3e}")
         assert err_o <= 1e-5 and err_s <= 1e-5
+
+
+@pytest.mark.parametrize("segs", [1, 2, 3, 4])
+@pytest.mark.parametrize("shape", [(2, 1000, 3), (1, 777, 2), (3, 1024, 1)])
+def test_time_segments(shape, segs):
+    """The forward split into time segments (a local end state per segment,
+    folded into the next segments' starting states) equals one pass; with a
+    starting state and the handed-on state too."""
+    torch, dev = torch_dev()
+    B, T, H = shape
+    log(f"wkv5_forward B={B} T={T} H={H} segments={segs}")
+    inp = synth.wkv5_inputs(B, T, H, 64, seed=90 + T + segs)
+    s0 = (np.random.default_rng(segs).standard_normal((B, H, 64, 64)) * 0.3).astype(np.float32)
+    old = os.environ.get("RWKV_WKV5_SEGS")
+    os.environ["RWKV_WKV5_SEGS"] = str(segs)
+    try:
+        o, s1 = rw.rwkv_wkv5_forward_state(_bits(inp, "r", np.s_[:]), _bits(inp, "k", np.s_[:]),
+                                           _bits(inp, "v", np.s_[:]), to_dev(inp["w"]),
+                                           to_dev(inp["u"]), s_in=to_dev(s0), s_out=True)
+        torch.cuda.synchronize()
+    finally:
+        if old is None:
+            del os.environ["RWKV_WKV5_SEGS"]
+        else:
+            os.environ["RWKV_WKV5_SEGS"] = old
+    o_ref, s_ref = O.wkv5_recurrent(inp["r"], inp["k"], inp["v"], inp["w"], inp["u"], S0=s0)
+    o_abs, s_abs = O.wkv5_recurrent(np.abs(inp["r"]), np.abs(inp["k"]), np.abs(inp["v"]),
+                                    inp["w"], np.abs(inp["u"]), S0=np.abs(s0))
+    err_o = wkv5_scaled_err(o.cpu().numpy(), o_ref, o_abs)
+    err_s = wkv5_scaled_err(s1.cpu().numpy(), s_ref, s_abs)
+    log(f"  err o={err_o:.3e} state={err_s:.3e}")
+    assert err_o <= WKV5_TOL and err_s <= WKV5_TOL
+
+
+def test_time_segments_with_exact_recurrence_heads():
+    """A head outside the factorised range runs the exact recurrence in one
+    piece while the other heads are split."""
+    torch, dev = torch_dev()
+    inp = synth.wkv5_inputs(1, 1000, 3, 64, seed=5)
+    w = inp["w"].copy()
+    w[1] = 0.05  # |log2 w| > 3.6: exact path for head 1
+    case = dict(inp, w=w)
+    old = os.environ.get("RWKV_WKV5_SEGS")
+    os.environ["RWKV_WKV5_SEGS"] = "3"
+    try:
+        o = gpu_wkv5(case)
+    finally:
+        if old is None:
+            del os.environ["RWKV_WKV5_SEGS"]
+        else:
+            os.environ["RWKV_WKV5_SEGS"] = old
+    o_ref, o_abs = oracle_wkv5(case)
+    assert wkv5_scaled_err(o, o_ref, o_abs) <= WKV5_TOL
