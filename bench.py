@@ -261,14 +261,22 @@ def bench_wkv5(torch, rw, cfg, reps):
     r, k, v = (to(inp[n + "_bits"]).view(torch.bfloat16) for n in ("r", "k", "v"))
     w, u = to(inp["w"]), to(inp["u"])
     o = torch.empty((cfg.B, cfg.T, cfg.H, cfg.D), dtype=torch.float32, device=dev)
-    rw.rwkv_wkv5_forward(r, k, v, w, u, o=o)
+    lib = rw.load_library()
+    need = lib.rwkv_wkv5_forward_workspace(cfg.B, cfg.T, cfg.H, cfg.D)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    args = (cfg.B, cfg.T, cfg.H, cfg.D, P(r), P(k), P(v), P(w), P(u), P(o), P(ws), need,
+            ctypes.c_void_p(stream.cuda_stream))
+    assert lib.rwkv_wkv5_forward(*args) == 0
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
+    s.record(stream)
     for _ in range(reps):
-        rw.rwkv_wkv5_forward(r, k, v, w, u, o=o)
-    e.record()
+        assert lib.rwkv_wkv5_forward(*args) == 0
+    e.record(stream)
     torch.cuda.synchronize()
+    assert torch.isfinite(o).all().item()
     ms = s.elapsed_time(e) / reps
     elems = cfg.B * cfg.T * cfg.H * cfg.D
     return {"ms": ms, "elems": elems, "bytes": 10 * elems, "flops": 4 * cfg.D * elems}

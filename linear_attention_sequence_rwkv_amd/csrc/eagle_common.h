@@ -23,9 +23,9 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t x) {
 __device__ __forceinline__ __bf16 to_bf16(float x) { return static_cast<__bf16>(x); }
 
 // One chunk's raw inputs for this thread: token tau = tid/4, dims 16*(tid%4)
-// of r and k, and DV/4 value dims of this workgroup's slice (8 or 4).
+// of r and k, and DV/4 value dims of this workgroup's slice (16, 8 or 4).
 struct ChunkRegs {
-  uint4 r0, r1, k0, k1, v0;
+  uint4 r0, r1, k0, k1, v0, v1;  // v1: the second half of 16 value dims (DV = 64)
 };
 
 template <int DV>
@@ -43,14 +43,18 @@ __device__ __forceinline__ void load_chunk(ChunkRegs& x, int t0, int T, int H, i
     x.r1 = rp[1];
     x.k0 = kp[0];
     x.k1 = kp[1];
-    if constexpr (DV == 32) {
+    x.v1 = uint4{0u, 0u, 0u, 0u};
+    if constexpr (DV == 64) {
+      x.v0 = *reinterpret_cast<const uint4*>(v + off + 16 * q4);
+      x.v1 = *reinterpret_cast<const uint4*>(v + off + 16 * q4 + 8);
+    } else if constexpr (DV == 32) {
       x.v0 = *reinterpret_cast<const uint4*>(v + off + j0 + 8 * q4);
     } else {
       const uint2 t = *reinterpret_cast<const uint2*>(v + off + j0 + 4 * q4);
       x.v0 = uint4{t.x, t.y, 0u, 0u};
     }
   } else {
-    x.r0 = x.r1 = x.k0 = x.k1 = x.v0 = uint4{0u, 0u, 0u, 0u};
+    x.r0 = x.r1 = x.k0 = x.k1 = x.v0 = x.v1 = uint4{0u, 0u, 0u, 0u};
   }
 }
 

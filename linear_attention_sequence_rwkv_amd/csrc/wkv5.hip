@@ -179,7 +179,7 @@ __device__ __forceinline__ void stage_chunk(const ChunkRegs& x, const StageConst
   *reinterpret_cast<bf16x8*>(&s.rt[tau][d0 + 8]) = rt1;
   *reinterpret_cast<bf16x8*>(&s.kt[tau][d0]) = kt0;
   *reinterpret_cast<bf16x8*>(&s.kt[tau][d0 + 8]) = kt1;
-  const uint32_t vw[4] = {x.v0.x, x.v0.y, x.v0.z, x.v0.w};
+  const uint32_t vw[8] = {x.v0.x, x.v0.y, x.v0.z, x.v0.w, x.v1.x, x.v1.y, x.v1.z, x.v1.w};
   constexpr int VPT = DV / 4;  // value dims per thread
 #pragma unroll
   for (int e = 0; e < VPT / 2; ++e) {
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
         ap[nb >> 1][(nb & 1) * 4 + rr] = to_bf16(val);
       }
 
-    // O = A' V + rt S'  (16 tokens x 32 value columns per wave).
+    // O = A' V + rt S'  (16 tokens x DV value columns per wave).
     floatx4 oacc[NJB];
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) oacc[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -447,8 +447,11 @@ __global__ __launch_bounds__(256) void wkv5_seg_state(int T, int H, int BH, int 
     const size_t off = ((size_t(b) * T + size_t(c) * kL + tau) * H + h) * kD;
     const uint4* kp = reinterpret_cast<const uint4*>(k + off + d0);
     const uint4 k0 = kp[0], k1 = kp[1];
-    uint4 v0;
-    if constexpr (DV == 32) {
+    uint4 v0, v1 = uint4{0u, 0u, 0u, 0u};
+    if constexpr (DV == 64) {
+      v0 = *reinterpret_cast<const uint4*>(v + off + 16 * q4);
+      v1 = *reinterpret_cast<const uint4*>(v + off + 16 * q4 + 8);
+    } else if constexpr (DV == 32) {
       v0 = *reinterpret_cast<const uint4*>(v + off + j0 + 8 * q4);
     } else {
       const uint2 t2 = *reinterpret_cast<const uint2*>(v + off + j0 + 4 * q4);
@@ -460,7 +463,7 @@ __global__ __launch_bounds__(256) void wkv5_seg_state(int T, int H, int BH, int 
       s_kh[d0 + 2 * e][tau] = to_bf16(lo_half(kw[e]) * fh[2 * e]);
       s_kh[d0 + 2 * e + 1][tau] = to_bf16(hi_half(kw[e]) * fh[2 * e + 1]);
     }
-    const uint32_t vw[4] = {v0.x, v0.y, v0.z, v0.w};
+    const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     constexpr int VPT = DV / 4;
 #pragma unroll
     for (int e = 0; e < VPT / 2; ++e) {
@@ -534,11 +537,12 @@ __global__ __launch_bounds__(64) void wkv5_step_kernel(
 
 namespace {
 
-// Time segments per head: about four workgroups per CU over the launch (two
-// are resident at a time within the register budget; measured 197 us in one
-// segment, 175 us in two, 168 us in four at B=4 T=4096 H=32), segments of
-// at least four chunks.  RWKV_WKV5_SEGS overrides (tests, sweeps).
-constexpr int64_t kTargetWorkgroups = 1024;
+// Time segments per head: about two workgroups per CU over the launch,
+// segments of at least four chunks.  Measured at B=4 T=4096 H=32 with whole
+// heads per workgroup: 242 us in one segment, 128 us in four, 133 us in
+// eight (with 32-column slices the best was 166 us).  RWKV_WKV5_SEGS
+// overrides (tests, sweeps).
+constexpr int64_t kTargetWorkgroups = 512;
 
 int wkv5_segments(int64_t BH, int64_t T, int ns) {
   const int64_t n_chunks = (T + kL - 1) / kL;
@@ -551,8 +555,11 @@ int wkv5_segments(int64_t BH, int64_t T, int ns) {
 }
 
 int wkv5_dv() {
-  if (const char* env = getenv("RWKV_WKV5_DV")) return atoi(env) == 16 ? 16 : 32;
-  return 32;
+  if (const char* env = getenv("RWKV_WKV5_DV")) {
+    const int dv = atoi(env);
+    return dv == 16 || dv == 64 ? dv : 32;
+  }
+  return 64;  // whole heads: the intra-chunk products are not repeated per slice
 }
 
 }  // namespace
@@ -580,6 +587,9 @@ hipError_t wkv5_forward_launch(int64_t B, int64_t T, int64_t H, int64_t D,
     if (dv == 16)
       hipLaunchKernelGGL(wkv5_seg_state<16>, dim3(per_seg * unsigned(nseg - 1)), dim3(256), 0,
                          stream, int(T), int(H), int(BH), seg_chunks, nseg, k, v, w, seg_state);
+    else if (dv == 64)
+      hipLaunchKernelGGL(wkv5_seg_state<64>, dim3(per_seg * unsigned(nseg - 1)), dim3(256), 0,
+                         stream, int(T), int(H), int(BH), seg_chunks, nseg, k, v, w, seg_state);
     else
       hipLaunchKernelGGL(wkv5_seg_state<32>, dim3(per_seg * unsigned(nseg - 1)), dim3(256), 0,
                          stream, int(T), int(H), int(BH), seg_chunks, nseg, k, v, w, seg_state);
@@ -589,6 +599,9 @@ hipError_t wkv5_forward_launch(int64_t B, int64_t T, int64_t H, int64_t D,
   const dim3 grid(per_seg * unsigned(nseg));
   if (dv == 16)
     hipLaunchKernelGGL(wkv5_fwd_chunked<16>, grid, dim3(256), 0, stream, int(T), int(H), int(BH),
+                       r, k, v, w, u, o, s_in, s_out, seg_chunks, seg_state);
+  else if (dv == 64)
+    hipLaunchKernelGGL(wkv5_fwd_chunked<64>, grid, dim3(256), 0, stream, int(T), int(H), int(BH),
                        r, k, v, w, u, o, s_in, s_out, seg_chunks, seg_state);
   else
     hipLaunchKernelGGL(wkv5_fwd_chunked<32>, grid, dim3(256), 0, stream, int(T), int(H), int(BH),

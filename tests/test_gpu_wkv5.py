@@ -47,7 +47,7 @@ def oracle_wkv5(inp, b_idx=None, h_idx=None):
     return o, O.wkv5_scale(r, k, v, w, u)
 
 
-@pytest.mark.parametrize("dv", [32, 16])
+@pytest.mark.parametrize("dv", [64, 32, 16])
 @pytest.mark.parametrize("shape", [(1, 1, 1), (2, 100, 3), (1, 257, 2), (3, 64, 1), (2, 200, 9)])
 def test_small_shapes(shape, dv):
     B, T, H = shape
@@ -74,7 +74,7 @@ def test_eagle_workload_sampled_heads():
     assert np.all(np.isfinite(o))
 
 
-@pytest.mark.parametrize("dv", [32, 16])
+@pytest.mark.parametrize("dv", [64, 32, 16])
 def test_no_decay_and_fast_decay_extremes(dv):
     B, T, H = 1, 300, 2
     inp = synth.wkv5_inputs(B, T, H, 64, seed=77)
@@ -111,7 +111,7 @@ def _with_dv(dv, fn):
             os.environ["RWKV_WKV5_DV"] = old
 
 
-@pytest.mark.parametrize("dv", [32, 16])
+@pytest.mark.parametrize("dv", [64, 32, 16])
 @pytest.mark.parametrize("case", [("decay", 100, 5, 129), ("decay", 128, 0, 64),
                                   ("decay", 1, 2, 63), ("w=0.05", 70, 3, 90)])
 def test_forward_state_chain_matches_whole_sequence(case, dv):
@@ -179,7 +179,7 @@ def test_steps_from_a_given_state():
     assert err_o <= 1e-5 and err_s <= 1e-5
 
 
-@pytest.mark.parametrize("dv", [32, 16])
+@pytest.mark.parametrize("dv", [64, 32, 16])
 def test_forward_from_a_given_state(dv):
     """A random (not chain-built) starting state through the chunked path."""
     torch, dev = torch_dev()
