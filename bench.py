@@ -293,8 +293,10 @@ def bench_wkv6(torch, rw, cfg, reps):
     lib = rw.load_library()
     stream = torch.cuda.current_stream(dev)
     P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    args = (cfg.B, cfg.T, cfg.H, cfg.D, P(r), P(k), P(v), P(wt), P(u), P(o), None, None,
-            ctypes.c_void_p(stream.cuda_stream))
+    need = lib.rwkv_wkv6_forward_workspace(cfg.B, cfg.T, cfg.H, cfg.D)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+    args = (cfg.B, cfg.T, cfg.H, cfg.D, P(r), P(k), P(v), P(wt), P(u), P(o), None, None, P(ws),
+            need, ctypes.c_void_p(stream.cuda_stream))
     assert lib.rwkv_wkv6_forward(*args) == 0
     torch.cuda.synchronize()
     s, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -250,15 +250,19 @@ int rwkv_wkv5_step(int64_t B, int64_t H, int64_t D,
  *   s_in, s_out [B,H,D,D] float32 states before the first / after the last
  *                       token, either may be NULL (zero start / not wanted);
  *                       s_out may equal s_in.
- *   D must be 64.  No workspace.
+ *   ws, ws_bytes: at least rwkv_wkv6_forward_workspace(B,T,H,D) bytes (may be
+ *   0, then ws may be NULL); no zero-fill needed.
+ *   D must be 64.
  * Accuracy: as rwkv_wkv5_forward, against the same magnitude recurrence with
  * the per-token decays.
  * ---------------------------------------------------------------------- */
+size_t rwkv_wkv6_forward_workspace(int64_t B, int64_t T, int64_t H, int64_t D);
 int rwkv_wkv6_forward(int64_t B, int64_t T, int64_t H, int64_t D,
                       const uint16_t* r, const uint16_t* k, const uint16_t* v,
                       const float* w, const float* u,
                       float* o,
-                      const float* s_in, float* s_out, hipStream_t stream);
+                      const float* s_in, float* s_out,
+                      void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Finch single-token step: as rwkv_wkv5_step with this token's decay.

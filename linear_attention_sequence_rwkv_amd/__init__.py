@@ -52,8 +52,9 @@ _SIGNATURES = {
     "rwkv_wkv5_forward_state": (ctypes.c_int, [_i64, _i64, _i64, _i64, _p, _p, _p, _p, _p,
                                                _p, _p, _p, _p, _sz, _p]),
     "rwkv_wkv5_step": (ctypes.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "rwkv_wkv6_forward_workspace": (_sz, [_i64, _i64, _i64, _i64]),
     "rwkv_wkv6_forward": (ctypes.c_int, [_i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p,
-                                         _p]),
+                                         _p, _sz, _p]),
     "rwkv_wkv6_step": (ctypes.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p]),
 }
 
@@ -447,7 +448,11 @@ def _finch_w(w, shape):
     return w
 
 
-def rwkv_wkv6_forward(r, k, v, w, u, s_in=None, s_out=None, o=None, stream=None):
+def rwkv_wkv6_forward_workspace(B: int, T: int, H: int, D: int) -> int:
+    return int(load_library().rwkv_wkv6_forward_workspace(B, T, H, D))
+
+
+def rwkv_wkv6_forward(r, k, v, w, u, s_in=None, s_out=None, o=None, ws=None, stream=None):
     """Finch forward: r, k, v [B,T,H,D] bf16, w [B,T,H,D] float32 per-token
     decays, u [H,D].  ``s_in``/``s_out`` as for rwkv_wkv5_forward_state.
     Returns (o, s_out)."""
@@ -462,8 +467,13 @@ def rwkv_wkv6_forward(r, k, v, w, u, s_in=None, s_out=None, o=None, stream=None)
         s_out = torch.empty((B, H, D, D), dtype=torch.float32, device=r.device)
     if s_out is not None:
         s_out = _wkv5_state_arg("s_out", s_out, B, H, D)
+    st = _stream(r.device, stream)
+    need = lib.rwkv_wkv6_forward_workspace(B, T, H, D)
+    if ws is None:
+        ws = _workspace("wkv6", r.device, st.value or 0, need)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     status = lib.rwkv_wkv6_forward(B, T, H, D, _ptr(r), _ptr(k), _ptr(v), _ptr(w), _ptr(u),
-                                   _ptr(o), _ptr(s_in), _ptr(s_out), _stream(r.device, stream))
+                                   _ptr(o), _ptr(s_in), _ptr(s_out), _ptr(ws), nbytes, st)
     _check("rwkv_wkv6_forward", status)
     return o, s_out
 

@@ -238,10 +238,16 @@ RWKV_API int rwkv_wkv5_step(int64_t B, int64_t H, int64_t D, float* s, const uin
 
 // ------------------------------------------------------------------- Finch
 
+RWKV_API size_t rwkv_wkv6_forward_workspace(int64_t B, int64_t T, int64_t H, int64_t D) {
+  int64_t n;
+  if (!dims_ok({B, T, H, D}, &n) || n == 0 || D != 64) return 0;
+  return rwkv::wkv6_workspace_bytes(B, T, H);
+}
+
 RWKV_API int rwkv_wkv6_forward(int64_t B, int64_t T, int64_t H, int64_t D, const uint16_t* r,
                                const uint16_t* k, const uint16_t* v, const float* w,
                                const float* u, float* o, const float* s_in, float* s_out,
-                               hipStream_t stream) {
+                               void* ws, size_t ws_bytes, hipStream_t stream) {
   int64_t n;
   if (!dims_ok({B, T, H, D}, &n)) return RWKV_ERR_SHAPE;
   if (n == 0) return RWKV_OK;
@@ -251,7 +257,13 @@ RWKV_API int rwkv_wkv6_forward(int64_t B, int64_t T, int64_t H, int64_t D, const
   if (!aligned16(r) || !aligned16(k) || !aligned16(v) || !aligned16(w) || !aligned16(u) ||
       !aligned16(o) || (s_in && !aligned16(s_in)) || (s_out && !aligned16(s_out)))
     return RWKV_ERR_ALIGN;
-  return hip_status(rwkv::wkv6_forward_launch(B, T, H, r, k, v, w, u, o, s_in, s_out, stream));
+  const size_t need = rwkv::wkv6_workspace_bytes(B, T, H);
+  if (need > 0) {
+    if (!ws || ws_bytes < need) return RWKV_ERR_WORKSPACE;
+    if (!aligned16(ws)) return RWKV_ERR_ALIGN;
+  }
+  return hip_status(
+      rwkv::wkv6_forward_launch(B, T, H, r, k, v, w, u, o, s_in, s_out, ws, stream));
 }
 
 RWKV_API int rwkv_wkv6_step(int64_t B, int64_t H, int64_t D, float* s, const uint16_t* r,

@@ -29,6 +29,10 @@
 #include "wkv_device.h"
 #include "wkv_internal.h"
 
+#include <stdlib.h>
+
+#include <algorithm>
+
 namespace rwkv {
 
 namespace {
@@ -42,7 +46,6 @@ constexpr float kMinLog2Decay = -126.f;  // log2 w below this counts as this (2^
 template <int DV>
 struct LdsF {
   __bf16 rr[kL][kPad];   // r, raw [tau][i]
-  __bf16 r0[kL][kPad];   // r 2^c_tau [tau][i]
   __bf16 kb[kL][kPad];   // k 2^(c_{block end} - c_{sigma+1}) [sigma][i]
   __bf16 kd[kL][kPad];   // k 2^(c_{block mid} - c_{sigma+1}), or raw k for exact diagonals
   __bf16 kh[kD][kPad];   // (k 2^(c_64 - c_{sigma+1}))^T [i][sigma]
@@ -78,8 +81,9 @@ __device__ __forceinline__ void load_w(ChunkW& x, int t0, int T, int H, int b, i
 
 // Exclusive prefix c[tau][i] of log2 w over the chunk's tokens.  Returns
 // whether some |log2 w| exceeds the fast diagonal's range (block-wide).
-template <int DV>
-__device__ __forceinline__ bool decay_prefix(const ChunkW& x, LdsF<DV>& s) {
+typedef float CTable[kL + 1][kCPad];
+
+__device__ __forceinline__ bool decay_prefix(const ChunkW& x, CTable& c) {
   const int tid = threadIdx.x;
   const int tau = tid >> 2, d0 = 16 * (tid & 3);
   const float wv[16] = {x.a.x, x.a.y, x.a.z, x.a.w, x.b.x, x.b.y, x.b.z, x.b.w,
@@ -89,9 +93,9 @@ __device__ __forceinline__ bool decay_prefix(const ChunkW& x, LdsF<DV>& s) {
   for (int e = 0; e < 16; ++e) {
     const float l2 = fmaxf(__log2f(wv[e]), kMinLog2Decay);
     fast_ok &= l2 >= -kMaxDiagLog2;
-    s.c[tau + 1][d0 + e] = l2;
+    c[tau + 1][d0 + e] = l2;
   }
-  if (tid < kD) s.c[0][tid] = 0.f;
+  if (tid < kD) c[0][tid] = 0.f;
   const bool exact = __syncthreads_or(!fast_ok) != 0;
   // per channel: four threads each take 16 rows, then add the totals of the
   // segments before theirs
@@ -99,16 +103,16 @@ __device__ __forceinline__ bool decay_prefix(const ChunkW& x, LdsF<DV>& s) {
   float run = 0.f;
 #pragma unroll
   for (int j = 1; j <= 16; ++j) {
-    run += s.c[16 * sg + j][ch];
-    s.c[16 * sg + j][ch] = run;
+    run += c[16 * sg + j][ch];
+    c[16 * sg + j][ch] = run;
   }
   __syncthreads();
   float off = 0.f;
-  for (int j = 0; j < sg; ++j) off += s.c[16 * j + 16][ch];
+  for (int j = 0; j < sg; ++j) off += c[16 * j + 16][ch];
   __syncthreads();
   if (sg > 0) {
 #pragma unroll
-    for (int j = 1; j <= 16; ++j) s.c[16 * sg + j][ch] += off;
+    for (int j = 1; j <= 16; ++j) c[16 * sg + j][ch] += off;
   }
   __syncthreads();
   return exact;
@@ -134,36 +138,31 @@ __device__ __forceinline__ void stage_chunk_f(const ChunkRegs& x, bool exact, Ld
   *reinterpret_cast<uint4*>(&s.rr[tau][d0]) = x.r0;
   *reinterpret_cast<uint4*>(&s.rr[tau][d0 + 8]) = x.r1;
   float bpart = 0.f;
-  bf16x8 r0a, r0b, kba, kbb, kda, kdb;
+  bf16x8 kba, kbb, kda, kdb;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const int i = d0 + e;
-    const float ct = s.c[tau][i], ct1 = s.c[tau + 1][i];
-    const float fr0 = exp2_fast(ct);
+    const float ct1 = s.c[tau + 1][i];
     const float fkb = exp2_fast(s.c[16 * blk + 16][i] - ct1);
     const float fkd = exp2_fast(s.c[16 * blk + 8][i] - ct1);
     const float fkh = exp2_fast(s.c[kL][i] - ct1);
-    const __bf16 vr0 = to_bf16(rv[e] * fr0), vkb = to_bf16(kv[e] * fkb);
+    const __bf16 vkb = to_bf16(kv[e] * fkb);
     const __bf16 vkd = exact ? to_bf16(kv[e]) : to_bf16(kv[e] * fkd);
     if (e < 8) {
-      r0a[e] = vr0;
       kba[e] = vkb;
       kda[e] = vkd;
     } else {
-      r0b[e - 8] = vr0;
       kbb[e - 8] = vkb;
       kdb[e - 8] = vkd;
     }
     s.kh[i][tau] = to_bf16(kv[e] * fkh);
     bpart = fmaf(rv[e] * s.u[i], kv[e], bpart);
   }
-  *reinterpret_cast<bf16x8*>(&s.r0[tau][d0]) = r0a;
-  *reinterpret_cast<bf16x8*>(&s.r0[tau][d0 + 8]) = r0b;
   *reinterpret_cast<bf16x8*>(&s.kb[tau][d0]) = kba;
   *reinterpret_cast<bf16x8*>(&s.kb[tau][d0 + 8]) = kbb;
   *reinterpret_cast<bf16x8*>(&s.kd[tau][d0]) = kda;
   *reinterpret_cast<bf16x8*>(&s.kd[tau][d0 + 8]) = kdb;
-  const uint32_t vw[4] = {x.v0.x, x.v0.y, x.v0.z, x.v0.w};
+  const uint32_t vw[8] = {x.v0.x, x.v0.y, x.v0.z, x.v0.w, x.v1.x, x.v1.y, x.v1.z, x.v1.w};
   constexpr int VPT = DV / 4;
 #pragma unroll
   for (int e = 0; e < VPT / 2; ++e) {
@@ -193,11 +192,14 @@ template <int DV>
 __global__ __launch_bounds__(256) void wkv6_fwd_chunked(
     int T, int H, int BH, const uint16_t* __restrict__ r, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ w,
-    const float* __restrict__ u, float* __restrict__ o, const float* s_in, float* s_out) {
+    const float* __restrict__ u, float* __restrict__ o, const float* s_in, float* s_out,
+    int seg_chunks, const float* __restrict__ seg_state) {
   constexpr int NS = kD / DV;
   constexpr int NJB = DV / 16;
   __shared__ LdsF<DV> s;
-  const int bx = blockIdx.x;
+  const int per_seg = (BH + 7) / 8 * 8 * NS;  // workgroups per time segment
+  const int seg = blockIdx.x / per_seg;
+  const int bx = blockIdx.x - seg * per_seg;
   const int bh = (bx / (8 * NS)) * 8 + (bx & 7);
   const int slice = (bx >> 3) % NS;
   if (bh >= BH) return;
@@ -220,6 +222,22 @@ __global__ __launch_bounds__(256) void wkv6_fwd_chunked(
     for (int rr = 0; rr < 4; ++rr)
       sacc[jb][rr] = s_in ? s_in[sbase + size_t(16 * q + crow + rr) * kD + j0 + 16 * jb + row]
                           : 0.f;
+  // A later segment starts from the earlier segments' local end states:
+  // S <- diag(2^L_seg) S + S_seg, L_seg the segment's summed log2 decay.
+  if (seg > 0) {
+    const int nseg = int(gridDim.x) / per_seg;
+    for (int sg = 0; sg < seg; ++sg) {
+      const float* src = seg_state + (size_t(bh) * (nseg - 1) + sg) * (kD * kD + kD);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int i = 16 * q + crow + rr;
+        const float d = exp2_fast(src[kD * kD + i]);
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb)
+          sacc[jb][rr] = fmaf(d, sacc[jb][rr], src[size_t(i) * kD + j0 + 16 * jb + row]);
+      }
+    }
+  }
   auto write_sp = [&]() {
     typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
@@ -233,16 +251,18 @@ __global__ __launch_bounds__(256) void wkv6_fwd_chunked(
   write_sp();
 
   const int n_chunks = (T + kL - 1) / kL;
+  const int c_begin = seg * seg_chunks;
+  const int c_end = min(n_chunks, c_begin + seg_chunks);
   ChunkRegs cur, nxt;
   ChunkW wc, wn;
-  load_chunk<DV>(cur, 0, T, H, b, h, j0, r, k, v);
-  load_w(wc, 0, T, H, b, h, w);
-  for (int c = 0; c < n_chunks; ++c) {
+  load_chunk<DV>(cur, c_begin * kL, T, H, b, h, j0, r, k, v);
+  load_w(wc, c_begin * kL, T, H, b, h, w);
+  for (int c = c_begin; c < c_end; ++c) {
     const int t0 = c * kL;
-    const bool exact = decay_prefix(wc, s);
+    const bool exact = decay_prefix(wc, s.c);
     stage_chunk_f(cur, exact, s);
     __syncthreads();
-    if (c + 1 < n_chunks) {
+    if (c + 1 < c_end) {
       load_chunk<DV>(nxt, t0 + kL, T, H, b, h, j0, r, k, v);
       load_w(wn, t0 + kL, T, H, b, h, w);
     }
@@ -316,7 +336,8 @@ __global__ __launch_bounds__(256) void wkv6_fwd_chunked(
       }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.r0[16 * q + row][32 * ks + kq]);
+      // r 2^c_tau (row 0 of the prefix table is zero)
+      const bf16x8 a = scaled_queries(s, 16 * q + row, 32 * ks + kq, 0);
 #pragma unroll
       for (int jb = 0; jb < NJB; ++jb) {
         const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s.sp[16 * jb + row][32 * ks + kq]);
@@ -354,7 +375,7 @@ __global__ __launch_bounds__(256) void wkv6_fwd_chunked(
     cur = nxt;
     wc = wn;
   }
-  if (s_out) {
+  if (s_out && c_end == n_chunks) {
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
@@ -363,17 +384,142 @@ __global__ __launch_bounds__(256) void wkv6_fwd_chunked(
   }
 }
 
+// Local end state of one time segment (all but the last) from a zero start,
+// and the segment's summed log2 decay per key channel, for one value slice:
+// seg_state[bh][seg] holds S[i][j] (64 x 64) then L[i] (64).
+template <int DV>
+__global__ __launch_bounds__(256) void wkv6_seg_state(int T, int H, int BH, int seg_chunks,
+                                                      int nseg, const uint16_t* __restrict__ k,
+                                                      const uint16_t* __restrict__ v,
+                                                      const float* __restrict__ w,
+                                                      float* __restrict__ seg_state) {
+  constexpr int NS = kD / DV;
+  constexpr int NJB = DV / 16;
+  __shared__ CTable s_c;
+  __shared__ __bf16 s_kh[kD][kPad];
+  __shared__ __bf16 s_vt[DV][kPad];
+  const int per_seg = (BH + 7) / 8 * 8 * NS;
+  const int seg = blockIdx.x / per_seg;
+  const int bx = blockIdx.x - seg * per_seg;
+  const int bh = (bx / (8 * NS)) * 8 + (bx & 7);
+  const int slice = (bx >> 3) % NS;
+  if (bh >= BH) return;
+  const int b = bh / H, h = bh - (bh / H) * H;
+  const int j0 = slice * DV;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int q = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row = lane & 15, kq = 8 * (lane >> 4), crow = 4 * (lane >> 4);
+  const int tau = tid >> 2, q4 = tid & 3, d0 = 16 * q4;
+  floatx4 sacc[NJB];
+#pragma unroll
+  for (int jb = 0; jb < NJB; ++jb) sacc[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float ltot = 0.f;  // thread tid < 64: channel tid
+  const int c_begin = seg * seg_chunks;
+  for (int c = c_begin; c < c_begin + seg_chunks; ++c) {
+    // every chunk here is whole: only the last segment reaches the end of T
+    ChunkRegs x;
+    ChunkW xw;
+    load_chunk<DV>(x, c * kL, T, H, b, h, j0, k, k, v);
+    load_w(xw, c * kL, T, H, b, h, w);
+    decay_prefix(xw, s_c);
+    const uint32_t kw[8] = {x.k0.x, x.k0.y, x.k0.z, x.k0.w, x.k1.x, x.k1.y, x.k1.z, x.k1.w};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int i = d0 + e;
+      const float kvv = (e & 1) ? hi_half(kw[e >> 1]) : lo_half(kw[e >> 1]);
+      s_kh[i][tau] = to_bf16(kvv * exp2_fast(s_c[kL][i] - s_c[tau + 1][i]));
+    }
+    const uint32_t vw[8] = {x.v0.x, x.v0.y, x.v0.z, x.v0.w, x.v1.x, x.v1.y, x.v1.z, x.v1.w};
+    constexpr int VPT = DV / 4;
+#pragma unroll
+    for (int e = 0; e < VPT / 2; ++e) {
+      s_vt[VPT * q4 + 2 * e][tau] = to_bf16(lo_half(vw[e]));
+      s_vt[VPT * q4 + 2 * e + 1][tau] = to_bf16(hi_half(vw[e]));
+    }
+    if (tid < kD) ltot += s_c[kL][tid];
+    __syncthreads();
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float dall = exp2_fast(s_c[kL][16 * q + crow + rr]);
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) sacc[jb][rr] *= dall;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s_kh[16 * q + row][32 * ks + kq]);
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) {
+        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s_vt[16 * jb + row][32 * ks + kq]);
+        sacc[jb] = mfma(a, bb, sacc[jb]);
+      }
+    }
+    __syncthreads();
+  }
+  float* dst = seg_state + (size_t(bh) * (nseg - 1) + seg) * (kD * kD + kD);
+#pragma unroll
+  for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      dst[size_t(16 * q + crow + rr) * kD + j0 + 16 * jb + row] = sacc[jb][rr];
+  if (slice == 0 && tid < kD) dst[kD * kD + tid] = ltot;
+}
+
+// Time segments per head (as for Eagle): about two workgroups per CU over the
+// launch, segments of at least four chunks; RWKV_WKV6_SEGS overrides.
+constexpr int64_t kTargetWorkgroups = 512;
+
+int wkv6_dv() {
+  if (const char* env = getenv("RWKV_WKV6_DV")) return atoi(env) == 32 ? 32 : 64;
+  return 64;
+}
+
+int wkv6_segments(int64_t BH, int64_t T, int ns) {
+  const int64_t n_chunks = (T + kL - 1) / kL;
+  const int64_t per_seg = (BH + 7) / 8 * 8 * ns;
+  int64_t nseg = (kTargetWorkgroups + per_seg - 1) / per_seg;
+  if (const char* env = getenv("RWKV_WKV6_SEGS")) nseg = atoi(env);
+  nseg = std::max<int64_t>(1, std::min<int64_t>(nseg, n_chunks / 4));
+  const int64_t seg_chunks = (n_chunks + nseg - 1) / nseg;
+  return int((n_chunks + seg_chunks - 1) / seg_chunks);
+}
+
+template <int DV>
+hipError_t launch_wkv6(int64_t T, int64_t H, int64_t BH, const uint16_t* r, const uint16_t* k,
+                       const uint16_t* v, const float* w, const float* u, float* o,
+                       const float* s_in, float* s_out, float* seg_state, hipStream_t stream) {
+  constexpr int NS = kD / DV;
+  const int nseg = wkv6_segments(BH, T, NS);
+  const int64_t n_chunks = (T + kL - 1) / kL;
+  const int seg_chunks = int((n_chunks + nseg - 1) / nseg);
+  const unsigned per_seg = unsigned((BH + 7) / 8 * 8 * NS);
+  if (nseg > 1) {
+    hipLaunchKernelGGL(wkv6_seg_state<DV>, dim3(per_seg * unsigned(nseg - 1)), dim3(256), 0,
+                       stream, int(T), int(H), int(BH), seg_chunks, nseg, k, v, w, seg_state);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(wkv6_fwd_chunked<DV>, dim3(per_seg * unsigned(nseg)), dim3(256), 0, stream,
+                     int(T), int(H), int(BH), r, k, v, w, u, o, s_in, s_out, seg_chunks,
+                     seg_state);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+size_t wkv6_workspace_bytes(int64_t B, int64_t T, int64_t H) {
+  const int nseg = wkv6_segments(B * H, T, kD / wkv6_dv());
+  return size_t(B * H) * size_t(nseg - 1) * (kD * kD + kD) * sizeof(float);
+}
 
 hipError_t wkv6_forward_launch(int64_t B, int64_t T, int64_t H, const uint16_t* r,
                                const uint16_t* k, const uint16_t* v, const float* w,
                                const float* u, float* o, const float* s_in, float* s_out,
-                               hipStream_t stream) {
-  const int64_t BH = B * H;
-  const unsigned grid = unsigned((BH + 7) / 8 * 8 * (kD / 32));
-  hipLaunchKernelGGL(wkv6_fwd_chunked<32>, dim3(grid), dim3(256), 0, stream, int(T), int(H),
-                     int(BH), r, k, v, w, u, o, s_in, s_out);
-  return hipGetLastError();
+                               void* ws, hipStream_t stream) {
+  float* seg_state = static_cast<float*>(ws);
+  if (wkv6_dv() == 32)
+    return launch_wkv6<32>(T, H, B * H, r, k, v, w, u, o, s_in, s_out, seg_state, stream);
+  return launch_wkv6<64>(T, H, B * H, r, k, v, w, u, o, s_in, s_out, seg_state, stream);
 }
 
 }  // namespace rwkv

@@ -93,10 +93,12 @@ hipError_t wkv5_step_launch(int64_t B, int64_t H, float* s, const uint16_t* r,
                             const float* u, float* o, hipStream_t stream);
 
 // ----- Finch (RWKV-6): per-token decay w [B, T, H, D] (step: [B, H, D]) -----
+size_t wkv6_workspace_bytes(int64_t B, int64_t T, int64_t H);
+
 hipError_t wkv6_forward_launch(int64_t B, int64_t T, int64_t H, const uint16_t* r,
                                const uint16_t* k, const uint16_t* v, const float* w,
                                const float* u, float* o, const float* s_in, float* s_out,
-                               hipStream_t stream);
+                               void* ws, hipStream_t stream);
 
 hipError_t wkv6_step_launch(int64_t B, int64_t H, float* s, const uint16_t* r,
                             const uint16_t* k, const uint16_t* v, const float* w,

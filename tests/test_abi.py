@@ -46,7 +46,7 @@ def test_header_declares_the_boundary():
         "rwkv_wkv4_backward_workspace", "rwkv_wkv4_backward",
         "rwkv_wkv4_state_init", "rwkv_wkv4_step", "rwkv_wkv5_forward_workspace",
         "rwkv_wkv5_forward", "rwkv_wkv5_forward_state", "rwkv_wkv5_step",
-        "rwkv_wkv6_forward", "rwkv_wkv6_step",
+        "rwkv_wkv6_forward_workspace", "rwkv_wkv6_forward", "rwkv_wkv6_step",
     ])
 
 
@@ -218,13 +218,17 @@ def test_wkv6_rejections(lib):
     f = lib.rwkv_wkv6_forward
     names = "r k v w u o s_in s_out".split()
     ptrs = lambda **kw: [kw.get(n, FAKE) for n in names]  # noqa: E731
-    assert f(0, 64, 2, 64, *[NULL] * 8, NULL) == OK
-    assert f(1, 64, 2, 32, *ptrs(), NULL) == UNSUPPORTED
-    assert f(1, -64, 2, 64, *ptrs(), NULL) == SHAPE
+    need = lib.rwkv_wkv6_forward_workspace(4, 4096, 32, 64)
+    assert need > 0 and lib.rwkv_wkv6_forward_workspace(4, 4096, 32, 32) == 0
+    assert f(0, 64, 2, 64, *[NULL] * 8, NULL, 0, NULL) == OK
+    assert f(1, 64, 2, 32, *ptrs(), NULL, 0, NULL) == UNSUPPORTED
+    assert f(1, -64, 2, 64, *ptrs(), NULL, 0, NULL) == SHAPE
     for n in names[:6]:
-        assert f(1, 64, 2, 64, *ptrs(**{n: NULL}), NULL) == NULLPTR, n
+        assert f(1, 64, 2, 64, *ptrs(**{n: NULL}), NULL, 0, NULL) == NULLPTR, n
     for n in names:
-        assert f(1, 64, 2, 64, *ptrs(**{n: MISALIGNED}), NULL) == ALIGN, n
+        assert f(1, 64, 2, 64, *ptrs(**{n: MISALIGNED}), NULL, 0, NULL) == ALIGN, n
+    assert f(4, 4096, 32, 64, *ptrs(), NULL, need, NULL) == WORKSPACE
+    assert f(4, 4096, 32, 64, *ptrs(), FAKE, need - 1, NULL) == WORKSPACE
     st = lib.rwkv_wkv6_step
     names = "s r k v w u o".split()
     ptrs = lambda **kw: [kw.get(n, FAKE) for n in names]  # noqa: E731

@@ -143,3 +143,36 @@ def test_steps_from_a_given_state():
     err_s = wkv5_scaled_err(s.cpu().numpy(), s_ref, s_abs)
     log(f"  err o={err_o:.3e} state={err_s:.3e}")
     assert err_o <= 1e-5 and err_s <= 1e-5
+
+
+@pytest.mark.parametrize("dv", ["64", "32"])
+@pytest.mark.parametrize("segs", [1, 2, 3, 4])
+def test_time_segments_and_slices(segs, dv):
+    """Split over time segments (local end states and summed log-decays folded
+    into later segments) and over value slices, with a starting state and the
+    handed-on state; one chunk of fast decays takes the exact diagonal path."""
+    import os
+    torch, dev = torch_dev()
+    e = synth.wkv6_inputs(2, 1000, 2, 64, seed=20 + segs, delta_std=1.0)
+    wt = e["wt"].copy()
+    wt[:, 300:340] = 1e-12
+    e = dict(e, wt=wt)
+    s0 = (np.random.default_rng(segs).standard_normal((2, 2, 64, 64)) * 0.3).astype(np.float32)
+    log(f"wkv6_forward segments={segs} value columns={dv}")
+    old = {n: os.environ.get(n) for n in ("RWKV_WKV6_SEGS", "RWKV_WKV6_DV")}
+    os.environ["RWKV_WKV6_SEGS"] = str(segs)
+    os.environ["RWKV_WKV6_DV"] = dv
+    try:
+        o, s1 = gpu_finch(e, s_in=to_dev(s0), s_out=True)
+    finally:
+        for n, val in old.items():
+            if val is None:
+                os.environ.pop(n, None)
+            else:
+                os.environ[n] = val
+    o_ref, s_ref = O.wkv6_recurrent(e["r"], e["k"], e["v"], e["wt"], e["u"], S0=s0)
+    o_abs, s_abs = O.wkv6_scale(e["r"], e["k"], e["v"], e["wt"], e["u"], S0=s0)
+    err_o = wkv5_scaled_err(o, o_ref, o_abs)
+    err_s = wkv5_scaled_err(s1, s_ref, s_abs)
+    log(f"  err o={err_o:.3e} state={err_s:.3e}")
+    assert err_o <= WKV5_TOL and err_s <= WKV5_TOL
