@@ -22,8 +22,36 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t x) {
 // float -> bf16, round to nearest even (finite inputs; NaN stays NaN).
 __device__ __forceinline__ __bf16 to_bf16(float x) { return static_cast<__bf16>(x); }
 
+// Chunks stream through buffer resources spanning one chunk's rows of a
+// [B, T, H, kD] tensor: a lane's offset within the chunk is computed once,
+// no 64-bit address arithmetic is spent per access, bytes past the last row
+// of the sequence read as zero and stores there are dropped by the hardware.
+// The span is at most 64 rows of H kD floats, below 2^31 bytes for
+// H < 2^17 (the callers reject larger H).  r, k, v and o are touched once:
+// non-temporal.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit access, gfx9 family
+constexpr int kNonTemporal = 0;
+
+// Resource over rows t0 .. t0 + n_tok - 1 of head h (element size `esz`).
+__device__ __forceinline__ Rsrc chunk_rsrc(const void* base, int t0, int T, int H, int b, int h,
+                                           int esz) {
+  const size_t e0 = ((size_t(b) * T + t0) * H + h) * kD;
+  const int n_tok = min(kL, T - t0);
+  const uint32_t bytes = uint32_t(((n_tok - 1) * H + 1) * kD * esz);
+  return __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(static_cast<const char*>(base)) + e0 * esz, 0, int(bytes), kRsrcWord3);
+}
+
+__device__ __forceinline__ uint4 load16(Rsrc rs, uint32_t voff) {
+  typedef int iv4 __attribute__((ext_vector_type(4)));
+  const iv4 t = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, kNonTemporal);
+  return uint4{uint32_t(t.x), uint32_t(t.y), uint32_t(t.z), uint32_t(t.w)};
+}
+
 // One chunk's raw inputs for this thread: token tau = tid/4, dims 16*(tid%4)
-// of r and k, and DV/4 value dims of this workgroup's slice (16, 8 or 4).
+// of r and k, and DV/4 value dims of this workgroup's slice (16, 8 or 4);
+// zeros past T.
 struct ChunkRegs {
   uint4 r0, r1, k0, k1, v0, v1;  // v1: the second half of 16 value dims (DV = 64)
 };
@@ -35,26 +63,26 @@ __device__ __forceinline__ void load_chunk(ChunkRegs& x, int t0, int T, int H, i
                                            const uint16_t* __restrict__ v) {
   const int tid = threadIdx.x;
   const int tau = tid >> 2, q4 = tid & 3;
-  if (t0 + tau < T) {
-    const size_t off = ((size_t(b) * T + t0 + tau) * H + h) * kD;
-    const uint4* rp = reinterpret_cast<const uint4*>(r + off + 16 * q4);
-    const uint4* kp = reinterpret_cast<const uint4*>(k + off + 16 * q4);
-    x.r0 = rp[0];
-    x.r1 = rp[1];
-    x.k0 = kp[0];
-    x.k1 = kp[1];
-    x.v1 = uint4{0u, 0u, 0u, 0u};
-    if constexpr (DV == 64) {
-      x.v0 = *reinterpret_cast<const uint4*>(v + off + 16 * q4);
-      x.v1 = *reinterpret_cast<const uint4*>(v + off + 16 * q4 + 8);
-    } else if constexpr (DV == 32) {
-      x.v0 = *reinterpret_cast<const uint4*>(v + off + j0 + 8 * q4);
-    } else {
-      const uint2 t = *reinterpret_cast<const uint2*>(v + off + j0 + 4 * q4);
-      x.v0 = uint4{t.x, t.y, 0u, 0u};
-    }
+  const uint32_t row = uint32_t(tau * H * kD);
+  const Rsrc rr = chunk_rsrc(r, t0, T, H, b, h, 2);
+  const Rsrc rk = chunk_rsrc(k, t0, T, H, b, h, 2);
+  const Rsrc rv = chunk_rsrc(v, t0, T, H, b, h, 2);
+  const uint32_t off = (row + 16 * q4) * 2;
+  x.r0 = load16(rr, off);
+  x.r1 = load16(rr, off + 16);
+  x.k0 = load16(rk, off);
+  x.k1 = load16(rk, off + 16);
+  x.v1 = uint4{0u, 0u, 0u, 0u};
+  if constexpr (DV == 64) {
+    x.v0 = load16(rv, off);
+    x.v1 = load16(rv, off + 16);
+  } else if constexpr (DV == 32) {
+    x.v0 = load16(rv, (row + j0 + 8 * q4) * 2);
   } else {
-    x.r0 = x.r1 = x.k0 = x.k1 = x.v0 = x.v1 = uint4{0u, 0u, 0u, 0u};
+    typedef int iv2 __attribute__((ext_vector_type(2)));
+    const iv2 t = __builtin_amdgcn_raw_buffer_load_b64(rv, (row + j0 + 4 * q4) * 2, 0,
+                                                       kNonTemporal);
+    x.v0 = uint4{uint32_t(t.x), uint32_t(t.y), 0u, 0u};
   }
 }
 

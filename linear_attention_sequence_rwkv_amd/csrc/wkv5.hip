@@ -12,13 +12,13 @@
 //         + sum_{sigma<tau} (sum_i r_tau[i] w_i^(tau-1-sigma) k_sigma[i]) v_sigma
 //         + (sum_i r_tau[i] u_i k_tau[i]) v_tau,
 //   S_next = diag(w^L) S + sum_sigma diag(w^(L-1-sigma)) k_sigma^T v_sigma.
-// With rt = r (.) w^(tau-32), kt = k (.) w^(31-sigma) and kh = k (.) w^(63-sigma)
-// (per element, a mid-chunk reference keeps both factors within
-// w^(+-32)), the chunk is four dense products on bf16 MFMA with fp32
-// accumulation:
+// With rt = r (.) w^(tau-32) and kt = k (.) w^(31-sigma) (per element, a
+// mid-chunk reference keeps both factors within w^(+-32)), the chunk is four
+// dense products on bf16 MFMA with fp32 accumulation:
 //   A  = strict_lower(rt kt^T) + diag(beta)         (64 x 64)
-//   O  = A V + rt (diag(w^32) S)                    (64 x 32 per workgroup)
-//   S' = diag(w^64) S + kh^T V                      (64 x 32, kept in fp32)
+//   O  = A V + rt (diag(w^32) S)                    (64 x DV per workgroup)
+//   S' = diag(w^32) (diag(w^32) S + kt^T V)         (64 x DV, kept in fp32)
+// since w^(63-sigma) = w^32 w^(31-sigma).
 // The factorisation needs w^(-32) and w^(31) inside bf16/fp32 range, i.e.
 // |log2 w| <= 3.6 for every channel of the head; a head outside that range
 // runs the exact fp32 recurrence instead (one branch per workgroup).
@@ -40,15 +40,14 @@ using namespace eagle;
 constexpr float kMaxLog2Decay = 3.6f;
 
 template <int DV>
-struct Lds {
+struct alignas(16) Lds {
   __bf16 rt[kL][kPad];    // rt[tau][i]
   __bf16 kt[kL][kPad];    // kt[sigma][i]
-  __bf16 kh[kD][kPad];    // kh^T[i][sigma]
+  __bf16 ktt[kD][kPad];   // kt^T[i][sigma]
   __bf16 vt[DV][kPad];    // v^T[j][sigma]
   __bf16 sp[DV][kPad];    // (diag(w^32) S)^T[j][i]
   float l2w[kD];          // log2 w_i
   float w32[kD];          // w_i^32
-  float w64[kD];          // w_i^64
   float scratch[4][kD];   // the exact recurrence's per-token vectors
   float beta[kL];
   float u[kD];
@@ -113,8 +112,6 @@ __device__ void eagle_recurrent_slice(int T, int H, int b, int h, int j0,
 struct StageConsts {
   float fr[16];  // w^(tau-32)
   float fk[16];  // w^(31-tau)
-  float fh[16];  // w^(63-tau)
-  float ur[16];  // u
 };
 
 template <int DV>
@@ -126,17 +123,14 @@ __device__ __forceinline__ void stage_consts(StageConsts& c, const Lds<DV>& s) {
     const float l2 = s.l2w[d0 + e];
     c.fr[e] = exp2f(float(tau - 32) * l2);
     c.fk[e] = exp2f(float(31 - tau) * l2);
-    c.fh[e] = exp2f(float(63 - tau) * l2);
-    c.ur[e] = s.u[d0 + e];
   }
 }
 
-// Scale one chunk into LDS: rt, kt, kh^T, v^T, beta.
-// `n_last` > 0 marks a final chunk of n_last < kL tokens whose state update
-// must decay from its own end: kh = k w^(n_last-1-sigma) (else w^(63-sigma)).
+// Scale one chunk into LDS: rt, kt, kt^T, v^T, beta.  Tokens past T were
+// loaded as zeros, so they add nothing to any product.
 template <int DV>
 __device__ __forceinline__ void stage_chunk(const ChunkRegs& x, const StageConsts& f,
-                                            Lds<DV>& s, int n_last = 0) {
+                                            Lds<DV>& s) {
   const int tid = threadIdx.x;
   const int tau = tid >> 2, q4 = tid & 3;
   const int d0 = 16 * q4;
@@ -159,32 +153,25 @@ __device__ __forceinline__ void stage_chunk(const ChunkRegs& x, const StageConst
     kt0[e] = to_bf16(kv[e] * f.fk[e]);
     kt1[e] = to_bf16(kv[8 + e] * f.fk[8 + e]);
   }
-  if (n_last > 0) {
-    // rare: once per call, only when the final state is wanted
-    const float back = float(max(n_last - 1 - tau, 0));
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float dh = exp2f(back * s.l2w[d0 + e]);
-      s.kh[d0 + e][tau] = to_bf16(tau < n_last ? kv[e] * dh : 0.f);
-      bpart = fmaf(rv[e] * f.ur[e], kv[e], bpart);
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      s.kh[d0 + e][tau] = to_bf16(kv[e] * f.fh[e]);
-      bpart = fmaf(rv[e] * f.ur[e], kv[e], bpart);
-    }
-  }
+  for (int e = 0; e < 16; ++e) bpart = fmaf(rv[e] * s.u[d0 + e], kv[e], bpart);
   *reinterpret_cast<bf16x8*>(&s.rt[tau][d0]) = rt0;
   *reinterpret_cast<bf16x8*>(&s.rt[tau][d0 + 8]) = rt1;
   *reinterpret_cast<bf16x8*>(&s.kt[tau][d0]) = kt0;
   *reinterpret_cast<bf16x8*>(&s.kt[tau][d0 + 8]) = kt1;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    s.ktt[d0 + e][tau] = kt0[e];
+    s.ktt[d0 + 8 + e][tau] = kt1[e];
+  }
   const uint32_t vw[8] = {x.v0.x, x.v0.y, x.v0.z, x.v0.w, x.v1.x, x.v1.y, x.v1.z, x.v1.w};
   constexpr int VPT = DV / 4;  // value dims per thread
+  // v is already bf16: its halves go to v^T as they are
+  uint16_t(*vt)[kPad] = reinterpret_cast<uint16_t(*)[kPad]>(&s.vt[0][0]);
 #pragma unroll
   for (int e = 0; e < VPT / 2; ++e) {
-    s.vt[VPT * q4 + 2 * e][tau] = to_bf16(lo_half(vw[e]));
-    s.vt[VPT * q4 + 2 * e + 1][tau] = to_bf16(hi_half(vw[e]));
+    vt[VPT * q4 + 2 * e][tau] = uint16_t(vw[e]);
+    vt[VPT * q4 + 2 * e + 1][tau] = uint16_t(vw[e] >> 16);
   }
   // the four threads of a token sit in adjacent lanes of one wave
   bpart += __shfl_xor(bpart, 1);
@@ -196,7 +183,7 @@ __device__ __forceinline__ void stage_chunk(const ChunkRegs& x, const StageConst
 // places the 64/DV slices of a head 8 apart, so that they land on the same
 // XCD (dispatch is round-robin over 8 XCDs) and share r, k reads in its L2.
 template <int DV>
-__global__ __launch_bounds__(256) void wkv5_fwd_chunked(
+__global__ __launch_bounds__(256, 2) void wkv5_fwd_chunked(
     int T, int H, int BH, const uint16_t* __restrict__ r, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ w,
     const float* __restrict__ u, float* __restrict__ o, const float* s_in, float* s_out,
@@ -226,7 +213,6 @@ __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
     const float l2w = __log2f(wi);
     s.l2w[tid] = l2w;
     s.w32[tid] = exp2f(32.f * l2w);
-    s.w64[tid] = exp2f(64.f * l2w);
     if (!(fabsf(l2w) <= kMaxLog2Decay)) atomicOr(&s.fallback, 1);  // also catches NaN, w<=0
   }
   __syncthreads();
@@ -288,28 +274,34 @@ __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
   const int n_chunks = (T + kL - 1) / kL;
   const int c_begin = seg * seg_chunks;
   const int c_end = min(n_chunks, c_begin + seg_chunks);
+  // o offsets of this lane within a chunk: tokens 16 q + crow + rr
+  uint32_t ooff[4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr)
+    ooff[rr] = uint32_t(((16 * q + crow + rr) * H * kD + j0 + row) * 4);
   ChunkRegs cur, nxt;
   load_chunk<DV>(cur, c_begin * kL, T, H, b, h, j0, r, k, v);
   for (int c = c_begin; c < c_end; ++c) {
     const int t0 = c * kL;
     const int n_last = (s_out && c == n_chunks - 1 && T - t0 < kL) ? T - t0 : 0;
-    stage_chunk(cur, f, s, n_last);
+    stage_chunk(cur, f, s);
     __syncthreads();
     if (c + 1 < c_end) load_chunk<DV>(nxt, t0 + kL, T, H, b, h, j0, r, k, v);
 
-    // A^T = kt rt^T for sigma blocks 0..q against this wave's 16 tokens:
-    // lane holds column tau = 16q + row, rows sigma = 16nb + crow .. +3.
+    // A^T = kt rt^T for all four sigma blocks against this wave's 16 tokens
+    // (blocks after the wave's own are masked to zero below; computing them
+    // costs a few MFMAs but no branches): lane holds column tau = 16q + row,
+    // rows sigma = 16nb + crow .. +3.
     floatx4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
                       {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s.rt[16 * q + row][32 * ks + kq]);
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        if (nb <= q) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.kt[16 * nb + row][32 * ks + kq]);
-          acc[nb] = mfma(a, bb, acc[nb]);
-        }
+      for (int nb = 0; nb < 4; ++nb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.kt[16 * nb + row][32 * ks + kq]);
+        acc[nb] = mfma(a, bb, acc[nb]);
+      }
     }
     // Causal mask and the bonus on the diagonal, in registers.  The pair of
     // sigma tiles (2ks, 2ks+1) held by a lane is directly an A operand of a
@@ -323,8 +315,7 @@ __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int sig = 16 * nb + crow + rr;
-        float val = 0.f;
-        if (nb <= q) val = sig < tau_l ? acc[nb][rr] : (sig == tau_l ? beta : 0.f);
+        const float val = sig < tau_l ? acc[nb][rr] : (sig == tau_l ? beta : 0.f);
         ap[nb >> 1][(nb & 1) * 4 + rr] = to_bf16(val);
       }
 
@@ -332,20 +323,18 @@ __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
     floatx4 oacc[NJB];
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) oacc[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const int nks = (q + 2) >> 1;  // 32-wide sigma steps that can be non-zero
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      if (ks < nks) {
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-        for (int jb = 0; jb < NJB; ++jb) {
-          const __bf16* vr = &s.vt[16 * jb + row][32 * ks + crow];
-          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 16);
-          const bf16x8 bb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          oacc[jb] = mfma(ap[ks], bb, oacc[jb]);
-        }
+      for (int jb = 0; jb < NJB; ++jb) {
+        const __bf16* vr = &s.vt[16 * jb + row][32 * ks + crow];
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 16);
+        const bf16x8 bb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        oacc[jb] = mfma(ap[ks], bb, oacc[jb]);
       }
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.rt[16 * q + row][32 * ks + kq]);
@@ -355,34 +344,42 @@ __global__ __launch_bounds__(256) void wkv5_fwd_chunked(
         oacc[jb] = mfma(a, bb, oacc[jb]);
       }
     }
+    {
+      const Rsrc ro = chunk_rsrc(o, t0, T, H, b, h, 4);  // rows past T are dropped
 #pragma unroll
-    for (int jb = 0; jb < NJB; ++jb)
+      for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int tau = 16 * q + crow + rr;
-        if (t0 + tau < T)
-          o[((size_t(b) * T + t0 + tau) * H + h) * kD + j0 + 16 * jb + row] = oacc[jb][rr];
-      }
+        for (int rr = 0; rr < 4; ++rr)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(oacc[jb][rr]), ro, ooff[rr],
+                                                64 * jb, kNonTemporal);
+    }
 
-    // S <- diag(w^64) S + kh^T V for key rows 16q..16q+15 (a ragged final
-    // chunk decays by w^n_last).
+    // S <- diag(w^32) (diag(w^32) S + kt^T V) for key rows 16q..16q+15.  A
+    // ragged final chunk of n tokens ends with diag(w^(n-32)) instead, which
+    // decays S by w^n and token sigma by w^(n-1-sigma).
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const int i = 16 * q + crow + rr;
-      const float d64 = n_last > 0 ? exp2f(float(n_last) * s.l2w[i]) : s.w64[i];
+      const float w32 = s.w32[16 * q + crow + rr];
 #pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) sacc[jb][rr] *= d64;
+      for (int jb = 0; jb < NJB; ++jb) sacc[jb][rr] *= w32;
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.kh[16 * q + row][32 * ks + kq]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.ktt[16 * q + row][32 * ks + kq]);
 #pragma unroll
       for (int jb = 0; jb < NJB; ++jb) {
         const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s.vt[16 * jb + row][32 * ks + kq]);
         sacc[jb] = mfma(a, bb, sacc[jb]);
       }
     }
-    __syncthreads();  // every wave is done with rt, kt, kh, vt, sp of this chunk
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int i = 16 * q + crow + rr;
+      const float post = n_last > 0 ? exp2f(float(n_last - 32) * s.l2w[i]) : s.w32[i];
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) sacc[jb][rr] *= post;
+    }
+    __syncthreads();  // every wave is done with rt, kt, kt^T, vt, sp of this chunk
 
     write_sp();  // S' for the next chunk
     cur = nxt;
@@ -407,8 +404,8 @@ __global__ __launch_bounds__(256) void wkv5_seg_state(int T, int H, int BH, int 
                                                       float* __restrict__ seg_state) {
   constexpr int NS = kD / DV;
   constexpr int NJB = DV / 16;
-  __shared__ __bf16 s_kh[kD][kPad];
-  __shared__ __bf16 s_vt[DV][kPad];
+  __shared__ __attribute__((aligned(16))) __bf16 s_kh[kD][kPad];
+  __shared__ __attribute__((aligned(16))) __bf16 s_vt[DV][kPad];
   __shared__ float s_l2w[kD];
   __shared__ float s_w64[kD];
   __shared__ int s_fallback;

@@ -44,7 +44,7 @@ constexpr float kMaxDiagLog2 = 15.f;     // fast diagonal blocks need every |log
 constexpr float kMinLog2Decay = -126.f;  // log2 w below this counts as this (2^-126: no memory)
 
 template <int DV>
-struct LdsF {
+struct alignas(16) LdsF {
   __bf16 rr[kL][kPad];   // r, raw [tau][i]
   __bf16 kb[kL][kPad];   // k 2^(c_{block end} - c_{sigma+1}) [sigma][i]
   __bf16 kd[kL][kPad];   // k 2^(c_{block mid} - c_{sigma+1}), or raw k for exact diagonals
@@ -396,8 +396,8 @@ __global__ __launch_bounds__(256) void wkv6_seg_state(int T, int H, int BH, int 
   constexpr int NS = kD / DV;
   constexpr int NJB = DV / 16;
   __shared__ CTable s_c;
-  __shared__ __bf16 s_kh[kD][kPad];
-  __shared__ __bf16 s_vt[DV][kPad];
+  __shared__ __attribute__((aligned(16))) __bf16 s_kh[kD][kPad];
+  __shared__ __attribute__((aligned(16))) __bf16 s_vt[DV][kPad];
   const int per_seg = (BH + 7) / 8 * 8 * NS;
   const int seg = blockIdx.x / per_seg;
   const int bx = blockIdx.x - seg * per_seg;
