@@ -56,7 +56,8 @@ struct ChunkRegs {
   uint4 r0, r1, k0, k1, v0, v1;  // v1: the second half of 16 value dims (DV = 64)
 };
 
-template <int DV>
+// WITH_R = false (segment states) skips r.
+template <int DV, bool WITH_R = true>
 __device__ __forceinline__ void load_chunk(ChunkRegs& x, int t0, int T, int H, int b, int h,
                                            int j0, const uint16_t* __restrict__ r,
                                            const uint16_t* __restrict__ k,
@@ -64,12 +65,16 @@ __device__ __forceinline__ void load_chunk(ChunkRegs& x, int t0, int T, int H, i
   const int tid = threadIdx.x;
   const int tau = tid >> 2, q4 = tid & 3;
   const uint32_t row = uint32_t(tau * H * kD);
-  const Rsrc rr = chunk_rsrc(r, t0, T, H, b, h, 2);
   const Rsrc rk = chunk_rsrc(k, t0, T, H, b, h, 2);
   const Rsrc rv = chunk_rsrc(v, t0, T, H, b, h, 2);
   const uint32_t off = (row + 16 * q4) * 2;
-  x.r0 = load16(rr, off);
-  x.r1 = load16(rr, off + 16);
+  if constexpr (WITH_R) {
+    const Rsrc rr = chunk_rsrc(r, t0, T, H, b, h, 2);
+    x.r0 = load16(rr, off);
+    x.r1 = load16(rr, off + 16);
+  } else {
+    x.r0 = x.r1 = uint4{0u, 0u, 0u, 0u};
+  }
   x.k0 = load16(rk, off);
   x.k1 = load16(rk, off + 16);
   x.v1 = uint4{0u, 0u, 0u, 0u};
@@ -88,6 +93,34 @@ __device__ __forceinline__ void load_chunk(ChunkRegs& x, int t0, int T, int H, i
 
 __device__ __forceinline__ float lo_half(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float hi_half(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// MFMA operands of a product summed over tokens (K = sigma), read from a
+// row-major [sigma][column] tile with gfx950's LDS transpose load: within each
+// 16-lane group, lane r addresses 4 elements of row k0 + r/4, columns
+// c0 + 4 (r % 4) .. + 3, and lane i receives column c0 + i of rows k0 .. k0 + 3
+// (lane layout confirmed by an in-bounds probe).  Two such loads give an
+// 8-element operand; K is ordered per 16-lane group g as sigma =
+// s0 + 4g + 0..3, then s0 + 16 + 4g + 0..3, which is the order of the masked
+// score tiles held in registers (the accumulator rows of two 16-token
+// blocks), so every product over sigma uses it.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ v4i16 lds_read_tr(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(const_cast<__bf16*>(p)));
+}
+
+// Operand for tokens s0 .. s0 + 31 (in the order above) and columns
+// c0 .. c0 + 15 of a [sigma][kPad] tile.
+__device__ __forceinline__ bf16x8 sigma_operand(const __bf16 (*tile)[kPad], int s0, int c0,
+                                                int lane) {
+  const int g = lane >> 4, r = lane & 15;
+  const __bf16* p = &tile[s0 + 4 * g + (r >> 2)][c0 + 4 * (r & 3)];
+  const v4i16 lo = lds_read_tr(p);
+  const v4i16 hi = lds_read_tr(p + 16 * kPad);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 
 __device__ __forceinline__ floatx4 mfma(const bf16x8& a, const bf16x8& b, const floatx4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

@@ -43,8 +43,7 @@ template <int DV>
 struct alignas(16) Lds {
   __bf16 rt[kL][kPad];    // rt[tau][i]
   __bf16 kt[kL][kPad];    // kt[sigma][i]
-  __bf16 ktt[kD][kPad];   // kt^T[i][sigma]
-  __bf16 vt[DV][kPad];    // v^T[j][sigma]
+  __bf16 v[kL][kPad];     // v[sigma][j], DV columns
   __bf16 sp[DV][kPad];    // (diag(w^32) S)^T[j][i]
   float l2w[kD];          // log2 w_i
   float w32[kD];          // w_i^32
@@ -126,8 +125,9 @@ __device__ __forceinline__ void stage_consts(StageConsts& c, const Lds<DV>& s) {
   }
 }
 
-// Scale one chunk into LDS: rt, kt, kt^T, v^T, beta.  Tokens past T were
-// loaded as zeros, so they add nothing to any product.
+// Scale one chunk into LDS: rt, kt, v (all row-major: products over sigma
+// read them with the transpose load) and beta.  Tokens past T were loaded as
+// zeros, so they add nothing to any product.
 template <int DV>
 __device__ __forceinline__ void stage_chunk(const ChunkRegs& x, const StageConsts& f,
                                             Lds<DV>& s) {
@@ -159,19 +159,14 @@ __device__ __forceinline__ void stage_chunk(const ChunkRegs& x, const StageConst
   *reinterpret_cast<bf16x8*>(&s.rt[tau][d0 + 8]) = rt1;
   *reinterpret_cast<bf16x8*>(&s.kt[tau][d0]) = kt0;
   *reinterpret_cast<bf16x8*>(&s.kt[tau][d0 + 8]) = kt1;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    s.ktt[d0 + e][tau] = kt0[e];
-    s.ktt[d0 + 8 + e][tau] = kt1[e];
-  }
-  const uint32_t vw[8] = {x.v0.x, x.v0.y, x.v0.z, x.v0.w, x.v1.x, x.v1.y, x.v1.z, x.v1.w};
-  constexpr int VPT = DV / 4;  // value dims per thread
-  // v is already bf16: its halves go to v^T as they are
-  uint16_t(*vt)[kPad] = reinterpret_cast<uint16_t(*)[kPad]>(&s.vt[0][0]);
-#pragma unroll
-  for (int e = 0; e < VPT / 2; ++e) {
-    vt[VPT * q4 + 2 * e][tau] = uint16_t(vw[e]);
-    vt[VPT * q4 + 2 * e + 1][tau] = uint16_t(vw[e] >> 16);
+  // v is already bf16: DV / 4 value dims of this token go in as loaded
+  if constexpr (DV == 64) {
+    *reinterpret_cast<uint4*>(&s.v[tau][16 * q4]) = x.v0;
+    *reinterpret_cast<uint4*>(&s.v[tau][16 * q4 + 8]) = x.v1;
+  } else if constexpr (DV == 32) {
+    *reinterpret_cast<uint4*>(&s.v[tau][8 * q4]) = x.v0;
+  } else {
+    *reinterpret_cast<uint2*>(&s.v[tau][4 * q4]) = uint2{x.v0.x, x.v0.y};
   }
   // the four threads of a token sit in adjacent lanes of one wave
   bpart += __shfl_xor(bpart, 1);
@@ -306,7 +301,7 @@ __global__ __launch_bounds__(256, 2) void wkv5_fwd_chunked(
     // Causal mask and the bonus on the diagonal, in registers.  The pair of
     // sigma tiles (2ks, 2ks+1) held by a lane is directly an A operand of a
     // 32-wide K step, with K ordered as sigma = 32ks + crow + 0..3, then
-    // 32ks + 16 + crow + 0..3; V below is read in the same order.
+    // 32ks + 16 + crow + 0..3: the order of sigma_operand.
     const int tau_l = 16 * q + row;
     const float beta = s.beta[tau_l];
     bf16x8 ap[2];
@@ -319,20 +314,28 @@ __global__ __launch_bounds__(256, 2) void wkv5_fwd_chunked(
         ap[nb >> 1][(nb & 1) * 4 + rr] = to_bf16(val);
       }
 
-    // O = A' V + rt S'  (16 tokens x DV value columns per wave).
+    // O = A' V + rt S' (16 tokens x DV value columns per wave) and
+    // S <- diag(w^32) (diag(w^32) S + kt^T V) for key rows 16q..16q+15: the
+    // two products over sigma share their V operands.  A ragged final chunk
+    // of n tokens ends with diag(w^(n-32)) instead, which decays S by w^n and
+    // token sigma by w^(n-1-sigma).
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float w32 = s.w32[16 * q + crow + rr];
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) sacc[jb][rr] *= w32;
+    }
     floatx4 oacc[NJB];
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) oacc[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 kop = sigma_operand(s.kt, 32 * ks, 16 * q, lane);
 #pragma unroll
       for (int jb = 0; jb < NJB; ++jb) {
-        const __bf16* vr = &s.vt[16 * jb + row][32 * ks + crow];
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 16);
-        const bf16x8 bb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        oacc[jb] = mfma(ap[ks], bb, oacc[jb]);
+        const bf16x8 vop = sigma_operand(s.v, 32 * ks, 16 * jb, lane);
+        oacc[jb] = mfma(ap[ks], vop, oacc[jb]);
+        sacc[jb] = mfma(kop, vop, sacc[jb]);
       }
     }
 #pragma unroll
@@ -353,25 +356,6 @@ __global__ __launch_bounds__(256, 2) void wkv5_fwd_chunked(
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(oacc[jb][rr]), ro, ooff[rr],
                                                 64 * jb, kNonTemporal);
     }
-
-    // S <- diag(w^32) (diag(w^32) S + kt^T V) for key rows 16q..16q+15.  A
-    // ragged final chunk of n tokens ends with diag(w^(n-32)) instead, which
-    // decays S by w^n and token sigma by w^(n-1-sigma).
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const float w32 = s.w32[16 * q + crow + rr];
-#pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) sacc[jb][rr] *= w32;
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.ktt[16 * q + row][32 * ks + kq]);
-#pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) {
-        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s.vt[16 * jb + row][32 * ks + kq]);
-        sacc[jb] = mfma(a, bb, sacc[jb]);
-      }
-    }
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int i = 16 * q + crow + rr;
@@ -379,7 +363,7 @@ __global__ __launch_bounds__(256, 2) void wkv5_fwd_chunked(
 #pragma unroll
       for (int jb = 0; jb < NJB; ++jb) sacc[jb][rr] *= post;
     }
-    __syncthreads();  // every wave is done with rt, kt, kt^T, vt, sp of this chunk
+    __syncthreads();  // every wave is done with rt, kt, v, sp of this chunk
 
     write_sp();  // S' for the next chunk
     cur = nxt;
@@ -394,8 +378,10 @@ __global__ __launch_bounds__(256, 2) void wkv5_fwd_chunked(
 }
 
 // Local end state of one time segment (all but the last), from a zero
-// start: S <- w^64 S + kh^T V over its chunks, for one value slice.  Written
-// to seg_state[bh][seg] as [key i][value j].
+// start, over its chunks: S <- diag(w^32) (diag(w^32) S + kt^T V) as in the
+// forward (kt = k w^(31-sigma)), for one value slice; the next chunk's k, v
+// load while this one multiplies.  Written to seg_state[bh][seg] as
+// [key i][value j].
 template <int DV>
 __global__ __launch_bounds__(256) void wkv5_seg_state(int T, int H, int BH, int seg_chunks,
                                                       int nseg, const uint16_t* __restrict__ k,
@@ -404,10 +390,10 @@ __global__ __launch_bounds__(256) void wkv5_seg_state(int T, int H, int BH, int 
                                                       float* __restrict__ seg_state) {
   constexpr int NS = kD / DV;
   constexpr int NJB = DV / 16;
-  __shared__ __attribute__((aligned(16))) __bf16 s_kh[kD][kPad];
-  __shared__ __attribute__((aligned(16))) __bf16 s_vt[DV][kPad];
+  __shared__ __attribute__((aligned(16))) __bf16 s_kt[kL][kPad];
+  __shared__ __attribute__((aligned(16))) __bf16 s_v[kL][kPad];
   __shared__ float s_l2w[kD];
-  __shared__ float s_w64[kD];
+  __shared__ float s_w32[kD];
   __shared__ int s_fallback;
   const int per_seg = (BH + 7) / 8 * 8 * NS;
   const int seg = blockIdx.x / per_seg;
@@ -420,70 +406,71 @@ __global__ __launch_bounds__(256) void wkv5_seg_state(int T, int H, int BH, int 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int q = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int row = lane & 15, kq = 8 * (lane >> 4), crow = 4 * (lane >> 4);
+  const int row = lane & 15, crow = 4 * (lane >> 4);
   if (tid == 0) s_fallback = 0;
   __syncthreads();
   if (tid < kD) {
     const float l2w = __log2f(w[h * kD + tid]);
     s_l2w[tid] = l2w;
-    s_w64[tid] = exp2f(64.f * l2w);
+    s_w32[tid] = exp2f(32.f * l2w);
     if (!(fabsf(l2w) <= kMaxLog2Decay)) atomicOr(&s_fallback, 1);
   }
   __syncthreads();
   if (s_fallback) return;  // that head runs the exact recurrence in one piece
   const int tau = tid >> 2, q4 = tid & 3, d0 = 16 * q4;
-  float fh[16];
+  float fk[16];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) fh[e] = exp2f(float(63 - tau) * s_l2w[d0 + e]);
+  for (int e = 0; e < 16; ++e) fk[e] = exp2f(float(31 - tau) * s_l2w[d0 + e]);
+  float w32[4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) w32[rr] = s_w32[16 * q + crow + rr];
   floatx4 sacc[NJB];
 #pragma unroll
   for (int jb = 0; jb < NJB; ++jb) sacc[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
   const int c_begin = seg * seg_chunks;
-  for (int c = c_begin; c < c_begin + seg_chunks; ++c) {
-    // every chunk here is whole: only the last segment reaches the end of T
-    const size_t off = ((size_t(b) * T + size_t(c) * kL + tau) * H + h) * kD;
-    const uint4* kp = reinterpret_cast<const uint4*>(k + off + d0);
-    const uint4 k0 = kp[0], k1 = kp[1];
-    uint4 v0, v1 = uint4{0u, 0u, 0u, 0u};
+  const int c_end = c_begin + seg_chunks;  // every chunk here is whole
+  ChunkRegs cur, nxt;
+  load_chunk<DV, false>(cur, c_begin * kL, T, H, b, h, j0, nullptr, k, v);
+  for (int c = c_begin; c < c_end; ++c) {
+    const uint32_t kw[8] = {cur.k0.x, cur.k0.y, cur.k0.z, cur.k0.w,
+                            cur.k1.x, cur.k1.y, cur.k1.z, cur.k1.w};
+    bf16x8 kt0, kt1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      kt0[2 * e] = to_bf16(lo_half(kw[e]) * fk[2 * e]);
+      kt0[2 * e + 1] = to_bf16(hi_half(kw[e]) * fk[2 * e + 1]);
+      kt1[2 * e] = to_bf16(lo_half(kw[4 + e]) * fk[8 + 2 * e]);
+      kt1[2 * e + 1] = to_bf16(hi_half(kw[4 + e]) * fk[8 + 2 * e + 1]);
+    }
+    *reinterpret_cast<bf16x8*>(&s_kt[tau][d0]) = kt0;
+    *reinterpret_cast<bf16x8*>(&s_kt[tau][d0 + 8]) = kt1;
     if constexpr (DV == 64) {
-      v0 = *reinterpret_cast<const uint4*>(v + off + 16 * q4);
-      v1 = *reinterpret_cast<const uint4*>(v + off + 16 * q4 + 8);
+      *reinterpret_cast<uint4*>(&s_v[tau][16 * q4]) = cur.v0;
+      *reinterpret_cast<uint4*>(&s_v[tau][16 * q4 + 8]) = cur.v1;
     } else if constexpr (DV == 32) {
-      v0 = *reinterpret_cast<const uint4*>(v + off + j0 + 8 * q4);
+      *reinterpret_cast<uint4*>(&s_v[tau][8 * q4]) = cur.v0;
     } else {
-      const uint2 t2 = *reinterpret_cast<const uint2*>(v + off + j0 + 4 * q4);
-      v0 = uint4{t2.x, t2.y, 0u, 0u};
-    }
-    const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      s_kh[d0 + 2 * e][tau] = to_bf16(lo_half(kw[e]) * fh[2 * e]);
-      s_kh[d0 + 2 * e + 1][tau] = to_bf16(hi_half(kw[e]) * fh[2 * e + 1]);
-    }
-    const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    constexpr int VPT = DV / 4;
-#pragma unroll
-    for (int e = 0; e < VPT / 2; ++e) {
-      s_vt[VPT * q4 + 2 * e][tau] = to_bf16(lo_half(vw[e]));
-      s_vt[VPT * q4 + 2 * e + 1][tau] = to_bf16(hi_half(vw[e]));
+      *reinterpret_cast<uint2*>(&s_v[tau][4 * q4]) = uint2{cur.v0.x, cur.v0.y};
     }
     __syncthreads();
+    if (c + 1 < c_end) load_chunk<DV, false>(nxt, (c + 1) * kL, T, H, b, h, j0, nullptr, k, v);
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const float d64 = s_w64[16 * q + crow + rr];
+    for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) sacc[jb][rr] *= d64;
-    }
+      for (int jb = 0; jb < NJB; ++jb) sacc[jb][rr] *= w32[rr];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s_kh[16 * q + row][32 * ks + kq]);
+      const bf16x8 kop = sigma_operand(s_kt, 32 * ks, 16 * q, lane);
 #pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) {
-        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s_vt[16 * jb + row][32 * ks + kq]);
-        sacc[jb] = mfma(a, bb, sacc[jb]);
-      }
+      for (int jb = 0; jb < NJB; ++jb)
+        sacc[jb] = mfma(kop, sigma_operand(s_v, 32 * ks, 16 * jb, lane), sacc[jb]);
     }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) sacc[jb][rr] *= w32[rr];
     __syncthreads();
+    cur = nxt;
   }
   float* dst = seg_state + (size_t(bh) * (nseg - 1) + seg) * kD * kD;
 #pragma unroll
