@@ -48,8 +48,8 @@ struct alignas(16) LdsF {
   __bf16 rr[kL][kPad];   // r, raw [tau][i]
   __bf16 kb[kL][kPad];   // k 2^(c_{block end} - c_{sigma+1}) [sigma][i]
   __bf16 kd[kL][kPad];   // k 2^(c_{block mid} - c_{sigma+1}), or raw k for exact diagonals
-  __bf16 kh[kD][kPad];   // (k 2^(c_64 - c_{sigma+1}))^T [i][sigma]
-  __bf16 vt[DV][kPad];   // v^T [j][sigma]
+  __bf16 kh[kL][kPad];   // k 2^(c_64 - c_{sigma+1}) [sigma][i]
+  __bf16 v[kL][kPad];    // v [sigma][j], DV columns
   __bf16 sp[DV][kPad];   // S^T [j][i]
   float c[kL + 1][kCPad];
   float beta[kL];
@@ -118,7 +118,8 @@ __device__ __forceinline__ bool decay_prefix(const ChunkW& x, CTable& c) {
   return exact;
 }
 
-// Scaled copies of one chunk into LDS (the decay prefix must be in place).
+// Scaled copies of one chunk into LDS (the decay prefix must be in place),
+// all row-major: products over sigma read kh and v with the transpose load.
 template <int DV>
 __device__ __forceinline__ void stage_chunk_f(const ChunkRegs& x, bool exact, LdsF<DV>& s) {
   const int tid = threadIdx.x;
@@ -138,7 +139,7 @@ __device__ __forceinline__ void stage_chunk_f(const ChunkRegs& x, bool exact, Ld
   *reinterpret_cast<uint4*>(&s.rr[tau][d0]) = x.r0;
   *reinterpret_cast<uint4*>(&s.rr[tau][d0 + 8]) = x.r1;
   float bpart = 0.f;
-  bf16x8 kba, kbb, kda, kdb;
+  bf16x8 kba, kbb, kda, kdb, kha, khb;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const int i = d0 + e;
@@ -148,26 +149,32 @@ __device__ __forceinline__ void stage_chunk_f(const ChunkRegs& x, bool exact, Ld
     const float fkh = exp2_fast(s.c[kL][i] - ct1);
     const __bf16 vkb = to_bf16(kv[e] * fkb);
     const __bf16 vkd = exact ? to_bf16(kv[e]) : to_bf16(kv[e] * fkd);
+    const __bf16 vkh = to_bf16(kv[e] * fkh);
     if (e < 8) {
       kba[e] = vkb;
       kda[e] = vkd;
+      kha[e] = vkh;
     } else {
       kbb[e - 8] = vkb;
       kdb[e - 8] = vkd;
+      khb[e - 8] = vkh;
     }
-    s.kh[i][tau] = to_bf16(kv[e] * fkh);
     bpart = fmaf(rv[e] * s.u[i], kv[e], bpart);
   }
   *reinterpret_cast<bf16x8*>(&s.kb[tau][d0]) = kba;
   *reinterpret_cast<bf16x8*>(&s.kb[tau][d0 + 8]) = kbb;
   *reinterpret_cast<bf16x8*>(&s.kd[tau][d0]) = kda;
   *reinterpret_cast<bf16x8*>(&s.kd[tau][d0 + 8]) = kdb;
-  const uint32_t vw[8] = {x.v0.x, x.v0.y, x.v0.z, x.v0.w, x.v1.x, x.v1.y, x.v1.z, x.v1.w};
-  constexpr int VPT = DV / 4;
-#pragma unroll
-  for (int e = 0; e < VPT / 2; ++e) {
-    s.vt[VPT * q4 + 2 * e][tau] = to_bf16(lo_half(vw[e]));
-    s.vt[VPT * q4 + 2 * e + 1][tau] = to_bf16(hi_half(vw[e]));
+  *reinterpret_cast<bf16x8*>(&s.kh[tau][d0]) = kha;
+  *reinterpret_cast<bf16x8*>(&s.kh[tau][d0 + 8]) = khb;
+  // v is already bf16: DV / 4 value dims of this token go in as loaded
+  if constexpr (DV == 64) {
+    *reinterpret_cast<uint4*>(&s.v[tau][16 * q4]) = x.v0;
+    *reinterpret_cast<uint4*>(&s.v[tau][16 * q4 + 8]) = x.v1;
+  } else if constexpr (DV == 32) {
+    *reinterpret_cast<uint4*>(&s.v[tau][8 * q4]) = x.v0;
+  } else {
+    *reinterpret_cast<uint2*>(&s.v[tau][4 * q4]) = uint2{x.v0.x, x.v0.y};
   }
   bpart += __shfl_xor(bpart, 1);
   bpart += __shfl_xor(bpart, 2);
@@ -189,7 +196,7 @@ __device__ __forceinline__ bf16x8 scaled_queries(const LdsF<DV>& s, int tau, int
 // Workgroup: 4 waves; (batch, head, slice of DV value columns), placed as in
 // the Eagle kernel.
 template <int DV>
-__global__ __launch_bounds__(256) void wkv6_fwd_chunked(
+__global__ __launch_bounds__(256, 2) void wkv6_fwd_chunked(
     int T, int H, int BH, const uint16_t* __restrict__ r, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ w,
     const float* __restrict__ u, float* __restrict__ o, const float* s_in, float* s_out,
@@ -253,6 +260,11 @@ __global__ __launch_bounds__(256) void wkv6_fwd_chunked(
   const int n_chunks = (T + kL - 1) / kL;
   const int c_begin = seg * seg_chunks;
   const int c_end = min(n_chunks, c_begin + seg_chunks);
+  // o offsets of this lane within a chunk: tokens 16 q + crow + rr
+  uint32_t ooff[4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr)
+    ooff[rr] = uint32_t(((16 * q + crow + rr) * H * kD + j0 + row) * 4);
   ChunkRegs cur, nxt;
   ChunkW wc, wn;
   load_chunk<DV>(cur, c_begin * kL, T, H, b, h, j0, r, k, v);
@@ -311,29 +323,31 @@ __global__ __launch_bounds__(256) void wkv6_fwd_chunked(
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int sig = 16 * nb + crow + rr;
-        float val = 0.f;
-        if (nb <= q) val = sig < tau_l ? acc[nb][rr] : (sig == tau_l ? beta : 0.f);
+        const float val = sig < tau_l ? acc[nb][rr] : (sig == tau_l ? beta : 0.f);
         ap[nb >> 1][(nb & 1) * 4 + rr] = to_bf16(val);
       }
 
-    // O = A' V + (r 2^c) S.
+    // O = A' V + (r 2^c) S, and S <- diag(2^c_64) S + kh^T V for key rows
+    // 16q..16q+15; the products over sigma share their V operands.
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float dall = exp2_fast(s.c[kL][16 * q + crow + rr]);
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) sacc[jb][rr] *= dall;
+    }
     floatx4 oacc[NJB];
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) oacc[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const int nks = (q + 2) >> 1;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      if (ks < nks) {
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 kop = sigma_operand(s.kh, 32 * ks, 16 * q, lane);
 #pragma unroll
-        for (int jb = 0; jb < NJB; ++jb) {
-          const __bf16* vr = &s.vt[16 * jb + row][32 * ks + crow];
-          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 16);
-          const bf16x8 bb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          oacc[jb] = mfma(ap[ks], bb, oacc[jb]);
-        }
+      for (int jb = 0; jb < NJB; ++jb) {
+        const bf16x8 vop = sigma_operand(s.v, 32 * ks, 16 * jb, lane);
+        oacc[jb] = mfma(ap[ks], vop, oacc[jb]);
+        sacc[jb] = mfma(kop, vop, sacc[jb]);
       }
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       // r 2^c_tau (row 0 of the prefix table is zero)
@@ -344,30 +358,14 @@ __global__ __launch_bounds__(256) void wkv6_fwd_chunked(
         oacc[jb] = mfma(a, bb, oacc[jb]);
       }
     }
+    {
+      const Rsrc ro = chunk_rsrc(o, t0, T, H, b, h, 4);  // rows past T are dropped
 #pragma unroll
-    for (int jb = 0; jb < NJB; ++jb)
+      for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int tau = 16 * q + crow + rr;
-        if (t0 + tau < T)
-          o[((size_t(b) * T + t0 + tau) * H + h) * kD + j0 + 16 * jb + row] = oacc[jb][rr];
-      }
-
-    // S <- diag(2^c_64) S + kh^T V for key rows 16q..16q+15.
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const float dall = exp2_fast(s.c[kL][16 * q + crow + rr]);
-#pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) sacc[jb][rr] *= dall;
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.kh[16 * q + row][32 * ks + kq]);
-#pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) {
-        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s.vt[16 * jb + row][32 * ks + kq]);
-        sacc[jb] = mfma(a, bb, sacc[jb]);
-      }
+        for (int rr = 0; rr < 4; ++rr)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(oacc[jb][rr]), ro, ooff[rr],
+                                                64 * jb, kNonTemporal);
     }
     __syncthreads();  // every wave is done with this chunk's LDS
 
@@ -386,7 +384,8 @@ __global__ __launch_bounds__(256) void wkv6_fwd_chunked(
 
 // Local end state of one time segment (all but the last) from a zero start,
 // and the segment's summed log2 decay per key channel, for one value slice:
-// seg_state[bh][seg] holds S[i][j] (64 x 64) then L[i] (64).
+// seg_state[bh][seg] holds S[i][j] (64 x 64) then L[i] (64).  The next
+// chunk's k, v and decays load while this one multiplies.
 template <int DV>
 __global__ __launch_bounds__(256) void wkv6_seg_state(int T, int H, int BH, int seg_chunks,
                                                       int nseg, const uint16_t* __restrict__ k,
@@ -396,8 +395,8 @@ __global__ __launch_bounds__(256) void wkv6_seg_state(int T, int H, int BH, int 
   constexpr int NS = kD / DV;
   constexpr int NJB = DV / 16;
   __shared__ CTable s_c;
-  __shared__ __attribute__((aligned(16))) __bf16 s_kh[kD][kPad];
-  __shared__ __attribute__((aligned(16))) __bf16 s_vt[DV][kPad];
+  __shared__ __attribute__((aligned(16))) __bf16 s_kh[kL][kPad];
+  __shared__ __attribute__((aligned(16))) __bf16 s_v[kL][kPad];
   const int per_seg = (BH + 7) / 8 * 8 * NS;
   const int seg = blockIdx.x / per_seg;
   const int bx = blockIdx.x - seg * per_seg;
@@ -409,36 +408,49 @@ __global__ __launch_bounds__(256) void wkv6_seg_state(int T, int H, int BH, int 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int q = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int row = lane & 15, kq = 8 * (lane >> 4), crow = 4 * (lane >> 4);
+  const int row = lane & 15, crow = 4 * (lane >> 4);
   const int tau = tid >> 2, q4 = tid & 3, d0 = 16 * q4;
   floatx4 sacc[NJB];
 #pragma unroll
   for (int jb = 0; jb < NJB; ++jb) sacc[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
   float ltot = 0.f;  // thread tid < 64: channel tid
   const int c_begin = seg * seg_chunks;
-  for (int c = c_begin; c < c_begin + seg_chunks; ++c) {
-    // every chunk here is whole: only the last segment reaches the end of T
-    ChunkRegs x;
-    ChunkW xw;
-    load_chunk<DV>(x, c * kL, T, H, b, h, j0, k, k, v);
-    load_w(xw, c * kL, T, H, b, h, w);
-    decay_prefix(xw, s_c);
-    const uint32_t kw[8] = {x.k0.x, x.k0.y, x.k0.z, x.k0.w, x.k1.x, x.k1.y, x.k1.z, x.k1.w};
+  const int c_end = c_begin + seg_chunks;  // every chunk here is whole
+  ChunkRegs cur, nxt;
+  ChunkW wc, wn;
+  load_chunk<DV, false>(cur, c_begin * kL, T, H, b, h, j0, nullptr, k, v);
+  load_w(wc, c_begin * kL, T, H, b, h, w);
+  for (int c = c_begin; c < c_end; ++c) {
+    decay_prefix(wc, s_c);
+    const uint32_t kw[8] = {cur.k0.x, cur.k0.y, cur.k0.z, cur.k0.w,
+                            cur.k1.x, cur.k1.y, cur.k1.z, cur.k1.w};
+    bf16x8 kh0, kh1;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int i = d0 + e;
       const float kvv = (e & 1) ? hi_half(kw[e >> 1]) : lo_half(kw[e >> 1]);
-      s_kh[i][tau] = to_bf16(kvv * exp2_fast(s_c[kL][i] - s_c[tau + 1][i]));
+      const __bf16 x = to_bf16(kvv * exp2_fast(s_c[kL][i] - s_c[tau + 1][i]));
+      if (e < 8)
+        kh0[e] = x;
+      else
+        kh1[e - 8] = x;
     }
-    const uint32_t vw[8] = {x.v0.x, x.v0.y, x.v0.z, x.v0.w, x.v1.x, x.v1.y, x.v1.z, x.v1.w};
-    constexpr int VPT = DV / 4;
-#pragma unroll
-    for (int e = 0; e < VPT / 2; ++e) {
-      s_vt[VPT * q4 + 2 * e][tau] = to_bf16(lo_half(vw[e]));
-      s_vt[VPT * q4 + 2 * e + 1][tau] = to_bf16(hi_half(vw[e]));
+    *reinterpret_cast<bf16x8*>(&s_kh[tau][d0]) = kh0;
+    *reinterpret_cast<bf16x8*>(&s_kh[tau][d0 + 8]) = kh1;
+    if constexpr (DV == 64) {
+      *reinterpret_cast<uint4*>(&s_v[tau][16 * q4]) = cur.v0;
+      *reinterpret_cast<uint4*>(&s_v[tau][16 * q4 + 8]) = cur.v1;
+    } else if constexpr (DV == 32) {
+      *reinterpret_cast<uint4*>(&s_v[tau][8 * q4]) = cur.v0;
+    } else {
+      *reinterpret_cast<uint2*>(&s_v[tau][4 * q4]) = uint2{cur.v0.x, cur.v0.y};
     }
     if (tid < kD) ltot += s_c[kL][tid];
     __syncthreads();
+    if (c + 1 < c_end) {
+      load_chunk<DV, false>(nxt, (c + 1) * kL, T, H, b, h, j0, nullptr, k, v);
+      load_w(wn, (c + 1) * kL, T, H, b, h, w);
+    }
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const float dall = exp2_fast(s_c[kL][16 * q + crow + rr]);
@@ -447,14 +459,14 @@ __global__ __launch_bounds__(256) void wkv6_seg_state(int T, int H, int BH, int 
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s_kh[16 * q + row][32 * ks + kq]);
+      const bf16x8 kop = sigma_operand(s_kh, 32 * ks, 16 * q, lane);
 #pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) {
-        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s_vt[16 * jb + row][32 * ks + kq]);
-        sacc[jb] = mfma(a, bb, sacc[jb]);
-      }
+      for (int jb = 0; jb < NJB; ++jb)
+        sacc[jb] = mfma(kop, sigma_operand(s_v, 32 * ks, 16 * jb, lane), sacc[jb]);
     }
     __syncthreads();
+    cur = nxt;
+    wc = wn;
   }
   float* dst = seg_state + (size_t(bh) * (nseg - 1) + seg) * (kD * kD + kD);
 #pragma unroll
