@@ -52,6 +52,10 @@ struct alignas(16) LdsF {
   __bf16 v[kL][kPad];    // v [sigma][j], DV columns
   __bf16 sp[DV][kPad];   // S^T [j][i]
   float c[kL + 1][kCPad];
+  // fast chunks only (decay_tables): per-channel ratios of decay powers
+  float g_blk[4][kD];     // 2^(c_{16b+16} - c_{16b+8})
+  float h_blk[4][kD];     // 2^(c_64 - c_{16b+16})
+  float q_ref[4][4][kD];  // [q][m]: 2^(c_{16q+8} - c_ref), ref = 16m+16 (m < 3) or 0 (m = 3)
   float beta[kL];
   float u[kD];
 };
@@ -118,6 +122,25 @@ __device__ __forceinline__ bool decay_prefix(const ChunkW& x, CTable& c) {
   return exact;
 }
 
+// For a chunk whose decays all satisfy |log2 w| <= 15, every power the
+// chunk needs is one power within 8 tokens of a block middle (finite in fp32)
+// times per-channel ratios, which are computed here once per chunk:
+//   2^(c_{16b+16} - c_{s+1}) = 2^(c_{16b+8} - c_{s+1}) g_blk[b],
+//   2^(c_64 - c_{s+1})       = 2^(c_{16b+16} - c_{s+1}) h_blk[b],
+//   2^(c_t - c_ref)          = 2^(c_t - c_{16q+8}) q_ref[q][m].
+// Ratios that no product uses (a reference after the block) may be inf.
+template <int DV>
+__device__ __forceinline__ void decay_tables(LdsF<DV>& s) {
+  const int tid = threadIdx.x;
+  const int i = tid & 63, bq = tid >> 6;
+  s.g_blk[bq][i] = exp2_fast(s.c[16 * bq + 16][i] - s.c[16 * bq + 8][i]);
+  s.h_blk[bq][i] = exp2_fast(s.c[kL][i] - s.c[16 * bq + 16][i]);
+  const float cm = s.c[16 * bq + 8][i];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) s.q_ref[bq][m][i] = exp2_fast(cm - s.c[m < 3 ? 16 * m + 16 : 0][i]);
+  __syncthreads();
+}
+
 // Scaled copies of one chunk into LDS (the decay prefix must be in place),
 // all row-major: products over sigma read kh and v with the transpose load.
 template <int DV>
@@ -144,9 +167,16 @@ __device__ __forceinline__ void stage_chunk_f(const ChunkRegs& x, bool exact, Ld
   for (int e = 0; e < 16; ++e) {
     const int i = d0 + e;
     const float ct1 = s.c[tau + 1][i];
-    const float fkb = exp2_fast(s.c[16 * blk + 16][i] - ct1);
-    const float fkd = exp2_fast(s.c[16 * blk + 8][i] - ct1);
-    const float fkh = exp2_fast(s.c[kL][i] - ct1);
+    float fkb, fkd, fkh;
+    if (exact) {
+      fkb = exp2_fast(s.c[16 * blk + 16][i] - ct1);
+      fkd = exp2_fast(s.c[16 * blk + 8][i] - ct1);
+      fkh = exp2_fast(s.c[kL][i] - ct1);
+    } else {
+      fkd = exp2_fast(s.c[16 * blk + 8][i] - ct1);
+      fkb = fkd * s.g_blk[blk][i];
+      fkh = fkb * s.h_blk[blk][i];
+    }
     const __bf16 vkb = to_bf16(kv[e] * fkb);
     const __bf16 vkd = exact ? to_bf16(kv[e]) : to_bf16(kv[e] * fkd);
     const __bf16 vkh = to_bf16(kv[e] * fkh);
@@ -272,6 +302,7 @@ __global__ __launch_bounds__(256, 2) void wkv6_fwd_chunked(
   for (int c = c_begin; c < c_end; ++c) {
     const int t0 = c * kL;
     const bool exact = decay_prefix(wc, s.c);
+    if (!exact) decay_tables(s);
     stage_chunk_f(cur, exact, s);
     __syncthreads();
     if (c + 1 < c_end) {
@@ -280,27 +311,54 @@ __global__ __launch_bounds__(256, 2) void wkv6_fwd_chunked(
     }
 
     // A^T: key blocks nb <= q against this wave's 16 queries (column
-    // tau = 16q + row of the lane, rows sigma = 16nb + crow .. +3).
+    // tau = 16q + row of the lane, rows sigma = 16nb + crow .. +3).  The
+    // lane's scaled queries r 2^c_tau for the inter-chunk product share its
+    // operand position and are formed here too.
     const int tau_l = 16 * q + row;
     floatx4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
                       {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    bf16x8 ainter[2];
+    if (!exact) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int i0 = 32 * ks + kq;
+      for (int ks = 0; ks < 2; ++ks) {
+        const int i0 = 32 * ks + kq;
+        const bf16x8 raw = *reinterpret_cast<const bf16x8*>(&s.rr[tau_l][i0]);
+        float qb[8];  // r 2^(c_tau - c_{16q+8})
 #pragma unroll
-      for (int nb = 0; nb < 3; ++nb)
-        if (nb < q) {
-          const bf16x8 bq = scaled_queries(s, tau_l, i0, 16 * nb + 16);
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.kb[16 * nb + row][i0]);
-          acc[nb] = mfma(a, bq, acc[nb]);
+        for (int e = 0; e < 8; ++e)
+          qb[e] = float(raw[e]) * exp2_fast(s.c[tau_l][i0 + e] - s.c[16 * q + 8][i0 + e]);
+#pragma unroll
+        for (int nb = 0; nb < 3; ++nb)
+          if (nb < q) {
+            bf16x8 bq;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bq[e] = to_bf16(qb[e] * s.q_ref[q][nb][i0 + e]);
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.kb[16 * nb + row][i0]);
+            acc[nb] = mfma(a, bq, acc[nb]);
+          }
+        bf16x8 bq;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          bq[e] = to_bf16(qb[e]);
+          ainter[ks][e] = to_bf16(qb[e] * s.q_ref[q][3][i0 + e]);
         }
-      if (!exact) {
-        const bf16x8 bq = scaled_queries(s, tau_l, i0, 16 * q + 8);
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.kd[16 * q + row][i0]);
         acc[q] = mfma(a, bq, acc[q]);
       }
-    }
-    if (exact) {
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int i0 = 32 * ks + kq;
+#pragma unroll
+        for (int nb = 0; nb < 3; ++nb)
+          if (nb < q) {
+            const bf16x8 bq = scaled_queries(s, tau_l, i0, 16 * nb + 16);
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.kb[16 * nb + row][i0]);
+            acc[nb] = mfma(a, bq, acc[nb]);
+          }
+        // r 2^c_tau (row 0 of the prefix table is zero)
+        ainter[ks] = scaled_queries(s, tau_l, i0, 0);
+      }
       // diagonal block in fp32: sum_i r[tau][i] k[sigma][i] 2^(c_tau - c_{sigma+1})[i]
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
@@ -350,12 +408,10 @@ __global__ __launch_bounds__(256, 2) void wkv6_fwd_chunked(
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      // r 2^c_tau (row 0 of the prefix table is zero)
-      const bf16x8 a = scaled_queries(s, 16 * q + row, 32 * ks + kq, 0);
 #pragma unroll
       for (int jb = 0; jb < NJB; ++jb) {
         const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s.sp[16 * jb + row][32 * ks + kq]);
-        oacc[jb] = mfma(a, bb, oacc[jb]);
+        oacc[jb] = mfma(ainter[ks], bb, oacc[jb]);
       }
     }
     {
