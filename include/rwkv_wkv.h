@@ -183,7 +183,7 @@ int rwkv_wkv4_step(int64_t B, int64_t C,
  *   w        [H,D]      float32 decay factor in (0, 1]
  *   u        [H,D]      float32 current-token bonus
  *   o        [B,T,H,D]  float32 output
- *   D must be 64 (RWKV_ERR_UNSUPPORTED otherwise).
+ *   D must be 64 and H < 65536 (RWKV_ERR_UNSUPPORTED otherwise).
  *   ws, ws_bytes: at least rwkv_wkv5_forward_workspace(B,T,H,D) bytes (may
  *   be 0, then ws may be NULL).
  * Accuracy: max |o - exact| <= 2e-2 * o_abs, where o_abs is the same sum
@@ -252,7 +252,7 @@ int rwkv_wkv5_step(int64_t B, int64_t H, int64_t D,
  *                       s_out may equal s_in.
  *   ws, ws_bytes: at least rwkv_wkv6_forward_workspace(B,T,H,D) bytes (may be
  *   0, then ws may be NULL); no zero-fill needed.
- *   D must be 64.
+ *   D must be 64 and H < 65536 (RWKV_ERR_UNSUPPORTED otherwise).
  * Accuracy: as rwkv_wkv5_forward, against the same magnitude recurrence with
  * the per-token decays.
  * ---------------------------------------------------------------------- */

@@ -189,7 +189,8 @@ int wkv5_forward_impl(int64_t B, int64_t T, int64_t H, int64_t D, const uint16_t
   if (!dims_ok({B, T, H, D}, &n)) return RWKV_ERR_SHAPE;
   if (n == 0) return RWKV_OK;
   if (D != 64) return RWKV_ERR_UNSUPPORTED;
-  if (T >= (int64_t(1) << 31) || B * H >= (int64_t(1) << 31)) return RWKV_ERR_UNSUPPORTED;
+  if (T >= (int64_t(1) << 31) || B * H >= (int64_t(1) << 31) || H >= 65536)
+    return RWKV_ERR_UNSUPPORTED;
   if (!r || !k || !v || !w || !u || !o) return RWKV_ERR_NULLPTR;
   if (!aligned16(r) || !aligned16(k) || !aligned16(v) || !aligned16(w) || !aligned16(u) ||
       !aligned16(o) || (s_in && !aligned16(s_in)) || (s_out && !aligned16(s_out)))
@@ -252,7 +253,8 @@ RWKV_API int rwkv_wkv6_forward(int64_t B, int64_t T, int64_t H, int64_t D, const
   if (!dims_ok({B, T, H, D}, &n)) return RWKV_ERR_SHAPE;
   if (n == 0) return RWKV_OK;
   if (D != 64) return RWKV_ERR_UNSUPPORTED;
-  if (T >= (int64_t(1) << 31) || B * H >= (int64_t(1) << 31)) return RWKV_ERR_UNSUPPORTED;
+  if (T >= (int64_t(1) << 31) || B * H >= (int64_t(1) << 31) || H >= 65536)
+    return RWKV_ERR_UNSUPPORTED;
   if (!r || !k || !v || !w || !u || !o) return RWKV_ERR_NULLPTR;
   if (!aligned16(r) || !aligned16(k) || !aligned16(v) || !aligned16(w) || !aligned16(u) ||
       !aligned16(o) || (s_in && !aligned16(s_in)) || (s_out && !aligned16(s_out)))

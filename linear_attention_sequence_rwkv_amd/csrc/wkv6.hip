@@ -421,7 +421,7 @@ __global__ __launch_bounds__(256, 2) void wkv6_fwd_chunked(
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(oacc[jb][rr]), ro, ooff[rr],
-                                                64 * jb, kNonTemporal);
+                                                64 * jb, kStoreAux);
     }
     __syncthreads();  // every wave is done with this chunk's LDS
 

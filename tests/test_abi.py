@@ -143,6 +143,8 @@ def test_wkv5_rejections(lib):
     need = lib.rwkv_wkv5_forward_workspace(4, 4096, 32, 64)
     assert f(0, 4096, 32, 64, *[NULL] * 6, NULL, 0, NULL) == OK
     assert f(4, 4096, 32, 32, *ptrs(), FAKE, need, NULL) == UNSUPPORTED
+    # chunks stream through 32-bit buffer ranges of 64 rows of H*D floats
+    assert f(1, 64, 65536, 64, *ptrs(), FAKE, 1 << 40, NULL) == UNSUPPORTED
     assert f(4, -1, 32, 64, *ptrs(), FAKE, need, NULL) == SHAPE
     for n in "r k v w u o".split():
         assert f(4, 4096, 32, 64, *ptrs(**{n: NULL}), FAKE, need, NULL) == NULLPTR, n
@@ -222,6 +224,7 @@ def test_wkv6_rejections(lib):
     assert need > 0 and lib.rwkv_wkv6_forward_workspace(4, 4096, 32, 32) == 0
     assert f(0, 64, 2, 64, *[NULL] * 8, NULL, 0, NULL) == OK
     assert f(1, 64, 2, 32, *ptrs(), NULL, 0, NULL) == UNSUPPORTED
+    assert f(1, 64, 65536, 64, *ptrs(), FAKE, 1 << 40, NULL) == UNSUPPORTED
     assert f(1, -64, 2, 64, *ptrs(), NULL, 0, NULL) == SHAPE
     for n in names[:6]:
         assert f(1, 64, 2, 64, *ptrs(**{n: NULL}), NULL, 0, NULL) == NULLPTR, n
