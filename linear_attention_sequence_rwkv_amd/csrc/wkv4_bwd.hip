@@ -357,18 +357,36 @@ __global__ __launch_bounds__(64 * NW) void wkv4_bwd_tiled(
 // gw[c] = -sum of the gw slots of channel c, gu[c] = sum of its gu slots, in
 // slot order (double accumulation).  Four threads per channel split the
 // slots and are combined in a fixed order.
-__global__ __launch_bounds__(256) void wkv4_bwd_reduce(int C, int rows,
-                                                       const uint64_t* __restrict__ part_w,
-                                                       const uint64_t* __restrict__ part_u,
-                                                       float* __restrict__ gw,
-                                                       float* __restrict__ gu) {
-  __shared__ double s_w[4][64], s_u[4][64];
+// Sums of the partial gw, gu slots per channel: a workgroup takes 64
+// channels (lane = channel, so every load is one coalesced row) and its 16
+// waves take every 16th row, four rows in flight per wave; the 16 wave sums
+// are added in a fixed order.  Double precision throughout.
+constexpr int kRedWaves = 16;
+
+__global__ __launch_bounds__(64 * kRedWaves) void wkv4_bwd_reduce(
+    int C, int rows, const uint64_t* __restrict__ part_w, const uint64_t* __restrict__ part_u,
+    float* __restrict__ gw, float* __restrict__ gu) {
+  __shared__ double s_w[kRedWaves][64], s_u[kRedWaves][64];
   const int cl = threadIdx.x & 63;
   const int r0 = threadIdx.x >> 6;
   const int c = blockIdx.x * 64 + cl;
   double sw = 0.0, su = 0.0;
   if (c < C) {
-    for (int r = r0; r < rows; r += 4) {
+    int r = r0;
+    for (; r + 3 * kRedWaves < rows; r += 4 * kRedWaves) {
+      float xw[4], xu[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        xw[j] = tag_val(part_w[size_t(r + j * kRedWaves) * C + c]);
+        xu[j] = tag_val(part_u[size_t(r + j * kRedWaves) * C + c]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sw += double(xw[j]);
+        su += double(xu[j]);
+      }
+    }
+    for (; r < rows; r += kRedWaves) {
       sw += double(tag_val(part_w[size_t(r) * C + c]));
       su += double(tag_val(part_u[size_t(r) * C + c]));
     }
@@ -377,8 +395,14 @@ __global__ __launch_bounds__(256) void wkv4_bwd_reduce(int C, int rows,
   s_u[r0][cl] = su;
   __syncthreads();
   if (r0 == 0 && c < C) {
-    gw[c] = float(-(s_w[0][cl] + s_w[1][cl] + s_w[2][cl] + s_w[3][cl]));
-    gu[c] = float(s_u[0][cl] + s_u[1][cl] + s_u[2][cl] + s_u[3][cl]);
+    double tw = 0.0, tu = 0.0;
+#pragma unroll
+    for (int g = 0; g < kRedWaves; ++g) {
+      tw += s_w[g][cl];
+      tu += s_u[g][cl];
+    }
+    gw[c] = float(-tw);
+    gu[c] = float(tu);
   }
 }
 
@@ -432,7 +456,8 @@ hipError_t wkv4_backward_launch(const Wkv4BwdPlan& pl, int64_t B, int64_t T, int
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // 3. gw, gu
-  hipLaunchKernelGGL(wkv4_bwd_reduce, dim3(unsigned((C + 63) / 64)), dim3(256), 0, stream, int(C),
+  hipLaunchKernelGGL(wkv4_bwd_reduce, dim3(unsigned((C + 63) / 64)), dim3(64 * kRedWaves), 0,
+                     stream, int(C),
                      int(pl.part_rows), part_w, part_u, gw, gu);
   return hipGetLastError();
 }
