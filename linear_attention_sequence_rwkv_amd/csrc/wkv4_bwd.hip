@@ -354,10 +354,8 @@ __global__ __launch_bounds__(64 * NW) void wkv4_bwd_tiled(
   }
 }
 
-// gw[c] = -sum of the gw slots of channel c, gu[c] = sum of its gu slots, in
-// slot order (double accumulation).  Four threads per channel split the
-// slots and are combined in a fixed order.
-// Sums of the partial gw, gu slots per channel: a workgroup takes 64
+// gw[c] = -(sum of the gw slots of channel c), gu[c] = sum of its gu slots.
+// A workgroup takes 64
 // channels (lane = channel, so every load is one coalesced row) and its 16
 // waves take every 16th row, four rows in flight per wave; the 16 wave sums
 // are added in a fixed order.  Double precision throughout.
