@@ -315,8 +315,10 @@ __global__ __launch_bounds__(256, 2) void wkv6_fwd_chunked(
     // lane's scaled queries r 2^c_tau for the inter-chunk product share its
     // operand position and are formed here too.
     const int tau_l = 16 * q + row;
-    floatx4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
-                      {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    // acc[nb]: key blocks before the wave's own; dacc: the diagonal block
+    // (kept apart so that no register array is indexed by the wave number)
+    floatx4 acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    floatx4 dacc = {0.f, 0.f, 0.f, 0.f};
     bf16x8 ainter[2];
     if (!exact) {
 #pragma unroll
@@ -343,7 +345,7 @@ __global__ __launch_bounds__(256, 2) void wkv6_fwd_chunked(
           ainter[ks][e] = to_bf16(qb[e] * s.q_ref[q][3][i0 + e]);
         }
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.kd[16 * q + row][i0]);
-        acc[q] = mfma(a, bq, acc[q]);
+        dacc = mfma(a, bq, dacc);
       }
     } else {
 #pragma unroll
@@ -369,7 +371,7 @@ __global__ __launch_bounds__(256, 2) void wkv6_fwd_chunked(
             a = fmaf(float(s.rr[tau_l][i]) * float(s.kd[sig][i]),
                      exp2_fast(s.c[tau_l][i] - s.c[sig + 1][i]), a);
         }
-        acc[q][rr] = a;
+        dacc[rr] = a;
       }
     }
 
@@ -381,7 +383,8 @@ __global__ __launch_bounds__(256, 2) void wkv6_fwd_chunked(
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int sig = 16 * nb + crow + rr;
-        const float val = sig < tau_l ? acc[nb][rr] : (sig == tau_l ? beta : 0.f);
+        const float sc = nb == q ? dacc[rr] : (nb < 3 ? acc[nb < 3 ? nb : 0][rr] : 0.f);
+        const float val = sig < tau_l ? sc : (sig == tau_l ? beta : 0.f);
         ap[nb >> 1][(nb & 1) * 4 + rr] = to_bf16(val);
       }
 
