@@ -39,7 +39,7 @@ namespace {
 
 using namespace eagle;
 
-constexpr int kCPad = 65;                // fp32 row length of the log-decay prefix table
+constexpr int kCPad = 68;                // fp32 row length of the log-decay prefix table (16-byte rows)
 constexpr float kMaxDiagLog2 = 15.f;     // fast diagonal blocks need every |log2 w| <= this
 constexpr float kMinLog2Decay = -126.f;  // log2 w below this counts as this (2^-126: no memory)
 
@@ -56,6 +56,7 @@ struct alignas(16) LdsF {
   float g_blk[4][kD];     // 2^(c_{16b+16} - c_{16b+8})
   float h_blk[4][kD];     // 2^(c_64 - c_{16b+16})
   float q_ref[4][4][kD];  // [q][m]: 2^(c_{16q+8} - c_ref), ref = 16m+16 (m < 3) or 0 (m = 3)
+  float cmid[4][kD];      // c_{16b+8}
   float beta[kL];
   float u[kD];
 };
@@ -93,12 +94,16 @@ __device__ __forceinline__ bool decay_prefix(const ChunkW& x, CTable& c) {
   const float wv[16] = {x.a.x, x.a.y, x.a.z, x.a.w, x.b.x, x.b.y, x.b.z, x.b.w,
                         x.c.x, x.c.y, x.c.z, x.c.w, x.d.x, x.d.y, x.d.z, x.d.w};
   int fast_ok = 1;
+  float l2[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const float l2 = fmaxf(__log2f(wv[e]), kMinLog2Decay);
-    fast_ok &= l2 >= -kMaxDiagLog2;
-    c[tau + 1][d0 + e] = l2;
+    l2[e] = fmaxf(__log2f(wv[e]), kMinLog2Decay);
+    fast_ok &= l2[e] >= -kMaxDiagLog2;
   }
+#pragma unroll
+  for (int e = 0; e < 16; e += 4)
+    *reinterpret_cast<float4*>(&c[tau + 1][d0 + e]) =
+        float4{l2[e], l2[e + 1], l2[e + 2], l2[e + 3]};
   if (tid < kD) c[0][tid] = 0.f;
   const bool exact = __syncthreads_or(!fast_ok) != 0;
   // per channel: four threads each take 16 rows, then add the totals of the
@@ -136,6 +141,7 @@ __device__ __forceinline__ void decay_tables(LdsF<DV>& s) {
   s.g_blk[bq][i] = exp2_fast(s.c[16 * bq + 16][i] - s.c[16 * bq + 8][i]);
   s.h_blk[bq][i] = exp2_fast(s.c[kL][i] - s.c[16 * bq + 16][i]);
   const float cm = s.c[16 * bq + 8][i];
+  s.cmid[bq][i] = cm;
 #pragma unroll
   for (int m = 0; m < 4; ++m) s.q_ref[bq][m][i] = exp2_fast(cm - s.c[m < 3 ? 16 * m + 16 : 0][i]);
   __syncthreads();
@@ -163,19 +169,50 @@ __device__ __forceinline__ void stage_chunk_f(const ChunkRegs& x, bool exact, Ld
   *reinterpret_cast<uint4*>(&s.rr[tau][d0 + 8]) = x.r1;
   float bpart = 0.f;
   bf16x8 kba, kbb, kda, kdb, kha, khb;
+  // this token's prefix and, on fast chunks, the block's reference and
+  // ratios for the 16 channels: 16-byte reads
+  float ct[16], cm[16], gb[16], hb[16];
+#pragma unroll
+  for (int e = 0; e < 16; e += 4) {
+    const float4 a = *reinterpret_cast<const float4*>(&s.c[tau + 1][d0 + e]);
+    ct[e] = a.x;
+    ct[e + 1] = a.y;
+    ct[e + 2] = a.z;
+    ct[e + 3] = a.w;
+  }
+  if (!exact) {
+#pragma unroll
+    for (int e = 0; e < 16; e += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(&s.cmid[blk][d0 + e]);
+      const float4 g4 = *reinterpret_cast<const float4*>(&s.g_blk[blk][d0 + e]);
+      const float4 h4 = *reinterpret_cast<const float4*>(&s.h_blk[blk][d0 + e]);
+      cm[e] = a.x;
+      cm[e + 1] = a.y;
+      cm[e + 2] = a.z;
+      cm[e + 3] = a.w;
+      gb[e] = g4.x;
+      gb[e + 1] = g4.y;
+      gb[e + 2] = g4.z;
+      gb[e + 3] = g4.w;
+      hb[e] = h4.x;
+      hb[e + 1] = h4.y;
+      hb[e + 2] = h4.z;
+      hb[e + 3] = h4.w;
+    }
+  }
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const int i = d0 + e;
-    const float ct1 = s.c[tau + 1][i];
+    const float ct1 = ct[e];
     float fkb, fkd, fkh;
     if (exact) {
       fkb = exp2_fast(s.c[16 * blk + 16][i] - ct1);
       fkd = exp2_fast(s.c[16 * blk + 8][i] - ct1);
       fkh = exp2_fast(s.c[kL][i] - ct1);
     } else {
-      fkd = exp2_fast(s.c[16 * blk + 8][i] - ct1);
-      fkb = fkd * s.g_blk[blk][i];
-      fkh = fkb * s.h_blk[blk][i];
+      fkd = exp2_fast(cm[e] - ct1);
+      fkb = fkd * gb[e];
+      fkh = fkb * hb[e];
     }
     const __bf16 vkb = to_bf16(kv[e] * fkb);
     const __bf16 vkd = exact ? to_bf16(kv[e]) : to_bf16(kv[e] * fkd);
@@ -325,24 +362,35 @@ __global__ __launch_bounds__(256, 2) void wkv6_fwd_chunked(
       for (int ks = 0; ks < 2; ++ks) {
         const int i0 = 32 * ks + kq;
         const bf16x8 raw = *reinterpret_cast<const bf16x8*>(&s.rr[tau_l][i0]);
-        float qb[8];  // r 2^(c_tau - c_{16q+8})
+        auto ld8 = [](const float* p, float (&x)[8]) {
+          const float4 a = *reinterpret_cast<const float4*>(p);
+          const float4 b = *reinterpret_cast<const float4*>(p + 4);
+          x[0] = a.x, x[1] = a.y, x[2] = a.z, x[3] = a.w;
+          x[4] = b.x, x[5] = b.y, x[6] = b.z, x[7] = b.w;
+        };
+        float ctl[8], cml[8], qb[8];  // qb: r 2^(c_tau - c_{16q+8})
+        ld8(&s.c[tau_l][i0], ctl);
+        ld8(&s.cmid[q][i0], cml);
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          qb[e] = float(raw[e]) * exp2_fast(s.c[tau_l][i0 + e] - s.c[16 * q + 8][i0 + e]);
+        for (int e = 0; e < 8; ++e) qb[e] = float(raw[e]) * exp2_fast(ctl[e] - cml[e]);
 #pragma unroll
         for (int nb = 0; nb < 3; ++nb)
           if (nb < q) {
+            float qr[8];
+            ld8(&s.q_ref[q][nb][i0], qr);
             bf16x8 bq;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) bq[e] = to_bf16(qb[e] * s.q_ref[q][nb][i0 + e]);
+            for (int e = 0; e < 8; ++e) bq[e] = to_bf16(qb[e] * qr[e]);
             const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.kb[16 * nb + row][i0]);
             acc[nb] = mfma(a, bq, acc[nb]);
           }
+        float q0[8];
+        ld8(&s.q_ref[q][3][i0], q0);
         bf16x8 bq;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           bq[e] = to_bf16(qb[e]);
-          ainter[ks][e] = to_bf16(qb[e] * s.q_ref[q][3][i0 + e]);
+          ainter[ks][e] = to_bf16(qb[e] * q0[e]);
         }
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.kd[16 * q + row][i0]);
         dacc = mfma(a, bq, dacc);
@@ -453,7 +501,7 @@ __global__ __launch_bounds__(256) void wkv6_seg_state(int T, int H, int BH, int 
                                                       float* __restrict__ seg_state) {
   constexpr int NS = kD / DV;
   constexpr int NJB = DV / 16;
-  __shared__ CTable s_c;
+  __shared__ __attribute__((aligned(16))) CTable s_c;
   __shared__ __attribute__((aligned(16))) __bf16 s_kh[kL][kPad];
   __shared__ __attribute__((aligned(16))) __bf16 s_v[kL][kPad];
   const int per_seg = (BH + 7) / 8 * 8 * NS;
@@ -483,12 +531,19 @@ __global__ __launch_bounds__(256) void wkv6_seg_state(int T, int H, int BH, int 
     decay_prefix(wc, s_c);
     const uint32_t kw[8] = {cur.k0.x, cur.k0.y, cur.k0.z, cur.k0.w,
                             cur.k1.x, cur.k1.y, cur.k1.z, cur.k1.w};
+    float ce[16], ct[16];  // c_64 and this token's c_{tau+1}, 16-byte reads
+#pragma unroll
+    for (int e = 0; e < 16; e += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(&s_c[kL][d0 + e]);
+      const float4 t = *reinterpret_cast<const float4*>(&s_c[tau + 1][d0 + e]);
+      ce[e] = a.x, ce[e + 1] = a.y, ce[e + 2] = a.z, ce[e + 3] = a.w;
+      ct[e] = t.x, ct[e + 1] = t.y, ct[e + 2] = t.z, ct[e + 3] = t.w;
+    }
     bf16x8 kh0, kh1;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int i = d0 + e;
       const float kvv = (e & 1) ? hi_half(kw[e >> 1]) : lo_half(kw[e >> 1]);
-      const __bf16 x = to_bf16(kvv * exp2_fast(s_c[kL][i] - s_c[tau + 1][i]));
+      const __bf16 x = to_bf16(kvv * exp2_fast(ce[e] - ct[e]));
       if (e < 8)
         kh0[e] = x;
       else
