@@ -39,7 +39,8 @@ namespace {
 
 using namespace eagle;
 
-constexpr int kCPad = 68;                // fp32 row length of the log-decay prefix table (16-byte rows)
+constexpr int kCPad = 68;                // fp32 row length of the log-decay prefix table (16-byte rows;
+                                         // columns 64..67 hold the prefix's segment totals)
 constexpr float kMaxDiagLog2 = 15.f;     // fast diagonal blocks need every |log2 w| <= this
 constexpr float kMinLog2Decay = -126.f;  // log2 w below this counts as this (2^-126: no memory)
 
@@ -106,23 +107,23 @@ __device__ __forceinline__ bool decay_prefix(const ChunkW& x, CTable& c) {
         float4{l2[e], l2[e + 1], l2[e + 2], l2[e + 3]};
   if (tid < kD) c[0][tid] = 0.f;
   const bool exact = __syncthreads_or(!fast_ok) != 0;
-  // per channel: four threads each take 16 rows, then add the totals of the
-  // segments before theirs
+  // per channel: four threads each take 16 rows and scan them in registers,
+  // then add the totals of the segments before theirs (kept in the rows'
+  // padding columns: segment sg of channel ch at c[ch][kD + sg])
   const int ch = tid & 63, sg = tid >> 6;
-  float run = 0.f;
+  float run[16];
+  float acc = 0.f;
 #pragma unroll
-  for (int j = 1; j <= 16; ++j) {
-    run += c[16 * sg + j][ch];
-    c[16 * sg + j][ch] = run;
+  for (int j = 0; j < 16; ++j) {
+    acc += c[16 * sg + j + 1][ch];
+    run[j] = acc;
   }
+  c[ch][kD + sg] = acc;
   __syncthreads();
   float off = 0.f;
-  for (int j = 0; j < sg; ++j) off += c[16 * j + 16][ch];
-  __syncthreads();
-  if (sg > 0) {
+  for (int j = 0; j < sg; ++j) off += c[ch][kD + j];
 #pragma unroll
-    for (int j = 1; j <= 16; ++j) c[16 * sg + j][ch] += off;
-  }
+  for (int j = 0; j < 16; ++j) c[16 * sg + j + 1][ch] = run[j] + off;
   __syncthreads();
   return exact;
 }
