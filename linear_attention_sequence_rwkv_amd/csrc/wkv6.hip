@@ -59,7 +59,7 @@ struct alignas(16) LdsF {
   float q_ref[4][4][kD];  // [q][m]: 2^(c_{16q+8} - c_ref), ref = 16m+16 (m < 3) or 0 (m = 3)
   float cmid[4][kD];      // c_{16b+8}
   float beta[kL];
-  float u[kD];
+  float u[kD];  // 16-byte aligned: the members before it are multiples of 16 bytes
 };
 
 // This thread's 16 decay factors (token tid/4, channels 16*(tid%4)..).
@@ -171,8 +171,13 @@ __device__ __forceinline__ void stage_chunk_f(const ChunkRegs& x, bool exact, Ld
   float bpart = 0.f;
   bf16x8 kba, kbb, kda, kdb, kha, khb;
   // this token's prefix and, on fast chunks, the block's reference and
-  // ratios for the 16 channels: 16-byte reads
-  float ct[16], cm[16], gb[16], hb[16];
+  // ratios for the 16 channels (and u): 16-byte reads
+  float ct[16], cm[16], gb[16], hb[16], uu[16];
+#pragma unroll
+  for (int e = 0; e < 16; e += 4) {
+    const float4 a = *reinterpret_cast<const float4*>(&s.u[d0 + e]);
+    uu[e] = a.x, uu[e + 1] = a.y, uu[e + 2] = a.z, uu[e + 3] = a.w;
+  }
 #pragma unroll
   for (int e = 0; e < 16; e += 4) {
     const float4 a = *reinterpret_cast<const float4*>(&s.c[tau + 1][d0 + e]);
@@ -227,7 +232,7 @@ __device__ __forceinline__ void stage_chunk_f(const ChunkRegs& x, bool exact, Ld
       kdb[e - 8] = vkd;
       khb[e - 8] = vkh;
     }
-    bpart = fmaf(rv[e] * s.u[i], kv[e], bpart);
+    bpart = fmaf(rv[e] * uu[e], kv[e], bpart);
   }
   *reinterpret_cast<bf16x8*>(&s.kb[tau][d0]) = kba;
   *reinterpret_cast<bf16x8*>(&s.kb[tau][d0 + 8]) = kbb;
