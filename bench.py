@@ -51,9 +51,10 @@ def kernel_source_hash(files=("wkv4.hip", "wkv4_scan.h", "wkv_device.h")) -> str
     return h.hexdigest()[:16]
 
 
-def read_counter_summary(name: str, src_hash: str):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, or
-    None when the summary is missing or was taken on other kernel source."""
+def read_counter_summary(name: str, src_hash: str, key: str = "hbm_bytes_per_launch"):
+    """A figure (HBM bytes per launch by default) from a committed rocprofv3
+    counter summary, or None when the summary is missing or was taken on
+    other kernel source.  The first line holding the key is used."""
     path = os.path.join(PROFILES, name)
     if not os.path.exists(path):
         return None
@@ -61,12 +62,12 @@ def read_counter_summary(name: str, src_hash: str):
     with open(path) as f:
         for line in f:
             m = re.match(r"^\s*-?\s*`?(\w+)`?\s*[:=]\s*`?([0-9a-fA-F.eE+-]+)`?\s*$", line)
-            if m:
+            if m and m.group(1) not in vals:
                 vals[m.group(1)] = m.group(2)
     if vals.get("kernel_source_sha256") != src_hash:
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals[key])
     except (KeyError, ValueError):
         return None
 
@@ -565,7 +566,11 @@ def main(argv=None):
             r = bench_wkv5(torch, rw, ec, reps=5)
             sec[ec.name] = {"ms": round(r["ms"], 4),
                             "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
-                            "algorithmic_TFLOPs": round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 2)}
+                            "algorithmic_TFLOPs": round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 2),
+                            "mfma_busy_pct": read_counter_summary(
+                                "wkv5_fwd_chunked_mfma_B4_T4096_H32_D64.md",
+                                kernel_source_hash(("wkv5.hip", "eagle_common.h", "wkv_device.h")),
+                                "mfma_busy_pct")}
         for key, bc, n_steps in (("backward", cfg, 100), ("backward-long", synth.CFG_WKV4_LONG, 3)):
             if key in want:
                 name = bc.name.replace("wkv4_fwd", "wkv4_bwd")
