@@ -44,6 +44,20 @@ constexpr int kCPad = 68;                // fp32 row length of the log-decay pre
 constexpr float kMaxDiagLog2 = 15.f;     // fast diagonal blocks need every |log2 w| <= this
 constexpr float kMinLog2Decay = -126.f;  // log2 w below this counts as this (2^-126: no memory)
 
+// Per-channel ratios of decay powers for a chunk whose decays all satisfy
+// |log2 w| <= 15: every power a product needs is then one power within 8
+// tokens of a block middle (finite in fp32) times one of these:
+//   2^(c_{16b+16} - c_{s+1}) = 2^(c_{16b+8} - c_{s+1}) g_blk[b],
+//   2^(c_64 - c_{s+1})       = 2^(c_{16b+16} - c_{s+1}) h_blk[b],
+//   2^(c_t - c_ref)          = 2^(c_t - c_{16q+8}) q_ref[q][m].
+// Ratios that no product uses (a reference after the block) may be inf.
+struct DecayTables {
+  float g_blk[4][kD];     // 2^(c_{16b+16} - c_{16b+8})
+  float h_blk[4][kD];     // 2^(c_64 - c_{16b+16})
+  float q_ref[4][4][kD];  // [q][m]: 2^(c_{16q+8} - c_ref), ref = 16m+16 (m < 3) or 0 (m = 3)
+  float cmid[4][kD];      // c_{16b+8}
+};
+
 template <int DV>
 struct alignas(16) LdsF {
   __bf16 rr[kL][kPad];   // r, raw [tau][i]
@@ -53,11 +67,7 @@ struct alignas(16) LdsF {
   __bf16 v[kL][kPad];    // v [sigma][j], DV columns
   __bf16 sp[DV][kPad];   // S^T [j][i]
   float c[kL + 1][kCPad];
-  // fast chunks only (decay_tables): per-channel ratios of decay powers
-  float g_blk[4][kD];     // 2^(c_{16b+16} - c_{16b+8})
-  float h_blk[4][kD];     // 2^(c_64 - c_{16b+16})
-  float q_ref[4][4][kD];  // [q][m]: 2^(c_{16q+8} - c_ref), ref = 16m+16 (m < 3) or 0 (m = 3)
-  float cmid[4][kD];      // c_{16b+8}
+  DecayTables tab;        // fast chunks only
   float beta[kL];
   float u[kD];  // 16-byte aligned: the members before it are multiples of 16 bytes
 };
@@ -89,7 +99,9 @@ __device__ __forceinline__ void load_w(ChunkW& x, int t0, int T, int H, int b, i
 // whether some |log2 w| exceeds the fast diagonal's range (block-wide).
 typedef float CTable[kL + 1][kCPad];
 
-__device__ __forceinline__ bool decay_prefix(const ChunkW& x, CTable& c) {
+// With `tab`, a fast chunk's ratio tables are filled from the same sums, by
+// the thread that owns (channel, block).
+__device__ __forceinline__ bool decay_prefix(const ChunkW& x, CTable& c, DecayTables* tab) {
   const int tid = threadIdx.x;
   const int tau = tid >> 2, d0 = 16 * (tid & 3);
   const float wv[16] = {x.a.x, x.a.y, x.a.z, x.a.w, x.b.x, x.b.y, x.b.z, x.b.w,
@@ -120,32 +132,31 @@ __device__ __forceinline__ bool decay_prefix(const ChunkW& x, CTable& c) {
   }
   c[ch][kD + sg] = acc;
   __syncthreads();
+  float tot[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) tot[j] = c[ch][kD + j];
   float off = 0.f;
-  for (int j = 0; j < sg; ++j) off += c[ch][kD + j];
+  for (int j = 0; j < sg; ++j) off += tot[j];
 #pragma unroll
   for (int j = 0; j < 16; ++j) c[16 * sg + j + 1][ch] = run[j] + off;
+  if (tab && !exact) {
+    // the same sums as the table entries c_{16b+8}, c_{16b+16}, c_64
+    float cend[4];  // c_{16m+16}
+    float om = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      cend[m] = om + tot[m];
+      om += tot[m];
+    }
+    const float cm = run[7] + off;
+    tab->cmid[sg][ch] = cm;
+    tab->g_blk[sg][ch] = exp2_fast(run[15] + off - cm);
+    tab->h_blk[sg][ch] = exp2_fast(cend[3] - (run[15] + off));
+#pragma unroll
+    for (int m = 0; m < 4; ++m) tab->q_ref[sg][m][ch] = exp2_fast(cm - (m < 3 ? cend[m] : 0.f));
+  }
   __syncthreads();
   return exact;
-}
-
-// For a chunk whose decays all satisfy |log2 w| <= 15, every power the
-// chunk needs is one power within 8 tokens of a block middle (finite in fp32)
-// times per-channel ratios, which are computed here once per chunk:
-//   2^(c_{16b+16} - c_{s+1}) = 2^(c_{16b+8} - c_{s+1}) g_blk[b],
-//   2^(c_64 - c_{s+1})       = 2^(c_{16b+16} - c_{s+1}) h_blk[b],
-//   2^(c_t - c_ref)          = 2^(c_t - c_{16q+8}) q_ref[q][m].
-// Ratios that no product uses (a reference after the block) may be inf.
-template <int DV>
-__device__ __forceinline__ void decay_tables(LdsF<DV>& s) {
-  const int tid = threadIdx.x;
-  const int i = tid & 63, bq = tid >> 6;
-  s.g_blk[bq][i] = exp2_fast(s.c[16 * bq + 16][i] - s.c[16 * bq + 8][i]);
-  s.h_blk[bq][i] = exp2_fast(s.c[kL][i] - s.c[16 * bq + 16][i]);
-  const float cm = s.c[16 * bq + 8][i];
-  s.cmid[bq][i] = cm;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) s.q_ref[bq][m][i] = exp2_fast(cm - s.c[m < 3 ? 16 * m + 16 : 0][i]);
-  __syncthreads();
 }
 
 // Scaled copies of one chunk into LDS (the decay prefix must be in place),
@@ -189,9 +200,9 @@ __device__ __forceinline__ void stage_chunk_f(const ChunkRegs& x, bool exact, Ld
   if (!exact) {
 #pragma unroll
     for (int e = 0; e < 16; e += 4) {
-      const float4 a = *reinterpret_cast<const float4*>(&s.cmid[blk][d0 + e]);
-      const float4 g4 = *reinterpret_cast<const float4*>(&s.g_blk[blk][d0 + e]);
-      const float4 h4 = *reinterpret_cast<const float4*>(&s.h_blk[blk][d0 + e]);
+      const float4 a = *reinterpret_cast<const float4*>(&s.tab.cmid[blk][d0 + e]);
+      const float4 g4 = *reinterpret_cast<const float4*>(&s.tab.g_blk[blk][d0 + e]);
+      const float4 h4 = *reinterpret_cast<const float4*>(&s.tab.h_blk[blk][d0 + e]);
       cm[e] = a.x;
       cm[e + 1] = a.y;
       cm[e + 2] = a.z;
@@ -344,8 +355,7 @@ __global__ __launch_bounds__(256, 2) void wkv6_fwd_chunked(
   load_w(wc, c_begin * kL, T, H, b, h, w);
   for (int c = c_begin; c < c_end; ++c) {
     const int t0 = c * kL;
-    const bool exact = decay_prefix(wc, s.c);
-    if (!exact) decay_tables(s);
+    const bool exact = decay_prefix(wc, s.c, &s.tab);
     stage_chunk_f(cur, exact, s);
     __syncthreads();
     if (c + 1 < c_end) {
@@ -376,14 +386,14 @@ __global__ __launch_bounds__(256, 2) void wkv6_fwd_chunked(
         };
         float ctl[8], cml[8], qb[8];  // qb: r 2^(c_tau - c_{16q+8})
         ld8(&s.c[tau_l][i0], ctl);
-        ld8(&s.cmid[q][i0], cml);
+        ld8(&s.tab.cmid[q][i0], cml);
 #pragma unroll
         for (int e = 0; e < 8; ++e) qb[e] = float(raw[e]) * exp2_fast(ctl[e] - cml[e]);
 #pragma unroll
         for (int nb = 0; nb < 3; ++nb)
           if (nb < q) {
             float qr[8];
-            ld8(&s.q_ref[q][nb][i0], qr);
+            ld8(&s.tab.q_ref[q][nb][i0], qr);
             bf16x8 bq;
 #pragma unroll
             for (int e = 0; e < 8; ++e) bq[e] = to_bf16(qb[e] * qr[e]);
@@ -391,7 +401,7 @@ __global__ __launch_bounds__(256, 2) void wkv6_fwd_chunked(
             acc[nb] = mfma(a, bq, acc[nb]);
           }
         float q0[8];
-        ld8(&s.q_ref[q][3][i0], q0);
+        ld8(&s.tab.q_ref[q][3][i0], q0);
         bf16x8 bq;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -534,7 +544,7 @@ __global__ __launch_bounds__(256) void wkv6_seg_state(int T, int H, int BH, int 
   load_chunk<DV, false>(cur, c_begin * kL, T, H, b, h, j0, nullptr, k, v);
   load_w(wc, c_begin * kL, T, H, b, h, w);
   for (int c = c_begin; c < c_end; ++c) {
-    decay_prefix(wc, s_c);
+    decay_prefix(wc, s_c, nullptr);
     const uint32_t kw[8] = {cur.k0.x, cur.k0.y, cur.k0.z, cur.k0.w,
                             cur.k1.x, cur.k1.y, cur.k1.z, cur.k1.w};
     float ce[16], ct[16];  // c_64 and this token's c_{tau+1}, 16-byte reads
