@@ -83,14 +83,16 @@ __device__ __forceinline__ void write_state(const StateIO& sio, const Hist (&h)[
 }
 
 // EMIT = false: publish the tiles' histories only (the backward's prefix
-// pass); no output rows, no state.
+// pass); no output rows, no state.  With `mids`, each tile also publishes the
+// inclusive history at its middle (after NW/2 waves), for a consumer tiled at
+// half the length.
 template <int CPL, int L, int NW, bool EMIT = true>
 __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
     int T, int C, int n_cblk, int groups, int n_tiles,
     const float* __restrict__ w, const float* __restrict__ u,
     const float* __restrict__ k, const float* __restrict__ v, float* __restrict__ y,
     uint32_t* __restrict__ hdr, uint64_t* __restrict__ counters, uint64_t* __restrict__ slots,
-    StateIO sio) {
+    StateIO sio, uint64_t* __restrict__ mids) {
   constexpr int W = 64 * CPL;        // channels per block
   constexpr int TILE = L * NW;       // tokens per tile
   constexpr int SLOT = 8 * W;        // words per (tile, block): agg A,B,kr,n then inc A,B,kr,n
@@ -283,6 +285,21 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
     }
 #pragma unroll
     for (int c = 0; c < CPL; ++c) s_pre.put(ch0 + c, pre[c]);
+    if (!EMIT && mids) {
+      uint64_t* q = mids + (size_t(tile) * groups + g) * (4 * W) + ch0;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        Hist mid = pre[c];
+        for (int i = 0; i < NW / 2; ++i) {
+          const int ni = max(0, min(L, T - (tile_t0 + i * L)));
+          mid = hist_concat(mid, s_sum[i].get(ch0 + c), float(ni), w2[c]);
+        }
+        tagged_store(q + 0 * W + c, mid.A, tag);
+        tagged_store(q + 1 * W + c, mid.Bd, tag);
+        tagged_store(q + 2 * W + c, mid.kr, tag);
+        tagged_store(q + 3 * W + c, mid.n, tag);
+      }
+    }
   }
   __syncthreads();
 
@@ -387,7 +404,7 @@ hipError_t launch_tiled(const Wkv4Plan& pl, int64_t T, int64_t C, const float* w
   const unsigned grid = unsigned(pl.n_tiles * pl.groups);
   hipLaunchKernelGGL((wkv4_fwd_tiled<CPL, L, NW>), dim3(grid), dim3(64 * NW), 0, stream,
                      int(T), int(C), int(pl.n_cblk), int(pl.groups), int(pl.n_tiles),
-                     w, u, k, v, y, hdr, counters, slots, sio);
+                     w, u, k, v, y, hdr, counters, slots, sio, nullptr);
   return hipGetLastError();
 }
 
@@ -441,17 +458,17 @@ bool wkv4_plan(int64_t B, int64_t T, int64_t C, Wkv4Plan* plan) {
 
 hipError_t wkv4_prefix_launch(const Wkv4Plan& pl, int64_t T, int64_t C, const float* w,
                               const float* u, const float* k, const float* v, void* ws,
-                              hipStream_t stream) {
-  if (pl.cpl != 1 || pl.L != 16 || pl.NW != 4) return hipErrorInvalidValue;
+                              void* mids, hipStream_t stream) {
+  if (pl.cpl != 1 || pl.L != 32 || pl.NW != 4) return hipErrorInvalidValue;
   char* base = static_cast<char*>(ws);
   uint32_t* hdr = reinterpret_cast<uint32_t*>(base);
   uint64_t* counters = reinterpret_cast<uint64_t*>(base + kWkv4HeaderBytes);
   uint64_t* slots = reinterpret_cast<uint64_t*>(base + pl.slots_offset);
   const unsigned grid = unsigned(pl.n_tiles * pl.groups);
   const StateIO none{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
-  hipLaunchKernelGGL((wkv4_fwd_tiled<1, 16, 4, false>), dim3(grid), dim3(256), 0, stream,
+  hipLaunchKernelGGL((wkv4_fwd_tiled<1, 32, 4, false>), dim3(grid), dim3(256), 0, stream,
                      int(T), int(C), int(pl.n_cblk), int(pl.groups), int(pl.n_tiles), w, u, k,
-                     v, nullptr, hdr, counters, slots, none);
+                     v, nullptr, hdr, counters, slots, none, static_cast<uint64_t*>(mids));
   return hipGetLastError();
 }
 

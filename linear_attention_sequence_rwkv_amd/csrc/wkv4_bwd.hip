@@ -16,12 +16,14 @@
 // g_t WKV_t with "keys" -log2 D_t, plus their age-weighted versions for gw.
 //
 // Three launches on one stream:
-//   1. the forward's tiled scan without its output pass publishes every
-//      tile's inclusive forward history in the workspace;
-//   2. wkv4_bwd_tiled: tiles are claimed from the last one backwards; each
-//      wave rescans its tokens forward from the published prefix to recover
-//      WKV_t, log2 D_t and p_{t,t} in registers, summarises its reverse
-//      history, and wave 0 publishes the tile's reverse aggregate and folds
+//   1. the forward's tiled scan without its output pass (128-token tiles)
+//      publishes every tile's inclusive forward history in the workspace,
+//      and the one after each tile's first 64 tokens;
+//   2. wkv4_bwd_tiled (64-token tiles): tiles are claimed from the last one
+//      backwards; each wave rescans its tokens forward from the published
+//      prefix to recover WKV_t, log2 D_t and p_{t,t} in registers, summarises
+//      its reverse history, and wave 0 publishes the tile's reverse aggregate
+//      and folds
 //      the later tiles' (deterministic look-back, as in the forward); every
 //      wave then runs the reverse scan, writing gk and gv and summing its
 //      lanes' gw and gu terms, which go to a per-(tile, sequence) slot;
@@ -117,6 +119,7 @@ __global__ __launch_bounds__(64 * NW) void wkv4_bwd_tiled(
     const float* __restrict__ k, const float* __restrict__ v, const float* __restrict__ gy,
     float* __restrict__ gk, float* __restrict__ gv,
     const uint64_t* __restrict__ fwd_slots,  // inclusive forward histories (launch 1)
+    const uint64_t* __restrict__ fwd_mids,   // and those after the first half of its tiles
     uint32_t* __restrict__ hdr, uint64_t* __restrict__ counters, uint64_t* __restrict__ slots,
     uint64_t* __restrict__ part_w, uint64_t* __restrict__ part_u) {
   constexpr int W = 64;
@@ -187,7 +190,13 @@ __global__ __launch_bounds__(64 * NW) void wkv4_bwd_tiled(
   {
     Hist h = hist_empty();
     if (tile > 0) {
-      const uint64_t* q = fwd_slots + (size_t(tile - 1) * groups + g) * FSLOT + 4 * W + ch;
+      // the prefix pass's tiles are twice as long: the history after this
+      // tile's predecessor p is the inclusive history of prefix tile p / 2
+      // (p odd) or the one after its first half (p even)
+      const int pk = tile - 1;
+      const uint64_t* q =
+          (pk & 1) ? fwd_slots + (size_t(pk >> 1) * groups + g) * FSLOT + 4 * W + ch
+                   : fwd_mids + (size_t(pk >> 1) * groups + g) * (4 * W) + ch;
       h = Hist{tag_val(q[0]), tag_val(q[W]), tag_val(q[2 * W]), tag_val(q[3 * W])};
     }
     for (int i = 0; i < wid; ++i) h = hist_concat(h, s_fsum[i].get(ch), float(L), w2);
@@ -411,17 +420,24 @@ constexpr int kBwdNW = 4;
 
 bool wkv4_backward_plan(int64_t B, int64_t T, int64_t C, Wkv4BwdPlan* plan) {
   Wkv4BwdPlan p;
-  if (!wkv4_plan_fixed(B, T, C, 1, kBwdL, kBwdNW, &p.fwd)) return false;
-  const int64_t n_tiles = p.fwd.n_tiles, groups = p.fwd.groups;
+  // The prefix pass streams k, v in the forward's 128-token tiles; the
+  // reverse pass holds six values per token and lane, so its tiles are half
+  // that long and read the prefix pass's mid-tile histories too.
+  if (!wkv4_plan_fixed(B, T, C, 1, 2 * kBwdL, kBwdNW, &p.fwd)) return false;
+  const int64_t groups = p.fwd.groups;
+  p.rev_tiles = (T + kBwdL * kBwdNW - 1) / (kBwdL * kBwdNW);
+  if (p.rev_tiles * groups >= (int64_t(1) << 31)) return false;
   // Both passes share the header and counters at the start (the prefix pass
   // leaves each counter primed with the reverse pass's tag); everything after
   // them holds tagged words only, so the layout of any later call of another
   // shape finds nothing but smaller tags wherever its counters land.
-  p.rev_slots_offset = (p.fwd.ws_bytes + 255) / 256 * 256;
+  p.mid_offset = (p.fwd.ws_bytes + 255) / 256 * 256;
+  const size_t mid_bytes = size_t(p.fwd.n_tiles) * size_t(groups) * 4 * 64 * sizeof(uint64_t);
+  p.rev_slots_offset = (p.mid_offset + mid_bytes + 255) / 256 * 256;
   const size_t rev_slot_bytes =
-      size_t(n_tiles) * size_t(groups) * 2 * kRevFields * 64 * sizeof(uint64_t);
+      size_t(p.rev_tiles) * size_t(groups) * 2 * kRevFields * 64 * sizeof(uint64_t);
   p.part_offset = (p.rev_slots_offset + rev_slot_bytes + 255) / 256 * 256;
-  p.part_rows = n_tiles * B;
+  p.part_rows = p.rev_tiles * B;
   const size_t part_bytes = size_t(p.part_rows) * size_t(C) * sizeof(uint64_t);
   p.ws_bytes = p.part_offset + 2 * ((part_bytes + 255) / 256 * 256);
   *plan = p;
@@ -434,8 +450,9 @@ hipError_t wkv4_backward_launch(const Wkv4BwdPlan& pl, int64_t B, int64_t T, int
                                 float* gk, float* gv, void* ws, hipStream_t stream) {
   (void)B;
   char* base = static_cast<char*>(ws);
-  // 1. forward prefixes of every tile
-  hipError_t e = wkv4_prefix_launch(pl.fwd, T, C, w, u, k, v, base, stream);
+  uint64_t* mids = reinterpret_cast<uint64_t*>(base + pl.mid_offset);
+  // 1. forward prefixes of every tile and half tile
+  hipError_t e = wkv4_prefix_launch(pl.fwd, T, C, w, u, k, v, base, mids, stream);
   if (e != hipSuccess) return e;
   // 2. reverse scan, on the same header and counters
   const uint64_t* fwd_slots = reinterpret_cast<const uint64_t*>(base + pl.fwd.slots_offset);
@@ -446,11 +463,11 @@ hipError_t wkv4_backward_launch(const Wkv4BwdPlan& pl, int64_t B, int64_t T, int
   const size_t part_bytes = size_t(pl.part_rows) * size_t(C) * sizeof(uint64_t);
   uint64_t* part_u =
       reinterpret_cast<uint64_t*>(base + pl.part_offset + (part_bytes + 255) / 256 * 256);
-  const unsigned grid = unsigned(pl.fwd.n_tiles * pl.fwd.groups);
+  const unsigned grid = unsigned(pl.rev_tiles * pl.fwd.groups);
   hipLaunchKernelGGL((wkv4_bwd_tiled<kBwdL, kBwdNW>), dim3(grid), dim3(64 * kBwdNW), 0, stream,
-                     int(T), int(C), int(pl.fwd.n_cblk), int(pl.fwd.groups),
-                     int(pl.fwd.n_tiles), w, u, k, v, gy, gk, gv, fwd_slots, hdr, counters,
-                     slots, part_w, part_u);
+                     int(T), int(C), int(pl.fwd.n_cblk), int(pl.fwd.groups), int(pl.rev_tiles),
+                     w, u, k, v, gy, gk, gv, fwd_slots, mids, hdr, counters, slots, part_w,
+                     part_u);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // 3. gw, gu

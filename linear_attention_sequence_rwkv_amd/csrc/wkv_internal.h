@@ -37,10 +37,12 @@ bool wkv4_plan(int64_t B, int64_t T, int64_t C, Wkv4Plan* plan);
 bool wkv4_plan_fixed(int64_t B, int64_t T, int64_t C, int cpl, int L, int NW, Wkv4Plan* plan);
 
 // The forward scan without output rows: publishes every tile's inclusive
-// history in the workspace (plan: one channel per lane, 16 x 4 tiles).
+// history in the workspace (plan: one channel per lane, 32 x 4 tiles) and,
+// in `mids` (tagged words, 4 x 64 per tile and channel block), the inclusive
+// history after the first 64 tokens of each tile.
 hipError_t wkv4_prefix_launch(const Wkv4Plan& plan, int64_t T, int64_t C, const float* w,
                               const float* u, const float* k, const float* v, void* ws,
-                              hipStream_t stream);
+                              void* mids, hipStream_t stream);
 
 // a/b/p_in: optional history before the first token; a/b/p_out: optional
 // state after the last token (both [B, C], step-API form; may be null).
@@ -64,10 +66,12 @@ hipError_t wkv4_step_launch(int64_t B, int64_t C, float* a, float* b, float* p,
 // fields, aggregate and inclusive, per tile and channel), then the gw and gu
 // partial sums per (tile, sequence, channel) as tagged words.
 struct Wkv4BwdPlan {
-  Wkv4Plan fwd;  // tiling shared by both passes
+  Wkv4Plan fwd;      // prefix pass: 128-token tiles
+  int64_t rev_tiles;  // reverse pass: 64-token tiles, same channel blocks
+  size_t mid_offset;  // the prefix pass's mid-tile histories
   size_t rev_slots_offset;
   size_t part_offset;
-  int64_t part_rows;  // n_tiles * B
+  int64_t part_rows;  // rev_tiles * B
   size_t ws_bytes;
 };
 
