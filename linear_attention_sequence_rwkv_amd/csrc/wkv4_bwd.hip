@@ -23,10 +23,10 @@
 //      backwards; each wave rescans its tokens forward from the published
 //      prefix to recover WKV_t, log2 D_t and p_{t,t} in registers, summarises
 //      its reverse history, and wave 0 publishes the tile's reverse aggregate
-//      and folds
-//      the later tiles' (deterministic look-back, as in the forward); every
-//      wave then runs the reverse scan, writing gk and gv and summing its
-//      lanes' gw and gu terms, which go to a per-(tile, sequence) slot;
+//      and folds the later tiles' (deterministic look-back, as in the
+//      forward); every wave then runs the reverse scan, writing gk and gv and
+//      summing its lanes' gw and gu terms, which go to a per-(tile, sequence)
+//      slot;
 //   3. wkv4_bwd_reduce sums those slots per channel in a fixed order.
 // Every result is deterministic: no float atomics, folds in chain order.
 #include "wkv4_scan.h"
