@@ -8,8 +8,9 @@
  *                  its recurrent form with states a_t, b_t.
  *   [RWKV-summary] "RWKV: Reinventing RNNs for the Transformer Era"
  *                  (flashpapers.ai summary), sec. 3 "The WKV Operator".
- *   [Eagle-Finch]  "RWKV-5 Eagle and RWKV-6 Finch" (ql.gl blog), section
- *                  "Eagle: extending vector memory to matrix memory".
+ *   [Eagle-Finch]  "RWKV-5 Eagle and RWKV-6 Finch" (ql.gl blog), sections
+ *                  "Eagle: extending vector memory to matrix memory" and
+ *                  "Finch: making the recurrence respond to the input".
  *
  * Common rules for every entry point:
  *   - Pointers named as device pointers are device memory of the current HIP
