@@ -11,9 +11,11 @@
 //   gk_i = sum_{t>=i} g_t p_{t,i} (v_i - WKV_t),
 //   gu   = sum_t g_t p_{t,t} (v_t - WKV_t),
 //   gw   = -sum_t sum_{i<t} (t-1-i) g_t p_{t,i} (v_i - WKV_t).
-// For i < t, p_{t,i} = 2^{k2_i} 2^{-(t-1-i) w2 - log2 D_t} (base-2 domain), so
-// the sums over t > i are reverse-time histories of the values g_t and
-// g_t WKV_t with "keys" -log2 D_t, plus their age-weighted versions for gw.
+// For i < t, p_{t,i} = 2^{k2_i} 2^{-(t-1-i) w2} / D_t (base-2 domain), so
+// the sums over t > i are reverse-time histories of the values g_t / D_t and
+// g_t WKV_t / D_t, plus their age-weighted versions for gw.  D_t is carried
+// as 2^{sc_t} den_t (den_t in [1, t+1]): the values g_t / den_t with "keys"
+// -sc_t.
 //
 // Three launches on one stream:
 //   1. the forward's tiled scan without its output pass (128-token tiles)
@@ -21,7 +23,7 @@
 //      and the one after each tile's first 64 tokens;
 //   2. wkv4_bwd_tiled (64-token tiles): tiles are claimed from the last one
 //      backwards; each wave rescans its tokens forward from the published
-//      prefix to recover WKV_t, log2 D_t and p_{t,t} in registers, summarises
+//      prefix to recover WKV_t, D_t and p_{t,t} in registers, summarises
 //      its reverse history, and wave 0 publishes the tile's reverse aggregate
 //      and folds the later tiles' (deterministic look-back, as in the
 //      forward); every wave then runs the reverse scan, writing gk and gv and
@@ -39,10 +41,10 @@ namespace {
 
 using namespace scan;
 
-// Sums over later tokens t of c_t 2^{-log2 D_t - (t-1-i) w2} for c_t = g_t
-// (G) and g_t WKV_t (H), and the same weighted by the age t-1-i (G1, H1),
-// seen from a position i.  The common scale is anchored as in Hist:
-// kr - n w2, kr the key (-log2 D) of the anchor term and n the decays since.
+// Sums over later tokens t of c_t 2^{-sc_t - (t-1-i) w2} for c_t = g_t / den_t
+// (G) and g_t WKV_t / den_t (H), and the same weighted by the age t-1-i (G1,
+// H1), seen from a position i.  The common scale is anchored as in Hist:
+// kr - n w2, kr the key (-sc) of the anchor term and n the decays since.
 struct RevHist {
   float G, H, G1, H1, kr, n;
 };
@@ -71,9 +73,13 @@ __device__ __forceinline__ RevHist rev_concat(const RevHist& y, const RevHist& x
 }
 
 // Forward read of token t fused with the push (as hist_read_push), also
-// returning log2 D_t and p_{t,t} = 2^{u2+k2-log2 D_t}.
+// returning D_t split as 2^{sc} * den (sc: the scale of the larger of the
+// history and the token's own term, which contributes exactly 1 to den),
+// 1 / den, and the own term's factor pe, so that p_{t,t} = pe / den.  The
+// reverse pass carries g_t / den with "key" sc: the sums over 1 / D_t
+// without a logarithm per token.
 __device__ __forceinline__ float read_push_ld(Hist& h, float k2, float v, float u2, float w2,
-                                              float& lg, float& ptt) {
+                                              float& sc, float& pe, float& rd) {
   const float base = fmaf(-h.n, w2, h.kr - k2);  // p - k2
   const float dr = base - u2;
   const float dp = base - w2;
@@ -83,8 +89,9 @@ __device__ __forceinline__ float read_push_ld(Hist& h, float k2, float v, float 
   const float num = kr_keep ? fmaf(er, v, h.A) : fmaf(er, h.A, v);
   const float den = kr_keep ? (h.Bd + er) : fmaf(er, h.Bd, 1.f);
   const float rden = rcp_fast(den);
-  lg = (kr_keep ? base + k2 : u2 + k2) + __builtin_amdgcn_logf(den);
-  ptt = (kr_keep ? er : 1.f) * rden;
+  sc = kr_keep ? base + k2 : u2 + k2;
+  pe = kr_keep ? er : 1.f;
+  rd = rden;
   const bool kp_keep = dp >= 0.f;
   h.A = kp_keep ? fmaf(ep, v, h.A) : fmaf(ep, h.A, v);
   h.Bd = kp_keep ? (h.Bd + ep) : fmaf(ep, h.Bd, 1.f);
@@ -205,12 +212,17 @@ __global__ __launch_bounds__(64 * NW) void wkv4_bwd_tiled(
       yy[s] = 0.f;
       ll[s] = 0.f;
       pp[s] = 0.f;
-      if (full || s < n) yy[s] = read_push_ld(h, kk[s][0], vv[s][0], u2, w2, ll[s], pp[s]);
+      if (full || s < n) {
+        float rd;
+        yy[s] = read_push_ld(h, kk[s][0], vv[s][0], u2, w2, ll[s], pp[s], rd);
+        gg[s] *= rd;  // g_t / den_t from here on
+      }
     }
   }
 
   // Reverse summary of this wave's tokens seen from position t0 - 1: token
-  // t0 + s has age s and key -log2 D.  Fixed reference: the largest term.
+  // t0 + s has age s, key -sc and value g / den.  Fixed reference: the
+  // largest exponent, so every factor is at most 1.
   {
     float P = kEmptyP;
 #pragma unroll
@@ -331,7 +343,7 @@ __global__ __launch_bounds__(64 * NW) void wkv4_bwd_tiled(
         store_row<1>(rgv, voff_out, uint32_t(s) * row_bytes, o_v);
         store_row<1>(rgk, voff_out, uint32_t(s) * row_bytes, o_k);
         // move the view to the token before: ages grow by one, then this
-        // token's own term (key -log2 D, age 0) joins
+        // token's own term (key -sc, value g / den, age 0) joins
         h.G1 += h.G;
         h.H1 += h.H;
         const float d = fmaf(-(h.n + 1.f), w2, h.kr + ll[s]);
