@@ -22,18 +22,23 @@
 //   * every wave rebuilds its starting history from the tile prefix and the
 //     summaries of the waves before it, rescans its tokens from registers and
 //     writes y.
-// Tiles of a channel block are claimed in order from that block's own
-// counter, so a workgroup only ever waits on workgroups that are already
-// running: every wait ends.  Every word the kernel writes to the workspace
-// carries the call's tag, the workspace epoch + 1, which the call that
-// completes advances; nothing is reset between calls whatever their shapes,
-// and launches replayed from a captured graph stay correct.
+// A wait must only ever be on a running workgroup.  When the device holds
+// every workgroup of the grid at once, tile t of a block is simply the
+// (t * blocks + block)-th workgroup; otherwise tiles of a channel block are
+// claimed in arrival order from that block's own counter (one atomic round
+// trip before the loads can start, about 0.8 us of a 20 us launch).  Every
+// word the kernel writes to the workspace carries the call's tag, the
+// workspace epoch + 1, which the call advances once all its workgroups have
+// read it; nothing is reset between calls whatever their shapes, and launches
+// replayed from a captured graph stay correct.
 #include "wkv4_scan.h"
 #include "wkv_device.h"
 #include "wkv_internal.h"
 
 #include <stdio.h>
 #include <stdlib.h>
+
+#include <mutex>
 
 
 namespace rwkv {
@@ -86,9 +91,15 @@ __device__ __forceinline__ void write_state(const StateIO& sio, const Hist (&h)[
 // pass); no output rows, no state.  With `mids`, each tile also publishes the
 // inclusive history at its middle (after NW/2 waves), for a consumer tiled at
 // half the length.
+//
+// in_order != 0 (EMIT only): the launch has checked that every workgroup of
+// the grid can be resident at once, so tiles follow the launch index; the
+// epoch advances when the last tile of every block has seen its prefix,
+// which every other tile's published words (carrying the tag it read) have
+// then reached.  in_order == 0: tiles are claimed in arrival order.
 template <int CPL, int L, int NW, bool EMIT = true>
 __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
-    int T, int C, int n_cblk, int groups, int n_tiles,
+    int T, int C, int n_cblk, int groups, int n_tiles, int in_order,
     const float* __restrict__ w, const float* __restrict__ u,
     const float* __restrict__ k, const float* __restrict__ v, float* __restrict__ y,
     uint32_t* __restrict__ hdr, uint64_t* __restrict__ counters, uint64_t* __restrict__ slots,
@@ -109,7 +120,12 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
   const int g = int(blockIdx.x) % groups;
   if (threadIdx.x == 0) {
     uint32_t tg;
-    s_tile = claim_tile(hdr, counters, g, n_tiles, groups, tg);
+    if (EMIT && in_order) {
+      tg = hdr_load(hdr, kHdrEpoch) + 1u;
+      s_tile = int(blockIdx.x) / groups;
+    } else {
+      s_tile = claim_tile(hdr, counters, g, n_tiles, groups, tg);
+    }
     s_tag = tg;
   }
   __syncthreads();
@@ -163,6 +179,9 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
   }
   __syncthreads();
 
+  // Blocks whose last tile has its prefix (in-order launches), as counted
+  // before this one; read at the end so the round trip overlaps pass 2.
+  uint32_t done_before = 0;
   // Tile prefix: wave 0 publishes the aggregate and looks back.
   if (wid == 0) {
     const int tile_n = min(TILE, T - tile_t0);
@@ -285,6 +304,8 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
     }
 #pragma unroll
     for (int c = 0; c < CPL; ++c) s_pre.put(ch0 + c, pre[c]);
+    if (EMIT && in_order && tile == n_tiles - 1 && lane == 0)
+      done_before = hdr_add(hdr, kHdrClaimed, 1u);
     if (!EMIT && mids) {
       uint64_t* q = mids + (size_t(tile) * groups + g) * (4 * W) + ch0;
 #pragma unroll
@@ -318,6 +339,12 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
       emit_rows<L, CPL, true>(ry, voff_out, row_bytes, n, hs, kk, vv, u2, w2);
     else
       emit_rows<L, CPL, false>(ry, voff_out, row_bytes, n, hs, kk, vv, u2, w2);
+  }
+  if (EMIT && in_order && wid == 0 && lane == 0 && tile == n_tiles - 1 &&
+      done_before == uint32_t(groups - 1)) {
+    // Every block is done reading the epoch: leave the header for the next call.
+    hdr_store(hdr, kHdrClaimed, 0u);
+    hdr_store(hdr, kHdrEpoch, tag);
   }
 }
 
@@ -401,6 +428,34 @@ constexpr Variant kVariants[] = {{4, 8, 8}, {4, 16, 4}, {4, 16, 8},
                                  {2, 16, 8}, {2, 32, 4}, {2, 16, 4},
                                  {1, 32, 8}, {1, 32, 4}, {1, 64, 1}, {1, 16, 4}};
 
+// Workgroups of `kern` (`block` threads, no dynamic LDS) that the current
+// device holds at once, cached per device; 0 if it cannot be determined.
+int64_t resident_workgroups(const void* kern, int block) {
+  constexpr int kMaxDev = 64;
+  struct Entry {
+    const void* kern;
+    int64_t n;
+  };
+  static std::mutex mu;
+  static Entry cache[kMaxDev][16] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (Entry& e : cache[dev]) {
+    if (e.kern == kern) return e.n;
+    if (e.kern == nullptr) {
+      int per_cu = 0, cus = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, block, 0) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+      e.kern = kern;
+      e.n = int64_t(per_cu) * cus;
+      return e.n;
+    }
+  }
+  return 0;
+}
+
 template <int CPL, int L, int NW>
 hipError_t launch_tiled(const Wkv4Plan& pl, int64_t T, int64_t C, const float* w,
                         const float* u, const float* k, const float* v, float* y, void* ws,
@@ -409,10 +464,12 @@ hipError_t launch_tiled(const Wkv4Plan& pl, int64_t T, int64_t C, const float* w
   uint32_t* hdr = reinterpret_cast<uint32_t*>(base);
   uint64_t* counters = reinterpret_cast<uint64_t*>(base + kWkv4HeaderBytes);
   uint64_t* slots = reinterpret_cast<uint64_t*>(base + pl.slots_offset);
-  const unsigned grid = unsigned(pl.n_tiles * pl.groups);
-  hipLaunchKernelGGL((wkv4_fwd_tiled<CPL, L, NW>), dim3(grid), dim3(64 * NW), 0, stream,
-                     int(T), int(C), int(pl.n_cblk), int(pl.groups), int(pl.n_tiles),
-                     w, u, k, v, y, hdr, counters, slots, sio, nullptr);
+  const int64_t grid = pl.n_tiles * pl.groups;
+  const void* kern = reinterpret_cast<const void*>(&wkv4_fwd_tiled<CPL, L, NW>);
+  const int in_order = grid <= resident_workgroups(kern, 64 * NW) ? 1 : 0;
+  hipLaunchKernelGGL((wkv4_fwd_tiled<CPL, L, NW>), dim3(unsigned(grid)), dim3(64 * NW), 0,
+                     stream, int(T), int(C), int(pl.n_cblk), int(pl.groups), int(pl.n_tiles),
+                     in_order, w, u, k, v, y, hdr, counters, slots, sio, nullptr);
   return hipGetLastError();
 }
 
@@ -475,8 +532,8 @@ hipError_t wkv4_prefix_launch(const Wkv4Plan& pl, int64_t T, int64_t C, const fl
   const unsigned grid = unsigned(pl.n_tiles * pl.groups);
   const StateIO none{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   hipLaunchKernelGGL((wkv4_fwd_tiled<1, 32, 4, false>), dim3(grid), dim3(256), 0, stream,
-                     int(T), int(C), int(pl.n_cblk), int(pl.groups), int(pl.n_tiles), w, u, k,
-                     v, nullptr, hdr, counters, slots, none, static_cast<uint64_t*>(mids));
+                     int(T), int(C), int(pl.n_cblk), int(pl.groups), int(pl.n_tiles), 0, w, u,
+                     k, v, nullptr, hdr, counters, slots, none, static_cast<uint64_t*>(mids));
   return hipGetLastError();
 }
 

@@ -151,6 +151,25 @@ def test_workspace_reuse_across_shapes():
         assert wkv4_scaled_err(gpu_forward(b), yb_ref, Sb) <= WKV4_TOL, i
 
 
+def test_in_order_and_claimed_launches_share_a_workspace():
+    """A grid the device holds at once takes tiles in launch order; a larger
+    one (here 32 tiles x 96 channel blocks) claims them in arrival order.
+    Both advance the same workspace epoch: alternate them on one workspace."""
+    torch, dev = torch_dev()
+    shapes = [(2, 900, 96), (4, 4096, 1536)]
+    cases = [synth.wkv4_inputs(B, T, C, seed=90 + i) for i, (B, T, C) in enumerate(shapes)]
+    refs = [oracle_forward(inp) for inp in cases]
+    need = max(rw.rwkv_wkv4_forward_workspace(*shp) for shp in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    bufs = [{n: to_dev(inp[n]) for n in ("w", "u", "k", "v")} for inp in cases]
+    for rnd in range(3):
+        for shp, bf, (y_ref, S) in zip(shapes, bufs, refs):
+            log(f"wkv4_forward shared workspace round {rnd} shape {shp}")
+            y = rw.rwkv_wkv4_forward(bf["w"], bf["u"], bf["k"], bf["v"], ws=ws)
+            torch.cuda.synchronize()
+            assert wkv4_scaled_err(y.cpu().numpy(), y_ref, S) <= WKV4_TOL, (rnd, shp)
+
+
 def test_workspace_layout_changes():
     """Regression: one workspace serves calls whose channel-block counts grow
     and shrink, so earlier calls' words sit where later calls keep their
