@@ -47,103 +47,19 @@ namespace {
 
 using namespace scan;
 
-// Output pass of a full wave in blocks of kBlk tokens.  Within a block,
-// multiplying the history before local token t by 2^{t w2} makes every term
-// time-independent: token i enters with exponent k2_i + (i+1) w2 and the
-// history with its scale p_h.  Measured from the block's middle token a
-// (anchor), token i sits at x_i = (k2_i - k2_a) + (i-a) w2 and the history at
-// D = p_h - k2_a - (a+1) w2, each formed with one rounding at the size of
-// the difference (at most about 4 w2 apart for terms that matter together).
-// The frame is the larger of the anchor and the history; every read and push
-// of the block then costs a single exp2 (the bonus term is the token's own
-// term times 2^{u2 - w2}), where the exact update needs two plus the anchor
-// bookkeeping.  The block leaves the history in anchor form: (k2_a,
-// kBlk-1-a decays) if the anchor was the frame, else the history's own
-// anchor plus kBlk decays; the denominator stays >= 1.
-// A block whose terms could leave the float range takes the exact update:
-// some lane with its history more than 2^{kBlkBelow} under the frame (the
-// empty history of a sequence's first block; a key jump of ~100 log2 units),
-// a token more than 2^{kBlkAbove} over it, or u2 - w2 > 40.  Ragged waves
-// take the exact update throughout.
-constexpr int kBlk = 8;
-constexpr int kBlkAnchor = kBlk / 2 - 1;
-constexpr float kBlkBelow = 100.f;
-constexpr float kBlkAbove = 80.f;
-
+// Output pass of a full wave: the blocked rescan, each token's y stored as
+// it is produced.
 template <int L, int CPL>
 __device__ __forceinline__ void emit_rows_blocked(Rsrc ry, uint32_t voff, uint32_t row_bytes,
                                                   Hist (&hs)[CPL], const float (&kk)[L][CPL],
                                                   const float (&vv)[L][CPL],
                                                   const float (&u2)[CPL],
                                                   const float (&w2)[CPL]) {
-  static_assert(L % kBlk == 0, "whole blocks");
-  float cb[CPL];
-  bool lane_ok = true;
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    cb[c] = exp2_fast(u2[c] - w2[c]);
-    lane_ok = lane_ok && u2[c] - w2[c] <= 40.f;
-  }
-#pragma unroll
-  for (int j = 0; j < L / kBlk; ++j) {
-    constexpr int a = kBlkAnchor;
-    float x[kBlk][CPL], D[CPL], Dp[CPL];
-    bool ok = lane_ok;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const float ka = kk[j * kBlk + a][c];
-      float mx = 0.f;  // x_a
-#pragma unroll
-      for (int i = 0; i < kBlk; ++i) {
-        x[i][c] = fmaf(float(i - a), w2[c], kk[j * kBlk + i][c] - ka);
-        mx = fmaxf(mx, x[i][c]);
-      }
-      D[c] = fmaf(-(hs[c].n + float(a + 1)), w2[c], hs[c].kr - ka);
-      Dp[c] = fmaxf(D[c], 0.f);
-      ok = ok && D[c] >= -kBlkBelow && mx - Dp[c] <= kBlkAbove;
-    }
-    if (__all(ok)) {
-      float A[CPL], B[CPL];
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const float sh = exp2_fast(fminf(D[c], 0.f));
-        A[c] = hs[c].A * sh;
-        B[c] = hs[c].Bd * sh;
-      }
-#pragma unroll
-      for (int i = 0; i < kBlk; ++i) {
-        float ys[CPL];
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          const float e = exp2_fast(x[i][c] - Dp[c]);
-          const float eb = e * cb[c];
-          const float num = fmaf(eb, vv[j * kBlk + i][c], A[c]);
-          const float den = B[c] + eb;
-          ys[c] = num * rcp_fast(den);
-          A[c] = fmaf(e, vv[j * kBlk + i][c], A[c]);
-          B[c] += e;
-        }
-        store_row<CPL>(ry, voff, uint32_t(j * kBlk + i) * row_bytes, ys);
-      }
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const bool hist_frame = D[c] >= 0.f;
-        hs[c].A = A[c];
-        hs[c].Bd = B[c];
-        hs[c].kr = hist_frame ? hs[c].kr : kk[j * kBlk + a][c];
-        hs[c].n = hist_frame ? hs[c].n + float(kBlk) : float(kBlk - 1 - a);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kBlk; ++i) {
-        float ys[CPL];
-#pragma unroll
-        for (int c = 0; c < CPL; ++c)
-          ys[c] = hist_read_push(hs[c], kk[j * kBlk + i][c], vv[j * kBlk + i][c], u2[c], w2[c]);
-        store_row<CPL>(ry, voff, uint32_t(j * kBlk + i) * row_bytes, ys);
-      }
-    }
-  }
+  rescan_blocked<L, CPL>(hs, kk, vv, u2, w2,
+                         [&](int s, const float (&y)[CPL], const float (&)[CPL],
+                             const float (&)[CPL], const float (&)[CPL]) {
+                           store_row<CPL>(ry, voff, uint32_t(s) * row_bytes, y);
+                         });
 }
 
 template <int L, int CPL, bool FULL>

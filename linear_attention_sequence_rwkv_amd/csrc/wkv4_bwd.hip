@@ -72,34 +72,6 @@ __device__ __forceinline__ RevHist rev_concat(const RevHist& y, const RevHist& x
   return r;
 }
 
-// Forward read of token t fused with the push (as hist_read_push), also
-// returning D_t split as 2^{sc} * den (sc: the scale of the larger of the
-// history and the token's own term, which contributes exactly 1 to den),
-// 1 / den, and the own term's factor pe, so that p_{t,t} = pe / den.  The
-// reverse pass carries g_t / den with "key" sc: the sums over 1 / D_t
-// without a logarithm per token.
-__device__ __forceinline__ float read_push_ld(Hist& h, float k2, float v, float u2, float w2,
-                                              float& sc, float& pe, float& rd) {
-  const float base = fmaf(-h.n, w2, h.kr - k2);  // p - k2
-  const float dr = base - u2;
-  const float dp = base - w2;
-  const float er = exp2_fast(-fabsf(dr));
-  const float ep = exp2_fast(-fabsf(dp));
-  const bool kr_keep = dr >= 0.f;
-  const float num = kr_keep ? fmaf(er, v, h.A) : fmaf(er, h.A, v);
-  const float den = kr_keep ? (h.Bd + er) : fmaf(er, h.Bd, 1.f);
-  const float rden = rcp_fast(den);
-  sc = kr_keep ? base + k2 : u2 + k2;
-  pe = kr_keep ? er : 1.f;
-  rd = rden;
-  const bool kp_keep = dp >= 0.f;
-  h.A = kp_keep ? fmaf(ep, v, h.A) : fmaf(ep, h.A, v);
-  h.Bd = kp_keep ? (h.Bd + ep) : fmaf(ep, h.Bd, 1.f);
-  h.kr = kp_keep ? h.kr : k2;
-  h.n = kp_keep ? (h.n + 1.f) : 0.f;
-  return num * rden;
-}
-
 template <int W>
 struct RevLds {
   float f[6][W];
@@ -207,15 +179,28 @@ __global__ __launch_bounds__(64 * NW) void wkv4_bwd_tiled(
       h = Hist{tag_val(q[0]), tag_val(q[W]), tag_val(q[2 * W]), tag_val(q[3 * W])};
     }
     for (int i = 0; i < wid; ++i) h = hist_concat(h, s_fsum[i].get(ch), float(L), w2);
+    if (full) {
+      Hist hs[1] = {h};
+      const float u2a[1] = {u2}, w2a[1] = {w2};
+      rescan_blocked<L, 1>(hs, kk, vv, u2a, w2a,
+                           [&](int s, const float (&y)[1], const float (&sc)[1],
+                               const float (&pe)[1], const float (&rd)[1]) {
+                             yy[s] = y[0];
+                             ll[s] = sc[0];
+                             pp[s] = pe[0];
+                             gg[s] *= rd[0];  // g_t / den_t from here on
+                           });
+    } else {
 #pragma unroll
-    for (int s = 0; s < L; ++s) {
-      yy[s] = 0.f;
-      ll[s] = 0.f;
-      pp[s] = 0.f;
-      if (full || s < n) {
-        float rd;
-        yy[s] = read_push_ld(h, kk[s][0], vv[s][0], u2, w2, ll[s], pp[s], rd);
-        gg[s] *= rd;  // g_t / den_t from here on
+      for (int s = 0; s < L; ++s) {
+        yy[s] = 0.f;
+        ll[s] = 0.f;
+        pp[s] = 0.f;
+        if (s < n) {
+          float rd;
+          yy[s] = read_push_ld(h, kk[s][0], vv[s][0], u2, w2, ll[s], pp[s], rd);
+          gg[s] *= rd;  // g_t / den_t from here on
+        }
       }
     }
   }

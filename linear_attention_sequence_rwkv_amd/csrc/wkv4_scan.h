@@ -118,6 +118,140 @@ __device__ __forceinline__ Hist summarize(const float (&kk)[L][CPL], const float
   return n > 0 ? Hist{A, Bd, P, 0.f} : hist_empty();
 }
 
+// Forward read of token t fused with the push (as hist_read_push), also
+// returning D_t split as 2^{sc} * den (sc: the scale of the larger of the
+// history and the token's own term, which contributes exactly 1 to den),
+// 1 / den, and the own term's factor pe, so that p_{t,t} = pe / den.  The
+// reverse pass carries g_t / den with "key" sc: the sums over 1 / D_t
+// without a logarithm per token.
+__device__ __forceinline__ float read_push_ld(Hist& h, float k2, float v, float u2, float w2,
+                                              float& sc, float& pe, float& rd) {
+  const float base = fmaf(-h.n, w2, h.kr - k2);  // p - k2
+  const float dr = base - u2;
+  const float dp = base - w2;
+  const float er = exp2_fast(-fabsf(dr));
+  const float ep = exp2_fast(-fabsf(dp));
+  const bool kr_keep = dr >= 0.f;
+  const float num = kr_keep ? fmaf(er, v, h.A) : fmaf(er, h.A, v);
+  const float den = kr_keep ? (h.Bd + er) : fmaf(er, h.Bd, 1.f);
+  const float rden = rcp_fast(den);
+  sc = kr_keep ? base + k2 : u2 + k2;
+  pe = kr_keep ? er : 1.f;
+  rd = rden;
+  const bool kp_keep = dp >= 0.f;
+  h.A = kp_keep ? fmaf(ep, v, h.A) : fmaf(ep, h.A, v);
+  h.Bd = kp_keep ? (h.Bd + ep) : fmaf(ep, h.Bd, 1.f);
+  h.kr = kp_keep ? h.kr : k2;
+  h.n = kp_keep ? (h.n + 1.f) : 0.f;
+  return num * rden;
+}
+
+// Rescan of a full wave from its starting history hs, in blocks of kBlk
+// tokens, calling emit(s, y, sc, pe, rden) for every token s with, per
+// channel, y = WKV_s, and D_s = 2^{sc} / rden split as in read_push_ld with
+// own-term factor pe (p_{s,s} = pe * rden).
+//
+// Within a block, multiplying the history before local token t by 2^{t w2}
+// makes every term time-independent: token i enters with exponent
+// k2_i + (i+1) w2 and the history with its scale p_h.  Measured from the
+// block's middle token a (anchor), token i sits at x_i = (k2_i - k2_a) +
+// (i-a) w2 and the history at D = p_h - k2_a - (a+1) w2, each formed with one
+// rounding at the size of the difference (at most about 4 w2 apart for terms
+// that matter together).  The frame is the larger of the anchor and the
+// history; every read and push of the block then costs a single exp2 (the
+// bonus term is the token's own term times 2^{u2 - w2}), where the exact
+// update needs two plus the anchor bookkeeping.  The block leaves the
+// history in anchor form: (k2_a, kBlk-1-a decays) if the anchor was the
+// frame, else the history's own anchor plus kBlk decays; the denominator
+// stays >= 1.  A block whose terms could leave the float range takes the
+// exact update: some lane with its history more than 2^{kBlkBelow} under the
+// frame (the empty history of a sequence's first block; a key jump of ~100
+// log2 units), a token more than 2^{kBlkAbove} over it, or u2 - w2 > 40.
+constexpr int kBlk = 8;
+constexpr int kBlkAnchor = kBlk / 2 - 1;
+constexpr float kBlkBelow = 100.f;
+constexpr float kBlkAbove = 80.f;
+
+template <int L, int CPL, class Emit>
+__device__ __forceinline__ void rescan_blocked(Hist (&hs)[CPL], const float (&kk)[L][CPL],
+                                               const float (&vv)[L][CPL],
+                                               const float (&u2)[CPL],
+                                               const float (&w2)[CPL], Emit&& emit) {
+  static_assert(L % kBlk == 0, "whole blocks");
+  float cb[CPL];
+  bool lane_ok = true;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    cb[c] = exp2_fast(u2[c] - w2[c]);
+    lane_ok = lane_ok && u2[c] - w2[c] <= 40.f;
+  }
+#pragma unroll
+  for (int j = 0; j < L / kBlk; ++j) {
+    constexpr int a = kBlkAnchor;
+    float x[kBlk][CPL], D[CPL], Dp[CPL];
+    bool ok = lane_ok;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const float ka = kk[j * kBlk + a][c];
+      float mx = 0.f;  // x_a
+#pragma unroll
+      for (int i = 0; i < kBlk; ++i) {
+        x[i][c] = fmaf(float(i - a), w2[c], kk[j * kBlk + i][c] - ka);
+        mx = fmaxf(mx, x[i][c]);
+      }
+      D[c] = fmaf(-(hs[c].n + float(a + 1)), w2[c], hs[c].kr - ka);  // p_h - k2_a - (a+1) w2
+      Dp[c] = fmaxf(D[c], 0.f);
+      ok = ok && D[c] >= -kBlkBelow && mx - Dp[c] <= kBlkAbove;
+    }
+    if (__all(ok)) {
+      float A[CPL], B[CPL], f0[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const float sh = exp2_fast(fminf(D[c], 0.f));
+        A[c] = hs[c].A * sh;
+        B[c] = hs[c].Bd * sh;
+        f0[c] = kk[j * kBlk + a][c] + Dp[c];  // frame exponent less (a+1) w2
+      }
+#pragma unroll
+      for (int i = 0; i < kBlk; ++i) {
+        float y[CPL], sc[CPL], pe[CPL], rd[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const float e = exp2_fast(x[i][c] - Dp[c]);
+          const float eb = e * cb[c];
+          const float num = fmaf(eb, vv[j * kBlk + i][c], A[c]);
+          const float den = B[c] + eb;
+          rd[c] = rcp_fast(den);
+          y[c] = num * rd[c];
+          sc[c] = fmaf(float(a + 1 - i), w2[c], f0[c]);  // D_i = den 2^{sc}
+          pe[c] = eb;
+          A[c] = fmaf(e, vv[j * kBlk + i][c], A[c]);
+          B[c] += e;
+        }
+        emit(j * kBlk + i, y, sc, pe, rd);
+      }
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const bool hist_frame = D[c] >= 0.f;
+        hs[c].A = A[c];
+        hs[c].Bd = B[c];
+        hs[c].kr = hist_frame ? hs[c].kr : kk[j * kBlk + a][c];
+        hs[c].n = hist_frame ? hs[c].n + float(kBlk) : float(kBlk - 1 - a);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kBlk; ++i) {
+        float y[CPL], sc[CPL], pe[CPL], rd[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+          y[c] = read_push_ld(hs[c], kk[j * kBlk + i][c], vv[j * kBlk + i][c], u2[c], w2[c],
+                              sc[c], pe[c], rd[c]);
+        emit(j * kBlk + i, y, sc, pe, rd);
+      }
+    }
+  }
+}
+
 // Loads of a wave's rows (FULL: all L of them, else the first n; the rest
 // are zero) and its second pass, specialised so that a full wave carries no
 // per-row checks.
