@@ -133,24 +133,25 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = int(blockIdx.x) % groups;
-  if (threadIdx.x == 0) {
-    uint32_t tg;
-    if (EMIT && in_order) {
-      tg = hdr_load(hdr, kHdrEpoch) + 1u;
-      s_tile = int(blockIdx.x) / groups;
-    } else {
+  int tile;
+  if (EMIT && in_order) {
+    // The tile is known at once, so the loads need not wait for anything;
+    // the tag is read after they are issued (below).
+    tile = int(blockIdx.x) / groups;
+  } else {
+    if (threadIdx.x == 0) {
+      uint32_t tg;
       s_tile = claim_tile(hdr, counters, g, n_tiles, groups, tg);
+      s_tag = tg;
     }
-    s_tag = tg;
-  }
-  __syncthreads();
-  const int tile = __builtin_amdgcn_readfirstlane(s_tile);
-  const uint32_t tag = __builtin_amdgcn_readfirstlane(s_tag);
-  // Only a workspace that was never zero-filled can get here: flag it and
-  // touch nothing.
-  if (tile < 0 || tile >= n_tiles) {
-    if (threadIdx.x == 0) raise_error(hdr + kHdrError, 2u);
-    return;
+    __syncthreads();
+    tile = __builtin_amdgcn_readfirstlane(s_tile);
+    // Only a workspace that was never zero-filled can get here: flag it and
+    // touch nothing.
+    if (tile < 0 || tile >= n_tiles) {
+      if (threadIdx.x == 0) raise_error(hdr + kHdrError, 2u);
+      return;
+    }
   }
   const int bi = g / n_cblk;
   const int cb = g - bi * n_cblk;
@@ -181,6 +182,7 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
     load_rows<L, CPL, true>(rk, rv, voff_in, row_bytes, n, kk, vv);
   else
     load_rows<L, CPL, false>(rk, rv, voff_in, row_bytes, n, kk, vv);
+  if (EMIT && in_order && threadIdx.x == 0) s_tag = hdr_load(hdr, kHdrEpoch) + 1u;
 
   // Pass 1: this wave's tokens from an empty history.
   if (full) {
@@ -193,6 +195,7 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
       s_sum[wid].put(ch0 + c, summarize<L, CPL, false>(kk, vv, c, n, w2[c]));
   }
   __syncthreads();
+  const uint32_t tag = __builtin_amdgcn_readfirstlane(s_tag);
 
   // Blocks whose last tile has its prefix (in-order launches), as counted
   // before this one; read at the end so the round trip overlaps pass 2.
