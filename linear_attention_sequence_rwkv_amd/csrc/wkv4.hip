@@ -107,11 +107,12 @@ __device__ __forceinline__ void write_state(const StateIO& sio, const Hist (&h)[
 // inclusive history at its middle (after NW/2 waves), for a consumer tiled at
 // half the length.
 //
-// in_order != 0 (EMIT only): the launch has checked that every workgroup of
-// the grid can be resident at once, so tiles follow the launch index; the
-// epoch advances when the last tile of every block has seen its prefix,
-// which every other tile's published words (carrying the tag it read) have
-// then reached.  in_order == 0: tiles are claimed in arrival order.
+// in_order != 0: the launch has checked that every workgroup of the grid can
+// be resident at once, so tiles follow the launch index; the epoch advances
+// when the last tile of every block has seen its prefix, which every other
+// tile's published words (carrying the tag it read) have then reached, and
+// that tile leaves its block's counter primed for a next call that claims.
+// in_order == 0: tiles are claimed in arrival order.
 template <int CPL, int L, int NW, bool EMIT = true>
 __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
     int T, int C, int n_cblk, int groups, int n_tiles, int in_order,
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = int(blockIdx.x) % groups;
   int tile;
-  if (EMIT && in_order) {
+  if (in_order) {
     // The tile is known at once, so the loads need not wait for anything;
     // the tag is read after they are issued (below).
     tile = int(blockIdx.x) / groups;
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
     load_rows<L, CPL, true>(rk, rv, voff_in, row_bytes, n, kk, vv);
   else
     load_rows<L, CPL, false>(rk, rv, voff_in, row_bytes, n, kk, vv);
-  if (EMIT && in_order && threadIdx.x == 0) s_tag = hdr_load(hdr, kHdrEpoch) + 1u;
+  if (in_order && threadIdx.x == 0) s_tag = hdr_load(hdr, kHdrEpoch) + 1u;
 
   // Pass 1: this wave's tokens from an empty history.
   if (full) {
@@ -322,8 +323,11 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
     }
 #pragma unroll
     for (int c = 0; c < CPL; ++c) s_pre.put(ch0 + c, pre[c]);
-    if (EMIT && in_order && tile == n_tiles - 1 && lane == 0)
+    if (in_order && tile == n_tiles - 1 && lane == 0) {
+      __hip_atomic_store(counters + size_t(g) * (kWkv4CounterStride / sizeof(uint64_t)),
+                         uint64_t(tag + 1u) << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       done_before = hdr_add(hdr, kHdrClaimed, 1u);
+    }
     if (!EMIT && mids) {
       uint64_t* q = mids + (size_t(tile) * groups + g) * (4 * W) + ch0;
 #pragma unroll
@@ -358,7 +362,7 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
     else
       emit_rows<L, CPL, false>(ry, voff_out, row_bytes, n, hs, kk, vv, u2, w2);
   }
-  if (EMIT && in_order && wid == 0 && lane == 0 && tile == n_tiles - 1 &&
+  if (in_order && wid == 0 && lane == 0 && tile == n_tiles - 1 &&
       done_before == uint32_t(groups - 1)) {
     // Every block is done reading the epoch: leave the header for the next call.
     hdr_store(hdr, kHdrClaimed, 0u);
@@ -547,11 +551,14 @@ hipError_t wkv4_prefix_launch(const Wkv4Plan& pl, int64_t T, int64_t C, const fl
   uint32_t* hdr = reinterpret_cast<uint32_t*>(base);
   uint64_t* counters = reinterpret_cast<uint64_t*>(base + kWkv4HeaderBytes);
   uint64_t* slots = reinterpret_cast<uint64_t*>(base + pl.slots_offset);
-  const unsigned grid = unsigned(pl.n_tiles * pl.groups);
+  const int64_t grid = pl.n_tiles * pl.groups;
   const StateIO none{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
-  hipLaunchKernelGGL((wkv4_fwd_tiled<1, 32, 4, false>), dim3(grid), dim3(256), 0, stream,
-                     int(T), int(C), int(pl.n_cblk), int(pl.groups), int(pl.n_tiles), 0, w, u,
-                     k, v, nullptr, hdr, counters, slots, none, static_cast<uint64_t*>(mids));
+  const void* kern = reinterpret_cast<const void*>(&wkv4_fwd_tiled<1, 32, 4, false>);
+  const int in_order = grid <= resident_workgroups(kern, 256) ? 1 : 0;
+  hipLaunchKernelGGL((wkv4_fwd_tiled<1, 32, 4, false>), dim3(unsigned(grid)), dim3(256), 0,
+                     stream, int(T), int(C), int(pl.n_cblk), int(pl.groups), int(pl.n_tiles),
+                     in_order, w, u, k, v, nullptr, hdr, counters, slots, none,
+                     static_cast<uint64_t*>(mids));
   return hipGetLastError();
 }
 

@@ -122,3 +122,18 @@ def test_workspace_layout_changes():
                     (4, 2048, 64)):
         log(f"wkv4_backward B={B} T={T} C={C} (shared workspace)")
         check(synth.wkv4_backward_inputs(B, T, C, seed=T + C))
+
+
+def test_claimed_and_in_order_prefix_passes_share_a_workspace():
+    """The prefix pass takes its tiles in launch order when its grid is
+    resident at once (then primes the reverse pass's counters itself) and
+    claims them otherwise (1 x 16384 x 4096: 8192 tiles); alternate the two
+    on the cached workspace."""
+    big = synth.wkv4_backward_inputs(1, 16384, 4096, seed=11)
+    small = synth.wkv4_backward_inputs(2, 1000, 200, seed=12)
+    ch = np.arange(0, 4096, 128)
+    for rnd in range(2):
+        log(f"wkv4_backward claimed prefix pass round {rnd} (sampled channels)")
+        check(big, ch)
+        log(f"wkv4_backward in-order prefix pass round {rnd}")
+        check(small)
