@@ -195,6 +195,16 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
     for (int c = 0; c < CPL; ++c)
       s_sum[wid].put(ch0 + c, summarize<L, CPL, false>(kk, vv, c, n, w2[c]));
   }
+  // Launch-order tiles: wave 0's first poll goes out before the barrier, so
+  // its round trip overlaps the wait for the other waves' summaries
+  // (8x1024x768: 17.4 -> 17.0 us; with claimed tiles, which arrive in a
+  // stream of many generations, it measured 2% slower and is not used).
+  uint64_t e_inc = 0, e_agg = 0;
+  if (in_order && wid == 0 && tile > 0 && lane < kWin && tile - 1 - lane >= 0) {
+    const uint64_t* sp = slots + (size_t(tile - 1 - lane) * groups + g) * SLOT;
+    e_inc = tagged_load(sp + 4 * W);
+    if (tile - 1 - lane > 0) e_agg = tagged_load(sp);  // tile 0 has no aggregate
+  }
   __syncthreads();
   const uint32_t tag = __builtin_amdgcn_readfirstlane(s_tag);
 
@@ -248,12 +258,17 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
       // timing offers: the forward is deterministic.
       Hist acc[CPL];
       uint32_t spins = 0;
+      bool early = in_order != 0;  // the first poll's words are already in
       for (;;) {
         // Poll kWin earlier tiles in one round trip: lane i reads the first
         // word of tile (tile-1-i)'s inclusive and aggregate histories.
         const int pi = tile - 1 - lane;
         bool inc_ok = false, agg_ok = false;
-        if (lane < kWin && pi >= 0) {
+        if (early) {
+          inc_ok = lane < kWin && pi >= 0 && tag_ok(e_inc, tag);
+          agg_ok = lane < kWin && pi > 0 && tag_ok(e_agg, tag);
+          early = false;
+        } else if (lane < kWin && pi >= 0) {
           const uint64_t* sp = slots + (size_t(pi) * groups + g) * SLOT;
           inc_ok = tag_ok(tagged_load(sp + 4 * W), tag);
           agg_ok = pi > 0 && tag_ok(tagged_load(sp), tag);  // tile 0 has no aggregate
