@@ -20,13 +20,15 @@
 //     look-back, 16 tiles polled per round trip): aggregates are folded in
 //     until an earlier tile's inclusive history ends the walk;
 //   * every wave rebuilds its starting history from the tile prefix and the
-//     summaries of the waves before it, rescans its tokens from registers and
-//     writes y.
+//     summaries of the waves before it, rescans its tokens from registers in
+//     8-token blocks with one exp2 per token (rescan_blocked) and writes y.
 // A wait must only ever be on a running workgroup.  When the device holds
 // every workgroup of the grid at once, tile t of a block is simply the
-// (t * blocks + block)-th workgroup; otherwise tiles of a channel block are
-// claimed in arrival order from that block's own counter (one atomic round
-// trip before the loads can start, about 0.8 us of a 20 us launch).  Every
+// (t * blocks + block)-th workgroup, whose loads go out before anything else
+// (the epoch is read after them, and wave 0's first look-back poll before the
+// summaries' barrier); otherwise tiles of a channel block are claimed in
+// arrival order from that block's own counter (one atomic round trip before
+// the loads can start, about 0.8 us of a 17 us launch).  Every
 // word the kernel writes to the workspace carries the call's tag, the
 // workspace epoch + 1, which the call advances once all its workgroups have
 // read it; nothing is reset between calls whatever their shapes, and launches
