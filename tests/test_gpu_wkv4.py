@@ -184,6 +184,28 @@ def test_in_order_and_claimed_launches_share_a_workspace():
             assert wkv4_scaled_err(y.cpu().numpy(), y_ref, S) <= WKV4_TOL, (rnd, shp)
 
 
+@pytest.mark.parametrize("cfg_name", ["169m", "tiny"])
+def test_launch_order_and_claimed_tiles_give_the_same_bits(cfg_name):
+    """Tiles taken in launch order (the whole grid resident) and claimed in
+    arrival order fold the same histories in the same chain order: the outputs
+    must agree bit for bit (RWKV_WKV4_ORDER=claim forces claims)."""
+    torch, _ = torch_dev()
+    cfg = synth.CFG_WKV4_169M if cfg_name == "169m" else synth.CFG_WKV4_TINY
+    inp = synth.wkv4_inputs_for(cfg)
+    log(f"wkv4_forward {cfg.name}: launch order vs claimed tiles, bitwise")
+    y_order = gpu_forward(inp)
+    old = os.environ.get("RWKV_WKV4_ORDER")
+    os.environ["RWKV_WKV4_ORDER"] = "claim"
+    try:
+        y_claim = gpu_forward(inp)
+    finally:
+        if old is None:
+            del os.environ["RWKV_WKV4_ORDER"]
+        else:
+            os.environ["RWKV_WKV4_ORDER"] = old
+    assert np.array_equal(y_order, y_claim)
+
+
 def test_workspace_layout_changes():
     """Regression: one workspace serves calls whose channel-block counts grow
     and shrink, so earlier calls' words sit where later calls keep their
