@@ -587,7 +587,11 @@ def main(argv=None):
             sec[fc.name] = {"ms": round(r["ms"], 4),
                             "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
                             "bytes_per_elem": 14,
-                            "algorithmic_TFLOPs": round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 2)}
+                            "algorithmic_TFLOPs": round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 2),
+                            "mfma_busy_pct": read_counter_summary(
+                                "wkv6_fwd_chunked_mfma_B4_T4096_H32_D64.md",
+                                kernel_source_hash(("wkv6.hip", "eagle_common.h", "wkv_device.h")),
+                                "mfma_busy_pct")}
         if "eagle-decode" in want:
             ed = synth.CFG_WKV5_DECODE
             log(f"bench: {ed.name}")
