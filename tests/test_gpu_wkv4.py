@@ -206,6 +206,32 @@ def test_launch_order_and_claimed_tiles_give_the_same_bits(cfg_name):
     assert np.array_equal(y_order, y_claim)
 
 
+def test_concurrent_streams_with_launch_order():
+    """Two 8x1024x768 forwards on two streams at once, each grid resident on
+    its own but not both together: a tile still only waits on workgroups
+    dispatched before it.  Both results must match the oracle."""
+    torch, dev = torch_dev()
+    cfg = synth.CFG_WKV4_169M
+    inps = [synth.wkv4_inputs(cfg.B, cfg.T, cfg.C, seed=140 + i) for i in range(2)]
+    refs = [oracle_forward(inp) for inp in inps]
+    need = rw.rwkv_wkv4_forward_workspace(cfg.B, cfg.T, cfg.C)
+    streams = [torch.cuda.Stream(dev) for _ in range(2)]
+    bufs, wss, ys = [], [], []
+    for inp in inps:
+        bufs.append({n: to_dev(inp[n]) for n in ("w", "u", "k", "v")})
+        wss.append(torch.zeros(need, dtype=torch.uint8, device=dev))
+        ys.append(torch.empty_like(bufs[-1]["k"]))
+    torch.cuda.synchronize()
+    for rnd in range(3):
+        log(f"wkv4_forward two streams round {rnd}")
+        for st, bf, ws, y in zip(streams, bufs, wss, ys):
+            with torch.cuda.stream(st):
+                rw.rwkv_wkv4_forward(bf["w"], bf["u"], bf["k"], bf["v"], y=y, ws=ws)
+        torch.cuda.synchronize()
+        for y, (y_ref, S) in zip(ys, refs):
+            assert wkv4_scaled_err(y.cpu().numpy(), y_ref, S) <= WKV4_TOL, rnd
+
+
 def test_workspace_layout_changes():
     """Regression: one workspace serves calls whose channel-block counts grow
     and shrink, so earlier calls' words sit where later calls keep their
