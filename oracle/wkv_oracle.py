@@ -47,7 +47,13 @@ closed forms (T=1, constant v, k=0 geometric series with the simulator's
 w=0.5/u=1 defaults, w=0 prefix softmax against scipy, very large w), the
 k-shift / v-affine / convex-hull invariants, Eagle recurrence against its
 unrolled sum, Eagle w=1 against a masked matrix product, Eagle D=1 against
-scipy.signal.lfilter, and linearity.  No function here is "parity unpinned".
+scipy.signal.lfilter, and linearity; Finch recurrence against its unrolled
+sum, Finch with a constant decay against Eagle, Finch with no decay on one
+channel as a prefix sum, a hand-worked case fixing when a token's decay
+applies, split sequences and the scale bound.  Planted mistakes (a dropped
+bonus term, the sign of w flipped, the decay one step early, a transposed
+Eagle state, the decay on the value index, Finch's decay applied after the
+add) each fail at least one pin.  No function here is "parity unpinned".
 """
 from __future__ import annotations
 
