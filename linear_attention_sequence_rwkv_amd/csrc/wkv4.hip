@@ -214,8 +214,12 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
   // Blocks whose last tile has its prefix (in-order launches), as counted
   // before this one; read at the end so the round trip overlaps pass 2.
   uint32_t done_before = 0;
-  // Tile prefix: wave 0 publishes the aggregate and looks back.
+  // Tile prefix: wave 0 publishes the aggregate and looks back, at raised
+  // issue priority: its short bursts of work between round trips then do not
+  // queue behind other workgroups' output passes on the same SIMD
+  // (8x1024x768: 16.73 -> 16.49 us).
   if (wid == 0) {
+    __builtin_amdgcn_s_setprio(3);
     const int tile_n = min(TILE, T - tile_t0);
     uint64_t* mine = slots + (size_t(tile) * groups + g) * SLOT + ch0;
     Hist agg[CPL], pre[CPL];
@@ -339,6 +343,7 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
       publish(1, inc);
       if (tile == n_tiles - 1) write_state(sio, inc, w2, valid, size_t(bi) * C + size_t(cb) * W + ch0);
     }
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int c = 0; c < CPL; ++c) s_pre.put(ch0 + c, pre[c]);
     if (in_order && tile == n_tiles - 1 && lane == 0) {
