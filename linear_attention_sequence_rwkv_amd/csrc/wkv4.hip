@@ -188,7 +188,10 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
     load_rows<L, CPL, false>(rk, rv, voff_in, row_bytes, n, kk, vv);
   if (in_order && threadIdx.x == 0) s_tag = hdr_load(hdr, kHdrEpoch) + 1u;
 
-  // Pass 1: this wave's tokens from an empty history.
+  // Pass 1: this wave's tokens from an empty history, at raised issue
+  // priority (the summaries gate the aggregate that later tiles wait for;
+  // 8x1024x768: 16.58 -> 16.49 us over five runs).
+  __builtin_amdgcn_s_setprio(2);
   if (full) {
 #pragma unroll
     for (int c = 0; c < CPL; ++c)
@@ -209,6 +212,7 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
     if (tile - 1 - lane > 0) e_agg = tagged_load(sp);  // tile 0 has no aggregate
   }
   __syncthreads();
+  __builtin_amdgcn_s_setprio(0);
   const uint32_t tag = __builtin_amdgcn_readfirstlane(s_tag);
 
   // Blocks whose last tile has its prefix (in-order launches), as counted
