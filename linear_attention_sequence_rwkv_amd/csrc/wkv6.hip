@@ -355,9 +355,14 @@ __global__ __launch_bounds__(256, 2) void wkv6_fwd_chunked(
   load_w(wc, c_begin * kL, T, H, b, h, w);
   for (int c = c_begin; c < c_end; ++c) {
     const int t0 = c * kL;
+    // The decay prefix and staging (latency-bound, barrier-separated) run at
+    // raised issue priority over the other workgroup's products on the same
+    // SIMDs (4x4096x32x64: 164.9 -> 162.7 us).
+    __builtin_amdgcn_s_setprio(2);
     const bool exact = decay_prefix(wc, s.c, &s.tab);
     stage_chunk_f(cur, exact, s);
     __syncthreads();
+    __builtin_amdgcn_s_setprio(0);
     if (c + 1 < c_end) {
       load_chunk<DV>(nxt, t0 + kL, T, H, b, h, j0, r, k, v);
       load_w(wn, t0 + kL, T, H, b, h, w);
