@@ -184,26 +184,41 @@ def test_in_order_and_claimed_launches_share_a_workspace():
             assert wkv4_scaled_err(y.cpu().numpy(), y_ref, S) <= WKV4_TOL, (rnd, shp)
 
 
-@pytest.mark.parametrize("cfg_name", ["169m", "tiny"])
+@pytest.mark.parametrize("cfg_name", ["169m", "tiny", "ragged"])
 def test_launch_order_and_claimed_tiles_give_the_same_bits(cfg_name):
     """Tiles taken in launch order (the whole grid resident) and claimed in
-    arrival order fold the same histories in the same chain order: the outputs
-    must agree bit for bit (RWKV_WKV4_ORDER=claim forces claims)."""
-    torch, _ = torch_dev()
-    cfg = synth.CFG_WKV4_169M if cfg_name == "169m" else synth.CFG_WKV4_TINY
-    inp = synth.wkv4_inputs_for(cfg)
-    log(f"wkv4_forward {cfg.name}: launch order vs claimed tiles, bitwise")
-    y_order = gpu_forward(inp)
+    arrival order fold the same histories in the same chain order: the
+    outputs and the final state must agree bit for bit
+    (RWKV_WKV4_ORDER=claim forces claims)."""
+    torch, dev = torch_dev()
+    if cfg_name == "ragged":
+        inp = synth.wkv4_inputs(3, 1100, 200, seed=77)
+    else:
+        cfg = synth.CFG_WKV4_169M if cfg_name == "169m" else synth.CFG_WKV4_TINY
+        inp = synth.wkv4_inputs_for(cfg)
+    B, T, C = inp["k"].shape
+    g = np.random.default_rng(5)
+    st = [torch.from_numpy(x.astype(np.float32)).to(dev)
+          for x in (g.random((B, C)), g.random((B, C)) + 0.5, g.normal(size=(B, C)))]
+    t = {n: torch.from_numpy(inp[n]).to(dev) for n in ("w", "u", "k", "v")}
+    outs = {}
     old = os.environ.get("RWKV_WKV4_ORDER")
-    os.environ["RWKV_WKV4_ORDER"] = "claim"
     try:
-        y_claim = gpu_forward(inp)
+        for mode in ("", "claim"):
+            log(f"wkv4_forward {B}x{T}x{C}: prefix mode {mode or 'default'}, bitwise")
+            os.environ["RWKV_WKV4_ORDER"] = mode
+            y = rw.rwkv_wkv4_forward(t["w"], t["u"], t["k"], t["v"])
+            y2, (a2, b2, p2) = rw.rwkv_wkv4_forward_state(t["w"], t["u"], t["k"], t["v"],
+                                                         state_in=tuple(st), state_out=True)
+            torch.cuda.synchronize()
+            outs[mode] = [x.cpu().numpy() for x in (y, y2, a2, b2, p2)]
     finally:
         if old is None:
             del os.environ["RWKV_WKV4_ORDER"]
         else:
             os.environ["RWKV_WKV4_ORDER"] = old
-    assert np.array_equal(y_order, y_claim)
+    for x, z in zip(outs[""], outs["claim"]):
+        assert np.array_equal(x, z)
 
 
 def test_concurrent_streams_with_launch_order():
