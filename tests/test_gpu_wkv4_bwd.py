@@ -103,6 +103,43 @@ def test_backward_is_deterministic():
             assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("shape", [(8, 1024, 768), (3, 1100, 200)])
+def test_launch_order_and_claimed_tiles_give_the_same_gradients(shape):
+    """The prefix pass takes its tiles in launch order when the grid fits on
+    the device and claims them otherwise (RWKV_WKV4_ORDER=claim forces
+    claims); the folds run in the same chain order, so all four gradients
+    must agree bit for bit, also when the two modes alternate on one
+    workspace."""
+    import os
+    torch, _ = torch_dev()
+    B, T, C = shape
+    inp = synth.wkv4_backward_inputs(B, T, C, seed=91)
+    args = [to_dev(inp[n]) for n in ("w", "u", "k", "v", "gy")]
+    ws = torch.zeros(max(rw.rwkv_wkv4_backward_workspace(B, T, C), 256), dtype=torch.uint8,
+                     device=args[0].device)
+    outs = {}
+    old = os.environ.get("RWKV_WKV4_ORDER")
+    try:
+        for rnd in range(2):
+            for mode in ("", "claim"):
+                log(f"wkv4_backward {shape}: tile order {mode or 'default'} round {rnd}")
+                os.environ["RWKV_WKV4_ORDER"] = mode
+                got = rw.rwkv_wkv4_backward(*args, ws=ws)
+                torch.cuda.synchronize()
+                got = [x.cpu() for x in got]
+                if mode in outs:
+                    for a, b in zip(outs[mode], got):
+                        assert torch.equal(a, b), (mode, rnd)
+                outs[mode] = got
+    finally:
+        if old is None:
+            del os.environ["RWKV_WKV4_ORDER"]
+        else:
+            os.environ["RWKV_WKV4_ORDER"] = old
+    for a, b in zip(outs[""], outs["claim"]):
+        assert torch.equal(a, b)
+
+
 def test_backward_after_forward_calls_of_other_shapes():
     """The two workspaces (forward's, backward's) are independent; calls of
     different shapes in any order stay correct."""
