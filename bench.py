@@ -160,6 +160,54 @@ def bench_wkv4_backward(torch, rw, cfg, steps, warmup):
     return {"ms": ms, "elems": B * T * C, "bytes": 20 * B * T * C}
 
 
+def bench_wkv4_train(torch, rw, cfg, steps, warmup):
+    """A training step's WKV: forward then backward on the same inputs, timed
+    as rwkv_wkv4_forward_train + rwkv_wkv4_backward_after_forward (one
+    workspace, the backward reuses the forward's tile histories) and as
+    rwkv_wkv4_forward + rwkv_wkv4_backward."""
+    import synth
+    dev = torch.device("cuda:0")
+    inp = synth.wkv4_backward_inputs(cfg.B, cfg.T, cfg.C, cfg.seed, omega_lo=cfg.omega_lo,
+                                     omega_hi=cfg.omega_hi, u_std=cfg.u_std, k_std=cfg.k_std,
+                                     v_std=cfg.v_std)
+    B, T, C = cfg.B, cfg.T, cfg.C
+    w, u, k, v, gy = (torch.from_numpy(inp[n]).to(dev) for n in ("w", "u", "k", "v", "gy"))
+    y = torch.empty_like(k)
+    gw, gu = torch.empty_like(w), torch.empty_like(u)
+    gk, gv = torch.empty_like(k), torch.empty_like(k)
+    lib = rw.load_library()
+    need_b = lib.rwkv_wkv4_backward_workspace(B, T, C)
+    need_f = lib.rwkv_wkv4_forward_workspace(B, T, C)
+    ws_b = torch.zeros(max(need_b, 256), dtype=torch.uint8, device=dev)
+    ws_f = torch.zeros(max(need_f, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    io = (P(w), P(u), P(k), P(v))
+    grads = (P(gy), P(gw), P(gu), P(gk), P(gv))
+    pair = ((lib.rwkv_wkv4_forward_train, (B, T, C, *io, P(y), P(ws_b), need_b, sh)),
+            (lib.rwkv_wkv4_backward_after_forward, (B, T, C, *io, *grads, P(ws_b), need_b, sh)))
+    separate = ((lib.rwkv_wkv4_forward, (B, T, C, *io, P(y), P(ws_f), need_f, sh)),
+                (lib.rwkv_wkv4_backward, (B, T, C, *io, *grads, P(ws_b), need_b, sh)))
+    out = {}
+    for key, calls in (("pair", pair), ("separate", separate)):
+        for _ in range(warmup):
+            for fn, a in calls:
+                assert fn(*a) == 0
+        torch.cuda.synchronize()
+        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st.record(stream)
+        for _ in range(steps):
+            for fn, a in calls:
+                assert fn(*a) == 0
+        en.record(stream)
+        torch.cuda.synchronize()
+        assert torch.isfinite(gk).all().item() and torch.isfinite(y).all().item()
+        out[key] = st.elapsed_time(en) / steps
+    return {"ms": out["pair"], "ms_separate": out["separate"], "elems": B * T * C,
+            "bytes": 32 * B * T * C}
+
+
 def cpu_sample_backward():
     """Oracle backward (reverse-time form) on 32 channels of the 8x1024x768
     workload, full T."""
@@ -479,9 +527,9 @@ def main(argv=None):
                     help="accepted for older command lines; the 1 GiB copy always runs")
     ap.add_argument("--secondary",
                     default="hot,long,decode,decode-graph,eagle,eagle-decode,finch,backward,"
-                            "backward-long",
+                            "backward-long,train",
                     help="comma list of secondary workloads: hot, long, decode, decode-graph, "
-                         "eagle, eagle-decode, finch, backward, backward-long")
+                         "eagle, eagle-decode, finch, backward, backward-long, train")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -580,6 +628,14 @@ def main(argv=None):
                              "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
                              "bytes_per_elem": 20,
                              "gelem_per_s": round(r["elems"] / (r["ms"] * 1e-3) / 1e9, 1)}
+        if "train" in want:
+            name = cfg.name.replace("wkv4_fwd", "wkv4_train_step")
+            log(f"bench: {name}")
+            r = bench_wkv4_train(torch, rw, cfg, steps=100, warmup=2)
+            sec[name] = {"ms": round(r["ms"], 5),
+                         "ms_forward_plus_backward": round(r["ms_separate"], 5),
+                         "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
+                         "bytes_per_elem": 32}
         if "finch" in want:
             fc = synth.CFG_WKV6_FINCH
             log(f"bench: {fc.name}")

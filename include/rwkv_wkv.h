@@ -119,6 +119,35 @@ int rwkv_wkv4_backward(int64_t B, int64_t T, int64_t C,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * RWKV-4 forward and backward for training, sharing one workspace.
+ * [RWKV-digest] (2) Time-mixing, WKV_t: the forward's time-parallel scan
+ * computes every tile's history before the tile; the backward needs exactly
+ * those histories.  rwkv_wkv4_forward_train computes y as rwkv_wkv4_forward
+ * does (same accuracy bound; the tile shape is the backward's, so the bits
+ * can differ from rwkv_wkv4_forward's) and leaves the histories in `ws`;
+ * rwkv_wkv4_backward_after_forward then returns what rwkv_wkv4_backward
+ * returns, bit for bit, without recomputing them (one read of k and v less).
+ *
+ *   arguments   as for rwkv_wkv4_forward / rwkv_wkv4_backward
+ *   ws, ws_bytes         a BACKWARD workspace: at least
+ *                        rwkv_wkv4_backward_workspace(B,T,C) bytes, zero-filled
+ *                        before its first use.
+ * The backward call must follow the forward call on the same stream, with the
+ * same B, T, C, w, u, k, v and workspace, and no other call on that workspace
+ * in between; otherwise its results are undefined (nothing checks this).
+ * ---------------------------------------------------------------------- */
+int rwkv_wkv4_forward_train(int64_t B, int64_t T, int64_t C,
+                            const float* w, const float* u,
+                            const float* k, const float* v,
+                            float* y,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+int rwkv_wkv4_backward_after_forward(int64_t B, int64_t T, int64_t C,
+                                     const float* w, const float* u,
+                                     const float* k, const float* v, const float* gy,
+                                     float* gw, float* gu, float* gk, float* gv,
+                                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * RWKV-4 recurrent state.   [RWKV-digest] (2) Time-mixing, recurrent form
  *   a_t = e^{-w} a_{t-1} + e^{k_t} v_t,   b_t = e^{-w} b_{t-1} + e^{k_t}.
  * The library stores the sums scaled: a_true = a * e^{p}, b_true = b * e^{p},

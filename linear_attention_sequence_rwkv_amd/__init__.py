@@ -18,7 +18,9 @@ import threading
 __all__ = [
     "LIB_PATH", "load_library", "RwkvError",
     "rwkv_abi_version", "rwkv_status_str", "rwkv_last_hip_error",
-    "rwkv_wkv4_forward_workspace", "rwkv_wkv4_forward",
+    "rwkv_wkv4_forward_workspace", "rwkv_wkv4_forward", "rwkv_wkv4_forward_state",
+    "rwkv_wkv4_backward_workspace", "rwkv_wkv4_backward",
+    "rwkv_wkv4_forward_train", "rwkv_wkv4_backward_after_forward",
     "rwkv_wkv4_state_init", "rwkv_wkv4_step",
     "rwkv_wkv5_forward_workspace", "rwkv_wkv5_forward",
 ]
@@ -44,6 +46,10 @@ _SIGNATURES = {
     "rwkv_wkv4_backward_workspace": (_sz, [_i64, _i64, _i64]),
     "rwkv_wkv4_backward": (ctypes.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                                           _p, _sz, _p]),
+    "rwkv_wkv4_forward_train": (ctypes.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _sz,
+                                               _p]),
+    "rwkv_wkv4_backward_after_forward": (ctypes.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p,
+                                                        _p, _p, _p, _p, _sz, _p]),
     "rwkv_wkv4_state_init": (ctypes.c_int, [_i64, _i64, _p, _p, _p, _p]),
     "rwkv_wkv4_step": (ctypes.c_int, [_i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "rwkv_wkv5_forward_workspace": (_sz, [_i64, _i64, _i64, _i64]),
@@ -262,7 +268,7 @@ def rwkv_wkv4_backward_workspace(B: int, T: int, C: int) -> int:
 
 
 def rwkv_wkv4_backward(w, u, k, v, gy, gw=None, gu=None, gk=None, gv=None, ws=None,
-                       stream=None):
+                       stream=None, _entry="rwkv_wkv4_backward"):
     """Gradients of sum(gy * WKV(w, u, k, v)).  Returns (gw, gu, gk, gv).
 
     ``ws`` (optional) is a caller-owned zero-initialised uint8 GPU tensor of at
@@ -291,12 +297,41 @@ def rwkv_wkv4_backward(w, u, k, v, gy, gw=None, gu=None, gk=None, gv=None, ws=No
     st = _stream(k.device, stream)
     need = lib.rwkv_wkv4_backward_workspace(B, T, C)
     if ws is None:
+        if _entry != "rwkv_wkv4_backward":
+            raise ValueError("rwkv_wkv4_backward_after_forward needs the workspace that "
+                             "rwkv_wkv4_forward_train used")
         ws = _workspace("wkv4_bwd", k.device, st.value or 0, need)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    status = lib.rwkv_wkv4_backward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(gy),
-                                    _ptr(gw), _ptr(gu), _ptr(gk), _ptr(gv), _ptr(ws), nbytes, st)
-    _check("rwkv_wkv4_backward", status)
+    status = getattr(lib, _entry)(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(gy),
+                                  _ptr(gw), _ptr(gu), _ptr(gk), _ptr(gv), _ptr(ws), nbytes, st)
+    _check(_entry, status)
     return gw, gu, gk, gv
+
+
+def rwkv_wkv4_forward_train(w, u, k, v, ws, y=None, stream=None):
+    """The forward for training: returns y as rwkv_wkv4_forward does and leaves
+    in ``ws`` (a zero-initialised uint8 GPU tensor of at least
+    rwkv_wkv4_backward_workspace(B, T, C) bytes) the tile histories that
+    rwkv_wkv4_backward_after_forward reads instead of recomputing."""
+    lib = load_library()
+    w, u, k, v, y = _wkv4_forward_args(w, u, k, v, y)
+    B, T, C = k.shape
+    if ws is None:
+        raise ValueError("rwkv_wkv4_forward_train needs a backward workspace")
+    st = _stream(k.device, stream)
+    nbytes = ws.numel() * ws.element_size()
+    status = lib.rwkv_wkv4_forward_train(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
+                                         _ptr(ws), nbytes, st)
+    _check("rwkv_wkv4_forward_train", status)
+    return y
+
+
+def rwkv_wkv4_backward_after_forward(w, u, k, v, gy, ws, gw=None, gu=None, gk=None, gv=None,
+                                     stream=None):
+    """rwkv_wkv4_backward's gradients, reusing the histories that the last
+    rwkv_wkv4_forward_train over the same inputs left in ``ws``."""
+    return rwkv_wkv4_backward(w, u, k, v, gy, gw, gu, gk, gv, ws, stream,
+                              _entry="rwkv_wkv4_backward_after_forward")
 
 
 def rwkv_wkv4_state_init(B: int, C: int, device="cuda", stream=None):

@@ -152,10 +152,12 @@ RWKV_API size_t rwkv_wkv4_backward_workspace(int64_t B, int64_t T, int64_t C) {
   return plan.ws_bytes;
 }
 
-RWKV_API int rwkv_wkv4_backward(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
-                                const float* k, const float* v, const float* gy, float* gw,
-                                float* gu, float* gk, float* gv, void* ws, size_t ws_bytes,
-                                hipStream_t stream) {
+namespace {
+
+int wkv4_backward_impl(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                       const float* k, const float* v, const float* gy, float* gw, float* gu,
+                       float* gk, float* gv, void* ws, size_t ws_bytes, bool prefix_ready,
+                       hipStream_t stream) {
   int64_t n;
   if (!dims_ok({B, T, C}, &n)) return RWKV_ERR_SHAPE;
   if (n == 0) return RWKV_OK;
@@ -167,8 +169,43 @@ RWKV_API int rwkv_wkv4_backward(int64_t B, int64_t T, int64_t C, const float* w,
   if (!rwkv::wkv4_backward_plan(B, T, C, &plan)) return RWKV_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < plan.ws_bytes) return RWKV_ERR_WORKSPACE;
   if (!aligned16(ws)) return RWKV_ERR_ALIGN;
-  return hip_status(
-      rwkv::wkv4_backward_launch(plan, B, T, C, w, u, k, v, gy, gw, gu, gk, gv, ws, stream));
+  return hip_status(rwkv::wkv4_backward_launch(plan, B, T, C, w, u, k, v, gy, gw, gu, gk, gv, ws,
+                                               prefix_ready, stream));
+}
+
+}  // namespace
+
+RWKV_API int rwkv_wkv4_backward(int64_t B, int64_t T, int64_t C, const float* w, const float* u,
+                                const float* k, const float* v, const float* gy, float* gw,
+                                float* gu, float* gk, float* gv, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  return wkv4_backward_impl(B, T, C, w, u, k, v, gy, gw, gu, gk, gv, ws, ws_bytes, false,
+                            stream);
+}
+
+RWKV_API int rwkv_wkv4_forward_train(int64_t B, int64_t T, int64_t C, const float* w,
+                                     const float* u, const float* k, const float* v, float* y,
+                                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  int64_t n;
+  if (!dims_ok({B, T, C}, &n)) return RWKV_ERR_SHAPE;
+  if (n == 0) return RWKV_OK;
+  if (!w || !u || !k || !v || !y) return RWKV_ERR_NULLPTR;
+  if (!aligned16(w) || !aligned16(u) || !aligned16(k) || !aligned16(v) || !aligned16(y))
+    return RWKV_ERR_ALIGN;
+  rwkv::Wkv4BwdPlan plan;
+  if (!rwkv::wkv4_backward_plan(B, T, C, &plan)) return RWKV_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < plan.ws_bytes) return RWKV_ERR_WORKSPACE;
+  if (!aligned16(ws)) return RWKV_ERR_ALIGN;
+  return hip_status(rwkv::wkv4_forward_train_launch(plan, T, C, w, u, k, v, y, ws, stream));
+}
+
+RWKV_API int rwkv_wkv4_backward_after_forward(int64_t B, int64_t T, int64_t C, const float* w,
+                                              const float* u, const float* k, const float* v,
+                                              const float* gy, float* gw, float* gu, float* gk,
+                                              float* gv, void* ws, size_t ws_bytes,
+                                              hipStream_t stream) {
+  return wkv4_backward_impl(B, T, C, w, u, k, v, gy, gw, gu, gk, gv, ws, ws_bytes, true,
+                            stream);
 }
 
 // ------------------------------------------------------------------- Eagle

@@ -116,7 +116,11 @@ __device__ __forceinline__ void write_state(const StateIO& sio, const Hist (&h)[
 // tile's published words (carrying the tag it read) have then reached, and
 // that tile leaves its block's counter primed for a next call that claims.
 // in_order == 0: tiles are claimed in arrival order.
-template <int CPL, int L, int NW, bool EMIT = true>
+//
+// TAPE (with outputs): also publish the mid-tile histories in `mids`, as the
+// prefix pass does, so that a backward over the same inputs can skip that
+// pass (a forward for training).
+template <int CPL, int L, int NW, bool EMIT = true, bool TAPE = false>
 __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
     int T, int C, int n_cblk, int groups, int n_tiles, int in_order,
     const float* __restrict__ w, const float* __restrict__ u,
@@ -355,7 +359,7 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
                          uint64_t(tag + 1u) << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       done_before = hdr_add(hdr, kHdrClaimed, 1u);
     }
-    if (!EMIT && mids) {
+    if ((!EMIT || TAPE) && mids) {
       uint64_t* q = mids + (size_t(tile) * groups + g) * (4 * W) + ch0;
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
@@ -588,6 +592,25 @@ hipError_t wkv4_prefix_launch(const Wkv4Plan& pl, int64_t T, int64_t C, const fl
   hipLaunchKernelGGL((wkv4_fwd_tiled<1, 32, 4, false>), dim3(unsigned(grid)), dim3(256), 0,
                      stream, int(T), int(C), int(pl.n_cblk), int(pl.groups), int(pl.n_tiles),
                      in_order, w, u, k, v, nullptr, hdr, counters, slots, none,
+                     static_cast<uint64_t*>(mids));
+  return hipGetLastError();
+}
+
+hipError_t wkv4_forward_tape_launch(const Wkv4Plan& pl, int64_t T, int64_t C, const float* w,
+                                   const float* u, const float* k, const float* v, float* y,
+                                   void* ws, void* mids, hipStream_t stream) {
+  if (pl.cpl != 1 || pl.L != 32 || pl.NW != 4) return hipErrorInvalidValue;
+  char* base = static_cast<char*>(ws);
+  uint32_t* hdr = reinterpret_cast<uint32_t*>(base);
+  uint64_t* counters = reinterpret_cast<uint64_t*>(base + kWkv4HeaderBytes);
+  uint64_t* slots = reinterpret_cast<uint64_t*>(base + pl.slots_offset);
+  const int64_t grid = pl.n_tiles * pl.groups;
+  const StateIO none{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  const void* kern = reinterpret_cast<const void*>(&wkv4_fwd_tiled<1, 32, 4, true, true>);
+  const int in_order = grid <= resident_workgroups(kern, 256) ? 1 : 0;
+  hipLaunchKernelGGL((wkv4_fwd_tiled<1, 32, 4, true, true>), dim3(unsigned(grid)), dim3(256), 0,
+                     stream, int(T), int(C), int(pl.n_cblk), int(pl.groups), int(pl.n_tiles),
+                     in_order, w, u, k, v, y, hdr, counters, slots, none,
                      static_cast<uint64_t*>(mids));
   return hipGetLastError();
 }

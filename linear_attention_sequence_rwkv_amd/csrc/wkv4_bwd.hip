@@ -447,13 +447,18 @@ bool wkv4_backward_plan(int64_t B, int64_t T, int64_t C, Wkv4BwdPlan* plan) {
 hipError_t wkv4_backward_launch(const Wkv4BwdPlan& pl, int64_t B, int64_t T, int64_t C,
                                 const float* w, const float* u, const float* k,
                                 const float* v, const float* gy, float* gw, float* gu,
-                                float* gk, float* gv, void* ws, hipStream_t stream) {
+                                float* gk, float* gv, void* ws, bool prefix_ready,
+                                hipStream_t stream) {
   (void)B;
   char* base = static_cast<char*>(ws);
   uint64_t* mids = reinterpret_cast<uint64_t*>(base + pl.mid_offset);
-  // 1. forward prefixes of every tile and half tile
-  hipError_t e = wkv4_prefix_launch(pl.fwd, T, C, w, u, k, v, base, mids, stream);
-  if (e != hipSuccess) return e;
+  // 1. forward prefixes of every tile and half tile, unless a forward for
+  //    training left them
+  hipError_t e = hipSuccess;
+  if (!prefix_ready) {
+    e = wkv4_prefix_launch(pl.fwd, T, C, w, u, k, v, base, mids, stream);
+    if (e != hipSuccess) return e;
+  }
   // 2. reverse scan, on the same header and counters
   const uint64_t* fwd_slots = reinterpret_cast<const uint64_t*>(base + pl.fwd.slots_offset);
   uint32_t* hdr = reinterpret_cast<uint32_t*>(base);
@@ -475,6 +480,14 @@ hipError_t wkv4_backward_launch(const Wkv4BwdPlan& pl, int64_t B, int64_t T, int
                      stream, int(C),
                      int(pl.part_rows), part_w, part_u, gw, gu);
   return hipGetLastError();
+}
+
+hipError_t wkv4_forward_train_launch(const Wkv4BwdPlan& pl, int64_t T, int64_t C,
+                                     const float* w, const float* u, const float* k,
+                                     const float* v, float* y, void* ws, hipStream_t stream) {
+  char* base = static_cast<char*>(ws);
+  return wkv4_forward_tape_launch(pl.fwd, T, C, w, u, k, v, y, base, base + pl.mid_offset,
+                                  stream);
 }
 
 }  // namespace rwkv

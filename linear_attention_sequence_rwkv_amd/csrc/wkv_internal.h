@@ -44,6 +44,12 @@ hipError_t wkv4_prefix_launch(const Wkv4Plan& plan, int64_t T, int64_t C, const 
                               const float* u, const float* k, const float* v, void* ws,
                               void* mids, hipStream_t stream);
 
+// The forward with outputs, also publishing the prefix pass's histories
+// (tile shape 1 x 32 x 4 only).
+hipError_t wkv4_forward_tape_launch(const Wkv4Plan& plan, int64_t T, int64_t C, const float* w,
+                                   const float* u, const float* k, const float* v, float* y,
+                                   void* ws, void* mids, hipStream_t stream);
+
 // a/b/p_in: optional history before the first token; a/b/p_out: optional
 // state after the last token (both [B, C], step-API form; may be null).
 hipError_t wkv4_forward_launch(const Wkv4Plan& plan, int64_t B, int64_t T, int64_t C,
@@ -77,10 +83,19 @@ struct Wkv4BwdPlan {
 
 bool wkv4_backward_plan(int64_t B, int64_t T, int64_t C, Wkv4BwdPlan* plan);
 
+// prefix_ready: the workspace already holds the prefix pass's histories,
+// left there by wkv4_forward_train_launch over the same inputs.
 hipError_t wkv4_backward_launch(const Wkv4BwdPlan& plan, int64_t B, int64_t T, int64_t C,
                                 const float* w, const float* u, const float* k,
                                 const float* v, const float* gy, float* gw, float* gu,
-                                float* gk, float* gv, void* ws, hipStream_t stream);
+                                float* gk, float* gv, void* ws, bool prefix_ready,
+                                hipStream_t stream);
+
+// The forward with outputs over a backward workspace, publishing the same
+// histories as the backward's prefix pass (with the prefix pass's tiles).
+hipError_t wkv4_forward_train_launch(const Wkv4BwdPlan& plan, int64_t T, int64_t C,
+                                     const float* w, const float* u, const float* k,
+                                     const float* v, float* y, void* ws, hipStream_t stream);
 
 // ----- Eagle (RWKV-5) forward -----
 size_t wkv5_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t D);

@@ -44,6 +44,7 @@ def test_header_declares_the_boundary():
         "rwkv_abi_version", "rwkv_status_str", "rwkv_last_hip_error",
         "rwkv_wkv4_forward_workspace", "rwkv_wkv4_forward", "rwkv_wkv4_forward_state",
         "rwkv_wkv4_backward_workspace", "rwkv_wkv4_backward",
+        "rwkv_wkv4_forward_train", "rwkv_wkv4_backward_after_forward",
         "rwkv_wkv4_state_init", "rwkv_wkv4_step", "rwkv_wkv5_forward_workspace",
         "rwkv_wkv5_forward", "rwkv_wkv5_forward_state", "rwkv_wkv5_step",
         "rwkv_wkv6_forward_workspace", "rwkv_wkv6_forward", "rwkv_wkv6_step",
@@ -196,9 +197,10 @@ def test_wkv5_state_and_step_rejections(lib):
     assert lib.rwkv_last_hip_error() == 0
 
 
-def test_wkv4_backward_rejections(lib):
+@pytest.mark.parametrize("entry", ["rwkv_wkv4_backward", "rwkv_wkv4_backward_after_forward"])
+def test_wkv4_backward_rejections(lib, entry):
     _skip_if_gpu()
-    f = lib.rwkv_wkv4_backward
+    f = getattr(lib, entry)
     need = lib.rwkv_wkv4_backward_workspace(2, 300, 128)
     assert need > lib.rwkv_wkv4_forward_workspace(2, 300, 128)
     names = "w u k v gy gw gu gk gv".split()
@@ -212,6 +214,27 @@ def test_wkv4_backward_rejections(lib):
     assert f(2, 300, 128, *args(), FAKE, need - 1, NULL) == WORKSPACE
     assert f(2, 300, 128, *args(), MISALIGNED, need, NULL) == ALIGN
     assert lib.rwkv_wkv4_backward_workspace(0, 10, 10) == 0
+    assert lib.rwkv_last_hip_error() == 0
+
+
+def test_wkv4_forward_train_rejections(lib):
+    """The training forward takes a backward workspace: a forward-sized one is
+    rejected before anything is launched."""
+    _skip_if_gpu()
+    f = lib.rwkv_wkv4_forward_train
+    need = lib.rwkv_wkv4_backward_workspace(2, 300, 128)
+    small = lib.rwkv_wkv4_forward_workspace(2, 300, 128)
+    names = "w u k v y".split()
+    args = lambda **kw: [kw.get(n, FAKE) for n in names]  # noqa: E731
+    assert f(0, 300, 128, *[NULL] * 5, NULL, 0, NULL) == OK
+    assert f(2, -1, 128, *args(), FAKE, need, NULL) == SHAPE
+    for n in names:
+        assert f(2, 300, 128, *args(**{n: NULL}), FAKE, need, NULL) == NULLPTR, n
+        assert f(2, 300, 128, *args(**{n: MISALIGNED}), FAKE, need, NULL) == ALIGN, n
+    assert f(2, 300, 128, *args(), NULL, need, NULL) == WORKSPACE
+    assert f(2, 300, 128, *args(), FAKE, small, NULL) == WORKSPACE
+    assert f(2, 300, 128, *args(), FAKE, need - 1, NULL) == WORKSPACE
+    assert f(2, 300, 128, *args(), MISALIGNED, need, NULL) == ALIGN
     assert lib.rwkv_last_hip_error() == 0
 
 

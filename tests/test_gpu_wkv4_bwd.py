@@ -11,7 +11,7 @@ import pytest
 import linear_attention_sequence_rwkv_amd as rw
 import oracle.wkv_oracle as O
 import synth
-from wkv_testutil import WKV4_TOL, log, to_dev, torch_dev
+from wkv_testutil import WKV4_TOL, log, to_dev, torch_dev, wkv4_scaled_err
 
 pytestmark = pytest.mark.gpu
 
@@ -174,3 +174,45 @@ def test_claimed_and_in_order_prefix_passes_share_a_workspace():
         check(big, ch)
         log(f"wkv4_backward in-order prefix pass round {rnd}")
         check(small)
+
+
+@pytest.mark.parametrize("shape", [(8, 1024, 768), (3, 1100, 200), (2, 300, 96), (1, 64, 64),
+                                   (1, 16384, 256)])
+def test_training_pair_matches_the_separate_calls(shape):
+    """rwkv_wkv4_forward_train leaves the prefix pass's tile histories in a
+    backward workspace and rwkv_wkv4_backward_after_forward reuses them: y is
+    within the bound of the oracle (and equal to rwkv_wkv4_forward's where both
+    use the same tiles), and the gradients equal rwkv_wkv4_backward's bit for
+    bit; a pair of another shape on another workspace in between changes
+    nothing."""
+    torch, dev = torch_dev()
+    B, T, C = shape
+    inp = synth.wkv4_backward_inputs(B, T, C, seed=303)
+    args = [to_dev(inp[n]) for n in ("w", "u", "k", "v")]
+    gy = to_dev(inp["gy"])
+    need = rw.rwkv_wkv4_backward_workspace(B, T, C)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+    other = synth.wkv4_backward_inputs(2, 700, 128, seed=304)
+    oargs = [to_dev(other[n]) for n in ("w", "u", "k", "v", "gy")]
+    ows = torch.zeros(max(rw.rwkv_wkv4_backward_workspace(2, 700, 128), 256),
+                      dtype=torch.uint8, device=dev)
+    ref_grads = [x.cpu() for x in rw.rwkv_wkv4_backward(*args, gy)]
+    y_plain = rw.rwkv_wkv4_forward(*args).cpu().numpy()
+    if T <= 4096:
+        y_ref, _ = O.wkv4_recurrent(inp["w"], inp["u"], inp["k"], inp["v"])
+        S = O.wkv4_scale(inp["w"], inp["u"], inp["k"], inp["v"])
+    for rnd in range(2):
+        log(f"wkv4 training pair {shape} round {rnd}")
+        y = rw.rwkv_wkv4_forward_train(*args, ws=ws)
+        if rnd == 1:
+            rw.rwkv_wkv4_forward_train(*oargs[:4], ws=ows)
+            rw.rwkv_wkv4_backward_after_forward(*oargs, ws=ows)
+        grads = rw.rwkv_wkv4_backward_after_forward(*args, gy, ws=ws)
+        torch.cuda.synchronize()
+        y = y.cpu().numpy()
+        if T <= 4096:
+            assert wkv4_scaled_err(y, y_ref, S) <= WKV4_TOL
+        if T > 64:  # both calls tile 128 tokens with one channel per lane
+            assert np.array_equal(y, y_plain)
+        for a, b in zip(ref_grads, grads):
+            assert torch.equal(a, b.cpu())
