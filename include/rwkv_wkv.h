@@ -62,6 +62,47 @@ const char* rwkv_status_str(int status);
 int rwkv_last_hip_error(void);
 
 /* ------------------------------------------------------------------------
+ * Plan overrides, for tests and tuning sweeps; results stay within the same
+ * accuracy bounds whatever the setting.  Each key holds 0 (the built-in plan)
+ * or an override.  The values start from the environment, read once at the
+ * first call that plans anything (RWKV_WKV4_TILE="cpl,L,NW",
+ * RWKV_WKV4_ORDER=claim, RWKV_WKV5_DV, RWKV_WKV5_SEGS, RWKV_WKV6_DV,
+ * RWKV_WKV6_SEGS), and rwkv_set_tuning changes them for the whole process.
+ * They change the plan and therefore the workspace sizes: query a workspace
+ * size under the setting it will be used with (a call whose workspace is too
+ * small for the current setting returns RWKV_ERR_WORKSPACE).  Changing a
+ * setting while another thread plans a call races with that call's plan.
+ * rwkv_set_tuning returns RWKV_ERR_UNSUPPORTED for an unknown key or value.
+ * ---------------------------------------------------------------------- */
+#define RWKV_TUNE_WKV4_TILE  1  /* cpl*10000 + L*100 + NW of a compiled RWKV-4 forward tile:
+                                   40808 41604 41608 21608 23204 21604 13208 13204 16401 11604 */
+#define RWKV_TUNE_WKV4_ORDER 2  /* 1: RWKV-4 tiles claimed in arrival order even where the
+                                   whole grid is resident (same results, bit for bit) */
+#define RWKV_TUNE_WKV5_DV    3  /* value columns per Eagle workgroup: 16, 32 or 64 */
+#define RWKV_TUNE_WKV5_SEGS  4  /* Eagle time segments, 1..4096 (each >= 4 chunks) */
+#define RWKV_TUNE_WKV6_DV    5  /* value columns per Finch workgroup: 32 or 64 */
+#define RWKV_TUNE_WKV6_SEGS  6  /* Finch time segments, 1..4096 (each >= 4 chunks) */
+int rwkv_set_tuning(int key, int value);
+int rwkv_get_tuning(int key);
+
+/* ------------------------------------------------------------------------
+ * Device-side errors of the RWKV-4 scans.  The first 32-bit word of a
+ * forward or backward workspace is an error word, 0 while all is well:
+ *   bit 0 (1): a tile waited for its predecessors longer than its spin limit
+ *              (about 2^24 polls) and gave up; its outputs are NaN;
+ *   bit 1 (2): a tile claim found a workspace that was never zero-filled;
+ *              the rows of that tile are NaN.
+ * Either bit means the outputs of the calls made since the word was last 0
+ * are not to be trusted.  The word is sticky: zero-filling the workspace
+ * (always allowed between calls) clears it.
+ * rwkv_wkv4_workspace_error enqueues on `stream` a copy of the word into
+ * *err (device memory or pinned host memory; valid once the stream has
+ * reached that point).  It checks only its own arguments.
+ * ---------------------------------------------------------------------- */
+int rwkv_wkv4_workspace_error(const void* ws, size_t ws_bytes, uint32_t* err,
+                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * RWKV-4 time-parallel forward.   [RWKV-digest] (2) Time-mixing, WKV_t;
  * [RWKV-summary] sec. 3 "The WKV Operator".
  *
@@ -81,6 +122,11 @@ int rwkv_last_hip_error(void);
  *                        whose workspace size is 0 accepts ws == NULL.
  * Accuracy: max |y - exact| <= 1e-4 * S, where S is the same weighted mean
  * taken over |v| (float32 arithmetic, hardware exp2 and reciprocal).
+ * Limit: T <= 2^24 - 64 per call (decay counts are held in float32, exact
+ * for integers up to 2^24); longer sequences are cut and chained through
+ * rwkv_wkv4_forward_state.  Larger T returns RWKV_ERR_UNSUPPORTED (and the
+ * workspace query 0).  The same limit holds for the backward and training
+ * calls.
  * ---------------------------------------------------------------------- */
 size_t rwkv_wkv4_forward_workspace(int64_t B, int64_t T, int64_t C);
 int rwkv_wkv4_forward(int64_t B, int64_t T, int64_t C,

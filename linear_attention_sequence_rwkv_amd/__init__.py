@@ -18,11 +18,17 @@ import threading
 __all__ = [
     "LIB_PATH", "load_library", "RwkvError",
     "rwkv_abi_version", "rwkv_status_str", "rwkv_last_hip_error",
+    "RWKV_TUNE_WKV4_TILE", "RWKV_TUNE_WKV4_ORDER", "RWKV_TUNE_WKV5_DV",
+    "RWKV_TUNE_WKV5_SEGS", "RWKV_TUNE_WKV6_DV", "RWKV_TUNE_WKV6_SEGS",
+    "rwkv_set_tuning", "rwkv_get_tuning", "tuning",
+    "rwkv_wkv4_workspace_error",
     "rwkv_wkv4_forward_workspace", "rwkv_wkv4_forward", "rwkv_wkv4_forward_state",
     "rwkv_wkv4_backward_workspace", "rwkv_wkv4_backward",
     "rwkv_wkv4_forward_train", "rwkv_wkv4_backward_after_forward",
     "rwkv_wkv4_state_init", "rwkv_wkv4_step",
-    "rwkv_wkv5_forward_workspace", "rwkv_wkv5_forward",
+    "rwkv_wkv5_forward_workspace", "rwkv_wkv5_forward", "rwkv_wkv5_forward_state",
+    "rwkv_wkv5_step",
+    "rwkv_wkv6_forward_workspace", "rwkv_wkv6_forward", "rwkv_wkv6_step",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librwkv_wkv.so")
@@ -39,6 +45,9 @@ _SIGNATURES = {
     "rwkv_abi_version": (ctypes.c_int, []),
     "rwkv_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "rwkv_last_hip_error": (ctypes.c_int, []),
+    "rwkv_set_tuning": (ctypes.c_int, [ctypes.c_int, ctypes.c_int]),
+    "rwkv_get_tuning": (ctypes.c_int, [ctypes.c_int]),
+    "rwkv_wkv4_workspace_error": (ctypes.c_int, [_p, _sz, _p, _p]),
     "rwkv_wkv4_forward_workspace": (_sz, [_i64, _i64, _i64]),
     "rwkv_wkv4_forward": (ctypes.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "rwkv_wkv4_forward_state": (ctypes.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _p,
@@ -115,6 +124,41 @@ def rwkv_last_hip_error() -> int:
     return load_library().rwkv_last_hip_error()
 
 
+# Plan override keys (include/rwkv_wkv.h).
+RWKV_TUNE_WKV4_TILE = 1
+RWKV_TUNE_WKV4_ORDER = 2
+RWKV_TUNE_WKV5_DV = 3
+RWKV_TUNE_WKV5_SEGS = 4
+RWKV_TUNE_WKV6_DV = 5
+RWKV_TUNE_WKV6_SEGS = 6
+
+
+def rwkv_set_tuning(key: int, value: int) -> None:
+    _check("rwkv_set_tuning", load_library().rwkv_set_tuning(key, value))
+
+
+def rwkv_get_tuning(key: int) -> int:
+    return int(load_library().rwkv_get_tuning(key))
+
+
+class tuning:
+    """Context manager: a plan override for the duration of a block, e.g.
+    ``with tuning(RWKV_TUNE_WKV5_DV, 32): ...`` (the previous value returns
+    afterwards)."""
+
+    def __init__(self, key: int, value: int):
+        self.key, self.value, self.old = key, value, None
+
+    def __enter__(self):
+        self.old = rwkv_get_tuning(self.key)
+        rwkv_set_tuning(self.key, self.value)
+        return self
+
+    def __exit__(self, *exc):
+        rwkv_set_tuning(self.key, self.old)
+        return False
+
+
 # ---------------------------------------------------------------- helpers ---
 
 def _torch():
@@ -141,32 +185,88 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
 
 
-def _stream(device, stream=None):
+def _launch_stream(device, stream=None):
+    """(torch stream, handle) of the stream the library call is enqueued on."""
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream(device)
-    return ctypes.c_void_p(s.cuda_stream)
+    return s, ctypes.c_void_p(s.cuda_stream)
+
+
+def _use_on(stream, *tensors):
+    """A call on a stream other than torch's current one: tell torch's
+    allocator that these tensors are in use there until that stream's work
+    is done (outputs the binding allocates are allocated on `stream` itself,
+    see _alloc)."""
+    torch = _torch()
+    if stream is None or stream == torch.cuda.current_stream(stream.device):
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
+def _alloc(stream, fn, *args, **kw):
+    """Allocate (and fill) a tensor with torch on `stream`, so that its
+    memory is ordered with the library call enqueued there."""
+    torch = _torch()
+    with torch.cuda.stream(stream):
+        return fn(*args, **kw)
 
 
 # Workspaces are zero-filled once and reused per (device, stream): the
-# library leaves them ready for the next call on the same stream.
+# library leaves them ready for the next call on the same stream.  The fill
+# and the allocation happen on that stream, ahead of the call.
 _ws_cache: dict = {}
 _ws_lock = threading.Lock()
 
 
-def _workspace(kind: str, device, stream_handle: int, nbytes: int):
+def _workspace(kind: str, device, stream, nbytes: int):
     if nbytes == 0:
         return None
     torch = _torch()
-    key = (kind, device.index, stream_handle)
+    key = (kind, device.index, stream.cuda_stream)
     with _ws_lock:
         buf = _ws_cache.get(key)
         if buf is None or buf.numel() < nbytes:
-            buf = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+            buf = _alloc(stream, torch.zeros, max(nbytes, 1 << 16), dtype=torch.uint8,
+                         device=device)
             _ws_cache[key] = buf
         return buf
 
 
+def rwkv_wkv4_workspace_error(ws, stream=None) -> int:
+    """The error word of an RWKV-4 workspace (0: no device-side error since
+    it was zero-filled).  Synchronises ``stream`` (default: the current one)."""
+    torch = _torch()
+    lib = load_library()
+    ws = _dev_tensor("ws", ws, (torch.uint8,))
+    s, sh = _launch_stream(ws.device, stream)
+    out = _alloc(s, torch.zeros, 1, dtype=torch.int32, device=ws.device)
+    _check("rwkv_wkv4_workspace_error",
+           lib.rwkv_wkv4_workspace_error(_ptr(ws), ws.numel(), _ptr(out), sh))
+    s.synchronize()
+    return int(out.item()) & 0xFFFFFFFF
+
+
+def default_workspace(kind: str, device, stream=None):
+    """The workspace the binding keeps for (kind, device, stream), or None;
+    kind is one of "wkv4", "wkv4_bwd", "wkv5", "wkv6"."""
+    torch = _torch()
+    dev = torch.device(device)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    with _ws_lock:
+        return _ws_cache.get((kind, dev.index, s.cuda_stream))
+
+
 # ----------------------------------------------------------------- RWKV-4 ---
+#
+# Every entry point enqueues on ``stream`` (default: torch's current stream).
+# Outputs the binding allocates, and its cached workspaces, are allocated (and
+# zero-filled) on that stream, so they are ordered with the call; with an
+# explicit stream that is not the current one, every tensor argument is
+# recorded on it for torch's allocator.  Inputs written on another stream must
+# be made visible to ``stream`` by the caller, as for any torch work on a side
+# stream.
 
 def rwkv_wkv4_forward_workspace(B: int, T: int, C: int) -> int:
     return int(load_library().rwkv_wkv4_forward_workspace(B, T, C))
@@ -185,25 +285,23 @@ def _wkv4_inputs(w, u, k, v):
     return w, u, k, v
 
 
-def _wkv4_forward_args(w, u, k, v, y):
+def _out(name, t, shape, device, s):
+    """A float32 output: allocated on the launch stream, or the caller's
+    tensor checked for shape."""
     torch = _torch()
-    f32 = (torch.float32,)
-    w, u, k, v = _wkv4_inputs(w, u, k, v)
-    B, T, C = k.shape
-    if y is None:
-        y = torch.empty_like(k)
-    else:
-        y = _dev_tensor("y", y, f32, 3)
-        if tuple(y.shape) != (B, T, C):
-            raise ValueError("y has the wrong shape")
-    return w, u, k, v, y
+    if t is None:
+        return _alloc(s, torch.empty, shape, dtype=torch.float32, device=device)
+    t = _dev_tensor(name, t, (torch.float32,), len(shape))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has the wrong shape")
+    return t
 
 
-def _wkv4_ws(lib, k, ws, st):
+def _wkv4_ws(lib, k, ws, s):
     B, T, C = k.shape
     need = lib.rwkv_wkv4_forward_workspace(B, T, C)
     if ws is None:
-        ws = _workspace("wkv4", k.device, st.value or 0, need)
+        ws = _workspace("wkv4", k.device, s, need)
     return ws, (0 if ws is None else ws.numel() * ws.element_size())
 
 
@@ -215,12 +313,14 @@ def rwkv_wkv4_forward(w, u, k, v, y=None, ws=None, stream=None):
     per (device, stream) is used.
     """
     lib = load_library()
-    w, u, k, v, y = _wkv4_forward_args(w, u, k, v, y)
+    w, u, k, v = _wkv4_inputs(w, u, k, v)
     B, T, C = k.shape
-    st = _stream(k.device, stream)
-    ws, nbytes = _wkv4_ws(lib, k, ws, st)
+    s, sh = _launch_stream(k.device, stream)
+    y = _out("y", y, (B, T, C), k.device, s)
+    ws, nbytes = _wkv4_ws(lib, k, ws, s)
+    _use_on(stream, w, u, k, v, y, ws)
     status = lib.rwkv_wkv4_forward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
-                                   _ptr(ws), nbytes, st)
+                                   _ptr(ws), nbytes, sh)
     _check("rwkv_wkv4_forward", status)
     return y
 
@@ -246,19 +346,21 @@ def rwkv_wkv4_forward_state(w, u, k, v, state_in=None, state_out=None, y=None, w
     """
     torch = _torch()
     lib = load_library()
-    w, u, k, v, y = _wkv4_forward_args(w, u, k, v, y)
+    w, u, k, v = _wkv4_inputs(w, u, k, v)
     B, T, C = k.shape
+    s, sh = _launch_stream(k.device, stream)
+    y = _out("y", y, (B, T, C), k.device, s)
     sin = (None, None, None) if state_in is None else _wkv4_state_args("state_in", state_in, B, C)
     if state_out is True:
-        state_out = tuple(torch.empty((B, C), dtype=torch.float32, device=k.device)
+        state_out = tuple(_alloc(s, torch.empty, (B, C), dtype=torch.float32, device=k.device)
                           for _ in range(3))
     sout = (None, None, None) if state_out is None else _wkv4_state_args("state_out", state_out,
                                                                         B, C)
-    st = _stream(k.device, stream)
-    ws, nbytes = _wkv4_ws(lib, k, ws, st)
+    ws, nbytes = _wkv4_ws(lib, k, ws, s)
+    _use_on(stream, w, u, k, v, y, ws, *sin, *sout)
     status = lib.rwkv_wkv4_forward_state(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
                                          *(_ptr(t) for t in sin), *(_ptr(t) for t in sout),
-                                         _ptr(ws), nbytes, st)
+                                         _ptr(ws), nbytes, sh)
     _check("rwkv_wkv4_forward_state", status)
     return y, (None if state_out is None else sout)
 
@@ -277,33 +379,24 @@ def rwkv_wkv4_backward(w, u, k, v, gy, gw=None, gu=None, gk=None, gv=None, ws=No
     """
     torch = _torch()
     lib = load_library()
-    f32 = (torch.float32,)
     w, u, k, v = _wkv4_inputs(w, u, k, v)
     B, T, C = k.shape
-    gy = _dev_tensor("gy", gy, f32, 3)
+    gy = _dev_tensor("gy", gy, (torch.float32,), 3)
     if tuple(gy.shape) != (B, T, C):
         raise ValueError("gy has the wrong shape")
-
-    def out(name, t, shape):
-        if t is None:
-            return torch.empty(shape, dtype=torch.float32, device=k.device)
-        t = _dev_tensor(name, t, f32, len(shape))
-        if tuple(t.shape) != shape:
-            raise ValueError(f"{name} has the wrong shape")
-        return t
-
-    gw, gu = out("gw", gw, (C,)), out("gu", gu, (C,))
-    gk, gv = out("gk", gk, (B, T, C)), out("gv", gv, (B, T, C))
-    st = _stream(k.device, stream)
+    s, sh = _launch_stream(k.device, stream)
+    gw, gu = _out("gw", gw, (C,), k.device, s), _out("gu", gu, (C,), k.device, s)
+    gk, gv = _out("gk", gk, (B, T, C), k.device, s), _out("gv", gv, (B, T, C), k.device, s)
     need = lib.rwkv_wkv4_backward_workspace(B, T, C)
     if ws is None:
         if _entry != "rwkv_wkv4_backward":
             raise ValueError("rwkv_wkv4_backward_after_forward needs the workspace that "
                              "rwkv_wkv4_forward_train used")
-        ws = _workspace("wkv4_bwd", k.device, st.value or 0, need)
+        ws = _workspace("wkv4_bwd", k.device, s, need)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _use_on(stream, w, u, k, v, gy, gw, gu, gk, gv, ws)
     status = getattr(lib, _entry)(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(gy),
-                                  _ptr(gw), _ptr(gu), _ptr(gk), _ptr(gv), _ptr(ws), nbytes, st)
+                                  _ptr(gw), _ptr(gu), _ptr(gk), _ptr(gv), _ptr(ws), nbytes, sh)
     _check(_entry, status)
     return gw, gu, gk, gv
 
@@ -314,14 +407,16 @@ def rwkv_wkv4_forward_train(w, u, k, v, ws, y=None, stream=None):
     rwkv_wkv4_backward_workspace(B, T, C) bytes) the tile histories that
     rwkv_wkv4_backward_after_forward reads instead of recomputing."""
     lib = load_library()
-    w, u, k, v, y = _wkv4_forward_args(w, u, k, v, y)
+    w, u, k, v = _wkv4_inputs(w, u, k, v)
     B, T, C = k.shape
     if ws is None:
         raise ValueError("rwkv_wkv4_forward_train needs a backward workspace")
-    st = _stream(k.device, stream)
+    s, sh = _launch_stream(k.device, stream)
+    y = _out("y", y, (B, T, C), k.device, s)
     nbytes = ws.numel() * ws.element_size()
+    _use_on(stream, w, u, k, v, y, ws)
     status = lib.rwkv_wkv4_forward_train(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
-                                         _ptr(ws), nbytes, st)
+                                         _ptr(ws), nbytes, sh)
     _check("rwkv_wkv4_forward_train", status)
     return y
 
@@ -339,8 +434,10 @@ def rwkv_wkv4_state_init(B: int, C: int, device="cuda", stream=None):
     torch = _torch()
     lib = load_library()
     dev = torch.device(device)
-    a, b, p = (torch.empty((B, C), dtype=torch.float32, device=dev) for _ in range(3))
-    status = lib.rwkv_wkv4_state_init(B, C, _ptr(a), _ptr(b), _ptr(p), _stream(dev, stream))
+    s, sh = _launch_stream(dev, stream)
+    a, b, p = (_alloc(s, torch.empty, (B, C), dtype=torch.float32, device=dev)
+               for _ in range(3))
+    status = lib.rwkv_wkv4_state_init(B, C, _ptr(a), _ptr(b), _ptr(p), sh)
     _check("rwkv_wkv4_state_init", status)
     return a, b, p
 
@@ -361,14 +458,11 @@ def rwkv_wkv4_step(a, b, p, w, u, k, v, y=None, stream=None):
             raise ValueError(f"{n} has the wrong shape")
     if w.shape[0] != C or u.shape[0] != C:
         raise ValueError("w, u must have C entries")
-    if y is None:
-        y = torch.empty_like(k)
-    else:
-        y = _dev_tensor("y", y, f32, 2)
-        if tuple(y.shape) != (B, C):
-            raise ValueError("y has the wrong shape")
+    s, sh = _launch_stream(a.device, stream)
+    y = _out("y", y, (B, C), a.device, s)
+    _use_on(stream, a, b, p, w, u, k, v, y)
     status = lib.rwkv_wkv4_step(B, C, _ptr(a), _ptr(b), _ptr(p), _ptr(w), _ptr(u), _ptr(k),
-                                _ptr(v), _ptr(y), _stream(a.device, stream))
+                                _ptr(v), _ptr(y), sh)
     _check("rwkv_wkv4_step", status)
     return y
 
@@ -379,7 +473,7 @@ def rwkv_wkv5_forward_workspace(B: int, T: int, H: int, D: int) -> int:
     return int(load_library().rwkv_wkv5_forward_workspace(B, T, H, D))
 
 
-def _wkv5_args(r, k, v, w, u, o, ndim):
+def _wkv5_args(r, k, v, w, u, ndim):
     torch = _torch()
     half = (torch.bfloat16, torch.int16, torch.uint16)
     r = _dev_tensor("r", r, half, ndim)
@@ -394,42 +488,46 @@ def _wkv5_args(r, k, v, w, u, o, ndim):
         raise ValueError("r, k, v shapes differ")
     if (w is not None and tuple(w.shape) != (H, D)) or tuple(u.shape) != (H, D):
         raise ValueError("w, u must be [H, D]")
-    if o is None:
-        o = torch.empty(shape, dtype=torch.float32, device=r.device)
-    else:
-        o = _dev_tensor("o", o, (torch.float32,), ndim)
-        if tuple(o.shape) != shape:
-            raise ValueError("o has the wrong shape")
-    return r, k, v, w, u, o
+    return r, k, v, w, u
 
 
-def _wkv5_ws(lib, r, ws, st):
-    B, T, H, D = r.shape
-    need = lib.rwkv_wkv5_forward_workspace(B, T, H, D)
+def _ws(kind, query, shape, device, ws, s):
+    need = query(*shape)
     if ws is None:
-        ws = _workspace("wkv5", r.device, st.value or 0, need)
+        ws = _workspace(kind, device, s, need)
     return ws, (0 if ws is None else ws.numel() * ws.element_size())
 
 
 def rwkv_wkv5_forward(r, k, v, w, u, o=None, ws=None, stream=None):
     """o[B,T,H,D] float32 from bf16 r, k, v [B,T,H,D] and float32 w, u [H,D]."""
     lib = load_library()
-    r, k, v, w, u, o = _wkv5_args(r, k, v, w, u, o, 4)
+    r, k, v, w, u = _wkv5_args(r, k, v, w, u, 4)
     B, T, H, D = r.shape
-    st = _stream(r.device, stream)
-    ws, nbytes = _wkv5_ws(lib, r, ws, st)
+    s, sh = _launch_stream(r.device, stream)
+    o = _out("o", o, (B, T, H, D), r.device, s)
+    ws, nbytes = _ws("wkv5", lib.rwkv_wkv5_forward_workspace, (B, T, H, D), r.device, ws, s)
+    _use_on(stream, r, k, v, w, u, o, ws)
     status = lib.rwkv_wkv5_forward(B, T, H, D, _ptr(r), _ptr(k), _ptr(v), _ptr(w), _ptr(u),
-                                   _ptr(o), _ptr(ws), nbytes, st)
+                                   _ptr(o), _ptr(ws), nbytes, sh)
     _check("rwkv_wkv5_forward", status)
     return o
 
 
-def _wkv5_state_arg(name, s, B, H, D):
+def _wkv5_state_arg(name, st, B, H, D):
     torch = _torch()
-    s = _dev_tensor(name, s, (torch.float32,), 4)
-    if tuple(s.shape) != (B, H, D, D):
+    st = _dev_tensor(name, st, (torch.float32,), 4)
+    if tuple(st.shape) != (B, H, D, D):
         raise ValueError(f"{name} must be [B, H, D, D] = [{B}, {H}, {D}, {D}]")
-    return s
+    return st
+
+
+def _state_out(s_out, B, H, D, device, s):
+    torch = _torch()
+    if s_out is True:
+        return _alloc(s, torch.empty, (B, H, D, D), dtype=torch.float32, device=device)
+    if s_out is not None:
+        return _wkv5_state_arg("s_out", s_out, B, H, D)
+    return None
 
 
 def rwkv_wkv5_forward_state(r, k, v, w, u, s_in=None, s_out=None, o=None, ws=None,
@@ -439,21 +537,19 @@ def rwkv_wkv5_forward_state(r, k, v, w, u, s_in=None, s_out=None, o=None, ws=Non
     ``s_out``: None (not wanted), True (allocate) or a float32 [B,H,D,D]
     tensor (may be ``s_in``).  Returns (o, s_out).
     """
-    torch = _torch()
     lib = load_library()
-    r, k, v, w, u, o = _wkv5_args(r, k, v, w, u, o, 4)
+    r, k, v, w, u = _wkv5_args(r, k, v, w, u, 4)
     B, T, H, D = r.shape
+    s, sh = _launch_stream(r.device, stream)
+    o = _out("o", o, (B, T, H, D), r.device, s)
     if s_in is not None:
         s_in = _wkv5_state_arg("s_in", s_in, B, H, D)
-    if s_out is True:
-        s_out = torch.empty((B, H, D, D), dtype=torch.float32, device=r.device)
-    if s_out is not None:
-        s_out = _wkv5_state_arg("s_out", s_out, B, H, D)
-    st = _stream(r.device, stream)
-    ws, nbytes = _wkv5_ws(lib, r, ws, st)
+    s_out = _state_out(s_out, B, H, D, r.device, s)
+    ws, nbytes = _ws("wkv5", lib.rwkv_wkv5_forward_workspace, (B, T, H, D), r.device, ws, s)
+    _use_on(stream, r, k, v, w, u, o, ws, s_in, s_out)
     status = lib.rwkv_wkv5_forward_state(B, T, H, D, _ptr(r), _ptr(k), _ptr(v), _ptr(w),
                                          _ptr(u), _ptr(o), _ptr(s_in), _ptr(s_out), _ptr(ws),
-                                         nbytes, st)
+                                         nbytes, sh)
     _check("rwkv_wkv5_forward_state", status)
     return o, s_out
 
@@ -464,11 +560,14 @@ def rwkv_wkv5_step(s, r, k, v, w, u, o=None, stream=None):
     Returns o [B,H,D] float32.
     """
     lib = load_library()
-    r, k, v, w, u, o = _wkv5_args(r, k, v, w, u, o, 3)
+    r, k, v, w, u = _wkv5_args(r, k, v, w, u, 3)
     B, H, D = r.shape
-    s = _wkv5_state_arg("s", s, B, H, D)
-    status = lib.rwkv_wkv5_step(B, H, D, _ptr(s), _ptr(r), _ptr(k), _ptr(v), _ptr(w), _ptr(u),
-                                _ptr(o), _stream(r.device, stream))
+    st = _wkv5_state_arg("s", s, B, H, D)
+    ls, sh = _launch_stream(r.device, stream)
+    o = _out("o", o, (B, H, D), r.device, ls)
+    _use_on(stream, st, r, k, v, w, u, o)
+    status = lib.rwkv_wkv5_step(B, H, D, _ptr(st), _ptr(r), _ptr(k), _ptr(v), _ptr(w), _ptr(u),
+                                _ptr(o), sh)
     _check("rwkv_wkv5_step", status)
     return o
 
@@ -491,24 +590,19 @@ def rwkv_wkv6_forward(r, k, v, w, u, s_in=None, s_out=None, o=None, ws=None, str
     """Finch forward: r, k, v [B,T,H,D] bf16, w [B,T,H,D] float32 per-token
     decays, u [H,D].  ``s_in``/``s_out`` as for rwkv_wkv5_forward_state.
     Returns (o, s_out)."""
-    torch = _torch()
     lib = load_library()
-    r, k, v, _, u, o = _wkv5_args(r, k, v, None, u, o, 4)
+    r, k, v, _, u = _wkv5_args(r, k, v, None, u, 4)
     B, T, H, D = r.shape
     w = _finch_w(w, (B, T, H, D))
+    s, sh = _launch_stream(r.device, stream)
+    o = _out("o", o, (B, T, H, D), r.device, s)
     if s_in is not None:
         s_in = _wkv5_state_arg("s_in", s_in, B, H, D)
-    if s_out is True:
-        s_out = torch.empty((B, H, D, D), dtype=torch.float32, device=r.device)
-    if s_out is not None:
-        s_out = _wkv5_state_arg("s_out", s_out, B, H, D)
-    st = _stream(r.device, stream)
-    need = lib.rwkv_wkv6_forward_workspace(B, T, H, D)
-    if ws is None:
-        ws = _workspace("wkv6", r.device, st.value or 0, need)
-    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    s_out = _state_out(s_out, B, H, D, r.device, s)
+    ws, nbytes = _ws("wkv6", lib.rwkv_wkv6_forward_workspace, (B, T, H, D), r.device, ws, s)
+    _use_on(stream, r, k, v, w, u, o, ws, s_in, s_out)
     status = lib.rwkv_wkv6_forward(B, T, H, D, _ptr(r), _ptr(k), _ptr(v), _ptr(w), _ptr(u),
-                                   _ptr(o), _ptr(s_in), _ptr(s_out), _ptr(ws), nbytes, st)
+                                   _ptr(o), _ptr(s_in), _ptr(s_out), _ptr(ws), nbytes, sh)
     _check("rwkv_wkv6_forward", status)
     return o, s_out
 
@@ -517,11 +611,14 @@ def rwkv_wkv6_step(s, r, k, v, w, u, o=None, stream=None):
     """One Finch token: r, k, v [B,H,D] bf16, w [B,H,D] float32; s updated in
     place.  Returns o [B,H,D] float32."""
     lib = load_library()
-    r, k, v, _, u, o = _wkv5_args(r, k, v, None, u, o, 3)
+    r, k, v, _, u = _wkv5_args(r, k, v, None, u, 3)
     B, H, D = r.shape
     w = _finch_w(w, (B, H, D))
-    s = _wkv5_state_arg("s", s, B, H, D)
-    status = lib.rwkv_wkv6_step(B, H, D, _ptr(s), _ptr(r), _ptr(k), _ptr(v), _ptr(w), _ptr(u),
-                                _ptr(o), _stream(r.device, stream))
+    st = _wkv5_state_arg("s", s, B, H, D)
+    ls, sh = _launch_stream(r.device, stream)
+    o = _out("o", o, (B, H, D), r.device, ls)
+    _use_on(stream, st, r, k, v, w, u, o)
+    status = lib.rwkv_wkv6_step(B, H, D, _ptr(st), _ptr(r), _ptr(k), _ptr(v), _ptr(w), _ptr(u),
+                                _ptr(o), sh)
     _check("rwkv_wkv6_step", status)
     return o

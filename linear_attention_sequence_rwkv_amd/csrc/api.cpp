@@ -4,8 +4,13 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
+#include <atomic>
 #include <initializer_list>
+#include <mutex>
 
 #include "rwkv_wkv.h"
 #include "wkv_internal.h"
@@ -46,6 +51,67 @@ int hip_status(hipError_t e) {
 
 }  // namespace
 
+// ------------------------------------------------------------ plan overrides
+
+namespace rwkv {
+
+namespace {
+
+std::atomic<int> g_tune[kTuneKeys];
+std::once_flag g_tune_once;
+
+int env_int(const char* name) {
+  const char* e = getenv(name);
+  return e ? atoi(e) : 0;
+}
+
+// The environment's overrides, read once; values that no plan accepts are
+// ignored (the built-in plan stays).
+void tuning_from_env() {
+  if (const char* e = getenv("RWKV_WKV4_TILE")) {
+    int c = 0, l = 0, nw = 0;
+    if (sscanf(e, "%d,%d,%d", &c, &l, &nw) == 3 && c > 0 && l > 0 && nw > 0)
+      set_tuning(kTuneWkv4Tile, c * 10000 + l * 100 + nw);
+  }
+  if (const char* e = getenv("RWKV_WKV4_ORDER"))
+    if (strcmp(e, "claim") == 0) set_tuning(kTuneWkv4Order, 1);
+  set_tuning(kTuneWkv5Dv, env_int("RWKV_WKV5_DV"));
+  set_tuning(kTuneWkv5Segs, env_int("RWKV_WKV5_SEGS"));
+  set_tuning(kTuneWkv6Dv, env_int("RWKV_WKV6_DV"));
+  set_tuning(kTuneWkv6Segs, env_int("RWKV_WKV6_SEGS"));
+}
+
+}  // namespace
+
+bool set_tuning(int key, int value) {
+  bool ok = false;
+  switch (key) {
+    case kTuneWkv4Tile: ok = value == 0 || wkv4_variant_exists(value); break;
+    case kTuneWkv4Order: ok = value == 0 || value == 1; break;
+    case kTuneWkv5Dv: ok = value == 0 || value == 16 || value == 32 || value == 64; break;
+    case kTuneWkv6Dv: ok = value == 0 || value == 32 || value == 64; break;
+    case kTuneWkv5Segs:
+    case kTuneWkv6Segs: ok = value >= 0 && value <= 4096; break;
+    default: ok = false;
+  }
+  if (ok) g_tune[key].store(value, std::memory_order_relaxed);
+  return ok;
+}
+
+int tuning(int key) {
+  std::call_once(g_tune_once, tuning_from_env);
+  return key > 0 && key < kTuneKeys ? g_tune[key].load(std::memory_order_relaxed) : 0;
+}
+
+}  // namespace rwkv
+
+RWKV_API int rwkv_set_tuning(int key, int value) {
+  rwkv::tuning(key);  // the environment is read before the first explicit setting
+  return rwkv::set_tuning(key, value) ? RWKV_OK : RWKV_ERR_UNSUPPORTED;
+}
+
+RWKV_API int rwkv_get_tuning(int key) { return rwkv::tuning(key); }
+
 RWKV_API int rwkv_abi_version(void) { return RWKV_WKV_ABI_VERSION; }
 
 RWKV_API const char* rwkv_status_str(int status) {
@@ -62,6 +128,14 @@ RWKV_API const char* rwkv_status_str(int status) {
 }
 
 RWKV_API int rwkv_last_hip_error(void) { return g_last_hip_error; }
+
+RWKV_API int rwkv_wkv4_workspace_error(const void* ws, size_t ws_bytes, uint32_t* err,
+                                       hipStream_t stream) {
+  if (!ws || !err) return RWKV_ERR_NULLPTR;
+  if (ws_bytes < sizeof(uint32_t)) return RWKV_ERR_WORKSPACE;
+  if (!aligned16(ws)) return RWKV_ERR_ALIGN;
+  return hip_status(hipMemcpyAsync(err, ws, sizeof(uint32_t), hipMemcpyDefault, stream));
+}
 
 // ------------------------------------------------------------------ RWKV-4
 

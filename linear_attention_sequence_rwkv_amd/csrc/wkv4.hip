@@ -37,10 +37,6 @@
 #include "wkv_device.h"
 #include "wkv_internal.h"
 
-#include <stdio.h>
-#include <stdlib.h>
-#include <string.h>
-
 #include <mutex>
 
 
@@ -79,6 +75,24 @@ __device__ __forceinline__ void emit_rows(Rsrc ry, uint32_t voff, uint32_t row_b
       store_row<CPL>(ry, voff, uint32_t(s) * row_bytes, ys);
     }
   }
+}
+
+// NaN over one tile's output rows: the mark of a tile that could not run.
+template <int CPL, int L, int NW>
+__device__ void nan_rows(int tile, int g, int T, int C, int n_cblk, float* __restrict__ y) {
+  constexpr int W = 64 * CPL;
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int bi = g / n_cblk, cb = g - bi * n_cblk;
+  const int t0 = tile * L * NW + wid * L;
+  const int n = max(0, min(L, T - t0));
+#pragma unroll 1
+  for (int s = 0; s < n; ++s)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = cb * W + lane * CPL + c;
+      if (ch < C) y[(size_t(bi) * T + t0 + s) * C + ch] = __builtin_nanf("");
+    }
 }
 
 // Optional recurrent state around a forward call, in the step API's form
@@ -155,9 +169,11 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
     __syncthreads();
     tile = __builtin_amdgcn_readfirstlane(s_tile);
     // Only a workspace that was never zero-filled can get here: flag it and
-    // touch nothing.
+    // write NaN over the rows of the tile this workgroup's launch index
+    // names (the caller must not mistake them for results).
     if (tile < 0 || tile >= n_tiles) {
-      if (threadIdx.x == 0) raise_error(hdr + kHdrError, 2u);
+      if (threadIdx.x == 0) raise_error(hdr + kHdrError, kErrNotZeroed);
+      if (EMIT) nan_rows<CPL, L, NW>(int(blockIdx.x) / groups, g, T, C, n_cblk, y);
       return;
     }
   }
@@ -332,7 +348,7 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
           if (ok) break;
         }
         if (++spins > kSpinLimit) {
-          if (lane == 0) raise_error(hdr + kHdrError, 1u);
+          if (lane == 0) raise_error(hdr + kHdrError, kErrGaveUp);
 #pragma unroll
           for (int c = 0; c < CPL; ++c) {
             const float nan = __builtin_nanf("");
@@ -483,10 +499,10 @@ constexpr Variant kVariants[] = {{4, 8, 8}, {4, 16, 4}, {4, 16, 8},
 
 // Workgroups of `kern` (`block` threads, no dynamic LDS) that the current
 // device holds at once, cached per device; 0 if it cannot be determined, or
-// if RWKV_WKV4_ORDER=claim asks for claimed tiles (tests compare the modes).
+// if the kTuneWkv4Order override asks for claimed tiles (tests compare the
+// modes).
 int64_t resident_workgroups(const void* kern, int block) {
-  if (const char* env = getenv("RWKV_WKV4_ORDER"))
-    if (strcmp(env, "claim") == 0) return 0;
+  if (tuning(kTuneWkv4Order) == 1) return 0;
   constexpr int kMaxDev = 64;
   struct Entry {
     const void* kern;
@@ -542,7 +558,7 @@ bool wkv4_plan_fixed(int64_t B, int64_t T, int64_t C, int cpl, int L, int NW, Wk
   p.groups = B * p.n_cblk;
   // Tiles, token and channel indices are 32-bit in the kernel; byte offsets
   // within a wave's rows are 32-bit, below the 2^31 drop offset.
-  if (p.n_tiles * p.groups >= (int64_t(1) << 31) || T >= (int64_t(1) << 31) ||
+  if (p.n_tiles * p.groups >= (int64_t(1) << 31) || T > kWkv4MaxT ||
       p.groups >= (int64_t(1) << 31) ||
       (int64_t(L - 1) * C + 64 * cpl) * 4 >= (int64_t(1) << 31))
     return false;
@@ -563,18 +579,22 @@ bool wkv4_plan(int64_t B, int64_t T, int64_t C, Wkv4Plan* plan) {
     L = 64;
     NW = 1;
   }
-  if (const char* env = getenv("RWKV_WKV4_TILE")) {
-    int c = 0, l = 0, nw = 0;
-    if (sscanf(env, "%d,%d,%d", &c, &l, &nw) == 3 && C % c == 0) {
-      for (const Variant& vv : kVariants)
-        if (vv.cpl == c && vv.L == l && vv.NW == nw) {
-          cpl = c;
-          L = l;
-          NW = nw;
-        }
-    }
+  // An override applies where its channel width divides C.
+  if (const int code = tuning(kTuneWkv4Tile)) {
+    for (const Variant& vv : kVariants)
+      if (vv.cpl * 10000 + vv.L * 100 + vv.NW == code && C % vv.cpl == 0) {
+        cpl = vv.cpl;
+        L = vv.L;
+        NW = vv.NW;
+      }
   }
   return wkv4_plan_fixed(B, T, C, cpl, L, NW, plan);
+}
+
+bool wkv4_variant_exists(int code) {
+  for (const Variant& vv : kVariants)
+    if (vv.cpl * 10000 + vv.L * 100 + vv.NW == code) return true;
+  return false;
 }
 
 hipError_t wkv4_prefix_launch(const Wkv4Plan& pl, int64_t T, int64_t C, const float* w,

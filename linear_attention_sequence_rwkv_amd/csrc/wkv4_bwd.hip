@@ -125,7 +125,22 @@ __global__ __launch_bounds__(64 * NW) void wkv4_bwd_tiled(
   const int tile = __builtin_amdgcn_readfirstlane(s_tile);
   const uint32_t tag = __builtin_amdgcn_readfirstlane(s_tag);
   if (tile < 0 || tile >= n_tiles) {
-    if (threadIdx.x == 0) raise_error(hdr + kHdrError, 2u);
+    // A workspace that was never zero-filled: flag it, and write NaN over the
+    // gradient rows of the tile this workgroup's launch index names.
+    if (threadIdx.x == 0) raise_error(hdr + kHdrError, kErrNotZeroed);
+    const int lt = n_tiles - 1 - int(blockIdx.x) / groups;
+    const int bi = g / n_cblk, cb = g - bi * n_cblk;
+    const int ch = cb * 64 + (threadIdx.x & 63);
+    const int t0 = lt * L * NW + int(threadIdx.x >> 6) * L;
+    const int n = max(0, min(L, T - t0));
+    if (ch < C) {
+#pragma unroll 1
+      for (int s = 0; s < n; ++s) {
+        const size_t i = (size_t(bi) * T + t0 + s) * C + ch;
+        gk[i] = __builtin_nanf("");
+        gv[i] = __builtin_nanf("");
+      }
+    }
     return;
   }
   const int bi = g / n_cblk;
@@ -292,7 +307,7 @@ __global__ __launch_bounds__(64 * NW) void wkv4_bwd_tiled(
           }
         }
         if (++spins > kSpinLimit) {
-          if (lane == 0) raise_error(hdr + kHdrError, 1u);
+          if (lane == 0) raise_error(hdr + kHdrError, kErrGaveUp);
           const float nan = __builtin_nanf("");
           suf = RevHist{nan, nan, nan, nan, nan, 0.f};
           break;

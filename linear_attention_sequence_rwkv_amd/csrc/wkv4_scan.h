@@ -22,6 +22,9 @@ __device__ __forceinline__ void raise_error(uint32_t* err, uint32_t bit) {
 
 // Header words (uint32) at the start of a scan workspace.
 enum : int { kHdrError = 0, kHdrEpoch = 1, kHdrClaimed = 2 };
+// Bits of the error word (sticky until the workspace is zero-filled again).
+constexpr uint32_t kErrGaveUp = 1u;     // a look-back exceeded its spin limit
+constexpr uint32_t kErrNotZeroed = 2u;  // a claim found a workspace never zero-filled
 
 __device__ __forceinline__ uint32_t hdr_load(uint32_t* h, int i) {
   return __hip_atomic_load(h + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

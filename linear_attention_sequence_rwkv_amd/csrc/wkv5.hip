@@ -524,26 +524,24 @@ namespace {
 // Time segments per head: about two workgroups per CU over the launch,
 // segments of at least four chunks.  Measured at B=4 T=4096 H=32 with whole
 // heads per workgroup: 242 us in one segment, 128 us in four, 133 us in
-// eight (with 32-column slices the best was 166 us).  RWKV_WKV5_SEGS
-// overrides (tests, sweeps).
+// eight (with 32-column slices the best was 166 us).  The kTuneWkv5Segs
+// override replaces the target (tests, sweeps).
 constexpr int64_t kTargetWorkgroups = 512;
 
 int wkv5_segments(int64_t BH, int64_t T, int ns) {
   const int64_t n_chunks = (T + kL - 1) / kL;
   const int64_t per_seg = (BH + 7) / 8 * 8 * ns;
   int64_t nseg = (kTargetWorkgroups + per_seg - 1) / per_seg;
-  if (const char* env = getenv("RWKV_WKV5_SEGS")) nseg = atoi(env);
+  if (const int o = tuning(kTuneWkv5Segs)) nseg = o;
   nseg = std::max<int64_t>(1, std::min<int64_t>(nseg, n_chunks / 4));
   const int64_t seg_chunks = (n_chunks + nseg - 1) / nseg;
   return int((n_chunks + seg_chunks - 1) / seg_chunks);
 }
 
 int wkv5_dv() {
-  if (const char* env = getenv("RWKV_WKV5_DV")) {
-    const int dv = atoi(env);
-    return dv == 16 || dv == 64 ? dv : 32;
-  }
-  return 64;  // whole heads: the intra-chunk products are not repeated per slice
+  // whole heads by default: the intra-chunk products are not repeated per slice
+  const int o = tuning(kTuneWkv5Dv);
+  return o ? o : 64;
 }
 
 }  // namespace

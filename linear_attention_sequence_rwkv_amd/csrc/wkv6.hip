@@ -46,15 +46,21 @@ constexpr float kMinLog2Decay = -126.f;  // log2 w below this counts as this (2^
 
 // Per-channel ratios of decay powers for a chunk whose decays all satisfy
 // |log2 w| <= 15: every power a product needs is then one power within 8
-// tokens of a block middle (finite in fp32) times one of these:
+// tokens of a block middle (finite in fp32) times some of these:
 //   2^(c_{16b+16} - c_{s+1}) = 2^(c_{16b+8} - c_{s+1}) g_blk[b],
 //   2^(c_64 - c_{s+1})       = 2^(c_{16b+16} - c_{s+1}) h_blk[b],
-//   2^(c_t - c_ref)          = 2^(c_t - c_{16q+8}) q_ref[q][m].
+//   2^(c_t - c_ref)          = (2^(c_t - c_{16q+8}) q_start[q]) q_ref[q][m].
+// The query factor for a reference before the block goes through the
+// block's first token: q_start and q_ref are both <= 1, so their product
+// with 2^(c_t - c_{16q+8}) (up to 2^120) flushes to zero only where the
+// true factor is itself below the float range (a direct ratio
+// 2^(c_{16q+8} - c_ref) could flush while the factor is as large as 2^-6).
 // Ratios that no product uses (a reference after the block) may be inf.
 struct DecayTables {
   float g_blk[4][kD];     // 2^(c_{16b+16} - c_{16b+8})
   float h_blk[4][kD];     // 2^(c_64 - c_{16b+16})
-  float q_ref[4][4][kD];  // [q][m]: 2^(c_{16q+8} - c_ref), ref = 16m+16 (m < 3) or 0 (m = 3)
+  float q_ref[4][4][kD];  // [q][m]: 2^(c_{16q} - c_ref), ref = 16m+16 (m < 3) or 0 (m = 3)
+  float q_start[4][kD];   // 2^(c_{16q+8} - c_{16q}), in [2^-120, 1]
   float cmid[4][kD];      // c_{16b+8}
 };
 
@@ -71,6 +77,8 @@ struct alignas(16) LdsF {
   float beta[kL];
   float u[kD];  // 16-byte aligned: the members before it are multiples of 16 bytes
 };
+// Two workgroups per CU share its 160 KB of LDS.
+static_assert(sizeof(LdsF<64>) <= 80 * 1024, "two Finch workgroups per CU");
 
 // This thread's 16 decay factors (token tid/4, channels 16*(tid%4)..).
 struct ChunkW {
@@ -148,12 +156,13 @@ __device__ __forceinline__ bool decay_prefix(const ChunkW& x, CTable& c, DecayTa
       cend[m] = om + tot[m];
       om += tot[m];
     }
-    const float cm = run[7] + off;
+    const float cm = run[7] + off;  // c_{16 sg + 8}; off = c_{16 sg}
     tab->cmid[sg][ch] = cm;
     tab->g_blk[sg][ch] = exp2_fast(run[15] + off - cm);
     tab->h_blk[sg][ch] = exp2_fast(cend[3] - (run[15] + off));
+    tab->q_start[sg][ch] = exp2_fast(cm - off);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) tab->q_ref[sg][m][ch] = exp2_fast(cm - (m < 3 ? cend[m] : 0.f));
+    for (int m = 0; m < 4; ++m) tab->q_ref[sg][m][ch] = exp2_fast(off - (m < 3 ? cend[m] : 0.f));
   }
   __syncthreads();
   return exact;
@@ -389,11 +398,16 @@ __global__ __launch_bounds__(256, 2) void wkv6_fwd_chunked(
           x[0] = a.x, x[1] = a.y, x[2] = a.z, x[3] = a.w;
           x[4] = b.x, x[5] = b.y, x[6] = b.z, x[7] = b.w;
         };
-        float ctl[8], cml[8], qb[8];  // qb: r 2^(c_tau - c_{16q+8})
+        // qb: r 2^(c_tau - c_{16q+8}) (diagonal block); qs: r 2^(c_tau - c_{16q})
+        float ctl[8], cml[8], qst[8], qb[8], qs[8];
         ld8(&s.c[tau_l][i0], ctl);
         ld8(&s.tab.cmid[q][i0], cml);
+        ld8(&s.tab.q_start[q][i0], qst);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qb[e] = float(raw[e]) * exp2_fast(ctl[e] - cml[e]);
+        for (int e = 0; e < 8; ++e) {
+          qb[e] = float(raw[e]) * exp2_fast(ctl[e] - cml[e]);
+          qs[e] = qb[e] * qst[e];
+        }
 #pragma unroll
         for (int nb = 0; nb < 3; ++nb)
           if (nb < q) {
@@ -401,7 +415,7 @@ __global__ __launch_bounds__(256, 2) void wkv6_fwd_chunked(
             ld8(&s.tab.q_ref[q][nb][i0], qr);
             bf16x8 bq;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) bq[e] = to_bf16(qb[e] * qr[e]);
+            for (int e = 0; e < 8; ++e) bq[e] = to_bf16(qs[e] * qr[e]);
             const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.kb[16 * nb + row][i0]);
             acc[nb] = mfma(a, bq, acc[nb]);
           }
@@ -411,7 +425,7 @@ __global__ __launch_bounds__(256, 2) void wkv6_fwd_chunked(
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           bq[e] = to_bf16(qb[e]);
-          ainter[ks][e] = to_bf16(qb[e] * q0[e]);
+          ainter[ks][e] = to_bf16(qs[e] * q0[e]);
         }
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.kd[16 * q + row][i0]);
         dacc = mfma(a, bq, dacc);
@@ -613,19 +627,16 @@ __global__ __launch_bounds__(256) void wkv6_seg_state(int T, int H, int BH, int 
 }
 
 // Time segments per head (as for Eagle): about two workgroups per CU over the
-// launch, segments of at least four chunks; RWKV_WKV6_SEGS overrides.
+// launch, segments of at least four chunks; kTuneWkv6Segs overrides.
 constexpr int64_t kTargetWorkgroups = 512;
 
-int wkv6_dv() {
-  if (const char* env = getenv("RWKV_WKV6_DV")) return atoi(env) == 32 ? 32 : 64;
-  return 64;
-}
+int wkv6_dv() { return tuning(kTuneWkv6Dv) == 32 ? 32 : 64; }
 
 int wkv6_segments(int64_t BH, int64_t T, int ns) {
   const int64_t n_chunks = (T + kL - 1) / kL;
   const int64_t per_seg = (BH + 7) / 8 * 8 * ns;
   int64_t nseg = (kTargetWorkgroups + per_seg - 1) / per_seg;
-  if (const char* env = getenv("RWKV_WKV6_SEGS")) nseg = atoi(env);
+  if (const int o = tuning(kTuneWkv6Segs)) nseg = o;
   nseg = std::max<int64_t>(1, std::min<int64_t>(nseg, n_chunks / 4));
   const int64_t seg_chunks = (n_chunks + nseg - 1) / nseg;
   return int((n_chunks + seg_chunks - 1) / seg_chunks);

@@ -7,6 +7,32 @@
 
 namespace rwkv {
 
+// ----- Plan overrides (tests and sweeps) -----
+//
+// Each key holds 0 (the built-in plan) or an override; the values start from
+// the environment (RWKV_WKV4_TILE="cpl,L,NW", RWKV_WKV4_ORDER=claim,
+// RWKV_WKV5_DV, RWKV_WKV5_SEGS, RWKV_WKV6_DV, RWKV_WKV6_SEGS), read once, and
+// rwkv_set_tuning changes them.  They select other tile shapes, value slices
+// and time segments, and so change the workspace sizes.
+enum TuneKey : int {
+  kTuneWkv4Tile = 1,   // cpl * 10000 + L * 100 + NW of a compiled forward tile shape
+  kTuneWkv4Order = 2,  // 1: claimed tiles even where the grid is resident
+  kTuneWkv5Dv = 3,     // value columns per Eagle workgroup: 16, 32 or 64
+  kTuneWkv5Segs = 4,   // Eagle time segments (before the clamp to >= 4 chunks each)
+  kTuneWkv6Dv = 5,     // value columns per Finch workgroup: 32 or 64
+  kTuneWkv6Segs = 6,   // Finch time segments
+  kTuneKeys = 7
+};
+int tuning(int key);
+bool set_tuning(int key, int value);
+// Whether the forward has a compiled tile shape with this code (cpl*10000 + L*100 + NW).
+bool wkv4_variant_exists(int code);
+
+// Longest sequence of one RWKV-4 call: decay counts are held as floats,
+// exact for integers up to 2^24.  Longer sequences are cut and chained
+// through the state entry points.
+constexpr int64_t kWkv4MaxT = (int64_t(1) << 24) - 64;
+
 // ----- RWKV-4 forward: single-pass tiled scan with decoupled look-back -----
 //
 // A channel block is 64*CPL channels (CPL per lane); a tile is L tokens per
@@ -30,8 +56,9 @@ struct Wkv4Plan {
 constexpr size_t kWkv4HeaderBytes = 128;
 constexpr size_t kWkv4CounterStride = 128;  // one counter per 128-byte line
 
-// Plan for a shape; honours RWKV_WKV4_TILE="CPL,L,NW" for tests and sweeps.
-// Returns false if the shape cannot be planned (too large for 32-bit tickets).
+// Plan for a shape; honours the kTuneWkv4Tile override.  Returns false if
+// the shape cannot be planned (T > kWkv4MaxT, or too large for 32-bit
+// tickets and offsets).
 bool wkv4_plan(int64_t B, int64_t T, int64_t C, Wkv4Plan* plan);
 // The same for a given tile shape.
 bool wkv4_plan_fixed(int64_t B, int64_t T, int64_t C, int cpl, int L, int NW, Wkv4Plan* plan);

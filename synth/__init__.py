@@ -218,3 +218,132 @@ def wkv5_inputs_for(cfg: Wkv5Config) -> dict:
     return wkv5_inputs(cfg.B, cfg.T, cfg.H, cfg.D, cfg.seed,
                        omega_lo=cfg.omega_lo, omega_hi=cfg.omega_hi,
                        u_std=cfg.u_std)
+
+
+def dyadic_matrix_inputs(B: int, T: int, H: int, seed: int, *, per_token_decay=False,
+                         seams=(), slow_head=None) -> dict:
+    """Sparse one-hot inputs for bit-exact checks of the matrix-state paths.
+
+    Every nonzero r, k, v, u is +-1/2, +-1 or +-2 and every decay factor is 1,
+    1/2 or 1/4 (Eagle w [H, D]; with ``per_token_decay`` a Finch w_t
+    [B, T, H, D]), plus 1/16 on some key rows of ``slow_head`` (Eagle) or a
+    few factors 2^-16 (Finch).  Per (batch, head):
+
+    * each key row i is written by at most one token (k one-hot at i, v
+      one-hot at a column j), so every state entry is a single term;
+    * a token reads at most one row (r one-hot), so every output sum has at
+      most one nonzero term (the read row's entry, or the token's own bonus
+      when it reads the row it writes);
+    * a row that decays is read only a few decay steps after its write, and
+      a write that is still in the final state is either a few steps old or
+      old enough to have decayed below 2^-160.
+
+    Every exact result is then a power of two times +-1 inside the normal
+    float32 range, or zero: a correct kernel reproduces it bit for bit.
+    Writes and reads are placed at chunk edges (0, 31, 32, 63, 64, ...), at
+    the ``seams`` given (and one token to either side) and at random.
+
+    Returns the Eagle/Finch input dict (``w`` [H, D] or ``wt`` [B, T, H, D],
+    ``u``, and ``r/k/v`` with their ``_bits``).
+    """
+    D = 64
+    rng = rng_for(seed)
+    vals = np.array([0.5, 1.0, 2.0])
+
+    def pm(shape=None):
+        return rng.choice(vals, size=shape) * rng.choice([-1.0, 1.0], size=shape)
+
+    # Row kinds per (h, i).  reach: decay steps after a write within which it
+    # may be read; keep: a write still in the final state must be at most
+    # `reach` or at least `gone` steps old.
+    if per_token_decay:
+        # 0: no decay; 1: w_t in {1/4, 1/2}; 2: w_t in {1/4, 1/2, 1};
+        # 3: mostly 1/2 with some 2^-16
+        n_kinds = 4
+        reach = {0: 10 ** 9, 1: 30, 2: 30, 3: 6}
+        gone = {0: None, 1: 160, 2: None, 3: 160}
+    else:
+        # 0: w = 1; 1: w = 1/2; 2: w = 1/4; 3: w = 1/16 (slow_head only)
+        n_kinds = 3
+        reach = {0: 10 ** 9, 1: 60, 2: 30, 3: 7}
+        gone = {0: None, 1: 160, 2: 80, 3: 40}
+    kind = rng.integers(0, n_kinds, size=(H, D))
+    if slow_head is not None and not per_token_decay:
+        kind[slow_head, rng.permutation(D)[:8]] = 3
+    u = pm((H, D))
+    r = np.zeros((B, T, H, D))
+    k = np.zeros((B, T, H, D))
+    v = np.zeros((B, T, H, D))
+    if per_token_decay:
+        wt = np.ones((B, T, H, D))
+        for h in range(H):
+            for i in range(D):
+                kd = kind[h, i]
+                if kd == 1:
+                    wt[:, :, h, i] = rng.choice([0.25, 0.5], size=(B, T))
+                elif kd == 2:
+                    wt[:, :, h, i] = rng.choice([0.25, 0.5, 1.0], size=(B, T))
+                elif kd == 3:
+                    wt[:, :, h, i] = np.where(rng.random((B, T)) < 0.05, 2.0 ** -16, 0.5)
+    else:
+        w = np.choose(kind, [1.0, 0.5, 0.25, 0.0625])
+
+    special = set()
+    for e in (0, 31, 32, 63, 64, 95, 96, 127, 128, 191, 192, T - 2, T - 1):
+        special.add(e)
+    for s in seams:
+        special.update((s - 1, s, s + 1))
+    special = sorted(x for x in special if 0 <= x < T)
+
+    for b in range(B):
+        for h in range(H):
+            rows = rng.permutation(D)
+            n_w = min(D, max(1, T // 3))
+            times = list(special) + list(rng.permutation(T))
+            writer_t, used = {}, set()
+            for t in times:
+                if len(writer_t) >= n_w:
+                    break
+                if t in used:
+                    continue
+                i = int(rows[len(writer_t)])
+                age = T - 1 - t
+                kd = int(kind[h, i])
+                if age > reach[kd] and (gone[kd] is None or age < gone[kd]):
+                    continue  # would leave an unrepresentable entry in the final state
+                writer_t[i] = t
+                used.add(t)
+                k[b, t, h, i] = pm()
+                v[b, t, h, rng.integers(D)] = pm()
+            # readers: the writer itself (bonus), the next token, the edge of
+            # the reach, across the next chunk edge, and rows never written
+            reader = {}
+            for i, t0 in writer_t.items():
+                rc = reach[int(kind[h, i])]
+                nxt_edge = (t0 // 32 + 1) * 32
+                for t in (t0, t0 + 1, t0 + 1 + min(rc, 10 ** 6), nxt_edge, t0 + 1 + rc // 2):
+                    if t0 <= t < T and t - 1 - t0 <= rc and t not in reader:
+                        reader[t] = i
+                        break
+                for t in (t0 + 1, nxt_edge, nxt_edge + 1):
+                    if t0 < t < T and t - 1 - t0 <= rc and t not in reader:
+                        reader[t] = i
+                        break
+            unwritten = [i for i in range(D) if i not in writer_t]
+            for t in rng.permutation(T)[: max(1, T // 8)]:
+                if t not in reader and unwritten:
+                    reader[int(t)] = int(rng.choice(unwritten))
+            for t, i in reader.items():
+                r[b, t, h, i] = pm()
+
+    out = {"u": _f32(u)}
+    if per_token_decay:
+        out["wt"] = _f32(wt)
+        out["w"] = _f32(np.ones((H, D)))
+    else:
+        out["w"] = _f32(w)
+    for name, x in (("r", r), ("k", k), ("v", v)):
+        bits = bf16_bits_from_f32(_f32(x))
+        out[name + "_bits"] = bits
+        out[name] = f32_from_bf16_bits(bits)
+    return out

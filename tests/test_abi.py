@@ -42,6 +42,7 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     assert names == sorted([
         "rwkv_abi_version", "rwkv_status_str", "rwkv_last_hip_error",
+        "rwkv_set_tuning", "rwkv_get_tuning", "rwkv_wkv4_workspace_error",
         "rwkv_wkv4_forward_workspace", "rwkv_wkv4_forward", "rwkv_wkv4_forward_state",
         "rwkv_wkv4_backward_workspace", "rwkv_wkv4_backward",
         "rwkv_wkv4_forward_train", "rwkv_wkv4_backward_after_forward",
@@ -263,4 +264,64 @@ def test_wkv6_rejections(lib):
     for n in names:
         assert st(1, 2, 64, *ptrs(**{n: NULL}), NULL) == NULLPTR, n
         assert st(1, 2, 64, *ptrs(**{n: MISALIGNED}), NULL) == ALIGN, n
+    assert lib.rwkv_last_hip_error() == 0
+
+
+def test_tuning_overrides(lib):
+    """Plan overrides: unknown keys and values are rejected, accepted ones are
+    read back, and they change the plan (hence the workspace sizes)."""
+    keys = (1, 2, 3, 4, 5, 6)
+    old = {k: lib.rwkv_get_tuning(k) for k in keys}
+    try:
+        assert lib.rwkv_set_tuning(0, 1) == UNSUPPORTED
+        assert lib.rwkv_set_tuning(7, 1) == UNSUPPORTED
+        assert lib.rwkv_set_tuning(1, 13205) == UNSUPPORTED   # no such tile shape
+        assert lib.rwkv_set_tuning(1, 1) == UNSUPPORTED       # cpl 0: once a SIGFPE
+        assert lib.rwkv_set_tuning(2, 2) == UNSUPPORTED
+        assert lib.rwkv_set_tuning(3, 48) == UNSUPPORTED
+        assert lib.rwkv_set_tuning(5, 16) == UNSUPPORTED
+        assert lib.rwkv_set_tuning(4, -1) == UNSUPPORTED
+        for key, val in ((1, 40808), (2, 1), (3, 16), (4, 2), (5, 32), (6, 3)):
+            assert lib.rwkv_set_tuning(key, val) == OK
+            assert lib.rwkv_get_tuning(key) == val
+        # the Eagle workspace holds one state per head and earlier segment
+        assert lib.rwkv_set_tuning(4, 1) == OK
+        assert lib.rwkv_wkv5_forward_workspace(4, 4096, 32, 64) == 0
+        assert lib.rwkv_set_tuning(4, 4) == OK
+        assert lib.rwkv_wkv5_forward_workspace(4, 4096, 32, 64) == 4 * 32 * 3 * 64 * 64 * 4
+        # a 4-channel tile shape does not apply where 4 does not divide C
+        a = lib.rwkv_wkv4_forward_workspace(1, 1000, 66)
+        assert lib.rwkv_set_tuning(1, 0) == OK
+        assert lib.rwkv_wkv4_forward_workspace(1, 1000, 66) == a
+    finally:
+        for k, v in old.items():
+            assert lib.rwkv_set_tuning(k, v) == OK
+
+
+def test_wkv4_sequence_length_limit(lib):
+    """Decay counts are float32 integers: one call takes T <= 2^24 - 64."""
+    limit = (1 << 24) - 64
+    assert lib.rwkv_wkv4_forward_workspace(1, limit, 64) > 0
+    assert lib.rwkv_wkv4_forward_workspace(1, limit + 1, 64) == 0
+    assert lib.rwkv_wkv4_backward_workspace(1, limit, 64) > 0
+    assert lib.rwkv_wkv4_backward_workspace(1, limit + 1, 64) == 0
+    _skip_if_gpu()
+    args = [FAKE] * 5
+    assert lib.rwkv_wkv4_forward(1, limit + 1, 64, *args, FAKE, 1 << 62, NULL) == UNSUPPORTED
+    assert lib.rwkv_wkv4_forward_state(1, limit + 1, 64, *args, *[NULL] * 6, FAKE, 1 << 62,
+                                       NULL) == UNSUPPORTED
+    assert lib.rwkv_wkv4_backward(1, limit + 1, 64, *[FAKE] * 9, FAKE, 1 << 62,
+                                  NULL) == UNSUPPORTED
+    assert lib.rwkv_wkv4_forward_train(1, limit + 1, 64, *args, FAKE, 1 << 62,
+                                       NULL) == UNSUPPORTED
+    assert lib.rwkv_last_hip_error() == 0
+
+
+def test_workspace_error_query_rejections(lib):
+    _skip_if_gpu()
+    q = lib.rwkv_wkv4_workspace_error
+    assert q(NULL, 256, FAKE, NULL) == NULLPTR
+    assert q(FAKE, 256, NULL, NULL) == NULLPTR
+    assert q(FAKE, 3, FAKE, NULL) == WORKSPACE
+    assert q(MISALIGNED, 256, FAKE, NULL) == ALIGN
     assert lib.rwkv_last_hip_error() == 0

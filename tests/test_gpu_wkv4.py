@@ -5,7 +5,6 @@ the oracle's weighted mean of |v| with the same weights (S >= |y|): the
 condition scale of a convex combination.  Index-only properties (first
 token, identity map, shift map) are checked bit for bit.
 """
-import os
 
 import numpy as np
 import pytest
@@ -13,7 +12,7 @@ import pytest
 import linear_attention_sequence_rwkv_amd as rw
 import oracle.wkv_oracle as O
 import synth
-from wkv_testutil import WKV4_TOL, log, to_dev, torch_dev, wkv4_scaled_err
+from wkv_testutil import WKV4_TOL, log, to_dev, torch_dev, tuned, wkv4_scaled_err
 
 pytestmark = pytest.mark.gpu
 
@@ -23,19 +22,10 @@ TILE_VARIANTS = ["4,8,8", "4,16,4", "4,16,8", "2,16,8", "2,32,4", "2,16,4", "1,3
 
 def gpu_forward(inp, tile=None):
     torch, _ = torch_dev()
-    old = os.environ.get("RWKV_WKV4_TILE")
-    if tile is not None:
-        os.environ["RWKV_WKV4_TILE"] = tile
-    try:
+    with tuned(wkv4_tile=tile):
         y = rw.rwkv_wkv4_forward(to_dev(inp["w"]), to_dev(inp["u"]), to_dev(inp["k"]),
                                  to_dev(inp["v"]))
         torch.cuda.synchronize()
-    finally:
-        if tile is not None:
-            if old is None:
-                del os.environ["RWKV_WKV4_TILE"]
-            else:
-                os.environ["RWKV_WKV4_TILE"] = old
     return y.cpu().numpy()
 
 
@@ -189,7 +179,7 @@ def test_launch_order_and_claimed_tiles_give_the_same_bits(cfg_name):
     """Tiles taken in launch order (the whole grid resident) and claimed in
     arrival order fold the same histories in the same chain order: the
     outputs and the final state must agree bit for bit
-    (RWKV_WKV4_ORDER=claim forces claims)."""
+    (the RWKV_TUNE_WKV4_ORDER override forces claims)."""
     torch, dev = torch_dev()
     if cfg_name == "ragged":
         inp = synth.wkv4_inputs(3, 1100, 200, seed=77)
@@ -202,21 +192,14 @@ def test_launch_order_and_claimed_tiles_give_the_same_bits(cfg_name):
           for x in (g.random((B, C)), g.random((B, C)) + 0.5, g.normal(size=(B, C)))]
     t = {n: torch.from_numpy(inp[n]).to(dev) for n in ("w", "u", "k", "v")}
     outs = {}
-    old = os.environ.get("RWKV_WKV4_ORDER")
-    try:
-        for mode in ("", "claim"):
-            log(f"wkv4_forward {B}x{T}x{C}: prefix mode {mode or 'default'}, bitwise")
-            os.environ["RWKV_WKV4_ORDER"] = mode
+    for mode in ("", "claim"):
+        log(f"wkv4_forward {B}x{T}x{C}: prefix mode {mode or 'default'}, bitwise")
+        with tuned(wkv4_claim=mode == "claim"):
             y = rw.rwkv_wkv4_forward(t["w"], t["u"], t["k"], t["v"])
             y2, (a2, b2, p2) = rw.rwkv_wkv4_forward_state(t["w"], t["u"], t["k"], t["v"],
                                                          state_in=tuple(st), state_out=True)
             torch.cuda.synchronize()
-            outs[mode] = [x.cpu().numpy() for x in (y, y2, a2, b2, p2)]
-    finally:
-        if old is None:
-            del os.environ["RWKV_WKV4_ORDER"]
-        else:
-            os.environ["RWKV_WKV4_ORDER"] = old
+        outs[mode] = [x.cpu().numpy() for x in (y, y2, a2, b2, p2)]
     for x, z in zip(outs[""], outs["claim"]):
         assert np.array_equal(x, z)
 
@@ -382,17 +365,8 @@ def test_decode_workload_sampled_lanes():
 # ------------------------------------------------- forward with a state ---
 
 def _with_tile(tile, fn):
-    old = os.environ.get("RWKV_WKV4_TILE")
-    if tile is not None:
-        os.environ["RWKV_WKV4_TILE"] = tile
-    try:
+    with tuned(wkv4_tile=tile):
         return fn()
-    finally:
-        if tile is not None:
-            if old is None:
-                del os.environ["RWKV_WKV4_TILE"]
-            else:
-                os.environ["RWKV_WKV4_TILE"] = old
 
 
 @pytest.mark.parametrize("tile", [None, "4,8,8", "2,16,4", "1,64,1"])

@@ -11,7 +11,7 @@ import pytest
 import linear_attention_sequence_rwkv_amd as rw
 import oracle.wkv_oracle as O
 import synth
-from wkv_testutil import WKV4_TOL, log, to_dev, torch_dev, wkv4_scaled_err
+from wkv_testutil import WKV4_TOL, log, to_dev, torch_dev, tuned, wkv4_scaled_err
 
 pytestmark = pytest.mark.gpu
 
@@ -110,7 +110,6 @@ def test_launch_order_and_claimed_tiles_give_the_same_gradients(shape):
     claims); the folds run in the same chain order, so all four gradients
     must agree bit for bit, also when the two modes alternate on one
     workspace."""
-    import os
     torch, _ = torch_dev()
     B, T, C = shape
     inp = synth.wkv4_backward_inputs(B, T, C, seed=91)
@@ -118,24 +117,17 @@ def test_launch_order_and_claimed_tiles_give_the_same_gradients(shape):
     ws = torch.zeros(max(rw.rwkv_wkv4_backward_workspace(B, T, C), 256), dtype=torch.uint8,
                      device=args[0].device)
     outs = {}
-    old = os.environ.get("RWKV_WKV4_ORDER")
-    try:
-        for rnd in range(2):
-            for mode in ("", "claim"):
-                log(f"wkv4_backward {shape}: tile order {mode or 'default'} round {rnd}")
-                os.environ["RWKV_WKV4_ORDER"] = mode
+    for rnd in range(2):
+        for mode in ("", "claim"):
+            log(f"wkv4_backward {shape}: tile order {mode or 'default'} round {rnd}")
+            with tuned(wkv4_claim=mode == "claim"):
                 got = rw.rwkv_wkv4_backward(*args, ws=ws)
                 torch.cuda.synchronize()
-                got = [x.cpu() for x in got]
-                if mode in outs:
-                    for a, b in zip(outs[mode], got):
-                        assert torch.equal(a, b), (mode, rnd)
-                outs[mode] = got
-    finally:
-        if old is None:
-            del os.environ["RWKV_WKV4_ORDER"]
-        else:
-            os.environ["RWKV_WKV4_ORDER"] = old
+            got = [x.cpu() for x in got]
+            if mode in outs:
+                for a, b in zip(outs[mode], got):
+                    assert torch.equal(a, b), (mode, rnd)
+            outs[mode] = got
     for a, b in zip(outs[""], outs["claim"]):
         assert torch.equal(a, b)
 

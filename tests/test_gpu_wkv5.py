@@ -4,36 +4,25 @@ Tolerance: max |o_gpu - o_oracle| / o_abs <= 2e-2, where o_abs is the same
 recurrence over |r|, |k|, |v|, |u| (a bound on |o| that scales the rounding
 error of bf16 products with float32 accumulation).
 """
-import os
-
 import numpy as np
 import pytest
 
 import linear_attention_sequence_rwkv_amd as rw
 import oracle.wkv_oracle as O
 import synth
-from wkv_testutil import WKV5_TOL, log, to_dev, torch_dev, wkv5_scaled_err
+from wkv_testutil import WKV5_TOL, log, to_dev, torch_dev, tuned, wkv5_scaled_err
 
 pytestmark = pytest.mark.gpu
 
 
 def gpu_wkv5(inp, dv=None):
     torch, _ = torch_dev()
-    old = os.environ.get("RWKV_WKV5_DV")
-    if dv is not None:
-        os.environ["RWKV_WKV5_DV"] = str(dv)
-    try:
+    with tuned(wkv5_dv=dv):
         o = rw.rwkv_wkv5_forward(to_dev(inp["r_bits"], torch.bfloat16),
                                  to_dev(inp["k_bits"], torch.bfloat16),
                                  to_dev(inp["v_bits"], torch.bfloat16),
                                  to_dev(inp["w"]), to_dev(inp["u"]))
         torch.cuda.synchronize()
-    finally:
-        if dv is not None:
-            if old is None:
-                del os.environ["RWKV_WKV5_DV"]
-            else:
-                os.environ["RWKV_WKV5_DV"] = old
     return o.cpu().numpy()
 
 
@@ -100,15 +89,8 @@ def _magnitude(inp):
 
 
 def _with_dv(dv, fn):
-    old = os.environ.get("RWKV_WKV5_DV")
-    os.environ["RWKV_WKV5_DV"] = str(dv)
-    try:
+    with tuned(wkv5_dv=dv):
         return fn()
-    finally:
-        if old is None:
-            del os.environ["RWKV_WKV5_DV"]
-        else:
-            os.environ["RWKV_WKV5_DV"] = old
 
 
 @pytest.mark.parametrize("dv", [64, 32, 16])
@@ -245,18 +227,11 @@ def test_time_segments(shape, segs):
     log(f"wkv5_forward B={B} T={T} H={H} segments={segs}")
     inp = synth.wkv5_inputs(B, T, H, 64, seed=90 + T + segs)
     s0 = (np.random.default_rng(segs).standard_normal((B, H, 64, 64)) * 0.3).astype(np.float32)
-    old = os.environ.get("RWKV_WKV5_SEGS")
-    os.environ["RWKV_WKV5_SEGS"] = str(segs)
-    try:
+    with tuned(wkv5_segs=segs):
         o, s1 = rw.rwkv_wkv5_forward_state(_bits(inp, "r", np.s_[:]), _bits(inp, "k", np.s_[:]),
                                            _bits(inp, "v", np.s_[:]), to_dev(inp["w"]),
                                            to_dev(inp["u"]), s_in=to_dev(s0), s_out=True)
         torch.cuda.synchronize()
-    finally:
-        if old is None:
-            del os.environ["RWKV_WKV5_SEGS"]
-        else:
-            os.environ["RWKV_WKV5_SEGS"] = old
     o_ref, s_ref = O.wkv5_recurrent(inp["r"], inp["k"], inp["v"], inp["w"], inp["u"], S0=s0)
     o_abs, s_abs = O.wkv5_recurrent(np.abs(inp["r"]), np.abs(inp["k"]), np.abs(inp["v"]),
                                     inp["w"], np.abs(inp["u"]), S0=np.abs(s0))
@@ -274,14 +249,7 @@ def test_time_segments_with_exact_recurrence_heads():
     w = inp["w"].copy()
     w[1] = 0.05  # |log2 w| > 3.6: exact path for head 1
     case = dict(inp, w=w)
-    old = os.environ.get("RWKV_WKV5_SEGS")
-    os.environ["RWKV_WKV5_SEGS"] = "3"
-    try:
+    with tuned(wkv5_segs=3):
         o = gpu_wkv5(case)
-    finally:
-        if old is None:
-            del os.environ["RWKV_WKV5_SEGS"]
-        else:
-            os.environ["RWKV_WKV5_SEGS"] = old
     o_ref, o_abs = oracle_wkv5(case)
     assert wkv5_scaled_err(o, o_ref, o_abs) <= WKV5_TOL

@@ -11,7 +11,7 @@ import pytest
 import linear_attention_sequence_rwkv_amd as rw
 import oracle.wkv_oracle as O
 import synth
-from wkv_testutil import WKV5_TOL, log, to_dev, torch_dev, wkv5_scaled_err
+from wkv_testutil import WKV5_TOL, log, to_dev, torch_dev, tuned, wkv5_scaled_err
 
 pytestmark = pytest.mark.gpu
 
@@ -151,7 +151,6 @@ def test_time_segments_and_slices(segs, dv):
     """Split over time segments (local end states and summed log-decays folded
     into later segments) and over value slices, with a starting state and the
     handed-on state; one chunk of fast decays takes the exact diagonal path."""
-    import os
     torch, dev = torch_dev()
     e = synth.wkv6_inputs(2, 1000, 2, 64, seed=20 + segs, delta_std=1.0)
     wt = e["wt"].copy()
@@ -159,20 +158,43 @@ def test_time_segments_and_slices(segs, dv):
     e = dict(e, wt=wt)
     s0 = (np.random.default_rng(segs).standard_normal((2, 2, 64, 64)) * 0.3).astype(np.float32)
     log(f"wkv6_forward segments={segs} value columns={dv}")
-    old = {n: os.environ.get(n) for n in ("RWKV_WKV6_SEGS", "RWKV_WKV6_DV")}
-    os.environ["RWKV_WKV6_SEGS"] = str(segs)
-    os.environ["RWKV_WKV6_DV"] = dv
-    try:
+    with tuned(wkv6_segs=segs, wkv6_dv=dv):
         o, s1 = gpu_finch(e, s_in=to_dev(s0), s_out=True)
-    finally:
-        for n, val in old.items():
-            if val is None:
-                os.environ.pop(n, None)
-            else:
-                os.environ[n] = val
     o_ref, s_ref = O.wkv6_recurrent(e["r"], e["k"], e["v"], e["wt"], e["u"], S0=s0)
     o_abs, s_abs = O.wkv6_scale(e["r"], e["k"], e["v"], e["wt"], e["u"], S0=s0)
     err_o = wkv5_scaled_err(o, o_ref, o_abs)
     err_s = wkv5_scaled_err(s1, s_ref, s_abs)
     log(f"  err o={err_o:.3e} state={err_s:.3e}")
+    assert err_o <= WKV5_TOL and err_s <= WKV5_TOL
+
+
+def test_query_factor_across_a_deep_block_decay():
+    """A fast chunk whose second block starts with eight decays of 2^-14.9
+    after sixteen of 2^-0.5: the total decay to that block's middle
+    (2^-127.2) is below the float range, but the factor a query at the
+    block's first token applies to the carried state, 2^-8, is not.  The
+    factor must go through the block's first token (two ratios <= 1), not a
+    ratio to the block middle that flushes to zero; a large starting state
+    with small k, v makes the state term dominate the output."""
+    torch, _ = torch_dev()
+    B, T, H = 1, 64, 2
+    log("wkv6_forward: deep decay at a block start, large carried state")
+    e = synth.wkv6_inputs(B, T, H, 64, seed=77)
+    wt = np.full((B, T, H, 64), 2.0 ** -0.5, np.float32)
+    wt[:, 16:24] = np.float32(2.0 ** -14.9)
+    small = {}
+    for n in ("r", "k", "v"):
+        x = e[n] if n == "r" else e[n] * np.float32(0.01)
+        bits = synth.bf16_bits_from_f32(x)
+        small[n], small[n + "_bits"] = synth.f32_from_bf16_bits(bits), bits
+    e = dict(e, wt=wt, **small)
+    s0 = (np.random.default_rng(3).standard_normal((B, H, 64, 64)) * 100).astype(np.float32)
+    o, s1 = gpu_finch(e, s_in=to_dev(s0), s_out=True)
+    o_ref, s_ref = O.wkv6_recurrent(e["r"], e["k"], e["v"], e["wt"], e["u"], S0=s0)
+    o_abs, s_abs = O.wkv6_scale(e["r"], e["k"], e["v"], e["wt"], e["u"], S0=s0)
+    err_o = wkv5_scaled_err(o, o_ref, o_abs)
+    err_s = wkv5_scaled_err(s1, s_ref, s_abs)
+    # the tokens whose factor would have flushed
+    err_blk = wkv5_scaled_err(o[:, 16:24], o_ref[:, 16:24], o_abs[:, 16:24])
+    log(f"  err o={err_o:.3e} (tokens 16..23: {err_blk:.3e}) state={err_s:.3e}")
     assert err_o <= WKV5_TOL and err_s <= WKV5_TOL

@@ -1,4 +1,5 @@
 """Shared helpers for the GPU parity tests (not collected by pytest)."""
+import contextlib
 import sys
 
 import numpy as np
@@ -35,3 +36,31 @@ def wkv5_scaled_err(o, o_ref, o_abs):
 
 WKV4_TOL = 1e-4
 WKV5_TOL = 2e-2
+
+
+def tile_code(tile):
+    """RWKV_TUNE_WKV4_TILE value of a "cpl,L,NW" tile shape (None: default)."""
+    if tile is None:
+        return 0
+    c, l, nw = (int(x) for x in tile.split(","))
+    return c * 10000 + l * 100 + nw
+
+
+@contextlib.contextmanager
+def tuned(**settings):
+    """Plan overrides for a block: wkv4_tile="cpl,L,NW", wkv4_claim=True,
+    wkv5_dv=, wkv5_segs=, wkv6_dv=, wkv6_segs= (None leaves a key alone)."""
+    import linear_attention_sequence_rwkv_amd as rw
+    keys = {"wkv4_tile": (rw.RWKV_TUNE_WKV4_TILE, tile_code),
+            "wkv4_claim": (rw.RWKV_TUNE_WKV4_ORDER, lambda x: 1 if x else 0),
+            "wkv5_dv": (rw.RWKV_TUNE_WKV5_DV, int),
+            "wkv5_segs": (rw.RWKV_TUNE_WKV5_SEGS, int),
+            "wkv6_dv": (rw.RWKV_TUNE_WKV6_DV, int),
+            "wkv6_segs": (rw.RWKV_TUNE_WKV6_SEGS, int)}
+    with contextlib.ExitStack() as stack:
+        for name, val in settings.items():
+            if val is None:
+                continue
+            key, conv = keys[name]
+            stack.enter_context(rw.tuning(key, conv(val)))
+        yield
