@@ -3,18 +3,23 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-A "step" is one RWKV-4 WKV forward over the workload B=8 T=1024 C=768
-(float32 k, v, y; seeded synthetic inputs already resident in HBM).  Five
-copies of (k, v, y) rotate so that the 377 MB working set exceeds
-the 256 MB Infinity Cache and every step reads from HBM.
+A "step" is one RWKV-4 WKV forward over the long-sequence workload
+B=1 T=65536 C=5120 (the 14B-model width; float32 k, v, y; seeded synthetic
+inputs already resident in HBM).  Its 4.03 GB working set is far larger than
+the 256 MB Infinity Cache, so every step streams from HBM.  This is the
+largest single-GPU workload of the forward, the one the time-parallel scan
+exists for (few channels, a long sequence).
 
 Printed: ONE JSON line.  `value` is achieved algorithmic HBM bandwidth
-(12 bytes per element: read k, v; write y) over the timed steps.
+(12 bytes per element: read k, v; write y) over the K timed steps.
 `roofline` relates the forward kernel's algorithmic bytes per launch to its
-mean launch duration (HIP events around every launch, on the launch stream)
-and to the 8 TB/s HBM peak.  `cpu_baseline` is the fp64 NumPy oracle timed
-on this host on the same workload.  `secondary` holds the other entry points
-(long-sequence forward, the 4096-step decode loop, the Eagle forward).
+mean launch duration (two HIP events on the launch stream around K launches
+back to back, one kernel per launch) and to the 8 TB/s HBM peak; `traffic`
+is the HBM bytes per launch from the committed rocprofv3 counter summary
+when that summary was taken on the current kernel source.  `cpu_baseline` is
+the fp64 NumPy oracle on a channel sample of the same workload.  `secondary`
+holds the other workloads and entry points, each timed as the median of five
+repeats of at least 100 ms.
 """
 from __future__ import annotations
 
@@ -25,6 +30,7 @@ import json
 import os
 import platform
 import re
+import statistics
 import sys
 import time
 
@@ -37,13 +43,14 @@ HBM_PEAK_GBPS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "linear_attention_sequence_rwkv_amd", "csrc")
+WKV4_SOURCES = ("wkv4.hip", "wkv4_scan.h", "wkv_device.h")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash(files=("wkv4.hip", "wkv4_scan.h", "wkv_device.h")) -> str:
+def kernel_source_hash(files=WKV4_SOURCES) -> str:
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(CSRC, f), "rb") as fh:
@@ -72,19 +79,46 @@ def read_counter_summary(name: str, src_hash: str, key: str = "hbm_bytes_per_lau
         return None
 
 
-class Timer:
-    """A pair of HIP events bracketing the timed region on one stream."""
-
-    def __init__(self, torch):
-        E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-        self.start, self.end = E(), E()
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def bench_wkv4_forward(torch, rw, cfg, steps, warmup, rotate):
-    import synth
+def measure(torch, stream, launch, calls_hint=1, min_ms=100.0, repeats=5):
+    """Secondary-workload protocol: `launch(i)` enqueues call i on `stream`.
+    The number of calls per repeat is raised until a repeat takes at least
+    `min_ms`; returns (median ms per call, calls per repeat, all repeats)."""
+    n = max(1, calls_hint)
+    while True:
+        s, e = _events(torch)
+        s.record(stream)
+        for i in range(n):
+            launch(i)
+        e.record(stream)
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e)
+        if ms >= min_ms or n >= 1 << 20:
+            break
+        n = max(n + 1, int(n * min_ms / max(ms, 1e-3) * 1.1))
+    per = []
+    for _ in range(repeats):
+        s, e = _events(torch)
+        s.record(stream)
+        for i in range(n):
+            launch(i)
+        e.record(stream)
+        torch.cuda.synchronize()
+        per.append(s.elapsed_time(e) / n)
+    return statistics.median(per), n, per
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+# ------------------------------------------------------------ RWKV-4 forward
+
+def wkv4_device_copies(torch, inp, rotate):
     dev = torch.device("cuda:0")
-    inp = synth.wkv4_inputs_for(cfg)
-    B, T, C = cfg.B, cfg.T, cfg.C
     w = torch.from_numpy(inp["w"]).to(dev)
     u = torch.from_numpy(inp["u"]).to(dev)
     k0 = torch.from_numpy(inp["k"]).to(dev)
@@ -92,42 +126,95 @@ def bench_wkv4_forward(torch, rw, cfg, steps, warmup, rotate):
     ks = [k0] + [k0.clone() for _ in range(rotate - 1)]
     vs = [v0] + [v0.clone() for _ in range(rotate - 1)]
     ys = [torch.empty_like(k0) for _ in range(rotate)]
+    return w, u, ks, vs, ys
+
+
+def wkv4_forward_calls(torch, rw, cfg, dev_inputs):
+    """Pre-marshalled C-ABI argument tuples, one per rotated copy."""
+    w, u, ks, vs, ys = dev_inputs
+    B, T, C = cfg.B, cfg.T, cfg.C
     lib = rw.load_library()
     need = lib.rwkv_wkv4_forward_workspace(B, T, C)
-    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=ks[0].device)
+    stream = torch.cuda.current_stream(ks[0].device)
     sh = ctypes.c_void_p(stream.cuda_stream)
-    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    # Marshalled once; the timed loop is nothing but C-ABI calls.
-    calls = [(B, T, C, P(w), P(u), P(ks[i]), P(vs[i]), P(ys[i]), P(ws), need, sh)
-             for i in range(rotate)]
-    fn = lib.rwkv_wkv4_forward
+    calls = [(B, T, C, _ptr(w), _ptr(u), _ptr(ks[i]), _ptr(vs[i]), _ptr(ys[i]), _ptr(ws), need, sh)
+             for i in range(len(ks))]
+    return lib.rwkv_wkv4_forward, calls, stream, ws
+
+
+def bench_wkv4_headline(torch, rw, cfg, dev_inputs, steps, warmup):
+    """The driver's protocol: W untimed steps, then exactly K steps between
+    two events (after a synchronisation on both sides)."""
+    fn, calls, stream, ws = wkv4_forward_calls(torch, rw, cfg, dev_inputs)
+    rot = len(calls)
     for i in range(warmup):
-        assert fn(*calls[i % rotate]) == 0
+        assert fn(*calls[i % rot]) == 0
     torch.cuda.synchronize()
-    # Timed region: K launches back to back, bracketed by two events.
-    tm = Timer(torch)
-    tm.start.record(stream)
+    s, e = _events(torch)
+    s.record(stream)
     for i in range(steps):
-        st = fn(*calls[i % rotate])
+        st = fn(*calls[i % rot])
         if st != 0:
             raise RuntimeError(f"rwkv_wkv4_forward status {st}")
-    tm.end.record(stream)
+    e.record(stream)
     torch.cuda.synchronize()
-    total_ms = tm.start.elapsed_time(tm.end)
-    # One kernel per call, launched back to back on this stream: its average
-    # duration is the timed region over K.  (An event pair around each launch
-    # would add the event packets' own dispatch gaps to every launch.)
-    kern_ms = total_ms / steps
-    # sanity: the output of the last launch is finite and the first token is v
-    y_last = ys[(steps - 1) % rotate]
-    assert torch.isfinite(y_last).all().item()
-    assert torch.equal(y_last[:, 0], vs[(steps - 1) % rotate][:, 0])
-    return {"ms_per_step": total_ms / steps, "kernel_ms": kern_ms,
-            "elems": B * T * C, "bytes": 12 * B * T * C}
+    total_ms = s.elapsed_time(e)
+    _check_wkv4_output(torch, rw, dev_inputs, (steps - 1) % rot, ws)
+    return total_ms / steps
 
 
-def bench_wkv4_backward(torch, rw, cfg, steps, warmup):
+def bench_wkv4_secondary(torch, rw, cfg, dev_inputs):
+    fn, calls, stream, ws = wkv4_forward_calls(torch, rw, cfg, dev_inputs)
+    rot = len(calls)
+    for i in range(3):
+        assert fn(*calls[i % rot]) == 0
+    ms, n, per = measure(torch, stream, lambda i: fn(*calls[i % rot]), calls_hint=8)
+    _check_wkv4_output(torch, rw, dev_inputs, (n - 1) % rot, ws)
+    return ms, n, per
+
+
+def _check_wkv4_output(torch, rw, dev_inputs, last, ws):
+    """Sanity of the last launch: finite output, the first token is v, and
+    the workspace's error word is clear."""
+    _, _, ks, vs, ys = dev_inputs
+    assert torch.isfinite(ys[last]).all().item()
+    assert torch.equal(ys[last][:, 0], vs[last][:, 0])
+    assert rw.rwkv_wkv4_workspace_error(ws) == 0
+
+
+def wkv4_roofline(cfg, kern_ms, profile):
+    nbytes = 12 * cfg.B * cfg.T * cfg.C
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    src = kernel_source_hash()
+    return {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": read_counter_summary(profile, src),
+            "kernel": "wkv4_fwd_tiled", "kernel_us": round(kern_ms * 1e3, 3),
+            "algorithmic_bytes_per_launch": nbytes, "kernel_source": src}
+
+
+def cpu_baseline_wkv4(cfg, inp, channels):
+    """The fp64 oracle recurrence on the first `channels` channels of the
+    same inputs over the full sequence (one host core: NumPy elementwise)."""
+    import oracle.wkv_oracle as O
+    sl = slice(0, channels)
+    k, v = inp["k"][..., sl], inp["v"][..., sl]
+    t0 = time.perf_counter()
+    O.wkv4_recurrent(inp["w"][sl], inp["u"][sl], k, v)
+    el = time.perf_counter() - t0
+    elems = cfg.B * cfg.T * channels
+    return {"value": round(12 * elems / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": (f"fp64 NumPy recurrence on channels 0..{channels - 1} of the "
+                       f"{cfg.name} inputs, full T={cfg.T}: {el:.1f} s on one core of "
+                       f"{_cpu_name()} ({len(os.sched_getaffinity(0))} cores visible)"),
+            "gelem_per_s": round(elems / el / 1e9, 6)}
+
+
+# ------------------------------------------------------------------ others
+
+def bench_wkv4_backward(torch, rw, cfg):
     """One backward call (prefix pass, reverse scan, reduction) per step."""
     import synth
     dev = torch.device("cuda:0")
@@ -136,31 +223,25 @@ def bench_wkv4_backward(torch, rw, cfg, steps, warmup):
                                      v_std=cfg.v_std)
     B, T, C = cfg.B, cfg.T, cfg.C
     w, u, k, v, gy = (torch.from_numpy(inp[n]).to(dev) for n in ("w", "u", "k", "v", "gy"))
+    del inp
     gw, gu = torch.empty_like(w), torch.empty_like(u)
     gk, gv = torch.empty_like(k), torch.empty_like(k)
     lib = rw.load_library()
     need = lib.rwkv_wkv4_backward_workspace(B, T, C)
     ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    args = (B, T, C, P(w), P(u), P(k), P(v), P(gy), P(gw), P(gu), P(gk), P(gv), P(ws), need,
-            ctypes.c_void_p(stream.cuda_stream))
+    args = (B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(gy), _ptr(gw), _ptr(gu), _ptr(gk),
+            _ptr(gv), _ptr(ws), need, ctypes.c_void_p(stream.cuda_stream))
     fn = lib.rwkv_wkv4_backward
-    for _ in range(warmup):
+    for _ in range(2):
         assert fn(*args) == 0
-    torch.cuda.synchronize()
-    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    st.record(stream)
-    for _ in range(steps):
-        assert fn(*args) == 0
-    en.record(stream)
-    torch.cuda.synchronize()
+    ms, n, _ = measure(torch, stream, lambda i: fn(*args))
     assert torch.isfinite(gk).all().item() and torch.isfinite(gw).all().item()
-    ms = st.elapsed_time(en) / steps
-    return {"ms": ms, "elems": B * T * C, "bytes": 20 * B * T * C}
+    assert rw.rwkv_wkv4_workspace_error(ws) == 0
+    return {"ms": ms, "elems": B * T * C, "bytes": 20 * B * T * C, "calls_per_repeat": n}
 
 
-def bench_wkv4_train(torch, rw, cfg, steps, warmup):
+def bench_wkv4_train(torch, rw, cfg):
     """A training step's WKV: forward then backward on the same inputs, timed
     as rwkv_wkv4_forward_train + rwkv_wkv4_backward_after_forward (one
     workspace, the backward reuses the forward's tile histories) and as
@@ -182,30 +263,163 @@ def bench_wkv4_train(torch, rw, cfg, steps, warmup):
     ws_f = torch.zeros(max(need_f, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sh = ctypes.c_void_p(stream.cuda_stream)
-    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    io = (P(w), P(u), P(k), P(v))
-    grads = (P(gy), P(gw), P(gu), P(gk), P(gv))
-    pair = ((lib.rwkv_wkv4_forward_train, (B, T, C, *io, P(y), P(ws_b), need_b, sh)),
-            (lib.rwkv_wkv4_backward_after_forward, (B, T, C, *io, *grads, P(ws_b), need_b, sh)))
-    separate = ((lib.rwkv_wkv4_forward, (B, T, C, *io, P(y), P(ws_f), need_f, sh)),
-                (lib.rwkv_wkv4_backward, (B, T, C, *io, *grads, P(ws_b), need_b, sh)))
+    io = (_ptr(w), _ptr(u), _ptr(k), _ptr(v))
+    grads = (_ptr(gy), _ptr(gw), _ptr(gu), _ptr(gk), _ptr(gv))
+    pair = ((lib.rwkv_wkv4_forward_train, (B, T, C, *io, _ptr(y), _ptr(ws_b), need_b, sh)),
+            (lib.rwkv_wkv4_backward_after_forward,
+             (B, T, C, *io, *grads, _ptr(ws_b), need_b, sh)))
+    separate = ((lib.rwkv_wkv4_forward, (B, T, C, *io, _ptr(y), _ptr(ws_f), need_f, sh)),
+                (lib.rwkv_wkv4_backward, (B, T, C, *io, *grads, _ptr(ws_b), need_b, sh)))
     out = {}
     for key, calls in (("pair", pair), ("separate", separate)):
-        for _ in range(warmup):
+        def launch(i, calls=calls):
             for fn, a in calls:
                 assert fn(*a) == 0
-        torch.cuda.synchronize()
-        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        st.record(stream)
-        for _ in range(steps):
-            for fn, a in calls:
-                assert fn(*a) == 0
-        en.record(stream)
-        torch.cuda.synchronize()
+        for i in range(2):
+            launch(i)
+        out[key], _, _ = measure(torch, stream, launch)
         assert torch.isfinite(gk).all().item() and torch.isfinite(y).all().item()
-        out[key] = st.elapsed_time(en) / steps
     return {"ms": out["pair"], "ms_separate": out["separate"], "elems": B * T * C,
             "bytes": 32 * B * T * C}
+
+
+def bench_decode(torch, rw, cfg, graph=True):
+    """The 4096-step decode loop, eager and replayed from a HIP graph; one
+    call of `launch` is one whole loop."""
+    import synth
+    dev = torch.device("cuda:0")
+    inp = synth.wkv4_step_inputs(cfg.B, cfg.C, cfg.pool, cfg.seed)
+    w = torch.from_numpy(inp["w"]).to(dev)
+    u = torch.from_numpy(inp["u"]).to(dev)
+    k_all = torch.from_numpy(inp["k"]).to(dev)
+    v_all = torch.from_numpy(inp["v"]).to(dev)
+    a, b, p = rw.rwkv_wkv4_state_init(cfg.B, cfg.C, device=dev)
+    y = torch.empty((cfg.B, cfg.C), dtype=torch.float32, device=dev)
+    lib = rw.load_library()
+
+    def run(stream):
+        sh = ctypes.c_void_p(stream.cuda_stream)
+        for t in range(cfg.steps):
+            i = t % cfg.pool
+            st = lib.rwkv_wkv4_step(cfg.B, cfg.C, _ptr(a), _ptr(b), _ptr(p), _ptr(w), _ptr(u),
+                                    _ptr(k_all[i]), _ptr(v_all[i]), _ptr(y), sh)
+            if st != 0:
+                raise RuntimeError(f"rwkv_wkv4_step status {st}")
+
+    stream = torch.cuda.current_stream(dev)
+    run(stream)  # warm-up
+    torch.cuda.synchronize()
+    eager_ms, _, _ = measure(torch, stream, lambda i: run(stream))
+    elems = cfg.B * cfg.C * cfg.steps
+    res = {"eager_ms": eager_ms, "graph_ms": None, "elems": elems, "bytes": 36 * elems}
+    if graph:
+        # The same 4096 launches captured once in a HIP graph and replayed.
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream(dev)
+        cap.wait_stream(stream)
+        with torch.cuda.graph(g, stream=cap):
+            run(torch.cuda.current_stream(dev))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        res["graph_ms"], _, _ = measure(torch, stream, lambda i: g.replay())
+    assert torch.isfinite(y).all().item()
+    return res
+
+
+def bench_matrix_forward(torch, rw, cfg, finch, rotate=2):
+    """Eagle (finch=False) or Finch forward; `rotate` copies of the inputs and
+    output alternate so that consecutive calls do not find them in cache."""
+    import synth
+    dev = torch.device("cuda:0")
+    e = (synth.wkv6_inputs(cfg.B, cfg.T, cfg.H, cfg.D, cfg.seed) if finch
+         else synth.wkv5_inputs_for(cfg))
+    to = lambda x: torch.from_numpy(x).to(dev)  # noqa: E731
+    copies = []
+    for _ in range(rotate):
+        r, k, v = (to(e[n + "_bits"]).view(torch.bfloat16) for n in ("r", "k", "v"))
+        wt = to(e["wt"]) if finch else None
+        o = torch.empty((cfg.B, cfg.T, cfg.H, cfg.D), dtype=torch.float32, device=dev)
+        copies.append((r, k, v, wt, o))
+    w, u = to(e["w"]), to(e["u"])
+    del e
+    lib = rw.load_library()
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    query = lib.rwkv_wkv6_forward_workspace if finch else lib.rwkv_wkv5_forward_workspace
+    need = query(cfg.B, cfg.T, cfg.H, cfg.D)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+    shape = (cfg.B, cfg.T, cfg.H, cfg.D)
+    if finch:
+        calls = [(lib.rwkv_wkv6_forward, (*shape, _ptr(r), _ptr(k), _ptr(v), _ptr(wt), _ptr(u),
+                                          _ptr(o), None, None, _ptr(ws), need, sh))
+                 for r, k, v, wt, o in copies]
+    else:
+        calls = [(lib.rwkv_wkv5_forward, (*shape, _ptr(r), _ptr(k), _ptr(v), _ptr(w), _ptr(u),
+                                          _ptr(o), _ptr(ws), need, sh))
+                 for r, k, v, _, o in copies]
+
+    def launch(i):
+        fn, a = calls[i % rotate]
+        assert fn(*a) == 0
+
+    for i in range(2):
+        launch(i)
+    ms, n, _ = measure(torch, stream, launch, calls_hint=8)
+    for c in copies:
+        assert torch.isfinite(c[4]).all().item()
+    elems = cfg.B * cfg.T * cfg.H * cfg.D
+    return {"ms": ms, "elems": elems, "bytes": (14 if finch else 10) * elems,
+            "flops": 4 * cfg.D * elems, "rotated_copies": rotate}
+
+
+def wkv5_step_bytes(B, H, D):
+    """Algorithmic bytes of one Eagle step: the fp32 state read and written,
+    r, k, v in bf16, o in fp32."""
+    return B * H * (2 * D * D * 4 + 3 * D * 2 + D * 4)
+
+
+def bench_wkv5_decode(torch, rw, cfg):
+    import synth
+    dev = torch.device("cuda:0")
+    inp = synth.wkv5_step_inputs(cfg)
+    to = lambda x: torch.from_numpy(x).to(dev)  # noqa: E731
+    # [B, pool, H, D] -> [pool, B, H, D]: one contiguous token per step
+    r, k, v = (to(inp[n + "_bits"]).view(torch.bfloat16).transpose(0, 1).contiguous()
+               for n in ("r", "k", "v"))
+    w, u = to(inp["w"]), to(inp["u"])
+    s = torch.zeros((cfg.B, cfg.H, cfg.D, cfg.D), dtype=torch.float32, device=dev)
+    o = torch.empty((cfg.B, cfg.H, cfg.D), dtype=torch.float32, device=dev)
+    lib = rw.load_library()
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    calls = [(cfg.B, cfg.H, cfg.D, _ptr(s), _ptr(r[i]), _ptr(k[i]), _ptr(v[i]), _ptr(w), _ptr(u),
+              _ptr(o), sh) for i in range(cfg.pool)]
+    fn = lib.rwkv_wkv5_step
+
+    def loop(_):
+        for t in range(cfg.steps):
+            assert fn(*calls[t % cfg.pool]) == 0
+
+    loop(0)
+    torch.cuda.synchronize()
+    ms, _, _ = measure(torch, stream, loop)
+    assert torch.isfinite(s).all().item()
+    return {"ms": ms, "bytes": cfg.steps * wkv5_step_bytes(cfg.B, cfg.H, cfg.D)}
+
+
+# ----------------------------------------------------- oracle samples (CPU)
+
+def _cpu_name():
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return cpu
 
 
 def cpu_sample_backward():
@@ -221,220 +435,6 @@ def cpu_sample_backward():
     elems = cfg.B * cfg.T * 32
     return {"value": round(20 * elems / el / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"B={cfg.B} T={cfg.T} x 32 channels, {el:.2f} s"}
-
-
-def bench_copy_peak(torch, nbytes=1 << 30, reps=20):
-    dev = torch.device("cuda:0")
-    a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
-    b = torch.empty_like(a)
-    for _ in range(3):
-        b.copy_(a)
-    torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(reps):
-        b.copy_(a)
-    e.record()
-    torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / reps
-    return 2 * nbytes / (ms * 1e-3) / 1e9
-
-
-def bench_decode(torch, rw, cfg, reps, graph=True):
-    import synth
-    dev = torch.device("cuda:0")
-    inp = synth.wkv4_step_inputs(cfg.B, cfg.C, cfg.pool, cfg.seed)
-    w = torch.from_numpy(inp["w"]).to(dev)
-    u = torch.from_numpy(inp["u"]).to(dev)
-    k_all = torch.from_numpy(inp["k"]).to(dev)
-    v_all = torch.from_numpy(inp["v"]).to(dev)
-    a, b, p = rw.rwkv_wkv4_state_init(cfg.B, cfg.C, device=dev)
-    y = torch.empty((cfg.B, cfg.C), dtype=torch.float32, device=dev)
-    lib = rw.load_library()
-    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-
-    def run(stream):
-        sh = ctypes.c_void_p(stream.cuda_stream)
-        for t in range(cfg.steps):
-            i = t % cfg.pool
-            st = lib.rwkv_wkv4_step(cfg.B, cfg.C, P(a), P(b), P(p), P(w), P(u), P(k_all[i]),
-                                    P(v_all[i]), P(y), sh)
-            if st != 0:
-                raise RuntimeError(f"rwkv_wkv4_step status {st}")
-
-    stream = torch.cuda.current_stream(dev)
-    run(stream)  # warm-up
-    torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record(stream)
-    for _ in range(reps):
-        run(stream)
-    e.record(stream)
-    torch.cuda.synchronize()
-    eager_ms = s.elapsed_time(e) / reps
-    elems = cfg.B * cfg.C * cfg.steps
-    if not graph:
-        assert torch.isfinite(y).all().item()
-        return {"eager_ms": eager_ms, "graph_ms": None, "elems": elems, "bytes": 36 * elems}
-    # The same 4096 launches captured once in a HIP graph and replayed.
-    g = torch.cuda.CUDAGraph()
-    cap = torch.cuda.Stream(dev)
-    cap.wait_stream(stream)
-    with torch.cuda.graph(g, stream=cap):
-        run(torch.cuda.current_stream(dev))
-    torch.cuda.synchronize()
-    g.replay()
-    torch.cuda.synchronize()
-    s.record(stream)
-    for _ in range(reps):
-        g.replay()
-    e.record(stream)
-    torch.cuda.synchronize()
-    graph_ms = s.elapsed_time(e) / reps
-    assert torch.isfinite(y).all().item()
-    return {"eager_ms": eager_ms, "graph_ms": graph_ms, "elems": elems, "bytes": 36 * elems}
-
-
-def bench_wkv5(torch, rw, cfg, reps):
-    import synth
-    dev = torch.device("cuda:0")
-    inp = synth.wkv5_inputs_for(cfg)
-    to = lambda x: torch.from_numpy(x).to(dev)  # noqa: E731
-    r, k, v = (to(inp[n + "_bits"]).view(torch.bfloat16) for n in ("r", "k", "v"))
-    w, u = to(inp["w"]), to(inp["u"])
-    o = torch.empty((cfg.B, cfg.T, cfg.H, cfg.D), dtype=torch.float32, device=dev)
-    lib = rw.load_library()
-    need = lib.rwkv_wkv5_forward_workspace(cfg.B, cfg.T, cfg.H, cfg.D)
-    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    args = (cfg.B, cfg.T, cfg.H, cfg.D, P(r), P(k), P(v), P(w), P(u), P(o), P(ws), need,
-            ctypes.c_void_p(stream.cuda_stream))
-    assert lib.rwkv_wkv5_forward(*args) == 0
-    torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record(stream)
-    for _ in range(reps):
-        assert lib.rwkv_wkv5_forward(*args) == 0
-    e.record(stream)
-    torch.cuda.synchronize()
-    assert torch.isfinite(o).all().item()
-    ms = s.elapsed_time(e) / reps
-    elems = cfg.B * cfg.T * cfg.H * cfg.D
-    return {"ms": ms, "elems": elems, "bytes": 10 * elems, "flops": 4 * cfg.D * elems}
-
-
-def bench_wkv6(torch, rw, cfg, reps):
-    import synth
-    dev = torch.device("cuda:0")
-    e = synth.wkv6_inputs(cfg.B, cfg.T, cfg.H, cfg.D, cfg.seed)
-    to = lambda x: torch.from_numpy(x).to(dev)  # noqa: E731
-    r, k, v = (to(e[n + "_bits"]).view(torch.bfloat16) for n in ("r", "k", "v"))
-    wt, u = to(e["wt"]), to(e["u"])
-    o = torch.empty((cfg.B, cfg.T, cfg.H, cfg.D), dtype=torch.float32, device=dev)
-    lib = rw.load_library()
-    stream = torch.cuda.current_stream(dev)
-    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    need = lib.rwkv_wkv6_forward_workspace(cfg.B, cfg.T, cfg.H, cfg.D)
-    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
-    args = (cfg.B, cfg.T, cfg.H, cfg.D, P(r), P(k), P(v), P(wt), P(u), P(o), None, None, P(ws),
-            need, ctypes.c_void_p(stream.cuda_stream))
-    assert lib.rwkv_wkv6_forward(*args) == 0
-    torch.cuda.synchronize()
-    s, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record(stream)
-    for _ in range(reps):
-        assert lib.rwkv_wkv6_forward(*args) == 0
-    en.record(stream)
-    torch.cuda.synchronize()
-    assert torch.isfinite(o).all().item()
-    ms = s.elapsed_time(en) / reps
-    elems = cfg.B * cfg.T * cfg.H * cfg.D
-    return {"ms": ms, "elems": elems, "bytes": 14 * elems, "flops": 4 * cfg.D * elems}
-
-
-def cpu_sample_finch():
-    """Oracle recurrence for 2 (batch, head) pairs over the full T."""
-    import oracle.wkv_oracle as O
-    import synth
-    cfg = synth.CFG_WKV6_FINCH
-    e = synth.wkv6_inputs(1, cfg.T, 2, cfg.D, cfg.seed)
-    t0 = time.perf_counter()
-    O.wkv6_recurrent(e["r"], e["k"], e["v"], e["wt"], e["u"])
-    el = time.perf_counter() - t0
-    elems = cfg.T * 2 * cfg.D
-    return {"value": round(14 * elems / el / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"2 heads x T={cfg.T} x D={cfg.D}, {el:.1f} s"}
-
-
-def wkv5_step_bytes(B, H, D):
-    """Algorithmic bytes of one Eagle step: the fp32 state read and written,
-    r, k, v in bf16, o in fp32."""
-    return B * H * (2 * D * D * 4 + 3 * D * 2 + D * 4)
-
-
-def bench_wkv5_decode(torch, rw, cfg, reps):
-    import synth
-    dev = torch.device("cuda:0")
-    inp = synth.wkv5_step_inputs(cfg)
-    to = lambda x: torch.from_numpy(x).to(dev)  # noqa: E731
-    # [B, pool, H, D] -> [pool, B, H, D]: one contiguous token per step
-    r, k, v = (to(inp[n + "_bits"]).view(torch.bfloat16).transpose(0, 1).contiguous()
-               for n in ("r", "k", "v"))
-    w, u = to(inp["w"]), to(inp["u"])
-    s = torch.zeros((cfg.B, cfg.H, cfg.D, cfg.D), dtype=torch.float32, device=dev)
-    o = torch.empty((cfg.B, cfg.H, cfg.D), dtype=torch.float32, device=dev)
-    lib = rw.load_library()
-    stream = torch.cuda.current_stream(dev)
-    sh = ctypes.c_void_p(stream.cuda_stream)
-    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    calls = [(cfg.B, cfg.H, cfg.D, P(s), P(r[i]), P(k[i]), P(v[i]), P(w), P(u), P(o), sh)
-             for i in range(cfg.pool)]
-    fn = lib.rwkv_wkv5_step
-    for i in range(8):
-        assert fn(*calls[i % cfg.pool]) == 0
-    torch.cuda.synchronize()
-    best = None
-    for _ in range(reps):
-        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        st.record(stream)
-        for t in range(cfg.steps):
-            assert fn(*calls[t % cfg.pool]) == 0
-        en.record(stream)
-        torch.cuda.synchronize()
-        ms = st.elapsed_time(en)
-        best = ms if best is None else min(best, ms)
-    assert torch.isfinite(s).all().item()
-    return {"ms": best, "bytes": cfg.steps * wkv5_step_bytes(cfg.B, cfg.H, cfg.D)}
-
-
-def _cpu_name():
-    cpu = platform.processor() or platform.machine()
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
-    except OSError:
-        pass
-    return cpu
-
-
-def cpu_sample_long(budget_s=4.0):
-    """Oracle on channels of the long-sequence workload, over the full T."""
-    import numpy as np
-    import oracle.wkv_oracle as O
-    import synth
-    cfg = synth.CFG_WKV4_LONG
-    inp = synth.wkv4_inputs(1, cfg.T, 64, cfg.seed, omega_lo=cfg.omega_lo, omega_hi=cfg.omega_hi,
-                            u_std=cfg.u_std, k_std=cfg.k_std)
-    t0 = time.perf_counter()
-    O.wkv4_recurrent(inp["w"], inp["u"], inp["k"], inp["v"])
-    el = time.perf_counter() - t0
-    elems = cfg.T * 64
-    del np
-    return {"value": round(12 * elems / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"64 channels x T={cfg.T} of the same distributions, {el:.1f} s"}
 
 
 def cpu_sample_decode():
@@ -457,17 +457,24 @@ def cpu_sample_decode():
             "sample": f"{L} lanes x {N} steps, {el:.1f} s"}
 
 
-def cpu_sample_eagle():
+def cpu_sample_matrix(finch):
     """Oracle recurrence for 2 (batch, head) pairs over the full T."""
     import oracle.wkv_oracle as O
     import synth
-    cfg = synth.CFG_WKV5_EAGLE
-    inp = synth.wkv5_inputs(1, cfg.T, 2, cfg.D, cfg.seed)
+    cfg = synth.CFG_WKV6_FINCH if finch else synth.CFG_WKV5_EAGLE
     t0 = time.perf_counter()
-    O.wkv5_recurrent(inp["r"], inp["k"], inp["v"], inp["w"], inp["u"])
+    if finch:
+        e = synth.wkv6_inputs(1, cfg.T, 2, cfg.D, cfg.seed)
+        t0 = time.perf_counter()
+        O.wkv6_recurrent(e["r"], e["k"], e["v"], e["wt"], e["u"])
+    else:
+        e = synth.wkv5_inputs(1, cfg.T, 2, cfg.D, cfg.seed)
+        t0 = time.perf_counter()
+        O.wkv5_recurrent(e["r"], e["k"], e["v"], e["w"], e["u"])
     el = time.perf_counter() - t0
     elems = cfg.T * 2 * cfg.D
-    return {"value": round(10 * elems / el / 1e9, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": round((14 if finch else 10) * elems / el / 1e9, 5), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
             "sample": f"2 heads x T={cfg.T} x D={cfg.D}, {el:.1f} s"}
 
 
@@ -489,47 +496,37 @@ def cpu_sample_eagle_decode():
             "sample": f"4 (stream, head) pairs x {cfg.steps} steps, {el:.2f} s"}
 
 
-def cpu_baseline(cfg, budget_s):
-    """The fp64 oracle's recurrence on the full workload, repeated for about
-    `budget_s` seconds of host time."""
-    import numpy as np
+def cpu_sample_169m():
+    """The fp64 oracle recurrence over the full 8x1024x768 workload, once."""
     import oracle.wkv_oracle as O
     import synth
+    cfg = synth.CFG_WKV4_169M
     inp = synth.wkv4_inputs_for(cfg)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        O.wkv4_recurrent(inp["w"], inp["u"], inp["k"], inp["v"])
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    elems = cfg.B * cfg.T * cfg.C * reps
-    cpu = _cpu_name()
-    del np
+    t0 = time.perf_counter()
+    O.wkv4_recurrent(inp["w"], inp["u"], inp["k"], inp["v"])
+    el = time.perf_counter() - t0
+    elems = cfg.B * cfg.T * cfg.C
     return {"value": round(12 * elems / el / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": (f"fp64 NumPy recurrence over the full B={cfg.B} T={cfg.T} C={cfg.C} "
-                       f"workload, {reps} run(s) in {el:.1f} s on one core of {cpu} "
-                       f"({len(os.sched_getaffinity(0))} cores visible)"),
-            "gelem_per_s": round(elems / el / 1e9, 6)}
+            "kind": "oracle", "sample": f"the full workload, {el:.1f} s"}
 
+
+# --------------------------------------------------------------------- main
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--rotate", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=10.0)
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="accepted for older command lines; the 1 GiB copy always runs")
+    ap.add_argument("--cpu-channels", type=int, default=2560,
+                    help="channels of the headline workload the oracle sample covers")
     ap.add_argument("--secondary",
-                    default="hot,long,decode,decode-graph,eagle,eagle-decode,finch,backward,"
-                            "backward-long,train",
-                    help="comma list of secondary workloads: hot, long, decode, decode-graph, "
-                         "eagle, eagle-decode, finch, backward, backward-long, train")
+                    default="169m,169m-hot,decode,decode-graph,eagle,eagle-decode,finch,"
+                            "backward,backward-long,train",
+                    help="comma list of secondary workloads: 169m, 169m-hot, decode, "
+                         "decode-graph, eagle, eagle-decode, finch, backward, backward-long, "
+                         "train")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -546,14 +543,15 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
 
-    cfg = synth.CFG_WKV4_169M
-    copy_gbps = bench_copy_peak(torch)
-    log(f"bench: {cfg.name} steps={args.steps} warmup={args.warmup} rotate={args.rotate}")
-    prim = bench_wkv4_forward(torch, rw, cfg, args.steps, args.warmup, args.rotate)
-    value = prim["bytes"] / (prim["ms_per_step"] * 1e-3) / 1e9
-    achieved = prim["bytes"] / (prim["kernel_ms"] * 1e-3) / 1e9
-    src_hash = kernel_source_hash()
-    traffic = read_counter_summary("wkv4_fwd_tiled_B8_T1024_C768.md", src_hash)
+    cfg = synth.CFG_WKV4_LONG
+    log(f"bench: {cfg.name} steps={args.steps} warmup={args.warmup}")
+    inp = synth.wkv4_inputs_for(cfg)
+    dev_inputs = wkv4_device_copies(torch, inp, rotate=1)
+    ms = bench_wkv4_headline(torch, rw, cfg, dev_inputs, args.steps, args.warmup)
+    del dev_inputs
+    torch.cuda.empty_cache()
+    nbytes = 12 * cfg.B * cfg.T * cfg.C
+    value = nbytes / (ms * 1e-3) / 1e9
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -561,7 +559,7 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(prim["ms_per_step"], 6),
+        "ms_per_step": round(ms, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -569,104 +567,101 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "C": cfg.C,
                    "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
-                   "pct_of_copy_peak": round(100 * value / copy_gbps, 2),
-                   "gelem_per_s": round(prim["elems"] / (prim["ms_per_step"] * 1e-3) / 1e9, 2),
-                   "bytes_per_elem": 12, "rotated_copies": args.rotate},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": "wkv4_fwd_tiled",
-                     "kernel_us": round(prim["kernel_ms"] * 1e3, 3),
-                     "kernel_source": src_hash},
+                   "gelem_per_s": round(cfg.B * cfg.T * cfg.C / (ms * 1e-3) / 1e9, 2),
+                   "bytes_per_elem": 12, "rotated_copies": 1},
+        # one kernel per step, launched back to back: the step time is the
+        # kernel's mean duration plus the sub-microsecond launch gap
+        "roofline": wkv4_roofline(cfg, ms, "wkv4_fwd_tiled_B1_T65536_C5120.md"),
     }
-    line["copy_peak_GBps"] = round(copy_gbps, 1)
 
     want = set() if args.no_secondary else {x for x in args.secondary.split(",") if x}
-    if want:
-        sec = {}
-        if "hot" in want:
-            log(f"bench: {cfg.name} hot (one copy of k, v, y)")
-            r = bench_wkv4_forward(torch, rw, cfg, steps=args.steps, warmup=args.warmup, rotate=1)
-            sec[cfg.name + "_hot"] = {
-                "ms": round(r["ms_per_step"], 5), "kernel_ms": round(r["kernel_ms"], 5),
-                "GBps": round(r["bytes"] / (r["ms_per_step"] * 1e-3) / 1e9, 1)}
-        if "long" in want:
-            lc = synth.CFG_WKV4_LONG
-            log(f"bench: {lc.name}")
-            r = bench_wkv4_forward(torch, rw, lc, steps=10, warmup=2, rotate=1)
-            sec[lc.name] = {"ms": round(r["ms_per_step"], 4),
-                            "kernel_ms": round(r["kernel_ms"], 4),
-                            "GBps": round(r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9, 1),
-                            "gelem_per_s": round(r["elems"] / (r["kernel_ms"] * 1e-3) / 1e9, 1)}
-        if "decode" in want or "decode-graph" in want:
-            dc = synth.CFG_WKV4_DECODE
-            log(f"bench: {dc.name}")
-            r = bench_decode(torch, rw, dc, reps=3, graph="decode-graph" in want)
-            d = {"eager_ms": round(r["eager_ms"], 3),
-                 "eager_GBps": round(r["bytes"] / (r["eager_ms"] * 1e-3) / 1e9, 1)}
-            if r["graph_ms"] is not None:
-                d.update({"graph_ms": round(r["graph_ms"], 3),
-                          "graph_GBps": round(r["bytes"] / (r["graph_ms"] * 1e-3) / 1e9, 1),
-                          "us_per_step_graph": round(1e3 * r["graph_ms"] / dc.steps, 3)})
-            sec[dc.name] = d
-        if "eagle" in want:
-            ec = synth.CFG_WKV5_EAGLE
-            log(f"bench: {ec.name}")
-            r = bench_wkv5(torch, rw, ec, reps=5)
-            sec[ec.name] = {"ms": round(r["ms"], 4),
-                            "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
-                            "algorithmic_TFLOPs": round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 2),
-                            "mfma_busy_pct": read_counter_summary(
-                                "wkv5_fwd_chunked_mfma_B4_T4096_H32_D64.md",
-                                kernel_source_hash(("wkv5.hip", "eagle_common.h", "wkv_device.h")),
-                                "mfma_busy_pct")}
-        for key, bc, n_steps in (("backward", cfg, 100), ("backward-long", synth.CFG_WKV4_LONG, 3)):
-            if key in want:
-                name = bc.name.replace("wkv4_fwd", "wkv4_bwd")
-                log(f"bench: {name}")
-                r = bench_wkv4_backward(torch, rw, bc, steps=n_steps, warmup=2)
-                sec[name] = {"ms": round(r["ms"], 5),
-                             "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
-                             "bytes_per_elem": 20,
-                             "gelem_per_s": round(r["elems"] / (r["ms"] * 1e-3) / 1e9, 1)}
-        if "train" in want:
-            name = cfg.name.replace("wkv4_fwd", "wkv4_train_step")
+    sec = {}
+    if "169m" in want or "169m-hot" in want:
+        c2 = synth.CFG_WKV4_169M
+        i2 = synth.wkv4_inputs_for(c2)
+        for key, rot in (("169m", 5), ("169m-hot", 1)):
+            if key not in want:
+                continue
+            log(f"bench: {c2.name} rotating {rot} cop{'ies' if rot > 1 else 'y'}")
+            d2 = wkv4_device_copies(torch, i2, rot)
+            ms2, n2, per2 = bench_wkv4_secondary(torch, rw, c2, d2)
+            del d2
+            name = c2.name if rot > 1 else c2.name + "_hot"
+            g = 12 * c2.B * c2.T * c2.C / (ms2 * 1e-3) / 1e9
+            sec[name] = {"ms": round(ms2, 5), "GBps": round(g, 1),
+                         "gelem_per_s": round(c2.B * c2.T * c2.C / (ms2 * 1e-3) / 1e9, 1),
+                         "rotated_copies": rot, "calls_per_repeat": n2,
+                         "repeats_ms": [round(x, 5) for x in per2]}
+            if rot > 1:
+                sec[name]["roofline"] = wkv4_roofline(c2, ms2, "wkv4_fwd_tiled_B8_T1024_C768.md")
+    if "decode" in want or "decode-graph" in want:
+        dc = synth.CFG_WKV4_DECODE
+        log(f"bench: {dc.name}")
+        r = bench_decode(torch, rw, dc, graph="decode-graph" in want)
+        d = {"eager_ms": round(r["eager_ms"], 3),
+             "eager_GBps": round(r["bytes"] / (r["eager_ms"] * 1e-3) / 1e9, 1),
+             "us_per_step_eager": round(1e3 * r["eager_ms"] / dc.steps, 3),
+             "bytes_per_elem_step": 36,
+             "note": "effective bandwidth: the 12.6 MB state can stay in the 256 MB MALL"}
+        if r["graph_ms"] is not None:
+            d.update({"graph_ms": round(r["graph_ms"], 3),
+                      "graph_GBps": round(r["bytes"] / (r["graph_ms"] * 1e-3) / 1e9, 1),
+                      "us_per_step_graph": round(1e3 * r["graph_ms"] / dc.steps, 3)})
+        sec[dc.name] = d
+    for key, finch in (("eagle", False), ("finch", True)):
+        if key not in want:
+            continue
+        mc = synth.CFG_WKV6_FINCH if finch else synth.CFG_WKV5_EAGLE
+        log(f"bench: {mc.name}")
+        r = bench_matrix_forward(torch, rw, mc, finch)
+        hsrc = kernel_source_hash(("wkv6.hip" if finch else "wkv5.hip", "eagle_common.h",
+                                   "wkv_device.h"))
+        prof = (("wkv6" if finch else "wkv5") + "_fwd_chunked_mfma_B4_T4096_H32_D64.md")
+        sec[mc.name] = {"ms": round(r["ms"], 4),
+                        "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
+                        "bytes_per_elem": 14 if finch else 10,
+                        "algorithmic_TFLOPs": round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 2),
+                        "mfma_busy_pct": read_counter_summary(prof, hsrc, "mfma_busy_pct"),
+                        "rotated_copies": r["rotated_copies"]}
+    for key, bc in (("backward", synth.CFG_WKV4_169M), ("backward-long", synth.CFG_WKV4_LONG)):
+        if key in want:
+            name = bc.name.replace("wkv4_fwd", "wkv4_bwd")
             log(f"bench: {name}")
-            r = bench_wkv4_train(torch, rw, cfg, steps=100, warmup=2)
+            r = bench_wkv4_backward(torch, rw, bc)
             sec[name] = {"ms": round(r["ms"], 5),
-                         "ms_forward_plus_backward": round(r["ms_separate"], 5),
                          "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
-                         "bytes_per_elem": 32}
-        if "finch" in want:
-            fc = synth.CFG_WKV6_FINCH
-            log(f"bench: {fc.name}")
-            r = bench_wkv6(torch, rw, fc, reps=5)
-            sec[fc.name] = {"ms": round(r["ms"], 4),
-                            "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
-                            "bytes_per_elem": 14,
-                            "algorithmic_TFLOPs": round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 2),
-                            "mfma_busy_pct": read_counter_summary(
-                                "wkv6_fwd_chunked_mfma_B4_T4096_H32_D64.md",
-                                kernel_source_hash(("wkv6.hip", "eagle_common.h", "wkv_device.h")),
-                                "mfma_busy_pct")}
-        if "eagle-decode" in want:
-            ed = synth.CFG_WKV5_DECODE
-            log(f"bench: {ed.name}")
-            r = bench_wkv5_decode(torch, rw, ed, reps=3)
-            sec[ed.name] = {"ms": round(r["ms"], 4),
-                            "us_per_step": round(1e3 * r["ms"] / ed.steps, 3),
-                            "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1)}
+                         "bytes_per_elem": 20,
+                         "gelem_per_s": round(r["elems"] / (r["ms"] * 1e-3) / 1e9, 1)}
+    if "train" in want:
+        tc = synth.CFG_WKV4_169M
+        name = tc.name.replace("wkv4_fwd", "wkv4_train_step")
+        log(f"bench: {name}")
+        r = bench_wkv4_train(torch, rw, tc)
+        sec[name] = {"ms": round(r["ms"], 5),
+                     "ms_forward_plus_backward": round(r["ms_separate"], 5),
+                     "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
+                     "bytes_per_elem": 32}
+    if "eagle-decode" in want:
+        ed = synth.CFG_WKV5_DECODE
+        log(f"bench: {ed.name}")
+        r = bench_wkv5_decode(torch, rw, ed)
+        sec[ed.name] = {"ms": round(r["ms"], 4),
+                        "us_per_step": round(1e3 * r["ms"] / ed.steps, 3),
+                        "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
+                        "note": "effective bandwidth: the 32 MB state can stay in the MALL"}
+    if sec:
         line["secondary"] = sec
 
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
-        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
-        sec = line.get("secondary", {})
-        samplers = {synth.CFG_WKV4_LONG.name: cpu_sample_long,
+        line["cpu_baseline"] = cpu_baseline_wkv4(cfg, inp, min(args.cpu_channels, cfg.C))
+        samplers = {synth.CFG_WKV4_169M.name: cpu_sample_169m,
                     synth.CFG_WKV4_DECODE.name: cpu_sample_decode,
-                    synth.CFG_WKV5_EAGLE.name: cpu_sample_eagle,
+                    synth.CFG_WKV5_EAGLE.name: lambda: cpu_sample_matrix(False),
                     synth.CFG_WKV5_DECODE.name: cpu_sample_eagle_decode,
-                    synth.CFG_WKV6_FINCH.name: cpu_sample_finch,
-                    synth.CFG_WKV4_169M.name.replace("wkv4_fwd", "wkv4_bwd"): cpu_sample_backward}
+                    synth.CFG_WKV6_FINCH.name: lambda: cpu_sample_matrix(True),
+                    synth.CFG_WKV4_169M.name.replace("wkv4_fwd", "wkv4_bwd"):
+                        cpu_sample_backward}
         for name, fn in samplers.items():
             if name in sec:
                 sec[name]["cpu_baseline"] = fn()
