@@ -519,6 +519,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first copy 1 GiB three times with torch (a plain copy of known "
+                         "size, for scaling the HBM byte counters of a rocprofv3 run)")
     ap.add_argument("--cpu-channels", type=int, default=2560,
                     help="channels of the headline workload the oracle sample covers")
     ap.add_argument("--secondary",
@@ -542,6 +545,15 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+
+    if args.copy_calibration:
+        a = torch.ones((1 << 28,), dtype=torch.float32, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+        torch.cuda.empty_cache()
 
     cfg = synth.CFG_WKV4_LONG
     log(f"bench: {cfg.name} steps={args.steps} warmup={args.warmup}")

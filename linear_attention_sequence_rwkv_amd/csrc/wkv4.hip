@@ -119,6 +119,98 @@ __device__ __forceinline__ void write_state(const StateIO& sio, const Hist (&h)[
   }
 }
 
+// Look-back of tile `tile` of channel block g (one wave, lane = channel):
+// the history of every earlier tile of the block, rebuilt as
+// inc(p) + agg(p+1) + ... + agg(tile-1), folded in that order for the
+// nearest p (within kWin) whose inclusive history is out.  That is the order
+// in which the chain of inclusive histories is built, so the result has the
+// same bits whichever p the timing offers: the forward is deterministic.
+// With `early`, the first poll's words (lanes < kWin: inc and agg words of
+// tile-1-lane) were loaded by the caller.  A wait beyond kSpinLimit polls
+// raises the error word and returns NaN.
+template <int CPL, int TILE>
+__device__ __forceinline__ void lookback(int tile, int g, int groups,
+                                         const uint64_t* __restrict__ slots, uint32_t* hdr,
+                                         uint32_t tag, const float (&w2)[CPL], bool early,
+                                         uint64_t e_inc, uint64_t e_agg, Hist (&acc)[CPL]) {
+  constexpr int W = 64 * CPL;
+  constexpr int SLOT = 8 * W;  // words per (tile, block): agg A,B,kr,n then inc A,B,kr,n
+  // Predecessor payloads loaded per round trip while folding a prefix
+  // (the batch costs 8 VGPRs per payload and channel).
+  constexpr int kFoldBatch = CPL == 1 ? 2 : 1;
+  const int lane = threadIdx.x & 63;
+  const int ch0 = lane * CPL;
+  uint32_t spins = 0;
+  for (;;) {
+    // Poll kWin earlier tiles in one round trip: lane i reads the first
+    // word of tile (tile-1-i)'s inclusive and aggregate histories.
+    const int pi = tile - 1 - lane;
+    bool inc_ok = false, agg_ok = false;
+    if (early) {
+      inc_ok = lane < kWin && pi >= 0 && tag_ok(e_inc, tag);
+      agg_ok = lane < kWin && pi > 0 && tag_ok(e_agg, tag);
+      early = false;
+    } else if (lane < kWin && pi >= 0) {
+      const uint64_t* sp = slots + (size_t(pi) * groups + g) * SLOT;
+      inc_ok = tag_ok(tagged_load(sp + 4 * W), tag);
+      agg_ok = pi > 0 && tag_ok(tagged_load(sp), tag);  // tile 0 has no aggregate
+    }
+    const uint64_t inc_mask = __ballot(inc_ok);
+    const uint64_t agg_mask = __ballot(agg_ok);
+    const int m = inc_mask ? int(__builtin_ctzll(inc_mask)) : kWin;
+    const int a = int(__builtin_ctzll(~agg_mask));  // bits >= kWin are 0
+    if (inc_mask != 0 && a >= m) {
+      // Payload j = 0 is inc(tile-1-m), payload j >= 1 is agg(tile-1-m+j).
+      const int p0 = tile - 1 - m;
+      bool ok = true;
+      for (int j0 = 0; j0 <= m && ok; j0 += kFoldBatch) {
+        uint64_t x[kFoldBatch][CPL][4];
+#pragma unroll
+        for (int jj = 0; jj < kFoldBatch; ++jj) {
+          const int j = j0 + jj;
+          const uint64_t* q =
+              slots + (size_t(p0 + j) * groups + g) * SLOT + (j == 0 ? 4 * W : 0) + ch0;
+#pragma unroll
+          for (int c = 0; c < CPL; ++c)
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+              x[jj][c][f] = j <= m ? tagged_load(q + f * W + c) : (uint64_t(tag) << 32);
+        }
+#pragma unroll
+        for (int jj = 0; jj < kFoldBatch; ++jj)
+#pragma unroll
+          for (int c = 0; c < CPL; ++c)
+#pragma unroll
+            for (int f = 0; f < 4; ++f) ok = ok && tag_ok(x[jj][c][f], tag);
+        ok = __all(ok);  // a payload not yet visible on every lane: poll again
+        if (!ok) break;
+#pragma unroll
+        for (int jj = 0; jj < kFoldBatch; ++jj) {
+          const int j = j0 + jj;
+          if (j > m) break;
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            const Hist h{tag_val(x[jj][c][0]), tag_val(x[jj][c][1]), tag_val(x[jj][c][2]),
+                         tag_val(x[jj][c][3])};
+            acc[c] = j == 0 ? h : hist_concat(acc[c], h, float(TILE), w2[c]);
+          }
+        }
+      }
+      if (ok) break;
+    }
+    if (++spins > kSpinLimit) {
+      if (lane == 0) raise_error(hdr + kHdrError, kErrGaveUp);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const float nan = __builtin_nanf("");
+        acc[c] = Hist{nan, nan, nan, 0.f};
+      }
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
 // EMIT = false: publish the tiles' histories only (the backward's prefix
 // pass); no output rows, no state.  With `mids`, each tile also publishes the
 // inclusive history at its middle (after NW/2 waves), for a consumer tiled at
@@ -144,9 +236,6 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
   constexpr int W = 64 * CPL;        // channels per block
   constexpr int TILE = L * NW;       // tokens per tile
   constexpr int SLOT = 8 * W;        // words per (tile, block): agg A,B,kr,n then inc A,B,kr,n
-  // Predecessor payloads loaded per round trip while folding a prefix
-  // (the batch costs 8 VGPRs per payload and channel).
-  constexpr int kFoldBatch = CPL == 1 ? 2 : 1;
   __shared__ int s_tile;
   __shared__ uint32_t s_tag;
   __shared__ HistLds<W> s_sum[NW];
@@ -166,7 +255,7 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
       s_tile = claim_tile(hdr, counters, g, n_tiles, groups, tg);
       s_tag = tg;
     }
-    __syncthreads();
+    lds_barrier();
     tile = __builtin_amdgcn_readfirstlane(s_tile);
     // Only a workspace that was never zero-filled can get here: flag it and
     // write NaN over the rows of the tile this workgroup's launch index
@@ -231,7 +320,7 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
     e_inc = tagged_load(sp + 4 * W);
     if (tile - 1 - lane > 0) e_agg = tagged_load(sp);  // tile 0 has no aggregate
   }
-  __syncthreads();
+  lds_barrier();
   __builtin_amdgcn_s_setprio(0);
   const uint32_t tag = __builtin_amdgcn_readfirstlane(s_tag);
 
@@ -282,82 +371,8 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
       if (tile == n_tiles - 1) write_state(sio, inc, w2, valid, size_t(bi) * C + size_t(cb) * W + ch0);
     } else {
       publish(0, agg);
-      // The prefix is rebuilt as inc(p) + agg(p+1) + ... + agg(tile-1),
-      // folded in that order for the nearest p (within kWin) whose inclusive
-      // history is out.  That is the order in which the chain of inclusive
-      // histories is built, so the result has the same bits whichever p the
-      // timing offers: the forward is deterministic.
       Hist acc[CPL];
-      uint32_t spins = 0;
-      bool early = in_order != 0;  // the first poll's words are already in
-      for (;;) {
-        // Poll kWin earlier tiles in one round trip: lane i reads the first
-        // word of tile (tile-1-i)'s inclusive and aggregate histories.
-        const int pi = tile - 1 - lane;
-        bool inc_ok = false, agg_ok = false;
-        if (early) {
-          inc_ok = lane < kWin && pi >= 0 && tag_ok(e_inc, tag);
-          agg_ok = lane < kWin && pi > 0 && tag_ok(e_agg, tag);
-          early = false;
-        } else if (lane < kWin && pi >= 0) {
-          const uint64_t* sp = slots + (size_t(pi) * groups + g) * SLOT;
-          inc_ok = tag_ok(tagged_load(sp + 4 * W), tag);
-          agg_ok = pi > 0 && tag_ok(tagged_load(sp), tag);  // tile 0 has no aggregate
-        }
-        const uint64_t inc_mask = __ballot(inc_ok);
-        const uint64_t agg_mask = __ballot(agg_ok);
-        const int m = inc_mask ? int(__builtin_ctzll(inc_mask)) : kWin;
-        const int a = int(__builtin_ctzll(~agg_mask));  // bits >= kWin are 0
-        if (inc_mask != 0 && a >= m) {
-          // Payload j = 0 is inc(tile-1-m), payload j >= 1 is agg(tile-1-m+j).
-          const int p0 = tile - 1 - m;
-          bool ok = true;
-          for (int j0 = 0; j0 <= m && ok; j0 += kFoldBatch) {
-            uint64_t x[kFoldBatch][CPL][4];
-#pragma unroll
-            for (int jj = 0; jj < kFoldBatch; ++jj) {
-              const int j = j0 + jj;
-              const uint64_t* q =
-                  slots + (size_t(p0 + j) * groups + g) * SLOT + (j == 0 ? 4 * W : 0) + ch0;
-#pragma unroll
-              for (int c = 0; c < CPL; ++c)
-#pragma unroll
-                for (int f = 0; f < 4; ++f)
-                  x[jj][c][f] = j <= m ? tagged_load(q + f * W + c) : (uint64_t(tag) << 32);
-            }
-#pragma unroll
-            for (int jj = 0; jj < kFoldBatch; ++jj)
-#pragma unroll
-              for (int c = 0; c < CPL; ++c)
-#pragma unroll
-                for (int f = 0; f < 4; ++f) ok = ok && tag_ok(x[jj][c][f], tag);
-            ok = __all(ok);  // a payload not yet visible on every lane: poll again
-            if (!ok) break;
-#pragma unroll
-            for (int jj = 0; jj < kFoldBatch; ++jj) {
-              const int j = j0 + jj;
-              if (j > m) break;
-#pragma unroll
-              for (int c = 0; c < CPL; ++c) {
-                const Hist h{tag_val(x[jj][c][0]), tag_val(x[jj][c][1]), tag_val(x[jj][c][2]),
-                             tag_val(x[jj][c][3])};
-                acc[c] = j == 0 ? h : hist_concat(acc[c], h, float(TILE), w2[c]);
-              }
-            }
-          }
-          if (ok) break;
-        }
-        if (++spins > kSpinLimit) {
-          if (lane == 0) raise_error(hdr + kHdrError, kErrGaveUp);
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) {
-            const float nan = __builtin_nanf("");
-            acc[c] = Hist{nan, nan, nan, 0.f};
-          }
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
+      lookback<CPL, TILE>(tile, g, groups, slots, hdr, tag, w2, in_order != 0, e_inc, e_agg, acc);
       Hist inc[CPL];
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
@@ -391,7 +406,7 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // Pass 2: start from the tile prefix plus the earlier waves, emit y.
   if (EMIT && n > 0) {
@@ -413,6 +428,287 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
       done_before == uint32_t(groups - 1)) {
     // Every block is done reading the epoch: leave the header for the next call.
     hdr_store(hdr, kHdrClaimed, 0u);
+    hdr_store(hdr, kHdrEpoch, tag);
+  }
+}
+
+// Items per claim of the streamed forward: a workgroup takes this many
+// consecutive (tile, block) items per atomic, one batch ahead.
+constexpr int kStreamBatch = 2;
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8; an all-ones field waits for nothing).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
+
+// The streamed forward, for grids far larger than what the device holds at
+// once.  A resident-sized grid of workgroups works through all items (tile
+// t of channel block g is item t * groups + g) in increasing order:
+//   * one control wave per workgroup claims batches of kStreamBatch
+//     consecutive items from the header's counter {tag, count}, the next
+//     batch while the current one runs; for each item it joins the compute
+//     waves' summaries, publishes the tile's aggregate, resolves the tile
+//     prefix by the look-back and publishes the inclusive history;
+//   * NC compute waves (L tokens each) hold the current item's rows in
+//     registers while the next item's rows stream into shared memory
+//     (buffer loads straight to LDS, 16 KB per wave); at the start of an
+//     item a wave moves them into registers and sends the loads of the item
+//     after it.
+// The control wave issues no row loads, so its polls never wait behind them
+// (a wave's memory operations complete in issue order).  Items are claimed
+// in increasing order by running workgroups and wait only for smaller
+// items, so no grid size or residency can deadlock the launch.  The last
+// workgroup to finish advances the epoch and leaves the counter at
+// {tag + 1, 0} for the next call.  The summaries and prefix in shared memory
+// are double-buffered by item parity, so consecutive items need no barrier
+// between them.
+template <int L, int NC>
+__global__ __launch_bounds__(64 * (NC + 1)) void wkv4_fwd_stream(
+    int T, int C, int n_cblk, int groups, int n_tiles,
+    const float* __restrict__ w, const float* __restrict__ u,
+    const float* __restrict__ k, const float* __restrict__ v, float* __restrict__ y,
+    uint32_t* __restrict__ hdr, uint64_t* __restrict__ slots, StateIO sio) {
+  constexpr int W = 64;
+  constexpr int TILE = L * NC;
+  constexpr int SLOT = 8 * W;
+  constexpr int CTRL = NC;  // index of the control wave
+  typedef __attribute__((address_space(3))) void* LdsPtr;
+  __shared__ uint32_t s_tag;
+  __shared__ int s_batch;
+  __shared__ HistLds<W> s_sum[2][NC];
+  __shared__ HistLds<W> s_pre[2];
+  __shared__ __attribute__((aligned(16))) float s_rows[NC][2][L][W];  // next item's k, v rows
+
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool ctrl = wid == CTRL;
+  const bool claimer = ctrl && lane == 0;
+  const int items = n_tiles * groups;
+  uint64_t* ctr = reinterpret_cast<uint64_t*>(hdr + kHdrStream);
+
+  // The claim of the batch ahead: issued with one atomic, its reply read at
+  // the next batch change (claimer lane only).
+  uint64_t pending = 0;
+  auto resolve = [&](uint64_t old, uint32_t tg) -> int {
+    if (uint32_t(old >> 32) != tg) {
+      // Left by an earlier call, or never used: raise to {tag, 0} and claim
+      // again (a later tag cannot appear before this call's last workgroup
+      // has finished).
+      __hip_atomic_fetch_max(ctr, uint64_t(tg) << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      old = __hip_atomic_fetch_add(ctr, uint64_t(kStreamBatch), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (uint32_t(old >> 32) != tg) return -1;
+    return int(min(uint32_t(old), uint32_t(items)));
+  };
+  auto claim_ahead = [&]() {
+    pending = __hip_atomic_fetch_add(ctr, uint64_t(kStreamBatch), __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+  };
+
+  if (claimer) {
+    // The claim must not run before the epoch read has returned: tie the
+    // increment to the loaded value.
+    const uint32_t tg = hdr_load(hdr, kHdrEpoch) + 1u;
+    uint64_t inc = kStreamBatch;
+    asm volatile("" : "+v"(inc) : "v"(tg));
+    const uint64_t old =
+        __hip_atomic_fetch_add(ctr, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int first = resolve(old, tg);
+    s_tag = tg;
+    s_batch = first;
+    if (first >= 0 && first < items) claim_ahead();
+  }
+  lds_barrier();
+  const uint32_t tag = __builtin_amdgcn_readfirstlane(s_tag);
+  int item = __builtin_amdgcn_readfirstlane(s_batch);
+  if (item < 0) {
+    // A workspace that was never zero-filled: flag it, write NaN over the
+    // rows of the items this workgroup's launch index names, touch nothing.
+    if (claimer) raise_error(hdr + kHdrError, kErrNotZeroed);
+    if (!ctrl)
+      for (int it = int(blockIdx.x); it < items; it += int(gridDim.x))
+        nan_rows<1, L, NC>(it / groups, it % groups, T, C, n_cblk, y);
+    item = items;
+  }
+  int batch_end = min(item + kStreamBatch, items);
+
+  // The item after `it`: the next one of its batch, else the batch claimed
+  // ahead (whose successor is then claimed).  Uniform over the workgroup.
+  auto next_item = [&](int it) -> int {
+    if (it + 1 < batch_end) return it + 1;
+    if (claimer) {
+      const int nb = resolve(pending, tag);
+      s_batch = nb < 0 ? items : nb;
+      if (nb >= 0 && nb < items) claim_ahead();
+    }
+    lds_barrier();
+    const int nb = __builtin_amdgcn_readfirstlane(s_batch);
+    batch_end = min(nb + kStreamBatch, items);
+    return nb;
+  };
+
+  // Where this compute wave's rows of an item live.
+  struct Rows {
+    int n;       // tokens of this wave in the tile
+    int col;     // this lane's column in the block (clamped into range for loads)
+    int cl;      // its channel, cb * W + col
+    bool valid;  // the lane has a channel
+    size_t row0;
+  };
+  auto rows_of = [&](int it) -> Rows {
+    const int tile = it / groups, g = it - (it / groups) * groups;
+    const int bi = g / n_cblk, cb = g - (g / n_cblk) * n_cblk;
+    Rows r;
+    const int t0 = tile * TILE + wid * L;
+    r.n = ctrl ? 0 : max(0, min(L, T - t0));
+    r.valid = cb * W + lane < C;
+    r.col = r.valid ? lane : C - cb * W - 1;
+    r.cl = cb * W + r.col;
+    r.row0 = (size_t(bi) * size_t(T) + size_t(t0)) * size_t(C) + size_t(cb) * W;
+    return r;
+  };
+  const uint32_t row_bytes = uint32_t(C) * 4u;
+  const uint32_t span = uint32_t(L - 1) * row_bytes + uint32_t(W) * 4u;
+  // Sends the loads of an item's rows into this wave's shared rows (lane i
+  // fills word i of a row); w, u of the lane's channel go to registers.
+  // Returns the number of rows sent.
+  auto send = [&](int it, float& wv, float& uv) -> int {
+    const Rows r = rows_of(it);
+    wv = r.n > 0 ? w[r.cl] : 0.f;
+    uv = r.n > 0 ? u[r.cl] : 0.f;
+    const Rsrc rk = make_rsrc(k + r.row0, span);
+    const Rsrc rv = make_rsrc(v + r.row0, span);
+    const uint32_t voff = uint32_t(r.col) * 4u;
+    for (int s = 0; s < r.n; ++s) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LdsPtr)&s_rows[wid][0][s][0], 4, voff,
+                                               uint32_t(s) * row_bytes, 0, kNonTemporal);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LdsPtr)&s_rows[wid][1][s][0], 4, voff,
+                                               uint32_t(s) * row_bytes, 0, kNonTemporal);
+    }
+    return r.n;
+  };
+
+  float kk[L][1], vv[L][1];
+  float wv = 0.f, uv = 0.f;
+  // Memory operations this wave issued after its last row loads (the y
+  // stores of an item): the wait for the rows allows that many to remain.
+  int stores_after = 0;
+  if (!ctrl) send(item < items ? item : items, wv, uv);
+  int parity = 0;
+  while (item < items) {
+    const int nxt = next_item(item);
+    const int tile = item / groups, g = item - (item / groups) * groups;
+    const int bi = g / n_cblk, cb = g - (g / n_cblk) * n_cblk;
+    const Rows r = rows_of(item);
+    float w2 = 0.f, u2 = 0.f;
+    if (!ctrl) {
+      // This item's rows are in shared memory once the loads sent before the
+      // last item's stores are done.  (The compiler does not track loads
+      // that write shared memory: the waits are explicit.)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      if (stores_after == L)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(L));
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int s = 0; s < L; ++s) {
+        kk[s][0] = s < r.n ? s_rows[wid][0][s][lane] * kLog2e : 0.f;
+        vv[s][0] = s < r.n ? s_rows[wid][1][s][lane] : 0.f;
+      }
+      w2 = wv * kLog2e;
+      u2 = uv * kLog2e;
+      // The shared rows are read before the next item's loads overwrite them.
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      send(nxt, wv, uv);  // no loads past the last item
+      stores_after = 0;
+      __builtin_amdgcn_s_setprio(2);
+      s_sum[parity][wid].put(lane, summarize<L, 1, false>(kk, vv, 0, r.n, w2));
+      __builtin_amdgcn_s_setprio(0);
+    }
+    // Control wave: while the compute waves summarise, its first look-back
+    // poll goes out; once the summaries are in it publishes the tile's
+    // aggregate at once (later tiles fold it without waiting for this
+    // tile's prefix), then resolves the prefix and publishes the inclusive
+    // history.
+    float w2c[1] = {0.f};
+    uint64_t e_inc = 0, e_agg = 0;
+    if (ctrl) {
+      w2c[0] = w[r.cl] * kLog2e;
+      if (tile > 0 && lane < kWin && tile - 1 - lane >= 0) {
+        const uint64_t* sp = slots + (size_t(tile - 1 - lane) * groups + g) * SLOT;
+        e_inc = tagged_load(sp + 4 * W);
+        if (tile - 1 - lane > 0) e_agg = tagged_load(sp);  // tile 0 has no aggregate
+      }
+    }
+    lds_barrier();  // the summaries are in
+    if (ctrl) {
+      __builtin_amdgcn_s_setprio(3);
+      const int tile_t0 = tile * TILE;
+      const int tile_n = min(TILE, T - tile_t0);
+      Hist agg = s_sum[parity][0].get(lane);
+      for (int i = 1; i < NC; ++i) {
+        const int ni = max(0, min(L, T - (tile_t0 + i * L)));
+        agg = hist_concat(agg, s_sum[parity][i].get(lane), float(ni), w2c[0]);
+      }
+      uint64_t* mine = slots + (size_t(tile) * groups + g) * SLOT + lane;
+      auto publish = [&](int kind, const Hist& h) {
+        uint64_t* q = mine + kind * 4 * W;
+        tagged_store(q + 0 * W, h.A, tag);
+        tagged_store(q + 1 * W, h.Bd, tag);
+        tagged_store(q + 2 * W, h.kr, tag);
+        tagged_store(q + 3 * W, h.n, tag);
+      };
+      Hist pre[1];
+      if (tile == 0) {
+        // History before the first token: empty, or the caller's state.
+        pre[0] = hist_empty();
+        if (sio.a_in) {
+          const size_t si = size_t(bi) * C + r.cl;
+          pre[0] = Hist{sio.a_in[si], sio.b_in[si], sio.p_in[si] * kLog2e, 0.f};
+        }
+      } else {
+        publish(0, agg);
+        lookback<1, TILE>(tile, g, groups, slots, hdr, tag, w2c, true, e_inc, e_agg, pre);
+      }
+      const Hist inc = hist_concat(pre[0], agg, float(tile_n), w2c[0]);
+      publish(1, inc);
+      if (tile == n_tiles - 1) {
+        const Hist fin[1] = {inc};
+        write_state(sio, fin, w2c, r.valid, size_t(bi) * C + size_t(cb) * W + lane);
+      }
+      s_pre[parity].put(lane, pre[0]);
+      __builtin_amdgcn_s_setprio(0);
+    }
+    lds_barrier();  // the prefix is in
+    if (!ctrl && r.n > 0) {
+      const float w2a[1] = {w2}, u2a[1] = {u2};
+      Hist hs[1] = {s_pre[parity].get(lane)};
+      for (int i = 0; i < wid; ++i)
+        hs[0] = hist_concat(hs[0], s_sum[parity][i].get(lane), float(L), w2);
+      // A partial wave runs the blocked pass over its zero rows too (they
+      // come after its real tokens, so no real output depends on them); the
+      // resource ends at its last real row, so their stores are dropped.
+      const Rsrc ry = make_rsrc(y + r.row0, uint32_t(r.n - 1) * row_bytes + uint32_t(W) * 4u);
+      const uint32_t voff_out = r.valid ? uint32_t(lane) * 4u : kDropOffset;
+      emit_rows_blocked<L, 1>(ry, voff_out, row_bytes, hs, kk, vv, u2a, w2a);
+      stores_after = L;
+    }
+    parity ^= 1;
+    item = nxt;
+  }
+  // Every workgroup of this call has read the epoch and stopped claiming
+  // once the last one is here: it leaves the header for the next call.
+  if (claimer && hdr_add(hdr, kHdrClaimed, 1u) == gridDim.x - 1u) {
+    hdr_store(hdr, kHdrClaimed, 0u);
+    __hip_atomic_store(ctr, uint64_t(tag + 1u) << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     hdr_store(hdr, kHdrEpoch, tag);
   }
 }
@@ -501,8 +797,15 @@ constexpr Variant kVariants[] = {{4, 8, 8}, {4, 16, 4}, {4, 16, 8},
 // device holds at once, cached per device; 0 if it cannot be determined, or
 // if the kTuneWkv4Order override asks for claimed tiles (tests compare the
 // modes).
+int64_t device_capacity(const void* kern, int block);
+
 int64_t resident_workgroups(const void* kern, int block) {
   if (tuning(kTuneWkv4Order) == 1) return 0;
+  return device_capacity(kern, block);
+}
+
+// Workgroups of `kern` that the current device holds at once (0 if unknown).
+int64_t device_capacity(const void* kern, int block) {
   constexpr int kMaxDev = 64;
   struct Entry {
     const void* kern;
@@ -545,10 +848,39 @@ hipError_t launch_tiled(const Wkv4Plan& pl, int64_t T, int64_t C, const float* w
   return hipGetLastError();
 }
 
+// The streamed forward: 32 tokens x 4 compute waves per tile (the tiles of
+// the other forwards) and a control wave; the grid is what the device holds
+// at once, no larger than the number of batches.
+constexpr int kStreamL = 32;
+constexpr int kStreamNC = 4;
+
+hipError_t launch_stream(const Wkv4Plan& pl, int64_t T, int64_t C, const float* w,
+                         const float* u, const float* k, const float* v, float* y, void* ws,
+                         const StateIO& sio, hipStream_t stream) {
+  char* base = static_cast<char*>(ws);
+  uint32_t* hdr = reinterpret_cast<uint32_t*>(base);
+  uint64_t* slots = reinterpret_cast<uint64_t*>(base + pl.slots_offset);
+  constexpr int kThreads = 64 * (kStreamNC + 1);
+  const void* kern = reinterpret_cast<const void*>(&wkv4_fwd_stream<kStreamL, kStreamNC>);
+  int64_t grid = device_capacity(kern, kThreads);
+  if (grid <= 0) grid = 512;
+  const int64_t batches = (pl.n_tiles * pl.groups + kStreamBatch - 1) / kStreamBatch;
+  grid = grid < batches ? grid : batches;
+  hipLaunchKernelGGL((wkv4_fwd_stream<kStreamL, kStreamNC>), dim3(unsigned(grid)), dim3(kThreads),
+                     0, stream, int(T), int(C), int(pl.n_cblk), int(pl.groups), int(pl.n_tiles), w,
+                     u, k, v, y, hdr, slots, sio);
+  return hipGetLastError();
+}
+
+// Items (128-token tiles x channel blocks) from which the plan streams: far
+// more than the 1024 workgroups of 128-token tiles the device holds at once.
+constexpr int64_t kStreamMinItems = 8192;
+
 }  // namespace
 
 bool wkv4_plan_fixed(int64_t B, int64_t T, int64_t C, int cpl, int L, int NW, Wkv4Plan* plan) {
   Wkv4Plan p;
+  p.stream = 0;
   p.cpl = cpl;
   p.L = L;
   p.NW = NW;
@@ -587,6 +919,16 @@ bool wkv4_plan(int64_t B, int64_t T, int64_t C, Wkv4Plan* plan) {
         L = vv.L;
         NW = vv.NW;
       }
+  }
+  // Grids far beyond what the device holds at once stream their tiles
+  // through a resident-sized grid (B=1 T=65536 C=5120: 40,960 tiles).
+  const int st = tuning(kTuneWkv4Stream);
+  const int64_t items128 = B * ((T + 127) / 128) * ((C + 63) / 64);
+  if (st == 2 || (st == 0 && tuning(kTuneWkv4Tile) == 0 && items128 >= kStreamMinItems)) {
+    if (!wkv4_plan_fixed(B, T, C, 1, kStreamL, kStreamNC, plan)) return false;
+    plan->stream = 1;
+    plan->NW = kStreamNC + 1;
+    return true;
   }
   return wkv4_plan_fixed(B, T, C, cpl, L, NW, plan);
 }
@@ -642,6 +984,7 @@ hipError_t wkv4_forward_launch(const Wkv4Plan& pl, int64_t B, int64_t T, int64_t
                                float* b_out, float* p_out, hipStream_t stream) {
   (void)B;
   const StateIO sio{a_in, b_in, p_in, a_out, b_out, p_out};
+  if (pl.stream) return launch_stream(pl, T, C, w, u, k, v, y, ws, sio, stream);
   switch (pl.cpl * 10000 + pl.L * 100 + pl.NW) {
     case 40808: return launch_tiled<4, 8, 8>(pl, T, C, w, u, k, v, y, ws, sio, stream);
     case 41604: return launch_tiled<4, 16, 4>(pl, T, C, w, u, k, v, y, ws, sio, stream);

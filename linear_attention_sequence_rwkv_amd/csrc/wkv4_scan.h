@@ -21,7 +21,9 @@ __device__ __forceinline__ void raise_error(uint32_t* err, uint32_t bit) {
 }
 
 // Header words (uint32) at the start of a scan workspace.
-enum : int { kHdrError = 0, kHdrEpoch = 1, kHdrClaimed = 2 };
+// kHdrStream: a 64-bit {tag, count} item counter of the streamed forward
+// (words 4 and 5, 8-byte aligned).
+enum : int { kHdrError = 0, kHdrEpoch = 1, kHdrClaimed = 2, kHdrStream = 4 };
 // Bits of the error word (sticky until the workspace is zero-filled again).
 constexpr uint32_t kErrGaveUp = 1u;     // a look-back exceeded its spin limit
 constexpr uint32_t kErrNotZeroed = 2u;  // a claim found a workspace never zero-filled
@@ -34,6 +36,19 @@ __device__ __forceinline__ void hdr_store(uint32_t* h, int i, uint32_t x) {
 }
 __device__ __forceinline__ uint32_t hdr_add(uint32_t* h, int i, uint32_t x) {
   return __hip_atomic_fetch_add(h + i, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A workgroup barrier for data exchanged through shared memory only.
+// __syncthreads also fences global memory, which on gfx9 waits for every
+// outstanding load and store of the wave (s_waitcnt vmcnt(0)), including row
+// loads meant to stay in flight and stores nobody in the workgroup reads.
+// Here only this wave's shared-memory operations complete first; the empty
+// asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // k, v and y stream through buffer resources: a row's offset (s * C * 4
@@ -257,10 +272,11 @@ __device__ __forceinline__ void rescan_blocked(Hist (&hs)[CPL], const float (&kk
 
 // Loads of a wave's rows (FULL: all L of them, else the first n; the rest
 // are zero) and its second pass, specialised so that a full wave carries no
-// per-row checks.
+// per-row checks.  issue_rows only issues the loads (nothing here waits for
+// them); scale_keys, the first use of the values, converts k to base 2.
 template <int L, int CPL, bool FULL>
-__device__ __forceinline__ void load_rows(Rsrc rk, Rsrc rv, uint32_t voff, uint32_t row_bytes,
-                                          int n, float (&kk)[L][CPL], float (&vv)[L][CPL]) {
+__device__ __forceinline__ void issue_rows(Rsrc rk, Rsrc rv, uint32_t voff, uint32_t row_bytes,
+                                           int n, float (&kk)[L][CPL], float (&vv)[L][CPL]) {
 #pragma unroll
   for (int s = 0; s < L; ++s) {
     // Full waves issue their loads in blocks of 8 rows (8 of k, then 8 of v),
@@ -283,10 +299,21 @@ __device__ __forceinline__ void load_rows(Rsrc rk, Rsrc rv, uint32_t voff, uint3
       vv[s][c] = tv[c];
     }
   }
+}
+
+template <int L, int CPL>
+__device__ __forceinline__ void scale_keys(float (&kk)[L][CPL]) {
 #pragma unroll
   for (int s = 0; s < L; ++s)
 #pragma unroll
     for (int c = 0; c < CPL; ++c) kk[s][c] *= kLog2e;
+}
+
+template <int L, int CPL, bool FULL>
+__device__ __forceinline__ void load_rows(Rsrc rk, Rsrc rv, uint32_t voff, uint32_t row_bytes,
+                                          int n, float (&kk)[L][CPL], float (&vv)[L][CPL]) {
+  issue_rows<L, CPL, FULL>(rk, rv, voff, row_bytes, n, kk, vv);
+  scale_keys<L, CPL>(kk);
 }
 
 // Claims the next tile of channel block g for this workgroup (thread 0

@@ -21,7 +21,8 @@ enum TuneKey : int {
   kTuneWkv5Segs = 4,   // Eagle time segments (before the clamp to >= 4 chunks each)
   kTuneWkv6Dv = 5,     // value columns per Finch workgroup: 32 or 64
   kTuneWkv6Segs = 6,   // Finch time segments
-  kTuneKeys = 7
+  kTuneWkv4Stream = 7, // RWKV-4 streamed forward: 0 by size, 1 never, 2 always
+  kTuneKeys = 8
 };
 int tuning(int key);
 bool set_tuning(int key, int value);
@@ -42,10 +43,11 @@ constexpr int64_t kWkv4MaxT = (int64_t(1) << 24) - 64;
 // (tile, block) two published histories (aggregate, inclusive) of 4 tagged
 // 64-bit words per channel each.
 struct Wkv4Plan {
+  int stream;    // 1: the streamed forward (NW - 1 compute waves and a control wave)
   int cpl;       // channels per lane (vector width of the loads)
   int L;         // tokens per wave
   int NW;        // waves per workgroup
-  int64_t tile;  // L * NW
+  int64_t tile;  // L * NW (streamed: L * (NW - 1))
   int64_t n_tiles;
   int64_t n_cblk;  // ceil(C / (64 * cpl))
   int64_t groups;  // B * n_cblk

@@ -49,10 +49,12 @@ def tile_code(tile):
 @contextlib.contextmanager
 def tuned(**settings):
     """Plan overrides for a block: wkv4_tile="cpl,L,NW", wkv4_claim=True,
-    wkv5_dv=, wkv5_segs=, wkv6_dv=, wkv6_segs= (None leaves a key alone)."""
+    wkv4_stream=True/False (always / never the streamed forward), wkv5_dv=,
+    wkv5_segs=, wkv6_dv=, wkv6_segs= (None leaves a key alone)."""
     import linear_attention_sequence_rwkv_amd as rw
     keys = {"wkv4_tile": (rw.RWKV_TUNE_WKV4_TILE, tile_code),
             "wkv4_claim": (rw.RWKV_TUNE_WKV4_ORDER, lambda x: 1 if x else 0),
+            "wkv4_stream": (rw.RWKV_TUNE_WKV4_STREAM, lambda x: 2 if x else 1),
             "wkv5_dv": (rw.RWKV_TUNE_WKV5_DV, int),
             "wkv5_segs": (rw.RWKV_TUNE_WKV5_SEGS, int),
             "wkv6_dv": (rw.RWKV_TUNE_WKV6_DV, int),
