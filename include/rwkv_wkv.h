@@ -67,24 +67,23 @@ int rwkv_last_hip_error(void);
  * or an override.  The values start from the environment, read once at the
  * first call that plans anything (RWKV_WKV4_TILE="cpl,L,NW",
  * RWKV_WKV4_ORDER=claim, RWKV_WKV5_DV, RWKV_WKV5_SEGS, RWKV_WKV6_DV,
- * RWKV_WKV6_SEGS, RWKV_WKV4_STREAM), and rwkv_set_tuning changes them for
- * the whole process.
+ * RWKV_WKV6_SEGS), and rwkv_set_tuning changes them for the whole process.
  * They change the plan and therefore the workspace sizes: query a workspace
  * size under the setting it will be used with (a call whose workspace is too
  * small for the current setting returns RWKV_ERR_WORKSPACE).  Changing a
  * setting while another thread plans a call races with that call's plan.
  * rwkv_set_tuning returns RWKV_ERR_UNSUPPORTED for an unknown key or value.
  * ---------------------------------------------------------------------- */
-#define RWKV_TUNE_WKV4_TILE  1  /* cpl*10000 + L*100 + NW of a compiled RWKV-4 forward tile:
-                                   40808 41604 41608 21608 23204 21604 13208 13204 16401 11604 */
+#define RWKV_TUNE_WKV4_TILE  1  /* [cb*100000 +] cpl*10000 + L*100 + NW of a compiled RWKV-4
+                                   forward shape (cb: channel blocks per workgroup, 1 if absent):
+                                   40808 41604 41608 21608 23204 21604 13208 13204 16401 11604
+                                   213204 413204 */
 #define RWKV_TUNE_WKV4_ORDER 2  /* 1: RWKV-4 tiles claimed in arrival order even where the
                                    whole grid is resident (same results, bit for bit) */
 #define RWKV_TUNE_WKV5_DV    3  /* value columns per Eagle workgroup: 16, 32 or 64 */
 #define RWKV_TUNE_WKV5_SEGS  4  /* Eagle time segments, 1..4096 (each >= 4 chunks) */
 #define RWKV_TUNE_WKV6_DV    5  /* value columns per Finch workgroup: 32 or 64 */
 #define RWKV_TUNE_WKV6_SEGS  6  /* Finch time segments, 1..4096 (each >= 4 chunks) */
-#define RWKV_TUNE_WKV4_STREAM 7 /* RWKV-4 forward over a resident-sized grid that streams its
-                                   tiles (96 tokens): 0 by size, 1 never, 2 always */
 int rwkv_set_tuning(int key, int value);
 int rwkv_get_tuning(int key);
 

@@ -79,7 +79,6 @@ void tuning_from_env() {
   set_tuning(kTuneWkv5Segs, env_int("RWKV_WKV5_SEGS"));
   set_tuning(kTuneWkv6Dv, env_int("RWKV_WKV6_DV"));
   set_tuning(kTuneWkv6Segs, env_int("RWKV_WKV6_SEGS"));
-  set_tuning(kTuneWkv4Stream, env_int("RWKV_WKV4_STREAM"));
 }
 
 }  // namespace
@@ -93,7 +92,6 @@ bool set_tuning(int key, int value) {
     case kTuneWkv6Dv: ok = value == 0 || value == 32 || value == 64; break;
     case kTuneWkv5Segs:
     case kTuneWkv6Segs: ok = value >= 0 && value <= 4096; break;
-    case kTuneWkv4Stream: ok = value >= 0 && value <= 2; break;
     default: ok = false;
   }
   if (ok) g_tune[key].store(value, std::memory_order_relaxed);

@@ -79,10 +79,10 @@ __device__ __forceinline__ void emit_rows(Rsrc ry, uint32_t voff, uint32_t row_b
 
 // NaN over one tile's output rows: the mark of a tile that could not run.
 template <int CPL, int L, int NW>
-__device__ void nan_rows(int tile, int g, int T, int C, int n_cblk, float* __restrict__ y) {
+__device__ void nan_rows(int tile, int g, int wid, int T, int C, int n_cblk,
+                         float* __restrict__ y) {
   constexpr int W = 64 * CPL;
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
   const int bi = g / n_cblk, cb = g - bi * n_cblk;
   const int t0 = tile * L * NW + wid * L;
   const int n = max(0, min(L, T - t0));
@@ -226,8 +226,16 @@ __device__ __forceinline__ void lookback(int tile, int g, int groups,
 // TAPE (with outputs): also publish the mid-tile histories in `mids`, as the
 // prefix pass does, so that a backward over the same inputs can skip that
 // pass (a forward for training).
-template <int CPL, int L, int NW, bool EMIT = true, bool TAPE = false>
-__global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
+//
+// CB > 1: a workgroup covers CB adjacent channel blocks of one sequence
+// (n_cblk % CB == 0), NW waves along time for each; wave i serves block
+// i % CB at time slot i / CB.  Every block keeps its own 128-token tiles,
+// histories and look-back, so the results are those of CB = 1 bit for bit;
+// what changes is the memory pattern: the CB waves of a time slot read
+// adjacent 256-byte pieces of the same rows together.  Tiles are claimed
+// per group of CB blocks.
+template <int CPL, int L, int NW, bool EMIT = true, bool TAPE = false, int CB = 1>
+__global__ __launch_bounds__(64 * NW * CB) void wkv4_fwd_tiled(
     int T, int C, int n_cblk, int groups, int n_tiles, int in_order,
     const float* __restrict__ w, const float* __restrict__ u,
     const float* __restrict__ k, const float* __restrict__ v, float* __restrict__ y,
@@ -238,21 +246,27 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
   constexpr int SLOT = 8 * W;        // words per (tile, block): agg A,B,kr,n then inc A,B,kr,n
   __shared__ int s_tile;
   __shared__ uint32_t s_tag;
-  __shared__ HistLds<W> s_sum[NW];
-  __shared__ HistLds<W> s_pre;
+  __shared__ HistLds<W> s_sums[CB][NW];
+  __shared__ HistLds<W> s_pres[CB];
 
   const int lane = threadIdx.x & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = int(blockIdx.x) % groups;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wid = wave / CB;         // time slot of this wave in the tile
+  const int bo = wave - wid * CB;    // its block within the workgroup's CB blocks
+  const int ngrp = groups / CB;      // groups of CB blocks
+  const int gg = int(blockIdx.x) % ngrp;
+  const int g = gg * CB + bo;
+  HistLds<W>(&s_sum)[NW] = s_sums[bo];
+  HistLds<W>& s_pre = s_pres[bo];
   int tile;
   if (in_order) {
     // The tile is known at once, so the loads need not wait for anything;
     // the tag is read after they are issued (below).
-    tile = int(blockIdx.x) / groups;
+    tile = int(blockIdx.x) / ngrp;
   } else {
     if (threadIdx.x == 0) {
       uint32_t tg;
-      s_tile = claim_tile(hdr, counters, g, n_tiles, groups, tg);
+      s_tile = claim_tile(hdr, counters, gg, n_tiles, ngrp, tg);
       s_tag = tg;
     }
     lds_barrier();
@@ -262,7 +276,7 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
     // names (the caller must not mistake them for results).
     if (tile < 0 || tile >= n_tiles) {
       if (threadIdx.x == 0) raise_error(hdr + kHdrError, kErrNotZeroed);
-      if (EMIT) nan_rows<CPL, L, NW>(int(blockIdx.x) / groups, g, T, C, n_cblk, y);
+      if (EMIT) nan_rows<CPL, L, NW>(int(blockIdx.x) / ngrp, g, wid, T, C, n_cblk, y);
       return;
     }
   }
@@ -432,287 +446,6 @@ __global__ __launch_bounds__(64 * NW) void wkv4_fwd_tiled(
   }
 }
 
-// Items per claim of the streamed forward: a workgroup takes this many
-// consecutive (tile, block) items per atomic, one batch ahead.
-constexpr int kStreamBatch = 2;
-
-// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
-// 6:4, lgkmcnt 11:8; an all-ones field waits for nothing).
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
-
-// The streamed forward, for grids far larger than what the device holds at
-// once.  A resident-sized grid of workgroups works through all items (tile
-// t of channel block g is item t * groups + g) in increasing order:
-//   * one control wave per workgroup claims batches of kStreamBatch
-//     consecutive items from the header's counter {tag, count}, the next
-//     batch while the current one runs; for each item it joins the compute
-//     waves' summaries, publishes the tile's aggregate, resolves the tile
-//     prefix by the look-back and publishes the inclusive history;
-//   * NC compute waves (L tokens each) hold the current item's rows in
-//     registers while the next item's rows stream into shared memory
-//     (buffer loads straight to LDS, 16 KB per wave); at the start of an
-//     item a wave moves them into registers and sends the loads of the item
-//     after it.
-// The control wave issues no row loads, so its polls never wait behind them
-// (a wave's memory operations complete in issue order).  Items are claimed
-// in increasing order by running workgroups and wait only for smaller
-// items, so no grid size or residency can deadlock the launch.  The last
-// workgroup to finish advances the epoch and leaves the counter at
-// {tag + 1, 0} for the next call.  The summaries and prefix in shared memory
-// are double-buffered by item parity, so consecutive items need no barrier
-// between them.
-template <int L, int NC>
-__global__ __launch_bounds__(64 * (NC + 1)) void wkv4_fwd_stream(
-    int T, int C, int n_cblk, int groups, int n_tiles,
-    const float* __restrict__ w, const float* __restrict__ u,
-    const float* __restrict__ k, const float* __restrict__ v, float* __restrict__ y,
-    uint32_t* __restrict__ hdr, uint64_t* __restrict__ slots, StateIO sio) {
-  constexpr int W = 64;
-  constexpr int TILE = L * NC;
-  constexpr int SLOT = 8 * W;
-  constexpr int CTRL = NC;  // index of the control wave
-  typedef __attribute__((address_space(3))) void* LdsPtr;
-  __shared__ uint32_t s_tag;
-  __shared__ int s_batch;
-  __shared__ HistLds<W> s_sum[2][NC];
-  __shared__ HistLds<W> s_pre[2];
-  __shared__ __attribute__((aligned(16))) float s_rows[NC][2][L][W];  // next item's k, v rows
-
-  const int lane = threadIdx.x & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const bool ctrl = wid == CTRL;
-  const bool claimer = ctrl && lane == 0;
-  const int items = n_tiles * groups;
-  uint64_t* ctr = reinterpret_cast<uint64_t*>(hdr + kHdrStream);
-
-  // The claim of the batch ahead: issued with one atomic, its reply read at
-  // the next batch change (claimer lane only).
-  uint64_t pending = 0;
-  auto resolve = [&](uint64_t old, uint32_t tg) -> int {
-    if (uint32_t(old >> 32) != tg) {
-      // Left by an earlier call, or never used: raise to {tag, 0} and claim
-      // again (a later tag cannot appear before this call's last workgroup
-      // has finished).
-      __hip_atomic_fetch_max(ctr, uint64_t(tg) << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      old = __hip_atomic_fetch_add(ctr, uint64_t(kStreamBatch), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (uint32_t(old >> 32) != tg) return -1;
-    return int(min(uint32_t(old), uint32_t(items)));
-  };
-  auto claim_ahead = [&]() {
-    pending = __hip_atomic_fetch_add(ctr, uint64_t(kStreamBatch), __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-  };
-
-  if (claimer) {
-    // The claim must not run before the epoch read has returned: tie the
-    // increment to the loaded value.
-    const uint32_t tg = hdr_load(hdr, kHdrEpoch) + 1u;
-    uint64_t inc = kStreamBatch;
-    asm volatile("" : "+v"(inc) : "v"(tg));
-    const uint64_t old =
-        __hip_atomic_fetch_add(ctr, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int first = resolve(old, tg);
-    s_tag = tg;
-    s_batch = first;
-    if (first >= 0 && first < items) claim_ahead();
-  }
-  lds_barrier();
-  const uint32_t tag = __builtin_amdgcn_readfirstlane(s_tag);
-  int item = __builtin_amdgcn_readfirstlane(s_batch);
-  if (item < 0) {
-    // A workspace that was never zero-filled: flag it, write NaN over the
-    // rows of the items this workgroup's launch index names, touch nothing.
-    if (claimer) raise_error(hdr + kHdrError, kErrNotZeroed);
-    if (!ctrl)
-      for (int it = int(blockIdx.x); it < items; it += int(gridDim.x))
-        nan_rows<1, L, NC>(it / groups, it % groups, T, C, n_cblk, y);
-    item = items;
-  }
-  int batch_end = min(item + kStreamBatch, items);
-
-  // The item after `it`: the next one of its batch, else the batch claimed
-  // ahead (whose successor is then claimed).  Uniform over the workgroup.
-  auto next_item = [&](int it) -> int {
-    if (it + 1 < batch_end) return it + 1;
-    if (claimer) {
-      const int nb = resolve(pending, tag);
-      s_batch = nb < 0 ? items : nb;
-      if (nb >= 0 && nb < items) claim_ahead();
-    }
-    lds_barrier();
-    const int nb = __builtin_amdgcn_readfirstlane(s_batch);
-    batch_end = min(nb + kStreamBatch, items);
-    return nb;
-  };
-
-  // Where this compute wave's rows of an item live.
-  struct Rows {
-    int n;       // tokens of this wave in the tile
-    int col;     // this lane's column in the block (clamped into range for loads)
-    int cl;      // its channel, cb * W + col
-    bool valid;  // the lane has a channel
-    size_t row0;
-  };
-  auto rows_of = [&](int it) -> Rows {
-    const int tile = it / groups, g = it - (it / groups) * groups;
-    const int bi = g / n_cblk, cb = g - (g / n_cblk) * n_cblk;
-    Rows r;
-    const int t0 = tile * TILE + wid * L;
-    r.n = ctrl ? 0 : max(0, min(L, T - t0));
-    r.valid = cb * W + lane < C;
-    r.col = r.valid ? lane : C - cb * W - 1;
-    r.cl = cb * W + r.col;
-    r.row0 = (size_t(bi) * size_t(T) + size_t(t0)) * size_t(C) + size_t(cb) * W;
-    return r;
-  };
-  const uint32_t row_bytes = uint32_t(C) * 4u;
-  const uint32_t span = uint32_t(L - 1) * row_bytes + uint32_t(W) * 4u;
-  // Sends the loads of an item's rows into this wave's shared rows (lane i
-  // fills word i of a row); w, u of the lane's channel go to registers.
-  // Returns the number of rows sent.
-  auto send = [&](int it, float& wv, float& uv) -> int {
-    const Rows r = rows_of(it);
-    wv = r.n > 0 ? w[r.cl] : 0.f;
-    uv = r.n > 0 ? u[r.cl] : 0.f;
-    const Rsrc rk = make_rsrc(k + r.row0, span);
-    const Rsrc rv = make_rsrc(v + r.row0, span);
-    const uint32_t voff = uint32_t(r.col) * 4u;
-    for (int s = 0; s < r.n; ++s) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LdsPtr)&s_rows[wid][0][s][0], 4, voff,
-                                               uint32_t(s) * row_bytes, 0, kNonTemporal);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LdsPtr)&s_rows[wid][1][s][0], 4, voff,
-                                               uint32_t(s) * row_bytes, 0, kNonTemporal);
-    }
-    return r.n;
-  };
-
-  float kk[L][1], vv[L][1];
-  float wv = 0.f, uv = 0.f;
-  // Memory operations this wave issued after its last row loads (the y
-  // stores of an item): the wait for the rows allows that many to remain.
-  int stores_after = 0;
-  if (!ctrl) send(item < items ? item : items, wv, uv);
-  int parity = 0;
-  while (item < items) {
-    const int nxt = next_item(item);
-    const int tile = item / groups, g = item - (item / groups) * groups;
-    const int bi = g / n_cblk, cb = g - (g / n_cblk) * n_cblk;
-    const Rows r = rows_of(item);
-    float w2 = 0.f, u2 = 0.f;
-    if (!ctrl) {
-      // This item's rows are in shared memory once the loads sent before the
-      // last item's stores are done.  (The compiler does not track loads
-      // that write shared memory: the waits are explicit.)
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
-      if (stores_after == L)
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(L));
-      else
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-      __builtin_amdgcn_sched_barrier(0);
-      asm volatile("" ::: "memory");
-#pragma unroll
-      for (int s = 0; s < L; ++s) {
-        kk[s][0] = s < r.n ? s_rows[wid][0][s][lane] * kLog2e : 0.f;
-        vv[s][0] = s < r.n ? s_rows[wid][1][s][lane] : 0.f;
-      }
-      w2 = wv * kLog2e;
-      u2 = uv * kLog2e;
-      // The shared rows are read before the next item's loads overwrite them.
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      __builtin_amdgcn_sched_barrier(0);
-      asm volatile("" ::: "memory");
-      send(nxt, wv, uv);  // no loads past the last item
-      stores_after = 0;
-      __builtin_amdgcn_s_setprio(2);
-      s_sum[parity][wid].put(lane, summarize<L, 1, false>(kk, vv, 0, r.n, w2));
-      __builtin_amdgcn_s_setprio(0);
-    }
-    // Control wave: while the compute waves summarise, its first look-back
-    // poll goes out; once the summaries are in it publishes the tile's
-    // aggregate at once (later tiles fold it without waiting for this
-    // tile's prefix), then resolves the prefix and publishes the inclusive
-    // history.
-    float w2c[1] = {0.f};
-    uint64_t e_inc = 0, e_agg = 0;
-    if (ctrl) {
-      w2c[0] = w[r.cl] * kLog2e;
-      if (tile > 0 && lane < kWin && tile - 1 - lane >= 0) {
-        const uint64_t* sp = slots + (size_t(tile - 1 - lane) * groups + g) * SLOT;
-        e_inc = tagged_load(sp + 4 * W);
-        if (tile - 1 - lane > 0) e_agg = tagged_load(sp);  // tile 0 has no aggregate
-      }
-    }
-    lds_barrier();  // the summaries are in
-    if (ctrl) {
-      __builtin_amdgcn_s_setprio(3);
-      const int tile_t0 = tile * TILE;
-      const int tile_n = min(TILE, T - tile_t0);
-      Hist agg = s_sum[parity][0].get(lane);
-      for (int i = 1; i < NC; ++i) {
-        const int ni = max(0, min(L, T - (tile_t0 + i * L)));
-        agg = hist_concat(agg, s_sum[parity][i].get(lane), float(ni), w2c[0]);
-      }
-      uint64_t* mine = slots + (size_t(tile) * groups + g) * SLOT + lane;
-      auto publish = [&](int kind, const Hist& h) {
-        uint64_t* q = mine + kind * 4 * W;
-        tagged_store(q + 0 * W, h.A, tag);
-        tagged_store(q + 1 * W, h.Bd, tag);
-        tagged_store(q + 2 * W, h.kr, tag);
-        tagged_store(q + 3 * W, h.n, tag);
-      };
-      Hist pre[1];
-      if (tile == 0) {
-        // History before the first token: empty, or the caller's state.
-        pre[0] = hist_empty();
-        if (sio.a_in) {
-          const size_t si = size_t(bi) * C + r.cl;
-          pre[0] = Hist{sio.a_in[si], sio.b_in[si], sio.p_in[si] * kLog2e, 0.f};
-        }
-      } else {
-        publish(0, agg);
-        lookback<1, TILE>(tile, g, groups, slots, hdr, tag, w2c, true, e_inc, e_agg, pre);
-      }
-      const Hist inc = hist_concat(pre[0], agg, float(tile_n), w2c[0]);
-      publish(1, inc);
-      if (tile == n_tiles - 1) {
-        const Hist fin[1] = {inc};
-        write_state(sio, fin, w2c, r.valid, size_t(bi) * C + size_t(cb) * W + lane);
-      }
-      s_pre[parity].put(lane, pre[0]);
-      __builtin_amdgcn_s_setprio(0);
-    }
-    lds_barrier();  // the prefix is in
-    if (!ctrl && r.n > 0) {
-      const float w2a[1] = {w2}, u2a[1] = {u2};
-      Hist hs[1] = {s_pre[parity].get(lane)};
-      for (int i = 0; i < wid; ++i)
-        hs[0] = hist_concat(hs[0], s_sum[parity][i].get(lane), float(L), w2);
-      // A partial wave runs the blocked pass over its zero rows too (they
-      // come after its real tokens, so no real output depends on them); the
-      // resource ends at its last real row, so their stores are dropped.
-      const Rsrc ry = make_rsrc(y + r.row0, uint32_t(r.n - 1) * row_bytes + uint32_t(W) * 4u);
-      const uint32_t voff_out = r.valid ? uint32_t(lane) * 4u : kDropOffset;
-      emit_rows_blocked<L, 1>(ry, voff_out, row_bytes, hs, kk, vv, u2a, w2a);
-      stores_after = L;
-    }
-    parity ^= 1;
-    item = nxt;
-  }
-  // Every workgroup of this call has read the epoch and stopped claiming
-  // once the last one is here: it leaves the header for the next call.
-  if (claimer && hdr_add(hdr, kHdrClaimed, 1u) == gridDim.x - 1u) {
-    hdr_store(hdr, kHdrClaimed, 0u);
-    __hip_atomic_store(ctr, uint64_t(tag + 1u) << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    hdr_store(hdr, kHdrEpoch, tag);
-  }
-}
-
 // One thread per 4 consecutive channels of one stream: the step is
 // elementwise, 36 bytes of traffic per element.  The state stays on the
 // default cache policy (the next step reads it again); this token's k, v and
@@ -785,13 +518,14 @@ __global__ __launch_bounds__(256) void wkv4_state_fill(size_t n, float* __restri
 }
 
 struct Variant {
-  int cpl, L, NW;
+  int cpl, L, NW, cb;
+  constexpr int code() const { return (cb > 1 ? cb * 100000 : 0) + cpl * 10000 + L * 100 + NW; }
 };
 // Instantiated tile shapes: channels per lane, tokens per wave, waves per
-// workgroup.
-constexpr Variant kVariants[] = {{4, 8, 8}, {4, 16, 4}, {4, 16, 8},
-                                 {2, 16, 8}, {2, 32, 4}, {2, 16, 4},
-                                 {1, 32, 8}, {1, 32, 4}, {1, 64, 1}, {1, 16, 4}};
+// block and tile, channel blocks per workgroup.
+constexpr Variant kVariants[] = {{4, 8, 8, 1},  {4, 16, 4, 1}, {4, 16, 8, 1}, {2, 16, 8, 1},
+                                 {2, 32, 4, 1}, {2, 16, 4, 1}, {1, 32, 8, 1}, {1, 32, 4, 1},
+                                 {1, 64, 1, 1}, {1, 16, 4, 1}, {1, 32, 4, 2}, {1, 32, 4, 4}};
 
 // Workgroups of `kern` (`block` threads, no dynamic LDS) that the current
 // device holds at once, cached per device; 0 if it cannot be determined, or
@@ -831,7 +565,7 @@ int64_t device_capacity(const void* kern, int block) {
   return 0;
 }
 
-template <int CPL, int L, int NW>
+template <int CPL, int L, int NW, int CB = 1>
 hipError_t launch_tiled(const Wkv4Plan& pl, int64_t T, int64_t C, const float* w,
                         const float* u, const float* k, const float* v, float* y, void* ws,
                         const StateIO& sio, hipStream_t stream) {
@@ -839,48 +573,24 @@ hipError_t launch_tiled(const Wkv4Plan& pl, int64_t T, int64_t C, const float* w
   uint32_t* hdr = reinterpret_cast<uint32_t*>(base);
   uint64_t* counters = reinterpret_cast<uint64_t*>(base + kWkv4HeaderBytes);
   uint64_t* slots = reinterpret_cast<uint64_t*>(base + pl.slots_offset);
-  const int64_t grid = pl.n_tiles * pl.groups;
-  const void* kern = reinterpret_cast<const void*>(&wkv4_fwd_tiled<CPL, L, NW>);
-  const int in_order = grid <= resident_workgroups(kern, 64 * NW) ? 1 : 0;
-  hipLaunchKernelGGL((wkv4_fwd_tiled<CPL, L, NW>), dim3(unsigned(grid)), dim3(64 * NW), 0,
-                     stream, int(T), int(C), int(pl.n_cblk), int(pl.groups), int(pl.n_tiles),
-                     in_order, w, u, k, v, y, hdr, counters, slots, sio, nullptr);
+  const int64_t grid = pl.n_tiles * pl.groups / CB;
+  const void* kern = reinterpret_cast<const void*>(&wkv4_fwd_tiled<CPL, L, NW, true, false, CB>);
+  const int in_order = grid <= resident_workgroups(kern, 64 * NW * CB) ? 1 : 0;
+  hipLaunchKernelGGL((wkv4_fwd_tiled<CPL, L, NW, true, false, CB>), dim3(unsigned(grid)),
+                     dim3(64 * NW * CB), 0, stream, int(T), int(C), int(pl.n_cblk), int(pl.groups),
+                     int(pl.n_tiles), in_order, w, u, k, v, y, hdr, counters, slots, sio, nullptr);
   return hipGetLastError();
 }
 
-// The streamed forward: 32 tokens x 4 compute waves per tile (the tiles of
-// the other forwards) and a control wave; the grid is what the device holds
-// at once, no larger than the number of batches.
-constexpr int kStreamL = 32;
-constexpr int kStreamNC = 4;
-
-hipError_t launch_stream(const Wkv4Plan& pl, int64_t T, int64_t C, const float* w,
-                         const float* u, const float* k, const float* v, float* y, void* ws,
-                         const StateIO& sio, hipStream_t stream) {
-  char* base = static_cast<char*>(ws);
-  uint32_t* hdr = reinterpret_cast<uint32_t*>(base);
-  uint64_t* slots = reinterpret_cast<uint64_t*>(base + pl.slots_offset);
-  constexpr int kThreads = 64 * (kStreamNC + 1);
-  const void* kern = reinterpret_cast<const void*>(&wkv4_fwd_stream<kStreamL, kStreamNC>);
-  int64_t grid = device_capacity(kern, kThreads);
-  if (grid <= 0) grid = 512;
-  const int64_t batches = (pl.n_tiles * pl.groups + kStreamBatch - 1) / kStreamBatch;
-  grid = grid < batches ? grid : batches;
-  hipLaunchKernelGGL((wkv4_fwd_stream<kStreamL, kStreamNC>), dim3(unsigned(grid)), dim3(kThreads),
-                     0, stream, int(T), int(C), int(pl.n_cblk), int(pl.groups), int(pl.n_tiles), w,
-                     u, k, v, y, hdr, slots, sio);
-  return hipGetLastError();
-}
-
-// Items (128-token tiles x channel blocks) from which the plan streams: far
-// more than the 1024 workgroups of 128-token tiles the device holds at once.
-constexpr int64_t kStreamMinItems = 8192;
+// Tiles (128 tokens x 64 channels) from which the plan groups channel
+// blocks: far more than the ~1000 such workgroups the device holds at once.
+constexpr int64_t kGroupedMinTiles = 8192;
 
 }  // namespace
 
 bool wkv4_plan_fixed(int64_t B, int64_t T, int64_t C, int cpl, int L, int NW, Wkv4Plan* plan) {
   Wkv4Plan p;
-  p.stream = 0;
+  p.cb = 1;
   p.cpl = cpl;
   p.L = L;
   p.NW = NW;
@@ -906,36 +616,39 @@ bool wkv4_plan(int64_t B, int64_t T, int64_t C, Wkv4Plan* plan) {
   // One channel per lane, 32 tokens per wave, 4 waves per tile: about 116
   // VGPRs (4 waves per SIMD).  Measured faster than wider vector loads with
   // several channels per lane, which lengthen each lane's serial scan.
-  int cpl = 1, L = 32, NW = 4;
+  int cpl = 1, L = 32, NW = 4, cb = 1;
   if (T <= 64) {
     L = 64;
     NW = 1;
   }
-  // An override applies where its channel width divides C.
+  // Grids far beyond what the device holds at once (B=1 T=65536 C=5120:
+  // 40,960 tiles) group two adjacent channel blocks per workgroup: the rows
+  // then come in 512-byte pieces, which HBM serves faster (B=1 T=65536
+  // C=5120: 748 -> 718 us; a copy through the same pattern 703 -> 674 us).
+  // Grids the device holds at once run faster with one block per workgroup
+  // (8x1024x768: 16.1 against 17.4 us).
+  const int64_t n_cblk = (C + 63) / 64;
+  if (L == 32 && n_cblk % 2 == 0 && B * n_cblk * ((T + 127) / 128) >= kGroupedMinTiles) cb = 2;
+  // An override applies where its channel width divides C and its channel
+  // blocks per workgroup divide the blocks of a sequence.
   if (const int code = tuning(kTuneWkv4Tile)) {
     for (const Variant& vv : kVariants)
-      if (vv.cpl * 10000 + vv.L * 100 + vv.NW == code && C % vv.cpl == 0) {
+      if (vv.code() == code && C % vv.cpl == 0 &&
+          ((C + 64 * vv.cpl - 1) / (64 * vv.cpl)) % vv.cb == 0) {
         cpl = vv.cpl;
         L = vv.L;
         NW = vv.NW;
+        cb = vv.cb;
       }
   }
-  // Grids far beyond what the device holds at once stream their tiles
-  // through a resident-sized grid (B=1 T=65536 C=5120: 40,960 tiles).
-  const int st = tuning(kTuneWkv4Stream);
-  const int64_t items128 = B * ((T + 127) / 128) * ((C + 63) / 64);
-  if (st == 2 || (st == 0 && tuning(kTuneWkv4Tile) == 0 && items128 >= kStreamMinItems)) {
-    if (!wkv4_plan_fixed(B, T, C, 1, kStreamL, kStreamNC, plan)) return false;
-    plan->stream = 1;
-    plan->NW = kStreamNC + 1;
-    return true;
-  }
-  return wkv4_plan_fixed(B, T, C, cpl, L, NW, plan);
+  if (!wkv4_plan_fixed(B, T, C, cpl, L, NW, plan)) return false;
+  plan->cb = cb;
+  return true;
 }
 
 bool wkv4_variant_exists(int code) {
   for (const Variant& vv : kVariants)
-    if (vv.cpl * 10000 + vv.L * 100 + vv.NW == code) return true;
+    if (vv.code() == code) return true;
   return false;
 }
 
@@ -984,8 +697,9 @@ hipError_t wkv4_forward_launch(const Wkv4Plan& pl, int64_t B, int64_t T, int64_t
                                float* b_out, float* p_out, hipStream_t stream) {
   (void)B;
   const StateIO sio{a_in, b_in, p_in, a_out, b_out, p_out};
-  if (pl.stream) return launch_stream(pl, T, C, w, u, k, v, y, ws, sio, stream);
-  switch (pl.cpl * 10000 + pl.L * 100 + pl.NW) {
+  switch ((pl.cb > 1 ? pl.cb * 100000 : 0) + pl.cpl * 10000 + pl.L * 100 + pl.NW) {
+    case 213204: return launch_tiled<1, 32, 4, 2>(pl, T, C, w, u, k, v, y, ws, sio, stream);
+    case 413204: return launch_tiled<1, 32, 4, 4>(pl, T, C, w, u, k, v, y, ws, sio, stream);
     case 40808: return launch_tiled<4, 8, 8>(pl, T, C, w, u, k, v, y, ws, sio, stream);
     case 41604: return launch_tiled<4, 16, 4>(pl, T, C, w, u, k, v, y, ws, sio, stream);
     case 41608: return launch_tiled<4, 16, 8>(pl, T, C, w, u, k, v, y, ws, sio, stream);

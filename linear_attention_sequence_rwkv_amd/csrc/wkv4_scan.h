@@ -21,9 +21,7 @@ __device__ __forceinline__ void raise_error(uint32_t* err, uint32_t bit) {
 }
 
 // Header words (uint32) at the start of a scan workspace.
-// kHdrStream: a 64-bit {tag, count} item counter of the streamed forward
-// (words 4 and 5, 8-byte aligned).
-enum : int { kHdrError = 0, kHdrEpoch = 1, kHdrClaimed = 2, kHdrStream = 4 };
+enum : int { kHdrError = 0, kHdrEpoch = 1, kHdrClaimed = 2 };
 // Bits of the error word (sticky until the workspace is zero-filled again).
 constexpr uint32_t kErrGaveUp = 1u;     // a look-back exceeded its spin limit
 constexpr uint32_t kErrNotZeroed = 2u;  // a claim found a workspace never zero-filled

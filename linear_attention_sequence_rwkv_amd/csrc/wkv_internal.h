@@ -15,18 +15,17 @@ namespace rwkv {
 // rwkv_set_tuning changes them.  They select other tile shapes, value slices
 // and time segments, and so change the workspace sizes.
 enum TuneKey : int {
-  kTuneWkv4Tile = 1,   // cpl * 10000 + L * 100 + NW of a compiled forward tile shape
+  kTuneWkv4Tile = 1,   // [cb * 100000 +] cpl * 10000 + L * 100 + NW of a compiled forward shape
   kTuneWkv4Order = 2,  // 1: claimed tiles even where the grid is resident
   kTuneWkv5Dv = 3,     // value columns per Eagle workgroup: 16, 32 or 64
   kTuneWkv5Segs = 4,   // Eagle time segments (before the clamp to >= 4 chunks each)
   kTuneWkv6Dv = 5,     // value columns per Finch workgroup: 32 or 64
   kTuneWkv6Segs = 6,   // Finch time segments
-  kTuneWkv4Stream = 7, // RWKV-4 streamed forward: 0 by size, 1 never, 2 always
-  kTuneKeys = 8
+  kTuneKeys = 7
 };
 int tuning(int key);
 bool set_tuning(int key, int value);
-// Whether the forward has a compiled tile shape with this code (cpl*10000 + L*100 + NW).
+// Whether the forward has a compiled tile shape with this code.
 bool wkv4_variant_exists(int code);
 
 // Longest sequence of one RWKV-4 call: decay counts are held as floats,
@@ -43,11 +42,11 @@ constexpr int64_t kWkv4MaxT = (int64_t(1) << 24) - 64;
 // (tile, block) two published histories (aggregate, inclusive) of 4 tagged
 // 64-bit words per channel each.
 struct Wkv4Plan {
-  int stream;    // 1: the streamed forward (NW - 1 compute waves and a control wave)
+  int cb;        // channel blocks per workgroup (each with its own tiles)
   int cpl;       // channels per lane (vector width of the loads)
   int L;         // tokens per wave
   int NW;        // waves per workgroup
-  int64_t tile;  // L * NW (streamed: L * (NW - 1))
+  int64_t tile;  // L * NW
   int64_t n_tiles;
   int64_t n_cblk;  // ceil(C / (64 * cpl))
   int64_t groups;  // B * n_cblk

@@ -270,19 +270,18 @@ def test_wkv6_rejections(lib):
 def test_tuning_overrides(lib):
     """Plan overrides: unknown keys and values are rejected, accepted ones are
     read back, and they change the plan (hence the workspace sizes)."""
-    keys = (1, 2, 3, 4, 5, 6, 7)
+    keys = (1, 2, 3, 4, 5, 6)
     old = {k: lib.rwkv_get_tuning(k) for k in keys}
     try:
         assert lib.rwkv_set_tuning(0, 1) == UNSUPPORTED
-        assert lib.rwkv_set_tuning(8, 1) == UNSUPPORTED
-        assert lib.rwkv_set_tuning(7, 3) == UNSUPPORTED
+        assert lib.rwkv_set_tuning(7, 1) == UNSUPPORTED
         assert lib.rwkv_set_tuning(1, 13205) == UNSUPPORTED   # no such tile shape
         assert lib.rwkv_set_tuning(1, 1) == UNSUPPORTED       # cpl 0: once a SIGFPE
         assert lib.rwkv_set_tuning(2, 2) == UNSUPPORTED
         assert lib.rwkv_set_tuning(3, 48) == UNSUPPORTED
         assert lib.rwkv_set_tuning(5, 16) == UNSUPPORTED
         assert lib.rwkv_set_tuning(4, -1) == UNSUPPORTED
-        for key, val in ((1, 40808), (2, 1), (3, 16), (4, 2), (5, 32), (6, 3), (7, 2)):
+        for key, val in ((1, 40808), (2, 1), (3, 16), (4, 2), (5, 32), (6, 3)):
             assert lib.rwkv_set_tuning(key, val) == OK
             assert lib.rwkv_get_tuning(key) == val
         # the Eagle workspace holds one state per head and earlier segment
@@ -290,13 +289,6 @@ def test_tuning_overrides(lib):
         assert lib.rwkv_wkv5_forward_workspace(4, 4096, 32, 64) == 0
         assert lib.rwkv_set_tuning(4, 4) == OK
         assert lib.rwkv_wkv5_forward_workspace(4, 4096, 32, 64) == 4 * 32 * 3 * 64 * 64 * 4
-        # the streamed forward keeps 128-token tiles: the same workspace
-        assert lib.rwkv_set_tuning(7, 2) == OK
-        assert lib.rwkv_set_tuning(1, 0) == OK
-        s_need = lib.rwkv_wkv4_forward_workspace(2, 1000, 300)
-        assert lib.rwkv_set_tuning(7, 1) == OK
-        assert lib.rwkv_wkv4_forward_workspace(2, 1000, 300) == s_need
-        assert lib.rwkv_set_tuning(1, 40808) == OK
         # a 4-channel tile shape does not apply where 4 does not divide C
         a = lib.rwkv_wkv4_forward_workspace(1, 1000, 66)
         assert lib.rwkv_set_tuning(1, 0) == OK

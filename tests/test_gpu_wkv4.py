@@ -16,16 +16,12 @@ from wkv_testutil import WKV4_TOL, log, to_dev, torch_dev, tuned, wkv4_scaled_er
 
 pytestmark = pytest.mark.gpu
 
-# "stream": the streamed forward (a resident-sized grid that claims tiles in
-# batches and loads the next tile's rows while it works on the current one)
 TILE_VARIANTS = ["4,8,8", "4,16,4", "4,16,8", "2,16,8", "2,32,4", "2,16,4", "1,32,8",
-                 "1,32,4", "1,64,1", "1,16,4", "stream"]
+                 "1,32,4", "1,64,1", "1,16,4", "1,32,4,2", "1,32,4,4"]
 
 
 def _tile_settings(tile):
-    if tile == "stream":
-        return {"wkv4_stream": True}
-    return {"wkv4_tile": tile, "wkv4_stream": None if tile is None else False}
+    return {"wkv4_tile": tile}
 
 
 def gpu_forward(inp, tile=None):
@@ -377,7 +373,7 @@ def _with_tile(tile, fn):
         return fn()
 
 
-@pytest.mark.parametrize("tile", [None, "4,8,8", "2,16,4", "1,64,1", "stream"])
+@pytest.mark.parametrize("tile", [None, "4,8,8", "2,16,4", "1,64,1", "1,32,4,2"])
 @pytest.mark.parametrize("cut", [(500, 7, 333), (40, 0, 1), (1, 3, 1000), (256, 1, 64)])
 def test_forward_state_chain_matches_whole_sequence(cut, tile):
     """forward(T1) -> N steps -> forward(T2), the state handed on each time
@@ -458,119 +454,33 @@ def test_forward_is_deterministic(cfg_name):
         assert torch.equal(y0, y1)
 
 
-# ------------------------------------------------------- streamed forward ---
-
-@pytest.mark.parametrize("shape", [(8, 1024, 768), (3, 1100, 200), (1, 4096, 5120),
-                                   (2, 256, 64)])
-def test_streamed_tiles_give_the_same_bits(shape):
-    """The streamed forward works on the same 128-token tiles as the default
-    launch-order and claimed forwards and folds the same histories in the
-    same chain order, so outputs and final state agree bit for bit with both
-    (a wave with fewer than 32 tokens, at a ragged end, runs the blocked
-    output pass over its zero rows where the others take the exact update:
-    its outputs are compared with the oracle instead)."""
+@pytest.mark.parametrize("shape", [(8, 1024, 768), (3, 1100, 256), (1, 65536, 5120)])
+def test_channel_block_groups_give_the_same_bits(shape):
+    """Workgroups of 2 or 4 adjacent channel blocks keep every block's own
+    128-token tiles, histories and look-back: outputs and final states equal
+    those of one block per workgroup bit for bit, in launch order and with
+    claimed tiles, on one shared workspace."""
     torch, dev = torch_dev()
     B, T, C = shape
-    inp = synth.wkv4_inputs(B, T, C, seed=31 + T)
-    g = np.random.default_rng(6)
+    inp = synth.wkv4_inputs(B, T, C, seed=51 + T, omega_lo=-5.0, omega_hi=2.0, u_std=1.0,
+                            k_std=3.0)
+    g = np.random.default_rng(9)
     st = [torch.from_numpy(x.astype(np.float32)).to(dev)
           for x in (g.random((B, C)), g.random((B, C)) + 0.5, g.normal(size=(B, C)))]
     t = {n: torch.from_numpy(inp[n]).to(dev) for n in ("w", "u", "k", "v")}
+    ws = torch.zeros(rw.rwkv_wkv4_forward_workspace(B, T, C), dtype=torch.uint8, device=dev)
     outs = {}
-    for mode, kw in (("launch", {"wkv4_stream": False}),
-                     ("claim", {"wkv4_stream": False, "wkv4_claim": True}),
-                     ("stream", {"wkv4_stream": True})):
-        log(f"wkv4_forward {B}x{T}x{C}: {mode}, bitwise")
-        with tuned(**kw):
-            y = rw.rwkv_wkv4_forward(t["w"], t["u"], t["k"], t["v"])
-            y2, (a2, b2, p2) = rw.rwkv_wkv4_forward_state(t["w"], t["u"], t["k"], t["v"],
-                                                         state_in=tuple(st), state_out=True)
-            torch.cuda.synchronize()
-        outs[mode] = [x.cpu().numpy() for x in (y, y2, a2, b2, p2)]
-    full = T // 32 * 32
-    for mode in ("claim", "stream"):
-        for i, (x, z) in enumerate(zip(outs["launch"], outs[mode])):
-            if i < 2:
-                assert np.array_equal(x[:, :full], z[:, :full]), (mode, i)
-            else:
-                assert np.array_equal(x, z), (mode, i)
-    y_ref, S = oracle_forward(inp)
-    assert wkv4_scaled_err(outs["stream"][0], y_ref, S) <= WKV4_TOL
-
-
-def test_streamed_long_workload_matches_claimed_tiles():
-    """B=1 T=65536 C=5120 (40,960 tiles, streamed by default) bit for bit
-    equal to the same forward with claimed tiles; the workspace's error
-    word stays clear."""
-    torch, dev = torch_dev()
-    cfg = synth.CFG_WKV4_LONG
-    log(f"wkv4_forward {cfg.name}: streamed vs claimed tiles, bitwise")
-    inp = synth.wkv4_inputs_for(cfg)
-    w, u, k, v = (to_dev(inp[n]) for n in ("w", "u", "k", "v"))
-    ws = torch.zeros(rw.rwkv_wkv4_forward_workspace(cfg.B, cfg.T, cfg.C), dtype=torch.uint8,
-                     device=dev)
-    y_s = rw.rwkv_wkv4_forward(w, u, k, v, ws=ws)
-    with tuned(wkv4_stream=False):
-        y_c = rw.rwkv_wkv4_forward(w, u, k, v, ws=ws)
-    y_s2 = rw.rwkv_wkv4_forward(w, u, k, v, ws=ws)
-    torch.cuda.synchronize()
-    assert torch.equal(y_s, y_c)
-    assert torch.equal(y_s, y_s2)
+    for tile in ("1,32,4", "1,32,4,2", "1,32,4,4"):
+        for claim in (False, True):
+            log(f"wkv4_forward {B}x{T}x{C} tile {tile} claim={claim}, bitwise")
+            with tuned(wkv4_tile=tile, wkv4_claim=claim):
+                y = rw.rwkv_wkv4_forward(t["w"], t["u"], t["k"], t["v"], ws=ws)
+                y2, (a2, b2, p2) = rw.rwkv_wkv4_forward_state(
+                    t["w"], t["u"], t["k"], t["v"], state_in=tuple(st), state_out=True, ws=ws)
+                torch.cuda.synchronize()
+            outs[(tile, claim)] = [x.cpu().numpy() for x in (y, y2, a2, b2, p2)]
+    ref = outs[("1,32,4", False)]
+    for key, got in outs.items():
+        for i, (x, z) in enumerate(zip(ref, got)):
+            assert np.array_equal(x, z), (key, i)
     assert rw.rwkv_wkv4_workspace_error(ws) == 0
-
-
-def test_streamed_and_tiled_calls_share_a_workspace():
-    """Streamed, launch-order and claimed calls of several shapes alternate
-    on one workspace: each advances the same epoch, and the streamed call's
-    counter is left ready for the next streamed call."""
-    torch, dev = torch_dev()
-    shapes = [(2, 900, 96), (4, 4096, 1536), (1, 300, 64)]
-    modes = [{"wkv4_stream": True}, {"wkv4_stream": False},
-             {"wkv4_stream": False, "wkv4_claim": True}]
-    cases = [synth.wkv4_inputs(B, T, C, seed=190 + i) for i, (B, T, C) in enumerate(shapes)]
-    refs = [oracle_forward(inp) for inp in cases]
-    need = 0
-    for kw in modes:
-        with tuned(**kw):
-            need = max([need] + [rw.rwkv_wkv4_forward_workspace(*shp) for shp in shapes])
-    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
-    bufs = [{n: to_dev(inp[n]) for n in ("w", "u", "k", "v")} for inp in cases]
-    for rnd in range(3):
-        for j, (shp, bf, (y_ref, S)) in enumerate(zip(shapes, bufs, refs)):
-            kw = modes[(rnd + j) % 3]
-            log(f"wkv4_forward shared workspace round {rnd} shape {shp} {kw}")
-            with tuned(**kw):
-                y = rw.rwkv_wkv4_forward(bf["w"], bf["u"], bf["k"], bf["v"], ws=ws)
-            torch.cuda.synchronize()
-            assert wkv4_scaled_err(y.cpu().numpy(), y_ref, S) <= WKV4_TOL, (rnd, shp, kw)
-    assert rw.rwkv_wkv4_workspace_error(ws) == 0
-
-
-def test_streamed_forward_replayed_from_captured_graph():
-    """The streamed forward's counter and epoch advance on the device, so
-    replays of a captured call stay correct, with eager calls in between."""
-    torch, dev = torch_dev()
-    B, T, C = 2, 2000, 320
-    inps = [synth.wkv4_inputs(B, T, C, seed=260 + i) for i in range(2)]
-    with tuned(wkv4_stream=True):
-        need = rw.rwkv_wkv4_forward_workspace(B, T, C)
-        ws = torch.zeros(need, dtype=torch.uint8, device=dev)
-        bf = {n: to_dev(inps[0][n]) for n in ("w", "u", "k", "v")}
-        y = torch.empty_like(bf["k"])
-        graph = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream(dev)
-        side.wait_stream(torch.cuda.current_stream(dev))
-        with torch.cuda.graph(graph, stream=side):
-            rw.rwkv_wkv4_forward(bf["w"], bf["u"], bf["k"], bf["v"], y=y, ws=ws)
-        torch.cuda.synchronize()
-        for rnd in range(4):
-            inp = inps[rnd % 2]
-            for n in ("w", "u", "k", "v"):
-                bf[n].copy_(to_dev(inp[n]))
-            rw.rwkv_wkv4_forward(bf["w"], bf["u"], bf["k"], bf["v"], ws=ws)
-            torch.cuda.synchronize()
-            log(f"wkv4_forward streamed graph replay {rnd}")
-            graph.replay()
-            torch.cuda.synchronize()
-            y_ref, S = oracle_forward(inp)
-            assert wkv4_scaled_err(y.cpu().numpy(), y_ref, S) <= WKV4_TOL, rnd

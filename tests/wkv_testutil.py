@@ -39,22 +39,23 @@ WKV5_TOL = 2e-2
 
 
 def tile_code(tile):
-    """RWKV_TUNE_WKV4_TILE value of a "cpl,L,NW" tile shape (None: default)."""
+    """RWKV_TUNE_WKV4_TILE value of a "cpl,L,NW" or "cpl,L,NW,CB" shape (CB:
+    channel blocks per workgroup; None: the default plan)."""
     if tile is None:
         return 0
-    c, l, nw = (int(x) for x in tile.split(","))
-    return c * 10000 + l * 100 + nw
+    parts = [int(x) for x in tile.split(",")]
+    c, l, nw = parts[:3]
+    cb = parts[3] if len(parts) > 3 else 1
+    return (cb * 100000 if cb > 1 else 0) + c * 10000 + l * 100 + nw
 
 
 @contextlib.contextmanager
 def tuned(**settings):
     """Plan overrides for a block: wkv4_tile="cpl,L,NW", wkv4_claim=True,
-    wkv4_stream=True/False (always / never the streamed forward), wkv5_dv=,
-    wkv5_segs=, wkv6_dv=, wkv6_segs= (None leaves a key alone)."""
+    wkv5_dv=, wkv5_segs=, wkv6_dv=, wkv6_segs= (None leaves a key alone)."""
     import linear_attention_sequence_rwkv_amd as rw
     keys = {"wkv4_tile": (rw.RWKV_TUNE_WKV4_TILE, tile_code),
             "wkv4_claim": (rw.RWKV_TUNE_WKV4_ORDER, lambda x: 1 if x else 0),
-            "wkv4_stream": (rw.RWKV_TUNE_WKV4_STREAM, lambda x: 2 if x else 1),
             "wkv5_dv": (rw.RWKV_TUNE_WKV5_DV, int),
             "wkv5_segs": (rw.RWKV_TUNE_WKV5_SEGS, int),
             "wkv6_dv": (rw.RWKV_TUNE_WKV6_DV, int),
