@@ -138,6 +138,28 @@ int rwkv_wkv4_forward(int64_t B, int64_t T, int64_t C,
                       void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * RWKV-4 forward that allocates nothing and takes no workspace.  For callers
+ * that cannot allocate or hand over device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Arguments, results (bit for bit) and accuracy as rwkv_wkv4_forward.  The
+ * look-back workspace is a 32 MiB device array inside the library, one per
+ * GPU, held until the process ends: shapes whose
+ * rwkv_wkv4_forward_workspace(B, T, C) exceeds 32 MiB (under the current
+ * plan overrides) return RWKV_ERR_WORKSPACE and enqueue nothing.  The array
+ * is zero-filled by a kernel on `stream` at the first call on each device
+ * (and again every 2^30 calls); it keeps the last call's contents, which the
+ * next call needs no clearing of.  Every call on one GPU shares the array:
+ * calls that overlap in time on that GPU (other streams, other threads)
+ * race and are not allowed.  The array's error word is not exposed; a tile
+ * that cannot run still writes NaN over its rows, as in rwkv_wkv4_forward.
+ * ---------------------------------------------------------------------- */
+int rwkv_wkv4_forward_noalloc(int64_t B, int64_t T, int64_t C,
+                              const float* w, const float* u,
+                              const float* k, const float* v,
+                              float* y, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * RWKV-4 backward: gradients of L = sum_{b,t,c} gy[b,t,c] * y[b,t,c], with y
  * the output of rwkv_wkv4_forward (empty starting history).
  * [RWKV-digest] (2) Time-mixing, WKV_t; the pages give no derivatives.  With

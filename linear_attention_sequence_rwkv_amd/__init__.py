@@ -23,6 +23,7 @@ __all__ = [
     "rwkv_set_tuning", "rwkv_get_tuning", "tuning",
     "rwkv_wkv4_workspace_error",
     "rwkv_wkv4_forward_workspace", "rwkv_wkv4_forward", "rwkv_wkv4_forward_state",
+    "rwkv_wkv4_forward_noalloc",
     "rwkv_wkv4_backward_workspace", "rwkv_wkv4_backward",
     "rwkv_wkv4_forward_train", "rwkv_wkv4_backward_after_forward",
     "rwkv_wkv4_state_init", "rwkv_wkv4_step",
@@ -49,6 +50,7 @@ _SIGNATURES = {
     "rwkv_get_tuning": (ctypes.c_int, [ctypes.c_int]),
     "rwkv_wkv4_workspace_error": (ctypes.c_int, [_p, _sz, _p, _p]),
     "rwkv_wkv4_forward_workspace": (_sz, [_i64, _i64, _i64]),
+    "rwkv_wkv4_forward_noalloc": (ctypes.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p]),
     "rwkv_wkv4_forward": (ctypes.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "rwkv_wkv4_forward_state": (ctypes.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _p,
                                                _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
@@ -322,6 +324,21 @@ def rwkv_wkv4_forward(w, u, k, v, y=None, ws=None, stream=None):
     status = lib.rwkv_wkv4_forward(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
                                    _ptr(ws), nbytes, sh)
     _check("rwkv_wkv4_forward", status)
+    return y
+
+
+def rwkv_wkv4_forward_noalloc(w, u, k, v, y=None, stream=None):
+    """rwkv_wkv4_forward with the library's own workspace (nothing allocated
+    by the library; ``y`` is allocated here if not given)."""
+    lib = load_library()
+    w, u, k, v = _wkv4_inputs(w, u, k, v)
+    B, T, C = k.shape
+    s, sh = _launch_stream(k.device, stream)
+    y = _out("y", y, (B, T, C), k.device, s)
+    _use_on(stream, w, u, k, v, y)
+    status = lib.rwkv_wkv4_forward_noalloc(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(y),
+                                           sh)
+    _check("rwkv_wkv4_forward_noalloc", status)
     return y
 
 

@@ -194,6 +194,24 @@ RWKV_API int rwkv_wkv4_forward_state(int64_t B, int64_t T, int64_t C, const floa
                            ws_bytes, stream);
 }
 
+RWKV_API int rwkv_wkv4_forward_noalloc(int64_t B, int64_t T, int64_t C, const float* w,
+                                       const float* u, const float* k, const float* v, float* y,
+                                       hipStream_t stream) {
+  // Every check of the plain forward; a null workspace stops at the
+  // workspace check (every plan needs one), after all the others.
+  const int st = wkv4_forward_impl(B, T, C, w, u, k, v, y, nullptr, nullptr, nullptr, nullptr,
+                                   nullptr, nullptr, nullptr, 0, stream);
+  if (st != RWKV_ERR_WORKSPACE) return st;
+  rwkv::Wkv4Plan plan;
+  if (!rwkv::wkv4_plan(B, T, C, &plan)) return RWKV_ERR_UNSUPPORTED;
+  if (plan.ws_bytes > rwkv::noalloc_scratch_bytes()) return RWKV_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const hipError_t e = rwkv::noalloc_scratch(&ws, stream);
+  if (e != hipSuccess) return hip_status(e);
+  return wkv4_forward_impl(B, T, C, w, u, k, v, y, nullptr, nullptr, nullptr, nullptr, nullptr,
+                           nullptr, ws, rwkv::noalloc_scratch_bytes(), stream);
+}
+
 RWKV_API int rwkv_wkv4_state_init(int64_t B, int64_t C, float* a, float* b, float* p,
                                   hipStream_t stream) {
   int64_t n;

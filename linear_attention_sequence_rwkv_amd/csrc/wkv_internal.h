@@ -93,6 +93,12 @@ hipError_t wkv4_step_launch(int64_t B, int64_t C, float* a, float* b, float* p,
                             const float* w, const float* u, const float* k,
                             const float* v, float* y, hipStream_t stream);
 
+// The forward's workspace for callers that cannot allocate: a file-scope
+// device array of noalloc_scratch_bytes() per GPU, zero-filled on `stream`
+// at its first use on the current device (and again every 2^30 calls).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** out, hipStream_t stream);
+
 // ----- RWKV-4 backward -----
 //
 // Workspace: the prefix pass's forward workspace (its header and counters

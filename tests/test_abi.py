@@ -44,6 +44,7 @@ def test_header_declares_the_boundary():
         "rwkv_abi_version", "rwkv_status_str", "rwkv_last_hip_error",
         "rwkv_set_tuning", "rwkv_get_tuning", "rwkv_wkv4_workspace_error",
         "rwkv_wkv4_forward_workspace", "rwkv_wkv4_forward", "rwkv_wkv4_forward_state",
+        "rwkv_wkv4_forward_noalloc",
         "rwkv_wkv4_backward_workspace", "rwkv_wkv4_backward",
         "rwkv_wkv4_forward_train", "rwkv_wkv4_backward_after_forward",
         "rwkv_wkv4_state_init", "rwkv_wkv4_step", "rwkv_wkv5_forward_workspace",
@@ -324,4 +325,22 @@ def test_workspace_error_query_rejections(lib):
     assert q(FAKE, 256, NULL, NULL) == NULLPTR
     assert q(FAKE, 3, FAKE, NULL) == WORKSPACE
     assert q(MISALIGNED, 256, FAKE, NULL) == ALIGN
+    assert lib.rwkv_last_hip_error() == 0
+
+
+def test_wkv4_forward_noalloc_rejections(lib):
+    """The no-allocation forward checks what the plain forward checks, and
+    rejects shapes whose workspace exceeds its 32 MiB array, before any HIP
+    call."""
+    _skip_if_gpu()
+    f = lib.rwkv_wkv4_forward_noalloc
+    args = lambda **kw: [kw.get(n, FAKE) for n in ("w", "u", "k", "v", "y")]  # noqa: E731
+    assert f(0, 1024, 768, NULL, NULL, NULL, NULL, NULL, NULL) == OK
+    assert f(-1, 1024, 768, *args(), NULL) == SHAPE
+    for n in ("w", "u", "k", "v", "y"):
+        assert f(8, 1024, 768, *args(**{n: NULL}), NULL) == NULLPTR, n
+        assert f(8, 1024, 768, *args(**{n: MISALIGNED}), NULL) == ALIGN, n
+    assert lib.rwkv_wkv4_forward_workspace(1, 65536, 5120) > 32 << 20
+    assert f(1, 65536, 5120, *args(), NULL) == WORKSPACE
+    assert f(1, (1 << 24) - 63, 64, *args(), NULL) == UNSUPPORTED
     assert lib.rwkv_last_hip_error() == 0
