@@ -207,6 +207,11 @@ def cpu_baseline_wkv4(cfg, inp, channels):
     return {"value": round(12 * elems / el / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
             "sample": (f"fp64 NumPy recurrence on channels 0..{channels - 1} of the "
+                       f"{cfg.name} inputs (all {cfg.C}: the whole workload), full T={cfg.T}: "
+                       f"{el:.1f} s on one core of {_cpu_name()} "
+                       f"({len(os.sched_getaffinity(0))} cores visible)"
+                       if channels == cfg.C else
+                       f"fp64 NumPy recurrence on channels 0..{channels - 1} of the "
                        f"{cfg.name} inputs, full T={cfg.T}: {el:.1f} s on one core of "
                        f"{_cpu_name()} ({len(os.sched_getaffinity(0))} cores visible)"),
             "gelem_per_s": round(elems / el / 1e9, 6)}
@@ -522,7 +527,7 @@ def main(argv=None):
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB three times with torch (a plain copy of known "
                          "size, for scaling the HBM byte counters of a rocprofv3 run)")
-    ap.add_argument("--cpu-channels", type=int, default=2560,
+    ap.add_argument("--cpu-channels", type=int, default=5120,
                     help="channels of the headline workload the oracle sample covers")
     ap.add_argument("--secondary",
                     default="169m,169m-hot,decode,decode-graph,eagle,eagle-decode,finch,"
@@ -555,36 +560,15 @@ def main(argv=None):
         del a, b
         torch.cuda.empty_cache()
 
+    # The headline's inputs are made (host work of several seconds) and put
+    # in device memory first; the secondary workloads run next and the
+    # headline last, so that its W warmup and K timed steps follow busy
+    # seconds of GPU work: after an idle spell the device's clocks take about
+    # 15 ms of load to settle, over which the first launches run up to 5%
+    # slower.
     cfg = synth.CFG_WKV4_LONG
-    log(f"bench: {cfg.name} steps={args.steps} warmup={args.warmup}")
     inp = synth.wkv4_inputs_for(cfg)
     dev_inputs = wkv4_device_copies(torch, inp, rotate=1)
-    ms = bench_wkv4_headline(torch, rw, cfg, dev_inputs, args.steps, args.warmup)
-    del dev_inputs
-    torch.cuda.empty_cache()
-    nbytes = 12 * cfg.B * cfg.T * cfg.C
-    value = nbytes / (ms * 1e-3) / 1e9
-    line = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 6),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "C": cfg.C,
-                   "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
-                   "gelem_per_s": round(cfg.B * cfg.T * cfg.C / (ms * 1e-3) / 1e9, 2),
-                   "bytes_per_elem": 12, "rotated_copies": 1},
-        # one kernel per step, launched back to back: the step time is the
-        # kernel's mean duration plus the sub-microsecond launch gap
-        "roofline": wkv4_roofline(cfg, ms, "wkv4_fwd_tiled_B1_T65536_C5120.md"),
-    }
 
     want = set() if args.no_secondary else {x for x in args.secondary.split(",") if x}
     sec = {}
@@ -620,6 +604,14 @@ def main(argv=None):
                       "graph_GBps": round(r["bytes"] / (r["graph_ms"] * 1e-3) / 1e9, 1),
                       "us_per_step_graph": round(1e3 * r["graph_ms"] / dc.steps, 3)})
         sec[dc.name] = d
+    if "eagle-decode" in want:
+        ed = synth.CFG_WKV5_DECODE
+        log(f"bench: {ed.name}")
+        r = bench_wkv5_decode(torch, rw, ed)
+        sec[ed.name] = {"ms": round(r["ms"], 4),
+                        "us_per_step": round(1e3 * r["ms"] / ed.steps, 3),
+                        "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
+                        "note": "effective bandwidth: the 32 MB state can stay in the MALL"}
     for key, finch in (("eagle", False), ("finch", True)):
         if key not in want:
             continue
@@ -635,7 +627,7 @@ def main(argv=None):
                         "algorithmic_TFLOPs": round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 2),
                         "mfma_busy_pct": read_counter_summary(prof, hsrc, "mfma_busy_pct"),
                         "rotated_copies": r["rotated_copies"]}
-    for key, bc in (("backward", synth.CFG_WKV4_169M), ("backward-long", synth.CFG_WKV4_LONG)):
+    def backward(key, bc):
         if key in want:
             name = bc.name.replace("wkv4_fwd", "wkv4_bwd")
             log(f"bench: {name}")
@@ -644,6 +636,8 @@ def main(argv=None):
                          "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
                          "bytes_per_elem": 20,
                          "gelem_per_s": round(r["elems"] / (r["ms"] * 1e-3) / 1e9, 1)}
+
+    backward("backward", synth.CFG_WKV4_169M)
     if "train" in want:
         tc = synth.CFG_WKV4_169M
         name = tc.name.replace("wkv4_fwd", "wkv4_train_step")
@@ -653,14 +647,36 @@ def main(argv=None):
                      "ms_forward_plus_backward": round(r["ms_separate"], 5),
                      "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
                      "bytes_per_elem": 32}
-    if "eagle-decode" in want:
-        ed = synth.CFG_WKV5_DECODE
-        log(f"bench: {ed.name}")
-        r = bench_wkv5_decode(torch, rw, ed)
-        sec[ed.name] = {"ms": round(r["ms"], 4),
-                        "us_per_step": round(1e3 * r["ms"] / ed.steps, 3),
-                        "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
-                        "note": "effective bandwidth: the 32 MB state can stay in the MALL"}
+    backward("backward-long", synth.CFG_WKV4_LONG)
+
+    log(f"bench: {cfg.name} steps={args.steps} warmup={args.warmup}")
+    ms = bench_wkv4_headline(torch, rw, cfg, dev_inputs, args.steps, args.warmup)
+    del dev_inputs
+    torch.cuda.empty_cache()
+    nbytes = 12 * cfg.B * cfg.T * cfg.C
+    value = nbytes / (ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "C": cfg.C,
+                   "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+                   "gelem_per_s": round(cfg.B * cfg.T * cfg.C / (ms * 1e-3) / 1e9, 2),
+                   "bytes_per_elem": 12, "rotated_copies": 1,
+                   "after_secondary_workloads": bool(sec)},
+        # one kernel per step, launched back to back: the step time is the
+        # kernel's mean duration plus the sub-microsecond launch gap
+        "roofline": wkv4_roofline(cfg, ms, "wkv4_fwd_tiled_B1_T65536_C5120.md"),
+    }
     if sec:
         line["secondary"] = sec
 
