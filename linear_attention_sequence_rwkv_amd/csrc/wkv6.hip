@@ -40,7 +40,8 @@ namespace {
 using namespace eagle;
 
 constexpr int kCPad = 68;                // fp32 row length of the log-decay prefix table (16-byte rows;
-                                         // columns 64..67 hold the prefix's segment totals)
+                                         // columns 64..67 of rows 0..63 hold the prefix's segment
+                                         // totals, of row 64 the per-wave range flags)
 constexpr float kMaxDiagLog2 = 15.f;     // fast diagonal blocks need every |log2 w| <= this
 constexpr float kMinLog2Decay = -126.f;  // log2 w below this counts as this (2^-126: no memory)
 
@@ -77,7 +78,9 @@ struct alignas(16) LdsF {
   float beta[kL];
   float u[kD];  // 16-byte aligned: the members before it are multiples of 16 bytes
 };
-// Two workgroups per CU share its 160 KB of LDS.
+// Two workgroups per CU share its 160 KB of LDS (nothing else of the kernel
+// is in LDS: at 80 KB + 16 B the compiler drops to one workgroup per CU and
+// spends the freed registers).
 static_assert(sizeof(LdsF<64>) <= 80 * 1024, "two Finch workgroups per CU");
 
 // This thread's 16 decay factors (token tid/4, channels 16*(tid%4)..).
@@ -126,7 +129,15 @@ __device__ __forceinline__ bool decay_prefix(const ChunkW& x, CTable& c, DecayTa
     *reinterpret_cast<float4*>(&c[tau + 1][d0 + e]) =
         float4{l2[e], l2[e + 1], l2[e + 2], l2[e + 3]};
   if (tid < kD) c[0][tid] = 0.f;
-  const bool exact = __syncthreads_or(!fast_ok) != 0;
+  // Whether some decay of the chunk is outside the fast range, over the
+  // workgroup: a ballot per wave, kept in the spare cells c[kL][kD + wave]
+  // (row kL's padding columns hold nothing else).  __syncthreads_or would
+  // take 256 more bytes of LDS, past what two Finch workgroups per CU leave.
+  const int wave = tid >> 6;
+  const bool wave_any = __ballot(!fast_ok) != 0;
+  if ((tid & 63) == 0) c[kL][kD + wave] = wave_any ? 1.f : 0.f;
+  __syncthreads();
+  const bool exact = c[kL][kD] + c[kL][kD + 1] + c[kL][kD + 2] + c[kL][kD + 3] != 0.f;
   // per channel: four threads each take 16 rows and scan them in registers,
   // then add the totals of the segments before theirs (kept in the rows'
   // padding columns: segment sg of channel ch at c[ch][kD + sg])
