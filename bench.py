@@ -530,11 +530,11 @@ def main(argv=None):
     ap.add_argument("--cpu-channels", type=int, default=5120,
                     help="channels of the headline workload the oracle sample covers")
     ap.add_argument("--secondary",
-                    default="169m,169m-hot,decode,decode-graph,eagle,eagle-decode,finch,"
-                            "backward,backward-long,train",
+                    default="169m,169m-hot,decode,decode-graph,eagle,eagle-wide,eagle-decode,"
+                            "finch,backward,backward-long,train",
                     help="comma list of secondary workloads: 169m, 169m-hot, decode, "
-                         "decode-graph, eagle, eagle-decode, finch, backward, backward-long, "
-                         "train")
+                         "decode-graph, eagle, eagle-wide, eagle-decode, finch, backward, "
+                         "backward-long, train")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -612,10 +612,11 @@ def main(argv=None):
                         "us_per_step": round(1e3 * r["ms"] / ed.steps, 3),
                         "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
                         "note": "effective bandwidth: the 32 MB state can stay in the MALL"}
-    for key, finch in (("eagle", False), ("finch", True)):
+    for key, mc, finch in (("eagle", synth.CFG_WKV5_EAGLE, False),
+                           ("eagle-wide", synth.CFG_WKV5_EAGLE_WIDE, False),
+                           ("finch", synth.CFG_WKV6_FINCH, True)):
         if key not in want:
             continue
-        mc = synth.CFG_WKV6_FINCH if finch else synth.CFG_WKV5_EAGLE
         log(f"bench: {mc.name}")
         r = bench_matrix_forward(torch, rw, mc, finch)
         hsrc = kernel_source_hash(("wkv6.hip" if finch else "wkv5.hip", "eagle_common.h",

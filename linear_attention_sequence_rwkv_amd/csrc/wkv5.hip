@@ -4,7 +4,8 @@
 // blog), section "Eagle: extending vector memory to matrix memory":
 //   s' = diag(w) s + k^T v,   wkv' = s + diag(u) k^T v,
 // read by the receptance like a query.  Per (batch, head) the state s is
-// D x D (D = 64), indexed [key i][value j]; diag(w) scales key rows.
+// D x D (D = 64), indexed [key i][value j]; diag(w) scales key rows.  The
+// section parameterises the decay as w = exp(-exp(omega)), in (0, 1).
 //
 // Chunked form (chunks of L = 64 tokens; tau, sigma are positions in the
 // chunk, S the state at the chunk start).  Unrolling the recurrence,
@@ -12,16 +13,30 @@
 //         + sum_{sigma<tau} (sum_i r_tau[i] w_i^(tau-1-sigma) k_sigma[i]) v_sigma
 //         + (sum_i r_tau[i] u_i k_tau[i]) v_tau,
 //   S_next = diag(w^L) S + sum_sigma diag(w^(L-1-sigma)) k_sigma^T v_sigma.
-// With rt = r (.) w^(tau-32) and kt = k (.) w^(31-sigma) (per element, a
-// mid-chunk reference keeps both factors within w^(+-32)), the chunk is four
-// dense products on bf16 MFMA with fp32 accumulation:
-//   A  = strict_lower(rt kt^T) + diag(beta)         (64 x 64)
-//   O  = A V + rt (diag(w^32) S)                    (64 x DV per workgroup)
-//   S' = diag(w^32) (diag(w^32) S + kt^T V)         (64 x DV, kept in fp32)
-// since w^(63-sigma) = w^32 w^(31-sigma).
-// The factorisation needs w^(-32) and w^(31) inside bf16/fp32 range, i.e.
-// |log2 w| <= 3.6 for every channel of the head; a head outside that range
-// runs the exact fp32 recurrence instead (one branch per workgroup).
+// Every product runs on bf16 MFMA with fp32 accumulation; S stays fp32.
+// How the decay powers are split between queries and keys depends on the
+// head's fastest decay (one branch per workgroup):
+//
+// * Mid-chunk reference, when every |log2 w| <= 3.6.  With
+//   rt = r (.) w^(tau-32) and kt = k (.) w^(31-sigma), both within w^(+-32),
+//   the chunk is four dense products:
+//     A  = strict_lower(rt kt^T) + diag(beta)         (64 x 64)
+//     O  = A V + rt (diag(w^32) S)                    (64 x DV per workgroup)
+//     S' = diag(w^32) (diag(w^32) S + kt^T V)
+//   since w^(63-sigma) = w^32 w^(31-sigma).
+// * 16-token blocks, for faster decays.  Wave q owns the queries
+//   tau = 16q + p.  A key block nb < q is referred to its end 16nb + 16: keys
+//   k w^(15 - sigma%16), queries r w^p w^(16(q-1-nb)), both factors <= 1.
+//   The diagonal block is referred to its middle, k w^(7 - sigma%16) and
+//   r w^(p-8), within w^(+-8): that needs every |log2 w| <= 15, and a head
+//   with a faster decay sums its diagonal blocks exactly in fp32 instead.
+//   The inter-chunk term uses r w^tau (<= 1) against S itself, the update
+//   k w^(63-sigma) (<= 1).  As w is the same for every token, each of these
+//   factors is fixed per thread.
+// * A head with some w outside [0, 1] (or NaN), outside that
+//   parameterisation, runs the exact fp32 recurrence: one workgroup per
+//   head and value slice over the whole sequence.
+// On the chunked paths a decay below 2^-126 acts as 2^-126.
 #include "eagle_common.h"
 #include "wkv_device.h"
 #include "wkv_internal.h"
@@ -36,21 +51,45 @@ namespace {
 
 using namespace eagle;
 
-// Largest |log2 w| for which w^(-32) and w^31 stay far inside fp32/bf16 range.
-constexpr float kMaxLog2Decay = 3.6f;
+constexpr float kMaxLog2Decay = 3.6f;    // mid-chunk reference: every |log2 w| <= this
+constexpr float kMaxDiagLog2 = 15.f;     // fast diagonal blocks: every |log2 w| <= this
+constexpr float kMinLog2Decay = -126.f;  // log2 w below this counts as this
+
+// A head's path, from its decays (bits, ORed over its channels).
+constexpr int kModeBlocks = 1;     // some |log2 w| > kMaxLog2Decay: 16-token blocks
+constexpr int kModeExactDiag = 2;  // some |log2 w| > kMaxDiagLog2: exact diagonal blocks
+constexpr int kModeRecurrent = 4;  // some w outside [0, 1], or NaN
+
+// log2 w of channel threadIdx.x (< kD) of head h; its mode bits are ORed
+// into *mode.
+__device__ __forceinline__ float head_decay(const float* __restrict__ w, int h, int* mode) {
+  const float wi = w[h * kD + threadIdx.x];
+  const float l2w = fmaxf(__log2f(wi), kMinLog2Decay);  // log2(0) = -inf
+  int m = 0;
+  if (!(wi >= 0.f && wi <= 1.f)) m |= kModeRecurrent;
+  if (!(fabsf(l2w) <= kMaxLog2Decay)) m |= kModeBlocks;
+  if (!(fabsf(l2w) <= kMaxDiagLog2)) m |= kModeExactDiag;
+  if (m) atomicOr(mode, m);
+  return l2w;
+}
 
 template <int DV>
 struct alignas(16) Lds {
-  __bf16 rt[kL][kPad];    // rt[tau][i]
-  __bf16 kt[kL][kPad];    // kt[sigma][i]
+  // the chunk's scaled operands, [token][channel]: mid-chunk path a[0] = rt,
+  // a[1] = kt; block path a[0] = r, a[1] = kb (keys to their block's end),
+  // a[2] = kd (to its middle; raw k for exact diagonals), a[3] = kh (to the
+  // chunk's end)
+  __bf16 a[4][kL][kPad];
   __bf16 v[kL][kPad];     // v[sigma][j], DV columns
-  __bf16 sp[DV][kPad];    // (diag(w^32) S)^T[j][i]
+  __bf16 sp[DV][kPad];    // S^T[j][i] as the inter-chunk product reads it
   float l2w[kD];          // log2 w_i
   float w32[kD];          // w_i^32
+  float w16m[4][kD];      // w_i^(16m)
+  float wpow[15][kD];     // w_i^d (exact diagonal blocks)
   float scratch[4][kD];   // the exact recurrence's per-token vectors
   float beta[kL];
   float u[kD];
-  int fallback;
+  int mode;
 };
 
 // Exact fp32 recurrence for one (batch, head, value slice): lane j < DV
@@ -125,7 +164,7 @@ __device__ __forceinline__ void stage_consts(StageConsts& c, const Lds<DV>& s) {
   }
 }
 
-// Scale one chunk into LDS: rt, kt, v (all row-major: products over sigma
+// Mid-chunk path: scale one chunk into LDS: rt, kt, v (all row-major: products over sigma
 // read them with the transpose load) and beta.  Tokens past T were loaded as
 // zeros, so they add nothing to any product.
 template <int DV>
@@ -155,10 +194,10 @@ __device__ __forceinline__ void stage_chunk(const ChunkRegs& x, const StageConst
   }
 #pragma unroll
   for (int e = 0; e < 16; ++e) bpart = fmaf(rv[e] * s.u[d0 + e], kv[e], bpart);
-  *reinterpret_cast<bf16x8*>(&s.rt[tau][d0]) = rt0;
-  *reinterpret_cast<bf16x8*>(&s.rt[tau][d0 + 8]) = rt1;
-  *reinterpret_cast<bf16x8*>(&s.kt[tau][d0]) = kt0;
-  *reinterpret_cast<bf16x8*>(&s.kt[tau][d0 + 8]) = kt1;
+  *reinterpret_cast<bf16x8*>(&s.a[0][tau][d0]) = rt0;
+  *reinterpret_cast<bf16x8*>(&s.a[0][tau][d0 + 8]) = rt1;
+  *reinterpret_cast<bf16x8*>(&s.a[1][tau][d0]) = kt0;
+  *reinterpret_cast<bf16x8*>(&s.a[1][tau][d0 + 8]) = kt1;
   // v is already bf16: DV / 4 value dims of this token go in as loaded
   if constexpr (DV == 64) {
     *reinterpret_cast<uint4*>(&s.v[tau][16 * q4]) = x.v0;
@@ -172,6 +211,95 @@ __device__ __forceinline__ void stage_chunk(const ChunkRegs& x, const StageConst
   bpart += __shfl_xor(bpart, 1);
   bpart += __shfl_xor(bpart, 2);
   if (q4 == 0) s.beta[tau] = bpart;
+}
+
+// Block path: the key factors of the 16 channels this thread stages
+// (token tau = tid/4, channels 16 (tid%4) ..), the same for every chunk.
+struct BlockStageConsts {
+  float fb[16];  // w^(15 - tau%16): to the key's block end
+  float fd[16];  // w^(7 - tau%16): to its block middle
+  float fh[16];  // w^(63 - tau): to the chunk end
+};
+
+template <int DV>
+__device__ __forceinline__ void block_stage_consts(BlockStageConsts& c, const Lds<DV>& s) {
+  const int tid = threadIdx.x;
+  const int tau = tid >> 2, p = tau & 15, d0 = 16 * (tid & 3);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float l2 = s.l2w[d0 + e];
+    c.fb[e] = exp2f(float(15 - p) * l2);
+    c.fd[e] = exp2f(float(7 - p) * l2);
+    c.fh[e] = exp2f(float(63 - tau) * l2);
+  }
+}
+
+// Block path: one chunk into LDS: raw r, kb, kd (raw k for exact
+// diagonals), kh, v and beta.  n_last > 0 marks the sequence's ragged last
+// chunk of n_last tokens whose end state is wanted: its update keys carry
+// w^(n_last-1-sigma) instead, and 0 past the last token.
+template <int DV>
+__device__ __forceinline__ void block_stage_chunk(const ChunkRegs& x, const BlockStageConsts& f,
+                                                  bool exact_diag, int n_last, Lds<DV>& s) {
+  const int tid = threadIdx.x;
+  const int tau = tid >> 2, q4 = tid & 3;
+  const int d0 = 16 * q4;
+  float rv[16], kv[16];
+  const uint32_t rw[8] = {x.r0.x, x.r0.y, x.r0.z, x.r0.w, x.r1.x, x.r1.y, x.r1.z, x.r1.w};
+  const uint32_t kw[8] = {x.k0.x, x.k0.y, x.k0.z, x.k0.w, x.k1.x, x.k1.y, x.k1.z, x.k1.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    rv[2 * e] = lo_half(rw[e]);
+    rv[2 * e + 1] = hi_half(rw[e]);
+    kv[2 * e] = lo_half(kw[e]);
+    kv[2 * e + 1] = hi_half(kw[e]);
+  }
+  *reinterpret_cast<uint4*>(&s.a[0][tau][d0]) = x.r0;
+  *reinterpret_cast<uint4*>(&s.a[0][tau][d0 + 8]) = x.r1;
+  bf16x8 kb0, kb1, kd0, kd1, kh0, kh1;
+  float bpart = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    float fh = f.fh[e];
+    if (n_last > 0) fh = tau < n_last ? exp2f(float(n_last - 1 - tau) * s.l2w[d0 + e]) : 0.f;
+    const __bf16 xb = to_bf16(kv[e] * f.fb[e]);
+    const __bf16 xd = exact_diag ? to_bf16(kv[e]) : to_bf16(kv[e] * f.fd[e]);
+    const __bf16 xh = to_bf16(kv[e] * fh);
+    if (e < 8) {
+      kb0[e] = xb;
+      kd0[e] = xd;
+      kh0[e] = xh;
+    } else {
+      kb1[e - 8] = xb;
+      kd1[e - 8] = xd;
+      kh1[e - 8] = xh;
+    }
+    bpart = fmaf(rv[e] * s.u[d0 + e], kv[e], bpart);
+  }
+  *reinterpret_cast<bf16x8*>(&s.a[1][tau][d0]) = kb0;
+  *reinterpret_cast<bf16x8*>(&s.a[1][tau][d0 + 8]) = kb1;
+  *reinterpret_cast<bf16x8*>(&s.a[2][tau][d0]) = kd0;
+  *reinterpret_cast<bf16x8*>(&s.a[2][tau][d0 + 8]) = kd1;
+  *reinterpret_cast<bf16x8*>(&s.a[3][tau][d0]) = kh0;
+  *reinterpret_cast<bf16x8*>(&s.a[3][tau][d0 + 8]) = kh1;
+  if constexpr (DV == 64) {
+    *reinterpret_cast<uint4*>(&s.v[tau][16 * q4]) = x.v0;
+    *reinterpret_cast<uint4*>(&s.v[tau][16 * q4 + 8]) = x.v1;
+  } else if constexpr (DV == 32) {
+    *reinterpret_cast<uint4*>(&s.v[tau][8 * q4]) = x.v0;
+  } else {
+    *reinterpret_cast<uint2*>(&s.v[tau][4 * q4]) = uint2{x.v0.x, x.v0.y};
+  }
+  bpart += __shfl_xor(bpart, 1);
+  bpart += __shfl_xor(bpart, 2);
+  if (q4 == 0) s.beta[tau] = bpart;
+}
+
+__device__ __forceinline__ void ld8(const float* p, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x, x[1] = a.y, x[2] = a.z, x[3] = a.w;
+  x[4] = b.x, x[5] = b.y, x[6] = b.z, x[7] = b.w;
 }
 
 // Workgroup: 4 waves; (batch, head, slice of DV value columns).  blockIdx
@@ -198,32 +326,36 @@ __global__ __launch_bounds__(256, 2) void wkv5_fwd_chunked(
   const int lane = tid & 63;
   const int q = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // log2 w, the powers used every chunk, and the range check that picks the
-  // path.
-  if (tid == 0) s.fallback = 0;
+  // log2 w, the powers used every chunk, and the head's path.
+  if (tid == 0) s.mode = 0;
   __syncthreads();
   if (tid < kD) {
-    const float wi = w[h * kD + tid];
     s.u[tid] = u[h * kD + tid];
-    const float l2w = __log2f(wi);
+    const float l2w = head_decay(w, h, &s.mode);
     s.l2w[tid] = l2w;
     s.w32[tid] = exp2f(32.f * l2w);
-    if (!(fabsf(l2w) <= kMaxLog2Decay)) atomicOr(&s.fallback, 1);  // also catches NaN, w<=0
+#pragma unroll
+    for (int m = 0; m < 4; ++m) s.w16m[m][tid] = exp2f(float(16 * m) * l2w);
+#pragma unroll
+    for (int d = 0; d < 15; ++d) s.wpow[d][tid] = exp2f(float(d) * l2w);
   }
   __syncthreads();
-  if (s.fallback) {
+  const int mode = __builtin_amdgcn_readfirstlane(s.mode);
+  if (mode & kModeRecurrent) {
     // the exact recurrence runs the whole sequence in the first segment
     if (seg == 0) eagle_recurrent_slice<DV>(T, H, b, h, j0, r, k, v, w, u, o, s_in, s_out, s);
     return;
   }
+  const bool blocks = (mode & kModeBlocks) != 0;
 
   const int row = lane & 15;         // MFMA operand row/column of this lane
   const int kq = 8 * (lane >> 4);    // first K element of this lane in a 32-wide step
   const int crow = 4 * (lane >> 4);  // first accumulator row of this lane
   const size_t sbase = size_t(bh) * kD * kD;  // state s[i][j] at sbase + i*kD + j
 
-  // S lives in registers (wave q: key rows 16q..16q+15); S' = diag(w^32) S
-  // goes to LDS, transposed, for the inter-chunk product.
+  // S lives in registers (wave q: key rows 16q..16q+15) and goes to LDS,
+  // transposed, for the inter-chunk product: as diag(w^32) S on the
+  // mid-chunk path, as S on the block path.
   floatx4 sacc[NJB];
 #pragma unroll
   for (int jb = 0; jb < NJB; ++jb)
@@ -257,15 +389,13 @@ __global__ __launch_bounds__(256, 2) void wkv5_fwd_chunked(
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int i = 16 * q + crow + rr;
-        pk[rr] = to_bf16(sacc[jb][rr] * s.w32[i]);
+        pk[rr] = to_bf16(blocks ? sacc[jb][rr] : sacc[jb][rr] * s.w32[i]);
       }
       *reinterpret_cast<bf16x4*>(&s.sp[16 * jb + row][16 * q + crow]) = pk;
     }
   };
   write_sp();
 
-  StageConsts f;
-  stage_consts(f, s);
   const int n_chunks = (T + kL - 1) / kL;
   const int c_begin = seg * seg_chunks;
   const int c_end = min(n_chunks, c_begin + seg_chunks);
@@ -274,99 +404,227 @@ __global__ __launch_bounds__(256, 2) void wkv5_fwd_chunked(
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr)
     ooff[rr] = uint32_t(((16 * q + crow + rr) * H * kD + j0 + row) * 4);
+  const int tau_l = 16 * q + row;  // this lane's query in the score and inter-chunk operands
+  auto store_o = [&](const floatx4 (&oacc)[NJB], int t0) {
+    const Rsrc ro = chunk_rsrc(o, t0, T, H, b, h, 4);  // rows past T are dropped
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(oacc[jb][rr]), ro, ooff[rr],
+                                              64 * jb, kStoreAux);
+  };
   ChunkRegs cur, nxt;
   load_chunk<DV>(cur, c_begin * kL, T, H, b, h, j0, r, k, v);
-  for (int c = c_begin; c < c_end; ++c) {
-    const int t0 = c * kL;
-    const int n_last = (s_out && c == n_chunks - 1 && T - t0 < kL) ? T - t0 : 0;
-    stage_chunk(cur, f, s);
-    __syncthreads();
-    if (c + 1 < c_end) load_chunk<DV>(nxt, t0 + kL, T, H, b, h, j0, r, k, v);
 
-    // A^T = kt rt^T for all four sigma blocks against this wave's 16 tokens
-    // (blocks after the wave's own are masked to zero below; computing them
-    // costs a few MFMAs but no branches): lane holds column tau = 16q + row,
-    // rows sigma = 16nb + crow .. +3.
-    floatx4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
-                      {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  if (blocks) {
+    const bool exact_diag = (mode & kModeExactDiag) != 0;
+    BlockStageConsts f;
+    block_stage_consts(f, s);
+    // this lane's query factors: w^p and w^(p-8), p = row, for its channels
+    // 32 ks + kq + e
+    float fq[16], fdq[16];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s.rt[16 * q + row][32 * ks + kq]);
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.kt[16 * nb + row][32 * ks + kq]);
-        acc[nb] = mfma(a, bb, acc[nb]);
+      for (int e = 0; e < 8; ++e) {
+        const float l2 = s.l2w[32 * ks + kq + e];
+        fq[8 * ks + e] = exp2f(float(row) * l2);
+        fdq[8 * ks + e] = exp2f(float(row - 8) * l2);
       }
-    }
-    // Causal mask and the bonus on the diagonal, in registers.  The pair of
-    // sigma tiles (2ks, 2ks+1) held by a lane is directly an A operand of a
-    // 32-wide K step, with K ordered as sigma = 32ks + crow + 0..3, then
-    // 32ks + 16 + crow + 0..3: the order of sigma_operand.
-    const int tau_l = 16 * q + row;
-    const float beta = s.beta[tau_l];
-    bf16x8 ap[2];
+    for (int c = c_begin; c < c_end; ++c) {
+      const int t0 = c * kL;
+      const int n_last = (s_out && c == n_chunks - 1 && T - t0 < kL) ? T - t0 : 0;
+      block_stage_chunk(cur, f, exact_diag, n_last, s);
+      __syncthreads();
+      if (c + 1 < c_end) load_chunk<DV>(nxt, t0 + kL, T, H, b, h, j0, r, k, v);
+
+      // A^T: key blocks nb < q (each against the queries referred to its
+      // end) and the diagonal block; the inter-chunk queries r w^tau are
+      // formed alongside.  Lane: column tau_l, rows sigma = 16nb + crow ..
+      floatx4 acc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      floatx4 dacc = {0.f, 0.f, 0.f, 0.f};
+      bf16x8 ainter[2];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+      for (int ks = 0; ks < 2; ++ks) {
+        const int i0 = 32 * ks + kq;
+        const bf16x8 raw = *reinterpret_cast<const bf16x8*>(&s.a[0][tau_l][i0]);
+        float rq[8];  // r w^p
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rq[e] = float(raw[e]) * fq[8 * ks + e];
+#pragma unroll
+        for (int nb = 0; nb < 3; ++nb)
+          if (nb < q) {
+            float wm[8];
+            ld8(&s.w16m[q - 1 - nb][i0], wm);
+            bf16x8 bq;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bq[e] = to_bf16(rq[e] * wm[e]);
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.a[1][16 * nb + row][i0]);
+            acc[nb] = mfma(a, bq, acc[nb]);
+          }
+        float wq[8];
+        ld8(&s.w16m[q][i0], wq);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ainter[ks][e] = to_bf16(rq[e] * wq[e]);
+        if (!exact_diag) {
+          bf16x8 bd;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) bd[e] = to_bf16(float(raw[e]) * fdq[8 * ks + e]);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.a[2][16 * q + row][i0]);
+          dacc = mfma(a, bd, dacc);
+        }
+      }
+      if (exact_diag) {
+        // sum_i r[tau][i] k[sigma][i] w_i^(tau-1-sigma), raw r and k in fp32
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int sig = 16 * q + crow + rr;
+          float a = 0.f;
+          if (sig < tau_l) {
+            const int d = tau_l - 1 - sig;  // 0 .. 14
+            for (int i = 0; i < kD; ++i)
+              a = fmaf(float(s.a[0][tau_l][i]) * float(s.a[2][sig][i]), s.wpow[d][i], a);
+          }
+          dacc[rr] = a;
+        }
+      }
+
+      // Causal mask and the bonus on the diagonal, in registers.
+      const float beta = s.beta[tau_l];
+      bf16x8 ap[2];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int sig = 16 * nb + crow + rr;
+          const float sc = nb == q ? dacc[rr] : (nb < 3 ? acc[nb < 3 ? nb : 0][rr] : 0.f);
+          const float val = sig < tau_l ? sc : (sig == tau_l ? beta : 0.f);
+          ap[nb >> 1][(nb & 1) * 4 + rr] = to_bf16(val);
+        }
+
+      // O = A' V + (r w^tau) S and S <- diag(w^64) S + kh^T V (w^n_last for a
+      // ragged last chunk whose end state is wanted); the two products over
+      // sigma share their V operands.
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int sig = 16 * nb + crow + rr;
-        const float val = sig < tau_l ? acc[nb][rr] : (sig == tau_l ? beta : 0.f);
-        ap[nb >> 1][(nb & 1) * 4 + rr] = to_bf16(val);
+        const float l2 = s.l2w[16 * q + crow + rr];
+        const float dall = exp2f(float(n_last > 0 ? n_last : kL) * l2);
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) sacc[jb][rr] *= dall;
       }
+      floatx4 oacc[NJB];
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) oacc[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 kop = sigma_operand(s.a[3], 32 * ks, 16 * q, lane);
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) {
+          const bf16x8 vop = sigma_operand(s.v, 32 * ks, 16 * jb, lane);
+          oacc[jb] = mfma(ap[ks], vop, oacc[jb]);
+          sacc[jb] = mfma(kop, vop, sacc[jb]);
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) {
+          const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s.sp[16 * jb + row][32 * ks + kq]);
+          oacc[jb] = mfma(ainter[ks], bb, oacc[jb]);
+        }
+      store_o(oacc, t0);
+      __syncthreads();  // every wave is done with this chunk's LDS
 
-    // O = A' V + rt S' (16 tokens x DV value columns per wave) and
-    // S <- diag(w^32) (diag(w^32) S + kt^T V) for key rows 16q..16q+15: the
-    // two products over sigma share their V operands.  A ragged final chunk
-    // of n tokens ends with diag(w^(n-32)) instead, which decays S by w^n and
-    // token sigma by w^(n-1-sigma).
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const float w32 = s.w32[16 * q + crow + rr];
-#pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) sacc[jb][rr] *= w32;
+      write_sp();  // S for the next chunk
+      cur = nxt;
     }
-    floatx4 oacc[NJB];
-#pragma unroll
-    for (int jb = 0; jb < NJB; ++jb) oacc[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 kop = sigma_operand(s.kt, 32 * ks, 16 * q, lane);
-#pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) {
-        const bf16x8 vop = sigma_operand(s.v, 32 * ks, 16 * jb, lane);
-        oacc[jb] = mfma(ap[ks], vop, oacc[jb]);
-        sacc[jb] = mfma(kop, vop, sacc[jb]);
-      }
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.rt[16 * q + row][32 * ks + kq]);
-#pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) {
-        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s.sp[16 * jb + row][32 * ks + kq]);
-        oacc[jb] = mfma(a, bb, oacc[jb]);
-      }
-    }
-    {
-      const Rsrc ro = chunk_rsrc(o, t0, T, H, b, h, 4);  // rows past T are dropped
-#pragma unroll
-      for (int jb = 0; jb < NJB; ++jb)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(oacc[jb][rr]), ro, ooff[rr],
-                                                64 * jb, kStoreAux);
-    }
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int i = 16 * q + crow + rr;
-      const float post = n_last > 0 ? exp2f(float(n_last - 32) * s.l2w[i]) : s.w32[i];
-#pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) sacc[jb][rr] *= post;
-    }
-    __syncthreads();  // every wave is done with rt, kt, v, sp of this chunk
+  } else {
+    StageConsts f;
+    stage_consts(f, s);
+    for (int c = c_begin; c < c_end; ++c) {
+      const int t0 = c * kL;
+      const int n_last = (s_out && c == n_chunks - 1 && T - t0 < kL) ? T - t0 : 0;
+      stage_chunk(cur, f, s);
+      __syncthreads();
+      if (c + 1 < c_end) load_chunk<DV>(nxt, t0 + kL, T, H, b, h, j0, r, k, v);
 
-    write_sp();  // S' for the next chunk
-    cur = nxt;
+      // A^T = kt rt^T for all four sigma blocks against this wave's 16 tokens
+      // (blocks after the wave's own are masked to zero below; computing them
+      // costs a few MFMAs but no branches): lane holds column tau = 16q + row,
+      // rows sigma = 16nb + crow .. +3.
+      floatx4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
+                        {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s.a[0][tau_l][32 * ks + kq]);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.a[1][16 * nb + row][32 * ks + kq]);
+          acc[nb] = mfma(a, bb, acc[nb]);
+        }
+      }
+      // Causal mask and the bonus on the diagonal, in registers.  The pair of
+      // sigma tiles (2ks, 2ks+1) held by a lane is directly an A operand of a
+      // 32-wide K step, with K ordered as sigma = 32ks + crow + 0..3, then
+      // 32ks + 16 + crow + 0..3: the order of sigma_operand.
+      const float beta = s.beta[tau_l];
+      bf16x8 ap[2];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int sig = 16 * nb + crow + rr;
+          const float val = sig < tau_l ? acc[nb][rr] : (sig == tau_l ? beta : 0.f);
+          ap[nb >> 1][(nb & 1) * 4 + rr] = to_bf16(val);
+        }
+
+      // O = A' V + rt S' (16 tokens x DV value columns per wave) and
+      // S <- diag(w^32) (diag(w^32) S + kt^T V) for key rows 16q..16q+15: the
+      // two products over sigma share their V operands.  A ragged final chunk
+      // of n tokens ends with diag(w^(n-32)) instead, which decays S by w^n and
+      // token sigma by w^(n-1-sigma).
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float w32 = s.w32[16 * q + crow + rr];
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) sacc[jb][rr] *= w32;
+      }
+      floatx4 oacc[NJB];
+#pragma unroll
+      for (int jb = 0; jb < NJB; ++jb) oacc[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 kop = sigma_operand(s.a[1], 32 * ks, 16 * q, lane);
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) {
+          const bf16x8 vop = sigma_operand(s.v, 32 * ks, 16 * jb, lane);
+          oacc[jb] = mfma(ap[ks], vop, oacc[jb]);
+          sacc[jb] = mfma(kop, vop, sacc[jb]);
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s.a[0][tau_l][32 * ks + kq]);
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) {
+          const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&s.sp[16 * jb + row][32 * ks + kq]);
+          oacc[jb] = mfma(a, bb, oacc[jb]);
+        }
+      }
+      store_o(oacc, t0);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int i = 16 * q + crow + rr;
+        const float post = n_last > 0 ? exp2f(float(n_last - 32) * s.l2w[i]) : s.w32[i];
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) sacc[jb][rr] *= post;
+      }
+      __syncthreads();  // every wave is done with rt, kt, v, sp of this chunk
+
+      write_sp();  // S' for the next chunk
+      cur = nxt;
+    }
   }
   if (s_out && c_end == n_chunks) {
 #pragma unroll
@@ -378,10 +636,11 @@ __global__ __launch_bounds__(256, 2) void wkv5_fwd_chunked(
 }
 
 // Local end state of one time segment (all but the last), from a zero
-// start, over its chunks: S <- diag(w^32) (diag(w^32) S + kt^T V) as in the
-// forward (kt = k w^(31-sigma)), for one value slice; the next chunk's k, v
-// load while this one multiplies.  Written to seg_state[bh][seg] as
-// [key i][value j].
+// start, over its chunks, for one value slice: S <- diag(w^64) S + kh^T V
+// with kh = k w^(63-sigma) (every factor <= 1, for any decay in [0, 1]);
+// the next chunk's k, v load while this one multiplies.  Written to
+// seg_state[bh][seg] as [key i][value j].  Heads on the exact recurrence
+// need none.
 template <int DV>
 __global__ __launch_bounds__(256) void wkv5_seg_state(int T, int H, int BH, int seg_chunks,
                                                       int nseg, const uint16_t* __restrict__ k,
@@ -390,11 +649,10 @@ __global__ __launch_bounds__(256) void wkv5_seg_state(int T, int H, int BH, int 
                                                       float* __restrict__ seg_state) {
   constexpr int NS = kD / DV;
   constexpr int NJB = DV / 16;
-  __shared__ __attribute__((aligned(16))) __bf16 s_kt[kL][kPad];
+  __shared__ __attribute__((aligned(16))) __bf16 s_kh[kL][kPad];
   __shared__ __attribute__((aligned(16))) __bf16 s_v[kL][kPad];
   __shared__ float s_l2w[kD];
-  __shared__ float s_w32[kD];
-  __shared__ int s_fallback;
+  __shared__ int s_mode;
   const int per_seg = (BH + 7) / 8 * 8 * NS;
   const int seg = blockIdx.x / per_seg;
   const int bx = blockIdx.x - seg * per_seg;
@@ -407,23 +665,18 @@ __global__ __launch_bounds__(256) void wkv5_seg_state(int T, int H, int BH, int 
   const int lane = tid & 63;
   const int q = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row = lane & 15, crow = 4 * (lane >> 4);
-  if (tid == 0) s_fallback = 0;
+  if (tid == 0) s_mode = 0;
   __syncthreads();
-  if (tid < kD) {
-    const float l2w = __log2f(w[h * kD + tid]);
-    s_l2w[tid] = l2w;
-    s_w32[tid] = exp2f(32.f * l2w);
-    if (!(fabsf(l2w) <= kMaxLog2Decay)) atomicOr(&s_fallback, 1);
-  }
+  if (tid < kD) s_l2w[tid] = head_decay(w, h, &s_mode);
   __syncthreads();
-  if (s_fallback) return;  // that head runs the exact recurrence in one piece
+  if (s_mode & kModeRecurrent) return;  // that head runs the exact recurrence in one piece
   const int tau = tid >> 2, q4 = tid & 3, d0 = 16 * q4;
-  float fk[16];
+  float fh[16];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) fk[e] = exp2f(float(31 - tau) * s_l2w[d0 + e]);
-  float w32[4];
+  for (int e = 0; e < 16; ++e) fh[e] = exp2f(float(63 - tau) * s_l2w[d0 + e]);
+  float w64[4];
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) w32[rr] = s_w32[16 * q + crow + rr];
+  for (int rr = 0; rr < 4; ++rr) w64[rr] = exp2f(64.f * s_l2w[16 * q + crow + rr]);
   floatx4 sacc[NJB];
 #pragma unroll
   for (int jb = 0; jb < NJB; ++jb) sacc[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -434,16 +687,16 @@ __global__ __launch_bounds__(256) void wkv5_seg_state(int T, int H, int BH, int 
   for (int c = c_begin; c < c_end; ++c) {
     const uint32_t kw[8] = {cur.k0.x, cur.k0.y, cur.k0.z, cur.k0.w,
                             cur.k1.x, cur.k1.y, cur.k1.z, cur.k1.w};
-    bf16x8 kt0, kt1;
+    bf16x8 kh0, kh1;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      kt0[2 * e] = to_bf16(lo_half(kw[e]) * fk[2 * e]);
-      kt0[2 * e + 1] = to_bf16(hi_half(kw[e]) * fk[2 * e + 1]);
-      kt1[2 * e] = to_bf16(lo_half(kw[4 + e]) * fk[8 + 2 * e]);
-      kt1[2 * e + 1] = to_bf16(hi_half(kw[4 + e]) * fk[8 + 2 * e + 1]);
+      kh0[2 * e] = to_bf16(lo_half(kw[e]) * fh[2 * e]);
+      kh0[2 * e + 1] = to_bf16(hi_half(kw[e]) * fh[2 * e + 1]);
+      kh1[2 * e] = to_bf16(lo_half(kw[4 + e]) * fh[8 + 2 * e]);
+      kh1[2 * e + 1] = to_bf16(hi_half(kw[4 + e]) * fh[8 + 2 * e + 1]);
     }
-    *reinterpret_cast<bf16x8*>(&s_kt[tau][d0]) = kt0;
-    *reinterpret_cast<bf16x8*>(&s_kt[tau][d0 + 8]) = kt1;
+    *reinterpret_cast<bf16x8*>(&s_kh[tau][d0]) = kh0;
+    *reinterpret_cast<bf16x8*>(&s_kh[tau][d0 + 8]) = kh1;
     if constexpr (DV == 64) {
       *reinterpret_cast<uint4*>(&s_v[tau][16 * q4]) = cur.v0;
       *reinterpret_cast<uint4*>(&s_v[tau][16 * q4 + 8]) = cur.v1;
@@ -457,18 +710,14 @@ __global__ __launch_bounds__(256) void wkv5_seg_state(int T, int H, int BH, int 
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) sacc[jb][rr] *= w32[rr];
+      for (int jb = 0; jb < NJB; ++jb) sacc[jb][rr] *= w64[rr];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 kop = sigma_operand(s_kt, 32 * ks, 16 * q, lane);
+      const bf16x8 kop = sigma_operand(s_kh, 32 * ks, 16 * q, lane);
 #pragma unroll
       for (int jb = 0; jb < NJB; ++jb)
         sacc[jb] = mfma(kop, sigma_operand(s_v, 32 * ks, 16 * jb, lane), sacc[jb]);
     }
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-      for (int jb = 0; jb < NJB; ++jb) sacc[jb][rr] *= w32[rr];
     __syncthreads();
     cur = nxt;
   }

@@ -32,7 +32,7 @@ import numpy as np
 __all__ = [
     "Wkv4Config", "Wkv4StepConfig", "Wkv5Config",
     "CFG_WKV4_TINY", "CFG_WKV4_169M", "CFG_WKV4_LONG", "CFG_WKV4_DECODE",
-    "CFG_WKV5_EAGLE", "CFG_WKV5_DECODE", "Wkv5StepConfig",
+    "CFG_WKV5_EAGLE", "CFG_WKV5_EAGLE_WIDE", "CFG_WKV5_DECODE", "Wkv5StepConfig",
     "rng_for", "wkv4_inputs", "wkv4_step_inputs", "wkv5_inputs", "wkv5_step_inputs",
     "wkv4_backward_inputs", "wkv6_inputs", "CFG_WKV6_FINCH",
     "bf16_bits_from_f32", "f32_from_bf16_bits",
@@ -100,6 +100,11 @@ CFG_WKV4_LONG = Wkv4Config("wkv4_fwd_B1_T65536_C5120", 1, 65536, 5120, 1003,
 # resident on the device.
 CFG_WKV4_DECODE = Wkv4StepConfig("wkv4_step_B256_C4096_x4096", 256, 4096, 4096, 64, 1004)
 CFG_WKV5_EAGLE = Wkv5Config("wkv5_fwd_B4_T4096_H32_D64", 4, 4096, 32, 64, 1005)
+# The Eagle workload's shape over the wider decay range omega ~ U(-6, 2)
+# (w down to exp(-e^2) = 6e-4, |log2 w| up to 10.7): every head has decays
+# too fast for the mid-chunk reference.
+CFG_WKV5_EAGLE_WIDE = Wkv5Config("wkv5_fwd_B4_T4096_H32_D64_omega-6to2", 4, 4096, 32, 64, 1008,
+                                 omega_lo=-6.0, omega_hi=2.0)
 # Finch forward at the Eagle workload's shape, with per-token decays.
 CFG_WKV6_FINCH = Wkv5Config("wkv6_fwd_B4_T4096_H32_D64", 4, 4096, 32, 64, 1007)
 # Eagle decode: 64 streams of 32 heads (a 32 MB fp32 state), 256 steps drawn
@@ -221,13 +226,15 @@ def wkv5_inputs_for(cfg: Wkv5Config) -> dict:
 
 
 def dyadic_matrix_inputs(B: int, T: int, H: int, seed: int, *, per_token_decay=False,
-                         seams=(), slow_head=None) -> dict:
+                         seams=(), slow_head=None, fast_head=None, growing_head=None) -> dict:
     """Sparse one-hot inputs for bit-exact checks of the matrix-state paths.
 
     Every nonzero r, k, v, u is +-1/2, +-1 or +-2 and every decay factor is 1,
     1/2 or 1/4 (Eagle w [H, D]; with ``per_token_decay`` a Finch w_t
-    [B, T, H, D]), plus 1/16 on some key rows of ``slow_head`` (Eagle) or a
-    few factors 2^-16 (Finch).  Per (batch, head):
+    [B, T, H, D]), plus (Eagle) 1/16 on some key rows of ``slow_head``, 2^-16
+    on some of ``fast_head`` and a factor 2 (a growing row, outside the
+    pages' (0, 1)) on one of ``growing_head``, or (Finch) a few factors
+    2^-16.  Per (batch, head):
 
     * each key row i is written by at most one token (k one-hot at i, v
       one-hot at a column j), so every state entry is a single term;
@@ -263,13 +270,20 @@ def dyadic_matrix_inputs(B: int, T: int, H: int, seed: int, *, per_token_decay=F
         reach = {0: 10 ** 9, 1: 30, 2: 30, 3: 6}
         gone = {0: None, 1: 160, 2: None, 3: 160}
     else:
-        # 0: w = 1; 1: w = 1/2; 2: w = 1/4; 3: w = 1/16 (slow_head only)
+        # 0: w = 1; 1: w = 1/2; 2: w = 1/4; 3: w = 1/16 (slow_head only);
+        # 4: w = 2^-16 (fast_head only); 5: w = 2 (growing_head only: written
+        # only within its reach of the end, read within it)
         n_kinds = 3
-        reach = {0: 10 ** 9, 1: 60, 2: 30, 3: 7}
-        gone = {0: None, 1: 160, 2: 80, 3: 40}
+        reach = {0: 10 ** 9, 1: 60, 2: 30, 3: 7, 4: 3, 5: 20}
+        gone = {0: None, 1: 160, 2: 80, 3: 40, 4: 10, 5: None}
     kind = rng.integers(0, n_kinds, size=(H, D))
-    if slow_head is not None and not per_token_decay:
-        kind[slow_head, rng.permutation(D)[:8]] = 3
+    if not per_token_decay:
+        if slow_head is not None:
+            kind[slow_head, rng.permutation(D)[:8]] = 3
+        if fast_head is not None:
+            kind[fast_head, rng.permutation(D)[:8]] = 4
+        if growing_head is not None:
+            kind[growing_head, rng.integers(D)] = 5
     u = pm((H, D))
     r = np.zeros((B, T, H, D))
     k = np.zeros((B, T, H, D))
@@ -286,7 +300,7 @@ def dyadic_matrix_inputs(B: int, T: int, H: int, seed: int, *, per_token_decay=F
                 elif kd == 3:
                     wt[:, :, h, i] = np.where(rng.random((B, T)) < 0.05, 2.0 ** -16, 0.5)
     else:
-        w = np.choose(kind, [1.0, 0.5, 0.25, 0.0625])
+        w = np.choose(kind, [1.0, 0.5, 0.25, 0.0625, 2.0 ** -16, 2.0])
 
     special = set()
     for e in (0, 31, 32, 63, 64, 95, 96, 127, 128, 191, 192, T - 2, T - 1):

@@ -50,8 +50,13 @@ def _mutant(r, k, v, w, u, kind, per_token):
 
 @pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])
 def test_exact_results_are_float32_powers_of_two(per_token):
-    e = synth.dyadic_matrix_inputs(2, 1100, 3, seed=11, per_token_decay=per_token,
-                                   seams=(320, 640, 960), slow_head=None if per_token else 2)
+    # Eagle: head 0 all decays in {1, 1/2, 1/4}, head 1 some 2^-16, head 2
+    # some 1/16, head 3 one growing row (factor 2)
+    H = 3 if per_token else 4
+    e = synth.dyadic_matrix_inputs(2, 1100, H, seed=11, per_token_decay=per_token,
+                                   seams=(320, 640, 960),
+                                   **({} if per_token else
+                                      dict(slow_head=2, fast_head=1, growing_head=3)))
     if per_token:
         o, S = O.wkv6_recurrent(e["r"], e["k"], e["v"], e["wt"], e["u"])
     else:
@@ -60,6 +65,15 @@ def test_exact_results_are_float32_powers_of_two(per_token):
     n_s = _powers_of_two(S)
     # dense enough to exercise every path: many nonzero outputs and states
     assert n_o > 500 and n_s > 100
+    if not per_token:
+        # the special rows are written and read: outputs that are the
+        # product of a 2^-16 decay, and of a factor 2 (w^d with d >= 1)
+        for h, kind_w in ((1, 2.0 ** -16), (3, 2.0)):
+            rows = np.flatnonzero(e["w"][h] == kind_w)
+            assert rows.size > 0
+            read = np.abs(e["r"][:, :, h][..., rows]).sum(-1) > 0
+            wrote_before = np.cumsum(np.abs(e["k"][:, :, h][..., rows]).sum(-1) > 0, axis=1) > 0
+            assert np.any(read & wrote_before & (np.abs(o[:, :, h]).sum(-1) > 0))
 
 
 @pytest.mark.parametrize("per_token", [False, True], ids=["eagle", "finch"])

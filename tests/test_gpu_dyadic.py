@@ -5,8 +5,9 @@ update s' = diag(w) s + k^T v and the read-out r (s + diag(u) k^T v);
 section "Finch": the same with a decay per token.
 
 The inputs (synth.dyadic_matrix_inputs) are sparse one-hot tokens with
-power-of-two values and decays of 1, 1/2, 1/4 (1/16 on one head, 2^-16 on
-some Finch tokens), placed across chunk edges and time-segment seams so that
+power-of-two values and decays of 1, 1/2, 1/4 (Eagle: 1/16 on one head,
+2^-16 on another, a growing factor 2 on a third; Finch: 2^-16 on some
+tokens), placed across chunk edges and time-segment seams so that
 every sum of the exact result has at most one nonzero term.  Every
 intermediate of the chunked forms (the decay-scaled bf16 queries and keys,
 the score tiles, the bf16 copy of the state) is then an exact power of two,
@@ -82,9 +83,14 @@ def test_eagle_forward_bit_exact(segs, dv):
     torch, _ = torch_dev()
     T = 1100
     seams = _seams(T, segs)
-    log(f"dyadic wkv5_forward B={B} T={T} H={H} segments={segs} value columns={dv} "
-        f"seams={seams} (head 2 has 1/16 decays)")
-    e = synth.dyadic_matrix_inputs(B, T, H, seed=300 + 10 * segs + dv, seams=seams, slow_head=2)
+    # one head per path of the kernel: 0 mid-chunk reference, 1 blocks with
+    # exact diagonals (2^-16 decays), 2 blocks (1/16 decays), 3 the exact
+    # recurrence (a growing row, w = 2)
+    H4 = 4
+    log(f"dyadic wkv5_forward B={B} T={T} H={H4} segments={segs} value columns={dv} "
+        f"seams={seams}")
+    e = synth.dyadic_matrix_inputs(B, T, H4, seed=300 + 10 * segs + dv, seams=seams,
+                                   slow_head=2, fast_head=1, growing_head=3)
     with tuned(wkv5_segs=segs, wkv5_dv=dv):
         o, s = _forward(e, False)
         torch.cuda.synchronize()
@@ -138,7 +144,9 @@ def test_forward_steps_forward_chain_bit_exact(cut, finch):
     T = 700
     log(f"dyadic {'wkv6' if finch else 'wkv5'} chain T1={T1} steps={N} T={T}")
     e = synth.dyadic_matrix_inputs(B, T, H, seed=600 + T1 + N + finch, per_token_decay=finch,
-                                   seams=(T1, T1 + N), slow_head=None if finch else 0)
+                                   seams=(T1, T1 + N),
+                                   **({} if finch else dict(slow_head=0, fast_head=1,
+                                                            growing_head=2)))
     o1, s = _forward(e, finch, np.s_[:, :T1])
     outs = [o1]
     for t in range(T1, T1 + N):

@@ -99,7 +99,7 @@ def _with_dv(dv, fn):
 def test_forward_state_chain_matches_whole_sequence(case, dv):
     """forward(T1) -> N steps -> forward(T2) with the state handed on (the
     last hand-over in place) equals one pass over the whole sequence; the
-    w=0.05 case runs the exact-recurrence path of the forward."""
+    w=0.05 case runs the 16-token block path of the forward."""
     torch, dev = torch_dev()
     kind, T1, N, T2 = case
     B, H = 2, 3
@@ -241,15 +241,99 @@ def test_time_segments(shape, segs):
     assert err_o <= WKV5_TOL and err_s <= WKV5_TOL
 
 
-def test_time_segments_with_exact_recurrence_heads():
-    """A head outside the factorised range runs the exact recurrence in one
-    piece while the other heads are split."""
+@pytest.mark.parametrize("dv", [64, 32, 16])
+@pytest.mark.parametrize("segs", [1, 3])
+def test_heads_on_every_path_in_one_launch(segs, dv):
+    """Head 0 on the mid-chunk reference, head 1 on 16-token blocks
+    (w = 0.05, |log2 w| = 4.3), head 2 on blocks with exact diagonals (some
+    w = 1e-6), head 3 on the exact recurrence (one w = 1.0005, outside
+    [0, 1]); split into time segments, from a starting state, handing on
+    the end state."""
     torch, dev = torch_dev()
-    inp = synth.wkv5_inputs(1, 1000, 3, 64, seed=5)
+    B, T, H = 2, 1000, 4
+    inp = synth.wkv5_inputs(B, T, H, 64, seed=5)
     w = inp["w"].copy()
-    w[1] = 0.05  # |log2 w| > 3.6: exact path for head 1
+    w[1] = 0.05
+    w[2, ::5] = 1e-6
+    w[3, 7] = 1.0005
     case = dict(inp, w=w)
-    with tuned(wkv5_segs=3):
-        o = gpu_wkv5(case)
-    o_ref, o_abs = oracle_wkv5(case)
-    assert wkv5_scaled_err(o, o_ref, o_abs) <= WKV5_TOL
+    s0 = (np.random.default_rng(4).standard_normal((B, H, 64, 64)) * 0.3).astype(np.float32)
+    log(f"wkv5_forward heads on all paths, segments={segs} value columns={dv}")
+    with tuned(wkv5_segs=segs, wkv5_dv=dv):
+        o, s1 = rw.rwkv_wkv5_forward_state(_bits(case, "r", np.s_[:]), _bits(case, "k", np.s_[:]),
+                                           _bits(case, "v", np.s_[:]), to_dev(w),
+                                           to_dev(case["u"]), s_in=to_dev(s0), s_out=True)
+        torch.cuda.synchronize()
+    o_ref, s_ref = O.wkv5_recurrent(case["r"], case["k"], case["v"], w, case["u"], S0=s0)
+    o_abs, s_abs = O.wkv5_recurrent(np.abs(case["r"]), np.abs(case["k"]), np.abs(case["v"]), w,
+                                    np.abs(case["u"]), S0=np.abs(s0))
+    for h in range(H):
+        err_o = wkv5_scaled_err(o.cpu().numpy()[:, :, h], o_ref[:, :, h], o_abs[:, :, h])
+        err_s = wkv5_scaled_err(s1.cpu().numpy()[:, h], s_ref[:, h], s_abs[:, h])
+        log(f"  head {h}: err o={err_o:.3e} state={err_s:.3e}")
+        assert err_o <= WKV5_TOL and err_s <= WKV5_TOL
+
+
+@pytest.mark.parametrize("dv", [64, 32, 16])
+@pytest.mark.parametrize("segs", [1, 2, 4])
+def test_wide_decay_range(segs, dv):
+    """omega ~ U(-6, 2) (w = exp(-exp(omega)) down to 6e-4): every head on the
+    16-token block path; ragged length, starting and handed-on state."""
+    torch, dev = torch_dev()
+    B, T, H = 2, 1000, 3
+    inp = synth.wkv5_inputs(B, T, H, 64, seed=17 + segs, omega_lo=-6.0, omega_hi=2.0)
+    s0 = (np.random.default_rng(segs).standard_normal((B, H, 64, 64)) * 0.3).astype(np.float32)
+    log(f"wkv5_forward omega~U(-6,2) segments={segs} value columns={dv}")
+    with tuned(wkv5_segs=segs, wkv5_dv=dv):
+        o, s1 = rw.rwkv_wkv5_forward_state(_bits(inp, "r", np.s_[:]), _bits(inp, "k", np.s_[:]),
+                                           _bits(inp, "v", np.s_[:]), to_dev(inp["w"]),
+                                           to_dev(inp["u"]), s_in=to_dev(s0), s_out=True)
+        torch.cuda.synchronize()
+    o_ref, s_ref = O.wkv5_recurrent(inp["r"], inp["k"], inp["v"], inp["w"], inp["u"], S0=s0)
+    o_abs, s_abs = O.wkv5_recurrent(np.abs(inp["r"]), np.abs(inp["k"]), np.abs(inp["v"]),
+                                    inp["w"], np.abs(inp["u"]), S0=np.abs(s0))
+    err_o = wkv5_scaled_err(o.cpu().numpy(), o_ref, o_abs)
+    err_s = wkv5_scaled_err(s1.cpu().numpy(), s_ref, s_abs)
+    log(f"  err o={err_o:.3e} state={err_s:.3e}")
+    assert err_o <= WKV5_TOL and err_s <= WKV5_TOL
+
+
+def test_zero_and_vanishing_decays():
+    """w = 0 (acts as 2^-126) and w = 1e-30 on some channels, w = 1 on
+    others: blocks with exact diagonals; a ragged final chunk hands on its
+    state."""
+    torch, dev = torch_dev()
+    B, T, H = 1, 333, 2
+    inp = synth.wkv5_inputs(B, T, H, 64, seed=44)
+    w = inp["w"].copy()
+    w[:, ::3] = 0.0
+    w[:, 1::7] = 1e-30
+    w[1, 2::9] = 1.0
+    log("wkv5_forward with w = 0, 1e-30 and 1 channels")
+    o, s1 = rw.rwkv_wkv5_forward_state(_bits(inp, "r", np.s_[:]), _bits(inp, "k", np.s_[:]),
+                                       _bits(inp, "v", np.s_[:]), to_dev(w), to_dev(inp["u"]),
+                                       s_out=True)
+    torch.cuda.synchronize()
+    o_ref, s_ref = O.wkv5_recurrent(inp["r"], inp["k"], inp["v"], w, inp["u"])
+    o_abs, s_abs = O.wkv5_recurrent(np.abs(inp["r"]), np.abs(inp["k"]), np.abs(inp["v"]), w,
+                                    np.abs(inp["u"]))
+    err_o = wkv5_scaled_err(o.cpu().numpy(), o_ref, o_abs)
+    err_s = wkv5_scaled_err(s1.cpu().numpy(), s_ref, s_abs)
+    log(f"  err o={err_o:.3e} state={err_s:.3e}")
+    assert err_o <= WKV5_TOL and err_s <= WKV5_TOL
+    assert np.all(np.isfinite(o.cpu().numpy()))
+
+
+def test_wide_decay_workload_sampled_heads():
+    """B=4 T=4096 H=32 with omega ~ U(-6, 2) on the GPU (the timed wide-decay
+    workload); the oracle runs 2 batches x 4 heads."""
+    cfg = synth.CFG_WKV5_EAGLE_WIDE
+    log(f"wkv5_forward {cfg.name} (oracle on sampled heads)")
+    inp = synth.wkv5_inputs_for(cfg)
+    o = gpu_wkv5(inp)
+    bs, hs = np.array([1, 2]), np.array([3, 12, 25, 30])
+    o_ref, o_abs = oracle_wkv5(inp, bs, hs)
+    err = wkv5_scaled_err(o[bs][:, :, hs], o_ref, o_abs)
+    log(f"  err={err:.3e}")
+    assert err <= WKV5_TOL
+    assert np.all(np.isfinite(o))
