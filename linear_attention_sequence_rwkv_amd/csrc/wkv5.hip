@@ -334,10 +334,6 @@ __global__ __launch_bounds__(256, 2) void wkv5_fwd_chunked(
     const float l2w = head_decay(w, h, &s.mode);
     s.l2w[tid] = l2w;
     s.w32[tid] = exp2f(32.f * l2w);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) s.w16m[m][tid] = exp2f(float(16 * m) * l2w);
-#pragma unroll
-    for (int d = 0; d < 15; ++d) s.wpow[d][tid] = exp2f(float(d) * l2w);
   }
   __syncthreads();
   const int mode = __builtin_amdgcn_readfirstlane(s.mode);
@@ -347,6 +343,18 @@ __global__ __launch_bounds__(256, 2) void wkv5_fwd_chunked(
     return;
   }
   const bool blocks = (mode & kModeBlocks) != 0;
+  if (blocks) {
+    // the block path's per-channel power tables (filling them on every head
+    // cost the mid-chunk path 3 us of the 4x4096x32x64 call)
+    if (tid < kD) {
+      const float l2w = s.l2w[tid];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) s.w16m[m][tid] = exp2f(float(16 * m) * l2w);
+#pragma unroll
+      for (int d = 0; d < 15; ++d) s.wpow[d][tid] = exp2f(float(d) * l2w);
+    }
+    __syncthreads();  // uniform: the whole workgroup is on one path
+  }
 
   const int row = lane & 15;         // MFMA operand row/column of this lane
   const int kq = 8 * (lane >> 4);    // first K element of this lane in a 32-wide step
@@ -414,9 +422,9 @@ __global__ __launch_bounds__(256, 2) void wkv5_fwd_chunked(
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(oacc[jb][rr]), ro, ooff[rr],
                                               64 * jb, kStoreAux);
   };
+  // Each path's fixed factors come before the first chunk's loads (issued
+  // first, they cost the mid-chunk path 2.3 us of the 4x4096x32x64 call).
   ChunkRegs cur, nxt;
-  load_chunk<DV>(cur, c_begin * kL, T, H, b, h, j0, r, k, v);
-
   if (blocks) {
     const bool exact_diag = (mode & kModeExactDiag) != 0;
     BlockStageConsts f;
@@ -432,6 +440,7 @@ __global__ __launch_bounds__(256, 2) void wkv5_fwd_chunked(
         fq[8 * ks + e] = exp2f(float(row) * l2);
         fdq[8 * ks + e] = exp2f(float(row - 8) * l2);
       }
+    load_chunk<DV>(cur, c_begin * kL, T, H, b, h, j0, r, k, v);
     for (int c = c_begin; c < c_end; ++c) {
       const int t0 = c * kL;
       const int n_last = (s_out && c == n_chunks - 1 && T - t0 < kL) ? T - t0 : 0;
@@ -542,6 +551,7 @@ __global__ __launch_bounds__(256, 2) void wkv5_fwd_chunked(
   } else {
     StageConsts f;
     stage_consts(f, s);
+    load_chunk<DV>(cur, c_begin * kL, T, H, b, h, j0, r, k, v);
     for (int c = c_begin; c < c_end; ++c) {
       const int t0 = c * kL;
       const int n_last = (s_out && c == n_chunks - 1 && T - t0 < kL) ? T - t0 : 0;
