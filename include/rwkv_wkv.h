@@ -149,7 +149,9 @@ int rwkv_wkv4_forward(int64_t B, int64_t T, int64_t C,
  * plan overrides) return RWKV_ERR_WORKSPACE and enqueue nothing.  The array
  * is zero-filled by a kernel on `stream` at the first call on each device
  * (and again every 2^30 calls); it keeps the last call's contents, which the
- * next call needs no clearing of.  Every call on one GPU shares the array:
+ * next call needs no clearing of.  Make the first call on each device
+ * outside graph capture (it also looks up the array's device address); a
+ * fill recorded into a graph is repeated at the next call made outside one.  Every call on one GPU shares the array:
  * calls that overlap in time on that GPU (other streams, other threads)
  * race and are not allowed.  The array's error word is not exposed; a tile
  * that cannot run still writes NaN over its rows, as in rwkv_wkv4_forward.

@@ -60,3 +60,42 @@ def test_noalloc_rejects_a_shape_beyond_its_array():
     st = lib.rwkv_wkv4_forward_noalloc(1, 65536, 5120, P, P, P, P, P,
                                        ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
     assert st == WORKSPACE
+
+
+def test_noalloc_replayed_from_a_captured_graph():
+    """What the entry point is for: calls captured in a HIP graph (no
+    allocation inside the capture) and replayed several times, with eager
+    calls of other shapes on the same array in between.  Every replay equals
+    the workspace forward on the replay's inputs, bit for bit."""
+    torch, dev = torch_dev()
+    lib = rw.load_library()
+    shapes = [(2, 700, 128), (1, 1300, 192)]
+    other = (3, 400, 320)
+    bufs = [{n: torch.from_numpy(synth.wkv4_inputs(*shp, seed=800 + i)[n]).to(dev)
+             for n in ("w", "u", "k", "v")} for i, shp in enumerate(shapes)]
+    ys = [torch.empty_like(bf["k"]) for bf in bufs]
+    o = {n: torch.from_numpy(x).to(dev)
+         for n, x in synth.wkv4_inputs(*other, seed=810).items()}
+    y_other = torch.empty_like(o["k"])
+    cur = torch.cuda.current_stream(dev)
+    assert _call_noalloc(lib, o, y_other, cur) == 0  # set-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(cur)
+    with torch.cuda.graph(graph, stream=side):
+        for bf, y in zip(bufs, ys):
+            assert _call_noalloc(lib, bf, y, torch.cuda.current_stream(dev)) == 0
+    torch.cuda.synchronize()
+    for rnd in range(4):
+        for i, (bf, shp) in enumerate(zip(bufs, shapes)):
+            fresh = synth.wkv4_inputs(*shp, seed=820 + 10 * rnd + i)
+            for n in ("w", "u", "k", "v"):
+                bf[n].copy_(torch.from_numpy(fresh[n]))
+        assert _call_noalloc(lib, o, y_other, cur) == 0  # eager, another shape, same array
+        log(f"wkv4_forward_noalloc graph replay {rnd}")
+        graph.replay()
+        refs = [rw.rwkv_wkv4_forward(bf["w"], bf["u"], bf["k"], bf["v"]) for bf in bufs]
+        torch.cuda.synchronize()
+        for y, y_ref in zip(ys, refs):
+            assert torch.equal(y, y_ref), rnd
