@@ -183,6 +183,35 @@ def _check_wkv4_output(torch, rw, dev_inputs, last, ws):
     assert rw.rwkv_wkv4_workspace_error(ws) == 0
 
 
+def copy_peak_gbps(torch, dev_inputs):
+    """GB/s of the copy-peak kernel (y = a + b, 12 B per element, the RWKV-4
+    forward's traffic with no dependencies; libwkv_copy_peak.so) over the
+    same k, v, y buffers, rotated as the forward rotates them: >= 100 ms per
+    repeat, median of 5.  None when that library has not been built."""
+    path = os.path.join(ROOT, "linear_attention_sequence_rwkv_amd", "libwkv_copy_peak.so")
+    if not os.path.exists(path):
+        log("bench: libwkv_copy_peak.so missing (build() makes it); no copy peak")
+        return None
+    lib = ctypes.CDLL(path)
+    lib.wkv_bench_add_copy.restype = ctypes.c_int
+    lib.wkv_bench_add_copy.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]
+    _, _, ks, vs, ys = dev_inputs
+    rot = len(ks)
+    n = ks[0].numel()
+    stream = torch.cuda.current_stream(ks[0].device)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+
+    def launch(i):
+        j = i % rot
+        if lib.wkv_bench_add_copy(_ptr(ks[j]), _ptr(vs[j]), _ptr(ys[j]), n, sh) != 0:
+            raise RuntimeError("wkv_bench_add_copy failed")
+
+    for i in range(3):
+        launch(i)
+    ms, _, _ = measure(torch, stream, launch)
+    return 12 * n / (ms * 1e-3) / 1e9
+
+
 def wkv4_roofline(cfg, kern_ms, profile):
     nbytes = 12 * cfg.B * cfg.T * cfg.C
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
@@ -581,6 +610,7 @@ def main(argv=None):
             log(f"bench: {c2.name} rotating {rot} cop{'ies' if rot > 1 else 'y'}")
             d2 = wkv4_device_copies(torch, i2, rot)
             ms2, n2, per2 = bench_wkv4_secondary(torch, rw, c2, d2)
+            cp2 = copy_peak_gbps(torch, d2) if rot > 1 else None
             del d2
             name = c2.name if rot > 1 else c2.name + "_hot"
             g = 12 * c2.B * c2.T * c2.C / (ms2 * 1e-3) / 1e9
@@ -590,6 +620,9 @@ def main(argv=None):
                          "repeats_ms": [round(x, 5) for x in per2]}
             if rot > 1:
                 sec[name]["roofline"] = wkv4_roofline(c2, ms2, "wkv4_fwd_tiled_B8_T1024_C768.md")
+                if cp2 is not None:
+                    sec[name]["copy_peak_GBps"] = round(cp2, 1)
+                    sec[name]["pct_of_copy_peak"] = round(100 * g / cp2, 2)
     if "decode" in want or "decode-graph" in want:
         dc = synth.CFG_WKV4_DECODE
         log(f"bench: {dc.name}")
@@ -652,6 +685,8 @@ def main(argv=None):
 
     log(f"bench: {cfg.name} steps={args.steps} warmup={args.warmup}")
     ms = bench_wkv4_headline(torch, rw, cfg, dev_inputs, args.steps, args.warmup)
+    log("bench: copy peak on the same buffers")
+    copy_peak = copy_peak_gbps(torch, dev_inputs)
     del dev_inputs
     torch.cuda.empty_cache()
     nbytes = 12 * cfg.B * cfg.T * cfg.C
@@ -673,7 +708,10 @@ def main(argv=None):
                    "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
                    "gelem_per_s": round(cfg.B * cfg.T * cfg.C / (ms * 1e-3) / 1e9, 2),
                    "bytes_per_elem": 12, "rotated_copies": 1,
-                   "after_secondary_workloads": bool(sec)},
+                   "after_secondary_workloads": bool(sec),
+                   "copy_peak_GBps": None if copy_peak is None else round(copy_peak, 1),
+                   "pct_of_copy_peak": (None if copy_peak is None
+                                        else round(100 * value / copy_peak, 2))},
         # one kernel per step, launched back to back: the step time is the
         # kernel's mean duration plus the sub-microsecond launch gap
         "roofline": wkv4_roofline(cfg, ms, "wkv4_fwd_tiled_B1_T65536_C5120.md"),

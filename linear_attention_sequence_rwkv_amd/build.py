@@ -3,8 +3,10 @@
     python -m linear_attention_sequence_rwkv_amd.build
 
 Each source under csrc/ is compiled by hipcc into _build/ in parallel and
-linked into linear_attention_sequence_rwkv_amd/librwkv_wkv.so.  Every call
-recompiles (the build is a few seconds per file).
+linked into linear_attention_sequence_rwkv_amd/librwkv_wkv.so.  The
+benchmark's copy-peak kernel (benchsrc/copy_peak.hip) becomes a library of
+its own, libwkv_copy_peak.so, next to it.  Every call recompiles (the build
+is a few seconds per file).
 """
 from __future__ import annotations
 
@@ -21,6 +23,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "librwkv_wkv.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+COPY_PEAK_SRC = os.path.join(PKG, "benchsrc", "copy_peak.hip")
+COPY_PEAK_PATH = os.path.join(PKG, "libwkv_copy_peak.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -66,9 +70,19 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB_PATH)
+    _link_one(hipcc, _compile(hipcc, COPY_PEAK_SRC, extra), COPY_PEAK_PATH)
     if verbose:
-        print(f"built {LIB_PATH} from {len(srcs)} sources")
+        print(f"built {LIB_PATH} from {len(srcs)} sources, and {COPY_PEAK_PATH}")
     return LIB_PATH
+
+
+def _link_one(hipcc: str, obj: str, path: str) -> None:
+    tmp = path + ".tmp"
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, path)
 
 
 if __name__ == "__main__":
