@@ -112,6 +112,35 @@ def test_identity_and_shift_maps_bit_exact():
         assert np.array_equal(y[:, 1:], inp["v"][:, :-1])
 
 
+def test_identity_and_shift_maps_at_the_longest_sequence():
+    """The longest sequence the forward accepts, T = 2^24 - 64 (its decay
+    count is a float), with C = 128: 131,072 tiles per channel block, two
+    blocks per workgroup, claimed tiles.  Both maps hold at any length, so
+    the 8.6 GB outputs are checked whole, on the GPU: u = +100 gives y == v,
+    w = 100 with u = -100 gives y[t] == v[t-1]."""
+    torch, dev = torch_dev()
+    B, T, C = 1, (1 << 24) - 64, 128
+    log(f"wkv4_forward identity/shift maps at B={B} T={T} C={C}")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    k = torch.randn((B, T, C), generator=gen, device=dev, dtype=torch.float32)
+    v = torch.randn((B, T, C), generator=gen, device=dev, dtype=torch.float32)
+    w = torch.rand((C,), generator=gen, device=dev, dtype=torch.float32) * 2.0
+    y = torch.empty_like(k)
+    rw.rwkv_wkv4_forward(w, torch.full((C,), 100.0, device=dev), k, v, y=y)
+    torch.cuda.synchronize()
+    assert torch.equal(y, v)
+    rw.rwkv_wkv4_forward(torch.full((C,), 100.0, device=dev), torch.full((C,), -100.0, device=dev),
+                         k, v, y=y)
+    torch.cuda.synchronize()
+    assert torch.equal(y[:, 0], v[:, 0])
+    assert torch.equal(y[:, 1:], v[:, :-1])
+    ws = rw.default_workspace("wkv4", dev)
+    assert rw.rwkv_wkv4_workspace_error(ws) == 0
+    del k, v, y
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("shift", [-80.0, 80.0])
 def test_key_shift_stability(shift):
     B, T, C = 1, 3000, 128
