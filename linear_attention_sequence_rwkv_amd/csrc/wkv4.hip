@@ -546,7 +546,7 @@ int64_t device_capacity(const void* kern, int block) {
     int64_t n;
   };
   static std::mutex mu;
-  static Entry cache[kMaxDev][16] = {};
+  static Entry cache[kMaxDev][32] = {};  // more than the kernels a process can launch
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
   std::lock_guard<std::mutex> lock(mu);
@@ -612,6 +612,17 @@ bool wkv4_plan_fixed(int64_t B, int64_t T, int64_t C, int cpl, int L, int NW, Wk
   return true;
 }
 
+int wkv4_grouped_cb(int64_t B, int64_t T, int64_t C) {
+  // Grids far beyond what the device holds at once (B=1 T=65536 C=5120:
+  // 40,960 tiles) group two adjacent channel blocks per workgroup: the rows
+  // then come in 512-byte pieces, which HBM serves faster (B=1 T=65536
+  // C=5120: 748 -> 718 us; a copy through the same pattern 703 -> 674 us).
+  // Grids the device holds at once run faster with one block per workgroup
+  // (8x1024x768: 16.1 against 17.4 us).
+  const int64_t n_cblk = (C + 63) / 64;
+  return n_cblk % 2 == 0 && B * n_cblk * ((T + 127) / 128) >= kGroupedMinTiles ? 2 : 1;
+}
+
 bool wkv4_plan(int64_t B, int64_t T, int64_t C, Wkv4Plan* plan) {
   // One channel per lane, 32 tokens per wave, 4 waves per tile: about 116
   // VGPRs (4 waves per SIMD).  Measured faster than wider vector loads with
@@ -621,14 +632,7 @@ bool wkv4_plan(int64_t B, int64_t T, int64_t C, Wkv4Plan* plan) {
     L = 64;
     NW = 1;
   }
-  // Grids far beyond what the device holds at once (B=1 T=65536 C=5120:
-  // 40,960 tiles) group two adjacent channel blocks per workgroup: the rows
-  // then come in 512-byte pieces, which HBM serves faster (B=1 T=65536
-  // C=5120: 748 -> 718 us; a copy through the same pattern 703 -> 674 us).
-  // Grids the device holds at once run faster with one block per workgroup
-  // (8x1024x768: 16.1 against 17.4 us).
-  const int64_t n_cblk = (C + 63) / 64;
-  if (L == 32 && n_cblk % 2 == 0 && B * n_cblk * ((T + 127) / 128) >= kGroupedMinTiles) cb = 2;
+  if (L == 32) cb = wkv4_grouped_cb(B, T, C);
   // An override applies where its channel width divides C and its channel
   // blocks per workgroup divide the blocks of a sequence.
   if (const int code = tuning(kTuneWkv4Tile)) {
@@ -652,42 +656,52 @@ bool wkv4_variant_exists(int code) {
   return false;
 }
 
-hipError_t wkv4_prefix_launch(const Wkv4Plan& pl, int64_t T, int64_t C, const float* w,
-                              const float* u, const float* k, const float* v, void* ws,
-                              void* mids, hipStream_t stream) {
-  if (pl.cpl != 1 || pl.L != 32 || pl.NW != 4) return hipErrorInvalidValue;
+namespace {
+
+// The prefix pass (EMIT = false) or the training forward (TAPE = true) of
+// the backward's plan: 1 channel per lane, 32 tokens x 4 waves, CB channel
+// blocks per workgroup.
+template <bool EMIT, bool TAPE, int CB>
+hipError_t launch_prefix_like(const Wkv4Plan& pl, int64_t T, int64_t C, const float* w,
+                              const float* u, const float* k, const float* v, float* y,
+                              void* ws, void* mids, hipStream_t stream) {
   char* base = static_cast<char*>(ws);
   uint32_t* hdr = reinterpret_cast<uint32_t*>(base);
   uint64_t* counters = reinterpret_cast<uint64_t*>(base + kWkv4HeaderBytes);
   uint64_t* slots = reinterpret_cast<uint64_t*>(base + pl.slots_offset);
-  const int64_t grid = pl.n_tiles * pl.groups;
+  const int64_t grid = pl.n_tiles * pl.groups / CB;
   const StateIO none{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
-  const void* kern = reinterpret_cast<const void*>(&wkv4_fwd_tiled<1, 32, 4, false>);
-  const int in_order = grid <= resident_workgroups(kern, 256) ? 1 : 0;
-  hipLaunchKernelGGL((wkv4_fwd_tiled<1, 32, 4, false>), dim3(unsigned(grid)), dim3(256), 0,
-                     stream, int(T), int(C), int(pl.n_cblk), int(pl.groups), int(pl.n_tiles),
-                     in_order, w, u, k, v, nullptr, hdr, counters, slots, none,
+  const void* kern = reinterpret_cast<const void*>(&wkv4_fwd_tiled<1, 32, 4, EMIT, TAPE, CB>);
+  const int in_order = grid <= resident_workgroups(kern, 256 * CB) ? 1 : 0;
+  hipLaunchKernelGGL((wkv4_fwd_tiled<1, 32, 4, EMIT, TAPE, CB>), dim3(unsigned(grid)),
+                     dim3(256 * CB), 0, stream, int(T), int(C), int(pl.n_cblk), int(pl.groups),
+                     int(pl.n_tiles), in_order, w, u, k, v, y, hdr, counters, slots, none,
                      static_cast<uint64_t*>(mids));
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t wkv4_prefix_launch(const Wkv4Plan& pl, int64_t T, int64_t C, const float* w,
+                              const float* u, const float* k, const float* v, void* ws,
+                              void* mids, hipStream_t stream) {
+  if (pl.cpl != 1 || pl.L != 32 || pl.NW != 4) return hipErrorInvalidValue;
+  if (pl.cb == 2)
+    return launch_prefix_like<false, false, 2>(pl, T, C, w, u, k, v, nullptr, ws, mids, stream);
+  if (pl.cb == 1)
+    return launch_prefix_like<false, false, 1>(pl, T, C, w, u, k, v, nullptr, ws, mids, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t wkv4_forward_tape_launch(const Wkv4Plan& pl, int64_t T, int64_t C, const float* w,
                                    const float* u, const float* k, const float* v, float* y,
                                    void* ws, void* mids, hipStream_t stream) {
   if (pl.cpl != 1 || pl.L != 32 || pl.NW != 4) return hipErrorInvalidValue;
-  char* base = static_cast<char*>(ws);
-  uint32_t* hdr = reinterpret_cast<uint32_t*>(base);
-  uint64_t* counters = reinterpret_cast<uint64_t*>(base + kWkv4HeaderBytes);
-  uint64_t* slots = reinterpret_cast<uint64_t*>(base + pl.slots_offset);
-  const int64_t grid = pl.n_tiles * pl.groups;
-  const StateIO none{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
-  const void* kern = reinterpret_cast<const void*>(&wkv4_fwd_tiled<1, 32, 4, true, true>);
-  const int in_order = grid <= resident_workgroups(kern, 256) ? 1 : 0;
-  hipLaunchKernelGGL((wkv4_fwd_tiled<1, 32, 4, true, true>), dim3(unsigned(grid)), dim3(256), 0,
-                     stream, int(T), int(C), int(pl.n_cblk), int(pl.groups), int(pl.n_tiles),
-                     in_order, w, u, k, v, y, hdr, counters, slots, none,
-                     static_cast<uint64_t*>(mids));
-  return hipGetLastError();
+  if (pl.cb == 2)
+    return launch_prefix_like<true, true, 2>(pl, T, C, w, u, k, v, y, ws, mids, stream);
+  if (pl.cb == 1)
+    return launch_prefix_like<true, true, 1>(pl, T, C, w, u, k, v, y, ws, mids, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t wkv4_forward_launch(const Wkv4Plan& pl, int64_t B, int64_t T, int64_t C,

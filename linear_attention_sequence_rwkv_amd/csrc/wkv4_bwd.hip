@@ -439,6 +439,11 @@ bool wkv4_backward_plan(int64_t B, int64_t T, int64_t C, Wkv4BwdPlan* plan) {
   // reverse pass holds six values per token and lane, so its tiles are half
   // that long and read the prefix pass's mid-tile histories too.
   if (!wkv4_plan_fixed(B, T, C, 1, 32, 4, &p.fwd)) return false;
+  // Two channel blocks per workgroup on grids far beyond the device's
+  // capacity, as the forward (the prefix pass and the training forward share
+  // it; the reverse pass claims through every block's counter, raising any
+  // the prefix pass left to its own tag first).
+  p.fwd.cb = wkv4_grouped_cb(B, T, C);
   const int64_t groups = p.fwd.groups;
   p.rev_tiles = (T + kBwdL * kBwdNW - 1) / (kBwdL * kBwdNW);
   if (p.rev_tiles * groups >= (int64_t(1) << 31)) return false;

@@ -63,6 +63,8 @@ constexpr size_t kWkv4CounterStride = 128;  // one counter per 128-byte line
 bool wkv4_plan(int64_t B, int64_t T, int64_t C, Wkv4Plan* plan);
 // The same for a given tile shape.
 bool wkv4_plan_fixed(int64_t B, int64_t T, int64_t C, int cpl, int L, int NW, Wkv4Plan* plan);
+// Channel blocks per workgroup (1 or 2) for the 1 x 32 x 4 tiles of a shape.
+int wkv4_grouped_cb(int64_t B, int64_t T, int64_t C);
 
 // The forward scan without output rows: publishes every tile's inclusive
 // history in the workspace (plan: one channel per lane, 32 x 4 tiles) and,

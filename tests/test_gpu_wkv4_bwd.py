@@ -169,14 +169,15 @@ def test_claimed_and_in_order_prefix_passes_share_a_workspace():
 
 
 @pytest.mark.parametrize("shape", [(8, 1024, 768), (3, 1100, 200), (2, 300, 96), (1, 64, 64),
-                                   (1, 16384, 256)])
+                                   (1, 16384, 256), (1, 65536, 1024)])
 def test_training_pair_matches_the_separate_calls(shape):
     """rwkv_wkv4_forward_train leaves the prefix pass's tile histories in a
     backward workspace and rwkv_wkv4_backward_after_forward reuses them: y is
     within the bound of the oracle (and equal to rwkv_wkv4_forward's where both
     use the same tiles), and the gradients equal rwkv_wkv4_backward's bit for
     bit; a pair of another shape on another workspace in between changes
-    nothing."""
+    nothing.  The last shape (8192 tiles of 128 x 64) runs the prefix pass and
+    the training forward with two channel blocks per workgroup."""
     torch, dev = torch_dev()
     B, T, C = shape
     inp = synth.wkv4_backward_inputs(B, T, C, seed=303)
