@@ -282,12 +282,16 @@ int rwkv_wkv4_step(int64_t B, int64_t C,
  *   s_{t+1}[i][j] = w[h,i] s_t[i][j] + k[b,t,h,i] v[b,t,h,j]
  *
  *   r, k, v  [B,T,H,D]  bfloat16 bit patterns (uint16)
- *   w        [H,D]      float32 decay factor in (0, 1]
+ *   w        [H,D]      float32 decay factor in [0, 1] (the section's
+ *                       exp(-exp(omega)) lies in (0, 1)); factors below
+ *                       2^-126 act as 2^-126.  A head with some w outside
+ *                       [0, 1], or NaN, is still computed, by the exact
+ *                       float32 recurrence (serially over T: slow).
  *   u        [H,D]      float32 current-token bonus
  *   o        [B,T,H,D]  float32 output
  *   D must be 64 and H < 65536 (RWKV_ERR_UNSUPPORTED otherwise).
  *   ws, ws_bytes: at least rwkv_wkv5_forward_workspace(B,T,H,D) bytes (may
- *   be 0, then ws may be NULL).
+ *   be 0, then ws may be NULL); no zero-fill needed.
  * Accuracy: max |o - exact| <= 2e-2 * o_abs, where o_abs is the same sum
  * over |r|, |k|, |v|, |u| (bf16 products, float32 accumulation).
  * ---------------------------------------------------------------------- */
