@@ -304,7 +304,7 @@ __global__ __launch_bounds__(256, 2) void wkv6_fwd_chunked(
     int T, int H, int BH, const uint16_t* __restrict__ r, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ w,
     const float* __restrict__ u, float* __restrict__ o, const float* s_in, float* s_out,
-    int seg_chunks, const float* __restrict__ seg_state) {
+    int seg_chunks, int pieces, const float* __restrict__ seg_state) {
   constexpr int NS = kD / DV;
   constexpr int NJB = DV / 16;
   __shared__ LdsF<DV> s;
@@ -333,12 +333,13 @@ __global__ __launch_bounds__(256, 2) void wkv6_fwd_chunked(
     for (int rr = 0; rr < 4; ++rr)
       sacc[jb][rr] = s_in ? s_in[sbase + size_t(16 * q + crow + rr) * kD + j0 + 16 * jb + row]
                           : 0.f;
-  // A later segment starts from the earlier segments' local end states:
-  // S <- diag(2^L_seg) S + S_seg, L_seg the segment's summed log2 decay.
+  // A later segment starts from the local end states of the earlier
+  // segments' pieces (`pieces` per segment), in order:
+  // S <- diag(2^L_piece) S + S_piece, L_piece the piece's summed log2 decay.
   if (seg > 0) {
-    const int nseg = int(gridDim.x) / per_seg;
-    for (int sg = 0; sg < seg; ++sg) {
-      const float* src = seg_state + (size_t(bh) * (nseg - 1) + sg) * (kD * kD + kD);
+    const int npieces = (int(gridDim.x) / per_seg - 1) * pieces;
+    for (int sg = 0; sg < seg * pieces; ++sg) {
+      const float* src = seg_state + (size_t(bh) * npieces + sg) * (kD * kD + kD);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int i = 16 * q + crow + rr;
@@ -541,7 +542,7 @@ __global__ __launch_bounds__(256, 2) void wkv6_fwd_chunked(
 // chunk's k, v and decays load while this one multiplies.
 template <int DV>
 __global__ __launch_bounds__(256) void wkv6_seg_state(int T, int H, int BH, int seg_chunks,
-                                                      int nseg, const uint16_t* __restrict__ k,
+                                                      int npieces, const uint16_t* __restrict__ k,
                                                       const uint16_t* __restrict__ v,
                                                       const float* __restrict__ w,
                                                       float* __restrict__ seg_state) {
@@ -628,7 +629,7 @@ __global__ __launch_bounds__(256) void wkv6_seg_state(int T, int H, int BH, int 
     cur = nxt;
     wc = wn;
   }
-  float* dst = seg_state + (size_t(bh) * (nseg - 1) + seg) * (kD * kD + kD);
+  float* dst = seg_state + (size_t(bh) * npieces + seg) * (kD * kD + kD);
 #pragma unroll
   for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
@@ -640,6 +641,12 @@ __global__ __launch_bounds__(256) void wkv6_seg_state(int T, int H, int BH, int 
 // Time segments per head (as for Eagle): about two workgroups per CU over the
 // launch, segments of at least four chunks; kTuneWkv6Segs overrides.
 constexpr int64_t kTargetWorkgroups = 512;
+
+// Pieces per segment for the segment pass: halves of segments of 8 or more
+// chunks, each with its local end state and summed decay, folded in order
+// (4x4096x32x64: 151.4 -> 149.6 us; four pieces 152.2).  The Eagle segment
+// pass, with less work per chunk, measured slower split.
+int wkv6_pieces(int64_t seg_chunks) { return seg_chunks % 2 == 0 && seg_chunks >= 8 ? 2 : 1; }
 
 int wkv6_dv() { return tuning(kTuneWkv6Dv) == 32 ? 32 : 64; }
 
@@ -661,15 +668,18 @@ hipError_t launch_wkv6(int64_t T, int64_t H, int64_t BH, const uint16_t* r, cons
   const int nseg = wkv6_segments(BH, T, NS);
   const int64_t n_chunks = (T + kL - 1) / kL;
   const int seg_chunks = int((n_chunks + nseg - 1) / nseg);
+  const int pieces = wkv6_pieces(seg_chunks);
+  const int npieces = (nseg - 1) * pieces;
   const unsigned per_seg = unsigned((BH + 7) / 8 * 8 * NS);
   if (nseg > 1) {
-    hipLaunchKernelGGL(wkv6_seg_state<DV>, dim3(per_seg * unsigned(nseg - 1)), dim3(256), 0,
-                       stream, int(T), int(H), int(BH), seg_chunks, nseg, k, v, w, seg_state);
+    hipLaunchKernelGGL(wkv6_seg_state<DV>, dim3(per_seg * unsigned(npieces)), dim3(256), 0,
+                       stream, int(T), int(H), int(BH), seg_chunks / pieces, npieces, k, v, w,
+                       seg_state);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(wkv6_fwd_chunked<DV>, dim3(per_seg * unsigned(nseg)), dim3(256), 0, stream,
-                     int(T), int(H), int(BH), r, k, v, w, u, o, s_in, s_out, seg_chunks,
+                     int(T), int(H), int(BH), r, k, v, w, u, o, s_in, s_out, seg_chunks, pieces,
                      seg_state);
   return hipGetLastError();
 }
@@ -678,7 +688,9 @@ hipError_t launch_wkv6(int64_t T, int64_t H, int64_t BH, const uint16_t* r, cons
 
 size_t wkv6_workspace_bytes(int64_t B, int64_t T, int64_t H) {
   const int nseg = wkv6_segments(B * H, T, kD / wkv6_dv());
-  return size_t(B * H) * size_t(nseg - 1) * (kD * kD + kD) * sizeof(float);
+  const int64_t n_chunks = (T + kL - 1) / kL;
+  const int pieces = wkv6_pieces((n_chunks + nseg - 1) / nseg);
+  return size_t(B * H) * size_t(nseg - 1) * size_t(pieces) * (kD * kD + kD) * sizeof(float);
 }
 
 hipError_t wkv6_forward_launch(int64_t B, int64_t T, int64_t H, const uint16_t* r,
