@@ -141,6 +141,34 @@ def test_identity_and_shift_maps_at_the_longest_sequence():
     torch.cuda.empty_cache()
 
 
+def test_widest_rows_sampled_channels():
+    """C = 2^22 + 37 channels (16 MB rows, a ragged last channel block): the
+    row offsets within a wave's 32 rows and the channel-block indices are at
+    their largest; 40 sampled channels, the last ones included, against the
+    oracle."""
+    torch, dev = torch_dev()
+    B, T, C = 1, 200, (1 << 22) + 37
+    log(f"wkv4_forward B={B} T={T} C={C}")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4321)
+    k = torch.randn((B, T, C), generator=gen, device=dev, dtype=torch.float32)
+    v = torch.randn((B, T, C), generator=gen, device=dev, dtype=torch.float32)
+    w = torch.exp(torch.rand((C,), generator=gen, device=dev) * 4.0 - 3.0)
+    u = torch.randn((C,), generator=gen, device=dev) * 0.5
+    y = rw.rwkv_wkv4_forward(w, u, k, v)
+    torch.cuda.synchronize()
+    ch = np.concatenate([np.arange(0, C, C // 32), np.arange(C - 8, C)])
+    cht = torch.from_numpy(ch).to(dev)
+    inp = {"w": w[cht].cpu().numpy(), "u": u[cht].cpu().numpy(),
+           "k": k[..., cht].cpu().numpy(), "v": v[..., cht].cpu().numpy()}
+    y_ref, S = oracle_forward(inp)
+    err = wkv4_scaled_err(y[..., cht].cpu().numpy(), y_ref, S)
+    log(f"  err={err:.3e} over {len(ch)} channels")
+    assert err <= WKV4_TOL
+    del k, v, y
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("shift", [-80.0, 80.0])
 def test_key_shift_stability(shift):
     B, T, C = 1, 3000, 128

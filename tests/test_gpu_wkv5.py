@@ -337,3 +337,30 @@ def test_wide_decay_workload_sampled_heads():
     log(f"  err={err:.3e}")
     assert err <= WKV5_TOL
     assert np.all(np.isfinite(o))
+
+def test_most_heads_sampled():
+    """H = 65535, the most the forward accepts (a chunk's rows of o span
+    64 x H x 64 floats, 1.07 GB, under the 2^31-byte buffer range), T = 70
+    (a ragged second chunk); six heads, the first and last included, against
+    the oracle."""
+    torch, dev = torch_dev()
+    B, T, H, D = 1, 70, 65535, 64
+    log(f"wkv5_forward B={B} T={T} H={H}")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77)
+    r, k, v = ((torch.randn((B, T, H, D), generator=gen, device=dev) / 8).to(torch.bfloat16)
+               for _ in range(3))
+    omega = torch.rand((H, D), generator=gen, device=dev) * 6.0 - 6.0
+    w = torch.exp(-torch.exp(omega))
+    u = torch.randn((H, D), generator=gen, device=dev) * 0.5
+    o = rw.rwkv_wkv5_forward(r, k, v, w, u)
+    torch.cuda.synchronize()
+    hs = torch.tensor([0, 1, 12345, 40000, H - 2, H - 1], device=dev)
+    f = lambda x: x[:, :, hs].float().cpu().numpy()  # noqa: E731
+    o_ref, _ = O.wkv5_recurrent(f(r), f(k), f(v), w[hs].cpu().numpy(), u[hs].cpu().numpy())
+    o_abs = O.wkv5_scale(f(r), f(k), f(v), w[hs].cpu().numpy(), u[hs].cpu().numpy())
+    err = wkv5_scaled_err(f(o), o_ref, o_abs)
+    log(f"  err={err:.3e} over {len(hs)} heads")
+    assert err <= WKV5_TOL
+    del r, k, v, o
+    torch.cuda.empty_cache()

@@ -198,3 +198,32 @@ def test_query_factor_across_a_deep_block_decay():
     err_blk = wkv5_scaled_err(o[:, 16:24], o_ref[:, 16:24], o_abs[:, 16:24])
     log(f"  err o={err_o:.3e} (tokens 16..23: {err_blk:.3e}) state={err_s:.3e}")
     assert err_o <= WKV5_TOL and err_s <= WKV5_TOL
+
+def test_most_heads_sampled():
+    """H = 65535, the most the forward accepts (a chunk's rows of o span
+    64 x H x 64 floats, 1.07 GB, under the 2^31-byte buffer range), T = 70
+    (a ragged second chunk); six heads, the first and last included, against
+    the oracle."""
+    torch, dev = torch_dev()
+    B, T, H, D = 1, 70, 65535, 64
+    log(f"wkv6_forward B={B} T={T} H={H}")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77)
+    r, k, v = ((torch.randn((B, T, H, D), generator=gen, device=dev) / 8).to(torch.bfloat16)
+               for _ in range(3))
+    omega = torch.rand((H, D), generator=gen, device=dev) * 6.0 - 6.0
+    w = torch.exp(-torch.exp(omega))
+    u = torch.randn((H, D), generator=gen, device=dev) * 0.5
+    wt = torch.exp(-torch.exp(omega[None, None] + torch.randn((B, T, H, D), generator=gen,
+                                                              device=dev) * 0.5))
+    o, _ = rw.rwkv_wkv6_forward(r, k, v, wt, u)
+    torch.cuda.synchronize()
+    hs = torch.tensor([0, 1, 12345, 40000, H - 2, H - 1], device=dev)
+    f = lambda x: x[:, :, hs].float().cpu().numpy()  # noqa: E731
+    o_ref, _ = O.wkv6_recurrent(f(r), f(k), f(v), f(wt), u[hs].cpu().numpy())
+    o_abs, _ = O.wkv6_scale(f(r), f(k), f(v), f(wt), u[hs].cpu().numpy())
+    err = wkv5_scaled_err(f(o), o_ref, o_abs)
+    log(f"  err={err:.3e} over {len(hs)} heads")
+    assert err <= WKV5_TOL
+    del r, k, v, o
+    torch.cuda.empty_cache()
