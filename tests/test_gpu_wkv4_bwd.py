@@ -209,3 +209,33 @@ def test_training_pair_matches_the_separate_calls(shape):
             assert np.array_equal(y, y_plain)
         for a, b in zip(ref_grads, grads):
             assert torch.equal(a, b.cpu())
+
+
+def test_identity_map_gradients_at_the_longest_sequence():
+    """The backward at the longest sequence the forward accepts (T = 2^24 - 64,
+    C = 128: 262,144 reverse tiles per block).  With u = +100 every output is
+    its own token's v (p_tt = 1, every other weight below e^-90), so
+    gv = gy and gk, gw, gu vanish; checked over the whole 8.6 GB gradients on
+    the GPU."""
+    torch, dev = torch_dev()
+    B, T, C = 1, (1 << 24) - 64, 128
+    log(f"wkv4_backward identity map at B={B} T={T} C={C}")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2468)
+    k = torch.randn((B, T, C), generator=gen, device=dev, dtype=torch.float32)
+    v = torch.randn((B, T, C), generator=gen, device=dev, dtype=torch.float32)
+    gy = torch.randn((B, T, C), generator=gen, device=dev, dtype=torch.float32)
+    w = torch.rand((C,), generator=gen, device=dev, dtype=torch.float32) * 2.0
+    u = torch.full((C,), 100.0, device=dev)
+    gw, gu, gk, gv = rw.rwkv_wkv4_backward(w, u, k, v, gy)
+    torch.cuda.synchronize()
+    rel = ((gv - gy).abs() / gy.abs().clamp_min(1e-30)).max().item()
+    log(f"  max |gv - gy| / |gy| = {rel:.2e}, max |gk| = {gk.abs().max().item():.2e}, "
+        f"max |gw| = {gw.abs().max().item():.2e}, max |gu| = {gu.abs().max().item():.2e}")
+    assert rel <= 1e-6
+    assert gk.abs().max().item() <= 1e-5
+    assert gw.abs().max().item() <= 1e-4 and gu.abs().max().item() <= 1e-4
+    ws = rw.default_workspace("wkv4_bwd", dev)
+    assert rw.rwkv_wkv4_workspace_error(ws) == 0
+    del k, v, gy, gk, gv
+    torch.cuda.empty_cache()
