@@ -566,10 +566,11 @@ def main(argv=None):
                     help="channels of the headline workload the oracle sample covers")
     ap.add_argument("--secondary",
                     default="169m,169m-hot,decode,decode-graph,eagle,eagle-wide,eagle-decode,"
-                            "finch,backward,backward-long,train",
+                            "finch,backward,backward-long,train,long-steady",
                     help="comma list of secondary workloads: 169m, 169m-hot, decode, "
                          "decode-graph, eagle, eagle-wide, eagle-decode, finch, backward, "
-                         "backward-long, train")
+                         "backward-long, train, long-steady (the headline workload "
+                         "itself, run last)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -690,6 +691,17 @@ def main(argv=None):
                      "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
                      "bytes_per_elem": 32}
     backward("backward-long", synth.CFG_WKV4_LONG)
+    if "long-steady" in want:
+        # The headline workload under the secondary protocol, last before the
+        # headline: its steady-state rate, and K timed steps that start on a
+        # device already running this kernel.
+        name = cfg.name + "_steady"
+        log(f"bench: {name}")
+        ms3, n3, per3 = bench_wkv4_secondary(torch, rw, cfg, dev_inputs)
+        sec[name] = {"ms": round(ms3, 5),
+                     "GBps": round(12 * cfg.B * cfg.T * cfg.C / (ms3 * 1e-3) / 1e9, 1),
+                     "rotated_copies": 1, "calls_per_repeat": n3,
+                     "repeats_ms": [round(x, 5) for x in per3]}
 
     log(f"bench: {cfg.name} steps={args.steps} warmup={args.warmup}")
     ms = bench_wkv4_headline(torch, rw, cfg, dev_inputs, args.steps, args.warmup)
