@@ -36,12 +36,14 @@ constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit access, gfx9 family
 constexpr int kLoadAux = 0;
 constexpr int kStoreAux = 2;            // non-temporal
 
-// Resource over rows t0 .. t0 + n_tok - 1 of head h (element size `esz`).
+// Resource over rows t0 .. t0 + n_tok - 1 of head h (element size `esz`);
+// with live = false it spans nothing, so every access through it is dropped
+// (reads give zero) without touching memory.
 __device__ __forceinline__ Rsrc chunk_rsrc(const void* base, int t0, int T, int H, int b, int h,
-                                           int esz) {
+                                           int esz, bool live = true) {
   const size_t e0 = ((size_t(b) * T + t0) * H + h) * kD;
   const int n_tok = min(kL, T - t0);
-  const uint32_t bytes = uint32_t(((n_tok - 1) * H + 1) * kD * esz);
+  const uint32_t bytes = live ? uint32_t(((n_tok - 1) * H + 1) * kD * esz) : 0u;
   return __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char*>(static_cast<const char*>(base)) + e0 * esz, 0, int(bytes), kRsrcWord3);
 }
@@ -59,20 +61,21 @@ struct ChunkRegs {
   uint4 r0, r1, k0, k1, v0, v1;  // v1: the second half of 16 value dims (DV = 64)
 };
 
-// WITH_R = false (segment states) skips r.
+// WITH_R = false (segment states) skips r.  live = false issues the same
+// loads through empty resources (zeros, no memory traffic).
 template <int DV, bool WITH_R = true>
 __device__ __forceinline__ void load_chunk(ChunkRegs& x, int t0, int T, int H, int b, int h,
                                            int j0, const uint16_t* __restrict__ r,
                                            const uint16_t* __restrict__ k,
-                                           const uint16_t* __restrict__ v) {
+                                           const uint16_t* __restrict__ v, bool live = true) {
   const int tid = threadIdx.x;
   const int tau = tid >> 2, q4 = tid & 3;
   const uint32_t row = uint32_t(tau * H * kD);
-  const Rsrc rk = chunk_rsrc(k, t0, T, H, b, h, 2);
-  const Rsrc rv = chunk_rsrc(v, t0, T, H, b, h, 2);
+  const Rsrc rk = chunk_rsrc(k, t0, T, H, b, h, 2, live);
+  const Rsrc rv = chunk_rsrc(v, t0, T, H, b, h, 2, live);
   const uint32_t off = (row + 16 * q4) * 2;
   if constexpr (WITH_R) {
-    const Rsrc rr = chunk_rsrc(r, t0, T, H, b, h, 2);
+    const Rsrc rr = chunk_rsrc(r, t0, T, H, b, h, 2, live);
     x.r0 = load16(rr, off);
     x.r1 = load16(rr, off + 16);
   } else {
