@@ -570,7 +570,7 @@ __global__ __launch_bounds__(256, 2) void wkv6_fwd_chunked(
 // Local end state of one time segment (all but the last) from a zero start,
 // and the segment's summed log2 decay per key channel, for one value slice:
 // seg_state[bh][seg] holds S[i][j] (64 x 64) then L[i] (64).  The next
-// chunk's k, v and decays load while this one multiplies.
+// chunk's k, v and decays load while this one is processed.
 template <int DV>
 __global__ __launch_bounds__(256) void wkv6_seg_state(int T, int H, int BH, int seg_chunks,
                                                       int npieces, const uint16_t* __restrict__ k,
