@@ -63,8 +63,9 @@ int rwkv_last_hip_error(void);
 
 /* ------------------------------------------------------------------------
  * Plan overrides, for tests and tuning sweeps; results stay within the same
- * accuracy bounds whatever the setting.  Each key holds 0 (the built-in plan)
- * or an override.  The values start from the environment, read once at the
+ * accuracy bounds whatever the setting, except under RWKV_TUNE_WKV4_SPIN,
+ * which exists to make look-backs give up.  Each key holds 0 (the built-in
+ * plan) or an override.  The values start from the environment, read once at the
  * first call that plans anything (RWKV_WKV4_TILE="cpl,L,NW",
  * RWKV_WKV4_ORDER=claim, RWKV_WKV5_DV, RWKV_WKV5_SEGS, RWKV_WKV6_DV,
  * RWKV_WKV6_SEGS), and rwkv_set_tuning changes them for the whole process.
@@ -84,6 +85,10 @@ int rwkv_last_hip_error(void);
 #define RWKV_TUNE_WKV5_SEGS  4  /* Eagle time segments, 1..4096 (each >= 4 chunks) */
 #define RWKV_TUNE_WKV6_DV    5  /* value columns per Finch workgroup: 32 or 64 */
 #define RWKV_TUNE_WKV6_SEGS  6  /* Finch time segments, 1..4096 (each >= 4 chunks) */
+#define RWKV_TUNE_WKV4_SPIN  7  /* polls an RWKV-4 look-back (forward or backward) makes
+                                   before it gives up, sets error bit 0 and writes NaN;
+                                   0: the default, 2^24.  For tests of that path: a small
+                                   limit makes tiles give up that would have succeeded. */
 int rwkv_set_tuning(int key, int value);
 int rwkv_get_tuning(int key);
 

@@ -19,7 +19,7 @@ __all__ = [
     "LIB_PATH", "load_library", "RwkvError",
     "rwkv_abi_version", "rwkv_status_str", "rwkv_last_hip_error",
     "RWKV_TUNE_WKV4_TILE", "RWKV_TUNE_WKV4_ORDER", "RWKV_TUNE_WKV5_DV",
-    "RWKV_TUNE_WKV5_SEGS", "RWKV_TUNE_WKV6_DV", "RWKV_TUNE_WKV6_SEGS",
+    "RWKV_TUNE_WKV5_SEGS", "RWKV_TUNE_WKV6_DV", "RWKV_TUNE_WKV6_SEGS", "RWKV_TUNE_WKV4_SPIN",
     "rwkv_set_tuning", "rwkv_get_tuning", "tuning",
     "rwkv_wkv4_workspace_error",
     "rwkv_wkv4_forward_workspace", "rwkv_wkv4_forward", "rwkv_wkv4_forward_state",
@@ -133,6 +133,7 @@ RWKV_TUNE_WKV5_DV = 3
 RWKV_TUNE_WKV5_SEGS = 4
 RWKV_TUNE_WKV6_DV = 5
 RWKV_TUNE_WKV6_SEGS = 6
+RWKV_TUNE_WKV4_SPIN = 7
 
 
 def rwkv_set_tuning(key: int, value: int) -> None:

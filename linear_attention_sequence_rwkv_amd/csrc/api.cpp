@@ -92,6 +92,7 @@ bool set_tuning(int key, int value) {
     case kTuneWkv6Dv: ok = value == 0 || value == 32 || value == 64; break;
     case kTuneWkv5Segs:
     case kTuneWkv6Segs: ok = value >= 0 && value <= 4096; break;
+    case kTuneWkv4Spin: ok = value >= 0; break;
     default: ok = false;
   }
   if (ok) g_tune[key].store(value, std::memory_order_relaxed);

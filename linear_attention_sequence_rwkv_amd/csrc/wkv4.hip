@@ -126,13 +126,14 @@ __device__ __forceinline__ void write_state(const StateIO& sio, const Hist (&h)[
 // in which the chain of inclusive histories is built, so the result has the
 // same bits whichever p the timing offers: the forward is deterministic.
 // With `early`, the first poll's words (lanes < kWin: inc and agg words of
-// tile-1-lane) were loaded by the caller.  A wait beyond kSpinLimit polls
+// tile-1-lane) were loaded by the caller.  A wait beyond spin_limit polls
 // raises the error word and returns NaN.
 template <int CPL, int TILE>
 __device__ __forceinline__ void lookback(int tile, int g, int groups,
                                          const uint64_t* __restrict__ slots, uint32_t* hdr,
                                          uint32_t tag, const float (&w2)[CPL], bool early,
-                                         uint64_t e_inc, uint64_t e_agg, Hist (&acc)[CPL]) {
+                                         uint64_t e_inc, uint64_t e_agg, Hist (&acc)[CPL],
+                                         uint32_t spin_limit) {
   constexpr int W = 64 * CPL;
   constexpr int SLOT = 8 * W;  // words per (tile, block): agg A,B,kr,n then inc A,B,kr,n
   // Predecessor payloads loaded per round trip while folding a prefix
@@ -198,7 +199,7 @@ __device__ __forceinline__ void lookback(int tile, int g, int groups,
       }
       if (ok) break;
     }
-    if (++spins > kSpinLimit) {
+    if (++spins > spin_limit) {
       if (lane == 0) raise_error(hdr + kHdrError, kErrGaveUp);
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
@@ -240,7 +241,7 @@ __global__ __launch_bounds__(64 * NW * CB) void wkv4_fwd_tiled(
     const float* __restrict__ w, const float* __restrict__ u,
     const float* __restrict__ k, const float* __restrict__ v, float* __restrict__ y,
     uint32_t* __restrict__ hdr, uint64_t* __restrict__ counters, uint64_t* __restrict__ slots,
-    StateIO sio, uint64_t* __restrict__ mids) {
+    StateIO sio, uint64_t* __restrict__ mids, uint32_t spin_limit) {
   constexpr int W = 64 * CPL;        // channels per block
   constexpr int TILE = L * NW;       // tokens per tile
   constexpr int SLOT = 8 * W;        // words per (tile, block): agg A,B,kr,n then inc A,B,kr,n
@@ -386,7 +387,8 @@ __global__ __launch_bounds__(64 * NW * CB) void wkv4_fwd_tiled(
     } else {
       publish(0, agg);
       Hist acc[CPL];
-      lookback<CPL, TILE>(tile, g, groups, slots, hdr, tag, w2, in_order != 0, e_inc, e_agg, acc);
+      lookback<CPL, TILE>(tile, g, groups, slots, hdr, tag, w2, in_order != 0, e_inc, e_agg, acc,
+                          spin_limit);
       Hist inc[CPL];
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
@@ -578,7 +580,8 @@ hipError_t launch_tiled(const Wkv4Plan& pl, int64_t T, int64_t C, const float* w
   const int in_order = grid <= resident_workgroups(kern, 64 * NW * CB) ? 1 : 0;
   hipLaunchKernelGGL((wkv4_fwd_tiled<CPL, L, NW, true, false, CB>), dim3(unsigned(grid)),
                      dim3(64 * NW * CB), 0, stream, int(T), int(C), int(pl.n_cblk), int(pl.groups),
-                     int(pl.n_tiles), in_order, w, u, k, v, y, hdr, counters, slots, sio, nullptr);
+                     int(pl.n_tiles), in_order, w, u, k, v, y, hdr, counters, slots, sio, nullptr,
+                     wkv4_spin_limit());
   return hipGetLastError();
 }
 
@@ -650,6 +653,11 @@ bool wkv4_plan(int64_t B, int64_t T, int64_t C, Wkv4Plan* plan) {
   return true;
 }
 
+uint32_t wkv4_spin_limit() {
+  const int s = tuning(kTuneWkv4Spin);
+  return s > 0 ? uint32_t(s) : kSpinLimit;
+}
+
 bool wkv4_variant_exists(int code) {
   for (const Variant& vv : kVariants)
     if (vv.code() == code) return true;
@@ -676,7 +684,7 @@ hipError_t launch_prefix_like(const Wkv4Plan& pl, int64_t T, int64_t C, const fl
   hipLaunchKernelGGL((wkv4_fwd_tiled<1, 32, 4, EMIT, TAPE, CB>), dim3(unsigned(grid)),
                      dim3(256 * CB), 0, stream, int(T), int(C), int(pl.n_cblk), int(pl.groups),
                      int(pl.n_tiles), in_order, w, u, k, v, y, hdr, counters, slots, none,
-                     static_cast<uint64_t*>(mids));
+                     static_cast<uint64_t*>(mids), wkv4_spin_limit());
   return hipGetLastError();
 }
 

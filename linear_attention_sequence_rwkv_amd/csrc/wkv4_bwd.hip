@@ -100,7 +100,7 @@ __global__ __launch_bounds__(64 * NW) void wkv4_bwd_tiled(
     const uint64_t* __restrict__ fwd_slots,  // inclusive forward histories (launch 1)
     const uint64_t* __restrict__ fwd_mids,   // and those after the first half of its tiles
     uint32_t* __restrict__ hdr, uint64_t* __restrict__ counters, uint64_t* __restrict__ slots,
-    uint64_t* __restrict__ part_w, uint64_t* __restrict__ part_u) {
+    uint64_t* __restrict__ part_w, uint64_t* __restrict__ part_u, uint32_t spin_limit) {
   constexpr int W = 64;
   constexpr int TILE = L * NW;
   constexpr int FSLOT = 8 * W;             // forward slot: agg A,B,kr,n then inc A,B,kr,n
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(64 * NW) void wkv4_bwd_tiled(
             break;
           }
         }
-        if (++spins > kSpinLimit) {
+        if (++spins > spin_limit) {
           if (lane == 0) raise_error(hdr + kHdrError, kErrGaveUp);
           const float nan = __builtin_nanf("");
           suf = RevHist{nan, nan, nan, nan, nan, 0.f};
@@ -492,7 +492,7 @@ hipError_t wkv4_backward_launch(const Wkv4BwdPlan& pl, int64_t B, int64_t T, int
   hipLaunchKernelGGL((wkv4_bwd_tiled<kBwdL, kBwdNW>), dim3(grid), dim3(64 * kBwdNW), 0, stream,
                      int(T), int(C), int(pl.fwd.n_cblk), int(pl.fwd.groups), int(pl.rev_tiles),
                      w, u, k, v, gy, gk, gv, fwd_slots, mids, hdr, counters, slots, part_w,
-                     part_u);
+                     part_u, wkv4_spin_limit());
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // 3. gw, gu

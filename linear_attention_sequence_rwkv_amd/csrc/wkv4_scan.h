@@ -12,7 +12,7 @@ namespace scan {
 
 // Look-back polls without progress before a workgroup gives up (seconds);
 // it then raises the error word and writes NaN, so no wait lasts forever.
-constexpr uint32_t kSpinLimit = 1u << 24;
+constexpr uint32_t kSpinLimit = 1u << 24;  // default; the kernels take theirs as an argument
 // Earlier tiles polled per round trip by the look-back.
 constexpr int kWin = 16;
 

@@ -21,7 +21,8 @@ enum TuneKey : int {
   kTuneWkv5Segs = 4,   // Eagle time segments (before the clamp to >= 4 chunks each)
   kTuneWkv6Dv = 5,     // value columns per Finch workgroup: 32 or 64
   kTuneWkv6Segs = 6,   // Finch time segments
-  kTuneKeys = 7
+  kTuneWkv4Spin = 7,   // polls of an RWKV-4 look-back before it gives up (0: the default)
+  kTuneKeys = 8
 };
 int tuning(int key);
 bool set_tuning(int key, int value);
@@ -56,6 +57,10 @@ struct Wkv4Plan {
 
 constexpr size_t kWkv4HeaderBytes = 128;
 constexpr size_t kWkv4CounterStride = 128;  // one counter per 128-byte line
+
+// Polls an RWKV-4 look-back (forward or reverse) makes before it gives up,
+// raises error bit 0 and writes NaN: the kTuneWkv4Spin override, else 2^24.
+uint32_t wkv4_spin_limit();
 
 // Plan for a shape; honours the kTuneWkv4Tile override.  Returns false if
 // the shape cannot be planned (T > kWkv4MaxT, or too large for 32-bit

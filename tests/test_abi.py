@@ -271,18 +271,19 @@ def test_wkv6_rejections(lib):
 def test_tuning_overrides(lib):
     """Plan overrides: unknown keys and values are rejected, accepted ones are
     read back, and they change the plan (hence the workspace sizes)."""
-    keys = (1, 2, 3, 4, 5, 6)
+    keys = (1, 2, 3, 4, 5, 6, 7)
     old = {k: lib.rwkv_get_tuning(k) for k in keys}
     try:
         assert lib.rwkv_set_tuning(0, 1) == UNSUPPORTED
-        assert lib.rwkv_set_tuning(7, 1) == UNSUPPORTED
+        assert lib.rwkv_set_tuning(8, 1) == UNSUPPORTED
+        assert lib.rwkv_set_tuning(7, -1) == UNSUPPORTED
         assert lib.rwkv_set_tuning(1, 13205) == UNSUPPORTED   # no such tile shape
         assert lib.rwkv_set_tuning(1, 1) == UNSUPPORTED       # cpl 0: once a SIGFPE
         assert lib.rwkv_set_tuning(2, 2) == UNSUPPORTED
         assert lib.rwkv_set_tuning(3, 48) == UNSUPPORTED
         assert lib.rwkv_set_tuning(5, 16) == UNSUPPORTED
         assert lib.rwkv_set_tuning(4, -1) == UNSUPPORTED
-        for key, val in ((1, 40808), (2, 1), (3, 16), (4, 2), (5, 32), (6, 3)):
+        for key, val in ((1, 40808), (2, 1), (3, 16), (4, 2), (5, 32), (6, 3), (7, 1)):
             assert lib.rwkv_set_tuning(key, val) == OK
             assert lib.rwkv_get_tuning(key) == val
         # the Eagle workspace holds one state per head and earlier segment

@@ -52,14 +52,15 @@ def tile_code(tile):
 @contextlib.contextmanager
 def tuned(**settings):
     """Plan overrides for a block: wkv4_tile="cpl,L,NW", wkv4_claim=True,
-    wkv5_dv=, wkv5_segs=, wkv6_dv=, wkv6_segs= (None leaves a key alone)."""
+    wkv5_dv=, wkv5_segs=, wkv6_dv=, wkv6_segs=, wkv4_spin= (None leaves a key alone)."""
     import linear_attention_sequence_rwkv_amd as rw
     keys = {"wkv4_tile": (rw.RWKV_TUNE_WKV4_TILE, tile_code),
             "wkv4_claim": (rw.RWKV_TUNE_WKV4_ORDER, lambda x: 1 if x else 0),
             "wkv5_dv": (rw.RWKV_TUNE_WKV5_DV, int),
             "wkv5_segs": (rw.RWKV_TUNE_WKV5_SEGS, int),
             "wkv6_dv": (rw.RWKV_TUNE_WKV6_DV, int),
-            "wkv6_segs": (rw.RWKV_TUNE_WKV6_SEGS, int)}
+            "wkv6_segs": (rw.RWKV_TUNE_WKV6_SEGS, int),
+            "wkv4_spin": (rw.RWKV_TUNE_WKV4_SPIN, int)}
     with contextlib.ExitStack() as stack:
         for name, val in settings.items():
             if val is None:
