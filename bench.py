@@ -409,8 +409,36 @@ def bench_matrix_forward(torch, rw, cfg, finch, rotate=2):
     for c in copies:
         assert torch.isfinite(c[4]).all().item()
     elems = cfg.B * cfg.T * cfg.H * cfg.D
-    return {"ms": ms, "elems": elems, "bytes": (14 if finch else 10) * elems,
-            "flops": 4 * cfg.D * elems, "rotated_copies": rotate}
+    nbytes = (14 if finch else 10) * elems
+    copy_ms = mix_copy_ms(torch, copies, elems, stream)
+    return {"ms": ms, "elems": elems, "bytes": nbytes,
+            "flops": 4 * cfg.D * elems, "rotated_copies": rotate,
+            "copy_peak_GBps": None if copy_ms is None else nbytes / (copy_ms * 1e-3) / 1e9}
+
+
+def mix_copy_ms(torch, copies, elems, stream):
+    """ms per call of the copy-peak kernel with the matrix-state forward's
+    traffic (o = r + k + v [+ w_t], bf16 inputs, fp32 output: 10 or 14 B per
+    element; libwkv_copy_peak.so) over the same rotated buffers: >= 100 ms
+    per repeat, median of 5.  None when that library has not been built."""
+    path = os.path.join(ROOT, "linear_attention_sequence_rwkv_amd", "libwkv_copy_peak.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.wkv_bench_mix_copy.restype = ctypes.c_int
+    lib.wkv_bench_mix_copy.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_size_t, ctypes.c_void_p]
+    sh = ctypes.c_void_p(stream.cuda_stream)
+
+    def launch(i):
+        r, k, v, wt, o = copies[i % len(copies)]
+        wp = _ptr(wt) if wt is not None else None
+        if lib.wkv_bench_mix_copy(_ptr(r), _ptr(k), _ptr(v), wp, _ptr(o), elems, sh) != 0:
+            raise RuntimeError("wkv_bench_mix_copy failed")
+
+    for i in range(3):
+        launch(i)
+    ms, _, _ = measure(torch, stream, launch)
+    return ms
 
 
 def wkv5_step_bytes(B, H, D):
@@ -662,9 +690,13 @@ def main(argv=None):
         hsrc = kernel_source_hash(("wkv6.hip" if finch else "wkv5.hip", "eagle_common.h",
                                    "wkv_device.h"))
         prof = (("wkv6" if finch else "wkv5") + "_fwd_chunked_mfma_B4_T4096_H32_D64.md")
+        g = r["bytes"] / (r["ms"] * 1e-3) / 1e9
+        cp = r["copy_peak_GBps"]
         sec[mc.name] = {"ms": round(r["ms"], 4),
-                        "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
+                        "GBps": round(g, 1),
                         "bytes_per_elem": 14 if finch else 10,
+                        "copy_peak_GBps": None if cp is None else round(cp, 1),
+                        "pct_of_copy_peak": None if cp is None else round(100 * g / cp, 2),
                         "algorithmic_TFLOPs": round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 2),
                         "mfma_busy_pct": read_counter_summary(
                             prof, hsrc, "mfma_busy_pct_wide" if key == "eagle-wide"
