@@ -278,7 +278,27 @@ def bench_wkv4_backward(torch, rw, cfg):
     ms, n, _ = measure(torch, stream, lambda i: fn(*args))
     assert torch.isfinite(gk).all().item() and torch.isfinite(gw).all().item()
     assert rw.rwkv_wkv4_workspace_error(ws) == 0
-    return {"ms": ms, "elems": B * T * C, "bytes": 20 * B * T * C, "calls_per_repeat": n}
+    copy_gbps = None
+    path = os.path.join(ROOT, "linear_attention_sequence_rwkv_amd", "libwkv_copy_peak.so")
+    if os.path.exists(path):
+        # the copy kernel with the backward's traffic, over its own buffers
+        cl = ctypes.CDLL(path)
+        cl.wkv_bench_three_two_copy.restype = ctypes.c_int
+        cl.wkv_bench_three_two_copy.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_size_t,
+                                                                        ctypes.c_void_p]
+        sh = ctypes.c_void_p(stream.cuda_stream)
+
+        def copy(i):
+            if cl.wkv_bench_three_two_copy(_ptr(k), _ptr(v), _ptr(gy), _ptr(gk), _ptr(gv),
+                                           B * T * C, sh) != 0:
+                raise RuntimeError("wkv_bench_three_two_copy failed")
+
+        for i in range(3):
+            copy(i)
+        cms, _, _ = measure(torch, stream, copy)
+        copy_gbps = 20 * B * T * C / (cms * 1e-3) / 1e9
+    return {"ms": ms, "elems": B * T * C, "bytes": 20 * B * T * C, "calls_per_repeat": n,
+            "copy_peak_GBps": copy_gbps}
 
 
 def bench_wkv4_train(torch, rw, cfg):
@@ -707,9 +727,13 @@ def main(argv=None):
             name = bc.name.replace("wkv4_fwd", "wkv4_bwd")
             log(f"bench: {name}")
             r = bench_wkv4_backward(torch, rw, bc)
+            g = r["bytes"] / (r["ms"] * 1e-3) / 1e9
+            cp = r["copy_peak_GBps"]
             sec[name] = {"ms": round(r["ms"], 5),
-                         "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
+                         "GBps": round(g, 1),
                          "bytes_per_elem": 20,
+                         "copy_peak_GBps": None if cp is None else round(cp, 1),
+                         "pct_of_copy_peak": None if cp is None else round(100 * g / cp, 2),
                          "gelem_per_s": round(r["elems"] / (r["ms"] * 1e-3) / 1e9, 1)}
 
     backward("backward", synth.CFG_WKV4_169M)

@@ -5,7 +5,8 @@
 // rate is compared against.  add_copy: y = a + b over float32 arrays (the
 // RWKV-4 forward's 12 bytes per element); mix_copy: three bfloat16 inputs
 // (and optionally a float32 one) into a float32 output (the Eagle and Finch
-// forwards' 10 and 14 bytes).
+// forwards' 10 and 14 bytes); three_two_copy: three float32 arrays into two
+// (the RWKV-4 backward's 20 bytes).
 #include <hip/hip_runtime.h>
 
 #include <stddef.h>
@@ -55,7 +56,44 @@ __global__ __launch_bounds__(256) void mix_copy(size_t n8, const us8* __restrict
   }
 }
 
+// The RWKV-4 backward's traffic: three float32 arrays read, two written.
+__global__ __launch_bounds__(256) void three_two_copy(size_t n4, const f4* __restrict__ a,
+                                                      const f4* __restrict__ b,
+                                                      const f4* __restrict__ c,
+                                                      f4* __restrict__ y, f4* __restrict__ z) {
+  const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n4) {
+    const f4 x0 = __builtin_nontemporal_load(a + i);
+    const f4 x1 = __builtin_nontemporal_load(b + i);
+    const f4 x2 = __builtin_nontemporal_load(c + i);
+    __builtin_nontemporal_store(x0 + x1, y + i);
+    __builtin_nontemporal_store(x1 + x2, z + i);
+  }
+}
+
 }  // namespace
+
+// y[i] = a[i] + b[i], z[i] = b[i] + c[i] for i < n, float32: 20 bytes per
+// element, the traffic of the RWKV-4 backward (k, v, gy read; gk, gv
+// written).  n must be a multiple of 4 and every pointer 16-byte aligned
+// (else -1).  Returns 0 or the launch's hipError_t.
+extern "C" __attribute__((visibility("default"))) int wkv_bench_three_two_copy(
+    const float* a, const float* b, const float* c, float* y, float* z, size_t n,
+    hipStream_t stream) {
+  if (n % 4 != 0 || (reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b) |
+                     reinterpret_cast<uintptr_t>(c) | reinterpret_cast<uintptr_t>(y) |
+                     reinterpret_cast<uintptr_t>(z)) % 16 != 0)
+    return -1;
+  const size_t n4 = n / 4;
+  if (n4 == 0) return 0;
+  const size_t blocks = (n4 + 255) / 256;
+  if (blocks >= (size_t(1) << 31)) return -1;
+  hipLaunchKernelGGL(three_two_copy, dim3(unsigned(blocks)), dim3(256), 0, stream, n4,
+                     reinterpret_cast<const f4*>(a), reinterpret_cast<const f4*>(b),
+                     reinterpret_cast<const f4*>(c), reinterpret_cast<f4*>(y),
+                     reinterpret_cast<f4*>(z));
+  return int(hipGetLastError());
+}
 
 // o[i] = r[i] + k[i] + v[i] (+ w[i] when w is not null) for i < n, with r, k,
 // v bfloat16 bit patterns and w, o float32: 10 (14 with w) bytes per
