@@ -337,7 +337,13 @@ __global__ __launch_bounds__(256, 2) void wkv6_fwd_chunked(
   const int j0 = slice * DV;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int q = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Wave w of the workgroup takes query block (w + blockIdx) mod 4: the last
+  // block has four key blocks of score work and the first one, and rotating
+  // the assignment spreads the heavy waves of the workgroups sharing a CU
+  // over its SIMDs (same results; 4x4096x32x64: 147.5 -> 145.7 us; the Eagle
+  // kernel, whose mid-chunk path multiplies all four key blocks on every
+  // wave, measured 2 us slower with it).
+  const int q = __builtin_amdgcn_readfirstlane(((tid >> 6) + (int(blockIdx.x) & 3)) & 3);
   const int row = lane & 15;
   const int kq = 8 * (lane >> 4);
   const int crow = 4 * (lane >> 4);
