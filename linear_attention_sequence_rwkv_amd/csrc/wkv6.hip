@@ -337,12 +337,12 @@ __global__ __launch_bounds__(256, 2) void wkv6_fwd_chunked(
   const int j0 = slice * DV;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  // Wave w of the workgroup takes query block (w + blockIdx) mod 4: the last
-  // block has four key blocks of score work and the first one, and rotating
-  // the assignment spreads the heavy waves of the workgroups sharing a CU
-  // over its SIMDs (same results; 4x4096x32x64: 147.5 -> 145.7 us; the Eagle
-  // kernel, whose mid-chunk path multiplies all four key blocks on every
-  // wave, measured 2 us slower with it).
+  // Wave w of the workgroup takes query block (w + blockIdx) mod 4 (the same
+  // for every workgroup of an XCD): the last block has four key blocks of
+  // score work and the first one, and which wave takes the heavy block
+  // matters (same results; 4x4096x32x64: 147.5 us with block w, 145.7 us with
+  // this, 145.9 us with block 3 - w, 150.1 us with a rotation that differs
+  // between the workgroups of one XCD).
   const int q = __builtin_amdgcn_readfirstlane(((tid >> 6) + (int(blockIdx.x) & 3)) & 3);
   const int row = lane & 15;
   const int kq = 8 * (lane >> 4);
