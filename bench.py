@@ -254,68 +254,80 @@ def cpu_baseline_wkv4(cfg, inp, channels):
 
 # ------------------------------------------------------------------ others
 
-def bench_wkv4_backward(torch, rw, cfg):
-    """One backward call (prefix pass, reverse scan, reduction) per step."""
+def bench_wkv4_backward(torch, rw, cfg, rotate=1):
+    """One backward call (prefix pass, reverse scan, reduction) per step,
+    cycling over `rotate` copies of (k, v, gy) and of the gradients so that
+    at 8x1024x768 the calls do not find their inputs in the 256 MB MALL."""
     import synth
     dev = torch.device("cuda:0")
     inp = synth.wkv4_backward_inputs(cfg.B, cfg.T, cfg.C, cfg.seed, omega_lo=cfg.omega_lo,
                                      omega_hi=cfg.omega_hi, u_std=cfg.u_std, k_std=cfg.k_std,
                                      v_std=cfg.v_std)
     B, T, C = cfg.B, cfg.T, cfg.C
-    w, u, k, v, gy = (torch.from_numpy(inp[n]).to(dev) for n in ("w", "u", "k", "v", "gy"))
+    w, u = (torch.from_numpy(inp[n]).to(dev) for n in ("w", "u"))
+    sets = []
+    for _ in range(rotate):
+        k, v, gy = (torch.from_numpy(inp[n]).to(dev) for n in ("k", "v", "gy"))
+        sets.append((k, v, gy, torch.empty_like(k), torch.empty_like(k)))
     del inp
     gw, gu = torch.empty_like(w), torch.empty_like(u)
-    gk, gv = torch.empty_like(k), torch.empty_like(k)
     lib = rw.load_library()
     need = lib.rwkv_wkv4_backward_workspace(B, T, C)
     ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-    args = (B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(gy), _ptr(gw), _ptr(gu), _ptr(gk),
-            _ptr(gv), _ptr(ws), need, ctypes.c_void_p(stream.cuda_stream))
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    args = [(B, T, C, _ptr(w), _ptr(u), _ptr(k), _ptr(v), _ptr(gy), _ptr(gw), _ptr(gu), _ptr(gk),
+             _ptr(gv), _ptr(ws), need, sh) for k, v, gy, gk, gv in sets]
     fn = lib.rwkv_wkv4_backward
-    for _ in range(2):
-        assert fn(*args) == 0
-    ms, n, _ = measure(torch, stream, lambda i: fn(*args))
-    assert torch.isfinite(gk).all().item() and torch.isfinite(gw).all().item()
+    for i in range(2 * rotate):
+        assert fn(*args[i % rotate]) == 0
+    ms, n, _ = measure(torch, stream, lambda i: fn(*args[i % rotate]))
+    for s in sets:
+        assert torch.isfinite(s[3]).all().item() and torch.isfinite(s[4]).all().item()
+    assert torch.isfinite(gw).all().item()
     assert rw.rwkv_wkv4_workspace_error(ws) == 0
     copy_gbps = None
     path = os.path.join(ROOT, "linear_attention_sequence_rwkv_amd", "libwkv_copy_peak.so")
     if os.path.exists(path):
-        # the copy kernel with the backward's traffic, over its own buffers
+        # the copy kernel with the backward's traffic, over the same buffers
         cl = ctypes.CDLL(path)
         cl.wkv_bench_three_two_copy.restype = ctypes.c_int
         cl.wkv_bench_three_two_copy.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_size_t,
                                                                         ctypes.c_void_p]
-        sh = ctypes.c_void_p(stream.cuda_stream)
 
         def copy(i):
+            k, v, gy, gk, gv = sets[i % rotate]
             if cl.wkv_bench_three_two_copy(_ptr(k), _ptr(v), _ptr(gy), _ptr(gk), _ptr(gv),
                                            B * T * C, sh) != 0:
                 raise RuntimeError("wkv_bench_three_two_copy failed")
 
-        for i in range(3):
+        for i in range(2 * rotate):
             copy(i)
         cms, _, _ = measure(torch, stream, copy)
         copy_gbps = 20 * B * T * C / (cms * 1e-3) / 1e9
     return {"ms": ms, "elems": B * T * C, "bytes": 20 * B * T * C, "calls_per_repeat": n,
-            "copy_peak_GBps": copy_gbps}
+            "copy_peak_GBps": copy_gbps, "rotated_copies": rotate}
 
 
-def bench_wkv4_train(torch, rw, cfg):
+def bench_wkv4_train(torch, rw, cfg, rotate=1):
     """A training step's WKV: forward then backward on the same inputs, timed
     as rwkv_wkv4_forward_train + rwkv_wkv4_backward_after_forward (one
     workspace, the backward reuses the forward's tile histories) and as
-    rwkv_wkv4_forward + rwkv_wkv4_backward."""
+    rwkv_wkv4_forward + rwkv_wkv4_backward, cycling over `rotate` copies of
+    the inputs and outputs as bench_wkv4_backward does."""
     import synth
     dev = torch.device("cuda:0")
     inp = synth.wkv4_backward_inputs(cfg.B, cfg.T, cfg.C, cfg.seed, omega_lo=cfg.omega_lo,
                                      omega_hi=cfg.omega_hi, u_std=cfg.u_std, k_std=cfg.k_std,
                                      v_std=cfg.v_std)
     B, T, C = cfg.B, cfg.T, cfg.C
-    w, u, k, v, gy = (torch.from_numpy(inp[n]).to(dev) for n in ("w", "u", "k", "v", "gy"))
-    y = torch.empty_like(k)
+    w, u = (torch.from_numpy(inp[n]).to(dev) for n in ("w", "u"))
+    sets = []
+    for _ in range(rotate):
+        k, v, gy = (torch.from_numpy(inp[n]).to(dev) for n in ("k", "v", "gy"))
+        sets.append((k, v, gy, torch.empty_like(k), torch.empty_like(k), torch.empty_like(k)))
+    del inp
     gw, gu = torch.empty_like(w), torch.empty_like(u)
-    gk, gv = torch.empty_like(k), torch.empty_like(k)
     lib = rw.load_library()
     need_b = lib.rwkv_wkv4_backward_workspace(B, T, C)
     need_f = lib.rwkv_wkv4_forward_workspace(B, T, C)
@@ -323,24 +335,27 @@ def bench_wkv4_train(torch, rw, cfg):
     ws_f = torch.zeros(max(need_f, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sh = ctypes.c_void_p(stream.cuda_stream)
-    io = (_ptr(w), _ptr(u), _ptr(k), _ptr(v))
-    grads = (_ptr(gy), _ptr(gw), _ptr(gu), _ptr(gk), _ptr(gv))
-    pair = ((lib.rwkv_wkv4_forward_train, (B, T, C, *io, _ptr(y), _ptr(ws_b), need_b, sh)),
-            (lib.rwkv_wkv4_backward_after_forward,
-             (B, T, C, *io, *grads, _ptr(ws_b), need_b, sh)))
-    separate = ((lib.rwkv_wkv4_forward, (B, T, C, *io, _ptr(y), _ptr(ws_f), need_f, sh)),
-                (lib.rwkv_wkv4_backward, (B, T, C, *io, *grads, _ptr(ws_b), need_b, sh)))
+    pair, separate = [], []
+    for k, v, gy, y, gk, gv in sets:
+        io = (_ptr(w), _ptr(u), _ptr(k), _ptr(v))
+        grads = (_ptr(gy), _ptr(gw), _ptr(gu), _ptr(gk), _ptr(gv))
+        pair.append(((lib.rwkv_wkv4_forward_train, (B, T, C, *io, _ptr(y), _ptr(ws_b), need_b, sh)),
+                     (lib.rwkv_wkv4_backward_after_forward,
+                      (B, T, C, *io, *grads, _ptr(ws_b), need_b, sh))))
+        separate.append(((lib.rwkv_wkv4_forward, (B, T, C, *io, _ptr(y), _ptr(ws_f), need_f, sh)),
+                         (lib.rwkv_wkv4_backward, (B, T, C, *io, *grads, _ptr(ws_b), need_b, sh))))
     out = {}
     for key, calls in (("pair", pair), ("separate", separate)):
         def launch(i, calls=calls):
-            for fn, a in calls:
+            for fn, a in calls[i % rotate]:
                 assert fn(*a) == 0
-        for i in range(2):
+        for i in range(2 * rotate):
             launch(i)
         out[key], _, _ = measure(torch, stream, launch)
-        assert torch.isfinite(gk).all().item() and torch.isfinite(y).all().item()
+        for s in sets:
+            assert torch.isfinite(s[3]).all().item() and torch.isfinite(s[4]).all().item()
     return {"ms": out["pair"], "ms_separate": out["separate"], "elems": B * T * C,
-            "bytes": 32 * B * T * C}
+            "bytes": 32 * B * T * C, "rotated_copies": rotate}
 
 
 def bench_decode(torch, rw, cfg, graph=True):
@@ -722,11 +737,11 @@ def main(argv=None):
                             prof, hsrc, "mfma_busy_pct_wide" if key == "eagle-wide"
                             else "mfma_busy_pct"),
                         "rotated_copies": r["rotated_copies"]}
-    def backward(key, bc):
+    def backward(key, bc, rotate):
         if key in want:
             name = bc.name.replace("wkv4_fwd", "wkv4_bwd")
             log(f"bench: {name}")
-            r = bench_wkv4_backward(torch, rw, bc)
+            r = bench_wkv4_backward(torch, rw, bc, rotate)
             g = r["bytes"] / (r["ms"] * 1e-3) / 1e9
             cp = r["copy_peak_GBps"]
             sec[name] = {"ms": round(r["ms"], 5),
@@ -734,19 +749,20 @@ def main(argv=None):
                          "bytes_per_elem": 20,
                          "copy_peak_GBps": None if cp is None else round(cp, 1),
                          "pct_of_copy_peak": None if cp is None else round(100 * g / cp, 2),
-                         "gelem_per_s": round(r["elems"] / (r["ms"] * 1e-3) / 1e9, 1)}
+                         "gelem_per_s": round(r["elems"] / (r["ms"] * 1e-3) / 1e9, 1),
+                         "rotated_copies": r["rotated_copies"]}
 
-    backward("backward", synth.CFG_WKV4_169M)
+    backward("backward", synth.CFG_WKV4_169M, 6)
     if "train" in want:
         tc = synth.CFG_WKV4_169M
         name = tc.name.replace("wkv4_fwd", "wkv4_train_step")
         log(f"bench: {name}")
-        r = bench_wkv4_train(torch, rw, tc)
+        r = bench_wkv4_train(torch, rw, tc, 6)
         sec[name] = {"ms": round(r["ms"], 5),
                      "ms_forward_plus_backward": round(r["ms_separate"], 5),
                      "GBps": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
-                     "bytes_per_elem": 32}
-    backward("backward-long", synth.CFG_WKV4_LONG)
+                     "bytes_per_elem": 32, "rotated_copies": r["rotated_copies"]}
+    backward("backward-long", synth.CFG_WKV4_LONG, 1)
     if "long-steady" in want:
         # The headline workload under the secondary protocol, last before the
         # headline: its steady-state rate, and K timed steps that start on a

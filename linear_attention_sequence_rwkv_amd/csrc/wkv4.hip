@@ -235,7 +235,8 @@ __device__ __forceinline__ void lookback(int tile, int g, int groups,
 // what changes is the memory pattern: the CB waves of a time slot read
 // adjacent 256-byte pieces of the same rows together.  Tiles are claimed
 // per group of CB blocks.
-template <int CPL, int L, int NW, bool EMIT = true, bool TAPE = false, int CB = 1>
+template <int CPL, int L, int NW, bool EMIT = true, bool TAPE = false, int CB = 1,
+          int POL = kLoadStream>
 __global__ __launch_bounds__(64 * NW * CB) void wkv4_fwd_tiled(
     int T, int C, int n_cblk, int groups, int n_tiles, int in_order,
     const float* __restrict__ w, const float* __restrict__ u,
@@ -307,9 +308,9 @@ __global__ __launch_bounds__(64 * NW * CB) void wkv4_fwd_tiled(
   float kk[L][CPL], vv[L][CPL];
   const bool full = n == L;
   if (full)
-    load_rows<L, CPL, true>(rk, rv, voff_in, row_bytes, n, kk, vv);
+    load_rows<L, CPL, true, POL>(rk, rv, voff_in, row_bytes, n, kk, vv);
   else
-    load_rows<L, CPL, false>(rk, rv, voff_in, row_bytes, n, kk, vv);
+    load_rows<L, CPL, false, POL>(rk, rv, voff_in, row_bytes, n, kk, vv);
   if (in_order && threadIdx.x == 0) s_tag = hdr_load(hdr, kHdrEpoch) + 1u;
 
   // Pass 1: this wave's tokens from an empty history, at raised issue
@@ -653,6 +654,11 @@ bool wkv4_plan(int64_t B, int64_t T, int64_t C, Wkv4Plan* plan) {
   return true;
 }
 
+bool wkv4_keep_rows(const Wkv4Plan& pl, int64_t T, int64_t C) {
+  const int64_t B = pl.groups / pl.n_cblk;
+  return 8 * B * T * C <= kKeepRowBytes;
+}
+
 uint32_t wkv4_spin_limit() {
   const int s = tuning(kTuneWkv4Spin);
   return s > 0 ? uint32_t(s) : kSpinLimit;
@@ -669,7 +675,7 @@ namespace {
 // The prefix pass (EMIT = false) or the training forward (TAPE = true) of
 // the backward's plan: 1 channel per lane, 32 tokens x 4 waves, CB channel
 // blocks per workgroup.
-template <bool EMIT, bool TAPE, int CB>
+template <bool EMIT, bool TAPE, int CB, int POL>
 hipError_t launch_prefix_like(const Wkv4Plan& pl, int64_t T, int64_t C, const float* w,
                               const float* u, const float* k, const float* v, float* y,
                               void* ws, void* mids, hipStream_t stream) {
@@ -679,9 +685,10 @@ hipError_t launch_prefix_like(const Wkv4Plan& pl, int64_t T, int64_t C, const fl
   uint64_t* slots = reinterpret_cast<uint64_t*>(base + pl.slots_offset);
   const int64_t grid = pl.n_tiles * pl.groups / CB;
   const StateIO none{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
-  const void* kern = reinterpret_cast<const void*>(&wkv4_fwd_tiled<1, 32, 4, EMIT, TAPE, CB>);
+  const void* kern =
+      reinterpret_cast<const void*>(&wkv4_fwd_tiled<1, 32, 4, EMIT, TAPE, CB, POL>);
   const int in_order = grid <= resident_workgroups(kern, 256 * CB) ? 1 : 0;
-  hipLaunchKernelGGL((wkv4_fwd_tiled<1, 32, 4, EMIT, TAPE, CB>), dim3(unsigned(grid)),
+  hipLaunchKernelGGL((wkv4_fwd_tiled<1, 32, 4, EMIT, TAPE, CB, POL>), dim3(unsigned(grid)),
                      dim3(256 * CB), 0, stream, int(T), int(C), int(pl.n_cblk), int(pl.groups),
                      int(pl.n_tiles), in_order, w, u, k, v, y, hdr, counters, slots, none,
                      static_cast<uint64_t*>(mids), wkv4_spin_limit());
@@ -694,10 +701,17 @@ hipError_t wkv4_prefix_launch(const Wkv4Plan& pl, int64_t T, int64_t C, const fl
                               const float* u, const float* k, const float* v, void* ws,
                               void* mids, hipStream_t stream) {
   if (pl.cpl != 1 || pl.L != 32 || pl.NW != 4) return hipErrorInvalidValue;
+  const bool keep = wkv4_keep_rows(pl, T, C);
   if (pl.cb == 2)
-    return launch_prefix_like<false, false, 2>(pl, T, C, w, u, k, v, nullptr, ws, mids, stream);
+    return keep ? launch_prefix_like<false, false, 2, kLoadKeep>(pl, T, C, w, u, k, v, nullptr,
+                                                                ws, mids, stream)
+                : launch_prefix_like<false, false, 2, kLoadStream>(pl, T, C, w, u, k, v, nullptr,
+                                                                  ws, mids, stream);
   if (pl.cb == 1)
-    return launch_prefix_like<false, false, 1>(pl, T, C, w, u, k, v, nullptr, ws, mids, stream);
+    return keep ? launch_prefix_like<false, false, 1, kLoadKeep>(pl, T, C, w, u, k, v, nullptr,
+                                                                ws, mids, stream)
+                : launch_prefix_like<false, false, 1, kLoadStream>(pl, T, C, w, u, k, v, nullptr,
+                                                                  ws, mids, stream);
   return hipErrorInvalidValue;
 }
 
@@ -705,10 +719,19 @@ hipError_t wkv4_forward_tape_launch(const Wkv4Plan& pl, int64_t T, int64_t C, co
                                    const float* u, const float* k, const float* v, float* y,
                                    void* ws, void* mids, hipStream_t stream) {
   if (pl.cpl != 1 || pl.L != 32 || pl.NW != 4) return hipErrorInvalidValue;
+  // The backward that follows reads k and v again: where they fit the
+  // memory-side cache, load them with the default policy so they stay there.
+  const bool keep = wkv4_keep_rows(pl, T, C);
   if (pl.cb == 2)
-    return launch_prefix_like<true, true, 2>(pl, T, C, w, u, k, v, y, ws, mids, stream);
+    return keep ? launch_prefix_like<true, true, 2, kLoadKeep>(pl, T, C, w, u, k, v, y, ws,
+                                                              mids, stream)
+                : launch_prefix_like<true, true, 2, kLoadStream>(pl, T, C, w, u, k, v, y, ws,
+                                                                mids, stream);
   if (pl.cb == 1)
-    return launch_prefix_like<true, true, 1>(pl, T, C, w, u, k, v, y, ws, mids, stream);
+    return keep ? launch_prefix_like<true, true, 1, kLoadKeep>(pl, T, C, w, u, k, v, y, ws,
+                                                              mids, stream)
+                : launch_prefix_like<true, true, 1, kLoadStream>(pl, T, C, w, u, k, v, y, ws,
+                                                                mids, stream);
   return hipErrorInvalidValue;
 }
 

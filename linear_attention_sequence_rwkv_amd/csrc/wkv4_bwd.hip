@@ -91,7 +91,7 @@ struct RevLds {
 constexpr int kRevFields = 6;
 
 // One channel per lane, L tokens per wave, NW waves per tile.
-template <int L, int NW>
+template <int L, int NW, int POL>
 __global__ __launch_bounds__(64 * NW) void wkv4_bwd_tiled(
     int T, int C, int n_cblk, int groups, int n_tiles,
     const float* __restrict__ w, const float* __restrict__ u,
@@ -165,13 +165,13 @@ __global__ __launch_bounds__(64 * NW) void wkv4_bwd_tiled(
   float kk[L][1], vv[L][1], gg[L];
   const bool full = n == L;
   if (full)
-    load_rows<L, 1, true>(rk, rv, voff_in, row_bytes, n, kk, vv);
+    load_rows<L, 1, true, POL>(rk, rv, voff_in, row_bytes, n, kk, vv);
   else
-    load_rows<L, 1, false>(rk, rv, voff_in, row_bytes, n, kk, vv);
+    load_rows<L, 1, false, POL>(rk, rv, voff_in, row_bytes, n, kk, vv);
 #pragma unroll
   for (int s = 0; s < L; ++s) {
     float t1[1] = {0.f};
-    if (full || s < n) load_row<1>(rg, voff_in, uint32_t(s) * row_bytes, t1);
+    if (full || s < n) load_row<1, POL>(rg, voff_in, uint32_t(s) * row_bytes, t1);
     gg[s] = t1[0];
   }
 
@@ -489,10 +489,16 @@ hipError_t wkv4_backward_launch(const Wkv4BwdPlan& pl, int64_t B, int64_t T, int
   uint64_t* part_u =
       reinterpret_cast<uint64_t*>(base + pl.part_offset + (part_bytes + 255) / 256 * 256);
   const unsigned grid = unsigned(pl.rev_tiles * pl.fwd.groups);
-  hipLaunchKernelGGL((wkv4_bwd_tiled<kBwdL, kBwdNW>), dim3(grid), dim3(64 * kBwdNW), 0, stream,
-                     int(T), int(C), int(pl.fwd.n_cblk), int(pl.fwd.groups), int(pl.rev_tiles),
-                     w, u, k, v, gy, gk, gv, fwd_slots, mids, hdr, counters, slots, part_w,
-                     part_u, wkv4_spin_limit());
+  if (wkv4_keep_rows(pl.fwd, T, C))
+    hipLaunchKernelGGL((wkv4_bwd_tiled<kBwdL, kBwdNW, kLoadKeep>), dim3(grid), dim3(64 * kBwdNW),
+                       0, stream, int(T), int(C), int(pl.fwd.n_cblk), int(pl.fwd.groups),
+                       int(pl.rev_tiles), w, u, k, v, gy, gk, gv, fwd_slots, mids, hdr, counters,
+                       slots, part_w, part_u, wkv4_spin_limit());
+  else
+    hipLaunchKernelGGL((wkv4_bwd_tiled<kBwdL, kBwdNW, kLoadStream>), dim3(grid),
+                       dim3(64 * kBwdNW), 0, stream, int(T), int(C), int(pl.fwd.n_cblk),
+                       int(pl.fwd.groups), int(pl.rev_tiles), w, u, k, v, gy, gk, gv, fwd_slots,
+                       mids, hdr, counters, slots, part_w, part_u, wkv4_spin_limit());
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // 3. gw, gu

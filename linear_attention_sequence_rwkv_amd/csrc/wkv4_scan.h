@@ -58,6 +58,11 @@ __device__ __forceinline__ void lds_barrier() {
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit access, gfx9 family
 constexpr int kNonTemporal = 2;
+// Row loads: non-temporal by default.  The backward reads k and v twice
+// (prefix pass or training forward, then reverse pass); where the two fit in
+// the MALL together those passes load on the default policy instead
+// (kLoadKeep), so that the second read finds them there.
+enum LoadPolicy : int { kLoadStream = kNonTemporal, kLoadKeep = 0 };
 constexpr uint32_t kDropOffset = 0x80000000u;
 
 __device__ __forceinline__ Rsrc make_rsrc(const float* base, uint32_t bytes) {
@@ -65,24 +70,24 @@ __device__ __forceinline__ Rsrc make_rsrc(const float* base, uint32_t bytes) {
 }
 
 // CPL adjacent floats of one row, loaded/stored with a single vector access.
-template <int CPL>
+template <int CPL, int POL = kLoadStream>
 __device__ __forceinline__ void load_row(Rsrc r, uint32_t voff, uint32_t soff,
                                          float (&x)[CPL]) {
   if constexpr (CPL == 4) {
     typedef int iv4 __attribute__((ext_vector_type(4)));
     const float4 t = __builtin_bit_cast(
-        float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNonTemporal));
+        float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POL));
     x[0] = t.x;
     x[1] = t.y;
     x[2] = t.z;
     x[3] = t.w;
   } else if constexpr (CPL == 2) {
     const float2 t = __builtin_bit_cast(
-        float2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kNonTemporal));
+        float2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, POL));
     x[0] = t.x;
     x[1] = t.y;
   } else {
-    x[0] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kNonTemporal));
+    x[0] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, POL));
   }
 }
 
@@ -272,7 +277,7 @@ __device__ __forceinline__ void rescan_blocked(Hist (&hs)[CPL], const float (&kk
 // are zero) and its second pass, specialised so that a full wave carries no
 // per-row checks.  issue_rows only issues the loads (nothing here waits for
 // them); scale_keys, the first use of the values, converts k to base 2.
-template <int L, int CPL, bool FULL>
+template <int L, int CPL, bool FULL, int POL = kLoadStream>
 __device__ __forceinline__ void issue_rows(Rsrc rk, Rsrc rv, uint32_t voff, uint32_t row_bytes,
                                            int n, float (&kk)[L][CPL], float (&vv)[L][CPL]) {
 #pragma unroll
@@ -288,8 +293,8 @@ __device__ __forceinline__ void issue_rows(Rsrc rk, Rsrc rv, uint32_t voff, uint
 #pragma unroll
     for (int c = 0; c < CPL; ++c) tk[c] = tv[c] = 0.f;
     if (FULL || s < n) {
-      load_row<CPL>(rk, voff, uint32_t(s) * row_bytes, tk);
-      load_row<CPL>(rv, voff, uint32_t(s) * row_bytes, tv);
+      load_row<CPL, POL>(rk, voff, uint32_t(s) * row_bytes, tk);
+      load_row<CPL, POL>(rv, voff, uint32_t(s) * row_bytes, tv);
     }
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
@@ -307,10 +312,10 @@ __device__ __forceinline__ void scale_keys(float (&kk)[L][CPL]) {
     for (int c = 0; c < CPL; ++c) kk[s][c] *= kLog2e;
 }
 
-template <int L, int CPL, bool FULL>
+template <int L, int CPL, bool FULL, int POL = kLoadStream>
 __device__ __forceinline__ void load_rows(Rsrc rk, Rsrc rv, uint32_t voff, uint32_t row_bytes,
                                           int n, float (&kk)[L][CPL], float (&vv)[L][CPL]) {
-  issue_rows<L, CPL, FULL>(rk, rv, voff, row_bytes, n, kk, vv);
+  issue_rows<L, CPL, FULL, POL>(rk, rv, voff, row_bytes, n, kk, vv);
   scale_keys<L, CPL>(kk);
 }
 

@@ -62,6 +62,17 @@ constexpr size_t kWkv4CounterStride = 128;  // one counter per 128-byte line
 // raises error bit 0 and writes NaN: the kTuneWkv4Spin override, else 2^24.
 uint32_t wkv4_spin_limit();
 
+// Whether the passes that read k and v twice (the backward's prefix and
+// reverse passes, the training forward and the backward after it) load them
+// on the default cache policy, so that the second read meets them in the
+// MALL, instead of non-temporally: k and v together at most kKeepRowBytes.
+// Backward at 8x1024x768: 53.0 -> 45.1 us on one input set, 54.7 -> 52.1 us
+// over six rotated sets; training pair: 57.2 -> 47.9 and 58.9 -> 58.6 us
+// (with the training forward left non-temporal, 62.0 over six sets).  At
+// 1x65536x5120 (2.7 GB) the default policy cost 1.3%.
+constexpr int64_t kKeepRowBytes = int64_t(128) << 20;
+bool wkv4_keep_rows(const Wkv4Plan& pl, int64_t T, int64_t C);
+
 // Plan for a shape; honours the kTuneWkv4Tile override.  Returns false if
 // the shape cannot be planned (T > kWkv4MaxT, or too large for 32-bit
 // tickets and offsets).
