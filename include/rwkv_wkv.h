@@ -125,8 +125,12 @@ int rwkv_wkv4_workspace_error(const void* ws, size_t ws_bytes, uint32_t* err,
  *   ws, ws_bytes         device workspace of at least
  *                        rwkv_wkv4_forward_workspace(B,T,C) bytes.  It must be
  *                        zero-filled before its first use; each call leaves it
- *                        ready for the next call on the same stream.  A call
- *                        whose workspace size is 0 accepts ws == NULL.
+ *                        ready for the next call on the same stream.  Its words
+ *                        are tagged with a 32-bit count of the launches made on
+ *                        it (one per call here, two for a backward), so it must
+ *                        be zero-filled again at least once every 2^30 calls,
+ *                        graph replays included.  A call whose workspace size
+ *                        is 0 accepts ws == NULL.
  * Accuracy: max |y - exact| <= 1e-4 * S, where S is the same weighted mean
  * taken over |v| (float32 arithmetic, hardware exp2 and reciprocal).
  * Limit: T <= 2^24 - 64 per call (decay counts are held in float32, exact
@@ -182,7 +186,8 @@ int rwkv_wkv4_forward_noalloc(int64_t B, int64_t T, int64_t C,
  *   gk, gv      [B,T,C]  float32  output
  *   ws, ws_bytes         device workspace of at least
  *                        rwkv_wkv4_backward_workspace(B,T,C) bytes, zero-filled
- *                        before its first use (as for the forward; it is not
+ *                        before its first use and again at least once every
+ *                        2^30 calls (as for the forward; it is not
  *                        interchangeable with a forward workspace).
  * Deterministic: repeated calls give the same bits.  Accuracy: each gradient
  * within 1e-4 of the same sum taken over absolute terms (|gy|, and
@@ -208,7 +213,8 @@ int rwkv_wkv4_backward(int64_t B, int64_t T, int64_t C,
  *   arguments   as for rwkv_wkv4_forward / rwkv_wkv4_backward
  *   ws, ws_bytes         a BACKWARD workspace: at least
  *                        rwkv_wkv4_backward_workspace(B,T,C) bytes, zero-filled
- *                        before its first use.
+ *                        before its first use and again at least once every
+ *                        2^30 calls.
  * The backward call must follow the forward call on the same stream, with the
  * same B, T, C, w, u, k, v and workspace, and no other call on that workspace
  * in between; otherwise its results are undefined (nothing checks this).

@@ -218,9 +218,14 @@ def _alloc(stream, fn, *args, **kw):
 
 # Workspaces are zero-filled once and reused per (device, stream): the
 # library leaves them ready for the next call on the same stream.  The fill
-# and the allocation happen on that stream, ahead of the call.
+# and the allocation happen on that stream, ahead of the call.  The RWKV-4
+# workspaces tag their words with a 32-bit count of launches (a call makes at
+# most two), so a cached one is zero-filled again every 2^30 calls, at the
+# first call made outside graph capture once the count has come round.
 _ws_cache: dict = {}
+_ws_calls: dict = {}
 _ws_lock = threading.Lock()
+_WS_REZERO_EVERY = 1 << 30
 
 
 def _workspace(kind: str, device, stream, nbytes: int):
@@ -234,6 +239,12 @@ def _workspace(kind: str, device, stream, nbytes: int):
             buf = _alloc(stream, torch.zeros, max(nbytes, 1 << 16), dtype=torch.uint8,
                          device=device)
             _ws_cache[key] = buf
+            _ws_calls[key] = 0
+        elif _ws_calls[key] >= _WS_REZERO_EVERY and not _alloc(
+                stream, torch.cuda.is_current_stream_capturing):
+            _alloc(stream, buf.zero_)
+            _ws_calls[key] = 0
+        _ws_calls[key] += 1
         return buf
 
 

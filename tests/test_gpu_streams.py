@@ -128,3 +128,27 @@ def test_matrix_state_entry_points_on_a_side_stream():
     for rep in range(2):
         log(f"Eagle and Finch forwards and steps on a side stream, call {rep}")
         _same(torch, dev, side, ref, run(side), "rwkv_wkv5/6")
+
+
+def test_cached_workspace_is_zero_filled_again_when_its_count_comes_round(monkeypatch):
+    """The binding zero-fills a cached RWKV-4 workspace again once it has
+    served its period of calls (2^30; 3 here), before the call that finds the
+    count come round: the workspace epoch (header word 1, one step per
+    forward launch) then counts from that fill, and every call's y is the
+    same."""
+    torch, dev = torch_dev()
+    monkeypatch.setattr(rw, "_WS_REZERO_EVERY", 3)
+    t = _wkv4(torch)
+    side = _side(torch, dev)
+    ys = []
+    for i in range(7):
+        log(f"wkv4_forward call {i} on a fresh side stream (re-zero period 3)")
+        ys.append(rw.rwkv_wkv4_forward(t["w"], t["u"], t["k"], t["v"], stream=side))
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    ws = rw.default_workspace("wkv4", dev, side)
+    # fills before calls 0 (allocation), 3 and 6: one launch since the last
+    assert ws.view(torch.int32)[1].item() == 1
+    assert rw.rwkv_wkv4_workspace_error(ws, stream=side) == 0
+    for y in ys[1:]:
+        assert torch.equal(y, ys[0])
