@@ -160,7 +160,11 @@ int rwkv_wkv4_forward(int64_t B, int64_t T, int64_t C,
  * (and again every 2^30 calls); it keeps the last call's contents, which the
  * next call needs no clearing of.  Make the first call on each device
  * outside graph capture (it also looks up the array's device address); a
- * fill recorded into a graph is repeated at the next call made outside one.  Every call on one GPU shares the array:
+ * fill recorded into a graph is repeated at the next call made outside one.
+ * Launches replayed from a captured graph are not counted: past 2^32
+ * launches without a fill the 32-bit call tags wrap, after which a call of
+ * a shape other than the last one's may find its tiles unclaimable and write
+ * NaN over its rows.  Every call on one GPU shares the array:
  * calls that overlap in time on that GPU (other streams, other threads)
  * race and are not allowed.  The array's error word is not exposed; a tile
  * that cannot run still writes NaN over its rows, as in rwkv_wkv4_forward.
