@@ -99,6 +99,8 @@ int rwkv_get_tuning(int key);
  *              (about 2^24 polls) and gave up; its outputs are NaN;
  *   bit 1 (2): a tile claim found a workspace that was never zero-filled;
  *              the rows of that tile are NaN.
+ * The backward's gw and gu, summed over every tile, are NaN in the channels
+ * of a tile of the call that gave up or could not be claimed.
  * Either bit means the outputs of the calls made since the word was last 0
  * are not to be trusted.  The word is sticky: zero-filling the workspace
  * (always allowed between calls) clears it.

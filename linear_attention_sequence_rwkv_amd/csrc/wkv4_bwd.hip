@@ -140,6 +140,12 @@ __global__ __launch_bounds__(64 * NW) void wkv4_bwd_tiled(
         gk[i] = __builtin_nanf("");
         gv[i] = __builtin_nanf("");
       }
+      // and the tile's gw, gu slots, so that the sums over tiles are NaN too
+      if (threadIdx.x < 64) {
+        const size_t pi = (size_t(lt) * (groups / n_cblk) + bi) * size_t(C) + size_t(ch);
+        tagged_store(part_w + pi, __builtin_nanf(""), tag);
+        tagged_store(part_u + pi, __builtin_nanf(""), tag);
+      }
     }
     return;
   }

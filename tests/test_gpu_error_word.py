@@ -12,8 +12,9 @@ forced with the spin-limit override at one poll: on 128 tiles per channel
 block the later tiles cannot see an inclusive history within their window in
 two polls, so they give up at once.
 
-Zero-filling the workspace clears the word, and the next call on it (with
-the default limit) is right again."""
+In the backward, gw and gu (sums over every tile) are NaN in the channels of
+a tile that gave up or was never claimed.  Zero-filling the workspace clears the word, and the next call on it
+(with the default limit) is right again."""
 import numpy as np
 import pytest
 
@@ -72,10 +73,11 @@ def test_backward_flags_a_workspace_never_zero_filled():
     ws = _poisoned(torch, need, B, C, dev)
     with tuned(wkv4_claim=True):
         log(f"wkv4_backward {B}x{T}x{C} on a workspace with foreign ticket counters")
-        _, _, gk, gv = rw.rwkv_wkv4_backward(*args, ws=ws)
+        gw, gu, gk, gv = rw.rwkv_wkv4_backward(*args, ws=ws)
         torch.cuda.synchronize()
         assert rw.rwkv_wkv4_workspace_error(ws) == 2
-        assert torch.isnan(gk).all().item() and torch.isnan(gv).all().item()
+        for g in (gw, gu, gk, gv):
+            assert torch.isnan(g).all().item()
         log("  zero-filled, again")
         ws.zero_()
         got = rw.rwkv_wkv4_backward(*args, ws=ws)
@@ -120,11 +122,14 @@ def test_backward_look_back_that_gives_up_sets_bit_0():
     ws = torch.zeros(rw.rwkv_wkv4_backward_workspace(B, T, C), dtype=torch.uint8, device=dev)
     with tuned(wkv4_spin=1):
         log(f"wkv4_backward {B}x{T}x{C} with a one-poll look-back limit")
-        _, _, gk, gv = rw.rwkv_wkv4_backward(*args, ws=ws)
+        gw, gu, gk, gv = rw.rwkv_wkv4_backward(*args, ws=ws)
         torch.cuda.synchronize()
         err = rw.rwkv_wkv4_workspace_error(ws)
         assert err & 1, err
         assert torch.isnan(gk).any().item()
+        # the channels of tiles that gave up
+        gave_up = torch.isnan(gk).any(dim=1).any(dim=0)
+        assert torch.isnan(gw)[gave_up].all().item() and torch.isnan(gu)[gave_up].all().item()
     log("  zero-filled, default limit")
     ws.zero_()
     got = rw.rwkv_wkv4_backward(*args, ws=ws)
