@@ -152,3 +152,33 @@ def test_cached_workspace_is_zero_filled_again_when_its_count_comes_round(monkey
     assert rw.rwkv_wkv4_workspace_error(ws, stream=side) == 0
     for y in ys[1:]:
         assert torch.equal(y, ys[0])
+
+
+@pytest.mark.parametrize("shape", [(8, 1024, 768), (1, 16384, 4096)])
+def test_two_streams_run_forwards_at_once(shape):
+    """Two streams, each with its own inputs and cached workspace, run RWKV-4
+    forwards that overlap on the device (launch-order tiles at 8x1024x768,
+    claimed tiles at 1x16384x4096): every output equals, bit for bit, the
+    same call made alone on the current stream."""
+    torch, dev = torch_dev()
+    B, T, C = shape
+    ins = []
+    for seed in (61, 62):
+        e = synth.wkv4_inputs(B, T, C, seed=seed)
+        ins.append([to_dev(e[n]) for n in ("w", "u", "k", "v")])
+    refs = [rw.rwkv_wkv4_forward(*a) for a in ins]
+    torch.cuda.synchronize()
+    streams = [_side(torch, dev), _side(torch, dev)]
+    log(f"wkv4_forward {B}x{T}x{C} on two streams at once, 6 calls each")
+    outs = [[], []]
+    for _ in range(6):
+        for j in (0, 1):
+            outs[j].append(rw.rwkv_wkv4_forward(*ins[j], stream=streams[j]))
+    for s in streams:
+        torch.cuda.current_stream(dev).wait_stream(s)
+    torch.cuda.synchronize()
+    for j in (0, 1):
+        ws = rw.default_workspace("wkv4", dev, streams[j])
+        assert rw.rwkv_wkv4_workspace_error(ws, stream=streams[j]) == 0
+        for y in outs[j]:
+            assert torch.equal(y, refs[j])
